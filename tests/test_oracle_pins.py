@@ -1,0 +1,297 @@
+"""Pins of the CPU oracle to facts fixed outside itself (CPU only).
+
+Every test here checks the oracle (and the input packers it reads) against a
+closed form, a hand-derived fixture under ``tests/golden``, an invariant, a
+textbook/library routine or exact brute force, so that a dropped term, a
+wrong sign, a wrong index or a transposed operand in the oracle fails one of
+them.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from conftest import read_golden
+
+
+# ---------------------------------------------------------------- layouts --
+
+def test_q3_closed_form_words():
+    for name, words, codes in read_golden("q3_pack_closed_forms.txt"):
+        w = np.array([int(h, 16) for h in words.split()], dtype=np.uint32)
+        c = np.array([int(v) for v in codes.split()])
+        got = oracle.unpack_q3(w.view(np.int32).reshape(3, 1))[:, 0]
+        assert np.array_equal(got, c), name
+        packed = synth.pack_q3(c.reshape(32, 1)).view(np.uint32)[:, 0]
+        assert np.array_equal(packed, w), name
+
+
+def test_q4_closed_form_words():
+    for name, word, codes in read_golden("q4_pack_closed_forms.txt"):
+        w = np.array([int(word, 16)], dtype=np.uint32)
+        q = np.array([int(v) for v in codes.split()])
+        got = oracle.unpack_q4(w.view(np.int32).reshape(1, 1))[:, 0]
+        assert np.array_equal(got, q), name
+        packed = synth.pack_q4((q + 8).reshape(8, 1)).view(np.uint32)[0, 0]
+        assert packed == w[0], name
+
+
+def test_q3_roundtrip_multiblock():
+    rng = np.random.default_rng(7)
+    codes = rng.integers(0, 8, size=(96, 5))
+    assert np.array_equal(oracle.unpack_q3(synth.pack_q3(codes)), codes)
+    # Columns and blocks are independent: a code changed in one (block, column)
+    # changes only that column's words of that block.
+    c2 = codes.copy()
+    c2[40, 3] ^= 5
+    d = synth.pack_q3(c2) != synth.pack_q3(codes)
+    assert set(zip(*np.nonzero(d))) <= {(3, 3), (4, 3), (5, 3)}
+
+
+def test_q4_roundtrip_multirow():
+    rng = np.random.default_rng(8)
+    q = rng.integers(-8, 8, size=(64, 7))
+    assert np.array_equal(oracle.unpack_q4(synth.pack_q4(q + 8)), q)
+
+
+# ----------------------------------------------------------- 3-bit matvec --
+
+def _q3_inputs(K, N, seed, codes=None, scales=None, zeros=None, x=None):
+    rng = np.random.default_rng(seed)
+    if codes is None:
+        codes = rng.integers(0, 8, size=(K, N))
+    if scales is None:
+        scales = rng.uniform(0.005, 0.02, N).astype(np.float32)
+    if zeros is None:
+        zeros = (scales * rng.integers(0, 8, N)).astype(np.float32)
+    if x is None:
+        x = rng.standard_normal(K).astype(np.float32)
+    return x, synth.pack_q3(codes), scales, zeros, codes
+
+
+def test_q3_all_zero_codes_closed_form():
+    # w = scale*0 - zero, so y[n] = -zero[n] * sum(x).
+    x, qw, s, z, _ = _q3_inputs(64, 12, 1, codes=np.zeros((64, 12), dtype=np.int64))
+    y = oracle.matvec_q3(x, qw, s, z)
+    expect = -z.astype(np.float64) * np.sum(x.astype(np.float64))
+    assert np.allclose(y, expect, rtol=1e-13, atol=1e-15)
+
+
+def test_q3_one_hot_rows():
+    # x = e_k selects row k of W: y[n] = scale[n]*q[k, n] - zero[n] for every k.
+    K, N = 64, 9
+    _, qw, s, z, codes = _q3_inputs(K, N, 2)
+    for k in range(K):
+        x = np.zeros(K, np.float32)
+        x[k] = 1.0
+        y = oracle.matvec_q3(x, qw, s, z)
+        expect = s.astype(np.float64) * codes[k] - z.astype(np.float64)
+        assert np.array_equal(y, expect), k
+
+
+def test_q3_integer_case_brute_force():
+    # scale 1, integer zero and small integer x: y is an exact integer.
+    K, N = 64, 6
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 8, size=(K, N))
+    z = rng.integers(0, 8, size=N)
+    x = rng.integers(-4, 5, size=K)
+    y = oracle.matvec_q3(x.astype(np.float32), synth.pack_q3(codes),
+                         np.ones(N, np.float32), z.astype(np.float32))
+    for n in range(N):
+        acc = 0
+        for k in range(K):
+            acc += int(x[k]) * (int(codes[k, n]) - int(z[n]))
+        assert y[n] == acc
+
+
+def test_q3_against_exact_rationals():
+    # 32x8 tile: fp64 oracle vs exact Fraction arithmetic on the stored fp32 values.
+    K, N = 32, 8
+    x, qw, s, z, codes = _q3_inputs(K, N, 4)
+    y = oracle.matvec_q3(x, qw, s, z)
+    for n in range(N):
+        exact = sum(Fraction(float(x[k])) * (Fraction(float(s[n])) * int(codes[k, n])
+                                             - Fraction(float(z[n]))) for k in range(K))
+        assert abs(Fraction(float(y[n])) - exact) <= abs(exact) * Fraction(1, 10 ** 13) + Fraction(1, 10 ** 30)
+
+
+def test_q3_scaling_invariance():
+    # y is linear in x and in (scale, zero) jointly.
+    x, qw, s, z, _ = _q3_inputs(96, 10, 5)
+    y = oracle.matvec_q3(x, qw, s, z)
+    assert np.array_equal(oracle.matvec_q3(2 * x, qw, s, z), 2 * y)
+    assert np.allclose(oracle.matvec_q3(x, qw, 4 * s, 4 * z), 4 * y, rtol=1e-14, atol=0)
+
+
+# --------------------------------------------------------- int8 group-wise --
+
+def test_q8_group_one_hot_uses_group_of_row():
+    K, N, G = 256, 5, 64
+    d = synth.gen_q8_group(1, K, N, G, seed=11)
+    for k in (0, 63, 64, 127, 128, 255):
+        x = np.zeros(K, np.float16)
+        x[k] = 1
+        y = oracle.gemm_q8_group(x, d["q"], d["scales"], G)[0]
+        expect = d["scales"][k // G].astype(np.float64) * d["q"][k].astype(np.float64)
+        assert np.array_equal(y, expect), k
+
+
+def test_q8_group_power_of_two_scales_closed_form():
+    # scale[g, n] = 2**g and x = 1: y[n] = sum_g 2**g * (sum of codes of group g).
+    K, N, G = 512, 7, 128
+    rng = np.random.default_rng(12)
+    q = rng.integers(-127, 128, size=(K, N)).astype(np.int8)
+    scales = np.array([[2.0 ** g] * N for g in range(K // G)], dtype=np.float32)
+    y = oracle.gemm_q8_group(np.ones(K, np.float16), q, scales, G)[0]
+    for n in range(N):
+        expect = 0
+        for g in range(K // G):
+            expect += 2 ** g * int(q[g * G:(g + 1) * G, n].astype(np.int64).sum())
+        assert y[n] == expect
+
+
+def test_q8_equal_scales_reduce_to_integer_dot():
+    # One scale everywhere: y = s * (x . q), with x small integers -> integer dot product.
+    K, N, G = 256, 16, 128
+    rng = np.random.default_rng(13)
+    q = rng.integers(-127, 128, size=(K, N)).astype(np.int8)
+    x = rng.integers(-3, 4, size=(2, K))
+    s = np.float32(0.25)
+    y = oracle.gemm_q8_group(x.astype(np.float16), q, np.full((K // G, N), s), G)
+    assert np.array_equal(y, float(s) * np.dot(x.astype(np.int64), q.astype(np.int64)))
+
+
+def test_q8_zero_codes():
+    d = synth.gen_q8_group(3, 256, 8, 128, seed=14)
+    y = oracle.gemm_q8_group(d["X"], np.zeros_like(d["q"]), d["scales"], 128)
+    assert np.all(y == 0)
+
+
+# ---------------------------------------------------------- 4-bit grouped --
+
+def test_q4_gidx_default_equals_k_over_g():
+    d = synth.gen_q4_group(2, 256, 12, 64, seed=21, act_order=False)
+    a = oracle.gemm_q4_group(d["X"], d["qweight"], d["scales"], None, 64)
+    b = oracle.gemm_q4_group(d["X"], d["qweight"], d["scales"], d["g_idx"], 64)
+    assert np.array_equal(a, b)
+
+
+def test_q4_one_hot_act_order():
+    K, N, G = 256, 9, 64
+    d = synth.gen_q4_group(1, K, N, G, seed=22, act_order=True)
+    assert not np.all(np.diff(d["g_idx"]) >= 0)       # really out of order
+    for k in (0, 1, 7, 8, 100, 255):
+        x = np.zeros(K, np.float16)
+        x[k] = 1
+        y = oracle.gemm_q4_group(x, d["qweight"], d["scales"], d["g_idx"], G)[0]
+        expect = d["scales"][d["g_idx"][k]].astype(np.float64) * d["codes"][k]
+        assert np.array_equal(y, expect), k
+
+
+def test_q4_consistent_k_permutation_invariance():
+    # Reordering K in codes, x and g_idx together leaves y unchanged (exact
+    # here: power-of-two scales and small integer activations).
+    K, N, G = 128, 6, 32
+    rng = np.random.default_rng(23)
+    q = rng.integers(-8, 8, size=(K, N))
+    g_idx = rng.permutation(np.repeat(np.arange(K // G), G)).astype(np.int32)
+    scales = (2.0 ** rng.integers(-3, 3, size=(K // G, N))).astype(np.float16)
+    x = rng.integers(-3, 4, size=(1, K)).astype(np.float16)
+    y = oracle.gemm_q4_group(x, synth.pack_q4(q + 8), scales, g_idx, G)
+    p = rng.permutation(K)
+    y2 = oracle.gemm_q4_group(x[:, p], synth.pack_q4(q[p] + 8), scales, g_idx[p], G)
+    assert np.array_equal(y, y2)
+
+
+def test_q4_zero_codes():
+    K, N, G = 64, 4, 32
+    qw = synth.pack_q4(np.full((K, N), 8))
+    y = oracle.gemm_q4_group(np.ones((3, K), np.float16), qw,
+                             np.ones((K // G, N), np.float16), None, G)
+    assert np.all(y == 0)
+
+
+def test_q4_generator_groups_balanced():
+    d = synth.gen_q4_group(1, 4096, 16, 128, seed=1300)
+    counts = np.bincount(d["g_idx"], minlength=32)
+    assert np.all(counts == 128)
+    assert d["codes"].min() >= -8 and d["codes"].max() <= 7
+
+
+# ------------------------------------------------------------------- W8A8 --
+
+def test_w8a8_quantiser_ties_and_extremes():
+    # Row absmax 127 -> Sx = 1 exactly; halves round to even.
+    X = np.array([[127.0, 2.5, -2.5, 3.5, -3.5, 0.5, 1.5, -127.0]], np.float32)
+    Xq, Sx = oracle.quantize_rows_int8(X)
+    assert Sx[0] == np.float32(1.0)
+    assert Xq[0].tolist() == [127, 2, -2, 4, -4, 0, 2, -127]
+
+
+def test_w8a8_quantiser_zero_row_and_bound():
+    rng = np.random.default_rng(31)
+    X = rng.standard_normal((4, 512)).astype(np.float32)
+    X[2] = 0
+    Xq, Sx = oracle.quantize_rows_int8(X)
+    assert Sx[2] == 0 and np.all(Xq[2] == 0)
+    for m in (0, 1, 3):
+        amax = np.max(np.abs(X[m]))
+        assert Sx[m] == np.float32(amax) / np.float32(127)
+        assert np.abs(Xq[m]).max() == 127
+        assert Xq[m][np.argmax(np.abs(X[m]))] == np.sign(X[m][np.argmax(np.abs(X[m]))]) * 127
+        err = np.abs(X[m].astype(np.float64) - Sx[m].astype(np.float64) * Xq[m])
+        assert np.all(err <= 0.5 * Sx[m] * (1 + 1e-6))
+
+
+def test_w8a8_rearrangement_identity():
+    # Y = (Sx*Xint).(Wint*Sw) = Sx*(Xint.Wint)*Sw ("Quantization CUDA", Dynamic Quantization).
+    d = synth.gen_w8a8(8, 256, 24, seed=32)
+    r = oracle.gemm_w8a8(d["X"], d["Wq"], d["Sw"])
+    lhs = ((r["Sx"].astype(np.float64)[:, None] * r["Xq"])
+           @ (d["Wq"].T.astype(np.float64) * d["Sw"].astype(np.float64)[None, :]))
+    assert np.allclose(lhs, r["y_exact"], rtol=1e-12, atol=1e-300)
+    # and the quantised product approximates the float one
+    ref = d["X"].astype(np.float64) @ (d["Wq"].T.astype(np.float64) * d["Sw"][None, :])
+    assert np.linalg.norm(r["y_exact"] - ref) / np.linalg.norm(ref) < 0.02
+
+
+def test_w8a8_accumulator_exact_vs_int64():
+    rng = np.random.default_rng(33)
+    Xq = rng.integers(-127, 128, size=(64, 8192)).astype(np.int8)
+    Wq = rng.integers(-127, 128, size=(64, 8192)).astype(np.int8)
+    acc = oracle.w8a8_accumulate(Xq, Wq)
+    ref = Xq.astype(np.int64) @ Wq.astype(np.int64).T
+    assert np.array_equal(acc.astype(np.int64), ref)
+    # extreme magnitudes: all +127 -> K * 127^2 exactly
+    big = oracle.w8a8_accumulate(np.full((1, 8192), 127, np.int8), np.full((1, 8192), -127, np.int8))
+    assert big[0, 0] == -8192 * 127 * 127
+
+
+def test_bf16_and_fp16_ties_golden():
+    for fmt, inp, exp in read_golden("rounding_ties.txt"):
+        v = np.array([float(inp)], np.float32)
+        if fmt == "bf16":
+            got = oracle.bf16_bits_to_f32(oracle.bf16_rne_bits(v))[0]
+        else:
+            got = v.astype(np.float16)[0]
+        assert float(got) == float(exp), (fmt, inp)
+
+
+def test_bf16_matches_torch_cpu():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(34)
+    v = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000),
+                        [0.0, -0.0, 1e-40, -1e-40, 3.0e38, -3.0e38]]).astype(np.float32)
+    ours = oracle.bf16_rne_bits(v)
+    theirs = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, theirs)
+
+
+def test_w8a8_epilogue_ties_through_path():
+    # Sx = Sw = 1: the epilogue is bf16(acc); 257 -> 256, 259 -> 260, 514 -> 512, 518 -> 520.
+    acc = np.array([[257, 259, 514, 518, -257]], np.int32)
+    y = oracle.bf16_bits_to_f32(oracle.w8a8_epilogue(acc, np.ones(1, np.float32), np.ones(5, np.float32)))
+    assert y.tolist() == [[256.0, 260.0, 512.0, 520.0, -256.0]]
