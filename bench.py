@@ -1,0 +1,286 @@
+"""Benchmark of the fused dequantize-and-multiply kernels on one MI355X.
+
+Default workload: the M=1 group-wise int8 weight-only GEMV, K = N = 4096,
+group 128 (fp16 activations, fp32 accumulation, fp16 output).  One step is
+one call of the fused kernel on one batch of synthetic input.  The metric is
+achieved HBM bandwidth over the algorithmic bytes of a call (packed weight,
+scales and activations read once, output written once), as GB/s and as a
+fraction of the 8 TB/s HBM3E peak.
+
+Inputs sit in HBM before timing starts.  To keep the weights from being
+served by the 256 MB Infinity Cache or the L2s, the argument set is
+replicated R times (R * bytes >= 512 MB) and the steps cycle through the
+copies.  Time is taken with HIP events on the stream the kernels are
+launched on, bracketing exactly `--steps` calls after `--warmup` untimed
+ones.
+
+Extra fields on the single JSON line:
+* roofline: the dominant (only) kernel's bandwidth against 8 TB/s; "traffic"
+  comes from the rocprofv3 counter summary committed under profiles/ when it
+  was taken on the current kernel source, else null.
+* cpu_baseline: the CPU oracle (numpy, fp64) timed on this host on the same
+  workload, repeated for a bounded ~10 s.
+* secondary (unless --headline-only): the other workloads of the library,
+  each as microseconds per call and GB/s (or TOPS) with the same method.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0
+MALL_BYTES = 256 << 20
+
+
+def _sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "q8_group": ["weight_only_quantized_dequant_amd/csrc/q8_group.hip",
+                 "weight_only_quantized_dequant_amd/csrc/wq_device.hpp"],
+}
+
+
+def committed_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if current."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha") != _sha(KERNEL_SOURCES[kernel]):
+        return None
+    try:
+        return int(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# --------------------------------------------------------------- workloads --
+
+class Workload:
+    """One configuration: builds R device copies and runs one step on copy i."""
+
+    def __init__(self, name, nbytes, make, run, flops=0):
+        self.name, self.nbytes, self.make, self.run, self.flops = name, nbytes, make, run, flops
+
+
+def _rotation(nbytes, floor=2 * MALL_BYTES, cap=64):
+    return int(min(cap, max(1, -(-floor // nbytes))))
+
+
+def wl_q8(wq, torch, dev):
+    import synth
+    M, K, N, G = 1, 4096, 4096, 128
+    nbytes = K * N + (K // G) * N * 4 + M * K * 2 + M * N * 2
+    d = synth.gen_q8_group(M, K, N, G, seed=synth.SEEDS["q8_group_4096"])
+
+    def make(R):
+        base = [torch.from_numpy(a).to(dev) for a in (d["X"], d["q"], d["scales"])]
+        copies = [[t.clone() for t in base] + [torch.empty((M, N), dtype=torch.float16, device=dev)]
+                  for _ in range(R)]
+        return copies
+
+    def run(c):
+        wq.gemm_q8_group(c[0], c[1], c[2], G, Y=c[3])
+
+    w = Workload("q8_group_gemv M=1 K=4096 N=4096 G=128", nbytes, make, run)
+    w.config = {"workload": w.name, "M": M, "K": K, "N": N, "group": G}
+    w.oracle = lambda: __import__("oracle").gemm_q8_group(d["X"], d["q"], d["scales"], G)
+    w.dtype = "int8 weight x fp16 act, fp32 accumulate"
+    return w
+
+
+def wl_q3(wq, torch, dev, K, N, dt, seed):
+    import synth
+    esz = 4 if dt == "f32" else 2
+    nbytes = (K // 32) * 3 * N * 4 + 2 * N * esz + K * esz + N * esz
+    d = synth.gen_q3(K, N, seed=seed, dtype=dt)
+
+    def make(R):
+        base = [torch.from_numpy(a).to(dev) for a in (d["x"], d["qweight"], d["scales"], d["zeros"])]
+        return [[t.clone() for t in base] + [torch.empty(N, dtype=base[0].dtype, device=dev)]
+                for _ in range(R)]
+
+    def run(c):
+        wq.matvec_q3(c[0], c[1], c[2], c[3], y=c[4])
+
+    w = Workload(f"q3_matvec_{dt} K={K} N={N}", nbytes, make, run)
+    w.oracle = lambda: __import__("oracle").matvec_q3(d["x"], d["qweight"], d["scales"], d["zeros"])
+    return w
+
+
+def wl_q4(wq, torch, dev, M):
+    import synth
+    K, N, G = 4096, 11008, 128
+    nbytes = (K // 8) * N * 4 + (K // G) * N * 2 + K * 4 + M * K * 2 + M * N * 2
+    d = synth.gen_q4_group(M, K, N, G, seed=synth.SEEDS["q4_group_actorder"])
+
+    def make(R):
+        qw = torch.from_numpy(d["qweight"]).to(dev)
+        packed, perm = wq.prepare_q4(qw, d["g_idx"], G)
+        base = [torch.from_numpy(d["X"]).to(dev), packed, torch.from_numpy(d["scales"]).to(dev), perm]
+        return [[t.clone() for t in base] + [torch.empty((M, N), dtype=torch.float16, device=dev)]
+                for _ in range(R)]
+
+    def run(c):
+        wq.gemm_q4_group(c[0], c[1], c[2], c[3], G, Y=c[4])
+
+    w = Workload(f"q4_group_actorder M={M} K={K} N={N} G={G}", nbytes, make, run)
+    w.oracle = lambda: __import__("oracle").gemm_q4_group(d["X"], d["qweight"], d["scales"], d["g_idx"], G)
+    return w
+
+
+def wl_w8a8(wq, torch, dev):
+    import synth
+    M, K, N = 256, 8192, 8192
+    # quantiser: read X fp32, write Xq + Sx; GEMM: read Xq, Wq, Sx, Sw, write Y
+    nbytes = (M * K * 4 + M * K + M * 4) + (M * K + N * K + M * 4 + N * 4 + M * N * 2)
+    d = synth.gen_w8a8(M, K, N, seed=synth.SEEDS["w8a8_256x8192x8192"])
+
+    def make(R):
+        base = [torch.from_numpy(a).to(dev) for a in (d["X"], d["Wq"], d["Sw"])]
+        return [[t.clone() for t in base] + [torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+                                             torch.empty((M, K), dtype=torch.int8, device=dev),
+                                             torch.empty(M, dtype=torch.float32, device=dev)]
+                for _ in range(R)]
+
+    def run(c):
+        wq.gemm_w8a8(c[0], c[1], c[2], Y=c[3], Xq=c[4], Sx=c[5])
+
+    w = Workload(f"w8a8_dynamic M={M} K={K} N={N}", nbytes, make, run, flops=2 * M * K * N)
+    w.oracle = lambda: __import__("oracle").gemm_w8a8(d["X"], d["Wq"], d["Sw"])
+    return w
+
+
+def time_workload(torch, w, steps, warmup, R=None):
+    R = R or _rotation(w.nbytes)
+    copies = w.make(R)
+    for i in range(warmup):
+        w.run(copies[i % R])
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        w.run(copies[i % R])
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    del copies
+    torch.cuda.empty_cache()
+    return ms, R
+
+
+def cpu_baseline(w, budget_s=10.0):
+    """Time the CPU oracle on the same workload, repeated for about budget_s."""
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        w.oracle()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 200:
+            break
+    per = el / n
+    return {"value": round(w.nbytes / per / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n} full oracle calls ({w.name}: unpack, fp64 dequantise, fp64 matmul), "
+                      f"{per * 1e3:.1f} ms each"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--headline-only", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="q8", help="q8 (headline) | q3_* | q4_m* | w8a8 (single line)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    import weight_only_quantized_dequant_amd as wq
+    wq.lib()
+    dev = torch.device("cuda:0")
+
+    def make(name):
+        if name == "q8":
+            return wl_q8(wq, torch, dev)
+        if name == "q3_f32_1024":
+            return wl_q3(wq, torch, dev, 1024, 1024, "f32", 1000)
+        if name.startswith("q3_f16_"):
+            K, N = (int(v) for v in name[len("q3_f16_"):].split("x"))
+            seed = {(4096, 4096): 1200, (4096, 11008): 1201, (11008, 4096): 1202}.get((K, N), 1203)
+            return wl_q3(wq, torch, dev, K, N, "f16", seed)
+        if name.startswith("q4_m"):
+            return wl_q4(wq, torch, dev, int(name[4:]))
+        if name == "w8a8":
+            return wl_w8a8(wq, torch, dev)
+        raise SystemExit(f"unknown workload {name}")
+
+    w = make(args.workload)
+    ms, R = time_workload(torch, w, args.steps, args.warmup)
+    gbs = w.nbytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "Achieved HBM GB/s (% of 8 TB/s) for M=1 fused-dequant GEMV, K=N=4096",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": getattr(w, "dtype", "see workload"), "data": "synthetic (seeded, see DESIGN.md)",
+        "config": dict(getattr(w, "config", {"workload": w.name}), rotation_copies=R,
+                       pct_of_hbm_peak=round(100 * gbs / HBM_PEAK_GBS, 2)),
+    }
+    kern = "q8_group" if args.workload == "q8" else None
+    traffic = committed_traffic(kern, "4096") if kern else None
+    out["roofline"] = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                       "algorithmic_bytes_per_launch": w.nbytes}
+    if not args.headline_only:
+        sec = {}
+        for name in ("q3_f32_1024", "q3_f16_4096x4096", "q3_f16_4096x11008", "q3_f16_11008x4096",
+                     "q4_m1", "q4_m2", "q4_m4", "q4_m8", "w8a8"):
+            sw = make(name)
+            sms, sR = time_workload(torch, sw, 300 if name != "w8a8" else 100, 30 if name != "w8a8" else 10)
+            e = {"us_per_call": round(sms * 1e3, 3), "GB_per_s": round(sw.nbytes / (sms * 1e-3) / 1e9, 1),
+                 "pct_hbm_peak": round(100 * sw.nbytes / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                 "rotation_copies": sR, "algorithmic_bytes": sw.nbytes}
+            if sw.flops:
+                e["TOPS"] = round(sw.flops / (sms * 1e-3) / 1e12, 1)
+                e["pct_int8_peak"] = round(100 * sw.flops / (sms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2)
+            sec[sw.name] = e
+            del sw
+        out["secondary"] = sec
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

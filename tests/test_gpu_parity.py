@@ -1,0 +1,288 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the CPU oracle.
+
+Bars: integer results (unpacked codes, the W8A8 activation codes, scales and
+int32 accumulators, and the bf16 output bits of the fixed-order epilogue)
+are compared bit for bit.  Floating outputs of the weight-only paths must
+have relative L2 error <= 1e-3 and max-abs error <= 5e-3 * RMS against the
+oracle's unrounded fp64 result; cases built so that every fp32 partial sum is
+an exact integer are compared exactly (after the same final rounding).
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+REL_L2, MAX_ABS_RMS = 1e-3, 5e-3
+
+
+@pytest.fixture(scope="module")
+def wq():
+    import weight_only_quantized_dequant_amd as m
+    m.lib()
+    return m
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def cu(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev())
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def assert_tol(y, y_exact, what=""):
+    y = np.asarray(y, np.float64).ravel()
+    e = np.asarray(y_exact, np.float64).ravel()
+    rms = np.sqrt(np.mean(e ** 2))
+    rel = np.linalg.norm(y - e) / max(np.linalg.norm(e), 1e-300)
+    mx = np.max(np.abs(y - e)) / max(rms, 1e-300)
+    print(f"{what}: rel_l2={rel:.3e} max_abs/rms={mx:.3e}")
+    assert rel <= REL_L2, (what, rel)
+    assert mx <= MAX_ABS_RMS, (what, mx)
+
+
+# ================================================================== int8 ==
+
+@pytest.mark.parametrize("M,K,N,G", [
+    (1, 4096, 4096, 128),        # the headline GEMV
+    (1, 256, 16, 128), (1, 384, 272, 128), (2, 512, 1024, 64), (3, 640, 528, 128),
+    (4, 4096, 1040, 128), (5, 1024, 256, 32), (8, 2048, 4096, 128), (9, 768, 784, 128),
+    (16, 256, 512, 256),
+])
+def test_q8_group_vs_oracle(wq, M, K, N, G):
+    d = synth.gen_q8_group(M, K, N, G, seed=1100 if (M, K, N) == (1, 4096, 4096) else 7 + M + K + N)
+    Y = wq.gemm_q8_group(cu(d["X"]), cu(d["q"]), cu(d["scales"]), G)
+    assert_tol(host(Y), oracle.gemm_q8_group(d["X"], d["q"], d["scales"], G), f"q8 {M}x{K}x{N} G{G}")
+
+
+def test_q8_integer_exact(wq):
+    # scale 1, small integer x: every fp32 partial sum is an exact integer.
+    M, K, N, G = 3, 1024, 528, 128
+    rng = np.random.default_rng(41)
+    q = rng.integers(-127, 128, size=(K, N)).astype(np.int8)
+    X = rng.integers(-2, 3, size=(M, K)).astype(np.float16)
+    s = np.ones((K // G, N), np.float32)
+    Y = host(wq.gemm_q8_group(cu(X), cu(q), cu(s), G))
+    ref = oracle.gemm_q8_group(X, q, s, G).astype(np.float16).astype(np.float64)
+    assert np.array_equal(Y, ref)
+
+
+def test_q8_output_rounding_ties(wq):
+    # sum x*q = 2049 -> fp16 2048 and 2051 -> 2052 (round half to even).
+    K, N, G = 128, 16, 128
+    q = np.zeros((K, N), np.int8)
+    x = np.zeros(K, np.float16)
+    q[0, :], x[0] = 127, 16            # 2032 in every column
+    q[2, 0], q[2, 1], x[2] = 17, 19, 1  # column 0: 2049, column 1: 2051
+    s = np.ones((1, N), np.float32)
+    y = host(wq.gemm_q8_group(cu(x), cu(q), cu(s), G))
+    assert y[0] == 2048 and y[1] == 2052
+
+
+def test_q8_one_hot_rows(wq):
+    K, N, G = 512, 272, 128
+    d = synth.gen_q8_group(1, K, N, G, seed=42)
+    for k in (0, 1, 127, 128, 300, 511):
+        x = np.zeros(K, np.float16)
+        x[k] = 1
+        y = host(wq.gemm_q8_group(cu(x), cu(d["q"]), cu(d["scales"]), G))
+        ref = (d["scales"][k // G].astype(np.float64) * d["q"][k]).astype(np.float16).astype(np.float64)
+        assert np.array_equal(y, ref), k
+
+
+def test_q8_deterministic_and_scale_exact(wq):
+    d = synth.gen_q8_group(1, 4096, 4096, 128, seed=1100)
+    X, q, s = cu(d["X"]), cu(d["q"]), cu(d["scales"])
+    y0 = wq.gemm_q8_group(X, q, s, 128).clone()
+    for _ in range(20):
+        assert torch.equal(wq.gemm_q8_group(X, q, s, 128), y0)
+    y2 = wq.gemm_q8_group(X * 2, q, s, 128)
+    assert torch.equal(y2, y0 * 2)
+
+
+@pytest.mark.parametrize("unit", ["8", "16", "32"])
+def test_q8_split_plans_agree(wq, unit):
+    d = synth.gen_q8_group(1, 4096, 4096, 128, seed=1100)
+    ref = oracle.gemm_q8_group(d["X"], d["q"], d["scales"], 128)
+    os.environ["WQ_SPLITK_UNIT"] = unit
+    try:
+        Y = host(wq.gemm_q8_group(cu(d["X"]), cu(d["q"]), cu(d["scales"]), 128))
+    finally:
+        del os.environ["WQ_SPLITK_UNIT"]
+    assert_tol(Y, ref, f"q8 unit {unit}")
+
+
+# ================================================================= 3-bit ==
+
+@pytest.mark.parametrize("K,N", [(1024, 1024), (4096, 4096), (4096, 11008), (11008, 4096), (96, 20)])
+def test_unpack_q3_bit_exact(wq, K, N):
+    d = synth.gen_q3(K, N, seed=5 + K + N, dtype="f16")
+    codes = wq.unpack_q3(cu(d["qweight"]), K)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy().astype(np.int64), oracle.unpack_q3(d["qweight"]))
+
+
+@pytest.mark.parametrize("K,N,dt,seed", [
+    (1024, 1024, "f32", 1000),                     # the 3-bit fp32 matvec
+    (4096, 4096, "f16", 1200), (4096, 11008, "f16", 1201), (11008, 4096, "f16", 1202),
+    (32, 4, "f32", 3), (96, 260, "f16", 4), (1056, 516, "f32", 5), (2080, 1028, "f16", 6),
+])
+def test_q3_vs_oracle(wq, K, N, dt, seed):
+    d = synth.gen_q3(K, N, seed=seed, dtype=dt)
+    y = wq.matvec_q3(cu(d["x"]), cu(d["qweight"]), cu(d["scales"]), cu(d["zeros"]))
+    ref = oracle.matvec_q3(d["x"], d["qweight"], d["scales"], d["zeros"])
+    assert_tol(host(y), ref, f"q3 {dt} {K}x{N}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_q3_integer_exact_and_zero_codes(wq, dt):
+    K, N = 1024, 516
+    rng = np.random.default_rng(51)
+    npdt = np.float32 if dt == "f32" else np.float16
+    codes = rng.integers(0, 8, size=(K, N))
+    z = rng.integers(0, 8, size=N).astype(npdt)
+    x = rng.integers(-3, 4, size=K).astype(npdt)
+    s = np.ones(N, npdt)
+    y = host(wq.matvec_q3(cu(x), cu(synth.pack_q3(codes)), cu(s), cu(z)))
+    ref = oracle.matvec_q3(x, synth.pack_q3(codes), s, z).astype(npdt).astype(np.float64)
+    assert np.array_equal(y, ref)
+    # all-zero codes: y = -zero * sum(x)
+    y0 = host(wq.matvec_q3(cu(x), cu(synth.pack_q3(np.zeros((K, N), np.int64))), cu(s), cu(z)))
+    assert np.array_equal(y0, (-z.astype(np.float64) * x.astype(np.float64).sum()).astype(npdt).astype(np.float64))
+
+
+def test_q3_one_hot_rows(wq):
+    K, N = 256, 260
+    d = synth.gen_q3(K, N, seed=52, dtype="f32")
+    for k in (0, 6, 10, 21, 31, 32, 100, 255):
+        x = np.zeros(K, np.float32)
+        x[k] = 1
+        y = host(wq.matvec_q3(cu(x), cu(d["qweight"]), cu(d["scales"]), cu(d["zeros"])))
+        ref = d["scales"].astype(np.float64) * d["codes"][k] - d["zeros"].astype(np.float64)
+        assert np.allclose(y, ref, rtol=1e-6, atol=1e-7), k
+
+
+# ================================================================= 4-bit ==
+
+@pytest.mark.parametrize("act", [True, False])
+def test_unpack_q4_bit_exact(wq, act):
+    K, N, G = 4096, 11008, 128
+    d = synth.gen_q4_group(1, K, N, G, seed=1300, act_order=act)
+    qw = cu(d["qweight"])
+    ref = oracle.unpack_q4(d["qweight"])
+    codes = wq.unpack_q4(qw, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy().astype(np.int64), ref)
+    packed, perm = wq.prepare_q4(qw, d["g_idx"] if act else None, G)
+    codes2 = wq.unpack_q4(packed, K, perm)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes2.cpu().numpy().astype(np.int64), ref)
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8])
+def test_q4_act_order_headline(wq, M):
+    K, N, G = 4096, 11008, 128
+    d = synth.gen_q4_group(M, K, N, G, seed=1300, act_order=True)
+    packed, perm = wq.prepare_q4(cu(d["qweight"]), d["g_idx"], G)
+    Y = wq.gemm_q4_group(cu(d["X"]), packed, cu(d["scales"]), perm, G)
+    ref = oracle.gemm_q4_group(d["X"], d["qweight"], d["scales"], d["g_idx"], G)
+    assert_tol(host(Y), ref, f"q4 M{M}")
+
+
+@pytest.mark.parametrize("M,K,N,G,act", [
+    (1, 128, 4, 32, True), (3, 384, 260, 64, True), (5, 1024, 1028, 128, False),
+    (9, 512, 516, 128, True), (2, 2048, 256, 32, False), (16, 256, 64, 128, True),
+])
+def test_q4_small_ragged(wq, M, K, N, G, act):
+    d = synth.gen_q4_group(M, K, N, G, seed=60 + M + K, act_order=act)
+    packed, perm = wq.prepare_q4(cu(d["qweight"]), d["g_idx"] if act else None, G)
+    Y = wq.gemm_q4_group(cu(d["X"]), packed, cu(d["scales"]), perm, G)
+    ref = oracle.gemm_q4_group(d["X"], d["qweight"], d["scales"], d["g_idx"], G)
+    assert_tol(host(Y), ref, f"q4 {M}x{K}x{N} G{G} act={act}")
+    if not act:  # without act-order the stored weight is used as is
+        Y2 = wq.gemm_q4_group(cu(d["X"]), cu(d["qweight"]), cu(d["scales"]), None, G)
+        assert torch.equal(Y, Y2)
+
+
+def test_q4_one_hot_act_order(wq):
+    K, N, G = 512, 260, 128
+    d = synth.gen_q4_group(1, K, N, G, seed=61, act_order=True)
+    packed, perm = wq.prepare_q4(cu(d["qweight"]), d["g_idx"], G)
+    for k in (0, 1, 5, 200, 511):
+        x = np.zeros(K, np.float16)
+        x[k] = 1
+        y = host(wq.gemm_q4_group(cu(x), packed, cu(d["scales"]), perm, G))
+        ref = (d["scales"][d["g_idx"][k]].astype(np.float64) * d["codes"][k]).astype(np.float16)
+        assert np.array_equal(y, ref.astype(np.float64)), k
+
+
+def test_q4_integer_exact(wq):
+    M, K, N, G = 4, 1024, 516, 128
+    rng = np.random.default_rng(62)
+    q = rng.integers(-8, 8, size=(K, N))
+    g_idx = rng.permutation(np.repeat(np.arange(K // G), G)).astype(np.int32)
+    s = np.ones((K // G, N), np.float16)
+    X = rng.integers(-3, 4, size=(M, K)).astype(np.float16)
+    qw = synth.pack_q4(q + 8)
+    packed, perm = wq.prepare_q4(cu(qw), g_idx, G)
+    Y = host(wq.gemm_q4_group(cu(X), packed, cu(s), perm, G))
+    ref = oracle.gemm_q4_group(X, qw, s, g_idx, G).astype(np.float16).astype(np.float64)
+    assert np.array_equal(Y, ref)
+
+
+# ================================================================== W8A8 ==
+
+def _w8a8_check(wq, d):
+    Y, Xq, Sx, acc = wq.gemm_w8a8(cu(d["X"]), cu(d["Wq"]), cu(d["Sw"]), want_acc=True)
+    torch.cuda.synchronize()
+    r = oracle.gemm_w8a8(d["X"], d["Wq"], d["Sw"])
+    assert np.array_equal(Xq.cpu().numpy(), r["Xq"])
+    assert np.array_equal(Sx.cpu().numpy().view(np.uint32), r["Sx"].view(np.uint32))
+    assert np.array_equal(acc.cpu().numpy(), r["acc"])
+    yb = Y.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(yb, r["y_bits"])
+    return Y, r
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 64, 16), (17, 192, 80), (128, 512, 256), (130, 256, 528),
+                                   (256, 1024, 1040)])
+def test_w8a8_small_bit_exact(wq, M, K, N):
+    _w8a8_check(wq, synth.gen_w8a8(M, K, N, seed=70 + M + K + N))
+
+
+def test_w8a8_headline_bit_exact(wq):
+    Y, r = _w8a8_check(wq, synth.gen_w8a8(256, 8192, 8192, seed=1400))
+    # reported, not gated: distance of the bf16 result to the unrounded product
+    y = Y.float().cpu().numpy().astype(np.float64)
+    e = r["y_exact"]
+    print("w8a8 bf16 vs exact: rel_l2=%.3e" % (np.linalg.norm(y - e) / np.linalg.norm(e)))
+
+
+def test_w8a8_ties_and_zero_row(wq):
+    K, N = 64, 16
+    X = np.zeros((3, K), np.float32)
+    X[0, 0], X[0, 1] = 127.0, 1.0        # Sx = 1; Xq = [127, 1, 0...]
+    X[1, :4] = [127.0, 2.5, -3.5, 0.5]   # halves round to even: 2, -4, 0
+    Wq = np.zeros((N, K), np.int8)
+    Wq[0, 0], Wq[0, 1] = 2, 3            # acc = 257 -> bf16 256
+    Wq[1, 0], Wq[1, 1] = 2, 5            # acc = 259 -> bf16 260
+    Wq[2, 0], Wq[2, 1] = 4, 6            # acc = 514 -> 512
+    Wq[3, 0], Wq[3, 1] = 4, 10           # acc = 518 -> 520
+    Sw = np.ones(N, np.float32)
+    Y, Xq, Sx, acc = wq.gemm_w8a8(cu(X), cu(Wq), cu(Sw), want_acc=True)
+    torch.cuda.synchronize()
+    y = Y.float().cpu().numpy()
+    assert y[0, :4].tolist() == [256.0, 260.0, 512.0, 520.0]
+    assert Xq.cpu().numpy()[1, :4].tolist() == [127, 2, -4, 0]
+    assert Sx.cpu().numpy()[2] == 0 and np.all(Xq.cpu().numpy()[2] == 0) and np.all(y[2] == 0)
