@@ -95,7 +95,8 @@ def wl_q8(wq, torch, dev):
     d = synth.gen_q8_group(M, K, N, G, seed=synth.SEEDS["q8_group_4096"])
 
     def make(R):
-        base = [torch.from_numpy(a).to(dev) for a in (d["X"], d["q"], d["scales"])]
+        base = [torch.from_numpy(d["X"]).to(dev), wq.prepack_q8(torch.from_numpy(d["q"]).to(dev)),
+                torch.from_numpy(d["scales"]).to(dev)]
         copies = [[t.clone() for t in base] + [torch.empty((M, N), dtype=torch.float16, device=dev)]
                   for _ in range(R)]
         return copies
@@ -118,6 +119,7 @@ def wl_q3(wq, torch, dev, K, N, dt, seed):
 
     def make(R):
         base = [torch.from_numpy(a).to(dev) for a in (d["x"], d["qweight"], d["scales"], d["zeros"])]
+        base[1] = wq.prepack_q3(base[1], K)
         return [[t.clone() for t in base] + [torch.empty(N, dtype=base[0].dtype, device=dev)]
                 for _ in range(R)]
 
@@ -137,8 +139,8 @@ def wl_q4(wq, torch, dev, M):
 
     def make(R):
         qw = torch.from_numpy(d["qweight"]).to(dev)
-        packed, perm = wq.prepare_q4(qw, d["g_idx"], G)
-        base = [torch.from_numpy(d["X"]).to(dev), packed, torch.from_numpy(d["scales"]).to(dev), perm]
+        packed, _, inv = wq.prepare_q4(qw, d["g_idx"], G)
+        base = [torch.from_numpy(d["X"]).to(dev), packed, torch.from_numpy(d["scales"]).to(dev), inv]
         return [[t.clone() for t in base] + [torch.empty((M, N), dtype=torch.float16, device=dev)]
                 for _ in range(R)]
 
@@ -173,19 +175,38 @@ def wl_w8a8(wq, torch, dev):
 
 
 def time_workload(torch, w, steps, warmup, R=None):
+    """Average time of one step over exactly `steps` back-to-back steps.
+
+    The steps are captured once into a HIP graph (each one a separate call on
+    the next copy of the arguments), so what is timed is the GPU work, not the
+    Python argument checks of each call.  HIP events bracket one replay of the
+    graph on the stream it runs on.
+    """
     R = R or _rotation(w.nbytes)
     copies = w.make(R)
     for i in range(warmup):
         w.run(copies[i % R])
     torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        w.run(copies[0])  # first call on the side stream, outside the capture
+        torch.cuda.current_stream().synchronize()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(steps):
+                w.run(copies[i % R])
+    torch.cuda.synchronize()
+    graph.replay()  # untimed: first replay uploads the graph
+    torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(steps):
-        w.run(copies[i % R])
-    end.record()
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        graph.replay()
+        end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
-    del copies
+    del graph, copies
     torch.cuda.empty_cache()
     return ms, R
 

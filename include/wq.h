@@ -24,29 +24,38 @@
  *     int8 multiply, int32 accumulation, Y = Sx * (Xint.Wint) * Sw with the
  *     rescale fused after the accumulation and a bf16 result).
  *
+ * Weight layouts
+ * --------------
+ * The weight-only products read a copy of the weight that wq_prepack_*
+ * writes once, offline (the weights are constant; "Quantization CUDA",
+ * section "Marlin 格式", re-lays quantised weights out the same way for its
+ * kernel).  The copy holds exactly the same codes, regrouped into column
+ * panels over the whole of K in the order the GPU threads read them, so one
+ * workgroup computes a panel of outputs alone and every load of a wave is
+ * contiguous.  Its size is wq_packed_bytes(); it is opaque, and only valid
+ * for the (op, K, N, G) it was made for.  wq_unpack_* read it back to plain
+ * codes through the same register-level extraction the products use.
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Memory: every array argument is a DEVICE pointer owned by the caller,
  *   except where an argument is marked HOST.  The library never allocates or
  *   frees memory, never synchronises a stream, and never changes the current
  *   device; work runs on the device that owns the buffers, on `stream`
- *   (a hipStream_t; NULL means the default stream), asynchronously.
- * - Layout: row-major and contiguous.  Packed weights keep N (the output
- *   column) contiguous; codes are packed along K.
+ *   (a hipStream_t; NULL means the default stream), asynchronously.  No
+ *   workspace is needed: no partial result ever leaves a workgroup.
+ * - Layout: row-major and contiguous.  Stored (unpacked) weights keep N (the
+ *   output column) contiguous; codes are packed along K.
  * - Outputs are overwritten, never accumulated into.
- * - Alignment: packed weights, X/x and scales must be 16-byte aligned.
+ * - Alignment: weights (plain and packed), X/x and scales must be 16-byte
+ *   aligned; so must g_idx-derived permutation arrays.
  * - Errors: every call returns a wq_status_t.  Argument checks run on the
  *   host before any HIP call; a failed check launches nothing.  A launch
  *   failure returns WQ_ERR_HIP (the hipError_t is kept per thread, see
  *   wq_last_hip_error).  A fault inside a kernel surfaces at the caller's next
  *   synchronisation, as for any HIP library.  Nothing throws or aborts.
- * - Workspace: the weight-only products split K across workgroups and need a
- *   device workspace of wq_workspace_bytes(...) bytes for the partial sums and
- *   the per-tile arrival counters.  It must be zero-filled once after
- *   allocation; every call leaves it zero-filled again.  Calls that may run
- *   concurrently (different streams) need distinct workspaces.
  * - Results are bitwise reproducible for a given shape: every reduction runs
- *   in a fixed order.
+ *   in a fixed order.  Calls are re-entrant and may run concurrently.
  */
 #ifndef WQ_H
 #define WQ_H
@@ -64,7 +73,6 @@ typedef enum wq_status {
   WQ_ERR_SHAPE = 2,     /* a size or divisibility rule is violated            */
   WQ_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned                   */
   WQ_ERR_DTYPE = 4,     /* unknown dtype code                                 */
-  WQ_ERR_WORKSPACE = 5, /* workspace missing or smaller than required         */
   WQ_ERR_HIP = 6        /* a HIP runtime call failed; see wq_last_hip_error() */
 } wq_status_t;
 
@@ -74,105 +82,106 @@ typedef enum wq_dtype {
 } wq_dtype_t;
 
 typedef enum wq_op {
-  WQ_OP_Q3 = 0,   /* wq_matvec_q3      */
-  WQ_OP_Q4G = 1,  /* wq_gemm_q4_group  */
-  WQ_OP_Q8G = 2   /* wq_gemm_q8_group  */
+  WQ_OP_Q3 = 0,   /* 3-bit matvec              */
+  WQ_OP_Q4G = 1,  /* 4-bit group-wise GEMM      */
+  WQ_OP_Q8G = 2   /* int8 group-wise GEMV/GEMM  */
 } wq_op_t;
 
-/* Workspace bytes needed by `op` at this shape (M rows of X, K, N, group
- * size G; M and G are ignored where they do not apply).  Returns 0 for an
- * invalid op or shape.  The size is a pure function of its arguments. */
-size_t wq_workspace_bytes(int op, int M, int K, int N, int G);
+/* Bytes of the packed weight for `op` at this shape (G is used by
+ * WQ_OP_Q4G only).  Returns 0 for an invalid op or shape.  Pure function. */
+size_t wq_packed_bytes(int op, int K, int N, int G);
+
+/* ---------------------------------------------------------------- 3-bit -- */
+
+/* Re-lay out a 3-bit weight.
+ * qweight [3K/32, N] int32: for column n and 32-row block b, the words
+ *   3b, 3b+1, 3b+2 form a 96-bit little-endian value whose bits 3i..3i+2 hold
+ *   the code q (0..7) of row 32b + i.
+ * packed: wq_packed_bytes(WQ_OP_Q3, K, N, 0) bytes, written.
+ * Rules: K % 32 == 0, K >= 32, N % 4 == 0, N >= 4. */
+int wq_prepack_q3(const int32_t* qweight, void* packed, int K, int N, void* stream);
 
 /* 3-bit matvec:  y[n] = sum_k x[k] * (scale[n] * q[k, n] - zero[n]).
- *
- * x       [K]           dtype (fp32 or fp16)
- * qweight [3K/32, N]    int32; for column n and 32-row block b, the words
- *                       3b, 3b+1, 3b+2 form a 96-bit little-endian value whose
- *                       bits 3i..3i+2 hold the code q (0..7) of row 32b + i.
- * scales  [N], zeros [N]  dtype; zero is the stored per-column offset
- *                       (w = scale*q - zero, the form of the page above).
- * y       [N]           dtype, written.
- * dtype   WQ_F32 or WQ_F16 (x, scales, zeros and y share it).  Accumulation
- *         is fp32 in both cases.
- * Rules:  K % 32 == 0, K >= 32, N % 4 == 0, N >= 4.
- */
-int wq_matvec_q3(const void* x, const int32_t* qweight, const void* scales,
-                 const void* zeros, void* y, int K, int N, int dtype,
-                 void* workspace, size_t workspace_bytes, void* stream);
+ * x [K], scales [N], zeros [N], y [N] (written) share `dtype` (WQ_F32 or
+ * WQ_F16); zero is the stored per-column offset (w = scale*q - zero).
+ * Accumulation is fp32 in both cases; the fp16 result is rounded once, to
+ * nearest even.  packed: from wq_prepack_q3 at the same (K, N).
+ * Rules: as wq_prepack_q3, and K <= 32768 (fp16) / 16384 (fp32). */
+int wq_matvec_q3(const void* x, const void* packed, const void* scales, const void* zeros,
+                 void* y, int K, int N, int dtype, void* stream);
+
+/* ----------------------------------------------------------------- int8 -- */
+
+/* Re-lay out a group-wise int8 weight qweight [K, N] (codes -127..127).
+ * packed: wq_packed_bytes(WQ_OP_Q8G, K, N, G) bytes, written.
+ * Rules: K % 32 == 0, N % 16 == 0. */
+int wq_prepack_q8(const int8_t* qweight, void* packed, int K, int N, void* stream);
 
 /* Group-wise int8 weight-only GEMM / GEMV:
  *   Y[m, n] = sum_k X[m, k] * (scale[k / G, n] * q[k, n]).
- *
- * X       [M, K]  fp16;   qweight [K, N] int8 (codes -127..127 symmetric);
- * scales  [K/G, N] fp32;  Y [M, N] fp16, written (fp32 accumulation, one
- *         round-to-nearest-even to fp16 at the end).
- * Rules:  M >= 1, K % 32 == 0, G % 32 == 0, K % G == 0, N % 16 == 0.
- */
-int wq_gemm_q8_group(const void* X, const int8_t* qweight, const float* scales,
-                     void* Y, int M, int K, int N, int G,
-                     void* workspace, size_t workspace_bytes, void* stream);
+ * X [M, K] fp16; packed: from wq_prepack_q8; scales [K/G, N] fp32;
+ * Y [M, N] fp16, written (fp32 accumulation, one round to nearest even).
+ * Rules: M >= 1, K % 32 == 0, N % 16 == 0, G % 32 == 0, K % G == 0. */
+int wq_gemm_q8_group(const void* X, const void* packed, const float* scales, void* Y, int M,
+                     int K, int N, int G, void* stream);
 
-/* Act-order preparation, step 1 (HOST arrays, runs on the CPU):
- * from g_idx[K] (row k belongs to group g_idx[k]) build perm[K], the K rows
- * listed group by group (rows of group 0 in increasing k, then group 1, ...).
- * g_idx == NULL means g_idx[k] = k / G (then perm is the identity).
+/* ---------------------------------------------------------------- 4-bit -- */
+
+/* Act-order preparation (HOST arrays, runs on the CPU): from g_idx[K] (row k
+ * belongs to group g_idx[k]) build perm[K], the rows listed group by group
+ * (rows of group 0 in increasing k, then group 1, ...), and its inverse
+ * invperm[K] (invperm[perm[i]] = i).  g_idx == NULL means g_idx[k] = k / G.
  * Returns WQ_ERR_SHAPE unless every group 0..K/G-1 owns exactly G rows (the
  * shape act-order quantisation produces). */
-int wq_q4_act_order_perm(const int32_t* g_idx, int K, int G, int32_t* perm);
+int wq_q4_act_order_perm(const int32_t* g_idx, int K, int G, int32_t* perm, int32_t* invperm);
 
-/* Act-order preparation, step 2 (device): reorder the rows of a 4-bit weight
- * into the order perm lists.  qweight_out row i (nibble i % 8 of word i / 8)
- * receives the code of original row perm[i].  qweight and qweight_out are
- * [K/8, N] int32 in the 4-bit layout of wq_gemm_q4_group and must not
- * overlap.  Rules: K % 8 == 0, N >= 1. */
-int wq_q4_prepack(const int32_t* qweight, const int32_t* perm, int32_t* qweight_out,
-                  int K, int N, void* stream);
+/* Re-lay out a 4-bit weight qweight [K/8, N] int32 (row 8r + j in nibble j,
+ * bits 4j..4j+3, of word r, stored as u = q + 8), its rows taken in the
+ * order perm lists (device array [K], or NULL for the stored order).
+ * packed: wq_packed_bytes(WQ_OP_Q4G, K, N, G) bytes, written.
+ * Rules: K % G == 0, G a power of two >= 32, N % 4 == 0. */
+int wq_prepack_q4(const int32_t* qweight, const int32_t* perm, void* packed, int K, int N, int G,
+                  void* stream);
 
 /* Group-wise 4-bit GEMM (symmetric, optional act-order):
- *   Y[m, n] = sum_i X[m, perm[i]] * scale[i / G, n] * q'[i, n]
- * where q' is the prepacked weight (rows in perm order, so rows
- * [gG, gG + G) all belong to group g).  With perm == NULL the weight is used
- * as stored and row k belongs to group k / G.
- *
- * X       [M, K]   fp16;
- * qweight [K/8, N] int32, row 8r + j in nibble j (bits 4j..4j+3) of word r,
- *                  stored as u = q + 8 (q in -8..7);
- * scales  [K/G, N] fp16;  perm [K] int32 device array or NULL;
- * Y       [M, N]   fp16, written (fp32 accumulation).
- * Rules:  M >= 1, K % G == 0, G % 32 == 0, N % 4 == 0.
- */
-int wq_gemm_q4_group(const void* X, const int32_t* qweight, const void* scales,
-                     const int32_t* perm, void* Y, int M, int K, int N, int G,
-                     void* workspace, size_t workspace_bytes, void* stream);
+ *   Y[m, n] = sum_k X[m, k] * scale[g_idx[k], n] * q[k, n]
+ * computed from the packed weight (rows in perm order) as
+ *   sum_i X[m, perm[i]] * scale[i / G, n] * q[perm[i], n].
+ * X [M, K] fp16; scales [K/G, N] fp16; invperm: device [K] from
+ * wq_q4_act_order_perm (NULL when the weight was packed with perm == NULL);
+ * Y [M, N] fp16, written (fp32 accumulation).
+ * Rules: as wq_prepack_q4, M >= 1. */
+int wq_gemm_q4_group(const void* X, const void* packed, const void* scales,
+                     const int32_t* invperm, void* Y, int M, int K, int N, int G, void* stream);
+
+/* ----------------------------------------------------------------- W8A8 -- */
 
 /* W8A8 dynamic-quantisation GEMM:
  *   a[m] = max_k |X[m, k]|;  Sx[m] = a[m] / 127 (fp32, round to nearest);
  *   Xq[m, k] = clamp(rint(X[m, k] / Sx[m]), -127, 127)  (0 when a[m] == 0);
  *   acc[m, n] = sum_k Xq[m, k] * Wq[n, k]   (exact int32);
  *   Y[m, n] = bf16_rne( (Sx[m] * float(acc)) * Sw[n] )  (two fp32 multiplies).
- *
- * X   [M, K] fp32;  Wq [N, K] int8 (quantised offline, K contiguous);
- * Sw  [N] fp32 per-output-channel scale;  Y [M, N] bf16 (uint16 bits), written;
- * Xq  [M, K] int8 and Sx [M] fp32: written (the run-time quantised X);
+ * X [M, K] fp32;  Wq [N, K] int8 (quantised offline, K contiguous);
+ * Sw [N] fp32 per-output-channel scale;  Y [M, N] bf16 (uint16 bits), written;
+ * Xq [M, K] int8 and Sx [M] fp32: written (the run-time quantised X);
  * acc_out [M, N] int32: written when non-NULL (for checking), else the
- *         accumulator never leaves the chip.
+ *   accumulator never leaves the chip.
  * Two launches on `stream` (quantiser, then GEMM).
- * Rules:  M >= 1, K % 64 == 0, N % 16 == 0, and K * 127 * 127 < 2^31.
- */
-int wq_gemm_w8a8(const float* X, const int8_t* Wq, const float* Sw, void* Y,
-                 int8_t* Xq, float* Sx, int32_t* acc_out, int M, int K, int N,
-                 void* stream);
+ * Rules: M >= 1, K % 64 == 0, N % 16 == 0, and K * 127 * 127 < 2^31. */
+int wq_gemm_w8a8(const float* X, const int8_t* Wq, const float* Sw, void* Y, int8_t* Xq,
+                 float* Sx, int32_t* acc_out, int M, int K, int N, void* stream);
 
-/* Bit-exact unpack checks: write the signed codes as int8 [K, N], through the
- * same device extraction routines the fused kernels use.
- * wq_unpack_q3: codes 0..7 from the 3-bit layout.  Rules: K % 32 == 0, N % 4 == 0.
- * wq_unpack_q4: codes q = u - 8 of the 4-bit layout; when perm is non-NULL the
- *   input is a prepacked weight and row i is written to codes row perm[i]
- *   (undoing the reorder).  Rules: K % 8 == 0, N % 4 == 0. */
-int wq_unpack_q3(const int32_t* qweight, int8_t* codes, int K, int N, void* stream);
-int wq_unpack_q4(const int32_t* qweight, const int32_t* perm, int8_t* codes,
-                 int K, int N, void* stream);
+/* ------------------------------------------------------ bit-exact checks -- */
+
+/* Write the signed codes a packed weight holds as int8 [K, N], through the
+ * same device extraction routines the products use.
+ * wq_unpack_q3: codes 0..7.  wq_unpack_q8: codes -127..127.
+ * wq_unpack_q4: codes q = u - 8, in the original row order (perm as given to
+ *   wq_prepack_q4, or NULL). */
+int wq_unpack_q3(const void* packed, int8_t* codes, int K, int N, void* stream);
+int wq_unpack_q8(const void* packed, int8_t* codes, int K, int N, void* stream);
+int wq_unpack_q4(const void* packed, const int32_t* perm, int8_t* codes, int K, int N, int G,
+                 void* stream);
 
 /* Static text for a status code. */
 const char* wq_status_str(int status);

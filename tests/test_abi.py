@@ -33,56 +33,56 @@ def test_status_strings(L):
     assert L.wq_last_hip_error() == 0
 
 
-def test_workspace_bytes_pure_and_valid(L):
-    a = L.wq_workspace_bytes(wq.WQ_OP_Q8G, 1, 4096, 4096, 128)
-    assert a > 0 and a == L.wq_workspace_bytes(wq.WQ_OP_Q8G, 1, 4096, 4096, 128)
-    assert L.wq_workspace_bytes(wq.WQ_OP_Q3, 1, 4096, 11008, 0) > 0
-    assert L.wq_workspace_bytes(wq.WQ_OP_Q4G, 8, 4096, 11008, 128) > 0
+def test_packed_bytes_pure_and_valid(L):
+    a = L.wq_packed_bytes(wq.WQ_OP_Q8G, 4096, 4096, 128)
+    assert a == 4096 * 4096 and a == L.wq_packed_bytes(wq.WQ_OP_Q8G, 4096, 4096, 0)
+    # the configured shapes re-lay out without padding
+    assert L.wq_packed_bytes(wq.WQ_OP_Q3, 4096, 11008, 0) == 4096 // 32 * 3 * 11008 * 4
+    assert L.wq_packed_bytes(wq.WQ_OP_Q3, 11008, 4096, 0) >= 11008 // 32 * 3 * 4096 * 4
+    assert L.wq_packed_bytes(wq.WQ_OP_Q4G, 4096, 11008, 128) == 4096 // 8 * 11008 * 4
     # invalid shapes / ops -> 0
-    assert L.wq_workspace_bytes(wq.WQ_OP_Q8G, 1, 4096, 4095, 128) == 0
-    assert L.wq_workspace_bytes(wq.WQ_OP_Q3, 1, 100, 64, 0) == 0
-    assert L.wq_workspace_bytes(7, 1, 4096, 4096, 128) == 0
+    assert L.wq_packed_bytes(wq.WQ_OP_Q8G, 4096, 4095, 128) == 0
+    assert L.wq_packed_bytes(wq.WQ_OP_Q3, 100, 64, 0) == 0
+    assert L.wq_packed_bytes(wq.WQ_OP_Q4G, 4096, 11008, 96) == 0   # G not a power of two
+    assert L.wq_packed_bytes(7, 4096, 4096, 128) == 0
 
 
 def test_q3_validation(L):
     f = L.wq_matvec_q3
-    ws = 1 << 20
-    assert f(None, P, P, P, P, 64, 64, 0, P, ws, None) == wq.WQ_ERR_NULL
-    assert f(P, P, P, P, P, 64, 64, 5, P, ws, None) == wq.WQ_ERR_DTYPE
-    assert f(P, P, P, P, P, 48, 64, 0, P, ws, None) == wq.WQ_ERR_SHAPE   # K % 32
-    assert f(P, P, P, P, P, 64, 62, 0, P, ws, None) == wq.WQ_ERR_SHAPE   # N % 4
-    assert f(P_MIS, P, P, P, P, 64, 64, 0, P, ws, None) == wq.WQ_ERR_ALIGN
-    assert f(P, P, P, P, P, 64, 64, 1, None, 0, None) in (wq.WQ_ERR_WORKSPACE,)
-    need = L.wq_workspace_bytes(wq.WQ_OP_Q3, 1, 4096, 4096, 0)
-    assert f(P, P, P, P, P, 4096, 4096, 1, P, need - 1, None) == wq.WQ_ERR_WORKSPACE
+    assert f(None, P, P, P, P, 64, 64, 0, None) == wq.WQ_ERR_NULL
+    assert f(P, P, P, P, P, 64, 64, 5, None) == wq.WQ_ERR_DTYPE
+    assert f(P, P, P, P, P, 48, 64, 0, None) == wq.WQ_ERR_SHAPE   # K % 32
+    assert f(P, P, P, P, P, 64, 62, 0, None) == wq.WQ_ERR_SHAPE   # N % 4
+    assert f(P, P, P, P, P, 32768 + 32, 64, 1, None) == wq.WQ_ERR_SHAPE  # LDS bound
+    assert f(P_MIS, P, P, P, P, 64, 64, 0, None) == wq.WQ_ERR_ALIGN
+    assert f(P, P_MIS, P, P, P, 64, 64, 0, None) == wq.WQ_ERR_ALIGN
+    assert L.wq_prepack_q3(P, None, 64, 64, None) == wq.WQ_ERR_NULL
+    assert L.wq_prepack_q3(P, P, 64, 66, None) == wq.WQ_ERR_SHAPE
 
 
 def test_q8_validation(L):
     f = L.wq_gemm_q8_group
-    ws = 1 << 24
-    assert f(P, None, P, P, 1, 4096, 4096, 128, P, ws, None) == wq.WQ_ERR_NULL
-    assert f(P, P, P, P, 0, 4096, 4096, 128, P, ws, None) == wq.WQ_ERR_SHAPE    # M
-    assert f(P, P, P, P, 1, 4096, 4104, 128, P, ws, None) == wq.WQ_ERR_SHAPE    # N % 16
-    assert f(P, P, P, P, 1, 4096, 4096, 96, P, ws, None) == wq.WQ_ERR_SHAPE     # K % G
-    assert f(P, P, P, P, 1, 4096, 4096, 48, P, ws, None) == wq.WQ_ERR_SHAPE     # G % 32
-    assert f(P, P_MIS, P, P, 1, 4096, 4096, 128, P, ws, None) == wq.WQ_ERR_ALIGN
-    need = L.wq_workspace_bytes(wq.WQ_OP_Q8G, 1, 4096, 4096, 128)
-    assert f(P, P, P, P, 1, 4096, 4096, 128, P, need - 16, None) == wq.WQ_ERR_WORKSPACE
-    assert f(P, P, P, P, 1, 4096, 4096, 128, P_MIS, need, None) == wq.WQ_ERR_ALIGN
+    assert f(P, None, P, P, 1, 4096, 4096, 128, None) == wq.WQ_ERR_NULL
+    assert f(P, P, P, P, 0, 4096, 4096, 128, None) == wq.WQ_ERR_SHAPE    # M
+    assert f(P, P, P, P, 1, 4096, 4104, 128, None) == wq.WQ_ERR_SHAPE    # N % 16
+    assert f(P, P, P, P, 1, 4096, 4096, 96, None) == wq.WQ_ERR_SHAPE     # K % G
+    assert f(P, P, P, P, 1, 4096, 4096, 48, None) == wq.WQ_ERR_SHAPE     # G % 32
+    assert f(P, P_MIS, P, P, 1, 4096, 4096, 128, None) == wq.WQ_ERR_ALIGN
+    assert L.wq_prepack_q8(P, P, 4096, 4100, None) == wq.WQ_ERR_SHAPE
+    assert L.wq_prepack_q8(P_MIS, P, 4096, 4096, None) == wq.WQ_ERR_ALIGN
 
 
 def test_q4_validation(L):
     f = L.wq_gemm_q4_group
-    ws = 1 << 24
-    assert f(P, P, None, None, P, 1, 4096, 11008, 128, P, ws, None) == wq.WQ_ERR_NULL
-    assert f(P, P, P, None, P, 1, 4096, 11006, 128, P, ws, None) == wq.WQ_ERR_SHAPE
-    assert f(P, P, P, None, P, 1, 4000, 11008, 128, P, ws, None) == wq.WQ_ERR_SHAPE
-    assert f(P, P, P, None, P, 1, 4096, 11008, 16, P, ws, None) == wq.WQ_ERR_SHAPE
-    assert f(P, P, P, None, P, 1, 4096, 11008, 128, None, 0, None) == wq.WQ_ERR_WORKSPACE
-    g = L.wq_q4_prepack
-    assert g(P, P, P, 12, 16, None) == wq.WQ_ERR_SHAPE
-    assert g(P, P, P, 64, 16, None) == wq.WQ_ERR_SHAPE   # in == out (overlap)
-    assert g(P, None, ctypes.c_void_p(1 << 30), 64, 16, None) == wq.WQ_ERR_NULL
+    assert f(P, P, None, None, P, 1, 4096, 11008, 128, None) == wq.WQ_ERR_NULL
+    assert f(P, P, P, None, P, 1, 4096, 11006, 128, None) == wq.WQ_ERR_SHAPE
+    assert f(P, P, P, None, P, 1, 4000, 11008, 128, None) == wq.WQ_ERR_SHAPE
+    assert f(P, P, P, None, P, 1, 4096, 11008, 16, None) == wq.WQ_ERR_SHAPE
+    assert f(P, P, P, None, P, 0, 4096, 11008, 128, None) == wq.WQ_ERR_SHAPE
+    assert f(P, P, P, P_MIS, P, 1, 4096, 11008, 128, None) == wq.WQ_ERR_ALIGN
+    g = L.wq_prepack_q4
+    assert g(P, None, P, 12, 16, 32, None) == wq.WQ_ERR_SHAPE
+    assert g(P, None, None, 64, 16, 32, None) == wq.WQ_ERR_NULL
 
 
 def test_w8a8_validation(L):
@@ -97,26 +97,28 @@ def test_w8a8_validation(L):
 
 def test_unpack_validation(L):
     assert L.wq_unpack_q3(P, P, 33, 64, None) == wq.WQ_ERR_SHAPE
-    assert L.wq_unpack_q4(P, None, P, 12, 64, None) == wq.WQ_ERR_SHAPE
-    assert L.wq_unpack_q4(None, None, P, 64, 64, None) == wq.WQ_ERR_NULL
+    assert L.wq_unpack_q8(P, P, 64, 60, None) == wq.WQ_ERR_SHAPE
+    assert L.wq_unpack_q4(P, None, P, 12, 64, 32, None) == wq.WQ_ERR_SHAPE
+    assert L.wq_unpack_q4(None, None, P, 64, 64, 32, None) == wq.WQ_ERR_NULL
 
 
 def test_act_order_perm_host():
     rng = np.random.default_rng(5)
     K, G = 512, 128
     g_idx = rng.permutation(np.repeat(np.arange(K // G), G)).astype(np.int32)
-    perm = wq.q4_act_order_perm(g_idx, K, G)
+    perm, inv = wq.q4_act_order_perm(g_idx, K, G)
     assert sorted(perm.tolist()) == list(range(K))
+    assert np.array_equal(inv[perm], np.arange(K))
     # rows [gG, gG+G) of the new order all belong to group g, in increasing k
     for g in range(K // G):
         seg = perm[g * G:(g + 1) * G]
         assert np.all(g_idx[seg] == g)
         assert np.all(np.diff(seg) > 0)
-    assert np.array_equal(wq.q4_act_order_perm(None, K, G), np.arange(K))
+    p0, i0 = wq.q4_act_order_perm(None, K, G)
+    assert np.array_equal(p0, np.arange(K)) and np.array_equal(i0, np.arange(K))
     bad = g_idx.copy()
-    bad[0], bad[1] = 0, 0
-    if np.bincount(bad, minlength=K // G).max() != G or np.bincount(bad).min() != G:
-        with pytest.raises(wq.WQError):
-            wq.q4_act_order_perm(bad, K, G)
+    bad[np.nonzero(bad == 1)[0][0]] = 0      # group 0 gets G+1 rows, group 1 G-1
+    with pytest.raises(wq.WQError):
+        wq.q4_act_order_perm(bad, K, G)
     with pytest.raises(wq.WQError):
         wq.q4_act_order_perm(np.full(K, 9, np.int32), K, G)

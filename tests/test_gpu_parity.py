@@ -62,7 +62,7 @@ def assert_tol(y, y_exact, what=""):
 ])
 def test_q8_group_vs_oracle(wq, M, K, N, G):
     d = synth.gen_q8_group(M, K, N, G, seed=1100 if (M, K, N) == (1, 4096, 4096) else 7 + M + K + N)
-    Y = wq.gemm_q8_group(cu(d["X"]), cu(d["q"]), cu(d["scales"]), G)
+    Y = wq.gemm_q8_group(cu(d["X"]), wq.prepack_q8(cu(d["q"])), cu(d["scales"]), G)
     assert_tol(host(Y), oracle.gemm_q8_group(d["X"], d["q"], d["scales"], G), f"q8 {M}x{K}x{N} G{G}")
 
 
@@ -73,7 +73,7 @@ def test_q8_integer_exact(wq):
     q = rng.integers(-127, 128, size=(K, N)).astype(np.int8)
     X = rng.integers(-2, 3, size=(M, K)).astype(np.float16)
     s = np.ones((K // G, N), np.float32)
-    Y = host(wq.gemm_q8_group(cu(X), cu(q), cu(s), G))
+    Y = host(wq.gemm_q8_group(cu(X), wq.prepack_q8(cu(q)), cu(s), G))
     ref = oracle.gemm_q8_group(X, q, s, G).astype(np.float16).astype(np.float64)
     assert np.array_equal(Y, ref)
 
@@ -86,41 +86,50 @@ def test_q8_output_rounding_ties(wq):
     q[0, :], x[0] = 127, 16            # 2032 in every column
     q[2, 0], q[2, 1], x[2] = 17, 19, 1  # column 0: 2049, column 1: 2051
     s = np.ones((1, N), np.float32)
-    y = host(wq.gemm_q8_group(cu(x), cu(q), cu(s), G))
+    y = host(wq.gemm_q8_group(cu(x), wq.prepack_q8(cu(q)), cu(s), G))
     assert y[0] == 2048 and y[1] == 2052
 
 
 def test_q8_one_hot_rows(wq):
     K, N, G = 512, 272, 128
     d = synth.gen_q8_group(1, K, N, G, seed=42)
+    packed = wq.prepack_q8(cu(d["q"]))
     for k in (0, 1, 127, 128, 300, 511):
         x = np.zeros(K, np.float16)
         x[k] = 1
-        y = host(wq.gemm_q8_group(cu(x), cu(d["q"]), cu(d["scales"]), G))
+        y = host(wq.gemm_q8_group(cu(x), packed, cu(d["scales"]), G))
         ref = (d["scales"][k // G].astype(np.float64) * d["q"][k]).astype(np.float16).astype(np.float64)
         assert np.array_equal(y, ref), k
 
 
 def test_q8_deterministic_and_scale_exact(wq):
     d = synth.gen_q8_group(1, 4096, 4096, 128, seed=1100)
-    X, q, s = cu(d["X"]), cu(d["q"]), cu(d["scales"])
+    X, q, s = cu(d["X"]), wq.prepack_q8(cu(d["q"])), cu(d["scales"])
     y0 = wq.gemm_q8_group(X, q, s, 128).clone()
     for _ in range(20):
         assert torch.equal(wq.gemm_q8_group(X, q, s, 128), y0)
+    # Doubling x doubles every fp32 partial sum exactly; the final fp16
+    # rounding commutes with the doubling wherever y is a normal fp16 value.
     y2 = wq.gemm_q8_group(X * 2, q, s, 128)
-    assert torch.equal(y2, y0 * 2)
+    normal = (y0.abs() >= 2.0 ** -14) & (y0.abs() < 2.0 ** 14)
+    assert int(normal.sum()) > 4000
+    assert torch.equal(y2[normal], (y0 * 2)[normal])
 
 
-@pytest.mark.parametrize("unit", ["8", "16", "32"])
-def test_q8_split_plans_agree(wq, unit):
-    d = synth.gen_q8_group(1, 4096, 4096, 128, seed=1100)
-    ref = oracle.gemm_q8_group(d["X"], d["q"], d["scales"], 128)
-    os.environ["WQ_SPLITK_UNIT"] = unit
-    try:
-        Y = host(wq.gemm_q8_group(cu(d["X"]), cu(d["q"]), cu(d["scales"]), 128))
-    finally:
-        del os.environ["WQ_SPLITK_UNIT"]
-    assert_tol(Y, ref, f"q8 unit {unit}")
+@pytest.mark.parametrize("K,N", [(4096, 4096), (4096, 11008), (11008, 4096), (1024, 8192), (96, 48)])
+def test_unpack_q8_bit_exact(wq, K, N):
+    d = synth.gen_q8_group(1, K, N, 32, seed=9 + K + N)
+    codes = wq.unpack_q8(wq.prepack_q8(cu(d["q"])), K, N)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy(), d["q"])
+
+
+def test_q8_wide_panels_and_long_k(wq):
+    # N >= 8192 switches to 32-column panels; K = 11008 gives 48-row slot spans.
+    for (M, K, N) in ((1, 4096, 11008), (2, 11008, 4096), (3, 1024, 8192)):
+        d = synth.gen_q8_group(M, K, N, 128, seed=M + K)
+        Y = wq.gemm_q8_group(cu(d["X"]), wq.prepack_q8(cu(d["q"])), cu(d["scales"]), 128)
+        assert_tol(host(Y), oracle.gemm_q8_group(d["X"], d["q"], d["scales"], 128), f"q8 {M}x{K}x{N}")
 
 
 # ================================================================= 3-bit ==
@@ -128,7 +137,7 @@ def test_q8_split_plans_agree(wq, unit):
 @pytest.mark.parametrize("K,N", [(1024, 1024), (4096, 4096), (4096, 11008), (11008, 4096), (96, 20)])
 def test_unpack_q3_bit_exact(wq, K, N):
     d = synth.gen_q3(K, N, seed=5 + K + N, dtype="f16")
-    codes = wq.unpack_q3(cu(d["qweight"]), K)
+    codes = wq.unpack_q3(wq.prepack_q3(cu(d["qweight"]), K), K, N)
     torch.cuda.synchronize()
     assert np.array_equal(codes.cpu().numpy().astype(np.int64), oracle.unpack_q3(d["qweight"]))
 
@@ -140,7 +149,7 @@ def test_unpack_q3_bit_exact(wq, K, N):
 ])
 def test_q3_vs_oracle(wq, K, N, dt, seed):
     d = synth.gen_q3(K, N, seed=seed, dtype=dt)
-    y = wq.matvec_q3(cu(d["x"]), cu(d["qweight"]), cu(d["scales"]), cu(d["zeros"]))
+    y = wq.matvec_q3(cu(d["x"]), wq.prepack_q3(cu(d["qweight"]), K), cu(d["scales"]), cu(d["zeros"]))
     ref = oracle.matvec_q3(d["x"], d["qweight"], d["scales"], d["zeros"])
     assert_tol(host(y), ref, f"q3 {dt} {K}x{N}")
 
@@ -154,21 +163,23 @@ def test_q3_integer_exact_and_zero_codes(wq, dt):
     z = rng.integers(0, 8, size=N).astype(npdt)
     x = rng.integers(-3, 4, size=K).astype(npdt)
     s = np.ones(N, npdt)
-    y = host(wq.matvec_q3(cu(x), cu(synth.pack_q3(codes)), cu(s), cu(z)))
+    y = host(wq.matvec_q3(cu(x), wq.prepack_q3(cu(synth.pack_q3(codes)), K), cu(s), cu(z)))
     ref = oracle.matvec_q3(x, synth.pack_q3(codes), s, z).astype(npdt).astype(np.float64)
     assert np.array_equal(y, ref)
     # all-zero codes: y = -zero * sum(x)
-    y0 = host(wq.matvec_q3(cu(x), cu(synth.pack_q3(np.zeros((K, N), np.int64))), cu(s), cu(z)))
+    zero_w = wq.prepack_q3(cu(synth.pack_q3(np.zeros((K, N), np.int64))), K)
+    y0 = host(wq.matvec_q3(cu(x), zero_w, cu(s), cu(z)))
     assert np.array_equal(y0, (-z.astype(np.float64) * x.astype(np.float64).sum()).astype(npdt).astype(np.float64))
 
 
 def test_q3_one_hot_rows(wq):
     K, N = 256, 260
     d = synth.gen_q3(K, N, seed=52, dtype="f32")
+    packed = wq.prepack_q3(cu(d["qweight"]), K)
     for k in (0, 6, 10, 21, 31, 32, 100, 255):
         x = np.zeros(K, np.float32)
         x[k] = 1
-        y = host(wq.matvec_q3(cu(x), cu(d["qweight"]), cu(d["scales"]), cu(d["zeros"])))
+        y = host(wq.matvec_q3(cu(x), packed, cu(d["scales"]), cu(d["zeros"])))
         ref = d["scales"].astype(np.float64) * d["codes"][k] - d["zeros"].astype(np.float64)
         assert np.allclose(y, ref, rtol=1e-6, atol=1e-7), k
 
@@ -179,23 +190,18 @@ def test_q3_one_hot_rows(wq):
 def test_unpack_q4_bit_exact(wq, act):
     K, N, G = 4096, 11008, 128
     d = synth.gen_q4_group(1, K, N, G, seed=1300, act_order=act)
-    qw = cu(d["qweight"])
-    ref = oracle.unpack_q4(d["qweight"])
-    codes = wq.unpack_q4(qw, K)
+    packed, perm, _ = wq.prepare_q4(cu(d["qweight"]), d["g_idx"] if act else None, G)
+    codes = wq.unpack_q4(packed, K, N, G, perm)
     torch.cuda.synchronize()
-    assert np.array_equal(codes.cpu().numpy().astype(np.int64), ref)
-    packed, perm = wq.prepare_q4(qw, d["g_idx"] if act else None, G)
-    codes2 = wq.unpack_q4(packed, K, perm)
-    torch.cuda.synchronize()
-    assert np.array_equal(codes2.cpu().numpy().astype(np.int64), ref)
+    assert np.array_equal(codes.cpu().numpy().astype(np.int64), oracle.unpack_q4(d["qweight"]))
 
 
 @pytest.mark.parametrize("M", [1, 2, 4, 8])
 def test_q4_act_order_headline(wq, M):
     K, N, G = 4096, 11008, 128
     d = synth.gen_q4_group(M, K, N, G, seed=1300, act_order=True)
-    packed, perm = wq.prepare_q4(cu(d["qweight"]), d["g_idx"], G)
-    Y = wq.gemm_q4_group(cu(d["X"]), packed, cu(d["scales"]), perm, G)
+    packed, _, inv = wq.prepare_q4(cu(d["qweight"]), d["g_idx"], G)
+    Y = wq.gemm_q4_group(cu(d["X"]), packed, cu(d["scales"]), inv, G)
     ref = oracle.gemm_q4_group(d["X"], d["qweight"], d["scales"], d["g_idx"], G)
     assert_tol(host(Y), ref, f"q4 M{M}")
 
@@ -203,26 +209,24 @@ def test_q4_act_order_headline(wq, M):
 @pytest.mark.parametrize("M,K,N,G,act", [
     (1, 128, 4, 32, True), (3, 384, 260, 64, True), (5, 1024, 1028, 128, False),
     (9, 512, 516, 128, True), (2, 2048, 256, 32, False), (16, 256, 64, 128, True),
+    (1, 4096, 4096, 128, True), (4, 11008, 4096, 128, True), (1, 544, 1024, 32, True),
 ])
 def test_q4_small_ragged(wq, M, K, N, G, act):
     d = synth.gen_q4_group(M, K, N, G, seed=60 + M + K, act_order=act)
-    packed, perm = wq.prepare_q4(cu(d["qweight"]), d["g_idx"] if act else None, G)
-    Y = wq.gemm_q4_group(cu(d["X"]), packed, cu(d["scales"]), perm, G)
+    packed, _, inv = wq.prepare_q4(cu(d["qweight"]), d["g_idx"] if act else None, G)
+    Y = wq.gemm_q4_group(cu(d["X"]), packed, cu(d["scales"]), inv, G)
     ref = oracle.gemm_q4_group(d["X"], d["qweight"], d["scales"], d["g_idx"], G)
     assert_tol(host(Y), ref, f"q4 {M}x{K}x{N} G{G} act={act}")
-    if not act:  # without act-order the stored weight is used as is
-        Y2 = wq.gemm_q4_group(cu(d["X"]), cu(d["qweight"]), cu(d["scales"]), None, G)
-        assert torch.equal(Y, Y2)
 
 
 def test_q4_one_hot_act_order(wq):
     K, N, G = 512, 260, 128
     d = synth.gen_q4_group(1, K, N, G, seed=61, act_order=True)
-    packed, perm = wq.prepare_q4(cu(d["qweight"]), d["g_idx"], G)
+    packed, _, inv = wq.prepare_q4(cu(d["qweight"]), d["g_idx"], G)
     for k in (0, 1, 5, 200, 511):
         x = np.zeros(K, np.float16)
         x[k] = 1
-        y = host(wq.gemm_q4_group(cu(x), packed, cu(d["scales"]), perm, G))
+        y = host(wq.gemm_q4_group(cu(x), packed, cu(d["scales"]), inv, G))
         ref = (d["scales"][d["g_idx"][k]].astype(np.float64) * d["codes"][k]).astype(np.float16)
         assert np.array_equal(y, ref.astype(np.float64)), k
 
@@ -235,8 +239,8 @@ def test_q4_integer_exact(wq):
     s = np.ones((K // G, N), np.float16)
     X = rng.integers(-3, 4, size=(M, K)).astype(np.float16)
     qw = synth.pack_q4(q + 8)
-    packed, perm = wq.prepare_q4(cu(qw), g_idx, G)
-    Y = host(wq.gemm_q4_group(cu(X), packed, cu(s), perm, G))
+    packed, _, inv = wq.prepare_q4(cu(qw), g_idx, G)
+    Y = host(wq.gemm_q4_group(cu(X), packed, cu(s), inv, G))
     ref = oracle.gemm_q4_group(X, qw, s, g_idx, G).astype(np.float16).astype(np.float64)
     assert np.array_equal(Y, ref)
 

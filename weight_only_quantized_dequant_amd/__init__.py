@@ -4,15 +4,16 @@ Argument marshalling only.  Every step of every product runs in the HIP
 kernels of libwq.so; torch supplies device memory and the current stream.
 There is no fallback: without the built library every call raises.
 
-Entry points (same names as the C ABI in ``include/wq.h``):
+Entry points (same names as the C ABI in ``include/wq.h``).  The weight-only
+products read a packed copy of the weight made once by ``prepack_*``:
 
-* ``matvec_q3(x, qweight, scales, zeros)``            -> y
-* ``gemm_q8_group(X, qweight, scales, group_size)``   -> Y
-* ``q4_act_order_perm(g_idx, K, group_size)``         -> perm (host, int32)
-* ``q4_prepack(qweight, perm)``                       -> prepacked qweight
-* ``gemm_q4_group(X, qweight, scales, perm, group_size)`` -> Y
-* ``gemm_w8a8(X, Wq, Sw, want_acc=False)``            -> (Y bf16, Xq, Sx, acc|None)
-* ``unpack_q3(qweight, K)`` / ``unpack_q4(qweight, K, perm=None)`` -> int8 codes
+* ``prepack_q3(qweight, K)`` / ``matvec_q3(x, packed, scales, zeros)``       -> y
+* ``prepack_q8(qweight)`` / ``gemm_q8_group(X, packed, scales, group_size)``  -> Y
+* ``q4_act_order_perm(g_idx, K, G)`` -> (perm, invperm) host int32 arrays
+* ``prepack_q4(qweight, perm, G)`` / ``gemm_q4_group(X, packed, scales, invperm, G)`` -> Y
+  (``prepare_q4(qweight, g_idx, G)`` does the act-order preparation in one go)
+* ``gemm_w8a8(X, Wq, Sw, want_acc=False)``  -> (Y bf16, Xq, Sx, acc | None)
+* ``unpack_q3`` / ``unpack_q8`` / ``unpack_q4``: codes held by a packed weight
 """
 from __future__ import annotations
 
@@ -27,21 +28,24 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libwq.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "wq.h")
 
-WQ_OK, WQ_ERR_NULL, WQ_ERR_SHAPE, WQ_ERR_ALIGN, WQ_ERR_DTYPE, WQ_ERR_WORKSPACE, WQ_ERR_HIP = range(7)
+WQ_OK, WQ_ERR_NULL, WQ_ERR_SHAPE, WQ_ERR_ALIGN, WQ_ERR_DTYPE, WQ_ERR_HIP = 0, 1, 2, 3, 4, 6
 WQ_F32, WQ_F16 = 0, 1
 WQ_OP_Q3, WQ_OP_Q4G, WQ_OP_Q8G = 0, 1, 2
 
 _vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 _SIGNATURES = {
-    "wq_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
-    "wq_matvec_q3": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp]),
-    "wq_gemm_q8_group": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]),
-    "wq_q4_act_order_perm": (_i, [_vp, _i, _i, _vp]),
-    "wq_q4_prepack": (_i, [_vp, _vp, _vp, _i, _i, _vp]),
-    "wq_gemm_q4_group": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "wq_packed_bytes": (_sz, [_i, _i, _i, _i]),
+    "wq_prepack_q3": (_i, [_vp, _vp, _i, _i, _vp]),
+    "wq_matvec_q3": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
+    "wq_prepack_q8": (_i, [_vp, _vp, _i, _i, _vp]),
+    "wq_gemm_q8_group": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
+    "wq_q4_act_order_perm": (_i, [_vp, _i, _i, _vp, _vp]),
+    "wq_prepack_q4": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
+    "wq_gemm_q4_group": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "wq_gemm_w8a8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
     "wq_unpack_q3": (_i, [_vp, _vp, _i, _i, _vp]),
-    "wq_unpack_q4": (_i, [_vp, _vp, _vp, _i, _i, _vp]),
+    "wq_unpack_q8": (_i, [_vp, _vp, _i, _i, _vp]),
+    "wq_unpack_q4": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
     "wq_status_str": (ctypes.c_char_p, [_i]),
     "wq_last_hip_error": (_i, []),
 }
@@ -112,131 +116,177 @@ def _need(t: torch.Tensor, name: str, dtype, shape, device=None):
         raise ValueError(f"{name} must be contiguous")
 
 
-# Per-(device, stream) workspaces: zero-filled once, left zeroed by every call.
-_workspaces: dict = {}
+def packed_bytes(op: int, K: int, N: int, G: int = 0) -> int:
+    n = int(lib().wq_packed_bytes(op, K, N, G))
+    if n == 0:
+        _check("wq_packed_bytes", WQ_ERR_SHAPE)
+    return n
 
 
-def workspace(op: int, M: int, K: int, N: int, G: int, device: torch.device) -> torch.Tensor:
-    need = int(lib().wq_workspace_bytes(op, M, K, N, G))
-    if need == 0:
-        _check("wq_workspace_bytes", WQ_ERR_SHAPE)
-    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
-    ws = _workspaces.get(key)
-    if ws is None or ws.numel() < need:
-        ws = torch.zeros(max(need, 1 << 16), dtype=torch.uint8, device=device)
-        _workspaces[key] = ws
-    return ws
+def _packed(op, K, N, G, device):
+    return torch.empty(packed_bytes(op, K, N, G), dtype=torch.uint8, device=device)
 
 
-def workspace_bytes(op: int, M: int, K: int, N: int, G: int) -> int:
-    return int(lib().wq_workspace_bytes(op, M, K, N, G))
+def _need_packed(t, op, K, N, G, device):
+    _need(t, "packed", torch.uint8, (packed_bytes(op, K, N, G),), device)
 
 
 # ----------------------------------------------------------------- 3-bit --
 
-def matvec_q3(x, qweight, scales, zeros, y=None):
-    """y = x . (scale * q - zero) for a 3-bit packed weight; fp32 or fp16."""
-    K = x.shape[0]
+def prepack_q3(qweight, K: int):
+    """Re-lay out a 3-bit weight [3K/32, N] int32 for matvec_q3."""
     N = qweight.shape[1]
+    dev = qweight.device
+    _need(qweight, "qweight", torch.int32, (3 * K // 32, N), dev)
+    out = _packed(WQ_OP_Q3, K, N, 0, dev)
+    _check("wq_prepack_q3", lib().wq_prepack_q3(_ptr(qweight), _ptr(out), K, N, _stream(dev)))
+    return out
+
+
+def matvec_q3(x, packed, scales, zeros, y=None):
+    """y = x . (scale * q - zero) from a packed 3-bit weight; fp32 or fp16."""
+    K, N = x.shape[0], scales.shape[0]
     dt = x.dtype
     if dt not in (torch.float32, torch.float16):
         raise TypeError("x must be float32 or float16")
     dev = x.device
     _need(x, "x", dt, (K,), dev)
-    _need(qweight, "qweight", torch.int32, (3 * K // 32, N), dev)
+    _need_packed(packed, WQ_OP_Q3, K, N, 0, dev)
     _need(scales, "scales", dt, (N,), dev)
     _need(zeros, "zeros", dt, (N,), dev)
     if y is None:
         y = torch.empty(N, dtype=dt, device=dev)
     _need(y, "y", dt, (N,), dev)
-    ws = workspace(WQ_OP_Q3, 1, K, N, 0, dev)
-    st = lib().wq_matvec_q3(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(y), K, N,
-                            WQ_F16 if dt == torch.float16 else WQ_F32, _ptr(ws), ws.numel(),
-                            _stream(dev))
+    st = lib().wq_matvec_q3(_ptr(x), _ptr(packed), _ptr(scales), _ptr(zeros), _ptr(y), K, N,
+                            WQ_F16 if dt == torch.float16 else WQ_F32, _stream(dev))
     _check("wq_matvec_q3", st)
     return y
 
 
+def unpack_q3(packed, K: int, N: int):
+    dev = packed.device
+    _need_packed(packed, WQ_OP_Q3, K, N, 0, dev)
+    codes = torch.empty((K, N), dtype=torch.int8, device=dev)
+    _check("wq_unpack_q3", lib().wq_unpack_q3(_ptr(packed), _ptr(codes), K, N, _stream(dev)))
+    return codes
+
+
 # ------------------------------------------------------------------ int8 --
 
-def gemm_q8_group(X, qweight, scales, group_size=128, Y=None):
-    """Y = X . (scale[k // G] * q) for a group-wise int8 weight [K, N]."""
+def prepack_q8(qweight):
+    """Re-lay out a group-wise int8 weight [K, N] for gemm_q8_group."""
+    K, N = qweight.shape
+    dev = qweight.device
+    _need(qweight, "qweight", torch.int8, (K, N), dev)
+    out = _packed(WQ_OP_Q8G, K, N, 0, dev)
+    _check("wq_prepack_q8", lib().wq_prepack_q8(_ptr(qweight), _ptr(out), K, N, _stream(dev)))
+    return out
+
+
+def gemm_q8_group(X, packed, scales, group_size=128, Y=None):
+    """Y = X . (scale[k // G] * q) from a packed int8 weight; X fp16 [M, K] or [K]."""
     squeeze = X.dim() == 1
     X2 = X.reshape(1, -1) if squeeze else X
     M, K = X2.shape
-    N = qweight.shape[1]
+    N = scales.shape[1]
     dev = X.device
     _need(X2, "X", torch.float16, (M, K), dev)
-    _need(qweight, "qweight", torch.int8, (K, N), dev)
+    _need_packed(packed, WQ_OP_Q8G, K, N, 0, dev)
     _need(scales, "scales", torch.float32, (K // group_size, N), dev)
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float16, device=dev)
     _need(Y, "Y", torch.float16, (M, N), dev)
-    ws = workspace(WQ_OP_Q8G, M, K, N, group_size, dev)
-    st = lib().wq_gemm_q8_group(_ptr(X2), _ptr(qweight), _ptr(scales), _ptr(Y), M, K, N,
-                                group_size, _ptr(ws), ws.numel(), _stream(dev))
+    st = lib().wq_gemm_q8_group(_ptr(X2), _ptr(packed), _ptr(scales), _ptr(Y), M, K, N,
+                                group_size, _stream(dev))
     _check("wq_gemm_q8_group", st)
     return Y.reshape(N) if squeeze else Y
 
 
+def unpack_q8(packed, K: int, N: int):
+    dev = packed.device
+    _need_packed(packed, WQ_OP_Q8G, K, N, 0, dev)
+    codes = torch.empty((K, N), dtype=torch.int8, device=dev)
+    _check("wq_unpack_q8", lib().wq_unpack_q8(_ptr(packed), _ptr(codes), K, N, _stream(dev)))
+    return codes
+
+
 # ----------------------------------------------------------------- 4-bit --
 
-def q4_act_order_perm(g_idx, K: int, group_size: int = 128) -> np.ndarray:
-    """Host: rows listed group by group (stable); ``g_idx=None`` is the identity."""
+def q4_act_order_perm(g_idx, K: int, group_size: int = 128):
+    """Host: (perm, invperm), rows listed group by group; ``g_idx=None`` is the identity."""
     perm = np.empty(K, dtype=np.int32)
+    inv = np.empty(K, dtype=np.int32)
+    pp, ip = perm.ctypes.data_as(ctypes.c_void_p), inv.ctypes.data_as(ctypes.c_void_p)
     if g_idx is None:
-        st = lib().wq_q4_act_order_perm(None, K, group_size, perm.ctypes.data_as(ctypes.c_void_p))
+        st = lib().wq_q4_act_order_perm(None, K, group_size, pp, ip)
     else:
         g = np.ascontiguousarray(np.asarray(g_idx.cpu() if isinstance(g_idx, torch.Tensor) else g_idx,
                                             dtype=np.int32))
         if g.shape != (K,):
             raise ValueError(f"g_idx must have shape ({K},)")
-        st = lib().wq_q4_act_order_perm(g.ctypes.data_as(ctypes.c_void_p), K, group_size,
-                                        perm.ctypes.data_as(ctypes.c_void_p))
+        st = lib().wq_q4_act_order_perm(g.ctypes.data_as(ctypes.c_void_p), K, group_size, pp, ip)
     _check("wq_q4_act_order_perm", st)
-    return perm
+    return perm, inv
 
 
-def q4_prepack(qweight, perm):
-    """Device: reorder the rows of a 4-bit weight into ``perm`` order."""
+def prepack_q4(qweight, perm=None, group_size=128):
+    """Device: re-lay out a 4-bit weight [K/8, N], rows in ``perm`` order (or as stored)."""
     R, N = qweight.shape
     K = 8 * R
     dev = qweight.device
     _need(qweight, "qweight", torch.int32, (R, N), dev)
-    _need(perm, "perm", torch.int32, (K,), dev)
-    out = torch.empty_like(qweight)
-    st = lib().wq_q4_prepack(_ptr(qweight), _ptr(perm), _ptr(out), K, N, _stream(dev))
-    _check("wq_q4_prepack", st)
+    if perm is not None:
+        _need(perm, "perm", torch.int32, (K,), dev)
+    out = _packed(WQ_OP_Q4G, K, N, group_size, dev)
+    st = lib().wq_prepack_q4(_ptr(qweight), _ptr(perm), _ptr(out), K, N, group_size, _stream(dev))
+    _check("wq_prepack_q4", st)
     return out
 
 
 def prepare_q4(qweight, g_idx, group_size=128):
-    """Act-order preparation: returns ``(qweight_prepacked, perm_device)``."""
+    """Act-order preparation in one go: ``(packed, perm_dev, invperm_dev)``.
+
+    With ``g_idx=None`` the stored order is kept and both permutations are None.
+    """
+    if g_idx is None:
+        return prepack_q4(qweight, None, group_size), None, None
     K = 8 * qweight.shape[0]
-    perm = torch.from_numpy(q4_act_order_perm(g_idx, K, group_size)).to(qweight.device)
-    return q4_prepack(qweight, perm), perm
+    perm, inv = q4_act_order_perm(g_idx, K, group_size)
+    perm_d = torch.from_numpy(perm).to(qweight.device)
+    inv_d = torch.from_numpy(inv).to(qweight.device)
+    return prepack_q4(qweight, perm_d, group_size), perm_d, inv_d
 
 
-def gemm_q4_group(X, qweight, scales, perm=None, group_size=128, Y=None):
-    """Y[m, n] = sum_i X[m, perm[i]] * scale[i // G, n] * q'[i, n] (prepacked q')."""
+def gemm_q4_group(X, packed, scales, invperm=None, group_size=128, Y=None):
+    """Y[m, n] = sum_k X[m, k] * scale[g_idx[k], n] * q[k, n] from a packed 4-bit weight."""
     squeeze = X.dim() == 1
     X2 = X.reshape(1, -1) if squeeze else X
     M, K = X2.shape
-    N = qweight.shape[1]
+    N = scales.shape[1]
     dev = X.device
     _need(X2, "X", torch.float16, (M, K), dev)
-    _need(qweight, "qweight", torch.int32, (K // 8, N), dev)
+    _need_packed(packed, WQ_OP_Q4G, K, N, group_size, dev)
     _need(scales, "scales", torch.float16, (K // group_size, N), dev)
-    if perm is not None:
-        _need(perm, "perm", torch.int32, (K,), dev)
+    if invperm is not None:
+        _need(invperm, "invperm", torch.int32, (K,), dev)
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float16, device=dev)
     _need(Y, "Y", torch.float16, (M, N), dev)
-    ws = workspace(WQ_OP_Q4G, M, K, N, group_size, dev)
-    st = lib().wq_gemm_q4_group(_ptr(X2), _ptr(qweight), _ptr(scales), _ptr(perm), _ptr(Y), M, K,
-                                N, group_size, _ptr(ws), ws.numel(), _stream(dev))
+    st = lib().wq_gemm_q4_group(_ptr(X2), _ptr(packed), _ptr(scales), _ptr(invperm), _ptr(Y), M,
+                                K, N, group_size, _stream(dev))
     _check("wq_gemm_q4_group", st)
     return Y.reshape(N) if squeeze else Y
+
+
+def unpack_q4(packed, K: int, N: int, group_size: int = 128, perm=None):
+    dev = packed.device
+    _need_packed(packed, WQ_OP_Q4G, K, N, group_size, dev)
+    if perm is not None:
+        _need(perm, "perm", torch.int32, (K,), dev)
+    codes = torch.empty((K, N), dtype=torch.int8, device=dev)
+    _check("wq_unpack_q4", lib().wq_unpack_q4(_ptr(packed), _ptr(perm), _ptr(codes), K, N,
+                                              group_size, _stream(dev)))
+    return codes
 
 
 # ------------------------------------------------------------------ W8A8 --
@@ -263,26 +313,3 @@ def gemm_w8a8(X, Wq, Sw, want_acc=False, Y=None, Xq=None, Sx=None, acc=None):
                             M, K, N, _stream(dev))
     _check("wq_gemm_w8a8", st)
     return Y, Xq, Sx, acc
-
-
-# ---------------------------------------------------------------- unpack --
-
-def unpack_q3(qweight, K: int):
-    N = qweight.shape[1]
-    dev = qweight.device
-    _need(qweight, "qweight", torch.int32, (3 * K // 32, N), dev)
-    codes = torch.empty((K, N), dtype=torch.int8, device=dev)
-    _check("wq_unpack_q3", lib().wq_unpack_q3(_ptr(qweight), _ptr(codes), K, N, _stream(dev)))
-    return codes
-
-
-def unpack_q4(qweight, K: int, perm=None):
-    N = qweight.shape[1]
-    dev = qweight.device
-    _need(qweight, "qweight", torch.int32, (K // 8, N), dev)
-    if perm is not None:
-        _need(perm, "perm", torch.int32, (K,), dev)
-    codes = torch.empty((K, N), dtype=torch.int8, device=dev)
-    _check("wq_unpack_q4", lib().wq_unpack_q4(_ptr(qweight), _ptr(perm), _ptr(codes), K, N,
-                                              _stream(dev)))
-    return codes

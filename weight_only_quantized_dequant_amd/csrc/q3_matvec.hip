@@ -12,67 +12,125 @@
 // pairs; the fp16 path here does the same with v_dot2_f32_f16, which
 // accumulates in fp32.
 //
-// Geometry.  A workgroup (4 wave64s) owns a 256-column tile (4 columns per
-// lane: one 128-bit load per word row) and 4*BPW consecutive 32-row blocks;
-// wave w takes BPW of them and issues all 3*BPW loads before converting.  The
-// activations of the workgroup's rows are staged in LDS in the order the
-// code pairs come out (see q3_block_pairs).  Partial sums are reduced across
-// waves in LDS and across the S workgroups of a tile through the workspace.
+// Layout.  The [3K/32, N] weight is re-laid out once, offline
+// (wq_prepack_q3), into column panels of P = 4*CPP columns over the whole of
+// K.  Thread t = s*CPP + c takes the 4 columns of chunk c and the blocks of
+// slot s; the three 16-byte word rows of one block of one chunk sit next to
+// each other, and consecutive threads' blocks are consecutive, so the three
+// loads of a step read 3 KB of contiguous memory per wave.  The activations
+// are staged in LDS in the order the code pairs come out (q3_pair), each
+// pair pre-scaled so that the subnormal code pairs of one accumulation class
+// carry a common power of two.
 #include "wq_device.hpp"
 #include "wq_internal.h"
 
 namespace wq {
 
-template <bool F16, int BPW>
-__global__ __launch_bounds__(kThreads) void q3_matvec_kernel(
-    const void* __restrict__ xv, const uint32_t* __restrict__ qw, const void* __restrict__ sv,
-    const void* __restrict__ zv, void* __restrict__ yv, float* __restrict__ part,
-    unsigned* __restrict__ counters, int K, int N, int S) {
-  constexpr int BPG = 4 * BPW;  // blocks per workgroup
-  constexpr int XW = F16 ? 1 : 2;
-  __shared__ uint32_t xp[BPG][16][XW];
-  __shared__ float red[4][kTileN + 4];
-  __shared__ float xsum_w[4];
-  __shared__ int last_flag;
+static int panel_width_3(int N) {
+  for (int P : {32, 16, 8, 4})
+    if (N % P == 0 && N / P >= 256) return P;
+  for (int P : {4, 8, 16, 32})
+    if (N % P == 0) return P;
+  return 4;
+}
 
-  const int nb = K / 32;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ct = blockIdx.x / S, s = blockIdx.x % S;
-  const int blk0 = s * BPG;
-  const int col0 = ct * kTileN + lane * 4;
-  const bool col_ok = col0 < N;
+PanelPlan plan_q3(int K, int N) {
+  PanelPlan p{};
+  p.P = panel_width_3(N);
+  p.cpp = p.P / 4;
+  p.npanels = N / p.P;
+  const int ns = kThreads / p.cpp;
+  const int ku = K / 32;  // blocks
+  p.u = (ku + ns - 1) / ns;
+  p.nsa = (ku + p.u - 1) / p.u;
+  p.packed_bytes = (size_t)p.npanels * p.u * p.nsa * p.cpp * 48;
+  return p;
+}
 
-  // 1. Stream this wave's blocks: 3 word rows each, 4 columns per lane.
-  //    Blocks past the end fall outside the buffer and read as zero.
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(qw, 3 * nb * N * 4);
-  u32x4 w[BPW][3];
+// ---------------------------------------------------------------------------
+// Offline re-layout: one thread per (block, 4-column chunk) piece of 48 bytes.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void q3_prepack_kernel(const uint32_t* __restrict__ qw,
+                                                              uint32_t* __restrict__ out, int K,
+                                                              int N, PanelPlan p) {
+  const int nta = p.nsa * p.cpp;
+  const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  const size_t total = (size_t)p.npanels * p.u * nta;
+  if (idx >= total) return;
+  const int t = (int)(idx % nta);
+  const size_t pi = idx / nta;
+  const int i = (int)(pi % p.u), panel = (int)(pi / p.u);
+  const int s = t / p.cpp, c = t % p.cpp;
+  const int blk = s * p.u + i;
+  const int col0 = panel * p.P + 4 * c;
 #pragma unroll
-  for (int i = 0; i < BPW; ++i) {
-    const int blk = blk0 + wave * BPW + i;
+  for (int j = 0; j < 3; ++j)
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
-      w[i][j] = buffer_stream(wr, col_ok ? ((3 * blk + j) * N + col0) * 4 : kOutOfRange);
-  }
+    for (int cc = 0; cc < 4; ++cc)
+      out[idx * 12 + j * 4 + cc] = blk < K / 32 ? qw[(size_t)(3 * blk + j) * N + col0 + cc] : 0u;
+}
 
-  // 2. Stage x for these blocks in pair order, and form sum_k x[k].
+// ---------------------------------------------------------------------------
+// The fused product.
+// ---------------------------------------------------------------------------
+template <bool F16, int CPP, int UB>
+__global__ __launch_bounds__(kThreads) void q3_panel_kernel(
+    const void* __restrict__ xv, const uint8_t* __restrict__ Wp, const void* __restrict__ sv,
+    const void* __restrict__ zv, void* __restrict__ yv, int K, int N, int u, int nsa,
+    int packed_bytes) {
+  constexpr int P = 4 * CPP;
+  constexpr int LOWBIT = CPP == 1 ? 0 : CPP == 2 ? 1 : CPP == 4 ? 2 : 3;
+  constexpr int NACC = F16 ? kQ3Classes : 1;
+  constexpr int XW = F16 ? 1 : 2;  // LDS words per pair
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  uint32_t* xp = reinterpret_cast<uint32_t*>(smem);  // [K/2][XW]
+  __shared__ float xsum_w[kThreads / 64];
+  __shared__ float red[kThreads / 64][CPP][4];
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int panel = blockIdx.x;
+  const int nta = nsa * CPP;
+  const int c = t % CPP, s = t / CPP;
+  const bool active = t < nta;
+  const int ku = K / 32;
+  const int blk0 = s * u;
+  const int nblk = active ? (blk0 + u <= ku ? u : (ku > blk0 ? ku - blk0 : 0)) : 0;
+
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wp, packed_bytes);
+  auto wload = [&](int i, int j) {
+    return buffer_stream(wr, (i < nblk) ? ((((panel * u + i) * nta + t) * 3 + j) * 16) : kOutOfRange);
+  };
+
+  // 1. First UB blocks of the weight stream.
+  u32x4 w[UB][3];
+#pragma unroll
+  for (int i = 0; i < UB; ++i)
+#pragma unroll
+    for (int j = 0; j < 3; ++j) w[i][j] = wload(i, j);
+
+  // 2. Stage x in pair order (pre-scaled) and form sum_k x[k].
   float my_sum = 0.0f;
-  for (int idx = tid; idx < BPG * 16; idx += kThreads) {
-    const int bl = idx >> 4, P = idx & 15;
-    const int blk = blk0 + bl;
-    const int ka = 32 * blk + q3_pair(P).a, kb = 32 * blk + q3_pair(P).b;
+  for (int e = t; e < K / 2; e += kThreads) {
+    const int blk = e >> 4, P = e & 15;
+    const Q3Pair q = q3_pair(P);
+    float a, b;
     if constexpr (F16) {
-      const _Float16* x = reinterpret_cast<const _Float16*>(xv);
-      _Float16 a = 0, b = 0;
-      if (blk < nb) { a = x[ka]; b = x[kb]; }
-      xp[bl][P][0] = as_u32((h2){a, b});
-      my_sum += (float)a + (float)b;
+      a = (float)reinterpret_cast<const _Float16*>(xv)[32 * blk + q.a];
+      b = (float)reinterpret_cast<const _Float16*>(xv)[32 * blk + q.b];
     } else {
-      const float* x = reinterpret_cast<const float*>(xv);
-      float a = 0.0f, b = 0.0f;
-      if (blk < nb) { a = x[ka]; b = x[kb]; }
-      xp[bl][P][0] = __builtin_bit_cast(uint32_t, a);
-      xp[bl][P][1] = __builtin_bit_cast(uint32_t, b);
-      my_sum += a + b;
+      a = reinterpret_cast<const float*>(xv)[32 * blk + q.a];
+      b = reinterpret_cast<const float*>(xv)[32 * blk + q.b];
+    }
+    my_sum += a + b;
+    if constexpr (F16) {
+      // class = max(pa, pb): the half with the smaller offset is divided by 2^d.
+      const int cls = q.pa > q.pb ? q.pa : q.pb;
+      const h2 v = {(_Float16)__builtin_ldexpf(a, cls - q.pa), (_Float16)__builtin_ldexpf(b, cls - q.pb)};
+      xp[e] = as_u32(v);
+    } else {
+      // fp32: undo the 2^(p - 24) of each subnormal code in the activation.
+      xp[2 * e] = __builtin_bit_cast(uint32_t, __builtin_ldexpf(a, 24 - q.pa));
+      xp[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_ldexpf(b, 24 - q.pb));
     }
   }
 #pragma unroll
@@ -81,118 +139,180 @@ __global__ __launch_bounds__(kThreads) void q3_matvec_kernel(
   __syncthreads();
   const float xsum = (xsum_w[0] + xsum_w[1]) + (xsum_w[2] + xsum_w[3]);
 
-  // 3. Exact codes times x, accumulated in fp32.
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  // 3. Exact codes times x, fp32 accumulation (one accumulator per class).
+  float acc[NACC][4];
 #pragma unroll
-  for (int i = 0; i < BPW; ++i) {
-    const int bl = wave * BPW + i;
-    uint32_t xr[16][XW];
+  for (int a = 0; a < NACC; ++a)
 #pragma unroll
-    for (int P = 0; P < 16; ++P)
+    for (int j = 0; j < 4; ++j) acc[a][j] = 0.0f;
+
+  for (int i0 = 0; i0 < nblk; i0 += UB) {
+    if (i0 > 0) {
 #pragma unroll
-      for (int t = 0; t < XW; ++t) xr[P][t] = xp[bl][P][t];
+      for (int i = 0; i < UB; ++i)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      h2 pr[16];
-      q3_block_pairs(w[i][0][c], w[i][1][c], w[i][2][c], pr);
+        for (int j = 0; j < 3; ++j) w[i][j] = wload(i0 + i, j);
+    }
 #pragma unroll
-      for (int P = 0; P < 16; ++P) {
-        if constexpr (F16) {
-          acc[c] = dot2(pr[P], as_h2(xr[P][0]), acc[c]);
-        } else {
-          acc[c] = __builtin_fmaf((float)pr[P].x, __builtin_bit_cast(float, xr[P][0]), acc[c]);
-          acc[c] = __builtin_fmaf((float)pr[P].y, __builtin_bit_cast(float, xr[P][1]), acc[c]);
+    for (int i = 0; i < UB; ++i) {
+      if (i0 + i >= nblk) break;
+      const int blk = blk0 + i0 + i;
+      uint32_t xr[16][XW];
+      const u32x4* xq = reinterpret_cast<const u32x4*>(xp + (size_t)blk * 16 * XW);
+#pragma unroll
+      for (int v4 = 0; v4 < 4 * XW; ++v4) {
+        const u32x4 tmp = xq[v4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xr[(v4 * 4 + e) / XW][(v4 * 4 + e) % XW] = tmp[e];
+      }
+#pragma unroll
+      for (int col = 0; col < 4; ++col) {
+        h2 pr[16];
+        q3_block_pairs_sub(w[i][0][col], w[i][1][col], w[i][2][col], pr);
+#pragma unroll
+        for (int P = 0; P < 16; ++P) {
+          if constexpr (F16) {
+            const int slot = q3_class_slot(q3_class(P));
+            acc[slot][col] = dot2(pr[P], as_h2(xr[P][0]), acc[slot][col]);
+          } else {
+            acc[0][col] = __builtin_fmaf((float)pr[P].x, __builtin_bit_cast(float, xr[P][0]), acc[0][col]);
+            acc[0][col] = __builtin_fmaf((float)pr[P].y, __builtin_bit_cast(float, xr[P][1]), acc[0][col]);
+          }
         }
       }
     }
   }
 
-  // 4. Across waves; thread t owns column t of the tile.
+  // 4. Classes back to one sum per column (powers of two: exact rescale).
+  float v[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) red[wave][lane * 4 + c] = acc[c];
-  __syncthreads();
-  const int n = ct * kTileN + tid;
-  const float A = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
-  float val = 0.0f;
-  if (n < N) {
-    float sc, ze;
+  for (int j = 0; j < 4; ++j) {
     if constexpr (F16) {
-      sc = (float)reinterpret_cast<const _Float16*>(sv)[n];
-      ze = (float)reinterpret_cast<const _Float16*>(zv)[n];
+      float a = 0.0f;
+#pragma unroll
+      for (int sl = 0; sl < NACC; ++sl) a = __builtin_fmaf(acc[sl][j], __builtin_ldexpf(1.0f, 24 - q3_slot_class(sl)), a);
+      v[j] = a;
     } else {
-      sc = reinterpret_cast<const float*>(sv)[n];
-      ze = reinterpret_cast<const float*>(zv)[n];
+      v[j] = acc[0][j];
     }
-    val = sc * A - ze * xsum;
   }
 
-  auto store = [&](float v) {
-    if constexpr (F16) reinterpret_cast<_Float16*>(yv)[n] = (_Float16)v;
-    else reinterpret_cast<float*>(yv)[n] = v;
-  };
-  if (S == 1) {
-    if (n < N) store(val);
-    return;
+  // 5. Over the slots of a chunk, then y = scale * A - zero * sum(x).
+  bfly<4, 5, LOWBIT>(v, lane);
+  bool owner;
+  const int base = bfly_base<4, LOWBIT>(lane, owner);
+  constexpr int LEFT = bfly_left<4, LOWBIT>();
+  if (owner) {
+#pragma unroll
+    for (int j = 0; j < LEFT; ++j) red[wave][c][base + j] = v[j];
   }
-  if (n < N) part[(size_t)s * N + n] = val;
-  if (splitk_arrive(&counters[ct], S, &last_flag)) {
-    if (n < N) {
-      float t = 0.0f;
-      for (int j = 0; j < S; ++j) t += part[(size_t)j * N + n];
-      store(t);
+  __syncthreads();
+  if (t < P) {
+    const int rc = t / 4, j = t % 4;
+    const int n = panel * P + t;
+    const float A = (red[0][rc][j] + red[1][rc][j]) + (red[2][rc][j] + red[3][rc][j]);
+    if constexpr (F16) {
+      const float sc = (float)reinterpret_cast<const _Float16*>(sv)[n];
+      const float ze = (float)reinterpret_cast<const _Float16*>(zv)[n];
+      reinterpret_cast<_Float16*>(yv)[n] = (_Float16)(sc * A - ze * xsum);
+    } else {
+      const float sc = reinterpret_cast<const float*>(sv)[n];
+      const float ze = reinterpret_cast<const float*>(zv)[n];
+      reinterpret_cast<float*>(yv)[n] = sc * A - ze * xsum;
     }
-    splitk_reset(&counters[ct]);
   }
 }
 
-// Blocks per wave: the most (loads in flight per lane) that still gives
-// enough workgroups to cover the GPU.
-SplitPlan plan_q3(int K, int N) {
-  SplitPlan p;
-  p.mt = 1;
-  p.n_tiles = (N + kTileN - 1) / kTileN;
-  const int nb = K / 32;
-  int bpw = 1;
-  for (int cand : {4, 2, 1}) {
-    const int S = (nb + 4 * cand - 1) / (4 * cand);
-    if (p.n_tiles * S >= 240 || cand == 1) { bpw = cand; break; }
+// ---------------------------------------------------------------------------
+// Bit-exact check: each packed block through q3_block_pairs_sub back to codes.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void q3_unpack_kernel(const uint8_t* __restrict__ Wp,
+                                                             int8_t* __restrict__ codes, int K,
+                                                             int N, PanelPlan p) {
+  const int nta = p.nsa * p.cpp;
+  const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  const size_t total = (size_t)p.npanels * p.u * nta;
+  if (idx >= total) return;
+  const int t = (int)(idx % nta);
+  const size_t pi = idx / nta;
+  const int i = (int)(pi % p.u), panel = (int)(pi / p.u);
+  const int s = t / p.cpp, c = t % p.cpp;
+  const int blk = s * p.u + i;
+  if (blk >= K / 32) return;
+  const int col0 = panel * p.P + 4 * c;
+  u32x4 w[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) w[j] = *reinterpret_cast<const u32x4*>(Wp + (idx * 3 + j) * 16);
+#pragma unroll
+  for (int col = 0; col < 4; ++col) {
+    h2 pr[16];
+    q3_block_pairs_sub(w[0][col], w[1][col], w[2][col], pr);
+#pragma unroll
+    for (int P = 0; P < 16; ++P) {
+      const uint32_t bits = as_u32(pr[P]);
+      const int ca = (int)((bits & 0xFFFFu) >> q3_pair(P).pa);
+      const int cb = (int)((bits >> 16) >> q3_pair(P).pb);
+      codes[(size_t)(32 * blk + q3_pair(P).a) * N + col0 + col] = (int8_t)ca;
+      codes[(size_t)(32 * blk + q3_pair(P).b) * N + col0 + col] = (int8_t)cb;
+    }
   }
-  const int ov = env_unit_override();
-  if (ov == 1 || ov == 2 || ov == 4 || ov == 8) bpw = ov;
-  p.unit = bpw;
-  p.splits = (nb + 4 * bpw - 1) / (4 * bpw);
-  return p;
 }
 
-template <bool F16, int BPW>
-static hipError_t launch_q3_t(const void* x, const int32_t* qw, const void* scales,
-                              const void* zeros, void* y, int K, int N, const SplitPlan& p,
-                              void* ws, hipStream_t s) {
-  unsigned* counters = reinterpret_cast<unsigned*>(ws);
-  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + ws_counter_bytes(p.n_tiles));
-  hipLaunchKernelGGL((q3_matvec_kernel<F16, BPW>), dim3(p.n_tiles * p.splits), dim3(kThreads), 0,
-                     s, x, reinterpret_cast<const uint32_t*>(qw), scales, zeros, y, part, counters,
-                     K, N, p.splits);
+hipError_t launch_q3_prepack(const int32_t* qw, void* out, int K, int N, hipStream_t s) {
+  const PanelPlan p = plan_q3(K, N);
+  const size_t total = (size_t)p.npanels * p.u * p.nsa * p.cpp;
+  hipLaunchKernelGGL(q3_prepack_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, reinterpret_cast<const uint32_t*>(qw),
+                     reinterpret_cast<uint32_t*>(out), K, N, p);
   return hipGetLastError();
 }
 
+hipError_t launch_q3_unpack(const void* packed, int8_t* codes, int K, int N, hipStream_t s) {
+  const PanelPlan p = plan_q3(K, N);
+  const size_t total = (size_t)p.npanels * p.u * p.nsa * p.cpp;
+  hipLaunchKernelGGL(q3_unpack_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, reinterpret_cast<const uint8_t*>(packed), codes, K, N, p);
+  return hipGetLastError();
+}
+
+template <bool F16, int CPP, int UB>
+static hipError_t launch_q3_t(const void* x, const void* packed, const void* scales,
+                              const void* zeros, void* y, int K, int N, const PanelPlan& p,
+                              hipStream_t s) {
+  const size_t lds = (size_t)(K / 2) * (F16 ? 4 : 8);
+  hipLaunchKernelGGL((q3_panel_kernel<F16, CPP, UB>), dim3(p.npanels), dim3(kThreads), lds, s, x,
+                     reinterpret_cast<const uint8_t*>(packed), scales, zeros, y, K, N, p.u, p.nsa,
+                     (int)p.packed_bytes);
+  return hipGetLastError();
+}
+
+template <bool F16, int CPP>
+static hipError_t launch_q3_ub(const void* x, const void* packed, const void* scales,
+                               const void* zeros, void* y, int K, int N, const PanelPlan& p,
+                               hipStream_t s) {
+  if (p.u <= 1) return launch_q3_t<F16, CPP, 1>(x, packed, scales, zeros, y, K, N, p, s);
+  if (p.u <= 2) return launch_q3_t<F16, CPP, 2>(x, packed, scales, zeros, y, K, N, p, s);
+  if (p.u <= 4) return launch_q3_t<F16, CPP, 4>(x, packed, scales, zeros, y, K, N, p, s);
+  return launch_q3_t<F16, CPP, 6>(x, packed, scales, zeros, y, K, N, p, s);
+}
+
 template <bool F16>
-static hipError_t launch_q3_f(const void* x, const int32_t* qw, const void* scales,
-                              const void* zeros, void* y, int K, int N, const SplitPlan& p,
-                              void* ws, hipStream_t s) {
-  switch (p.unit) {
-    case 1: return launch_q3_t<F16, 1>(x, qw, scales, zeros, y, K, N, p, ws, s);
-    case 2: return launch_q3_t<F16, 2>(x, qw, scales, zeros, y, K, N, p, ws, s);
-    case 4: return launch_q3_t<F16, 4>(x, qw, scales, zeros, y, K, N, p, ws, s);
-    default: return launch_q3_t<F16, 8>(x, qw, scales, zeros, y, K, N, p, ws, s);
+static hipError_t launch_q3_f(const void* x, const void* packed, const void* scales,
+                              const void* zeros, void* y, int K, int N, const PanelPlan& p,
+                              hipStream_t s) {
+  switch (p.cpp) {
+    case 1: return launch_q3_ub<F16, 1>(x, packed, scales, zeros, y, K, N, p, s);
+    case 2: return launch_q3_ub<F16, 2>(x, packed, scales, zeros, y, K, N, p, s);
+    case 4: return launch_q3_ub<F16, 4>(x, packed, scales, zeros, y, K, N, p, s);
+    default: return launch_q3_ub<F16, 8>(x, packed, scales, zeros, y, K, N, p, s);
   }
 }
 
-hipError_t launch_q3(const void* x, const int32_t* qw, const void* scales, const void* zeros,
-                     void* y, int K, int N, bool f16, const SplitPlan& p, void* ws,
-                     hipStream_t s) {
-  return f16 ? launch_q3_f<true>(x, qw, scales, zeros, y, K, N, p, ws, s)
-             : launch_q3_f<false>(x, qw, scales, zeros, y, K, N, p, ws, s);
+hipError_t launch_q3(const void* x, const void* packed, const void* scales, const void* zeros,
+                     void* y, int K, int N, bool f16, hipStream_t s) {
+  const PanelPlan p = plan_q3(K, N);
+  return f16 ? launch_q3_f<true>(x, packed, scales, zeros, y, K, N, p, s)
+             : launch_q3_f<false>(x, packed, scales, zeros, y, K, N, p, s);
 }
 
 }  // namespace wq

@@ -2,225 +2,388 @@
 //
 //   Y[m, n] = sum_g scale[g, n] * sum_{rows i of group g} X[m, perm[i]] * q'[i, n]
 //
-// Codes are 8 per int32 along K, stored as q + 8 ("Quantization CUDA",
+// Codes are 8 per int32 along K, stored as u = q + 8 ("Quantization CUDA",
 // tom-jerr.github.io, sections "Int4 Weight Only Quantization" and "Weight
 // Store"; "量化粒度": group-wise scales, groups of 128 along K).  With
 // act-order ("GPTQ算法解析", intelliparadigm.com, section 4.1: act_order) a
-// row's group is g_idx[k], which is not monotone in k.  The weight is
-// reordered once, offline, so that the rows of each group are contiguous
-// (wq_q4_prepack, the same idea as the offline re-layout of "Marlin 格式" on
-// the "Quantization CUDA" page); the kernel then gathers the activations
-// through perm while staging them, and every span of rows it reads belongs to
-// a single group whose scale is applied once.
+// row's group g_idx[k] is not monotone in k.  The weight is re-laid out once,
+// offline (wq_prepack_q4), the same idea as the offline re-layout of "Marlin
+// 格式" on the "Quantization CUDA" page: rows are put in group order (perm),
+// then into column panels over the whole of K in the order the threads read
+// them.  At run time each workgroup scatters X into LDS through the inverse
+// permutation (coalesced reads, LDS writes), so every 128-row batch a thread
+// reads is one group, scaled once.
 //
-// Geometry.  A workgroup (4 wave64s) owns a 256-column tile (4 columns per
-// lane) and 4*WPW word rows (32*WPW rows of K); wave w takes WPW word rows,
-// which lie in one group (8*WPW divides G).  Each code pair is reused for all
-// M rows of X.
+// Geometry.  A workgroup owns a panel of P = 4*CPP columns; thread
+// t = s*CPP + c takes the 4 columns of chunk c (one 128-bit load per word
+// row) and the u word rows of slot s, in batches of BW word rows (one group,
+// or a part of one).  The activations sit in LDS as the pairs
+// (rows 8r + j, 8r + j + 4) the codes come out in (q4_pairs_sub).
 #include "wq_device.hpp"
 #include "wq_internal.h"
 
 namespace wq {
 
-template <int MT, int WPW>
-__global__ __launch_bounds__(kThreads) void q4_group_kernel(
-    const _Float16* __restrict__ X, const uint32_t* __restrict__ qw,
-    const _Float16* __restrict__ scales, const int* __restrict__ perm, _Float16* __restrict__ Y,
-    float* __restrict__ part, unsigned* __restrict__ counters, int M, int K, int N, int G, int S) {
-  constexpr int RPG = 4 * WPW;  // word rows per workgroup
-  __shared__ h2 xs[MT][RPG][4];
-  __shared__ float red[4][MT][kTileN + 4];
-  __shared__ int last_flag;
+static int panel_width_4(int N) {
+  for (int P : {32, 16, 8, 4})
+    if (N % P == 0 && N / P >= 256) return P;
+  for (int P : {4, 8, 16, 32})
+    if (N % P == 0) return P;
+  return 4;
+}
 
-  const int nr = K / 8;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ct = blockIdx.x / S, s = blockIdx.x % S;
-  const int r0 = s * RPG;
-  const int col0 = ct * kTileN + lane * 4;
-  const bool col_ok = col0 < N;
-  const int rw0 = r0 + wave * WPW;  // this wave's first word row
+PanelPlan plan_q4(int K, int N, int G) {
+  PanelPlan p{};
+  p.P = panel_width_4(N);
+  p.cpp = p.P / 4;
+  p.npanels = N / p.P;
+  const int ns = kThreads / p.cpp;
+  const int ku = K / 8;                       // word rows
+  p.bw = (G / 8) < 16 ? (G / 8) : 16;         // word rows per batch: inside one group
+  p.u = p.bw * ((ku + ns * p.bw - 1) / (ns * p.bw));
+  p.nsa = (ku + p.u - 1) / p.u;
+  p.packed_bytes = (size_t)p.npanels * p.u * p.nsa * p.cpp * 16;
+  return p;
+}
 
-  // 1. Stream this wave's word rows (rows past the end read as zero).
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(qw, nr * N * 4);
-  u32x4 w[WPW];
+// One LDS copy of X holds K rounded up to 64 rows (the swizzle below permutes
+// word rows inside aligned groups of 8).
+static inline int q4_kpad(int K) { return (K + 63) / 64 * 64; }
+
+// Rows of X staged per launch: the LDS copies of X (MT * Kpad halves) stay <= 64 KB.
+int q4_max_mt(int K) {
+  int mt = 8;
+  while (mt > 1 && (size_t)mt * q4_kpad(K) * 2 > 65536) mt /= 2;
+  return mt;
+}
+
+// LDS word-row swizzle: slots that share a wave read different banks.  It
+// only flips the low 3 bits of r, so it stays inside r's aligned 8-row group.
+__device__ __forceinline__ int q4_swz(int r) { return r ^ ((r >> 4) & 7); }
+// Half-word index of row i (in group order) inside one LDS copy of X.
+__device__ __forceinline__ int q4_lds_half(int i) {
+  const int r = i >> 3, j = i & 7;
+  return (q4_swz(r) * 4 + (j & 3)) * 2 + (j >> 2);
+}
+
+// ---------------------------------------------------------------------------
+// Offline re-layout: one thread per 16-byte piece (4 columns of a word row).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void q4_prepack_kernel(const uint32_t* __restrict__ qw,
+                                                              const int* __restrict__ perm,
+                                                              uint32_t* __restrict__ out, int K,
+                                                              int N, PanelPlan p) {
+  const int nta = p.nsa * p.cpp;
+  const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  const size_t total = (size_t)p.npanels * p.u * nta;
+  if (idx >= total) return;
+  const int t = (int)(idx % nta);
+  const size_t pi = idx / nta;
+  const int i = (int)(pi % p.u), panel = (int)(pi / p.u);
+  const int s = t / p.cpp, c = t % p.cpp;
+  const int r = s * p.u + i;  // word row in group order
+  const int col0 = panel * p.P + 4 * c;
 #pragma unroll
-  for (int i = 0; i < WPW; ++i)
-    w[i] = buffer_stream(wr, col_ok ? ((rw0 + i) * N + col0) * 4 : kOutOfRange);
-
-  // 2. Stage X[m, perm[i]] as the pairs (rows 8r+j, 8r+j+4) the codes come in.
-  for (int idx = tid; idx < MT * RPG * 4; idx += kThreads) {
-    const int m = idx / (RPG * 4), rem = idx % (RPG * 4);
-    const int rw = rem >> 2, j = rem & 3;
-    const int ia = 8 * (r0 + rw) + j, ib = ia + 4;
-    _Float16 a = 0, b = 0;
-    if (m < M && ia < K) {
-      const int ka = perm ? perm[ia] : ia, kb = perm ? perm[ib] : ib;
-      a = X[(size_t)m * K + ka];
-      b = X[(size_t)m * K + kb];
+  for (int cc = 0; cc < 4; ++cc) {
+    uint32_t word = 0;  // padding rows: u = 0, so they add nothing whatever x is
+    if (r < K / 8) {
+      word = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int src = perm ? perm[8 * r + j] : 8 * r + j;
+        const uint32_t sw = qw[(size_t)(src >> 3) * N + col0 + cc];
+        word |= ((sw >> (4 * (src & 7))) & 15u) << (4 * j);
+      }
     }
-    xs[m][rw][j] = (h2){a, b};
+    out[idx * 4 + cc] = word;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The fused product.
+// ---------------------------------------------------------------------------
+template <int MT, int CPP, int BW>
+__global__ __launch_bounds__(kThreads) void q4_panel_kernel(
+    const _Float16* __restrict__ X, const uint8_t* __restrict__ Wp,
+    const _Float16* __restrict__ scales, const int* __restrict__ invperm,
+    _Float16* __restrict__ Y, int M, int K, int N, int G, int u, int nsa, int packed_bytes) {
+  constexpr int P = 4 * CPP;
+  constexpr int V = 4 * MT;  // results per chunk: [m][4 columns]
+  constexpr int LOWBIT = CPP == 1 ? 0 : CPP == 2 ? 1 : CPP == 4 ? 2 : 3;
+  constexpr int LEFT = bfly_left<V, LOWBIT>();
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  _Float16* xh = reinterpret_cast<_Float16*>(smem);  // MT copies of K halves
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int panel = blockIdx.x;
+  const int nta = nsa * CPP;
+  const int c = t % CPP, s = t / CPP;
+  const bool active = t < nta;
+  const int col0 = panel * P + 4 * c;
+  const int ku = K / 8;
+  const int kpad = (K + 63) / 64 * 64;  // halves per LDS copy of X
+
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wp, packed_bytes);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, (K / G) * N * 2);
+
+  // 1. First batch of the weight stream goes out before anything else.
+  u32x4 w[BW], wn[BW];
+  const int nb = u / BW;
+  auto load_batch = [&](u32x4* dst, int b) {
+    const int wbase = ((panel * u + b * BW) * nta + t) * 16;
+#pragma unroll
+    for (int i = 0; i < BW; ++i) dst[i] = buffer_stream(wr, active ? wbase + i * nta * 16 : kOutOfRange);
+  };
+  load_batch(w, 0);
+
+  // 2. Scatter X into LDS through the inverse permutation (group order).
+  for (int e = t * 8; e < MT * K; e += kThreads * 8) {
+    const int m = e / K, k = e % K;
+    u32x4 xv = {0u, 0u, 0u, 0u};
+    if (m < M) xv = *reinterpret_cast<const u32x4*>(X + (size_t)m * K + k);
+    int dst[8];
+    if (invperm) {
+      const u32x4 p0 = *reinterpret_cast<const u32x4*>(invperm + k);
+      const u32x4 p1 = *reinterpret_cast<const u32x4*>(invperm + k + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { dst[j] = (int)p0[j]; dst[4 + j] = (int)p1[j]; }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dst[j] = k + j;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t word = xv[j >> 1];
+      const uint16_t bits = (j & 1) ? (uint16_t)(word >> 16) : (uint16_t)(word & 0xFFFFu);
+      reinterpret_cast<uint16_t*>(xh)[(size_t)m * kpad + q4_lds_half(dst[j])] = bits;
+    }
   }
   __syncthreads();
 
-  // 3. Exact codes, fp32 accumulation.
-  float acc[MT][4];
+  const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+  float accT[MT][4];
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[m][c] = 0.0f;
+    for (int j = 0; j < 4; ++j) accT[m][j] = 0.0f;
+
+  for (int b = 0; b < nb; ++b) {
+    if (b + 1 < nb) load_batch(wn, b + 1);  // next batch in flight during this one
+    const int r0 = s * u + b * BW;  // first word row of the batch (group order)
+    const bool live = active && r0 < ku;
+    uint2 sraw = make_uint2(0u, 0u);
+    {
+      const int soff = live ? (((8 * r0) / G) * N + col0) * 2 : kOutOfRange;
+      const unsigned long long v64 = __builtin_bit_cast(
+          unsigned long long, __builtin_amdgcn_raw_buffer_load_b64(sr, soff, 0, 0));
+      sraw = make_uint2((uint32_t)v64, (uint32_t)(v64 >> 32));
+    }
+    // Sum of x over the batch: the CPP lanes of a slot split the word rows.
+    float xs[MT];
 #pragma unroll
-  for (int i = 0; i < WPW; ++i) {
-    h2 xv[MT][4];
+    for (int m = 0; m < MT; ++m) xs[m] = 0.0f;
+    for (int i = c; i < BW; i += CPP) {
+      const int r = r0 + i;
+      if (r < ku) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const u32x4 xv = *reinterpret_cast<const u32x4*>(xh + (size_t)m * kpad + q4_swz(r) * 8);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) xs[m] = dot2(as_h2(xv[j]), ones, xs[m]);
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < CPP; o <<= 1)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) xs[m] += __shfl_xor(xs[m], o);
+
+    // Codes are u = q + 8: start at -8 * sum(x) (2^-24 units).  acc0 holds the
+    // even nibbles (u * 2^-24), acc4 the odd ones (16u * 2^-24).
+    float acc0[MT][4], acc4[MT][4];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) xv[m][j] = xs[m][wave * WPW + i][j];
+      for (int j = 0; j < 4; ++j) {
+        acc0[m][j] = xs[m] * (-8.0f / kTwo24);
+        acc4[m][j] = 0.0f;
+      }
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      h2 pr[4];
-      q4_word_pairs(w[i][c], pr);
+    for (int i = 0; i < BW; ++i) {
+      const int r = r0 + i < ku ? r0 + i : ku - 1;  // rows past K: codes are 0, any x
+      u32x4 xv[MT];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int m = 0; m < MT; ++m) xv[m] = *reinterpret_cast<const u32x4*>(xh + (size_t)m * kpad + q4_swz(r) * 8);
 #pragma unroll
-        for (int m = 0; m < MT; ++m) acc[m][c] = dot2(pr[j], xv[m][j], acc[m][c]);
+      for (int j = 0; j < 4; ++j) {
+        h2 pr[4];
+        q4_pairs_sub(w[i][j], pr);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          acc0[m][j] = dot2(pr[0], as_h2(xv[m][0]), acc0[m][j]);
+          acc4[m][j] = dot2(pr[1], as_h2(xv[m][1]), acc4[m][j]);
+          acc0[m][j] = dot2(pr[2], as_h2(xv[m][2]), acc0[m][j]);
+          acc4[m][j] = dot2(pr[3], as_h2(xv[m][3]), acc4[m][j]);
+        }
+      }
     }
-  }
-
-  // 4. The span is one group: scale once.
-  if (col_ok && 8 * rw0 < K) {
-    const uint2 sraw = *reinterpret_cast<const uint2*>(scales + (size_t)((8 * rw0) / G) * N + col0);
     const h2 s01 = as_h2(sraw.x), s23 = as_h2(sraw.y);
     const float sc[4] = {(float)s01.x, (float)s01.y, (float)s23.x, (float)s23.y};
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[m][c] *= sc[c];
-  }
-
-  // 5. Across waves; thread t owns column t of the tile.
+      for (int j = 0; j < 4; ++j)
+        accT[m][j] = __builtin_fmaf(__builtin_fmaf(acc4[m][j], 0.0625f, acc0[m][j]), sc[j], accT[m][j]);
+    if (b + 1 < nb) {
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) red[wave][m][lane * 4 + c] = acc[m][c];
-  __syncthreads();
-  const int n = ct * kTileN + tid;
-  float sum[MT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-    sum[m] = (red[0][m][tid] + red[1][m][tid]) + (red[2][m][tid] + red[3][m][tid]);
-
-  if (S == 1) {
-    if (n < N)
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-        if (m < M) Y[(size_t)m * N + n] = (_Float16)sum[m];
-    return;
-  }
-  if (n < N)
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-      if (m < M) part[((size_t)s * MT + m) * N + n] = sum[m];
-  if (splitk_arrive(&counters[ct], S, &last_flag)) {
-    if (n < N) {
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        if (m >= M) continue;
-        float t = 0.0f;
-        for (int j = 0; j < S; ++j) t += part[((size_t)j * MT + m) * N + n];
-        Y[(size_t)m * N + n] = (_Float16)t;
-      }
+      for (int i = 0; i < BW; ++i) w[i] = wn[i];
     }
-    splitk_reset(&counters[ct]);
+  }
+
+  // Reduce over the slots of a chunk (LDS reused for the cross-wave step).
+  float v[V];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[m * 4 + j] = accT[m][j];
+  bfly<V, 5, LOWBIT>(v, lane);
+  bool owner;
+  const int base = bfly_base<V, LOWBIT>(lane, owner);
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);  // [4 waves][CPP][V]
+  if (owner) {
+#pragma unroll
+    for (int j = 0; j < LEFT; ++j) red[(wave * CPP + c) * V + base + j] = v[j];
+  }
+  __syncthreads();
+  for (int r = t; r < CPP * V; r += kThreads) {
+    const int rc = r / V, idx = r % V;
+    const int m = idx / 4, col = panel * P + 4 * rc + (idx % 4);
+    float sum = 0.0f;
+#pragma unroll
+    for (int w2 = 0; w2 < kThreads / 64; ++w2) sum += red[(w2 * CPP + rc) * V + idx];
+    if (m < M) Y[(size_t)m * N + col] = (_Float16)(sum * kTwo24);
   }
 }
 
-// Word rows per wave: one whole group when it is at most 128 rows (16 loads
-// of 128 bits in flight per lane), else 16.
-SplitPlan plan_q4(int M, int K, int N, int G) {
-  SplitPlan p;
-  p.mt = M == 1 ? 1 : (M == 2 ? 2 : (M <= 4 ? 4 : 8));
-  p.n_tiles = (N + kTileN - 1) / kTileN;
-  int wpw = G / 8 >= 16 ? 16 : G / 8;  // G % 32 == 0, so wpw is 4, 8 or 16
-  const int ov = env_unit_override();
-  if ((ov == 4 || ov == 8 || ov == 16) && (G / 8) % ov == 0) wpw = ov;
-  p.unit = wpw;
-  const int nr = K / 8;
-  p.splits = (nr + 4 * wpw - 1) / (4 * wpw);
-  return p;
+// ---------------------------------------------------------------------------
+// Bit-exact check: packed pieces through q4_pairs_sub back to signed codes in
+// the original row order (perm), one thread per piece.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void q4_unpack_kernel(const uint8_t* __restrict__ Wp,
+                                                             const int* __restrict__ perm,
+                                                             int8_t* __restrict__ codes, int K,
+                                                             int N, PanelPlan p) {
+  const int nta = p.nsa * p.cpp;
+  const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  const size_t total = (size_t)p.npanels * p.u * nta;
+  if (idx >= total) return;
+  const int t = (int)(idx % nta);
+  const size_t pi = idx / nta;
+  const int i = (int)(pi % p.u), panel = (int)(pi / p.u);
+  const int s = t / p.cpp, c = t % p.cpp;
+  const int r = s * p.u + i;
+  if (r >= K / 8) return;
+  const int col0 = panel * p.P + 4 * c;
+  const u32x4 w = *reinterpret_cast<const u32x4*>(Wp + idx * 16);
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+    h2 pr[4];
+    q4_pairs_sub(w[cc], pr);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t bits = as_u32(pr[j]);
+      const int sh = (j & 1) ? 4 : 0;  // pairs 1 and 3 sit at bit 4 of each half
+      const int ulo = (int)((bits & 0xFFFFu) >> sh), uhi = (int)((bits >> 16) >> sh);
+      const int ia = 8 * r + j, ib = ia + 4;
+      const int da = perm ? perm[ia] : ia, db = perm ? perm[ib] : ib;
+      codes[(size_t)da * N + col0 + cc] = (int8_t)(ulo - 8);
+      codes[(size_t)db * N + col0 + cc] = (int8_t)(uhi - 8);
+    }
+  }
 }
 
-template <int MT, int WPW>
-static hipError_t launch_q4_t(const void* X, const int32_t* qw, const void* scales,
-                              const int32_t* perm, void* Y, int M, int K, int N, int G,
-                              const SplitPlan& p, void* ws, hipStream_t s) {
-  unsigned* counters = reinterpret_cast<unsigned*>(ws);
-  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + ws_counter_bytes(p.n_tiles));
-  hipLaunchKernelGGL((q4_group_kernel<MT, WPW>), dim3(p.n_tiles * p.splits), dim3(kThreads), 0, s,
-                     reinterpret_cast<const _Float16*>(X), reinterpret_cast<const uint32_t*>(qw),
-                     reinterpret_cast<const _Float16*>(scales), perm,
-                     reinterpret_cast<_Float16*>(Y), part, counters, M, K, N, G, p.splits);
+hipError_t launch_q4_prepack(const int32_t* qw, const int32_t* perm, void* out, int K, int N, int G,
+                             hipStream_t s) {
+  const PanelPlan p = plan_q4(K, N, G);
+  const size_t total = (size_t)p.npanels * p.u * p.nsa * p.cpp;
+  hipLaunchKernelGGL(q4_prepack_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, reinterpret_cast<const uint32_t*>(qw), perm,
+                     reinterpret_cast<uint32_t*>(out), K, N, p);
   return hipGetLastError();
 }
 
-template <int MT>
-static hipError_t launch_q4_mt(const void* X, const int32_t* qw, const void* scales,
-                               const int32_t* perm, void* Y, int M, int K, int N, int G,
-                               const SplitPlan& p, void* ws, hipStream_t s) {
-  switch (p.unit) {
-    case 4: return launch_q4_t<MT, 4>(X, qw, scales, perm, Y, M, K, N, G, p, ws, s);
-    case 8: return launch_q4_t<MT, 8>(X, qw, scales, perm, Y, M, K, N, G, p, ws, s);
-    default: return launch_q4_t<MT, 16>(X, qw, scales, perm, Y, M, K, N, G, p, ws, s);
+hipError_t launch_q4_unpack(const void* packed, const int32_t* perm, int8_t* codes, int K, int N,
+                            int G, hipStream_t s) {
+  const PanelPlan p = plan_q4(K, N, G);
+  const size_t total = (size_t)p.npanels * p.u * p.nsa * p.cpp;
+  hipLaunchKernelGGL(q4_unpack_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, reinterpret_cast<const uint8_t*>(packed), perm, codes, K,
+                     N, p);
+  return hipGetLastError();
+}
+
+template <int MT, int CPP, int BW>
+static hipError_t launch_q4_t(const void* X, const void* packed, const void* scales,
+                              const int32_t* invperm, void* Y, int M, int K, int N, int G,
+                              const PanelPlan& p, hipStream_t s) {
+  const size_t xb = (size_t)MT * q4_kpad(K) * 2, rb = (size_t)kThreads / 64 * CPP * 4 * MT * 4;
+  const size_t lds = xb > rb ? xb : rb;
+  hipLaunchKernelGGL((q4_panel_kernel<MT, CPP, BW>), dim3(p.npanels), dim3(kThreads), lds, s,
+                     reinterpret_cast<const _Float16*>(X), reinterpret_cast<const uint8_t*>(packed),
+                     reinterpret_cast<const _Float16*>(scales), invperm,
+                     reinterpret_cast<_Float16*>(Y), M, K, N, G, p.u, p.nsa, (int)p.packed_bytes);
+  return hipGetLastError();
+}
+
+// Batch size: the plan's (one group, at most 16 word rows), smaller for
+// larger MT to stay inside the register file.  Any power of two up to the
+// plan's batch divides u, so the packed layout does not depend on it.
+template <int MT, int CPP>
+static hipError_t launch_q4_bw(const void* X, const void* packed, const void* scales,
+                               const int32_t* invperm, void* Y, int M, int K, int N, int G,
+                               const PanelPlan& p, hipStream_t s) {
+  constexpr int cap = MT >= 8 ? 4 : (MT >= 4 ? 8 : 16);
+  const int bw = p.bw < cap ? p.bw : cap;
+  switch (bw) {
+    case 4: return launch_q4_t<MT, CPP, 4>(X, packed, scales, invperm, Y, M, K, N, G, p, s);
+    case 8: return launch_q4_t<MT, CPP, (cap < 8 ? 4 : 8)>(X, packed, scales, invperm, Y, M, K, N, G, p, s);
+    default: return launch_q4_t<MT, CPP, cap>(X, packed, scales, invperm, Y, M, K, N, G, p, s);
   }
 }
 
-hipError_t launch_q4_group(const void* X, const int32_t* qw, const void* scales,
-                           const int32_t* perm, void* Y, int M, int K, int N, int G,
-                           const SplitPlan& p, void* ws, hipStream_t s) {
-  for (int m0 = 0; m0 < M; m0 += p.mt) {
-    const int mc = (M - m0) < p.mt ? (M - m0) : p.mt;
+template <int MT>
+static hipError_t launch_q4_mt(const void* X, const void* packed, const void* scales,
+                               const int32_t* invperm, void* Y, int M, int K, int N, int G,
+                               const PanelPlan& p, hipStream_t s) {
+  switch (p.cpp) {
+    case 1: return launch_q4_bw<MT, 1>(X, packed, scales, invperm, Y, M, K, N, G, p, s);
+    case 2: return launch_q4_bw<MT, 2>(X, packed, scales, invperm, Y, M, K, N, G, p, s);
+    case 4: return launch_q4_bw<MT, 4>(X, packed, scales, invperm, Y, M, K, N, G, p, s);
+    default: return launch_q4_bw<MT, 8>(X, packed, scales, invperm, Y, M, K, N, G, p, s);
+  }
+}
+
+hipError_t launch_q4_group(const void* X, const void* packed, const void* scales,
+                           const int32_t* invperm, void* Y, int M, int K, int N, int G,
+                           hipStream_t s) {
+  const PanelPlan p = plan_q4(K, N, G);
+  const int mtmax = q4_max_mt(K);
+  for (int m0 = 0; m0 < M; m0 += mtmax) {
+    const int mc = (M - m0) < mtmax ? (M - m0) : mtmax;
+    const int mt = mc == 1 ? 1 : (mc == 2 ? 2 : (mc <= 4 ? 4 : 8));
     const void* Xc = reinterpret_cast<const char*>(X) + (size_t)m0 * K * 2;
     void* Yc = reinterpret_cast<char*>(Y) + (size_t)m0 * N * 2;
     hipError_t e;
-    switch (p.mt) {
-      case 1: e = launch_q4_mt<1>(Xc, qw, scales, perm, Yc, mc, K, N, G, p, ws, s); break;
-      case 2: e = launch_q4_mt<2>(Xc, qw, scales, perm, Yc, mc, K, N, G, p, ws, s); break;
-      case 4: e = launch_q4_mt<4>(Xc, qw, scales, perm, Yc, mc, K, N, G, p, ws, s); break;
-      default: e = launch_q4_mt<8>(Xc, qw, scales, perm, Yc, mc, K, N, G, p, ws, s); break;
+    switch (mt) {
+      case 1: e = launch_q4_mt<1>(Xc, packed, scales, invperm, Yc, mc, K, N, G, p, s); break;
+      case 2: e = launch_q4_mt<2>(Xc, packed, scales, invperm, Yc, mc, K, N, G, p, s); break;
+      case 4: e = launch_q4_mt<4>(Xc, packed, scales, invperm, Yc, mc, K, N, G, p, s); break;
+      default: e = launch_q4_mt<8>(Xc, packed, scales, invperm, Yc, mc, K, N, G, p, s); break;
     }
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
-}
-
-// ---------------------------------------------------------------------------
-// Offline row reorder: out row i = original row perm[i] (one thread per word).
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void q4_prepack_kernel(const uint32_t* __restrict__ qw,
-                                                              const int* __restrict__ perm,
-                                                              uint32_t* __restrict__ out, int K,
-                                                              int N) {
-  const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
-  const size_t total = (size_t)(K / 8) * N;
-  if (idx >= total) return;
-  const int r = (int)(idx / N), n = (int)(idx % N);
-  uint32_t word = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int src = perm[8 * r + j];
-    const uint32_t sw = qw[(size_t)(src >> 3) * N + n];
-    word |= ((sw >> (4 * (src & 7))) & 15u) << (4 * j);
-  }
-  out[idx] = word;
-}
-
-hipError_t launch_q4_prepack(const int32_t* qw, const int32_t* perm, int32_t* out, int K, int N,
-                             hipStream_t s) {
-  const size_t total = (size_t)(K / 8) * N;
-  const unsigned blocks = (unsigned)((total + kThreads - 1) / kThreads);
-  hipLaunchKernelGGL(q4_prepack_kernel, dim3(blocks), dim3(kThreads), 0, s,
-                     reinterpret_cast<const uint32_t*>(qw), perm, reinterpret_cast<uint32_t*>(out),
-                     K, N);
-  return hipGetLastError();
 }
 
 }  // namespace wq

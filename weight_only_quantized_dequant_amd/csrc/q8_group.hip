@@ -2,203 +2,261 @@
 //
 //   Y[m, n] = sum_g scale[g, n] * sum_{k in group g} X[m, k] * q[k, n]
 //
-// i.e. Y = X.(Wint*Sw) rearranged as (X.Wint)*Sw per group ("Quantization
+// i.e. Y = X.(Wint*Sw) computed as (X.Wint)*Sw per group ("Quantization
 // CUDA", tom-jerr.github.io, section "Int8 Weight Only Quantization"), with
-// the int8 weight dequantised in registers as it is loaded and never stored
+// the int8 weight dequantised in registers as it streams in and never stored
 // as floating point ("融合反量化与GEMM：LLM推理的CUDA内核优化实践",
 // zingnex.cn, sections "核心优化思路" and "技术实现细节": one fp32 scale per 128
 // rows of K per column).
 //
-// Geometry.  A workgroup (4 wave64s) owns a 256-column tile and TK = 16*R
-// rows of K.  Lane (cc, rr) of wave w takes 16 columns (one 128-bit load per
-// row) and a contiguous span of R rows: slot = 4w + rr.  R divides the group
-// size, so each span lies inside one group and is scaled once.  Every lane
-// issues all R of its loads before it converts anything, so the whole tile is
-// in flight at once.  Spans are reduced across the 4 lanes of a wave that
-// share columns (shuffles) and across the 4 waves (LDS), then across the S
-// workgroups of a column tile through the workspace (split-K, fixed order).
+// Layout.  The [K, N] weight is re-laid out once, offline (wq_prepack_q8),
+// into column panels of P = 16*CPP columns.  A workgroup owns one panel over
+// the whole of K, so no partial sum ever leaves the workgroup.  Inside a
+// panel, thread t = s*CPP + c takes the 16 columns of chunk c and the u rows
+// of slot s; the packed order puts the 16-byte piece that thread t reads at
+// step i at ((panel*u + i) * active_threads + t) * 16, so every wave load is
+// 1 KB of contiguous memory.  Codes are stored biased (u = q + 128): the
+// bias is removed with one per-batch sum of x, and the biased byte goes
+// straight into an fp16 mantissa as a subnormal (see q8_pairs_sub).
 #include "wq_device.hpp"
 #include "wq_internal.h"
 
 namespace wq {
 
-template <int MT, int R>
-__global__ __launch_bounds__(kThreads) void q8_group_kernel(
-    const _Float16* __restrict__ X, const int8_t* __restrict__ Wq,
-    const float* __restrict__ scales, _Float16* __restrict__ Y, float* __restrict__ part,
-    unsigned* __restrict__ counters, int M, int K, int N, int G, int S) {
-  constexpr int TK = 16 * R;
-  constexpr int NP = TK / 2;  // row pairs per workgroup
-  __shared__ h2 xs[MT][NP];
-  __shared__ float red[4][MT][kTileN + 4];
-  __shared__ int last_flag;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ct = blockIdx.x / S, s = blockIdx.x % S;
-  const int kb = s * TK;
-  const int cc = lane & 15, rr = lane >> 4;
-  const int slot = wave * 4 + rr;
-  const int k0 = kb + slot * R;
-  const int col0 = ct * kTileN + cc * 16;
-  const bool col_ok = col0 < N;
-
-  // 1. Stream this lane's weight span: R rows x 16 columns.  Rows past K
-  //    and columns past N fall outside the buffer range and read as zero.
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wq, K * N);
-  const int off0 = col_ok ? k0 * N + col0 : kOutOfRange;
-  u32x4 w[R];
-#pragma unroll
-  for (int i = 0; i < R; ++i) w[i] = buffer_stream(wr, col_ok ? off0 + i * N : kOutOfRange);
-
-  // 2. Stage the activations of this K range as fp16 pairs (rows 2p, 2p+1).
-  for (int idx = tid; idx < MT * NP; idx += kThreads) {
-    const int m = idx / NP, p = idx % NP;
-    const int k = kb + 2 * p;
-    uint32_t v = 0;
-    if (m < M && k < K) v = *reinterpret_cast<const uint32_t*>(X + (size_t)m * K + k);
-    xs[m][p] = as_h2(v);
-  }
-  __syncthreads();
-
-  // 3. Dequantise in registers and accumulate in fp32.
-  float acc[MT][16];
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int c = 0; c < 16; ++c) acc[m][c] = 0.0f;
-
-  const int pbase = slot * (R / 2);
-#pragma unroll
-  for (int p = 0; p < R / 2; ++p) {
-    h2 xv[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) xv[m] = xs[m][pbase + p];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      h2 q[4];
-      q8_rowpair_pairs(w[2 * p][d], w[2 * p + 1][d], q);
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int m = 0; m < MT; ++m) acc[m][4 * d + c] = dot2(q[c], xv[m], acc[m][4 * d + c]);
-    }
-  }
-
-  // 4. One scale per (group, column) for the whole span.
-  if (col_ok && k0 < K) {
-    const float* sp = scales + (size_t)(k0 / G) * N + col0;
-    f32x4 sc[4];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) sc[d] = *reinterpret_cast<const f32x4*>(sp + 4 * d);
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int c = 0; c < 16; ++c) acc[m][c] *= sc[c >> 2][c & 3];
-  }
-
-  // 5. Reduce the 4 spans of a wave that share columns (lanes 16 apart).
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      float v = acc[m][c];
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      acc[m][c] = v;
-    }
-  if (rr == 0) {
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int c = 0; c < 16; ++c) red[wave][m][cc * 16 + c] = acc[m][c];
-  }
-  __syncthreads();
-
-  // 6. Across the 4 waves; thread t now owns column t of the tile.
-  const int n = ct * kTileN + tid;
-  float sum[MT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-    sum[m] = (red[0][m][tid] + red[1][m][tid]) + (red[2][m][tid] + red[3][m][tid]);
-
-  if (S == 1) {
-    if (n < N)
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-        if (m < M) Y[(size_t)m * N + n] = (_Float16)sum[m];
-    return;
-  }
-
-  // 7. Split-K: publish, and let the last workgroup of the tile finish.
-  if (n < N)
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-      if (m < M) part[((size_t)s * MT + m) * N + n] = sum[m];
-  if (splitk_arrive(&counters[ct], S, &last_flag)) {
-    if (n < N) {
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        if (m >= M) continue;
-        float t = 0.0f;
-        for (int j = 0; j < S; ++j) t += part[((size_t)j * MT + m) * N + n];
-        Y[(size_t)m * N + n] = (_Float16)t;
-      }
-    }
-    splitk_reset(&counters[ct]);
-  }
-}
-
-// Rows per lane span: as many as the register budget allows (all loads of a
-// lane are in flight together), fewer when that leaves too few workgroups.
-SplitPlan plan_q8(int M, int K, int N, int G) {
-  SplitPlan p;
-  p.mt = M == 1 ? 1 : (M == 2 ? 2 : (M <= 4 ? 4 : 8));
-  p.n_tiles = (N + kTileN - 1) / kTileN;
-  int R = p.mt >= 8 ? 8 : 16;
-  const int ov = env_unit_override();
-  if (ov == 8 || ov == 16 || (ov == 32 && p.mt <= 2)) R = ov;
-  while (R > 8 && G % R) R /= 2;
-  if (G % R) R = 8;  // G % 32 == 0 is required by the ABI, so 8 always divides G
-  p.unit = R;
-  const int TK = 16 * R;
-  p.splits = (K + TK - 1) / TK;
+// Panel plan: a pure function of (K, N); prepack and product agree on it.
+PanelPlan plan_q8(int K, int N) {
+  PanelPlan p{};
+  p.P = (N % 32 == 0 && N / 32 >= 256) ? 32 : 16;
+  p.cpp = p.P / 16;
+  p.npanels = N / p.P;
+  const int ns = kThreads / p.cpp;
+  p.u = 16 * ((K + 16 * ns - 1) / (16 * ns));  // rows per slot, whole 16-row batches
+  p.nsa = (K + p.u - 1) / p.u;                 // slots in use
+  p.packed_bytes = (size_t)p.npanels * p.u * p.nsa * p.cpp * 16;
   return p;
 }
 
-template <int MT, int R>
-static hipError_t launch_one(const void* X, const int8_t* Wq, const float* scales, void* Y, int M,
-                             int K, int N, int G, const SplitPlan& p, void* ws, hipStream_t s) {
-  unsigned* counters = reinterpret_cast<unsigned*>(ws);
-  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + ws_counter_bytes(p.n_tiles));
-  hipLaunchKernelGGL((q8_group_kernel<MT, R>), dim3(p.n_tiles * p.splits), dim3(kThreads), 0, s,
-                     reinterpret_cast<const _Float16*>(X), Wq, scales,
-                     reinterpret_cast<_Float16*>(Y), part, counters, M, K, N, G, p.splits);
+// ---------------------------------------------------------------------------
+// Offline re-layout: one thread per 16-byte output piece.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void q8_prepack_kernel(const int8_t* __restrict__ W,
+                                                              uint32_t* __restrict__ out, int K,
+                                                              int N, PanelPlan p) {
+  const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  const int nta = p.nsa * p.cpp;
+  const size_t total = (size_t)p.npanels * p.u * nta;
+  if (idx >= total) return;
+  const int t = (int)(idx % nta);
+  const size_t pi = idx / nta;
+  const int i = (int)(pi % p.u), panel = (int)(pi / p.u);
+  const int s = t / p.cpp, c = t % p.cpp;
+  const int row = s * p.u + i;
+  const int col0 = panel * p.P + 16 * c;
+  uint32_t v[4] = {0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u};  // padding rows: q = 0
+  if (row < K) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(W + (size_t)row * N + col0);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) v[d] = src[d] ^ 0x80808080u;
+  }
+#pragma unroll
+  for (int d = 0; d < 4; ++d) out[idx * 4 + d] = v[d];
+}
+
+// ---------------------------------------------------------------------------
+// The fused product.
+// ---------------------------------------------------------------------------
+template <int MT, int CPP>
+__global__ __launch_bounds__(kThreads) void q8_panel_kernel(
+    const _Float16* __restrict__ X, const uint8_t* __restrict__ Wp,
+    const float* __restrict__ scales, _Float16* __restrict__ Y, int M, int K, int N, int G,
+    int u, int nsa, int packed_bytes) {
+  constexpr int P = 16 * CPP;
+  constexpr int V = 16 * MT;                // results per chunk: [m][16 columns]
+  constexpr int LOWBIT = CPP == 1 ? 0 : 1;  // lane bit 0 selects the chunk when CPP == 2
+  constexpr int LEFT = bfly_left<V, LOWBIT>();
+  __shared__ float red[kThreads / 64][CPP][V];
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int panel = blockIdx.x;
+  const int nta = nsa * CPP;
+  const int c = t % CPP, s = t / CPP;
+  const bool active = t < nta;
+  const int col0 = panel * P + 16 * c;
+
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wp, packed_bytes);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, M * K * 2);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, (K / G) * N * 4);
+  const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+
+  float accT[MT][16];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) accT[m][j] = 0.0f;
+
+  const int nb = u / 16;
+  for (int b = 0; b < nb; ++b) {
+    const int row0 = s * u + 16 * b;
+    const bool live = active && row0 < K;
+    // Activations of these 16 rows: two 128-bit loads per row of X.
+    u32x4 xv[MT][2];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        xv[m][h] = __builtin_amdgcn_raw_buffer_load_b128(
+            xr, (live && m < M) ? ((m * K + row0 + 8 * h) * 2) : kOutOfRange, 0, 0);
+    // The weight stream: 16 rows x 16 columns; 1 KB contiguous per wave load.
+    u32x4 w[16];
+    const int wbase = ((panel * u + 16 * b) * nta + t) * 16;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i] = buffer_stream(wr, active ? wbase + i * nta * 16 : kOutOfRange);
+    f32x4 sc[4];
+    const int soff = live ? ((row0 / G) * N + col0) * 4 : kOutOfRange;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      sc[d] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, soff + 16 * d, 0, 0));
+
+    // The codes are u = q + 128, so every column starts at -128 * sum(x),
+    // in the 2^-24 units of the subnormal products.
+    float acc[MT][16];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      float xs = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) xs = dot2(as_h2(xv[m][q >> 2][q & 3]), ones, xs);
+      const float b0 = xs * (-128.0f / kTwo24);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[m][j] = b0;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {  // row pair (2q, 2q + 1)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        h2 pr[4];
+        q8_pairs_sub(w[2 * q][d], w[2 * q + 1][d], pr);
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+            acc[m][4 * d + cc] = dot2(pr[cc], as_h2(xv[m][q >> 2][q & 3]), acc[m][4 * d + cc]);
+      }
+    }
+    // One group per 16-row batch: scale once.
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) accT[m][j] = __builtin_fmaf(acc[m][j], sc[j >> 2][j & 3], accT[m][j]);
+  }
+
+  // Reduce over the slots of a chunk: the lanes of a wave, then the 4 waves.
+  float v[V];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[m * 16 + j] = accT[m][j];
+  bfly<V, 5, LOWBIT>(v, lane);
+  bool owner;
+  const int base = bfly_base<V, LOWBIT>(lane, owner);
+  if (owner) {
+#pragma unroll
+    for (int j = 0; j < LEFT; ++j) red[wave][c][base + j] = v[j];
+  }
+  __syncthreads();
+  for (int r = t; r < CPP * V; r += kThreads) {
+    const int rc = r / V, idx = r % V;
+    const int m = idx / 16, col = panel * P + 16 * rc + (idx % 16);
+    float sum = 0.0f;
+#pragma unroll
+    for (int w2 = 0; w2 < kThreads / 64; ++w2) sum += red[w2][rc][idx];
+    if (m < M) Y[(size_t)m * N + col] = (_Float16)(sum * kTwo24);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Bit-exact check of the packed layout: rows (2q, 2q+1) of a slot go through
+// q8_pairs_sub and are written back as signed codes.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void q8_unpack_kernel(const uint8_t* __restrict__ Wp,
+                                                             int8_t* __restrict__ codes, int K,
+                                                             int N, PanelPlan p) {
+  const int nta = p.nsa * p.cpp;
+  const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  const size_t total = (size_t)p.npanels * (p.u / 2) * nta;
+  if (idx >= total) return;
+  const int t = (int)(idx % nta);
+  const size_t pi = idx / nta;
+  const int q = (int)(pi % (p.u / 2)), panel = (int)(pi / (p.u / 2));
+  const int s = t / p.cpp, c = t % p.cpp;
+  const int row = s * p.u + 2 * q;
+  const int col0 = panel * p.P + 16 * c;
+  const u32x4 a = *reinterpret_cast<const u32x4*>(Wp + (((size_t)panel * p.u + 2 * q) * nta + t) * 16);
+  const u32x4 b =
+      *reinterpret_cast<const u32x4*>(Wp + (((size_t)panel * p.u + 2 * q + 1) * nta + t) * 16);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    h2 pr[4];
+    q8_pairs_sub(a[d], b[d], pr);
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const uint32_t bits = as_u32(pr[cc]);
+      const int ua = (int)(bits & 0xFFFFu), ub = (int)(bits >> 16);
+      const int col = col0 + 4 * d + cc;
+      if (row < K) codes[(size_t)row * N + col] = (int8_t)(ua - 128);
+      if (row + 1 < K) codes[(size_t)(row + 1) * N + col] = (int8_t)(ub - 128);
+    }
+  }
+}
+
+hipError_t launch_q8_prepack(const int8_t* W, void* packed, int K, int N, hipStream_t s) {
+  const PanelPlan p = plan_q8(K, N);
+  const size_t total = (size_t)p.npanels * p.u * p.nsa * p.cpp;
+  hipLaunchKernelGGL(q8_prepack_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, W, reinterpret_cast<uint32_t*>(packed), K, N, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_q8_unpack(const void* packed, int8_t* codes, int K, int N, hipStream_t s) {
+  const PanelPlan p = plan_q8(K, N);
+  const size_t total = (size_t)p.npanels * (p.u / 2) * p.nsa * p.cpp;
+  hipLaunchKernelGGL(q8_unpack_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, reinterpret_cast<const uint8_t*>(packed), codes, K, N,
+                     p);
+  return hipGetLastError();
+}
+
+template <int MT, int CPP>
+static hipError_t launch_q8_t(const void* X, const void* packed, const float* scales, void* Y,
+                              int M, int K, int N, int G, const PanelPlan& p, hipStream_t s) {
+  hipLaunchKernelGGL((q8_panel_kernel<MT, CPP>), dim3(p.npanels), dim3(kThreads), 0, s,
+                     reinterpret_cast<const _Float16*>(X), reinterpret_cast<const uint8_t*>(packed),
+                     scales, reinterpret_cast<_Float16*>(Y), M, K, N, G, p.u, p.nsa,
+                     (int)p.packed_bytes);
   return hipGetLastError();
 }
 
 template <int MT>
-static hipError_t launch_mt(const void* X, const int8_t* Wq, const float* scales, void* Y, int M,
-                            int K, int N, int G, const SplitPlan& p, void* ws, hipStream_t s) {
-  switch (p.unit) {
-    case 8: return launch_one<MT, 8>(X, Wq, scales, Y, M, K, N, G, p, ws, s);
-    case 16: return launch_one<MT, 16>(X, Wq, scales, Y, M, K, N, G, p, ws, s);
-    default: return launch_one<MT, (MT <= 2 ? 32 : 16)>(X, Wq, scales, Y, M, K, N, G, p, ws, s);
-  }
+static hipError_t launch_q8_mt(const void* X, const void* packed, const float* scales, void* Y,
+                               int M, int K, int N, int G, const PanelPlan& p, hipStream_t s) {
+  return p.cpp == 1 ? launch_q8_t<MT, 1>(X, packed, scales, Y, M, K, N, G, p, s)
+                    : launch_q8_t<MT, 2>(X, packed, scales, Y, M, K, N, G, p, s);
 }
 
-hipError_t launch_q8_group(const void* X, const int8_t* Wq, const float* scales, void* Y, int M,
-                           int K, int N, int G, const SplitPlan& p, void* ws, hipStream_t s) {
-  // Rows of X beyond the per-launch tile height run as further launches.
-  for (int m0 = 0; m0 < M; m0 += p.mt) {
-    const int mc = (M - m0) < p.mt ? (M - m0) : p.mt;
+hipError_t launch_q8_group(const void* X, const void* packed, const float* scales, void* Y, int M,
+                           int K, int N, int G, hipStream_t s) {
+  const PanelPlan p = plan_q8(K, N);
+  // Rows of X beyond 8 run as further launches over the same panels.
+  for (int m0 = 0; m0 < M; m0 += 8) {
+    const int mc = (M - m0) < 8 ? (M - m0) : 8;
+    const int mt = mc == 1 ? 1 : (mc == 2 ? 2 : (mc <= 4 ? 4 : 8));
     const void* Xc = reinterpret_cast<const char*>(X) + (size_t)m0 * K * 2;
     void* Yc = reinterpret_cast<char*>(Y) + (size_t)m0 * N * 2;
     hipError_t e;
-    switch (p.mt) {
-      case 1: e = launch_mt<1>(Xc, Wq, scales, Yc, mc, K, N, G, p, ws, s); break;
-      case 2: e = launch_mt<2>(Xc, Wq, scales, Yc, mc, K, N, G, p, ws, s); break;
-      case 4: e = launch_mt<4>(Xc, Wq, scales, Yc, mc, K, N, G, p, ws, s); break;
-      default: e = launch_mt<8>(Xc, Wq, scales, Yc, mc, K, N, G, p, ws, s); break;
+    switch (mt) {
+      case 1: e = launch_q8_mt<1>(Xc, packed, scales, Yc, mc, K, N, G, p, s); break;
+      case 2: e = launch_q8_mt<2>(Xc, packed, scales, Yc, mc, K, N, G, p, s); break;
+      case 4: e = launch_q8_mt<4>(Xc, packed, scales, Yc, mc, K, N, G, p, s); break;
+      default: e = launch_q8_mt<8>(Xc, packed, scales, Yc, mc, K, N, G, p, s); break;
     }
     if (e != hipSuccess) return e;
   }

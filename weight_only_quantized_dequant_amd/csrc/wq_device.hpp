@@ -1,14 +1,15 @@
 // Device helpers shared by the fused dequantize-and-multiply kernels (gfx950).
 //
-// Code -> fp16 conversion.  A binary16 value whose exponent field is that of
-// 1024 (bit pattern 0x6400) and whose 10 mantissa bits hold an integer v reads
-// exactly 1024 + v.  So a packed code masked into the mantissa of each half of
-// a 32-bit register, OR-ed with 0x64006400 (one v_and_or_b32), is a pair of
-// exact fp16 values; one packed fp16 FMA (x * 2^-p - 1024 * 2^-p - offset)
-// then recovers the signed code exactly, and v_dot2_f32_f16 multiplies the
-// pair with a pair of fp16 activations and accumulates in fp32.  Products of
-// an fp16 activation and a code of at most 8 bits are exact in fp32, so only
-// the fp32 accumulation rounds.
+// Code -> fp16 conversion without arithmetic.  A 32-bit register whose two
+// halves have a zero exponent field and an integer v (< 1024) in the mantissa
+// is the pair of fp16 subnormals (v_lo * 2^-24, v_hi * 2^-24), exactly.  So a
+// packed code masked into the mantissa of each half (one v_and_b32, or one
+// v_perm_b32 for bytes) is already an exact fp16 pair, and v_dot2_f32_f16
+// (which keeps fp16 subnormals: checked on gfx950) multiplies it with a pair
+// of fp16 activations and accumulates in fp32.  The 2^-24 and any bit offset
+// 2^p of the code inside the mantissa are powers of two, folded into one
+// scale at the end.  Products of an fp16 activation and a code of at most 8
+// bits are exact in fp32, so only the fp32 accumulation rounds.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -21,6 +22,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kMagic2 = 0x64006400u;  // fp16 1024.0 in both halves
+constexpr float kTwo24 = 16777216.0f;      // 2^24: undoes the subnormal scale
 
 __device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
@@ -159,6 +161,130 @@ __device__ __forceinline__ void q8_rowpair_pairs(uint32_t ra, uint32_t rb, h2 ou
   out[1] = as_h2(p1) + bias;
   out[2] = as_h2(p2) + bias;
   out[3] = as_h2(p3) + bias;
+}
+
+// ---------------------------------------------------------------------------
+// Subnormal-pair extractors (the fast path).  Values are in units of 2^-24.
+// ---------------------------------------------------------------------------
+
+// int8, stored biased as u = q + 128: words ra, rb hold 4 consecutive
+// columns of rows k and k+1; out[c] = (u[k][c], u[k+1][c]) * 2^-24.  One
+// v_perm_b32 per pair (byte c of each row into the low byte of each half).
+__device__ __forceinline__ void q8_pairs_sub(uint32_t ra, uint32_t rb, h2 out[4]) {
+  out[0] = as_h2(__builtin_amdgcn_perm(ra, rb, 0x0c000c04u));
+  out[1] = as_h2(__builtin_amdgcn_perm(ra, rb, 0x0c010c05u));
+  out[2] = as_h2(__builtin_amdgcn_perm(ra, rb, 0x0c020c06u));
+  out[3] = as_h2(__builtin_amdgcn_perm(ra, rb, 0x0c030c07u));
+}
+
+// 4-bit, u = q + 8: pairs (j, j+4).  out[0], out[2]: (u_j, u_j+4) * 2^-24
+// (j = 0, 2); out[1], out[3]: (u_j, u_j+4) * 2^-20 (j = 1, 3; nibble at bit 4
+// of each half).
+__device__ __forceinline__ void q4_pairs_sub(uint32_t w, h2 out[4]) {
+  const uint32_t w8 = w >> 8;
+  out[0] = as_h2(w & 0x000F000Fu);
+  out[1] = as_h2(w & 0x00F000F0u);
+  out[2] = as_h2(w8 & 0x000F000Fu);
+  out[3] = as_h2(w8 & 0x00F000F0u);
+}
+
+// 3-bit: pair P of q3_pair(P) as (c_a * 2^pa, c_b * 2^pb) * 2^-24.
+template <int P>
+__device__ __forceinline__ h2 q3_pair_sub(uint32_t w0, uint32_t w1, uint32_t w2) {
+  constexpr Q3Pair q = q3_pair(P);
+  constexpr uint32_t mask = (7u << q.pa) | (7u << (16 + q.pb));
+  return as_h2(q3_window<q.src>(w0, w1, w2) & mask);
+}
+
+// Accumulation class of a 3-bit pair: the larger of its two mantissa
+// offsets.  The activation pair is pre-scaled by (2^(cls-pa), 2^(cls-pb)) so
+// both products carry the same factor 2^(cls-24).
+__host__ __device__ constexpr int q3_class(int P) {
+  return q3_pair(P).pa > q3_pair(P).pb ? q3_pair(P).pa : q3_pair(P).pb;
+}
+// Classes in use (1, 2, 4, 5, 7) -> accumulator slot 0..4.
+__host__ __device__ constexpr int q3_class_slot(int cls) {
+  return cls == 1 ? 0 : cls == 2 ? 1 : cls == 4 ? 2 : cls == 5 ? 3 : 4;
+}
+constexpr int kQ3Classes = 5;
+__host__ __device__ constexpr int q3_slot_class(int slot) {
+  return slot == 0 ? 1 : slot == 1 ? 2 : slot == 2 ? 4 : slot == 3 ? 5 : 7;
+}
+
+template <int P>
+__device__ __forceinline__ void q3_block_sub_one(uint32_t w0, uint32_t w1, uint32_t w2, h2* out) {
+  out[P] = q3_pair_sub<P>(w0, w1, w2);
+}
+__device__ __forceinline__ void q3_block_pairs_sub(uint32_t w0, uint32_t w1, uint32_t w2, h2 out[16]) {
+  q3_block_sub_one<0>(w0, w1, w2, out);
+  q3_block_sub_one<1>(w0, w1, w2, out);
+  q3_block_sub_one<2>(w0, w1, w2, out);
+  q3_block_sub_one<3>(w0, w1, w2, out);
+  q3_block_sub_one<4>(w0, w1, w2, out);
+  q3_block_sub_one<5>(w0, w1, w2, out);
+  q3_block_sub_one<6>(w0, w1, w2, out);
+  q3_block_sub_one<7>(w0, w1, w2, out);
+  q3_block_sub_one<8>(w0, w1, w2, out);
+  q3_block_sub_one<9>(w0, w1, w2, out);
+  q3_block_sub_one<10>(w0, w1, w2, out);
+  q3_block_sub_one<11>(w0, w1, w2, out);
+  q3_block_sub_one<12>(w0, w1, w2, out);
+  q3_block_sub_one<13>(w0, w1, w2, out);
+  q3_block_sub_one<14>(w0, w1, w2, out);
+  q3_block_sub_one<15>(w0, w1, w2, out);
+}
+
+// ---------------------------------------------------------------------------
+// Transpose-butterfly reduction over lane bits [LOWBIT, 6) of a wave64.
+// Every lane enters with V values; lanes that differ only in those bits hold
+// partials of the same V results.  Each step halves the values a lane keeps
+// (the half picked by that lane bit) and adds the partner's matching half, so
+// the work is V/2 + V/4 + ... shuffles instead of V per bit.  On exit value j
+// of a lane is result index j + base (bfly_base), summed over all lanes that
+// share the lane bits below LOWBIT; lanes whose leftover bits are not zero
+// hold duplicates.
+// ---------------------------------------------------------------------------
+template <int V, int BIT, int LOWBIT>
+__device__ __forceinline__ void bfly(float* v, int lane) {
+  if constexpr (BIT >= LOWBIT) {
+    if constexpr (V > 1) {
+      const bool hi = (lane >> BIT) & 1;
+#pragma unroll
+      for (int j = 0; j < V / 2; ++j) {
+        const float mine = hi ? v[V / 2 + j] : v[j];
+        const float other = hi ? v[j] : v[V / 2 + j];
+        v[j] = mine + __shfl_xor(other, 1 << BIT);
+      }
+      bfly<V / 2, BIT - 1, LOWBIT>(v, lane);
+    } else {
+      v[0] += __shfl_xor(v[0], 1 << BIT);
+      bfly<1, BIT - 1, LOWBIT>(v, lane);
+    }
+  }
+}
+// Values left per lane after bfly<V, 5, LOWBIT>.
+template <int V, int LOWBIT>
+__host__ __device__ constexpr int bfly_left() {
+  int v = V;
+  for (int b = 5; b >= LOWBIT && v > 1; --b) v /= 2;
+  return v;
+}
+// Result index of a lane's value 0, and whether this lane is the one that
+// stores it (its non-transposing reduction bits are zero).
+template <int V, int LOWBIT>
+__device__ __forceinline__ int bfly_base(int lane, bool& owner) {
+  int base = 0, v = V;
+  owner = true;
+  for (int b = 5; b >= LOWBIT; --b) {
+    const int bitv = (lane >> b) & 1;
+    if (v > 1) {
+      v /= 2;
+      base += bitv * v;
+    } else if (bitv) {
+      owner = false;
+    }
+  }
+  return base;
 }
 
 // ---------------------------------------------------------------------------
