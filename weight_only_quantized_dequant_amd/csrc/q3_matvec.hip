@@ -101,37 +101,73 @@ __global__ __launch_bounds__(kThreads) void q3_panel_kernel(
     return buffer_stream(wr, (i < nblk) ? ((((panel * u + i) * nta + t) * 3 + j) * 16) : kOutOfRange);
   };
 
-  // 1. First UB blocks of the weight stream.
+  // 1. Activations first (thread t stages blocks t, t + 256, ...): all the
+  //    loads of the first XR rounds go out together, ahead of the weights.
+  constexpr int XV = F16 ? 4 : 8;  // 16-byte loads per 32-row block of x
+  constexpr int XR = 2;
+  const __amdgpu_buffer_rsrc_t xr_rsrc = make_rsrc(xv, K * (F16 ? 2 : 4));
+  u32x4 xraw[XR][XV];
+#pragma unroll
+  for (int r = 0; r < XR; ++r) {
+    const int blk = t + r * kThreads;
+#pragma unroll
+    for (int v = 0; v < XV; ++v)
+      xraw[r][v] = __builtin_amdgcn_raw_buffer_load_b128(
+          xr_rsrc, blk < ku ? (blk * XV + v) * 16 : kOutOfRange, 0, 0);
+  }
+
+  // 2. The first UB blocks of the weight stream.
   u32x4 w[UB][3];
 #pragma unroll
   for (int i = 0; i < UB; ++i)
 #pragma unroll
     for (int j = 0; j < 3; ++j) w[i][j] = wload(i, j);
 
-  // 2. Stage x in pair order (pre-scaled) and form sum_k x[k].
+  // 3. Pairs into LDS in code-pair order (pre-scaled), and sum_k x[k].
   float my_sum = 0.0f;
-  for (int e = t; e < K / 2; e += kThreads) {
-    const int blk = e >> 4, P = e & 15;
-    const Q3Pair q = q3_pair(P);
-    float a, b;
-    if constexpr (F16) {
-      a = (float)reinterpret_cast<const _Float16*>(xv)[32 * blk + q.a];
-      b = (float)reinterpret_cast<const _Float16*>(xv)[32 * blk + q.b];
-    } else {
-      a = reinterpret_cast<const float*>(xv)[32 * blk + q.a];
-      b = reinterpret_cast<const float*>(xv)[32 * blk + q.b];
+  auto stage_block = [&](int blk, const u32x4* raw) {
+    float xs[32];
+#pragma unroll
+    for (int v = 0; v < XV; ++v)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (F16) {
+          const h2 hv = as_h2(raw[v][e]);
+          xs[8 * v + 2 * e] = (float)hv.x;
+          xs[8 * v + 2 * e + 1] = (float)hv.y;
+        } else {
+          xs[4 * v + e] = as_f32(raw[v][e]);
+        }
+      }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) my_sum += xs[i];
+#pragma unroll
+    for (int P = 0; P < 16; ++P) {
+      const Q3Pair q = q3_pair(P);
+      if constexpr (F16) {
+        // class = max(pa, pb): the half with the smaller offset is divided by 2^d.
+        const int cls = q3_class(P);
+        const h2 hv = {(_Float16)__builtin_ldexpf(xs[q.a], cls - q.pa),
+                       (_Float16)__builtin_ldexpf(xs[q.b], cls - q.pb)};
+        xp[blk * 16 + P] = as_u32(hv);
+      } else {
+        // fp32: undo the 2^(p - 24) of each subnormal code in the activation.
+        xp[(blk * 16 + P) * 2] = __builtin_bit_cast(uint32_t, __builtin_ldexpf(xs[q.a], 24 - q.pa));
+        xp[(blk * 16 + P) * 2 + 1] = __builtin_bit_cast(uint32_t, __builtin_ldexpf(xs[q.b], 24 - q.pb));
+      }
     }
-    my_sum += a + b;
-    if constexpr (F16) {
-      // class = max(pa, pb): the half with the smaller offset is divided by 2^d.
-      const int cls = q.pa > q.pb ? q.pa : q.pb;
-      const h2 v = {(_Float16)__builtin_ldexpf(a, cls - q.pa), (_Float16)__builtin_ldexpf(b, cls - q.pb)};
-      xp[e] = as_u32(v);
-    } else {
-      // fp32: undo the 2^(p - 24) of each subnormal code in the activation.
-      xp[2 * e] = __builtin_bit_cast(uint32_t, __builtin_ldexpf(a, 24 - q.pa));
-      xp[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_ldexpf(b, 24 - q.pb));
-    }
+  };
+#pragma unroll
+  for (int r = 0; r < XR; ++r) {
+    const int blk = t + r * kThreads;
+    if (blk < ku) stage_block(blk, xraw[r]);
+  }
+  for (int blk = t + XR * kThreads; blk < ku; blk += kThreads) {  // K > 16384 only
+    u32x4 raw[XV];
+#pragma unroll
+    for (int v = 0; v < XV; ++v)
+      raw[v] = __builtin_amdgcn_raw_buffer_load_b128(xr_rsrc, (blk * XV + v) * 16, 0, 0);
+    stage_block(blk, raw);
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) my_sum += __shfl_xor(my_sum, o);

@@ -137,25 +137,41 @@ __global__ __launch_bounds__(kThreads) void q4_panel_kernel(
   load_batch(w, 0);
 
   // 2. Scatter X into LDS through the inverse permutation (group order).
-  for (int e = t * 8; e < MT * K; e += kThreads * 8) {
-    const int m = e / K, k = e % K;
-    u32x4 xv = {0u, 0u, 0u, 0u};
-    if (m < M) xv = *reinterpret_cast<const u32x4*>(X + (size_t)m * K + k);
-    int dst[8];
-    if (invperm) {
-      const u32x4 p0 = *reinterpret_cast<const u32x4*>(invperm + k);
-      const u32x4 p1 = *reinterpret_cast<const u32x4*>(invperm + k + 4);
+  //    Thread t takes the 8-row chunks t, t + 256, ...; for each chunk the
+  //    permutation is read once and reused for every row of X.  All loads of
+  //    a round of chunks go out before any LDS write.
+  constexpr int CR = MT >= 8 ? 1 : 2;  // chunks per thread per round
+  const int nchunk = K / 8;
+  for (int c0 = t; c0 < nchunk; c0 += CR * kThreads) {
+    u32x4 pv[CR][2], xq[CR][MT];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) { dst[j] = (int)p0[j]; dst[4 + j] = (int)p1[j]; }
-    } else {
+    for (int r = 0; r < CR; ++r) {
+      const int ch = c0 + r * kThreads;
+      const bool ok = ch < nchunk;
+      if (invperm) {
+        pv[r][0] = ok ? *reinterpret_cast<const u32x4*>(invperm + 8 * ch) : (u32x4){0u, 0u, 0u, 0u};
+        pv[r][1] = ok ? *reinterpret_cast<const u32x4*>(invperm + 8 * ch + 4) : (u32x4){0u, 0u, 0u, 0u};
+      }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) dst[j] = k + j;
+      for (int m = 0; m < MT; ++m)
+        xq[r][m] = (ok && m < M) ? *reinterpret_cast<const u32x4*>(X + (size_t)m * K + 8 * ch)
+                                 : (u32x4){0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t word = xv[j >> 1];
-      const uint16_t bits = (j & 1) ? (uint16_t)(word >> 16) : (uint16_t)(word & 0xFFFFu);
-      reinterpret_cast<uint16_t*>(xh)[(size_t)m * kpad + q4_lds_half(dst[j])] = bits;
+    for (int r = 0; r < CR; ++r) {
+      const int ch = c0 + r * kThreads;
+      if (ch >= nchunk) break;
+      int dst[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dst[j] = invperm ? (int)pv[r][j >> 2][j & 3] : 8 * ch + j;
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t word = xq[r][m][j >> 1];
+          const uint16_t bits = (j & 1) ? (uint16_t)(word >> 16) : (uint16_t)(word & 0xFFFFu);
+          reinterpret_cast<uint16_t*>(xh)[(size_t)m * kpad + q4_lds_half(dst[j])] = bits;
+        }
     }
   }
   __syncthreads();

@@ -13,15 +13,21 @@
 // into column panels of P = 16*CPP columns.  A workgroup owns one panel over
 // the whole of K, so no partial sum ever leaves the workgroup.  Inside a
 // panel, thread t = s*CPP + c takes the 16 columns of chunk c and the u rows
-// of slot s; the packed order puts the 16-byte piece that thread t reads at
-// step i at ((panel*u + i) * active_threads + t) * 16, so every wave load is
-// 1 KB of contiguous memory.  Codes are stored biased (u = q + 128): the
-// bias is removed with one per-batch sum of x, and the biased byte goes
-// straight into an fp16 mantissa as a subnormal (see q8_pairs_sub).
+// of slot s, in batches of 8 rows; the packed order puts the 16-byte piece
+// that thread t reads at step i at ((panel*u + i) * active_threads + t) * 16,
+// so every wave load is 1 KB of contiguous memory.  Codes are stored biased
+// (u = q + 128): the bias is removed with one per-batch sum of x, and the
+// biased byte goes straight into an fp16 mantissa as a subnormal (see
+// q8_pairs_sub).
 #include "wq_device.hpp"
 #include "wq_internal.h"
 
 namespace wq {
+
+// 512 threads (8 wave64s, two per SIMD): while one wave of a SIMD converts
+// its codes the other's loads are still landing.
+constexpr int kQ8Threads = 512;
+constexpr int kQ8Batch = 8;  // rows per batch (never straddles a group: G % 32 == 0)
 
 // Panel plan: a pure function of (K, N); prepack and product agree on it.
 PanelPlan plan_q8(int K, int N) {
@@ -29,9 +35,9 @@ PanelPlan plan_q8(int K, int N) {
   p.P = (N % 32 == 0 && N / 32 >= 256) ? 32 : 16;
   p.cpp = p.P / 16;
   p.npanels = N / p.P;
-  const int ns = kThreads / p.cpp;
-  p.u = 16 * ((K + 16 * ns - 1) / (16 * ns));  // rows per slot, whole 16-row batches
-  p.nsa = (K + p.u - 1) / p.u;                 // slots in use
+  const int ns = kQ8Threads / p.cpp;
+  p.u = kQ8Batch * ((K + kQ8Batch * ns - 1) / (kQ8Batch * ns));  // rows per slot
+  p.nsa = (K + p.u - 1) / p.u;                                     // slots in use
   p.packed_bytes = (size_t)p.npanels * p.u * p.nsa * p.cpp * 16;
   return p;
 }
@@ -66,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void q8_prepack_kernel(const int8_t* __re
 // The fused product.
 // ---------------------------------------------------------------------------
 template <int MT, int CPP>
-__global__ __launch_bounds__(kThreads) void q8_panel_kernel(
+__global__ __launch_bounds__(kQ8Threads) void q8_panel_kernel(
     const _Float16* __restrict__ X, const uint8_t* __restrict__ Wp,
     const float* __restrict__ scales, _Float16* __restrict__ Y, int M, int K, int N, int G,
     int u, int nsa, int packed_bytes) {
@@ -74,7 +80,8 @@ __global__ __launch_bounds__(kThreads) void q8_panel_kernel(
   constexpr int V = 16 * MT;                // results per chunk: [m][16 columns]
   constexpr int LOWBIT = CPP == 1 ? 0 : 1;  // lane bit 0 selects the chunk when CPP == 2
   constexpr int LEFT = bfly_left<V, LOWBIT>();
-  __shared__ float red[kThreads / 64][CPP][V];
+  constexpr int RB = kQ8Batch;
+  __shared__ float red[kQ8Threads / 64][CPP][V];
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int panel = blockIdx.x;
@@ -94,23 +101,21 @@ __global__ __launch_bounds__(kThreads) void q8_panel_kernel(
 #pragma unroll
     for (int j = 0; j < 16; ++j) accT[m][j] = 0.0f;
 
-  const int nb = u / 16;
+  const int nb = u / RB;
   for (int b = 0; b < nb; ++b) {
-    const int row0 = s * u + 16 * b;
+    const int row0 = s * u + RB * b;
     const bool live = active && row0 < K;
-    // Activations of these 16 rows: two 128-bit loads per row of X.
-    u32x4 xv[MT][2];
+    // Activations of these 8 rows: one 128-bit load per row of X.
+    u32x4 xv[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
+      xv[m] = __builtin_amdgcn_raw_buffer_load_b128(
+          xr, (live && m < M) ? ((m * K + row0) * 2) : kOutOfRange, 0, 0);
+    // The weight stream: 8 rows x 16 columns; 1 KB contiguous per wave load.
+    u32x4 w[RB];
+    const int wbase = ((panel * u + RB * b) * nta + t) * 16;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        xv[m][h] = __builtin_amdgcn_raw_buffer_load_b128(
-            xr, (live && m < M) ? ((m * K + row0 + 8 * h) * 2) : kOutOfRange, 0, 0);
-    // The weight stream: 16 rows x 16 columns; 1 KB contiguous per wave load.
-    u32x4 w[16];
-    const int wbase = ((panel * u + 16 * b) * nta + t) * 16;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) w[i] = buffer_stream(wr, active ? wbase + i * nta * 16 : kOutOfRange);
+    for (int i = 0; i < RB; ++i) w[i] = buffer_stream(wr, active ? wbase + i * nta * 16 : kOutOfRange);
     f32x4 sc[4];
     const int soff = live ? ((row0 / G) * N + col0) * 4 : kOutOfRange;
 #pragma unroll
@@ -124,13 +129,13 @@ __global__ __launch_bounds__(kThreads) void q8_panel_kernel(
     for (int m = 0; m < MT; ++m) {
       float xs = 0.0f;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) xs = dot2(as_h2(xv[m][q >> 2][q & 3]), ones, xs);
+      for (int q = 0; q < RB / 2; ++q) xs = dot2(as_h2(xv[m][q]), ones, xs);
       const float b0 = xs * (-128.0f / kTwo24);
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[m][j] = b0;
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {  // row pair (2q, 2q + 1)
+    for (int q = 0; q < RB / 2; ++q) {  // row pair (2q, 2q + 1)
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         h2 pr[4];
@@ -139,17 +144,17 @@ __global__ __launch_bounds__(kThreads) void q8_panel_kernel(
         for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
           for (int m = 0; m < MT; ++m)
-            acc[m][4 * d + cc] = dot2(pr[cc], as_h2(xv[m][q >> 2][q & 3]), acc[m][4 * d + cc]);
+            acc[m][4 * d + cc] = dot2(pr[cc], as_h2(xv[m][q]), acc[m][4 * d + cc]);
       }
     }
-    // One group per 16-row batch: scale once.
+    // One group per batch: scale once.
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int j = 0; j < 16; ++j) accT[m][j] = __builtin_fmaf(acc[m][j], sc[j >> 2][j & 3], accT[m][j]);
   }
 
-  // Reduce over the slots of a chunk: the lanes of a wave, then the 4 waves.
+  // Reduce over the slots of a chunk: the lanes of a wave, then the waves.
   float v[V];
 #pragma unroll
   for (int m = 0; m < MT; ++m)
@@ -163,12 +168,12 @@ __global__ __launch_bounds__(kThreads) void q8_panel_kernel(
     for (int j = 0; j < LEFT; ++j) red[wave][c][base + j] = v[j];
   }
   __syncthreads();
-  for (int r = t; r < CPP * V; r += kThreads) {
+  for (int r = t; r < CPP * V; r += kQ8Threads) {
     const int rc = r / V, idx = r % V;
     const int m = idx / 16, col = panel * P + 16 * rc + (idx % 16);
     float sum = 0.0f;
 #pragma unroll
-    for (int w2 = 0; w2 < kThreads / 64; ++w2) sum += red[w2][rc][idx];
+    for (int w2 = 0; w2 < kQ8Threads / 64; ++w2) sum += red[w2][rc][idx];
     if (m < M) Y[(size_t)m * N + col] = (_Float16)(sum * kTwo24);
   }
 }
@@ -228,7 +233,7 @@ hipError_t launch_q8_unpack(const void* packed, int8_t* codes, int K, int N, hip
 template <int MT, int CPP>
 static hipError_t launch_q8_t(const void* X, const void* packed, const float* scales, void* Y,
                               int M, int K, int N, int G, const PanelPlan& p, hipStream_t s) {
-  hipLaunchKernelGGL((q8_panel_kernel<MT, CPP>), dim3(p.npanels), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((q8_panel_kernel<MT, CPP>), dim3(p.npanels), dim3(kQ8Threads), 0, s,
                      reinterpret_cast<const _Float16*>(X), reinterpret_cast<const uint8_t*>(packed),
                      scales, reinterpret_cast<_Float16*>(Y), M, K, N, G, p.u, p.nsa,
                      (int)p.packed_bytes);
@@ -245,18 +250,18 @@ static hipError_t launch_q8_mt(const void* X, const void* packed, const float* s
 hipError_t launch_q8_group(const void* X, const void* packed, const float* scales, void* Y, int M,
                            int K, int N, int G, hipStream_t s) {
   const PanelPlan p = plan_q8(K, N);
-  // Rows of X beyond 8 run as further launches over the same panels.
-  for (int m0 = 0; m0 < M; m0 += 8) {
-    const int mc = (M - m0) < 8 ? (M - m0) : 8;
-    const int mt = mc == 1 ? 1 : (mc == 2 ? 2 : (mc <= 4 ? 4 : 8));
+  // Rows of X beyond 4 run as further launches over the same panels (the
+  // accumulators of 4 rows x 16 columns x 2 fill the register budget of a
+  // 512-thread workgroup).
+  for (int m0 = 0; m0 < M; m0 += 4) {
+    const int mc = (M - m0) < 4 ? (M - m0) : 4;
     const void* Xc = reinterpret_cast<const char*>(X) + (size_t)m0 * K * 2;
     void* Yc = reinterpret_cast<char*>(Y) + (size_t)m0 * N * 2;
     hipError_t e;
-    switch (mt) {
+    switch (mc) {
       case 1: e = launch_q8_mt<1>(Xc, packed, scales, Yc, mc, K, N, G, p, s); break;
       case 2: e = launch_q8_mt<2>(Xc, packed, scales, Yc, mc, K, N, G, p, s); break;
-      case 4: e = launch_q8_mt<4>(Xc, packed, scales, Yc, mc, K, N, G, p, s); break;
-      default: e = launch_q8_mt<8>(Xc, packed, scales, Yc, mc, K, N, G, p, s); break;
+      default: e = launch_q8_mt<4>(Xc, packed, scales, Yc, mc, K, N, G, p, s); break;
     }
     if (e != hipSuccess) return e;
   }

@@ -26,6 +26,9 @@ constexpr float kTwo24 = 16777216.0f;      // 2^24: undoes the subnormal scale
 
 __device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+// Takes its argument by value on purpose: __builtin_bit_cast applied directly
+// to an element of an ext_vector_type reads the vector's first element.
+__device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
 
 // 128-bit load of packed weights that are read exactly once: non-temporal, so
 // they do not push the activations, scales or partial sums out of the caches.
@@ -237,27 +240,63 @@ __device__ __forceinline__ void q3_block_pairs_sub(uint32_t w0, uint32_t w1, uin
 // ---------------------------------------------------------------------------
 // Transpose-butterfly reduction over lane bits [LOWBIT, 6) of a wave64.
 // Every lane enters with V values; lanes that differ only in those bits hold
-// partials of the same V results.  Each step halves the values a lane keeps
-// (the half picked by that lane bit) and adds the partner's matching half, so
-// the work is V/2 + V/4 + ... shuffles instead of V per bit.  On exit value j
-// of a lane is result index j + base (bfly_base), summed over all lanes that
-// share the lane bits below LOWBIT; lanes whose leftover bits are not zero
-// hold duplicates.
+// partials of the same V results.  Each step pairs every lane with a partner
+// that differs in one lane bit; the lane keeps the half of its values picked
+// by that bit and adds the partner's copy of that half, so the work is
+// V/2 + V/4 + ... adds instead of V per bit.  On exit value j of a lane is
+// result index j + base (bfly_base), summed over all lanes that share the
+// lane bits below LOWBIT; lanes whose leftover bits are not zero hold
+// duplicates.  No LDS traffic: the partners are reached with
+//   bit 5: v_permlane32_swap (lanes l <-> l ^ 32),
+//   bit 4: v_permlane16_swap (l <-> l ^ 16),
+//   bit 3: DPP row_ror:8     (l <-> l ^ 8 inside a 16-lane row),
+//   bit 2: two bank-masked DPP moves, row_shl:4 and row_shr:4 (l <-> l ^ 4),
+//   bit 1: DPP quad_perm [2,3,0,1] (l ^ 2),  bit 0: quad_perm [1,0,3,2] (l ^ 1).
 // ---------------------------------------------------------------------------
+template <int BIT>
+__device__ __forceinline__ float bfly_partner(float x) {
+  const int xi = __builtin_bit_cast(int, x);
+  if constexpr (BIT == 2) {
+    // l ^ 4 inside a 16-lane row: banks 0 and 2 (lanes 0-3, 8-11) read l + 4
+    // (row_shl:4), banks 1 and 3 read l - 4 (row_shr:4).
+    int r = __builtin_amdgcn_update_dpp(0, xi, 0x104, 0xF, 0x5, false);
+    r = __builtin_amdgcn_update_dpp(r, xi, 0x114, 0xF, 0xA, false);
+    return __builtin_bit_cast(float, r);
+  } else {
+    constexpr int ctrl = BIT == 3 ? 0x128 : BIT == 1 ? 0x4E : 0xB1;
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, xi, ctrl, 0xF, 0xF, false));
+  }
+}
+
+template <int BIT>
+__device__ __forceinline__ float bfly_pair(float lo, float hi, bool upper) {
+  if constexpr (BIT == 5 || BIT == 4) {
+    // After the swap, each lane's two registers hold its own copy and the
+    // partner's copy of the half it keeps.
+    const unsigned a = __builtin_bit_cast(unsigned, lo), b = __builtin_bit_cast(unsigned, hi);
+    const auto r = BIT == 5 ? __builtin_amdgcn_permlane32_swap(a, b, false, false)
+                            : __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+  } else {
+    const float mine = upper ? hi : lo, other = upper ? lo : hi;
+    return mine + bfly_partner<BIT>(other);
+  }
+}
+
 template <int V, int BIT, int LOWBIT>
 __device__ __forceinline__ void bfly(float* v, int lane) {
   if constexpr (BIT >= LOWBIT) {
     if constexpr (V > 1) {
-      const bool hi = (lane >> BIT) & 1;
+      const bool upper = (lane >> BIT) & 1;
 #pragma unroll
-      for (int j = 0; j < V / 2; ++j) {
-        const float mine = hi ? v[V / 2 + j] : v[j];
-        const float other = hi ? v[j] : v[V / 2 + j];
-        v[j] = mine + __shfl_xor(other, 1 << BIT);
-      }
+      for (int j = 0; j < V / 2; ++j) v[j] = bfly_pair<BIT>(v[j], v[V / 2 + j], upper);
       bfly<V / 2, BIT - 1, LOWBIT>(v, lane);
     } else {
-      v[0] += __shfl_xor(v[0], 1 << BIT);
+      if constexpr (BIT == 5 || BIT == 4) {
+        v[0] = bfly_pair<BIT>(v[0], v[0], false);
+      } else {
+        v[0] += bfly_partner<BIT>(v[0]);
+      }
       bfly<1, BIT - 1, LOWBIT>(v, lane);
     }
   }
