@@ -174,7 +174,7 @@ def wl_w8a8(wq, torch, dev):
     return w
 
 
-def time_workload(torch, w, steps, warmup, R=None):
+def time_workload(torch, w, steps, warmup, R=None, eager=False):
     """Average time of one step over exactly `steps` back-to-back steps.
 
     The steps are captured once into a HIP graph (each one a separate call on
@@ -187,6 +187,17 @@ def time_workload(torch, w, steps, warmup, R=None):
     for i in range(warmup):
         w.run(copies[i % R])
     torch.cuda.synchronize()
+    if eager:
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(steps):
+            w.run(copies[i % R])
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / steps
+        del copies
+        torch.cuda.empty_cache()
+        return ms, R
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
     graph = torch.cuda.CUDAGraph()
@@ -241,15 +252,29 @@ def main():
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="q8", help="q8 (headline) | q3_* | q4_m* | w8a8 (single line)")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every timed step from Python instead of replaying a captured graph")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy 5 times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
 
     import torch
+    dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        nbytes = 256 << 20
+        src = torch.full((nbytes,), 7, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": nbytes,
+                          "bytes_written_per_copy": nbytes, "copies": 5}))
+        return
     import weight_only_quantized_dequant_amd as wq
     wq.lib()
-    dev = torch.device("cuda:0")
 
     def make(name):
         if name == "q8":
@@ -267,7 +292,7 @@ def main():
         raise SystemExit(f"unknown workload {name}")
 
     w = make(args.workload)
-    ms, R = time_workload(torch, w, args.steps, args.warmup)
+    ms, R = time_workload(torch, w, args.steps, args.warmup, eager=args.eager)
     gbs = w.nbytes / (ms * 1e-3) / 1e9
     out = {
         "metric": "Achieved HBM GB/s (% of 8 TB/s) for M=1 fused-dequant GEMV, K=N=4096",
