@@ -260,7 +260,8 @@ def _w8a8_check(wq, d):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 64, 16), (17, 192, 80), (128, 512, 256), (130, 256, 528),
-                                   (256, 1024, 1040)])
+                                   (256, 1024, 1040), (64, 640, 64), (300, 4160, 208),
+                                   (3, 2048, 4096)])
 def test_w8a8_small_bit_exact(wq, M, K, N):
     _w8a8_check(wq, synth.gen_w8a8(M, K, N, seed=70 + M + K + N))
 
