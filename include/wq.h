@@ -167,7 +167,8 @@ int wq_gemm_q4_group(const void* X, const void* packed, const void* scales,
  * acc_out [M, N] int32: written when non-NULL (for checking), else the
  *   accumulator never leaves the chip.
  * Two launches on `stream` (quantiser, then GEMM).
- * Rules: M >= 1, K % 64 == 0, N % 16 == 0, and K * 127 * 127 < 2^31. */
+ * Rules: M >= 1, K % 64 == 0, N % 16 == 0, and K * 127 * 127 < 2^31;
+ * X, Wq, Sw, Y, Xq and acc_out (when given) 16-byte aligned. */
 int wq_gemm_w8a8(const float* X, const int8_t* Wq, const float* Sw, void* Y, int8_t* Xq,
                  float* Sx, int32_t* acc_out, int M, int K, int N, void* stream);
 

@@ -93,6 +93,9 @@ def test_w8a8_validation(L):
     assert f(P, P, P, P, P, P, None, 0, 8192, 8192, None) == wq.WQ_ERR_SHAPE
     assert f(P, P, P, P, P, P, None, 1, 1 << 20, 64, None) == wq.WQ_ERR_SHAPE  # int32 range
     assert f(P, P_MIS, P, P, P, P, None, 256, 8192, 8192, None) == wq.WQ_ERR_ALIGN
+    assert f(P, P, P, P_MIS, P, P, None, 256, 8192, 8192, None) == wq.WQ_ERR_ALIGN  # Y
+    assert f(P, P, P_MIS, P, P, P, None, 256, 8192, 8192, None) == wq.WQ_ERR_ALIGN  # Sw
+    assert f(P, P, P, P, P, P, P_MIS, 256, 8192, 8192, None) == wq.WQ_ERR_ALIGN     # acc_out
 
 
 def test_unpack_validation(L):

@@ -175,7 +175,9 @@ int wq_gemm_w8a8(const float* X, const int8_t* Wq, const float* Sw, void* Y, int
   if (M < 1 || K < 64 || N < 16 || K % 64 || N % 16) return WQ_ERR_SHAPE;
   if ((long long)K * 127 * 127 >= (1LL << 31)) return WQ_ERR_SHAPE;
   if ((long long)M * K > kMaxBytes || (long long)N * K > kMaxBytes) return WQ_ERR_SHAPE;
-  if (!aligned16(X) || !aligned16(Wq) || !aligned16(Xq)) return WQ_ERR_ALIGN;
+  if (!aligned16(X) || !aligned16(Wq) || !aligned16(Xq) || !aligned16(Sw) || !aligned16(Y) ||
+      !aligned16(acc_out))
+    return WQ_ERR_ALIGN;
   return hip_status(wq::launch_w8a8(X, Wq, Sw, Y, Xq, Sx, acc_out, M, K, N, as_stream(stream)));
 }
 
