@@ -24,12 +24,18 @@
 
 namespace wq {
 
+// Widest panel whose count spreads over kTargetCUs compute units in whole
+// rounds with at most 12% idle (each workgroup then walks a contiguous run of
+// panels); otherwise the narrowest width dividing N.
 static int panel_width_4(int N) {
-  for (int P : {32, 16, 8, 4})
-    if (N % P == 0 && N / P >= 256) return P;
-  for (int P : {4, 8, 16, 32})
-    if (N % P == 0) return P;
-  return 4;
+  int narrowest = 4;
+  for (int P : {32, 16, 8, 4}) {
+    if (N % P) continue;
+    const int np = N / P, rounds = (np + kTargetCUs - 1) / kTargetCUs;
+    if ((long long)rounds * kTargetCUs * 100 <= 112LL * np) return P;
+    narrowest = P;
+  }
+  return narrowest;
 }
 
 PanelPlan plan_q4(int K, int N, int G) {
@@ -40,6 +46,7 @@ PanelPlan plan_q4(int K, int N, int G) {
   const int ns = kThreads / p.cpp;
   const int ku = K / 8;                       // word rows
   p.bw = (G / 8) < 16 ? (G / 8) : 16;         // word rows per batch: inside one group
+  while (p.bw > 4 && ns * p.bw >= 2 * ku) p.bw /= 2;  // keep most slots busy
   p.u = p.bw * ((ku + ns * p.bw - 1) / (ns * p.bw));
   p.nsa = (ku + p.u - 1) / p.u;
   p.packed_bytes = (size_t)p.npanels * p.u * p.nsa * p.cpp * 16;
@@ -50,7 +57,8 @@ PanelPlan plan_q4(int K, int N, int G) {
 // word rows inside aligned groups of 8).
 static inline int q4_kpad(int K) { return (K + 63) / 64 * 64; }
 
-// Rows of X staged per launch: the LDS copies of X (MT * Kpad halves) stay <= 64 KB.
+// Rows of X staged per launch: the LDS copies of X (MT * Kpad halves) stay
+// <= 64 KB (plus the small cross-wave reduction buffer).
 int q4_max_mt(int K) {
   int mt = 8;
   while (mt > 1 && (size_t)mt * q4_kpad(K) * 2 > 65536) mt /= 2;
@@ -106,40 +114,45 @@ template <int MT, int CPP, int BW>
 __global__ __launch_bounds__(kThreads) void q4_panel_kernel(
     const _Float16* __restrict__ X, const uint8_t* __restrict__ Wp,
     const _Float16* __restrict__ scales, const int* __restrict__ invperm,
-    _Float16* __restrict__ Y, int M, int K, int N, int G, int u, int nsa, int packed_bytes) {
+    _Float16* __restrict__ Y, int M, int K, int N, int G, int u, int nsa, int npanels,
+    int packed_bytes) {
   constexpr int P = 4 * CPP;
   constexpr int V = 4 * MT;  // results per chunk: [m][4 columns]
   constexpr int LOWBIT = CPP == 1 ? 0 : CPP == 2 ? 1 : CPP == 4 ? 2 : 3;
   constexpr int LEFT = bfly_left<V, LOWBIT>();
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  _Float16* xh = reinterpret_cast<_Float16*>(smem);  // MT copies of K halves
+  const int kpad = (K + 63) / 64 * 64;  // halves per LDS copy of X
+  _Float16* xh = reinterpret_cast<_Float16*>(smem);  // MT copies of kpad halves
+  float* red = reinterpret_cast<float*>(smem + (size_t)MT * kpad * 2);  // [4 waves][CPP][V]
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int panel = blockIdx.x;
+  // This workgroup's contiguous run of panels.
+  const int p_begin = (int)((long long)blockIdx.x * npanels / gridDim.x);
+  const int p_end = (int)((long long)(blockIdx.x + 1) * npanels / gridDim.x);
   const int nta = nsa * CPP;
   const int c = t % CPP, s = t / CPP;
   const bool active = t < nta;
-  const int col0 = panel * P + 4 * c;
   const int ku = K / 8;
-  const int kpad = (K + 63) / 64 * 64;  // halves per LDS copy of X
+  const int nb = u / BW;                        // batches per panel
+  const int nunits = (p_end - p_begin) * nb;    // (panel, batch) units of the run
 
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wp, packed_bytes);
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, (K / G) * N * 2);
 
-  // 1. First batch of the weight stream goes out before anything else.
+  // 1. First unit of the weight stream goes out before anything else.
   u32x4 w[BW], wn[BW];
-  const int nb = u / BW;
-  auto load_batch = [&](u32x4* dst, int b) {
+  auto load_unit = [&](u32x4* dst, int q) {
+    const int panel = p_begin + q / nb, b = q % nb;
     const int wbase = ((panel * u + b * BW) * nta + t) * 16;
 #pragma unroll
     for (int i = 0; i < BW; ++i) dst[i] = buffer_stream(wr, active ? wbase + i * nta * 16 : kOutOfRange);
   };
-  load_batch(w, 0);
+  if (nunits > 0) load_unit(w, 0);
 
-  // 2. Scatter X into LDS through the inverse permutation (group order).
-  //    Thread t takes the 8-row chunks t, t + 256, ...; for each chunk the
-  //    permutation is read once and reused for every row of X.  All loads of
-  //    a round of chunks go out before any LDS write.
+  // 2. Scatter X into LDS through the inverse permutation (group order), once
+  //    for the whole run.  Thread t takes the 8-row chunks t, t + 256, ...; for
+  //    each chunk the permutation is read once and reused for every row of X.
+  //    All loads of a round of chunks go out before any LDS write.
   constexpr int CR = MT >= 8 ? 1 : 2;  // chunks per thread per round
   const int nchunk = K / 8;
   for (int c0 = t; c0 < nchunk; c0 += CR * kThreads) {
@@ -183,8 +196,10 @@ __global__ __launch_bounds__(kThreads) void q4_panel_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) accT[m][j] = 0.0f;
 
-  for (int b = 0; b < nb; ++b) {
-    if (b + 1 < nb) load_batch(wn, b + 1);  // next batch in flight during this one
+  for (int q = 0; q < nunits; ++q) {
+    if (q + 1 < nunits) load_unit(wn, q + 1);  // next unit in flight during this one
+    const int panel = p_begin + q / nb, b = q % nb;
+    const int col0 = panel * P + 4 * c;
     const int r0 = s * u + b * BW;  // first word row of the batch (group order)
     const bool live = active && r0 < ku;
     uint2 sraw = make_uint2(0u, 0u);
@@ -250,35 +265,39 @@ __global__ __launch_bounds__(kThreads) void q4_panel_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         accT[m][j] = __builtin_fmaf(__builtin_fmaf(acc4[m][j], 0.0625f, acc0[m][j]), sc[j], accT[m][j]);
-    if (b + 1 < nb) {
+    if (q + 1 < nunits) {
 #pragma unroll
       for (int i = 0; i < BW; ++i) w[i] = wn[i];
     }
-  }
 
-  // Reduce over the slots of a chunk (LDS reused for the cross-wave step).
-  float v[V];
+    if (b == nb - 1) {
+      // Panel done: reduce over the slots of each chunk and write P x MT results.
+      float v[V];
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
+      for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[m * 4 + j] = accT[m][j];
-  bfly<V, 5, LOWBIT>(v, lane);
-  bool owner;
-  const int base = bfly_base<V, LOWBIT>(lane, owner);
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(smem);  // [4 waves][CPP][V]
-  if (owner) {
+        for (int j = 0; j < 4; ++j) {
+          v[m * 4 + j] = accT[m][j];
+          accT[m][j] = 0.0f;
+        }
+      bfly<V, 5, LOWBIT>(v, lane);
+      bool owner;
+      const int base = bfly_base<V, LOWBIT>(lane, owner);
+      if (owner) {
 #pragma unroll
-    for (int j = 0; j < LEFT; ++j) red[(wave * CPP + c) * V + base + j] = v[j];
-  }
-  __syncthreads();
-  for (int r = t; r < CPP * V; r += kThreads) {
-    const int rc = r / V, idx = r % V;
-    const int m = idx / 4, col = panel * P + 4 * rc + (idx % 4);
-    float sum = 0.0f;
+        for (int j = 0; j < LEFT; ++j) red[(wave * CPP + c) * V + base + j] = v[j];
+      }
+      __syncthreads();
+      for (int r = t; r < CPP * V; r += kThreads) {
+        const int rc = r / V, idx = r % V;
+        const int m = idx / 4, col = panel * P + 4 * rc + (idx % 4);
+        float sum = 0.0f;
 #pragma unroll
-    for (int w2 = 0; w2 < kThreads / 64; ++w2) sum += red[(w2 * CPP + rc) * V + idx];
-    if (m < M) Y[(size_t)m * N + col] = (_Float16)(sum * kTwo24);
+        for (int w2 = 0; w2 < kThreads / 64; ++w2) sum += red[(w2 * CPP + rc) * V + idx];
+        if (m < M) Y[(size_t)m * N + col] = (_Float16)(sum * kTwo24);
+      }
+      __syncthreads();  // red is rewritten by the next panel
+    }
   }
 }
 
@@ -344,11 +363,18 @@ static hipError_t launch_q4_t(const void* X, const void* packed, const void* sca
                               const int32_t* invperm, void* Y, int M, int K, int N, int G,
                               const PanelPlan& p, hipStream_t s) {
   const size_t xb = (size_t)MT * q4_kpad(K) * 2, rb = (size_t)kThreads / 64 * CPP * 4 * MT * 4;
-  const size_t lds = xb > rb ? xb : rb;
-  hipLaunchKernelGGL((q4_panel_kernel<MT, CPP, BW>), dim3(p.npanels), dim3(kThreads), lds, s,
+  const int cus = device_cus();
+  const int grid = p.npanels < cus ? p.npanels : cus;
+  if (xb + rb > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&q4_panel_kernel<MT, CPP, BW>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)(xb + rb));
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((q4_panel_kernel<MT, CPP, BW>), dim3(grid), dim3(kThreads), xb + rb, s,
                      reinterpret_cast<const _Float16*>(X), reinterpret_cast<const uint8_t*>(packed),
                      reinterpret_cast<const _Float16*>(scales), invperm,
-                     reinterpret_cast<_Float16*>(Y), M, K, N, G, p.u, p.nsa, (int)p.packed_bytes);
+                     reinterpret_cast<_Float16*>(Y), M, K, N, G, p.u, p.nsa, p.npanels,
+                     (int)p.packed_bytes);
   return hipGetLastError();
 }
 

@@ -4,9 +4,27 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <vector>
 
 #include "wq_internal.h"
+
+namespace wq {
+
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kTargetCUs;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = kTargetCUs;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+}  // namespace wq
 
 namespace {
 

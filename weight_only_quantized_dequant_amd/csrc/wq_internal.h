@@ -9,9 +9,17 @@ namespace wq {
 
 constexpr int kThreads = 256;  // 4 wave64s per workgroup
 
+// Compute units the panel layouts are sized for (MI355X: 256).  Only the
+// choice of panel width depends on it; launches use the device's own count.
+constexpr int kTargetCUs = 256;
+
+// Compute units of the current device (queried once per device).
+int device_cus();
+
 // Panel plan of a re-laid-out weight: a pure function of the shape, shared by
 // the prepack kernel, the product and the unpack check.
-//   P        panel width (columns); one workgroup per panel over all of K
+//   P        panel width (columns); a panel spans all of K, and a workgroup
+//            takes one panel or a contiguous run of them
 //   cpp      column chunks per panel (16 columns for int8, 4 for 3/4-bit)
 //   npanels  N / P
 //   u        K units per slot (rows for int8, word rows for 4-bit, 32-row
