@@ -139,24 +139,32 @@ __global__ __launch_bounds__(kThreads) void q4_panel_kernel(
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wp, packed_bytes);
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, (K / G) * N * 2);
 
-  // 1. First unit of the weight stream goes out before anything else.
-  u32x4 w[BW], wn[BW];
-  auto load_unit = [&](u32x4* dst, int q) {
+  // A unit's loads: its scale pair first, then its BW weight pieces.  Units
+  // past the end of the run load nothing (out-of-range offsets), so the loads
+  // need no branch.
+  u32x4 w0[BW], w1[BW], w2[BW];
+  uint2 sc0, sc1, sc2;
+  auto load_unit = [&](u32x4* dst, uint2& sc, int q) {
+    const bool ok = active && q < nunits;
     const int panel = p_begin + q / nb, b = q % nb;
+    const int r0 = s * u + b * BW;
+    const int soff = (ok && r0 < ku) ? (((8 * r0) / G) * N + panel * P + 4 * c) * 2 : kOutOfRange;
+    const unsigned long long v64 = __builtin_bit_cast(
+        unsigned long long, __builtin_amdgcn_raw_buffer_load_b64(sr, soff, 0, 0));
+    sc = make_uint2((uint32_t)v64, (uint32_t)(v64 >> 32));
     const int wbase = ((panel * u + b * BW) * nta + t) * 16;
 #pragma unroll
-    for (int i = 0; i < BW; ++i) dst[i] = buffer_stream(wr, active ? wbase + i * nta * 16 : kOutOfRange);
+    for (int i = 0; i < BW; ++i) dst[i] = buffer_stream(wr, ok ? wbase + i * nta * 16 : kOutOfRange);
   };
-  if (nunits > 0) load_unit(w, 0);
 
-  // 2. Scatter X into LDS through the inverse permutation (group order), once
-  //    for the whole run.  Thread t takes the 8-row chunks t, t + 256, ...; for
-  //    each chunk the permutation is read once and reused for every row of X.
-  //    All loads of a round of chunks go out before any LDS write.
+  // Scatter X into LDS through the inverse permutation (group order), once
+  // for the whole run.  Thread t takes the 8-row chunks t, t + 256, ...; for
+  // each chunk the permutation is read once and reused for every row of X.
+  // All loads of a round of chunks go out before any LDS write; the first two
+  // units of the weight stream go out right after the first round's loads.
   constexpr int CR = MT >= 8 ? 1 : 2;  // chunks per thread per round
   const int nchunk = K / 8;
-  for (int c0 = t; c0 < nchunk; c0 += CR * kThreads) {
-    u32x4 pv[CR][2], xq[CR][MT];
+  auto stage_load = [&](int c0, u32x4 (&pv)[CR][2], u32x4 (&xq)[CR][MT]) {
 #pragma unroll
     for (int r = 0; r < CR; ++r) {
       const int ch = c0 + r * kThreads;
@@ -170,6 +178,8 @@ __global__ __launch_bounds__(kThreads) void q4_panel_kernel(
         xq[r][m] = (ok && m < M) ? *reinterpret_cast<const u32x4*>(X + (size_t)m * K + 8 * ch)
                                  : (u32x4){0u, 0u, 0u, 0u};
     }
+  };
+  auto stage_write = [&](int c0, const u32x4 (&pv)[CR][2], const u32x4 (&xq)[CR][MT]) {
 #pragma unroll
     for (int r = 0; r < CR; ++r) {
       const int ch = c0 + r * kThreads;
@@ -186,6 +196,18 @@ __global__ __launch_bounds__(kThreads) void q4_panel_kernel(
           reinterpret_cast<uint16_t*>(xh)[(size_t)m * kpad + q4_lds_half(dst[j])] = bits;
         }
     }
+  };
+  {
+    u32x4 pv[CR][2], xq[CR][MT];
+    stage_load(t, pv, xq);
+    load_unit(w0, sc0, 0);
+    load_unit(w1, sc1, 1);
+    stage_write(t, pv, xq);
+  }
+  for (int c0 = t + CR * kThreads; c0 < nchunk; c0 += CR * kThreads) {
+    u32x4 pv[CR][2], xq[CR][MT];
+    stage_load(c0, pv, xq);
+    stage_write(c0, pv, xq);
   }
   __syncthreads();
 
@@ -196,19 +218,15 @@ __global__ __launch_bounds__(kThreads) void q4_panel_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) accT[m][j] = 0.0f;
 
-  for (int q = 0; q < nunits; ++q) {
-    if (q + 1 < nunits) load_unit(wn, q + 1);  // next unit in flight during this one
+  // Units go through a ring of three register buffers: while unit q is
+  // multiplied, units q + 1 and q + 2 are in flight.  The loop is unrolled by
+  // three so every buffer keeps a fixed set of registers (a register copy of
+  // a buffer would wait for its loads).
+  auto step = [&](int q, const u32x4* w, const uint2& sraw, u32x4* pre, uint2& pre_sc) {
+    load_unit(pre, pre_sc, q + 2);
+    if (q >= nunits) return;
     const int panel = p_begin + q / nb, b = q % nb;
-    const int col0 = panel * P + 4 * c;
     const int r0 = s * u + b * BW;  // first word row of the batch (group order)
-    const bool live = active && r0 < ku;
-    uint2 sraw = make_uint2(0u, 0u);
-    {
-      const int soff = live ? (((8 * r0) / G) * N + col0) * 2 : kOutOfRange;
-      const unsigned long long v64 = __builtin_bit_cast(
-          unsigned long long, __builtin_amdgcn_raw_buffer_load_b64(sr, soff, 0, 0));
-      sraw = make_uint2((uint32_t)v64, (uint32_t)(v64 >> 32));
-    }
     // Sum of x over the batch: the CPP lanes of a slot split the word rows.
     float xs[MT];
 #pragma unroll
@@ -265,10 +283,6 @@ __global__ __launch_bounds__(kThreads) void q4_panel_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         accT[m][j] = __builtin_fmaf(__builtin_fmaf(acc4[m][j], 0.0625f, acc0[m][j]), sc[j], accT[m][j]);
-    if (q + 1 < nunits) {
-#pragma unroll
-      for (int i = 0; i < BW; ++i) w[i] = wn[i];
-    }
 
     if (b == nb - 1) {
       // Panel done: reduce over the slots of each chunk and write P x MT results.
@@ -298,6 +312,11 @@ __global__ __launch_bounds__(kThreads) void q4_panel_kernel(
       }
       __syncthreads();  // red is rewritten by the next panel
     }
+  };
+  for (int q = 0; q < nunits; q += 3) {
+    step(q, w0, sc0, w2, sc2);
+    step(q + 1, w1, sc1, w0, sc0);
+    step(q + 2, w2, sc2, w1, sc1);
   }
 }
 
