@@ -26,12 +26,18 @@
 
 namespace wq {
 
+// Widest panel whose count spreads over kTargetCUs compute units in whole
+// rounds with at most 12% idle (each workgroup then walks a contiguous run of
+// panels); otherwise the narrowest width dividing N.
 static int panel_width_3(int N) {
-  for (int P : {32, 16, 8, 4})
-    if (N % P == 0 && N / P >= 256) return P;
-  for (int P : {4, 8, 16, 32})
-    if (N % P == 0) return P;
-  return 4;
+  int narrowest = 4;
+  for (int P : {32, 16, 8, 4}) {
+    if (N % P) continue;
+    const int np = N / P, rounds = (np + kTargetCUs - 1) / kTargetCUs;
+    if ((long long)rounds * kTargetCUs * 100 <= 112LL * np) return P;
+    narrowest = P;
+  }
+  return narrowest;
 }
 
 PanelPlan plan_q3(int K, int N) {
@@ -49,6 +55,10 @@ PanelPlan plan_q3(int K, int N) {
 
 // ---------------------------------------------------------------------------
 // Offline re-layout: one thread per (block, 4-column chunk) piece of 48 bytes.
+// The piece's three 16-byte word rows are stored as three separate planes:
+// word row j of piece (panel, i, t) sits at ((panel u + i) 3 + j) nta + t, so
+// one load instruction of a wave (fixed i and j) reads 64 consecutive 16-byte
+// words.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void q3_prepack_kernel(const uint32_t* __restrict__ qw,
                                                               uint32_t* __restrict__ out, int K,
@@ -67,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void q3_prepack_kernel(const uint32_t* __
   for (int j = 0; j < 3; ++j)
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc)
-      out[idx * 12 + j * 4 + cc] = blk < K / 32 ? qw[(size_t)(3 * blk + j) * N + col0 + cc] : 0u;
+      out[((pi * 3 + j) * nta + t) * 4 + cc] = blk < K / 32 ? qw[(size_t)(3 * blk + j) * N + col0 + cc] : 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -76,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void q3_prepack_kernel(const uint32_t* __
 template <bool F16, int CPP, int UB>
 __global__ __launch_bounds__(kThreads) void q3_panel_kernel(
     const void* __restrict__ xv, const uint8_t* __restrict__ Wp, const void* __restrict__ sv,
-    const void* __restrict__ zv, void* __restrict__ yv, int K, int N, int u, int nsa,
+    const void* __restrict__ zv, void* __restrict__ yv, int K, int N, int u, int nsa, int npanels,
     int packed_bytes) {
   constexpr int P = 4 * CPP;
   constexpr int LOWBIT = CPP == 1 ? 0 : CPP == 2 ? 1 : CPP == 4 ? 2 : 3;
@@ -88,7 +98,11 @@ __global__ __launch_bounds__(kThreads) void q3_panel_kernel(
   __shared__ float red[kThreads / 64][CPP][4];
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int panel = blockIdx.x;
+  // This workgroup's contiguous run of panels; a unit is UB blocks of a panel.
+  const int p_begin = (int)((long long)blockIdx.x * npanels / gridDim.x);
+  const int p_end = (int)((long long)(blockIdx.x + 1) * npanels / gridDim.x);
+  const int nr = (u + UB - 1) / UB;  // units per panel
+  const int nunits = (p_end - p_begin) * nr;
   const int nta = nsa * CPP;
   const int c = t % CPP, s = t / CPP;
   const bool active = t < nta;
@@ -97,8 +111,16 @@ __global__ __launch_bounds__(kThreads) void q3_panel_kernel(
   const int nblk = active ? (blk0 + u <= ku ? u : (ku > blk0 ? ku - blk0 : 0)) : 0;
 
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wp, packed_bytes);
-  auto wload = [&](int i, int j) {
-    return buffer_stream(wr, (i < nblk) ? ((((panel * u + i) * nta + t) * 3 + j) * 16) : kOutOfRange);
+  // Units past the end of the run load nothing (out-of-range offsets).
+  auto load_unit = [&](u32x4 (&w)[UB][3], int q) {
+    const int panel = p_begin + q / nr, i0 = (q % nr) * UB;
+    const bool ok = q < nunits;
+#pragma unroll
+    for (int i = 0; i < UB; ++i)
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        w[i][j] = buffer_stream(
+            wr, (ok && i0 + i < nblk) ? ((((panel * u + i0 + i) * 3 + j) * nta + t) * 16) : kOutOfRange);
   };
 
   // 1. Activations first (thread t stages blocks t, t + 256, ...): all the
@@ -116,12 +138,10 @@ __global__ __launch_bounds__(kThreads) void q3_panel_kernel(
           xr_rsrc, blk < ku ? (blk * XV + v) * 16 : kOutOfRange, 0, 0);
   }
 
-  // 2. The first UB blocks of the weight stream.
-  u32x4 w[UB][3];
-#pragma unroll
-  for (int i = 0; i < UB; ++i)
-#pragma unroll
-    for (int j = 0; j < 3; ++j) w[i][j] = wload(i, j);
+  // 2. The first two units of the weight stream.
+  u32x4 w0[UB][3], w1[UB][3];
+  load_unit(w0, 0);
+  load_unit(w1, 1);
 
   // 3. Pairs into LDS in code-pair order (pre-scaled), and sum_k x[k].
   float my_sum = 0.0f;
@@ -175,20 +195,18 @@ __global__ __launch_bounds__(kThreads) void q3_panel_kernel(
   __syncthreads();
   const float xsum = (xsum_w[0] + xsum_w[1]) + (xsum_w[2] + xsum_w[3]);
 
-  // 3. Exact codes times x, fp32 accumulation (one accumulator per class).
+  // 4. Exact codes times x, fp32 accumulation (one accumulator per class).
   float acc[NACC][4];
 #pragma unroll
   for (int a = 0; a < NACC; ++a)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[a][j] = 0.0f;
 
-  for (int i0 = 0; i0 < nblk; i0 += UB) {
-    if (i0 > 0) {
-#pragma unroll
-      for (int i = 0; i < UB; ++i)
-#pragma unroll
-        for (int j = 0; j < 3; ++j) w[i][j] = wload(i0 + i, j);
-    }
+  // One unit: multiply the buffer `w`, refill `pre` with unit q + 2; at the
+  // last unit of a panel, reduce and write the panel's P outputs.
+  auto step = [&](int q, const u32x4 (&w)[UB][3], u32x4 (&pre)[UB][3]) {
+    if (q >= nunits) return;
+    const int panel = p_begin + q / nr, i0 = (q % nr) * UB;
 #pragma unroll
     for (int i = 0; i < UB; ++i) {
       if (i0 + i >= nblk) break;
@@ -217,45 +235,55 @@ __global__ __launch_bounds__(kThreads) void q3_panel_kernel(
         }
       }
     }
-  }
+    load_unit(pre, q + 2);  // `w` is consumed: its registers take unit q + 2
+    if (q % nr != nr - 1) return;
 
-  // 4. Classes back to one sum per column (powers of two: exact rescale).
-  float v[4];
+    // Classes back to one sum per column (powers of two: exact rescale).
+    float v[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if constexpr (F16) {
-      float a = 0.0f;
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (F16) {
+        float a = 0.0f;
 #pragma unroll
-      for (int sl = 0; sl < NACC; ++sl) a = __builtin_fmaf(acc[sl][j], __builtin_ldexpf(1.0f, 24 - q3_slot_class(sl)), a);
-      v[j] = a;
-    } else {
-      v[j] = acc[0][j];
+        for (int sl = 0; sl < NACC; ++sl) {
+          a = __builtin_fmaf(acc[sl][j], __builtin_ldexpf(1.0f, 24 - q3_slot_class(sl)), a);
+          acc[sl][j] = 0.0f;
+        }
+        v[j] = a;
+      } else {
+        v[j] = acc[0][j];
+        acc[0][j] = 0.0f;
+      }
     }
-  }
-
-  // 5. Over the slots of a chunk, then y = scale * A - zero * sum(x).
-  bfly<4, 5, LOWBIT>(v, lane);
-  bool owner;
-  const int base = bfly_base<4, LOWBIT>(lane, owner);
-  constexpr int LEFT = bfly_left<4, LOWBIT>();
-  if (owner) {
+    // Over the slots of a chunk, then y = scale * A - zero * sum(x).
+    bfly<4, 5, LOWBIT>(v, lane);
+    bool owner;
+    const int base = bfly_base<4, LOWBIT>(lane, owner);
+    constexpr int LEFT = bfly_left<4, LOWBIT>();
+    if (owner) {
 #pragma unroll
-    for (int j = 0; j < LEFT; ++j) red[wave][c][base + j] = v[j];
-  }
-  __syncthreads();
-  if (t < P) {
-    const int rc = t / 4, j = t % 4;
-    const int n = panel * P + t;
-    const float A = (red[0][rc][j] + red[1][rc][j]) + (red[2][rc][j] + red[3][rc][j]);
-    if constexpr (F16) {
-      const float sc = (float)reinterpret_cast<const _Float16*>(sv)[n];
-      const float ze = (float)reinterpret_cast<const _Float16*>(zv)[n];
-      reinterpret_cast<_Float16*>(yv)[n] = (_Float16)(sc * A - ze * xsum);
-    } else {
-      const float sc = reinterpret_cast<const float*>(sv)[n];
-      const float ze = reinterpret_cast<const float*>(zv)[n];
-      reinterpret_cast<float*>(yv)[n] = sc * A - ze * xsum;
+      for (int j = 0; j < LEFT; ++j) red[wave][c][base + j] = v[j];
     }
+    __syncthreads();
+    if (t < P) {
+      const int rc = t / 4, j = t % 4;
+      const int n = panel * P + t;
+      const float A = (red[0][rc][j] + red[1][rc][j]) + (red[2][rc][j] + red[3][rc][j]);
+      if constexpr (F16) {
+        const float sc = (float)reinterpret_cast<const _Float16*>(sv)[n];
+        const float ze = (float)reinterpret_cast<const _Float16*>(zv)[n];
+        reinterpret_cast<_Float16*>(yv)[n] = (_Float16)(sc * A - ze * xsum);
+      } else {
+        const float sc = reinterpret_cast<const float*>(sv)[n];
+        const float ze = reinterpret_cast<const float*>(zv)[n];
+        reinterpret_cast<float*>(yv)[n] = sc * A - ze * xsum;
+      }
+    }
+    __syncthreads();  // red is rewritten by the next panel
+  };
+  for (int q = 0; q < nunits; q += 2) {
+    step(q, w0, w0);
+    step(q + 1, w1, w1);
   }
 }
 
@@ -278,7 +306,7 @@ __global__ __launch_bounds__(kThreads) void q3_unpack_kernel(const uint8_t* __re
   const int col0 = panel * p.P + 4 * c;
   u32x4 w[3];
 #pragma unroll
-  for (int j = 0; j < 3; ++j) w[j] = *reinterpret_cast<const u32x4*>(Wp + (idx * 3 + j) * 16);
+  for (int j = 0; j < 3; ++j) w[j] = *reinterpret_cast<const u32x4*>(Wp + ((pi * 3 + j) * nta + t) * 16);
 #pragma unroll
   for (int col = 0; col < 4; ++col) {
     h2 pr[16];
@@ -316,9 +344,11 @@ static hipError_t launch_q3_t(const void* x, const void* packed, const void* sca
                               const void* zeros, void* y, int K, int N, const PanelPlan& p,
                               hipStream_t s) {
   const size_t lds = (size_t)(K / 2) * (F16 ? 4 : 8);
-  hipLaunchKernelGGL((q3_panel_kernel<F16, CPP, UB>), dim3(p.npanels), dim3(kThreads), lds, s, x,
+  const int cus = device_cus();
+  const int grid = p.npanels < cus ? p.npanels : cus;
+  hipLaunchKernelGGL((q3_panel_kernel<F16, CPP, UB>), dim3(grid), dim3(kThreads), lds, s, x,
                      reinterpret_cast<const uint8_t*>(packed), scales, zeros, y, K, N, p.u, p.nsa,
-                     (int)p.packed_bytes);
+                     p.npanels, (int)p.packed_bytes);
   return hipGetLastError();
 }
 
