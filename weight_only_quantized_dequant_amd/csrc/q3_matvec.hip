@@ -123,19 +123,25 @@ __global__ __launch_bounds__(kThreads) void q3_panel_kernel(
             wr, (ok && i0 + i < nblk) ? ((((panel * u + i0 + i) * 3 + j) * nta + t) * 16) : kOutOfRange);
   };
 
-  // 1. Activations first (thread t stages blocks t, t + 256, ...): all the
-  //    loads of the first XR rounds go out together, ahead of the weights.
+  // 1. Activations.  The slots of a wave cover a contiguous range of 32-row
+  //    blocks, and a wave reads x only there, so each wave stages its own
+  //    range into LDS and no workgroup barrier stands between the staging and
+  //    the products.  All loads of the first XR rounds go out together, ahead
+  //    of the weights.
   constexpr int XV = F16 ? 4 : 8;  // 16-byte loads per 32-row block of x
   constexpr int XR = 2;
+  constexpr int SPW = 64 / CPP;    // slots per wave
+  const int wlo = wave * SPW * u;
+  const int whi = (wave + 1) * SPW * u < ku ? (wave + 1) * SPW * u : ku;
   const __amdgpu_buffer_rsrc_t xr_rsrc = make_rsrc(xv, K * (F16 ? 2 : 4));
   u32x4 xraw[XR][XV];
 #pragma unroll
   for (int r = 0; r < XR; ++r) {
-    const int blk = t + r * kThreads;
+    const int blk = wlo + lane + 64 * r;
 #pragma unroll
     for (int v = 0; v < XV; ++v)
       xraw[r][v] = __builtin_amdgcn_raw_buffer_load_b128(
-          xr_rsrc, blk < ku ? (blk * XV + v) * 16 : kOutOfRange, 0, 0);
+          xr_rsrc, blk < whi ? (blk * XV + v) * 16 : kOutOfRange, 0, 0);
   }
 
   // 2. The first two units of the weight stream.
@@ -179,10 +185,10 @@ __global__ __launch_bounds__(kThreads) void q3_panel_kernel(
   };
 #pragma unroll
   for (int r = 0; r < XR; ++r) {
-    const int blk = t + r * kThreads;
-    if (blk < ku) stage_block(blk, xraw[r]);
+    const int blk = wlo + lane + 64 * r;
+    if (blk < whi) stage_block(blk, xraw[r]);
   }
-  for (int blk = t + XR * kThreads; blk < ku; blk += kThreads) {  // K > 16384 only
+  for (int blk = wlo + lane + 64 * XR; blk < whi; blk += 64) {
     u32x4 raw[XV];
 #pragma unroll
     for (int v = 0; v < XV; ++v)
@@ -191,9 +197,10 @@ __global__ __launch_bounds__(kThreads) void q3_panel_kernel(
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) my_sum += __shfl_xor(my_sum, o);
-  if (lane == 0) xsum_w[wave] = my_sum;
-  __syncthreads();
-  const float xsum = (xsum_w[0] + xsum_w[1]) + (xsum_w[2] + xsum_w[3]);
+  if (lane == 0) xsum_w[wave] = my_sum;  // read after the first panel's barrier
+  // The wave's own LDS writes are done before its lanes read each other's.
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
 
   // 4. Exact codes times x, fp32 accumulation (one accumulator per class).
   float acc[NACC][4];
@@ -266,6 +273,7 @@ __global__ __launch_bounds__(kThreads) void q3_panel_kernel(
     }
     __syncthreads();
     if (t < P) {
+      const float xsum = (xsum_w[0] + xsum_w[1]) + (xsum_w[2] + xsum_w[3]);
       const int rc = t / 4, j = t % 4;
       const int n = panel * P + t;
       const float A = (red[0][rc][j] + red[1][rc][j]) + (red[2][rc][j] + red[3][rc][j]);
@@ -352,14 +360,14 @@ static hipError_t launch_q3_t(const void* x, const void* packed, const void* sca
   return hipGetLastError();
 }
 
+// One 32-row block per unit: two units (six 16-byte loads a thread) stay in
+// flight, which keeps the per-CU load queue busy without stalling the issue of
+// the arithmetic behind a long run of loads.
 template <bool F16, int CPP>
 static hipError_t launch_q3_ub(const void* x, const void* packed, const void* scales,
                                const void* zeros, void* y, int K, int N, const PanelPlan& p,
                                hipStream_t s) {
-  if (p.u <= 1) return launch_q3_t<F16, CPP, 1>(x, packed, scales, zeros, y, K, N, p, s);
-  if (p.u <= 2) return launch_q3_t<F16, CPP, 2>(x, packed, scales, zeros, y, K, N, p, s);
-  if (p.u <= 4) return launch_q3_t<F16, CPP, 4>(x, packed, scales, zeros, y, K, N, p, s);
-  return launch_q3_t<F16, CPP, 6>(x, packed, scales, zeros, y, K, N, p, s);
+  return launch_q3_t<F16, CPP, 1>(x, packed, scales, zeros, y, K, N, p, s);
 }
 
 template <bool F16>
