@@ -37,9 +37,17 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, "wq_api.cpp")]
 
 
+# Per-source extra flags.  The 4-bit kernel keeps its matrix-core accumulators
+# in ordinary VGPRs: with the default choice the register allocator shuttles
+# them between AGPRs and VGPRs on every block.
+EXTRA = {
+    "q4_group.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON, "-x", "hip", "-c", src, "-o", obj]
+    cmd = [_hipcc(), *COMMON, *EXTRA.get(os.path.basename(src), []), "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

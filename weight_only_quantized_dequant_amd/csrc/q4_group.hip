@@ -9,350 +9,356 @@
 // row's group g_idx[k] is not monotone in k.  The weight is re-laid out once,
 // offline (wq_prepack_q4), the same idea as the offline re-layout of "Marlin
 // 格式" on the "Quantization CUDA" page: rows are put in group order (perm),
-// then into column panels over the whole of K in the order the threads read
-// them.  At run time each workgroup scatters X into LDS through the inverse
-// permutation (coalesced reads, LDS writes), so every 128-row batch a thread
-// reads is one group, scaled once.
+// then into the operand order of the matrix cores.  At run time each
+// workgroup scatters X into LDS through the inverse permutation (coalesced
+// reads, LDS writes), so the rows the cores combine are one group at a time.
 //
-// Geometry.  A workgroup owns a panel of P = 4*CPP columns; thread
-// t = s*CPP + c takes the 4 columns of chunk c (one 128-bit load per word
-// row) and the u word rows of slot s, in batches of BW word rows (one group,
-// or a part of one).  The activations sit in LDS as the pairs
-// (rows 8r + j, 8r + j + 4) the codes come out in (q4_pairs_sub).
+// The products run on v_mfma_f32_16x16x32_f16 for every M (rows of X past M
+// are zero lanes of the operand).  A code u (0..15) enters the cores as the
+// fp16 subnormal with mantissa u, i.e. exactly u * 2^-24, so each product
+// x * u * 2^-24 is exact in the fp32 accumulator.  Per group g the tile
+//   C = sum_k x[m, k] u[k, n] 2^-24,   S = sum_k x[m, k]   (a second MFMA
+// against a constant operand of ones) gives the group's share
+//   scale[g, n] * (C - 8 * 2^-24 * S)
+// of Y / 2^24: the (u - 8) offset is applied once per group, not per code.
+//
+// Layout.  Panels of 16 columns; a panel's rows (group order) are cut into
+// blocks of 128, zero-padded to a whole block.  Block (panel p, block b) is
+// 1 KB: lane l owns 16 bytes = 4 words, word j holding the 8 codes of column
+// 16 p + l % 16, rows 128 b + 32 j + 8 (l / 16) .. +7, row +e in nibble e —
+// the B operand of MFMA step j of the block, one 1 KB load per wave.
 #include "wq_device.hpp"
 #include "wq_internal.h"
 
 namespace wq {
 
-// Widest panel whose count spreads over kTargetCUs compute units in whole
-// rounds with at most 12% idle (each workgroup then walks a contiguous run of
-// panels); otherwise the narrowest width dividing N.
-static int panel_width_4(int N) {
-  int narrowest = 4;
-  for (int P : {32, 16, 8, 4}) {
-    if (N % P) continue;
-    const int np = N / P, rounds = (np + kTargetCUs - 1) / kTargetCUs;
-    if ((long long)rounds * kTargetCUs * 100 <= 112LL * np) return P;
-    narrowest = P;
-  }
-  return narrowest;
-}
+constexpr int kQ4Panel = 16;   // columns per panel (one MFMA tile)
+constexpr int kQ4Block = 128;  // rows per block (4 MFMA steps of 32)
+constexpr int kQ4Ring = 4;     // blocks in flight per wave
+constexpr int kQ4MaxRun = 8;   // panels a workgroup walks at most
+constexpr int kQ4Threads = 512;             // 8 waves: two per SIMD
+constexpr int kQ4Waves = kQ4Threads / 64;
+// Padding (halves) after each LDS row of X: 4 octets, so the 16-byte operand
+// reads of rows m and octets o fall on banks 4 m + o (mod 16 groups).
+constexpr int kQ4RowPad = 32;
 
+// PanelPlan for the 4-bit layout: P = 16, npanels = ceil(N / 16),
+// u = blocks per panel = ceil(K / 128); cpp, nsa and bw are unused.
 PanelPlan plan_q4(int K, int N, int G) {
+  (void)G;
   PanelPlan p{};
-  p.P = panel_width_4(N);
-  p.cpp = p.P / 4;
-  p.npanels = N / p.P;
-  const int ns = kThreads / p.cpp;
-  const int ku = K / 8;                       // word rows
-  p.bw = (G / 8) < 16 ? (G / 8) : 16;         // word rows per batch: inside one group
-  while (p.bw > 4 && ns * p.bw >= 2 * ku) p.bw /= 2;  // keep most slots busy
-  p.u = p.bw * ((ku + ns * p.bw - 1) / (ns * p.bw));
-  p.nsa = (ku + p.u - 1) / p.u;
-  p.packed_bytes = (size_t)p.npanels * p.u * p.nsa * p.cpp * 16;
+  p.P = kQ4Panel;
+  p.cpp = 0;
+  p.npanels = (N + kQ4Panel - 1) / kQ4Panel;
+  p.u = (K + kQ4Block - 1) / kQ4Block;
+  p.nsa = 0;
+  p.bw = 0;
+  p.packed_bytes = (size_t)p.npanels * p.u * 1024;
   return p;
 }
 
-// One LDS copy of X holds K rounded up to 64 rows (the swizzle below permutes
-// word rows inside aligned groups of 8).
-static inline int q4_kpad(int K) { return (K + 63) / 64 * 64; }
-
-// Rows of X staged per launch: the LDS copies of X (MT * Kpad halves) stay
-// <= 64 KB (plus the small cross-wave reduction buffer).
+// Rows of X staged per launch: the LDS copies of X (MT rows of u * 128
+// halves plus padding) stay <= 96 KB.
 int q4_max_mt(int K) {
+  const size_t kb = (size_t)(K + kQ4Block - 1) / kQ4Block * kQ4Block + kQ4RowPad;
   int mt = 8;
-  while (mt > 1 && (size_t)mt * q4_kpad(K) * 2 > 65536) mt /= 2;
+  while (mt > 1 && (size_t)mt * kb * 2 > 98304) mt /= 2;
   return mt;
 }
 
-// LDS word-row swizzle: slots that share a wave read different banks.  It
-// only flips the low 3 bits of r, so it stays inside r's aligned 8-row group.
-__device__ __forceinline__ int q4_swz(int r) { return r ^ ((r >> 4) & 7); }
-// Half-word index of row i (in group order) inside one LDS copy of X.
-__device__ __forceinline__ int q4_lds_half(int i) {
-  const int r = i >> 3, j = i & 7;
-  return (q4_swz(r) * 4 + (j & 3)) * 2 + (j >> 2);
+// Code pairs of one word as fp16 subnormals: (e, e + 4) for e = 0..3, i.e.
+// the 8 rows in the order 0 4 1 5 2 6 3 7 — the order X takes in LDS.
+__device__ __forceinline__ void q4_mfma_pairs(uint32_t w, h2 out[4]) {
+  out[0] = as_h2(w & 0x000F000Fu);
+  out[1] = as_h2((w >> 4) & 0x000F000Fu);
+  out[2] = as_h2((w >> 8) & 0x000F000Fu);
+  out[3] = as_h2((w >> 12) & 0x000F000Fu);
 }
+// Position of row e (0..7) of an octet among the 8 halves of an operand.
+__device__ __forceinline__ int q4_pos(int e) { return 2 * (e & 3) + (e >> 2); }
 
 // ---------------------------------------------------------------------------
-// Offline re-layout: one thread per 16-byte piece (4 columns of a word row).
+// Offline re-layout: one thread per (panel, block, lane) 16-byte piece.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void q4_prepack_kernel(const uint32_t* __restrict__ qw,
                                                               const int* __restrict__ perm,
                                                               uint32_t* __restrict__ out, int K,
-                                                              int N, PanelPlan p) {
-  const int nta = p.nsa * p.cpp;
+                                                              int N, int nb, int npanels) {
   const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
-  const size_t total = (size_t)p.npanels * p.u * nta;
-  if (idx >= total) return;
-  const int t = (int)(idx % nta);
-  const size_t pi = idx / nta;
-  const int i = (int)(pi % p.u), panel = (int)(pi / p.u);
-  const int s = t / p.cpp, c = t % p.cpp;
-  const int r = s * p.u + i;  // word row in group order
-  const int col0 = panel * p.P + 4 * c;
+  if (idx >= (size_t)npanels * nb * 64) return;
+  const int l = (int)(idx % 64);
+  const size_t pb = idx / 64;
+  const int b = (int)(pb % nb), panel = (int)(pb / nb);
+  const int n = panel * kQ4Panel + l % 16;
 #pragma unroll
-  for (int cc = 0; cc < 4; ++cc) {
-    uint32_t word = 0;  // padding rows: u = 0, so they add nothing whatever x is
-    if (r < K / 8) {
-      word = 0;
+  for (int j = 0; j < 4; ++j) {
+    const int i0 = kQ4Block * b + 32 * j + 8 * (l / 16);
+    uint32_t word = 0;  // padding rows and columns: u = 0, met by x = 0 or dropped
+    if (n < N) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int src = perm ? perm[8 * r + j] : 8 * r + j;
-        const uint32_t sw = qw[(size_t)(src >> 3) * N + col0 + cc];
-        word |= ((sw >> (4 * (src & 7))) & 15u) << (4 * j);
+      for (int e = 0; e < 8; ++e) {
+        const int i = i0 + e;
+        if (i >= K) break;
+        const int src = perm ? perm[i] : i;
+        const uint32_t sw = qw[(size_t)(src >> 3) * N + n];
+        word |= ((sw >> (4 * (src & 7))) & 15u) << (4 * e);
       }
     }
-    out[idx * 4 + cc] = word;
+    out[idx * 4 + j] = word;
   }
 }
 
 // ---------------------------------------------------------------------------
 // The fused product.
+//
+// A workgroup walks a contiguous run of panels; its 8 waves split every
+// panel's blocks into contiguous, group-aligned ranges and keep kQ4Ring
+// blocks in flight.  Each wave leaves its partial tile per panel in LDS; one
+// barrier at the end, then the workgroup sums the waves and writes Y.
+// NSC: scale loads per block (4 for G = 32, 2 for G = 64, 1 for G >= 128).
 // ---------------------------------------------------------------------------
-template <int MT, int CPP, int BW>
-__global__ __launch_bounds__(kThreads) void q4_panel_kernel(
+template <int MT, int NSC>
+__global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
     const _Float16* __restrict__ X, const uint8_t* __restrict__ Wp,
     const _Float16* __restrict__ scales, const int* __restrict__ invperm,
-    _Float16* __restrict__ Y, int M, int K, int N, int G, int u, int nsa, int npanels,
-    int packed_bytes) {
-  constexpr int P = 4 * CPP;
-  constexpr int V = 4 * MT;  // results per chunk: [m][4 columns]
-  constexpr int LOWBIT = CPP == 1 ? 0 : CPP == 2 ? 1 : CPP == 4 ? 2 : 3;
-  constexpr int LEFT = bfly_left<V, LOWBIT>();
+    _Float16* __restrict__ Y, int M, int K, int N, int G, int nb, int npanels, int packed_bytes) {
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  typedef float f4 __attribute__((ext_vector_type(4)));
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int kpad = (K + 63) / 64 * 64;  // halves per LDS copy of X
-  _Float16* xh = reinterpret_cast<_Float16*>(smem);  // MT copies of kpad halves
-  float* red = reinterpret_cast<float*>(smem + (size_t)MT * kpad * 2);  // [4 waves][CPP][V]
+  const int rs = nb * kQ4Block + kQ4RowPad;                           // halves per LDS row of X
+  const int xhalves = rs * MT;                                          // halves of X in LDS
+  _Float16* xa = reinterpret_cast<_Float16*>(smem);                     // [MT][octet][8], padded rows
+  float* red = reinterpret_cast<float*>(smem + (size_t)xhalves * 2);  // [run][wave][MT][16]
 
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  // This workgroup's contiguous run of panels.
+  const int t = threadIdx.x, lane = t & 63;
+  // Uniform across the wave: keeps the block range and cursors in scalar
+  // registers and their branches scalar.
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int p_begin = (int)((long long)blockIdx.x * npanels / gridDim.x);
   const int p_end = (int)((long long)(blockIdx.x + 1) * npanels / gridDim.x);
-  const int nta = nsa * CPP;
-  const int c = t % CPP, s = t / CPP;
-  const bool active = t < nta;
-  const int ku = K / 8;
-  const int nb = u / BW;                        // batches per panel
-  const int nunits = (p_end - p_begin) * nb;    // (panel, batch) units of the run
+  const int npr = p_end - p_begin;
+
+  // Blocks of this wave: a group-aligned contiguous range.
+  const int spg = G / 32;  // MFMA steps per group
+  const int bpg = G >= kQ4Block ? G / kQ4Block : 1;
+  const int nsplit = nb / bpg;
+  const int blo = (wave * nsplit / kQ4Waves) * bpg, bhi = ((wave + 1) * nsplit / kQ4Waves) * bpg;
+  const int nbw = bhi - blo;
+  const int nitems = npr * nbw;
 
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wp, packed_bytes);
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, (K / G) * N * 2);
+  const int col = lane & 15;
 
-  // A unit's loads: its scale pair first, then its BW weight pieces.  Units
-  // past the end of the run load nothing (out-of-range offsets), so the loads
-  // need no branch.
-  u32x4 w0[BW], w1[BW], w2[BW];
-  uint2 sc0, sc1, sc2;
-  auto load_unit = [&](u32x4* dst, uint2& sc, int q) {
-    const bool ok = active && q < nunits;
-    const int panel = p_begin + q / nb, b = q % nb;
-    const int r0 = s * u + b * BW;
-    const int soff = (ok && r0 < ku) ? (((8 * r0) / G) * N + panel * P + 4 * c) * 2 : kOutOfRange;
-    const unsigned long long v64 = __builtin_bit_cast(
-        unsigned long long, __builtin_amdgcn_raw_buffer_load_b64(sr, soff, 0, 0));
-    sc = make_uint2((uint32_t)v64, (uint32_t)(v64 >> 32));
-    const int wbase = ((panel * u + b * BW) * nta + t) * 16;
+  int lbpg = 0;  // log2(bpg): G is a power of two
+  while ((1 << lbpg) < bpg) ++lbpg;
+
+  // Ring buffers: one 16-byte word quadruple and NSC scale bits per block.
+  u32x4 wb0, wb1, wb2, wb3;
+  uint32_t sc0[NSC], sc1[NSC], sc2[NSC], sc3[NSC];
+  // Load cursor (panel of the run, block) walks the wave's blocks in order;
+  // past the end it loads nothing (out-of-range offsets).
+  int lp = nbw > 0 ? 0 : npr, lb = blo;
+  int woff = ((p_begin * nb + blo) * 64 + lane) * 16;
+  auto load_item = [&](u32x4& w, uint32_t (&sc)[NSC]) {
+    const bool ok = lp < npr;
+    const int n = (p_begin + lp) * kQ4Panel + col;
 #pragma unroll
-    for (int i = 0; i < BW; ++i) dst[i] = buffer_stream(wr, ok ? wbase + i * nta * 16 : kOutOfRange);
+    for (int k = 0; k < NSC; ++k) {
+      const int g = NSC == 1 ? (lb >> lbpg) : lb * NSC + k;  // the group step k closes
+      sc[k] = __builtin_amdgcn_raw_buffer_load_b16(sr, (ok && n < N) ? (g * N + n) * 2 : kOutOfRange,
+                                                   0, 0);
+    }
+    // The weights last: waiting for them covers the scales of the block.
+    w = buffer_stream(wr, ok ? woff : kOutOfRange);
+    woff += 1024;
+    if (++lb == bhi) {
+      lb = blo;
+      ++lp;
+      woff = (((p_begin + lp) * nb + blo) * 64 + lane) * 16;
+    }
   };
-
-  // Scatter X into LDS through the inverse permutation (group order), once
-  // for the whole run.  Thread t takes the 8-row chunks t, t + 256, ...; for
-  // each chunk the permutation is read once and reused for every row of X.
-  // All loads of a round of chunks go out before any LDS write; the first two
-  // units of the weight stream go out right after the first round's loads.
-  constexpr int CR = MT >= 8 ? 1 : 2;  // chunks per thread per round
+  // Stage X through the inverse permutation: row k of X goes to group-order
+  // row i = invperm[k], octet i / 8, position q4_pos(i % 8).  Rows past K
+  // (block padding) and rows m >= M stay zero.  The loads of the first round
+  // of chunks go out first, then the first kQ4Ring blocks of the weight
+  // stream, so the scatter waits only for its own data.
   const int nchunk = K / 8;
+  constexpr int CR = 2;  // chunks per thread per round
+  // Buffer loads: chunks past K and rows past M read zero without a branch.
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, M * K * 2);
+  const __amdgpu_buffer_rsrc_t pr_ = make_rsrc(invperm, invperm ? K * 4 : 0);
   auto stage_load = [&](int c0, u32x4 (&pv)[CR][2], u32x4 (&xq)[CR][MT]) {
 #pragma unroll
     for (int r = 0; r < CR; ++r) {
-      const int ch = c0 + r * kThreads;
+      const int ch = c0 + r * kQ4Threads;
       const bool ok = ch < nchunk;
-      if (invperm) {
-        pv[r][0] = ok ? *reinterpret_cast<const u32x4*>(invperm + 8 * ch) : (u32x4){0u, 0u, 0u, 0u};
-        pv[r][1] = ok ? *reinterpret_cast<const u32x4*>(invperm + 8 * ch + 4) : (u32x4){0u, 0u, 0u, 0u};
-      }
+      pv[r][0] = __builtin_amdgcn_raw_buffer_load_b128(pr_, ok ? 32 * ch : kOutOfRange, 0, 0);
+      pv[r][1] = __builtin_amdgcn_raw_buffer_load_b128(pr_, ok ? 32 * ch + 16 : kOutOfRange, 0, 0);
 #pragma unroll
       for (int m = 0; m < MT; ++m)
-        xq[r][m] = (ok && m < M) ? *reinterpret_cast<const u32x4*>(X + (size_t)m * K + 8 * ch)
-                                 : (u32x4){0u, 0u, 0u, 0u};
+        xq[r][m] = __builtin_amdgcn_raw_buffer_load_b128(
+            xr, (ok && m < M) ? (m * K + 8 * ch) * 2 : kOutOfRange, 0, 0);
     }
   };
   auto stage_write = [&](int c0, const u32x4 (&pv)[CR][2], const u32x4 (&xq)[CR][MT]) {
 #pragma unroll
     for (int r = 0; r < CR; ++r) {
-      const int ch = c0 + r * kThreads;
+      const int ch = c0 + r * kQ4Threads;
       if (ch >= nchunk) break;
-      int dst[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) dst[j] = invperm ? (int)pv[r][j >> 2][j & 3] : 8 * ch + j;
+      for (int j = 0; j < 8; ++j) {
+        const int i = invperm ? (int)pv[r][j >> 2][j & 3] : 8 * ch + j;
+        const int base = (i >> 3) * 8 + q4_pos(i & 7);
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int m = 0; m < MT; ++m) {
           const uint32_t word = xq[r][m][j >> 1];
           const uint16_t bits = (j & 1) ? (uint16_t)(word >> 16) : (uint16_t)(word & 0xFFFFu);
-          reinterpret_cast<uint16_t*>(xh)[(size_t)m * kpad + q4_lds_half(dst[j])] = bits;
+          reinterpret_cast<uint16_t*>(xa)[m * rs + base] = bits;
         }
+      }
     }
   };
   {
     u32x4 pv[CR][2], xq[CR][MT];
     stage_load(t, pv, xq);
-    load_unit(w0, sc0, 0);
-    load_unit(w1, sc1, 1);
+    load_item(wb0, sc0);
+    load_item(wb1, sc1);
+    load_item(wb2, sc2);
+    load_item(wb3, sc3);
+    // Rows m < MT beyond K (block padding): zero.  The reduction tiles: zero.
+    uint32_t* xz = reinterpret_cast<uint32_t*>(xa);
+    const int padw = (rs - K) / 2;  // words per row past K
+    for (int h = t; h < padw * MT; h += kQ4Threads) xz[(h / padw) * (rs / 2) + K / 2 + h % padw] = 0u;
+    for (int r = t; r < kQ4MaxRun * kQ4Waves * MT * 16; r += kQ4Threads) red[r] = 0.0f;
     stage_write(t, pv, xq);
   }
-  for (int c0 = t + CR * kThreads; c0 < nchunk; c0 += CR * kThreads) {
+  for (int c0 = t + CR * kQ4Threads; c0 < nchunk; c0 += CR * kQ4Threads) {
     u32x4 pv[CR][2], xq[CR][MT];
     stage_load(c0, pv, xq);
     stage_write(c0, pv, xq);
   }
   __syncthreads();
 
-  const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-  float accT[MT][4];
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) accT[m][j] = 0.0f;
+  const h8 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f,
+                   (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
+  // Operand rows past MT read row MT - 1: rows of the product depend only on
+  // their own row of X, and rows >= MT are never stored.
+  const int am = (lane & 15) < MT ? (lane & 15) : MT - 1, aq = lane >> 4;
+  const _Float16* xrow = xa + (size_t)am * rs + aq * 8;
+  f4 C0 = {0.0f, 0.0f, 0.0f, 0.0f}, C1 = C0, S0 = C0, S1 = C0, tot = C0;
 
-  // Units go through a ring of three register buffers: while unit q is
-  // multiplied, units q + 1 and q + 2 are in flight.  The loop is unrolled by
-  // three so every buffer keeps a fixed set of registers (a register copy of
-  // a buffer would wait for its loads).
-  auto step = [&](int q, const u32x4* w, const uint2& sraw, u32x4* pre, uint2& pre_sc) {
-    load_unit(pre, pre_sc, q + 2);
-    if (q >= nunits) return;
-    const int panel = p_begin + q / nb, b = q % nb;
-    const int r0 = s * u + b * BW;  // first word row of the batch (group order)
-    // Sum of x over the batch: the CPP lanes of a slot split the word rows.
-    float xs[MT];
+  // One block: 4 MFMA steps (and 4 against the ones, two chains each) and the
+  // group closes; at the wave's last block of a panel its partial tile goes
+  // to LDS.
+  int cp = 0, cb = blo;  // compute cursor: panel of the run, block
+  // Operands of X for the block about to be multiplied, read one block ahead
+  // (X is the same for every panel, so after a wave's last block comes blo).
+  h8 apf[4];
+  if (nbw > 0) {
 #pragma unroll
-    for (int m = 0; m < MT; ++m) xs[m] = 0.0f;
-    for (int i = c; i < BW; i += CPP) {
-      const int r = r0 + i;
-      if (r < ku) {
+    for (int j = 0; j < 4; ++j) apf[j] = *reinterpret_cast<const h8*>(xrow + (16 * blo + 4 * j) * 8);
+  }
+  auto compute = [&](const u32x4& w, const uint32_t (&sc)[NSC]) {
+    const int pi = cp, b = cb;
+    h8 a[4];
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          const u32x4 xv = *reinterpret_cast<const u32x4*>(xh + (size_t)m * kpad + q4_swz(r) * 8);
+    for (int j = 0; j < 4; ++j) a[j] = apf[j];
+    const int bn = b + 1 == bhi ? blo : b + 1;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) xs[m] = dot2(as_h2(xv[j]), ones, xs[m]);
+    for (int j = 0; j < 4; ++j) apf[j] = *reinterpret_cast<const h8*>(xrow + (16 * bn + 4 * j) * 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      h2 pr[4];
+      q4_mfma_pairs(w[j], pr);
+      const h8 bv = {pr[0].x, pr[0].y, pr[1].x, pr[1].y, pr[2].x, pr[2].y, pr[3].x, pr[3].y};
+      if (j & 1) {
+        C1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], bv, C1, 0, 0, 0);
+        S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], ones, S1, 0, 0, 0);
+      } else {
+        C0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], bv, C0, 0, 0, 0);
+        S0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], ones, S0, 0, 0, 0);
+      }
+      bool close;
+      int k = 0;
+      if constexpr (NSC > 1) {
+        close = ((j + 1) % (4 / NSC)) == 0;
+        k = j / (4 / NSC);
+      } else {
+        close = j == 3 && ((b + 1) & (bpg - 1)) == 0;
+      }
+      if (close) {
+        const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sc[k]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          tot[r] = __builtin_fmaf(s, __builtin_fmaf(S0[r] + S1[r], -8.0f / kTwo24, C0[r] + C1[r]), tot[r]);
+          C0[r] = C1[r] = S0[r] = S1[r] = 0.0f;
         }
       }
     }
+    if (++cb == bhi) {
+      // The wave's share of panel pi: rows 4 (lane / 16) + r, column lane % 16.
 #pragma unroll
-    for (int o = 1; o < CPP; o <<= 1)
-#pragma unroll
-      for (int m = 0; m < MT; ++m) xs[m] += __shfl_xor(xs[m], o);
-
-    // Codes are u = q + 8: start at -8 * sum(x) (2^-24 units).  acc0 holds the
-    // even nibbles (u * 2^-24), acc4 the odd ones (16u * 2^-24).
-    float acc0[MT][4], acc4[MT][4];
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc0[m][j] = xs[m] * (-8.0f / kTwo24);
-        acc4[m][j] = 0.0f;
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * (lane >> 4) + r;
+        if (m < MT) red[((pi * kQ4Waves + wave) * MT + m) * 16 + col] = tot[r];
+        tot[r] = 0.0f;
       }
-#pragma unroll
-    for (int i = 0; i < BW; ++i) {
-      const int r = r0 + i < ku ? r0 + i : ku - 1;  // rows past K: codes are 0, any x
-      u32x4 xv[MT];
-#pragma unroll
-      for (int m = 0; m < MT; ++m) xv[m] = *reinterpret_cast<const u32x4*>(xh + (size_t)m * kpad + q4_swz(r) * 8);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        h2 pr[4];
-        q4_pairs_sub(w[i][j], pr);
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          acc0[m][j] = dot2(pr[0], as_h2(xv[m][0]), acc0[m][j]);
-          acc4[m][j] = dot2(pr[1], as_h2(xv[m][1]), acc4[m][j]);
-          acc0[m][j] = dot2(pr[2], as_h2(xv[m][2]), acc0[m][j]);
-          acc4[m][j] = dot2(pr[3], as_h2(xv[m][3]), acc4[m][j]);
-        }
-      }
-    }
-    const h2 s01 = as_h2(sraw.x), s23 = as_h2(sraw.y);
-    const float sc[4] = {(float)s01.x, (float)s01.y, (float)s23.x, (float)s23.y};
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        accT[m][j] = __builtin_fmaf(__builtin_fmaf(acc4[m][j], 0.0625f, acc0[m][j]), sc[j], accT[m][j]);
-
-    if (b == nb - 1) {
-      // Panel done: reduce over the slots of each chunk and write P x MT results.
-      float v[V];
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v[m * 4 + j] = accT[m][j];
-          accT[m][j] = 0.0f;
-        }
-      bfly<V, 5, LOWBIT>(v, lane);
-      bool owner;
-      const int base = bfly_base<V, LOWBIT>(lane, owner);
-      if (owner) {
-#pragma unroll
-        for (int j = 0; j < LEFT; ++j) red[(wave * CPP + c) * V + base + j] = v[j];
-      }
-      __syncthreads();
-      for (int r = t; r < CPP * V; r += kThreads) {
-        const int rc = r / V, idx = r % V;
-        const int m = idx / 4, col = panel * P + 4 * rc + (idx % 4);
-        float sum = 0.0f;
-#pragma unroll
-        for (int w2 = 0; w2 < kThreads / 64; ++w2) sum += red[(w2 * CPP + rc) * V + idx];
-        if (m < M) Y[(size_t)m * N + col] = (_Float16)(sum * kTwo24);
-      }
-      __syncthreads();  // red is rewritten by the next panel
+      cb = blo;
+      ++cp;
     }
   };
-  for (int q = 0; q < nunits; q += 3) {
-    step(q, w0, sc0, w2, sc2);
-    step(q + 1, w1, sc1, w0, sc0);
-    step(q + 2, w2, sc2, w1, sc1);
+  auto step = [&](int q, u32x4& w, uint32_t (&sc)[NSC]) {
+    if (q < nitems) compute(w, sc);
+    // Unconditional (out-of-range past the end), so the loads of every ring
+    // slot keep one issue order and each wait covers just its own block.
+    load_item(w, sc);
+  };
+  for (int q = 0; q < nitems; q += kQ4Ring) {
+    step(q, wb0, sc0);
+    step(q + 1, wb1, sc1);
+    step(q + 2, wb2, sc2);
+    step(q + 3, wb3, sc3);
+  }
+  __syncthreads();
+  for (int r = t; r < npr * MT * 16; r += kQ4Threads) {
+    const int pi = r / (MT * 16), m = (r / 16) % MT, c = r % 16;
+    const int n = (p_begin + pi) * kQ4Panel + c;
+    const float* v = red + (pi * kQ4Waves * MT + m) * 16 + c;
+    float sum = 0.0f;
+#pragma unroll
+    for (int w2 = 0; w2 < kQ4Waves; ++w2) sum += v[w2 * MT * 16];
+    if (m < M && n < N) Y[(size_t)m * N + n] = (_Float16)(sum * kTwo24);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Bit-exact check: packed pieces through q4_pairs_sub back to signed codes in
-// the original row order (perm), one thread per piece.
+// Bit-exact check: each packed piece through q4_mfma_pairs back to signed
+// codes in the original row order (perm), one thread per piece.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void q4_unpack_kernel(const uint8_t* __restrict__ Wp,
                                                              const int* __restrict__ perm,
                                                              int8_t* __restrict__ codes, int K,
-                                                             int N, PanelPlan p) {
-  const int nta = p.nsa * p.cpp;
+                                                             int N, int nb, int npanels) {
   const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
-  const size_t total = (size_t)p.npanels * p.u * nta;
-  if (idx >= total) return;
-  const int t = (int)(idx % nta);
-  const size_t pi = idx / nta;
-  const int i = (int)(pi % p.u), panel = (int)(pi / p.u);
-  const int s = t / p.cpp, c = t % p.cpp;
-  const int r = s * p.u + i;
-  if (r >= K / 8) return;
-  const int col0 = panel * p.P + 4 * c;
+  if (idx >= (size_t)npanels * nb * 64) return;
+  const int l = (int)(idx % 64);
+  const size_t pb = idx / 64;
+  const int b = (int)(pb % nb), panel = (int)(pb / nb);
+  const int n = panel * kQ4Panel + l % 16;
+  if (n >= N) return;
   const u32x4 w = *reinterpret_cast<const u32x4*>(Wp + idx * 16);
 #pragma unroll
-  for (int cc = 0; cc < 4; ++cc) {
+  for (int j = 0; j < 4; ++j) {
     h2 pr[4];
-    q4_pairs_sub(w[cc], pr);
+    q4_mfma_pairs(w[j], pr);
+    const int i0 = kQ4Block * b + 32 * j + 8 * (l / 16);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t bits = as_u32(pr[j]);
-      const int sh = (j & 1) ? 4 : 0;  // pairs 1 and 3 sit at bit 4 of each half
-      const int ulo = (int)((bits & 0xFFFFu) >> sh), uhi = (int)((bits >> 16) >> sh);
-      const int ia = 8 * r + j, ib = ia + 4;
-      const int da = perm ? perm[ia] : ia, db = perm ? perm[ib] : ib;
-      codes[(size_t)da * N + col0 + cc] = (int8_t)(ulo - 8);
-      codes[(size_t)db * N + col0 + cc] = (int8_t)(uhi - 8);
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t bits = as_u32(pr[e]);
+      const int ia = i0 + e, ib = i0 + e + 4;
+      if (ia < K) codes[(size_t)(perm ? perm[ia] : ia) * N + n] = (int8_t)((int)(bits & 0xFFFFu) - 8);
+      if (ib < K) codes[(size_t)(perm ? perm[ib] : ib) * N + n] = (int8_t)((int)(bits >> 16) - 8);
     }
   }
 }
@@ -360,69 +366,51 @@ __global__ __launch_bounds__(kThreads) void q4_unpack_kernel(const uint8_t* __re
 hipError_t launch_q4_prepack(const int32_t* qw, const int32_t* perm, void* out, int K, int N, int G,
                              hipStream_t s) {
   const PanelPlan p = plan_q4(K, N, G);
-  const size_t total = (size_t)p.npanels * p.u * p.nsa * p.cpp;
+  const size_t total = (size_t)p.npanels * p.u * 64;
   hipLaunchKernelGGL(q4_prepack_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)),
                      dim3(kThreads), 0, s, reinterpret_cast<const uint32_t*>(qw), perm,
-                     reinterpret_cast<uint32_t*>(out), K, N, p);
+                     reinterpret_cast<uint32_t*>(out), K, N, p.u, p.npanels);
   return hipGetLastError();
 }
 
 hipError_t launch_q4_unpack(const void* packed, const int32_t* perm, int8_t* codes, int K, int N,
                             int G, hipStream_t s) {
   const PanelPlan p = plan_q4(K, N, G);
-  const size_t total = (size_t)p.npanels * p.u * p.nsa * p.cpp;
+  const size_t total = (size_t)p.npanels * p.u * 64;
   hipLaunchKernelGGL(q4_unpack_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)),
                      dim3(kThreads), 0, s, reinterpret_cast<const uint8_t*>(packed), perm, codes, K,
-                     N, p);
+                     N, p.u, p.npanels);
   return hipGetLastError();
 }
 
-template <int MT, int CPP, int BW>
+template <int MT, int NSC>
 static hipError_t launch_q4_t(const void* X, const void* packed, const void* scales,
                               const int32_t* invperm, void* Y, int M, int K, int N, int G,
                               const PanelPlan& p, hipStream_t s) {
-  const size_t xb = (size_t)MT * q4_kpad(K) * 2, rb = (size_t)kThreads / 64 * CPP * 4 * MT * 4;
   const int cus = device_cus();
-  const int grid = p.npanels < cus ? p.npanels : cus;
-  if (xb + rb > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&q4_panel_kernel<MT, CPP, BW>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)(xb + rb));
+  int grid = p.npanels < cus ? p.npanels : cus;
+  if ((p.npanels + grid - 1) / grid > kQ4MaxRun) grid = (p.npanels + kQ4MaxRun - 1) / kQ4MaxRun;
+  const size_t lds = ((size_t)p.u * kQ4Block + kQ4RowPad) * MT * 2 + (size_t)kQ4MaxRun * kQ4Waves * MT * 16 * 4;
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&q4_mfma_kernel<MT, NSC>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((q4_panel_kernel<MT, CPP, BW>), dim3(grid), dim3(kThreads), xb + rb, s,
+  hipLaunchKernelGGL((q4_mfma_kernel<MT, NSC>), dim3(grid), dim3(kQ4Threads), lds, s,
                      reinterpret_cast<const _Float16*>(X), reinterpret_cast<const uint8_t*>(packed),
                      reinterpret_cast<const _Float16*>(scales), invperm,
-                     reinterpret_cast<_Float16*>(Y), M, K, N, G, p.u, p.nsa, p.npanels,
+                     reinterpret_cast<_Float16*>(Y), M, K, N, G, p.u, p.npanels,
                      (int)p.packed_bytes);
   return hipGetLastError();
-}
-
-// Batch size: the plan's (one group, at most 16 word rows), smaller for
-// larger MT to stay inside the register file.  Any power of two up to the
-// plan's batch divides u, so the packed layout does not depend on it.
-template <int MT, int CPP>
-static hipError_t launch_q4_bw(const void* X, const void* packed, const void* scales,
-                               const int32_t* invperm, void* Y, int M, int K, int N, int G,
-                               const PanelPlan& p, hipStream_t s) {
-  constexpr int cap = MT >= 8 ? 4 : (MT >= 4 ? 8 : 16);
-  const int bw = p.bw < cap ? p.bw : cap;
-  switch (bw) {
-    case 4: return launch_q4_t<MT, CPP, 4>(X, packed, scales, invperm, Y, M, K, N, G, p, s);
-    case 8: return launch_q4_t<MT, CPP, (cap < 8 ? 4 : 8)>(X, packed, scales, invperm, Y, M, K, N, G, p, s);
-    default: return launch_q4_t<MT, CPP, cap>(X, packed, scales, invperm, Y, M, K, N, G, p, s);
-  }
 }
 
 template <int MT>
 static hipError_t launch_q4_mt(const void* X, const void* packed, const void* scales,
                                const int32_t* invperm, void* Y, int M, int K, int N, int G,
                                const PanelPlan& p, hipStream_t s) {
-  switch (p.cpp) {
-    case 1: return launch_q4_bw<MT, 1>(X, packed, scales, invperm, Y, M, K, N, G, p, s);
-    case 2: return launch_q4_bw<MT, 2>(X, packed, scales, invperm, Y, M, K, N, G, p, s);
-    case 4: return launch_q4_bw<MT, 4>(X, packed, scales, invperm, Y, M, K, N, G, p, s);
-    default: return launch_q4_bw<MT, 8>(X, packed, scales, invperm, Y, M, K, N, G, p, s);
-  }
+  if (G == 32) return launch_q4_t<MT, 4>(X, packed, scales, invperm, Y, M, K, N, G, p, s);
+  if (G == 64) return launch_q4_t<MT, 2>(X, packed, scales, invperm, Y, M, K, N, G, p, s);
+  return launch_q4_t<MT, 1>(X, packed, scales, invperm, Y, M, K, N, G, p, s);
 }
 
 hipError_t launch_q4_group(const void* X, const void* packed, const void* scales,
