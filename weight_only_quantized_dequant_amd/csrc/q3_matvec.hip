@@ -26,6 +26,11 @@
 
 namespace wq {
 
+// Threads of the product's workgroup: 8 waves (two per SIMD, one wave's
+// arithmetic overlapping another's loads) for the large shapes, 4 waves for
+// the small ones, where the shorter per-wave staging wins.
+static int q3_threads(int K, int N) { return (K >= 8192 || N >= 8192) ? 512 : 256; }
+
 // Widest panel whose count spreads over kTargetCUs compute units in whole
 // rounds with at most 12% idle (each workgroup then walks a contiguous run of
 // panels); otherwise the narrowest width dividing N.
@@ -45,7 +50,8 @@ PanelPlan plan_q3(int K, int N) {
   p.P = panel_width_3(N);
   p.cpp = p.P / 4;
   p.npanels = N / p.P;
-  const int ns = kThreads / p.cpp;
+  p.threads = q3_threads(K, N);
+  const int ns = p.threads / p.cpp;
   const int ku = K / 32;  // blocks
   p.u = (ku + ns - 1) / ns;
   p.nsa = (ku + p.u - 1) / p.u;
@@ -83,8 +89,8 @@ __global__ __launch_bounds__(kThreads) void q3_prepack_kernel(const uint32_t* __
 // ---------------------------------------------------------------------------
 // The fused product.
 // ---------------------------------------------------------------------------
-template <bool F16, int CPP, int UB>
-__global__ __launch_bounds__(kThreads) void q3_panel_kernel(
+template <bool F16, int CPP, int THREADS>
+__global__ __launch_bounds__(THREADS) void q3_panel_kernel(
     const void* __restrict__ xv, const uint8_t* __restrict__ Wp, const void* __restrict__ sv,
     const void* __restrict__ zv, void* __restrict__ yv, int K, int N, int u, int nsa, int npanels,
     int packed_bytes) {
@@ -94,8 +100,10 @@ __global__ __launch_bounds__(kThreads) void q3_panel_kernel(
   constexpr int XW = F16 ? 1 : 2;  // LDS words per pair
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint32_t* xp = reinterpret_cast<uint32_t*>(smem);  // [K/2][XW]
-  __shared__ float xsum_w[kThreads / 64];
-  __shared__ float red[kThreads / 64][CPP][4];
+  constexpr int UB = 1;  // 32-row blocks per streamed unit
+  constexpr int NW = THREADS / 64;
+  __shared__ float xsum_w[NW];
+  __shared__ float red[NW][CPP][4];
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   // This workgroup's contiguous run of panels; a unit is UB blocks of a panel.
@@ -111,16 +119,22 @@ __global__ __launch_bounds__(kThreads) void q3_panel_kernel(
   const int nblk = active ? (blk0 + u <= ku ? u : (ku > blk0 ? ku - blk0 : 0)) : 0;
 
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wp, packed_bytes);
-  // Units past the end of the run load nothing (out-of-range offsets).
-  auto load_unit = [&](u32x4 (&w)[UB][3], int q) {
-    const int panel = p_begin + q / nr, i0 = (q % nr) * UB;
-    const bool ok = q < nunits;
+  // Load cursor (panel of the run, unit) walks the units in order; units past
+  // the end of the run load nothing (out-of-range offsets).
+  int lpi = 0, lu = 0;
+  auto load_unit = [&](u32x4 (&w)[UB][3]) {
+    const int panel = p_begin + lpi, i0 = lu * UB;
+    const bool ok = panel < p_end;
 #pragma unroll
     for (int i = 0; i < UB; ++i)
 #pragma unroll
       for (int j = 0; j < 3; ++j)
         w[i][j] = buffer_stream(
             wr, (ok && i0 + i < nblk) ? ((((panel * u + i0 + i) * 3 + j) * nta + t) * 16) : kOutOfRange);
+    if (++lu == nr) {
+      lu = 0;
+      ++lpi;
+    }
   };
 
   // 1. Activations.  The slots of a wave cover a contiguous range of 32-row
@@ -146,8 +160,8 @@ __global__ __launch_bounds__(kThreads) void q3_panel_kernel(
 
   // 2. The first two units of the weight stream.
   u32x4 w0[UB][3], w1[UB][3];
-  load_unit(w0, 0);
-  load_unit(w1, 1);
+  load_unit(w0);
+  load_unit(w1);
 
   // 3. Pairs into LDS in code-pair order (pre-scaled), and sum_k x[k].
   float my_sum = 0.0f;
@@ -211,9 +225,15 @@ __global__ __launch_bounds__(kThreads) void q3_panel_kernel(
 
   // One unit: multiply the buffer `w`, refill `pre` with unit q + 2; at the
   // last unit of a panel, reduce and write the panel's P outputs.
+  int cpi = 0, cu = 0;  // compute cursor: panel of the run, unit
   auto step = [&](int q, const u32x4 (&w)[UB][3], u32x4 (&pre)[UB][3]) {
     if (q >= nunits) return;
-    const int panel = p_begin + q / nr, i0 = (q % nr) * UB;
+    const int panel = p_begin + cpi, i0 = cu * UB;
+    const bool last = cu == nr - 1;
+    if (++cu == nr) {
+      cu = 0;
+      ++cpi;
+    }
 #pragma unroll
     for (int i = 0; i < UB; ++i) {
       if (i0 + i >= nblk) break;
@@ -242,8 +262,8 @@ __global__ __launch_bounds__(kThreads) void q3_panel_kernel(
         }
       }
     }
-    load_unit(pre, q + 2);  // `w` is consumed: its registers take unit q + 2
-    if (q % nr != nr - 1) return;
+    load_unit(pre);  // `w` is consumed: its registers take unit q + 2
+    if (!last) return;
 
     // Classes back to one sum per column (powers of two: exact rescale).
     float v[4];
@@ -273,10 +293,14 @@ __global__ __launch_bounds__(kThreads) void q3_panel_kernel(
     }
     __syncthreads();
     if (t < P) {
-      const float xsum = (xsum_w[0] + xsum_w[1]) + (xsum_w[2] + xsum_w[3]);
+      float xsum = 0.0f;
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) xsum += xsum_w[w2];
       const int rc = t / 4, j = t % 4;
       const int n = panel * P + t;
-      const float A = (red[0][rc][j] + red[1][rc][j]) + (red[2][rc][j] + red[3][rc][j]);
+      float A = 0.0f;
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) A += red[w2][rc][j];
       if constexpr (F16) {
         const float sc = (float)reinterpret_cast<const _Float16*>(sv)[n];
         const float ze = (float)reinterpret_cast<const _Float16*>(zv)[n];
@@ -347,14 +371,14 @@ hipError_t launch_q3_unpack(const void* packed, int8_t* codes, int K, int N, hip
   return hipGetLastError();
 }
 
-template <bool F16, int CPP, int UB>
+template <bool F16, int CPP, int THREADS>
 static hipError_t launch_q3_t(const void* x, const void* packed, const void* scales,
                               const void* zeros, void* y, int K, int N, const PanelPlan& p,
                               hipStream_t s) {
   const size_t lds = (size_t)(K / 2) * (F16 ? 4 : 8);
   const int cus = device_cus();
   const int grid = p.npanels < cus ? p.npanels : cus;
-  hipLaunchKernelGGL((q3_panel_kernel<F16, CPP, UB>), dim3(grid), dim3(kThreads), lds, s, x,
+  hipLaunchKernelGGL((q3_panel_kernel<F16, CPP, THREADS>), dim3(grid), dim3(THREADS), lds, s, x,
                      reinterpret_cast<const uint8_t*>(packed), scales, zeros, y, K, N, p.u, p.nsa,
                      p.npanels, (int)p.packed_bytes);
   return hipGetLastError();
@@ -367,7 +391,8 @@ template <bool F16, int CPP>
 static hipError_t launch_q3_ub(const void* x, const void* packed, const void* scales,
                                const void* zeros, void* y, int K, int N, const PanelPlan& p,
                                hipStream_t s) {
-  return launch_q3_t<F16, CPP, 1>(x, packed, scales, zeros, y, K, N, p, s);
+  return p.threads == 512 ? launch_q3_t<F16, CPP, 512>(x, packed, scales, zeros, y, K, N, p, s)
+                          : launch_q3_t<F16, CPP, 256>(x, packed, scales, zeros, y, K, N, p, s);
 }
 
 template <bool F16>

@@ -22,12 +22,13 @@ int device_cus();
 //            takes one panel or a contiguous run of them
 //   cpp      column chunks per panel (16 columns for int8, 4 for 3/4-bit)
 //   npanels  N / P
-//   u        K units per slot (rows for int8, word rows for 4-bit, 32-row
-//            blocks for 3-bit); slot s covers units [s*u, s*u + u)
+//   u        int8 / 3-bit: K units per slot (rows / 32-row blocks); slot s
+//            covers units [s*u, s*u + u).  4-bit: 128-row blocks per panel
 //   nsa      slots in use; threads in use = nsa * cpp
-//   bw       4-bit only: word rows per batch (inside one group)
+//   bw       unused (0)
+//   threads  3-bit only: threads of the product's workgroup (slots = threads / cpp)
 struct PanelPlan {
-  int P, cpp, npanels, u, nsa, bw;
+  int P, cpp, npanels, u, nsa, bw, threads;
   size_t packed_bytes;
 };
 
