@@ -71,7 +71,11 @@ __global__ __launch_bounds__(kThreads) void q8_prepack_kernel(const int8_t* __re
 // ---------------------------------------------------------------------------
 // The fused product.
 // ---------------------------------------------------------------------------
-template <int MT, int CPP>
+// FOLD (M = 1, 16-column panels, 16 u == G): the 16 lanes of a quarter-wave
+// hold the rows of one group, so their sums are reduced first and the
+// group's scale is applied once per column on the reduced value: one 4-byte
+// scale load per lane instead of four 16-byte loads, and one multiply.
+template <int MT, int CPP, bool FOLD>
 __global__ __launch_bounds__(kQ8Threads) void q8_panel_kernel(
     const _Float16* __restrict__ X, const uint8_t* __restrict__ Wp,
     const float* __restrict__ scales, _Float16* __restrict__ Y, int M, int K, int N, int G,
@@ -81,10 +85,16 @@ __global__ __launch_bounds__(kQ8Threads) void q8_panel_kernel(
   constexpr int LOWBIT = CPP == 1 ? 0 : 1;  // lane bit 0 selects the chunk when CPP == 2
   constexpr int LEFT = bfly_left<V, LOWBIT>();
   constexpr int RB = kQ8Batch;
+  static_assert(!FOLD || (MT == 1 && CPP == 1), "FOLD needs one row and 16-column panels");
   __shared__ float red[kQ8Threads / 64][CPP][V];
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int panel = blockIdx.x;
+  // Workgroups b and b + 8 run on the same XCD (dispatch is round-robin over
+  // the 8 XCDs).  When the panel count allows, they take neighbouring panels,
+  // which share the 128-byte lines of the fp32 scale rows, so each line is
+  // fetched into one XCD's L2 only.
+  const int bid = blockIdx.x;
+  const int panel = (gridDim.x % 16 == 0) ? (bid & ~15) + 2 * (bid & 7) + ((bid >> 3) & 1) : bid;
   const int nta = nsa * CPP;
   const int c = t % CPP, s = t / CPP;
   const bool active = t < nta;
@@ -100,6 +110,15 @@ __global__ __launch_bounds__(kQ8Threads) void q8_panel_kernel(
   for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int j = 0; j < 16; ++j) accT[m][j] = 0.0f;
+
+  // FOLD: this lane's scale, group (s u) / G, column col0 + lane % 16.
+  float fold_scale = 0.0f;
+  if constexpr (FOLD) {
+    const bool live0 = active && s * u < K;
+    fold_scale = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(
+                   sr, live0 ? (((s * u) / G) * N + col0 + (lane & 15)) * 4 : kOutOfRange, 0, 0));
+  }
 
   const int nb = u / RB;
   for (int b = 0; b < nb; ++b) {
@@ -117,10 +136,12 @@ __global__ __launch_bounds__(kQ8Threads) void q8_panel_kernel(
 #pragma unroll
     for (int i = 0; i < RB; ++i) w[i] = buffer_stream(wr, active ? wbase + i * nta * 16 : kOutOfRange);
     f32x4 sc[4];
-    const int soff = live ? ((row0 / G) * N + col0) * 4 : kOutOfRange;
+    if constexpr (!FOLD) {
+      const int soff = live ? ((row0 / G) * N + col0) * 4 : kOutOfRange;
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
-      sc[d] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, soff + 16 * d, 0, 0));
+      for (int d = 0; d < 4; ++d)
+        sc[d] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, soff + 16 * d, 0, 0));
+    }
 
     // The codes are u = q + 128, so every column starts at -128 * sum(x),
     // in the 2^-24 units of the subnormal products.
@@ -147,11 +168,16 @@ __global__ __launch_bounds__(kQ8Threads) void q8_panel_kernel(
             acc[m][4 * d + cc] = dot2(pr[cc], as_h2(xv[m][q]), acc[m][4 * d + cc]);
       }
     }
-    // One group per batch: scale once.
+    // One group per batch: scale once (FOLD: after the reduction below).
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) accT[m][j] = __builtin_fmaf(acc[m][j], sc[j >> 2][j & 3], accT[m][j]);
+      for (int j = 0; j < 16; ++j) {
+        if constexpr (FOLD)
+          accT[m][j] += acc[m][j];
+        else
+          accT[m][j] = __builtin_fmaf(acc[m][j], sc[j >> 2][j & 3], accT[m][j]);
+      }
   }
 
   // Reduce over the slots of a chunk: the lanes of a wave, then the waves.
@@ -160,12 +186,21 @@ __global__ __launch_bounds__(kQ8Threads) void q8_panel_kernel(
   for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int j = 0; j < 16; ++j) v[m * 16 + j] = accT[m][j];
-  bfly<V, 5, LOWBIT>(v, lane);
-  bool owner;
-  const int base = bfly_base<V, LOWBIT>(lane, owner);
-  if (owner) {
+  if constexpr (FOLD) {
+    // Lane bits 3..0 first: lane l keeps column l % 16 of its quarter-wave's
+    // group; scale it; then bits 5 and 4 add the wave's four groups.
+    bfly<16, 3, 0>(v, lane);
+    v[0] *= fold_scale;
+    bfly<1, 5, 4>(v, lane);
+    if (lane < 16) red[wave][0][lane] = v[0];
+  } else {
+    bfly<V, 5, LOWBIT>(v, lane);
+    bool owner;
+    const int base = bfly_base<V, LOWBIT>(lane, owner);
+    if (owner) {
 #pragma unroll
-    for (int j = 0; j < LEFT; ++j) red[wave][c][base + j] = v[j];
+      for (int j = 0; j < LEFT; ++j) red[wave][c][base + j] = v[j];
+    }
   }
   __syncthreads();
   for (int r = t; r < CPP * V; r += kQ8Threads) {
@@ -230,10 +265,10 @@ hipError_t launch_q8_unpack(const void* packed, int8_t* codes, int K, int N, hip
   return hipGetLastError();
 }
 
-template <int MT, int CPP>
+template <int MT, int CPP, bool FOLD = false>
 static hipError_t launch_q8_t(const void* X, const void* packed, const float* scales, void* Y,
                               int M, int K, int N, int G, const PanelPlan& p, hipStream_t s) {
-  hipLaunchKernelGGL((q8_panel_kernel<MT, CPP>), dim3(p.npanels), dim3(kQ8Threads), 0, s,
+  hipLaunchKernelGGL((q8_panel_kernel<MT, CPP, FOLD>), dim3(p.npanels), dim3(kQ8Threads), 0, s,
                      reinterpret_cast<const _Float16*>(X), reinterpret_cast<const uint8_t*>(packed),
                      scales, reinterpret_cast<_Float16*>(Y), M, K, N, G, p.u, p.nsa,
                      (int)p.packed_bytes);
@@ -243,6 +278,10 @@ static hipError_t launch_q8_t(const void* X, const void* packed, const float* sc
 template <int MT>
 static hipError_t launch_q8_mt(const void* X, const void* packed, const float* scales, void* Y,
                                int M, int K, int N, int G, const PanelPlan& p, hipStream_t s) {
+  if constexpr (MT == 1) {
+    if (p.cpp == 1 && 16 * p.u == G)
+      return launch_q8_t<1, 1, true>(X, packed, scales, Y, M, K, N, G, p, s);
+  }
   return p.cpp == 1 ? launch_q8_t<MT, 1>(X, packed, scales, Y, M, K, N, G, p, s)
                     : launch_q8_t<MT, 2>(X, packed, scales, Y, M, K, N, G, p, s);
 }
