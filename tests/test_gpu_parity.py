@@ -59,6 +59,8 @@ def assert_tol(y, y_exact, what=""):
     (1, 256, 16, 128), (1, 384, 272, 128), (2, 512, 1024, 64), (3, 640, 528, 128),
     (4, 4096, 1040, 128), (5, 1024, 256, 32), (8, 2048, 4096, 128), (9, 768, 784, 128),
     (16, 256, 512, 256),
+    (1, 8192, 512, 256),         # scale folded after the reduction, two batches per slot
+    (1, 8192, 1024, 128),        # two groups per quarter-wave: scale per batch
 ])
 def test_q8_group_vs_oracle(wq, M, K, N, G):
     d = synth.gen_q8_group(M, K, N, G, seed=1100 if (M, K, N) == (1, 4096, 4096) else 7 + M + K + N)
