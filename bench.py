@@ -134,18 +134,19 @@ def wl_q3(wq, torch, dev, K, N, dt, seed):
 def wl_q4(wq, torch, dev, M):
     import synth
     K, N, G = 4096, 11008, 128
-    nbytes = (K // 8) * N * 4 + (K // G) * N * 2 + K * 4 + M * K * 2 + M * N * 2
+    # packed codes + scales + the uint16 row table + X + Y
+    nbytes = (K // 8) * N * 4 + (K // G) * N * 2 + K * 2 + M * K * 2 + M * N * 2
     d = synth.gen_q4_group(M, K, N, G, seed=synth.SEEDS["q4_group_actorder"])
 
     def make(R):
         qw = torch.from_numpy(d["qweight"]).to(dev)
-        packed, _, inv = wq.prepare_q4(qw, d["g_idx"], G)
-        base = [torch.from_numpy(d["X"]).to(dev), packed, torch.from_numpy(d["scales"]).to(dev), inv]
+        packed, _ = wq.prepare_q4(qw, d["g_idx"], G)
+        base = [torch.from_numpy(d["X"]).to(dev), packed, torch.from_numpy(d["scales"]).to(dev)]
         return [[t.clone() for t in base] + [torch.empty((M, N), dtype=torch.float16, device=dev)]
                 for _ in range(R)]
 
     def run(c):
-        wq.gemm_q4_group(c[0], c[1], c[2], c[3], G, Y=c[4])
+        wq.gemm_q4_group(c[0], c[1], c[2], G, Y=c[3])
 
     w = Workload(f"q4_group_actorder M={M} K={K} N={N} G={G}", nbytes, make, run)
     w.oracle = lambda: __import__("oracle").gemm_q4_group(d["X"], d["qweight"], d["scales"], d["g_idx"], G)

@@ -139,7 +139,8 @@ int wq_q4_act_order_perm(const int32_t* g_idx, int K, int G, int32_t* perm, int3
  * bits 4j..4j+3, of word r, stored as u = q + 8), its rows taken in the
  * order perm lists (device array [K], or NULL for the stored order).
  * packed: wq_packed_bytes(WQ_OP_Q4G, K, N, G) bytes, written.
- * Rules: K % G == 0, G a power of two >= 32, N % 4 == 0. */
+ * The packed weight also holds the inverse of perm as a table of K uint16.
+ * Rules: K % G == 0, G a power of two >= 32, K <= 32768, N % 4 == 0. */
 int wq_prepack_q4(const int32_t* qweight, const int32_t* perm, void* packed, int K, int N, int G,
                   void* stream);
 
@@ -147,12 +148,12 @@ int wq_prepack_q4(const int32_t* qweight, const int32_t* perm, void* packed, int
  *   Y[m, n] = sum_k X[m, k] * scale[g_idx[k], n] * q[k, n]
  * computed from the packed weight (rows in perm order) as
  *   sum_i X[m, perm[i]] * scale[i / G, n] * q[perm[i], n].
- * X [M, K] fp16; scales [K/G, N] fp16; invperm: device [K] from
- * wq_q4_act_order_perm (NULL when the weight was packed with perm == NULL);
- * Y [M, N] fp16, written (fp32 accumulation).
+ * X [M, K] fp16; packed: from wq_prepack_q4 (the row order perm travels
+ * inside it); scales [K/G, N] fp16; Y [M, N] fp16, written (fp32
+ * accumulation).
  * Rules: as wq_prepack_q4, M >= 1. */
-int wq_gemm_q4_group(const void* X, const void* packed, const void* scales,
-                     const int32_t* invperm, void* Y, int M, int K, int N, int G, void* stream);
+int wq_gemm_q4_group(const void* X, const void* packed, const void* scales, void* Y, int M, int K,
+                     int N, int G, void* stream);
 
 /* ----------------------------------------------------------------- W8A8 -- */
 

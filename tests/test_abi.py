@@ -39,7 +39,8 @@ def test_packed_bytes_pure_and_valid(L):
     # the configured shapes re-lay out without padding
     assert L.wq_packed_bytes(wq.WQ_OP_Q3, 4096, 11008, 0) == 4096 // 32 * 3 * 11008 * 4
     assert L.wq_packed_bytes(wq.WQ_OP_Q3, 11008, 4096, 0) >= 11008 // 32 * 3 * 4096 * 4
-    assert L.wq_packed_bytes(wq.WQ_OP_Q4G, 4096, 11008, 128) == 4096 // 8 * 11008 * 4
+    # 4-bit: the codes plus the uint16 row table
+    assert L.wq_packed_bytes(wq.WQ_OP_Q4G, 4096, 11008, 128) == 4096 // 8 * 11008 * 4 + 4096 * 2
     # invalid shapes / ops -> 0
     assert L.wq_packed_bytes(wq.WQ_OP_Q8G, 4096, 4095, 128) == 0
     assert L.wq_packed_bytes(wq.WQ_OP_Q3, 100, 64, 0) == 0
@@ -74,12 +75,13 @@ def test_q8_validation(L):
 
 def test_q4_validation(L):
     f = L.wq_gemm_q4_group
-    assert f(P, P, None, None, P, 1, 4096, 11008, 128, None) == wq.WQ_ERR_NULL
-    assert f(P, P, P, None, P, 1, 4096, 11006, 128, None) == wq.WQ_ERR_SHAPE
-    assert f(P, P, P, None, P, 1, 4000, 11008, 128, None) == wq.WQ_ERR_SHAPE
-    assert f(P, P, P, None, P, 1, 4096, 11008, 16, None) == wq.WQ_ERR_SHAPE
-    assert f(P, P, P, None, P, 0, 4096, 11008, 128, None) == wq.WQ_ERR_SHAPE
-    assert f(P, P, P, P_MIS, P, 1, 4096, 11008, 128, None) == wq.WQ_ERR_ALIGN
+    assert f(P, P, None, P, 1, 4096, 11008, 128, None) == wq.WQ_ERR_NULL
+    assert f(P, P, P, P, 1, 4096, 11006, 128, None) == wq.WQ_ERR_SHAPE
+    assert f(P, P, P, P, 1, 4000, 11008, 128, None) == wq.WQ_ERR_SHAPE
+    assert f(P, P, P, P, 1, 4096, 11008, 16, None) == wq.WQ_ERR_SHAPE
+    assert f(P, P, P, P, 0, 4096, 11008, 128, None) == wq.WQ_ERR_SHAPE
+    assert f(P, P, P, P, 1, 32768 + 128, 64, 128, None) == wq.WQ_ERR_SHAPE   # K bound
+    assert f(P, P_MIS, P, P, 1, 4096, 11008, 128, None) == wq.WQ_ERR_ALIGN
     g = L.wq_prepack_q4
     assert g(P, None, P, 12, 16, 32, None) == wq.WQ_ERR_SHAPE
     assert g(P, None, None, 64, 16, 32, None) == wq.WQ_ERR_NULL

@@ -192,7 +192,7 @@ def test_q3_one_hot_rows(wq):
 def test_unpack_q4_bit_exact(wq, act):
     K, N, G = 4096, 11008, 128
     d = synth.gen_q4_group(1, K, N, G, seed=1300, act_order=act)
-    packed, perm, _ = wq.prepare_q4(cu(d["qweight"]), d["g_idx"] if act else None, G)
+    packed, perm = wq.prepare_q4(cu(d["qweight"]), d["g_idx"] if act else None, G)
     codes = wq.unpack_q4(packed, K, N, G, perm)
     torch.cuda.synchronize()
     assert np.array_equal(codes.cpu().numpy().astype(np.int64), oracle.unpack_q4(d["qweight"]))
@@ -202,8 +202,8 @@ def test_unpack_q4_bit_exact(wq, act):
 def test_q4_act_order_headline(wq, M):
     K, N, G = 4096, 11008, 128
     d = synth.gen_q4_group(M, K, N, G, seed=1300, act_order=True)
-    packed, _, inv = wq.prepare_q4(cu(d["qweight"]), d["g_idx"], G)
-    Y = wq.gemm_q4_group(cu(d["X"]), packed, cu(d["scales"]), inv, G)
+    packed, _ = wq.prepare_q4(cu(d["qweight"]), d["g_idx"], G)
+    Y = wq.gemm_q4_group(cu(d["X"]), packed, cu(d["scales"]), G)
     ref = oracle.gemm_q4_group(d["X"], d["qweight"], d["scales"], d["g_idx"], G)
     assert_tol(host(Y), ref, f"q4 M{M}")
 
@@ -215,8 +215,8 @@ def test_q4_act_order_headline(wq, M):
 ])
 def test_q4_small_ragged(wq, M, K, N, G, act):
     d = synth.gen_q4_group(M, K, N, G, seed=60 + M + K, act_order=act)
-    packed, _, inv = wq.prepare_q4(cu(d["qweight"]), d["g_idx"] if act else None, G)
-    Y = wq.gemm_q4_group(cu(d["X"]), packed, cu(d["scales"]), inv, G)
+    packed, _ = wq.prepare_q4(cu(d["qweight"]), d["g_idx"] if act else None, G)
+    Y = wq.gemm_q4_group(cu(d["X"]), packed, cu(d["scales"]), G)
     ref = oracle.gemm_q4_group(d["X"], d["qweight"], d["scales"], d["g_idx"], G)
     assert_tol(host(Y), ref, f"q4 {M}x{K}x{N} G{G} act={act}")
 
@@ -224,11 +224,11 @@ def test_q4_small_ragged(wq, M, K, N, G, act):
 def test_q4_one_hot_act_order(wq):
     K, N, G = 512, 260, 128
     d = synth.gen_q4_group(1, K, N, G, seed=61, act_order=True)
-    packed, _, inv = wq.prepare_q4(cu(d["qweight"]), d["g_idx"], G)
+    packed, _ = wq.prepare_q4(cu(d["qweight"]), d["g_idx"], G)
     for k in (0, 1, 5, 200, 511):
         x = np.zeros(K, np.float16)
         x[k] = 1
-        y = host(wq.gemm_q4_group(cu(x), packed, cu(d["scales"]), inv, G))
+        y = host(wq.gemm_q4_group(cu(x), packed, cu(d["scales"]), G))
         ref = (d["scales"][d["g_idx"][k]].astype(np.float64) * d["codes"][k]).astype(np.float16)
         assert np.array_equal(y, ref.astype(np.float64)), k
 
@@ -241,8 +241,8 @@ def test_q4_integer_exact(wq):
     s = np.ones((K // G, N), np.float16)
     X = rng.integers(-3, 4, size=(M, K)).astype(np.float16)
     qw = synth.pack_q4(q + 8)
-    packed, _, inv = wq.prepare_q4(cu(qw), g_idx, G)
-    Y = host(wq.gemm_q4_group(cu(X), packed, cu(s), inv, G))
+    packed, _ = wq.prepare_q4(cu(qw), g_idx, G)
+    Y = host(wq.gemm_q4_group(cu(X), packed, cu(s), G))
     ref = oracle.gemm_q4_group(X, qw, s, g_idx, G).astype(np.float16).astype(np.float64)
     assert np.array_equal(Y, ref)
 

@@ -41,7 +41,7 @@ _SIGNATURES = {
     "wq_gemm_q8_group": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "wq_q4_act_order_perm": (_i, [_vp, _i, _i, _vp, _vp]),
     "wq_prepack_q4": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
-    "wq_gemm_q4_group": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
+    "wq_gemm_q4_group": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "wq_gemm_w8a8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
     "wq_unpack_q3": (_i, [_vp, _vp, _i, _i, _vp]),
     "wq_unpack_q8": (_i, [_vp, _vp, _i, _i, _vp]),
@@ -244,20 +244,21 @@ def prepack_q4(qweight, perm=None, group_size=128):
 
 
 def prepare_q4(qweight, g_idx, group_size=128):
-    """Act-order preparation in one go: ``(packed, perm_dev, invperm_dev)``.
+    """Act-order preparation in one go: ``(packed, perm_dev)``.
 
-    With ``g_idx=None`` the stored order is kept and both permutations are None.
+    The packed weight carries the row order (its inverse, as a row table), so
+    the product needs nothing else.  With ``g_idx=None`` the stored order is
+    kept and ``perm_dev`` is None.
     """
     if g_idx is None:
-        return prepack_q4(qweight, None, group_size), None, None
+        return prepack_q4(qweight, None, group_size), None
     K = 8 * qweight.shape[0]
-    perm, inv = q4_act_order_perm(g_idx, K, group_size)
+    perm, _ = q4_act_order_perm(g_idx, K, group_size)
     perm_d = torch.from_numpy(perm).to(qweight.device)
-    inv_d = torch.from_numpy(inv).to(qweight.device)
-    return prepack_q4(qweight, perm_d, group_size), perm_d, inv_d
+    return prepack_q4(qweight, perm_d, group_size), perm_d
 
 
-def gemm_q4_group(X, packed, scales, invperm=None, group_size=128, Y=None):
+def gemm_q4_group(X, packed, scales, group_size=128, Y=None):
     """Y[m, n] = sum_k X[m, k] * scale[g_idx[k], n] * q[k, n] from a packed 4-bit weight."""
     squeeze = X.dim() == 1
     X2 = X.reshape(1, -1) if squeeze else X
@@ -267,13 +268,11 @@ def gemm_q4_group(X, packed, scales, invperm=None, group_size=128, Y=None):
     _need(X2, "X", torch.float16, (M, K), dev)
     _need_packed(packed, WQ_OP_Q4G, K, N, group_size, dev)
     _need(scales, "scales", torch.float16, (K // group_size, N), dev)
-    if invperm is not None:
-        _need(invperm, "invperm", torch.int32, (K,), dev)
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float16, device=dev)
     _need(Y, "Y", torch.float16, (M, N), dev)
-    st = lib().wq_gemm_q4_group(_ptr(X2), _ptr(packed), _ptr(scales), _ptr(invperm), _ptr(Y), M,
-                                K, N, group_size, _stream(dev))
+    st = lib().wq_gemm_q4_group(_ptr(X2), _ptr(packed), _ptr(scales), _ptr(Y), M, K, N, group_size,
+                                _stream(dev))
     _check("wq_gemm_q4_group", st)
     return Y.reshape(N) if squeeze else Y
 

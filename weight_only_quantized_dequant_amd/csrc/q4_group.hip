@@ -9,9 +9,10 @@
 // row's group g_idx[k] is not monotone in k.  The weight is re-laid out once,
 // offline (wq_prepack_q4), the same idea as the offline re-layout of "Marlin
 // 格式" on the "Quantization CUDA" page: rows are put in group order (perm),
-// then into the operand order of the matrix cores.  At run time each
-// workgroup scatters X into LDS through the inverse permutation (coalesced
-// reads, LDS writes), so the rows the cores combine are one group at a time.
+// then into the operand order of the matrix cores; the inverse permutation
+// travels with the packed weight as a uint16 row table.  At run time each
+// workgroup scatters X into LDS through that table (coalesced reads, LDS
+// writes), so the rows the cores combine are one group at a time.
 //
 // The products run on v_mfma_f32_16x16x32_f16 for every M (rows of X past M
 // are zero lanes of the operand).  A code u (0..15) enters the cores as the
@@ -43,7 +44,10 @@ constexpr int kQ4Waves = kQ4Threads / 64;
 constexpr int kQ4RowPad = 32;
 
 // PanelPlan for the 4-bit layout: P = 16, npanels = ceil(N / 16),
-// u = blocks per panel = ceil(K / 128); cpp, nsa and bw are unused.
+// u = blocks per panel = ceil(K / 128); cpp, nsa and bw are unused.  The
+// packed weight is the blocks, then the row table: K uint16, entry k = the
+// group-order row of original row k (the inverse of perm), padded to 16 B.
+static size_t q4_block_bytes(const PanelPlan& p) { return (size_t)p.npanels * p.u * 1024; }
 PanelPlan plan_q4(int K, int N, int G) {
   (void)G;
   PanelPlan p{};
@@ -53,7 +57,7 @@ PanelPlan plan_q4(int K, int N, int G) {
   p.u = (K + kQ4Block - 1) / kQ4Block;
   p.nsa = 0;
   p.bw = 0;
-  p.packed_bytes = (size_t)p.npanels * p.u * 1024;
+  p.packed_bytes = q4_block_bytes(p) + ((size_t)K * 2 + 15) / 16 * 16;
   return p;
 }
 
@@ -82,9 +86,13 @@ __device__ __forceinline__ int q4_pos(int e) { return 2 * (e & 3) + (e >> 2); }
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void q4_prepack_kernel(const uint32_t* __restrict__ qw,
                                                               const int* __restrict__ perm,
-                                                              uint32_t* __restrict__ out, int K,
+                                                              uint32_t* __restrict__ out,
+                                                              uint16_t* __restrict__ table, int K,
                                                               int N, int nb, int npanels) {
   const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  // Row table: table[perm[i]] = i.
+  for (size_t i = idx; i < (size_t)K; i += (size_t)gridDim.x * kThreads)
+    table[perm ? perm[i] : (int)i] = (uint16_t)i;
   if (idx >= (size_t)npanels * nb * 64) return;
   const int l = (int)(idx % 64);
   const size_t pb = idx / 64;
@@ -120,8 +128,8 @@ __global__ __launch_bounds__(kThreads) void q4_prepack_kernel(const uint32_t* __
 template <int MT, int NSC>
 __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
     const _Float16* __restrict__ X, const uint8_t* __restrict__ Wp,
-    const _Float16* __restrict__ scales, const int* __restrict__ invperm,
-    _Float16* __restrict__ Y, int M, int K, int N, int G, int nb, int npanels, int packed_bytes) {
+    const _Float16* __restrict__ scales, _Float16* __restrict__ Y, int M, int K, int N, int G,
+    int nb, int npanels, int packed_bytes) {
   typedef _Float16 h8 __attribute__((ext_vector_type(8)));
   typedef float f4 __attribute__((ext_vector_type(4)));
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -178,37 +186,36 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
       woff = (((p_begin + lp) * nb + blo) * 64 + lane) * 16;
     }
   };
-  // Stage X through the inverse permutation: row k of X goes to group-order
-  // row i = invperm[k], octet i / 8, position q4_pos(i % 8).  Rows past K
-  // (block padding) and rows m >= M stay zero.  The loads of the first round
-  // of chunks go out first, then the first kQ4Ring blocks of the weight
+  // Stage X through the row table of the packed weight: row k of X goes to
+  // group-order row i = table[k], octet i / 8, position q4_pos(i % 8).  Rows
+  // past K (block padding) and rows m >= M stay zero.  The loads of the first
+  // round of chunks go out first, then the first kQ4Ring blocks of the weight
   // stream, so the scatter waits only for its own data.
   const int nchunk = K / 8;
   constexpr int CR = 2;  // chunks per thread per round
   // Buffer loads: chunks past K and rows past M read zero without a branch.
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, M * K * 2);
-  const __amdgpu_buffer_rsrc_t pr_ = make_rsrc(invperm, invperm ? K * 4 : 0);
-  auto stage_load = [&](int c0, u32x4 (&pv)[CR][2], u32x4 (&xq)[CR][MT]) {
+  const __amdgpu_buffer_rsrc_t tr = make_rsrc(Wp + (size_t)npanels * nb * 1024, K * 2);
+  auto stage_load = [&](int c0, u32x4 (&pv)[CR], u32x4 (&xq)[CR][MT]) {
 #pragma unroll
     for (int r = 0; r < CR; ++r) {
       const int ch = c0 + r * kQ4Threads;
       const bool ok = ch < nchunk;
-      pv[r][0] = __builtin_amdgcn_raw_buffer_load_b128(pr_, ok ? 32 * ch : kOutOfRange, 0, 0);
-      pv[r][1] = __builtin_amdgcn_raw_buffer_load_b128(pr_, ok ? 32 * ch + 16 : kOutOfRange, 0, 0);
+      pv[r] = __builtin_amdgcn_raw_buffer_load_b128(tr, ok ? 16 * ch : kOutOfRange, 0, 0);
 #pragma unroll
       for (int m = 0; m < MT; ++m)
         xq[r][m] = __builtin_amdgcn_raw_buffer_load_b128(
             xr, (ok && m < M) ? (m * K + 8 * ch) * 2 : kOutOfRange, 0, 0);
     }
   };
-  auto stage_write = [&](int c0, const u32x4 (&pv)[CR][2], const u32x4 (&xq)[CR][MT]) {
+  auto stage_write = [&](int c0, const u32x4 (&pv)[CR], const u32x4 (&xq)[CR][MT]) {
 #pragma unroll
     for (int r = 0; r < CR; ++r) {
       const int ch = c0 + r * kQ4Threads;
       if (ch >= nchunk) break;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int i = invperm ? (int)pv[r][j >> 2][j & 3] : 8 * ch + j;
+        const int i = (int)((pv[r][j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
         const int base = (i >> 3) * 8 + q4_pos(i & 7);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
@@ -220,7 +227,7 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
     }
   };
   {
-    u32x4 pv[CR][2], xq[CR][MT];
+    u32x4 pv[CR], xq[CR][MT];
     stage_load(t, pv, xq);
     load_item(wb0, sc0);
     load_item(wb1, sc1);
@@ -234,7 +241,7 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
     stage_write(t, pv, xq);
   }
   for (int c0 = t + CR * kQ4Threads; c0 < nchunk; c0 += CR * kQ4Threads) {
-    u32x4 pv[CR][2], xq[CR][MT];
+    u32x4 pv[CR], xq[CR][MT];
     stage_load(c0, pv, xq);
     stage_write(c0, pv, xq);
   }
@@ -369,7 +376,9 @@ hipError_t launch_q4_prepack(const int32_t* qw, const int32_t* perm, void* out, 
   const size_t total = (size_t)p.npanels * p.u * 64;
   hipLaunchKernelGGL(q4_prepack_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)),
                      dim3(kThreads), 0, s, reinterpret_cast<const uint32_t*>(qw), perm,
-                     reinterpret_cast<uint32_t*>(out), K, N, p.u, p.npanels);
+                     reinterpret_cast<uint32_t*>(out),
+                     reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(out) + q4_block_bytes(p)), K,
+                     N, p.u, p.npanels);
   return hipGetLastError();
 }
 
@@ -384,9 +393,8 @@ hipError_t launch_q4_unpack(const void* packed, const int32_t* perm, int8_t* cod
 }
 
 template <int MT, int NSC>
-static hipError_t launch_q4_t(const void* X, const void* packed, const void* scales,
-                              const int32_t* invperm, void* Y, int M, int K, int N, int G,
-                              const PanelPlan& p, hipStream_t s) {
+static hipError_t launch_q4_t(const void* X, const void* packed, const void* scales, void* Y,
+                              int M, int K, int N, int G, const PanelPlan& p, hipStream_t s) {
   const int cus = device_cus();
   int grid = p.npanels < cus ? p.npanels : cus;
   if ((p.npanels + grid - 1) / grid > kQ4MaxRun) grid = (p.npanels + kQ4MaxRun - 1) / kQ4MaxRun;
@@ -398,24 +406,21 @@ static hipError_t launch_q4_t(const void* X, const void* packed, const void* sca
   }
   hipLaunchKernelGGL((q4_mfma_kernel<MT, NSC>), dim3(grid), dim3(kQ4Threads), lds, s,
                      reinterpret_cast<const _Float16*>(X), reinterpret_cast<const uint8_t*>(packed),
-                     reinterpret_cast<const _Float16*>(scales), invperm,
-                     reinterpret_cast<_Float16*>(Y), M, K, N, G, p.u, p.npanels,
-                     (int)p.packed_bytes);
+                     reinterpret_cast<const _Float16*>(scales), reinterpret_cast<_Float16*>(Y), M,
+                     K, N, G, p.u, p.npanels, (int)q4_block_bytes(p));
   return hipGetLastError();
 }
 
 template <int MT>
-static hipError_t launch_q4_mt(const void* X, const void* packed, const void* scales,
-                               const int32_t* invperm, void* Y, int M, int K, int N, int G,
-                               const PanelPlan& p, hipStream_t s) {
-  if (G == 32) return launch_q4_t<MT, 4>(X, packed, scales, invperm, Y, M, K, N, G, p, s);
-  if (G == 64) return launch_q4_t<MT, 2>(X, packed, scales, invperm, Y, M, K, N, G, p, s);
-  return launch_q4_t<MT, 1>(X, packed, scales, invperm, Y, M, K, N, G, p, s);
+static hipError_t launch_q4_mt(const void* X, const void* packed, const void* scales, void* Y,
+                               int M, int K, int N, int G, const PanelPlan& p, hipStream_t s) {
+  if (G == 32) return launch_q4_t<MT, 4>(X, packed, scales, Y, M, K, N, G, p, s);
+  if (G == 64) return launch_q4_t<MT, 2>(X, packed, scales, Y, M, K, N, G, p, s);
+  return launch_q4_t<MT, 1>(X, packed, scales, Y, M, K, N, G, p, s);
 }
 
-hipError_t launch_q4_group(const void* X, const void* packed, const void* scales,
-                           const int32_t* invperm, void* Y, int M, int K, int N, int G,
-                           hipStream_t s) {
+hipError_t launch_q4_group(const void* X, const void* packed, const void* scales, void* Y, int M,
+                           int K, int N, int G, hipStream_t s) {
   const PanelPlan p = plan_q4(K, N, G);
   const int mtmax = q4_max_mt(K);
   for (int m0 = 0; m0 < M; m0 += mtmax) {
@@ -425,10 +430,10 @@ hipError_t launch_q4_group(const void* X, const void* packed, const void* scales
     void* Yc = reinterpret_cast<char*>(Y) + (size_t)m0 * N * 2;
     hipError_t e;
     switch (mt) {
-      case 1: e = launch_q4_mt<1>(Xc, packed, scales, invperm, Yc, mc, K, N, G, p, s); break;
-      case 2: e = launch_q4_mt<2>(Xc, packed, scales, invperm, Yc, mc, K, N, G, p, s); break;
-      case 4: e = launch_q4_mt<4>(Xc, packed, scales, invperm, Yc, mc, K, N, G, p, s); break;
-      default: e = launch_q4_mt<8>(Xc, packed, scales, invperm, Yc, mc, K, N, G, p, s); break;
+      case 1: e = launch_q4_mt<1>(Xc, packed, scales, Yc, mc, K, N, G, p, s); break;
+      case 2: e = launch_q4_mt<2>(Xc, packed, scales, Yc, mc, K, N, G, p, s); break;
+      case 4: e = launch_q4_mt<4>(Xc, packed, scales, Yc, mc, K, N, G, p, s); break;
+      default: e = launch_q4_mt<8>(Xc, packed, scales, Yc, mc, K, N, G, p, s); break;
     }
     if (e != hipSuccess) return e;
   }

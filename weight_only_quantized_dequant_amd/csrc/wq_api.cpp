@@ -58,6 +58,7 @@ int check_q8(int K, int N) {
 
 int check_q4(int K, int N, int G) {
   if (G < 32 || !pow2(G) || K < G || K % G || N < 4 || N % 4) return WQ_ERR_SHAPE;
+  if (K > 32768) return WQ_ERR_SHAPE;  // X staged in LDS; 16-bit row table
   if ((long long)(K / 8) * N * 4 > kMaxBytes / 2) return WQ_ERR_SHAPE;
   return WQ_OK;
 }
@@ -165,16 +166,14 @@ int wq_prepack_q4(const int32_t* qweight, const int32_t* perm, void* packed, int
   return hip_status(wq::launch_q4_prepack(qweight, perm, packed, K, N, G, as_stream(stream)));
 }
 
-int wq_gemm_q4_group(const void* X, const void* packed, const void* scales,
-                     const int32_t* invperm, void* Y, int M, int K, int N, int G, void* stream) {
+int wq_gemm_q4_group(const void* X, const void* packed, const void* scales, void* Y, int M, int K,
+                     int N, int G, void* stream) {
   if (!X || !packed || !scales || !Y) return WQ_ERR_NULL;
   if (int st = check_q4(K, N, G)) return st;
-  if (M < 1 || K > 32768) return WQ_ERR_SHAPE;  // X staged in 64 KB of LDS
+  if (M < 1) return WQ_ERR_SHAPE;
   if ((long long)M * K * 2 > kMaxBytes) return WQ_ERR_SHAPE;
   if (!aligned16(X) || !aligned16(packed) || !aligned16(scales)) return WQ_ERR_ALIGN;
-  if (invperm && !aligned16(invperm)) return WQ_ERR_ALIGN;
-  return hip_status(
-      wq::launch_q4_group(X, packed, scales, invperm, Y, M, K, N, G, as_stream(stream)));
+  return hip_status(wq::launch_q4_group(X, packed, scales, Y, M, K, N, G, as_stream(stream)));
 }
 
 int wq_unpack_q4(const void* packed, const int32_t* perm, int8_t* codes, int K, int N, int G,

@@ -49,9 +49,8 @@ hipError_t launch_q3_unpack(const void* packed, int8_t* codes, int K, int N, hip
 
 hipError_t launch_q4_prepack(const int32_t* qw, const int32_t* perm, void* packed, int K, int N,
                              int G, hipStream_t s);
-hipError_t launch_q4_group(const void* X, const void* packed, const void* scales,
-                           const int32_t* invperm, void* Y, int M, int K, int N, int G,
-                           hipStream_t s);
+hipError_t launch_q4_group(const void* X, const void* packed, const void* scales, void* Y, int M,
+                           int K, int N, int G, hipStream_t s);
 hipError_t launch_q4_unpack(const void* packed, const int32_t* perm, int8_t* codes, int K, int N,
                             int G, hipStream_t s);
 
