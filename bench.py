@@ -38,7 +38,8 @@ sys.path.insert(0, ROOT)
 import numpy as np  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
-INT8_PEAK_TOPS = 5000.0
+INT8_PEAK_TOPS = 5000.0     # dense int8 MFMA, POP/s x 1e-12
+FP16_PEAK_TFLOPS = 2500.0   # dense fp16 MFMA
 MALL_BYTES = 256 << 20
 
 
@@ -88,11 +89,11 @@ def _rotation(nbytes, floor=2 * MALL_BYTES, cap=64):
     return int(min(cap, max(1, -(-floor // nbytes))))
 
 
-def wl_q8(wq, torch, dev):
+def wl_q8(wq, torch, dev, M=1):
     import synth
-    M, K, N, G = 1, 4096, 4096, 128
+    K, N, G = 4096, 4096, 128
     nbytes = K * N + (K // G) * N * 4 + M * K * 2 + M * N * 2
-    d = synth.gen_q8_group(M, K, N, G, seed=synth.SEEDS["q8_group_4096"])
+    d = synth.gen_q8_group(M, K, N, G, seed=synth.SEEDS["q8_group_4096" if M == 1 else "q8_group_m512"])
 
     def make(R):
         base = [torch.from_numpy(d["X"]).to(dev), wq.prepack_q8(torch.from_numpy(d["q"]).to(dev)),
@@ -104,7 +105,10 @@ def wl_q8(wq, torch, dev):
     def run(c):
         wq.gemm_q8_group(c[0], c[1], c[2], G, Y=c[3])
 
-    w = Workload("q8_group_gemv M=1 K=4096 N=4096 G=128", nbytes, make, run)
+    kind = "gemv" if M == 1 else "gemm"
+    w = Workload(f"q8_group_{kind} M={M} K={K} N={N} G={G}", nbytes, make, run,
+                 flops=0 if M == 1 else 2 * M * K * N)
+    w.peak_tops = FP16_PEAK_TFLOPS
     w.config = {"workload": w.name, "M": M, "K": K, "N": N, "group": G}
     w.oracle = lambda: __import__("oracle").gemm_q8_group(d["X"], d["q"], d["scales"], G)
     w.dtype = "int8 weight x fp16 act, fp32 accumulate"
@@ -171,6 +175,7 @@ def wl_w8a8(wq, torch, dev):
         wq.gemm_w8a8(c[0], c[1], c[2], Y=c[3], Xq=c[4], Sx=c[5])
 
     w = Workload(f"w8a8_dynamic M={M} K={K} N={N}", nbytes, make, run, flops=2 * M * K * N)
+    w.peak_tops = INT8_PEAK_TOPS
     w.oracle = lambda: __import__("oracle").gemm_w8a8(d["X"], d["Wq"], d["Sw"])
     return w
 
@@ -280,6 +285,8 @@ def main():
     def make(name):
         if name == "q8":
             return wl_q8(wq, torch, dev)
+        if name.startswith("q8_m"):
+            return wl_q8(wq, torch, dev, int(name[4:]))
         if name == "q3_f32_1024":
             return wl_q3(wq, torch, dev, 1024, 1024, "f32", 1000)
         if name.startswith("q3_f16_"):
@@ -312,7 +319,7 @@ def main():
     if not args.headline_only:
         sec = {}
         for name in ("q3_f32_1024", "q3_f16_4096x4096", "q3_f16_4096x11008", "q3_f16_11008x4096",
-                     "q4_m1", "q4_m2", "q4_m4", "q4_m8", "w8a8"):
+                     "q4_m1", "q4_m2", "q4_m4", "q4_m8", "q8_m512", "w8a8"):
             sw = make(name)
             sms, sR = time_workload(torch, sw, 300 if name != "w8a8" else 100, 30 if name != "w8a8" else 10)
             e = {"us_per_call": round(sms * 1e3, 3), "GB_per_s": round(sw.nbytes / (sms * 1e-3) / 1e9, 1),
@@ -320,7 +327,7 @@ def main():
                  "rotation_copies": sR, "algorithmic_bytes": sw.nbytes}
             if sw.flops:
                 e["TOPS"] = round(sw.flops / (sms * 1e-3) / 1e12, 1)
-                e["pct_int8_peak"] = round(100 * sw.flops / (sms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2)
+                e["pct_mfma_peak"] = round(100 * sw.flops / (sms * 1e-3) / 1e12 / sw.peak_tops, 2)
             sec[sw.name] = e
             del sw
         out["secondary"] = sec

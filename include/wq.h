@@ -121,7 +121,14 @@ int wq_prepack_q8(const int8_t* qweight, void* packed, int K, int N, void* strea
  *   Y[m, n] = sum_k X[m, k] * (scale[k / G, n] * q[k, n]).
  * X [M, K] fp16; packed: from wq_prepack_q8; scales [K/G, N] fp32;
  * Y [M, N] fp16, written (fp32 accumulation, one round to nearest even).
- * Rules: M >= 1, K % 32 == 0, N % 16 == 0, G % 32 == 0, K % G == 0. */
+ * Evaluated per group as scale * (sum of X * q), exact products, fp32 sums.
+ * M < 32, or G not a multiple of 64: streaming passes over the packed weight
+ * (one per 4 rows of X).  Otherwise one tiled matrix-core launch (64 x 128
+ * output tiles) that reads the same packed weight.
+ * ("Quantization CUDA", tom-jerr.github.io, "Int8 Weight Only Quantization";
+ * "融合反量化与GEMM：LLM推理的CUDA内核优化实践", zingnex.cn, "技术实现细节".)
+ * Rules: M >= 1, K % 32 == 0, N % 16 == 0, G % 32 == 0, K % G == 0,
+ * M * K * 2 < 2^31; Y 16-byte aligned as well. */
 int wq_gemm_q8_group(const void* X, const void* packed, const float* scales, void* Y, int M,
                      int K, int N, int G, void* stream);
 

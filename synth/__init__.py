@@ -35,6 +35,7 @@ __all__ = [
 SEEDS = {
     "q3_f32_1024": 1000,
     "q8_group_4096": 1100,
+    "q8_group_m512": 1500,       # M = 512, K = N = 4096 (the tiled matrix-core path)
     "q3_f16_4096x4096": 1200,
     "q3_f16_4096x11008": 1201,
     "q3_f16_11008x4096": 1202,

@@ -69,6 +69,7 @@ def test_q8_validation(L):
     assert f(P, P, P, P, 1, 4096, 4096, 96, None) == wq.WQ_ERR_SHAPE     # K % G
     assert f(P, P, P, P, 1, 4096, 4096, 48, None) == wq.WQ_ERR_SHAPE     # G % 32
     assert f(P, P_MIS, P, P, 1, 4096, 4096, 128, None) == wq.WQ_ERR_ALIGN
+    assert f(P, P, P, P_MIS, 64, 4096, 4096, 128, None) == wq.WQ_ERR_ALIGN    # Y: 8-byte stores
     assert L.wq_prepack_q8(P, P, 4096, 4100, None) == wq.WQ_ERR_SHAPE
     assert L.wq_prepack_q8(P_MIS, P, 4096, 4096, None) == wq.WQ_ERR_ALIGN
 

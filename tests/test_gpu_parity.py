@@ -134,6 +134,66 @@ def test_q8_wide_panels_and_long_k(wq):
         assert_tol(host(Y), oracle.gemm_q8_group(d["X"], d["q"], d["scales"], 128), f"q8 {M}x{K}x{N}")
 
 
+# From 32 rows of X on (groups a multiple of 64 rows) the int8 product runs
+# on the matrix cores: 64 x 128 output tiles, K in stages of 64 rows.
+@pytest.mark.parametrize("M,K,N,G", [
+    (32, 4096, 4096, 128),     # first row count on the tiled path
+    (100, 1088, 4112, 64),     # ragged row and column tiles, 17 stages
+    (64, 64, 128, 64),         # a single stage
+    (40, 11008, 4096, 128),    # 24-row slots of the packed layout straddle stages
+    (72, 4096, 8192, 128),     # 32-column panels (two 16-column chunks each)
+    (33, 1152, 384, 192),      # groups of three stages
+    (130, 512, 1024, 512),     # one group over all of K; three row tiles
+])
+def test_q8_gemm_tiles_vs_oracle(wq, M, K, N, G):
+    d = synth.gen_q8_group(M, K, N, G, seed=31 + M + K + N)
+    Y = wq.gemm_q8_group(cu(d["X"]), wq.prepack_q8(cu(d["q"])), cu(d["scales"]), G)
+    assert_tol(host(Y), oracle.gemm_q8_group(d["X"], d["q"], d["scales"], G), f"q8 tiles {M}x{K}x{N} G{G}")
+
+
+def test_q8_gemm_integer_exact_and_deterministic(wq):
+    # Scales 1 and small integer X on the tiled path: every fp32 partial sum
+    # is an exact integer, so the result is bit-exact; repeated calls agree.
+    M, K, N, G = 80, 1024, 400, 128
+    rng = np.random.default_rng(43)
+    q = rng.integers(-127, 128, size=(K, N)).astype(np.int8)
+    X = rng.integers(-2, 3, size=(M, K)).astype(np.float16)
+    s = np.ones((K // G, N), np.float32)
+    Xd, P, Sd = cu(X), wq.prepack_q8(cu(q)), cu(s)
+    Y = wq.gemm_q8_group(Xd, P, Sd, G)
+    ref = oracle.gemm_q8_group(X, q, s, G).astype(np.float16).astype(np.float64)
+    assert np.array_equal(host(Y), ref)
+    for _ in range(5):
+        assert torch.equal(wq.gemm_q8_group(Xd, P, Sd, G), Y)
+
+
+def test_q8_gemm_rows_match_single_row_calls(wq):
+    # Row m of the tiled product against the streaming kernel on row m alone:
+    # both within the bar of the oracle, and close to each other.
+    M, K, N, G = 48, 2048, 1024, 128
+    d = synth.gen_q8_group(M, K, N, G, seed=77)
+    P, Sd = wq.prepack_q8(cu(d["q"])), cu(d["scales"])
+    Y = host(wq.gemm_q8_group(cu(d["X"]), P, Sd, G))
+    for m in (0, 17, 47):
+        y1 = host(wq.gemm_q8_group(cu(d["X"][m:m + 1]), P, Sd, G))
+        ref = oracle.gemm_q8_group(d["X"][m:m + 1], d["q"], d["scales"], G)
+        assert_tol(Y[m], ref, f"tiled row {m}")
+        assert_tol(y1, ref, f"streaming row {m}")
+
+
+def test_q8_gemm_full_size_sampled_rows(wq):
+    # M = 512, K = N = 4096, group 128: the int8 workload of the fused-kernel
+    # page.  All rows on the GPU; the oracle on a sample of rows (row m of Y
+    # depends on row m of X only).
+    M, K, N, G = 512, 4096, 4096, 128
+    d = synth.gen_q8_group(M, K, N, G, seed=1500)
+    Y = host(wq.gemm_q8_group(cu(d["X"]), wq.prepack_q8(cu(d["q"])), cu(d["scales"]), G))
+    rows = [0, 1, 63, 64, 127, 200, 255, 256, 383, 447, 510, 511]
+    ref = oracle.gemm_q8_group(d["X"][rows], d["q"], d["scales"], G)
+    assert_tol(Y[rows], ref, "q8 512x4096x4096 sampled rows")
+    assert np.all(np.isfinite(Y))
+
+
 # ================================================================= 3-bit ==
 
 @pytest.mark.parametrize("K,N", [(1024, 1024), (4096, 4096), (4096, 11008), (11008, 4096), (96, 20)])

@@ -37,11 +37,12 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, "wq_api.cpp")]
 
 
-# Per-source extra flags.  The 4-bit kernel keeps its matrix-core accumulators
-# in ordinary VGPRs: with the default choice the register allocator shuttles
-# them between AGPRs and VGPRs on every block.
+# Per-source extra flags.  The 4-bit kernel and the tiled int8 kernel keep
+# their matrix-core accumulators in ordinary VGPRs: with the default choice
+# the register allocator shuttles them between AGPRs and VGPRs on every block.
 EXTRA = {
     "q4_group.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "q8_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -28,6 +28,9 @@ namespace wq {
 // its codes the other's loads are still landing.
 constexpr int kQ8Threads = 512;
 constexpr int kQ8Batch = 8;  // rows per batch (never straddles a group: G % 32 == 0)
+// From this many rows of X on, the product runs as a tiled matrix-core GEMM
+// (q8_gemm.hip) instead of one streaming pass over the weight per 4 rows.
+constexpr int kQ8GemmMinRows = 32;
 
 // Panel plan: a pure function of (K, N); prepack and product agree on it.
 PanelPlan plan_q8(int K, int N) {
@@ -288,6 +291,8 @@ static hipError_t launch_q8_mt(const void* X, const void* packed, const float* s
 
 hipError_t launch_q8_group(const void* X, const void* packed, const float* scales, void* Y, int M,
                            int K, int N, int G, hipStream_t s) {
+  if (M >= kQ8GemmMinRows && q8_gemm_supported(M, K, N, G))
+    return launch_q8_gemm(X, packed, scales, Y, M, K, N, G, s);
   const PanelPlan p = plan_q8(K, N);
   // Rows of X beyond 4 run as further launches over the same panels (the
   // accumulators of 4 rows x 16 columns x 2 fill the register budget of a

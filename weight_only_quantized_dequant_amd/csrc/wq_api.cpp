@@ -119,7 +119,8 @@ int wq_gemm_q8_group(const void* X, const void* packed, const float* scales, voi
   if (M < 1 || G < 32 || G % 32 || K % G) return WQ_ERR_SHAPE;
   if ((long long)M * K * 2 > kMaxBytes || (long long)(K / G) * N * 4 > kMaxBytes)
     return WQ_ERR_SHAPE;
-  if (!aligned16(X) || !aligned16(packed) || !aligned16(scales)) return WQ_ERR_ALIGN;
+  if (!aligned16(X) || !aligned16(packed) || !aligned16(scales) || !aligned16(Y))
+    return WQ_ERR_ALIGN;
   return hip_status(wq::launch_q8_group(X, packed, scales, Y, M, K, N, G, as_stream(stream)));
 }
 

@@ -41,6 +41,10 @@ hipError_t launch_q8_prepack(const int8_t* W, void* packed, int K, int N, hipStr
 hipError_t launch_q8_group(const void* X, const void* packed, const float* scales, void* Y, int M,
                            int K, int N, int G, hipStream_t s);
 hipError_t launch_q8_unpack(const void* packed, int8_t* codes, int K, int N, hipStream_t s);
+// Matrix-core path of the same product for many rows of X (q8_gemm.hip).
+bool q8_gemm_supported(int M, int K, int N, int G);
+hipError_t launch_q8_gemm(const void* X, const void* packed, const float* scales, void* Y, int M,
+                          int K, int N, int G, hipStream_t s);
 
 hipError_t launch_q3_prepack(const int32_t* qw, void* packed, int K, int N, hipStream_t s);
 hipError_t launch_q3(const void* x, const void* packed, const void* scales, const void* zeros,
