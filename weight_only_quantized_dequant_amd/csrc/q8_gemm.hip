@@ -35,15 +35,18 @@ namespace {
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
-constexpr int kBM = 64, kBN = 128, kBK = 64, kStages = 8, kThreadsG = 512;
-constexpr int kRow = kBK * 2;                   // 128 bytes: one fp16 row of a stage
-constexpr int kStageA = kBM * kRow;             // X tile, fp16 [m][k]
-constexpr int kStageB = kBK * kBN;              // codes, 64 rows x 8 chunks of 16 bytes
-constexpr int kStageS = 1024;                   // scales of the stage's group (512 bytes used)
+constexpr int kBM = 64, kBN = 128, kBK = 128, kStages = 3, kThreadsG = 256;
+constexpr int kRowA = kBK * 2;                   // 256 bytes: one fp16 row of X per stage
+constexpr int kStageA = kBM * kRowA;             // X tile, fp16 [m][k], 16 KB
+constexpr int kStageB = kBK * kBN;               // codes: 128 rows x 8 chunks of 16 bytes
+constexpr int kStageS = 1024;                    // two scale rows of 128 columns
 constexpr int kStage = kStageA + kStageB + kStageS;
-constexpr int kTileB = kBN * kRow;              // converted weight tile, fp16 [n][k]
+constexpr int kLoads = 8;                        // direct-to-LDS loads per stage per wave
 
-__device__ __forceinline__ int swz(int row, int c) { return c ^ ((row >> 1) & 7); }
+// X rows of a stage are 16 chunks of 16 bytes; chunk c of row r sits at
+// position c ^ (r % 16), so the 16 rows of one fragment read hit distinct
+// LDS banks.
+__device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 15); }
 
 template <int VM>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -51,7 +54,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// All LDS accesses of this wave done, then a workgroup barrier; the empty asm
+// All LDS reads of this wave done, then a workgroup barrier; the empty asm
 // statements keep the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
@@ -60,41 +63,27 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// 8-byte LDS store issued as inline assembly.  A plain store into the same
-// LDS array that the direct-to-LDS loads fill makes the compiler wait for
-// every load in flight (it cannot tell the ring slots apart); here the
-// ordering is explicit: the store follows the workgroup barrier that retires
-// the tile's previous readers, and the barrier after the conversion waits for
-// it (lgkmcnt(0)).
-__device__ __forceinline__ void lds_store_b64(unsigned char* p, uint32_t lo, uint32_t hi) {
-  const uint32_t addr = (uint32_t)(uintptr_t)(lds_u8*)p;
-  const uint64_t v = ((uint64_t)hi << 32) | lo;
-  asm volatile("ds_write_b64 %0, %1" : : "v"(addr), "v"(v) : "memory");
-}
-
-// Loads per stage per wave: X and codes; wave 0 also loads the scale row.
-// Waiting until stage t + 1 has landed leaves the later stages in flight.
-template <int PENDING_STAGES>
-__device__ __forceinline__ void wait_stages(int wave) {
-  if (wave == 0)
-    wait_vmcnt<3 * PENDING_STAGES>();
-  else
-    wait_vmcnt<2 * PENDING_STAGES>();
-}
-
 }  // namespace
 
-// Stage slot layout of the codes: piece (row r, chunk c) of a stage, r = 8 o
-// + i, sits at 16-byte slot 8 (8 i + c) + o.  Load instruction i (one per
-// wave) therefore brings row i of every octet o for all 8 chunks, and its 8
-// lanes of one chunk read pieces that are consecutive in the packed layout
-// whenever a slot of that layout holds 8 or more rows per chunk.
+// Codes of a stage in LDS: the 16-byte piece of row r = 8 o + i (o = 0..15,
+// i = 0..7), chunk c (16 columns) sits at slot 16 (8 i + c) + (o ^ 4 (c % 4)).
+// A direct-to-LDS load writes 64 consecutive slots, so its 16 lanes of one
+// (i, c) read 16 pieces of consecutive octets o, which are adjacent in the
+// packed layout whenever one of its slots spans 8 rows; and the 64 lanes of
+// a fragment read (below) hit 64 distinct banks.
+//
+// Fragments.  Lane l of a wave with columns w0 .. w0 + 63 takes, for the
+// k32 step h, rows 32 h + 8 (l / 16) + e (e = 0..7) of chunk w0 / 16 + p and
+// the 4-byte word d of each (p = (l % 16) / 4, d = l % 4): 4 columns
+// 16 p + 4 d + j (j = 0..3), 8 rows each.  Column j of that word goes to the
+// matrix-core operand of block j, so block j, operand column t holds weight
+// column 16 (t / 4) + 4 (t % 4) + j; the transposed result then gives lane l
+// the 16 consecutive columns 16 (l / 16) + 4 r + j (r, j = 0..3) of one row.
 __global__ __launch_bounds__(kThreadsG) void q8_gemm_kernel(
     const _Float16* __restrict__ X, const uint8_t* __restrict__ Wp,
     const float* __restrict__ scales, _Float16* __restrict__ Y, int M, int K, int N, int G, int u,
     int nta, int cpp, int packed_bytes, int mtiles, int ntiles) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStage + kTileB];
-  unsigned char* const btile = smem + kStages * kStage;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStage];
 
   // Workgroups b and b + 8 run on the same XCD: the M tiles that share a
   // column tile of the weight are placed 8 apart.
@@ -105,206 +94,237 @@ __global__ __launch_bounds__(kThreadsG) void q8_gemm_kernel(
   const int m0 = mt * kBM, n0 = nt * kBN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nk = K / kBK;
+  const int nk = (K + kBK - 1) / kBK;
 
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, M * K * 2);
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wp, packed_bytes);
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, (K / G) * N * 4);
 
-  // X: wave w loads stage rows 8w .. 8w + 7, lane l row 8w + l / 8, chunk
-  // position l % 8.
-  const int a_row = 8 * wave + (lane >> 3);
-  const int a_off = m0 + a_row < M ? (m0 + a_row) * K * 2 + 16 * swz(a_row, lane & 7) : -1;
-  // Codes: wave w loads row w of octet o = l % 8 of chunk l / 8.  The piece of
-  // row k, chunk q sits at ((panel u + k % u) nta + (k / u) cpp + q % cpp) 16
-  // with panel = q / cpp; (bs, bi) track (k / u, k % u) from stage to stage.
-  const int q = n0 / 16 + (lane >> 3);
-  const bool b_live = q < N / 16;
-  const int b_panel = b_live ? q / cpp : 0, b_chunk = q % cpp;
-  int bs, bi;
-  {
-    const int k = 8 * (lane & 7) + wave;
-    bs = k / u;
-    bi = k % u;
+  // X: load t of wave w fills stage rows 4 (4 w + t) .. + 3; lane l brings
+  // row 4 (4 w + t) + l / 16, chunk position l % 16.
+  int a_off[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int row = 4 * (4 * wave + t) + (lane >> 4);
+    a_off[t] = m0 + row < M ? (m0 + row) * K * 2 + 16 * swz(row, lane & 15) : -1;
   }
-  const int step_s = kBK / u, step_i = kBK % u;
-  // Scales (wave 0): lane l < 32 loads columns n0 + 4 l .. + 3 of the group.
-  const int s_col = n0 + 4 * lane;
-  const bool s_live = lane < 32 && s_col < N;
+  // Codes: load t of wave w fills slots 64 (4 w + t) ..: i = 2 w + t / 2,
+  // chunk c = 4 (t % 2) + l / 16, octet o = (l % 16) ^ 4 (c % 4).  The piece of
+  // row k, 16-column chunk q sits at ((panel u + k % u) nta + (k / u) cpp +
+  // q % cpp) 16, panel = q / cpp; (bs, bi) track (k / u, k % u) per row.
+  const int b_oct = (lane & 15) ^ (4 * ((lane >> 4) & 3));
+  int b_base[2];  // chunk part of the piece offset
+  bool b_live[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int q = n0 / 16 + 4 * t + (lane >> 4);
+    b_live[t] = q < N / 16;
+    b_base[t] = b_live[t] ? ((q / cpp) * u * nta + q % cpp) * 16 : 0;
+  }
+  // Row part (k % u) nta 16 + (k / u) cpp 16 of the two rows, kept up to date
+  // from stage to stage without multiplies.
+  int bi[2], b_rowoff[2], brow[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    brow[r] = 8 * b_oct + 2 * wave + r;  // row within the stage
+    bi[r] = brow[r] % u;
+    b_rowoff[r] = (bi[r] * nta + (brow[r] / u) * cpp) * 16;
+  }
+  const int step_i = kBK % u;
+  const int step_off = (step_i * nta + (kBK / u) * cpp) * 16;  // no wrap of k % u
+  const int wrap_off = (cpp - u * nta) * 16;                   // extra when k % u wraps
+  // Scales (wave 0): lanes 0..31 columns n0 + 4 l .. + 3 of the group of the
+  // stage's first row, lanes 32..63 the same columns of the group of row 64.
+  const int s_col = n0 + 4 * (lane & 31);
+  const bool s_live = s_col < N;
 
   auto issue = [&](int kt, int slot) {
     const int k0 = kt * kBK;
     lds_u8* base = (lds_u8*)smem + slot * kStage;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)(base + 1024 * wave), 16,
-                                             a_off >= 0 ? a_off + 2 * k0 : kOutOfRange, 0, 0, 0);
-    const int boff = ((b_panel * u + bi) * nta + bs * cpp + b_chunk) * 16;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        wr, (__attribute__((address_space(3))) void*)(base + kStageA + 1024 * wave), 16,
-        b_live ? boff : kOutOfRange, 0, 0, 0);
-    bi += step_i;
-    const bool wrap = bi >= u;
-    bi -= wrap ? u : 0;
-    bs += step_s + (wrap ? 1 : 0);
-    if (wave == 0)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xr, (__attribute__((address_space(3))) void*)(base + 1024 * (4 * wave + t)), 16,
+          (a_off[t] >= 0 && k0 + 8 * swz(4 * (4 * wave + t) + (lane >> 4), lane & 15) < K)
+              ? a_off[t] + 2 * k0 : kOutOfRange,
+          0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int r = t >> 1, c = t & 1;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          wr, (__attribute__((address_space(3))) void*)(base + kStageA + 1024 * (4 * wave + t)), 16,
+          (b_live[c] && k0 + brow[r] < K) ? b_base[c] + b_rowoff[r] : kOutOfRange, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      bi[r] += step_i;
+      const bool wrap = bi[r] >= u;
+      bi[r] -= wrap ? u : 0;
+      b_rowoff[r] += step_off + (wrap ? wrap_off : 0);
+    }
+    if (wave == 0) {
+      const int g = (k0 + (lane >= 32 ? 64 : 0)) / G;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           sr, (__attribute__((address_space(3))) void*)(base + kStageA + kStageB), 16,
-          s_live ? ((k0 / G) * N + s_col) * 4 : kOutOfRange, 0, 0, 0);
-  };
-
-  // Codes of one stage -> fp16 tile [n][k].  Wave w takes rows 4 (w % 2) ..
-  // + 3 of every octet of chunks 2 (w / 2) and 2 (w / 2) + 1; lane l: chunk
-  // 2 (w / 2) + l / 32, octet (l / 4) % 8, 4-column group l % 4.  The 64
-  // lanes of one read hit 64 distinct banks.
-  const int cv_half = wave & 1, cv_chunk = 2 * (wave >> 1) + (lane >> 5);
-  const int cv_oct = (lane >> 2) & 7, cv_grp = lane & 3;
-  auto convert = [&](int slot) {
-    const unsigned char* Bq = smem + slot * kStage + kStageA;
-    unsigned char* Bt = btile;
-    uint32_t D[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 4 * cv_half + r;
-      D[r] = *reinterpret_cast<const uint32_t*>(Bq + (8 * (8 * i + cv_chunk) + cv_oct) * 16 + 4 * cv_grp);
-    }
-    // Rows (0, 1) and (2, 3) interleaved per column: bytes c0r0 c0r1 c1r0 c1r1.
-    const uint32_t t01[2] = {__builtin_amdgcn_perm(D[1], D[0], 0x05010400u),
-                             __builtin_amdgcn_perm(D[1], D[0], 0x07030602u)};
-    const uint32_t t23[2] = {__builtin_amdgcn_perm(D[3], D[2], 0x05010400u),
-                             __builtin_amdgcn_perm(D[3], D[2], 0x07030602u)};
-    const h2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // u = q + 128 into the low byte of fp16 1024 (0x64 high byte): 1024 + u.
-      const uint32_t sel = (j & 1) ? 0x04030402u : 0x04010400u;
-      const h2 a = as_h2(__builtin_amdgcn_perm(0x64646464u, t01[j >> 1], sel)) + bias;
-      const h2 b = as_h2(__builtin_amdgcn_perm(0x64646464u, t23[j >> 1], sel)) + bias;
-      const int n = 16 * cv_chunk + 4 * cv_grp + j;
-      lds_store_b64(Bt + n * kRow + 16 * swz(n, cv_oct) + 8 * cv_half, as_u32(a), as_u32(b));
+          s_live ? (g * N + s_col) * 4 : kOutOfRange, 0, 0, 0);
     }
   };
 
-  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves, each 32 x 32
+  const int wm = wave >> 1, wn = wave & 1;  // 2 x 2 waves, each 32 rows x 64 columns
   const int fr = lane & 15, fq = lane >> 4;
-  struct Frag {
-    h8 a[2][2], b[2][2];
-    f32x4 s[2];
-  };
-  auto read_frags = [&](int slot, bool group_end, Frag& f) {
-    const unsigned char* As = smem + slot * kStage;
-    const unsigned char* Bt = btile;
+  const int fp = fr >> 2, fd = fr & 3;
+  // Byte offset of this lane's code word in the stage for e = 0, k32 step h
+  // (e adds 2048: 8 i + c grows by 8).
+  // LDS byte offsets (within a stage) of this lane's fragment reads, per k32
+  // step h: X rows wm 32 + 16 i + l % 16; the code word of row e = 0 (row e
+  // adds 2048: 8 i + c grows by 8).
+  int a_lds[4][2], b_lds[4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = 4 * h + fq;
+  for (int h = 0; h < 4; ++h) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int row = wm * 32 + 16 * i + fr;
-        f.a[h][i] = *reinterpret_cast<const h8*>(As + row * kRow + 16 * swz(row, c));
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = wn * 32 + 16 * j + fr;
-        f.b[h][j] = *reinterpret_cast<const h8*>(Bt + n * kRow + 16 * swz(n, c));
-      }
+    for (int i = 0; i < 2; ++i) {
+      const int row = wm * 32 + 16 * i + fr;
+      a_lds[h][i] = row * kRowA + 16 * swz(row, 4 * h + fq);
     }
-    if (group_end) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        f.s[j] = *reinterpret_cast<const f32x4*>(As + kStageA + kStageB +
-                                                 4 * (wn * 32 + 16 * j + 4 * fq));
-    }
-  };
+    b_lds[h] = kStageA + (16 * (4 * wn + fp) + fq + 4 * (h ^ fp)) * 16 + 4 * fd;
+  }
 
-  // With the weight as the first operand the accumulator is C transposed:
-  // lane l holds C[m][n .. n + 3], m = l % 16, n = 4 (l / 16).
-  f32x4 acc[2][2], tot[2][2];
+  // acc: this group's sums of x * u (u = q + 128, as fp16 subnormals u 2^-24);
+  // xacc: the same sums with every u = 128, i.e. 128 2^-24 sum(x), one
+  // matrix-core product per row block against a constant operand; at the end
+  // of a group tot += (acc - xacc) * scale, all in units of 2^-24.
+  f32x4 acc[2][4], tot[2][4], xacc[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      acc[i][j] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-      tot[i][j] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < 4; ++j) tot[i][j] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+  const h8 c128 = __builtin_bit_cast(h8, (u32x4){0x00800080u, 0x00800080u, 0x00800080u, 0x00800080u});
+
+  // One k32 step of the stage in slot S: LDS reads; then each code byte into
+  // the low byte of an fp16 whose other bits are zero (the subnormal u 2^-24),
+  // two rows per register, one v_perm_b32 per register.
+  struct Step {
+    h8 a[2];
+    uint32_t D[8];
+  };
+  auto read_step = [&](const unsigned char* S, int h, Step& st) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) st.a[i] = *reinterpret_cast<const h8*>(S + a_lds[h][i]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.D[e] = *reinterpret_cast<const uint32_t*>(S + b_lds[h] + 2048 * e);
+  };
+  auto convert = [&](const Step& st, h8 b[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t sel = 0x0C000C00u | ((4u + j) << 16) | (uint32_t)j;
+      const u32x4 w = {__builtin_amdgcn_perm(st.D[1], st.D[0], sel), __builtin_amdgcn_perm(st.D[3], st.D[2], sel),
+                       __builtin_amdgcn_perm(st.D[5], st.D[4], sel), __builtin_amdgcn_perm(st.D[7], st.D[6], sel)};
+      b[j] = __builtin_bit_cast(h8, w);
     }
-  auto mma = [&](const Frag& f, bool group_end) {
+  };
+  auto group_end = [&](const unsigned char* S, int h) {
+    // 16 scales of this lane's columns, v[r][j] for column 16 (l / 16) + 4 r + j.
+    const unsigned char* sc = S + kStageA + kStageB + 512 * (h >> 1) + 4 * (wn * 64 + 16 * fq);
+    f32x4 v[4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int r = 0; r < 4; ++r) v[r] = *reinterpret_cast<const f32x4*>(sc + 16 * r);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.b[h][j], f.a[h][i], acc[i][j], 0, 0, 0);
-    if (group_end) {
+      for (int j = 0; j < 4; ++j) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+        for (int r = 0; r < 4; ++r)
+          tot[i][j][r] = __builtin_fmaf(acc[i][j][r] - xacc[i][r], v[r][j], tot[i][j][r]);
+      }
+    }
+  };
+  // Software pipeline over the 4 k32 steps of a stage: step h + 1's LDS
+  // reads are issued before step h's matrix-core work and its conversion
+  // runs while those instructions execute.
+  // gpos: offset of the stage's first row inside its group (a multiple of 64).
+  auto compute = [&](int slot, int gpos) {
+    const bool start0 = gpos == 0;          // a group starts at row 0 of the stage
+    const bool mid = gpos + 64 == G;        // ... ends at row 63 and the next starts at 64
+    const bool end3 = gpos + 128 == G || gpos + 128 == 2 * G;  // ... ends at row 127
+    const unsigned char* S = smem + slot * kStage;
+    Step st[2];
+    h8 b[2][4];
+    read_step(S, 0, st[0]);
+    convert(st[0], b[0]);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+    for (int h = 0; h < 4; ++h) {
+      if (h < 3) read_step(S, h + 1, st[(h + 1) & 1]);
+      // The first k32 step of a group starts its sums from zero.
+      const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+      if ((h == 0 && start0) || (h == 2 && mid)) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) tot[i][j][r] = __builtin_fmaf(acc[i][j][r], f.s[j][r], tot[i][j][r]);
-          acc[i][j] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+        for (int i = 0; i < 2; ++i) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[h & 1][j], st[h & 1].a[i], zero, 0, 0, 0);
+          xacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(c128, st[h & 1].a[i], zero, 0, 0, 0);
         }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[h & 1][j], st[h & 1].a[i], acc[i][j], 0, 0, 0);
+          xacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(c128, st[h & 1].a[i], xacc[i], 0, 0, 0);
+        }
+      }
+      if (h < 3) convert(st[(h + 1) & 1], b[(h + 1) & 1]);
+      if ((h == 1 && mid) || (h == 3 && end3)) group_end(S, h);
     }
   };
-  auto ends_group = [&](int kt) { return kt + 1 == nk || ((kt + 1) * kBK) % G == 0; };
 
-  // Prologue: fill every slot, wait for stage 0, convert it, read it.
-#pragma unroll
-  for (int s = 0; s < kStages; ++s)
-    if (s < nk) issue(s, s);
-  if (nk >= kStages)
-    wait_stages<kStages - 1>(wave);
-  else
-    wait_vmcnt<0>();
-  lds_barrier();
-  convert(0);
-  lds_barrier();
-  Frag F0, F1;
-  read_frags(0, ends_group(0), F0);
-
-  // Step t: stage t + 1 has landed for every wave; the slot of stage t (read
-  // and converted already) is refilled with stage t + kStages; stage t + 1 is
-  // converted and its fragments read; stage t (in registers) is multiplied.
-  auto step = [&](int kt, Frag& cur, Frag& nxt) {
-    if (kt + kStages - 1 < nk)
-      wait_stages<kStages - 2>(wave);
-    else
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
+  int gpos = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    // Stage kt has landed for this wave (stage kt + 1 may be in flight).
+    if (kt + 1 < nk) {
+      if (wave == 0)
+        wait_vmcnt<kLoads + 1>();
+      else
+        wait_vmcnt<kLoads>();
+    } else {
       wait_vmcnt<0>();
+    }
+    // ... for every wave; and every wave is done with stage kt - 1, whose
+    // slot takes stage kt + 2.
     lds_barrier();
-    if (kt + kStages < nk) issue(kt + kStages, kt % kStages);
-    convert((kt + 1) % kStages);
-    lds_barrier();
-    read_frags((kt + 1) % kStages, ends_group(kt + 1), nxt);
-    mma(cur, ends_group(kt));
-  };
-  int kt = 0;
-  for (; kt + 2 < nk; kt += 2) {
-    step(kt, F0, F1);
-    step(kt + 1, F1, F0);
-  }
-  if (kt + 1 < nk) {
-    step(kt, F0, F1);
-    mma(F1, true);
-  } else {
-    mma(F0, true);
+    if (kt + 2 < nk) issue(kt + 2, (kt + 2) % kStages);
+    compute(kt % kStages, gpos);
+    gpos += kBK;
+    gpos -= gpos >= G ? G : 0;
+    gpos -= gpos >= G ? G : 0;
   }
 
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int m = m0 + wm * 32 + 16 * i + fr;
-    if (m >= M) continue;
+    const int n = n0 + wn * 64 + 16 * fq;
+    if (m >= M || n >= N) continue;
+    uint32_t w[8];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + wn * 32 + 16 * j + 4 * fq;
-      if (n >= N) continue;
-      const h2 lo = {(_Float16)tot[i][j][0], (_Float16)tot[i][j][1]};
-      const h2 hi = {(_Float16)tot[i][j][2], (_Float16)tot[i][j][3]};
-      *reinterpret_cast<uint2*>(Y + (size_t)m * N + n) = make_uint2(as_u32(lo), as_u32(hi));
+    for (int r = 0; r < 4; ++r) {
+      const h2 lo = {(_Float16)(tot[i][0][r] * kTwo24), (_Float16)(tot[i][1][r] * kTwo24)};
+      const h2 hi = {(_Float16)(tot[i][2][r] * kTwo24), (_Float16)(tot[i][3][r] * kTwo24)};
+      w[2 * r] = as_u32(lo);
+      w[2 * r + 1] = as_u32(hi);
     }
+    uint4* dst = reinterpret_cast<uint4*>(Y + (size_t)m * N + n);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
   }
 }
 
 bool q8_gemm_supported(int M, int K, int N, int G) {
   (void)M;
   (void)N;
-  return G % kBK == 0 && K % kBK == 0;
+  (void)K;
+  return G % 64 == 0;
 }
 
 hipError_t launch_q8_gemm(const void* X, const void* packed, const float* scales, void* Y, int M,
