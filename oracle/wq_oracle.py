@@ -27,7 +27,10 @@ Sources (page title, then section):
   - "量化粒度" (granularity): x = S*(q - Z); per-channel scales for weights,
     per-token for activations, group-wise (group 128) for int4;
   - "Weight Store" / "Int4 Weight Only Quantization": int4 codes are packed
-    into a wider integer along the dimension one thread walks (K).
+    into a wider integer along the dimension one thread walks (K);
+  - "Marlin 格式" (its part on working with the compute kernel): the
+    asymmetric (AWQ) form rebuilds a weight as (W_int4 - Zero) * Scale from
+    an unsigned 4-bit value, a zero and a scale of its group.
 * "融合反量化与GEMM：LLM推理的CUDA内核优化实践" (zingnex.cn), "技术实现细节":
   symmetric int8 weights with one scale per group of 128 along K.
 * "GPTQ算法解析" (intelliparadigm.com), section 4.1: group size 128,
@@ -41,6 +44,9 @@ design notes):
   three consecutive int32 words of one column; 4-bit row ``8r + j`` in
   nibble ``j`` of word ``r``, stored as ``q + 8``.
 * 3-bit dequant uses the stored zero as given: ``w = scale*q - zero``.
+* The asymmetric 4-bit form takes the unsigned nibble ``u`` (0..15) as the
+  integer value and one fp16 zero and one fp16 scale per (group, column),
+  both as given: ``w = (u - zero) * scale``.
 * Outputs are overwritten (no accumulate into the caller's buffer), no bias.
 * The activation quantiser divides (``absmax / 127`` then ``x / Sx``) in fp32
   with IEEE round-to-nearest, rounds half to even and clamps to [-127, 127];
@@ -53,8 +59,9 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "bits_le", "unpack_q3", "unpack_q4", "dequant_q3", "dequant_q8_group",
-    "dequant_q4_group", "matvec_q3", "gemm_q8_group", "gemm_q4_group",
+    "bits_le", "unpack_q3", "unpack_u4", "unpack_q4", "dequant_q3", "dequant_q8_group",
+    "dequant_q4_group", "dequant_q4_zp", "matvec_q3", "gemm_q8_group", "gemm_q4_group",
+    "gemm_q4_zp",
     "quantize_rows_int8", "w8a8_accumulate", "w8a8_epilogue",
     "bf16_rne_bits", "bf16_bits_to_f32", "gemm_w8a8",
 ]
@@ -90,17 +97,22 @@ def unpack_q3(qweight: np.ndarray) -> np.ndarray:
     return codes.transpose(0, 2, 1).reshape(nb * 32, N)
 
 
-def unpack_q4(qweight: np.ndarray) -> np.ndarray:
-    """Signed 4-bit codes ``[K, N]`` (-8..7) from int32 ``[K/8, N]``.
+def unpack_u4(qweight: np.ndarray) -> np.ndarray:
+    """Unsigned 4-bit values ``[K, N]`` (0..15) from int32 ``[K/8, N]``.
 
-    Row 8r + j is bits 4j..4j+3 of word r (unsigned ``u``); the code is u - 8.
+    Row 8r + j is bits 4j..4j+3 of word r.
     """
     qweight = np.asarray(qweight)
     R, N = qweight.shape
     b = bits_le(qweight).astype(np.int64)             # [R, N, 32]
     nib = b.reshape(R, N, 8, 4)
     u = nib[..., 0] + 2 * nib[..., 1] + 4 * nib[..., 2] + 8 * nib[..., 3]  # [R, N, 8]
-    return u.transpose(0, 2, 1).reshape(R * 8, N) - 8
+    return u.transpose(0, 2, 1).reshape(R * 8, N)
+
+
+def unpack_q4(qweight: np.ndarray) -> np.ndarray:
+    """Signed 4-bit codes ``[K, N]`` (-8..7): the unsigned value u minus 8."""
+    return unpack_u4(qweight) - 8
 
 
 # --------------------------------------------------------------------------
@@ -129,6 +141,17 @@ def dequant_q4_group(q: np.ndarray, scales: np.ndarray, g_idx: np.ndarray | None
     return np.asarray(scales).astype(np.float64)[g, :] * q.astype(np.float64)
 
 
+def dequant_q4_zp(u: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
+                  g_idx: np.ndarray | None, G: int) -> np.ndarray:
+    """``W[k, n] = (u[k, n] - zero[g, n]) * scale[g, n]``, ``g = g_idx[k]``
+    (``k // G`` when ``g_idx`` is None), in fp64."""
+    K = u.shape[0]
+    g = (np.arange(K) // G) if g_idx is None else np.asarray(g_idx).astype(np.int64)
+    z = np.asarray(zeros).astype(np.float64)[g, :]
+    s = np.asarray(scales).astype(np.float64)[g, :]
+    return (u.astype(np.float64) - z) * s
+
+
 # --------------------------------------------------------------------------
 # Weight-only products (fp64, unrounded)
 # --------------------------------------------------------------------------
@@ -150,6 +173,13 @@ def gemm_q4_group(X: np.ndarray, qweight: np.ndarray, scales: np.ndarray,
                   g_idx: np.ndarray | None, G: int) -> np.ndarray:
     """``Y = X . W`` with W the dequantised group-wise 4-bit weight; fp64."""
     W = dequant_q4_group(unpack_q4(qweight), scales, g_idx, G)
+    return np.atleast_2d(np.asarray(X).astype(np.float64)) @ W
+
+
+def gemm_q4_zp(X: np.ndarray, qweight: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
+               g_idx: np.ndarray | None, G: int) -> np.ndarray:
+    """``Y = X . W`` with W the dequantised asymmetric 4-bit weight; fp64."""
+    W = dequant_q4_zp(unpack_u4(qweight), scales, zeros, g_idx, G)
     return np.atleast_2d(np.asarray(X).astype(np.float64)) @ W
 
 

@@ -28,7 +28,7 @@ import numpy as np
 
 __all__ = [
     "pack_q3", "pack_q4", "gen_q3", "gen_q8_group", "gen_q4_group",
-    "gen_w8a8", "SEEDS",
+    "gen_w8a8", "gen_q4_zp", "SEEDS",
 ]
 
 # Seeds of the named workloads (the tests and the benchmark use these).
@@ -40,6 +40,7 @@ SEEDS = {
     "q3_f16_4096x11008": 1201,
     "q3_f16_11008x4096": 1202,
     "q4_group_actorder": 1300,   # weights; activations use 1300 + M
+    "q4_zp": 1600,               # asymmetric 4-bit; activations use 1600 + M
     "w8a8_256x8192x8192": 1400,
 }
 
@@ -168,6 +169,47 @@ def gen_q4_group(M: int, K: int, N: int, G: int, seed: int, act_order: bool = Tr
     X = xr.standard_normal((M, K)).astype(np.float16)
     return {"X": X, "qweight": qweight, "scales": scales, "g_idx": g_idx,
             "codes": q, "M": M, "K": K, "N": N, "G": G}
+
+
+def gen_q4_zp(M: int, K: int, N: int, G: int, seed: int, act_order: bool = False,
+              x_seed: int | None = None) -> dict:
+    """Asymmetric (AWQ-style) 4-bit group-wise inputs: unsigned values, a zero
+    point and a scale per (group, column).
+
+    Draw order (weight rng ``seed``): W ~ N(0, 0.02) fp32 [K,N]; then, with
+    act-order, ``g_idx`` as in :func:`gen_q4_group` (else ``k // G``).  Per
+    (group, column): ``scale = fp16((max - min) / 15)`` over the group's rows,
+    ``zero = clip(rint(-min / fp32(scale)), 0, 15)`` (an integer, stored fp16)
+    and ``u = clip(rint(W / fp32(scale)) + zero, 0, 15)``, packed as
+    :func:`pack_q4`.  X ~ N(0,1) fp16 [M,K] from rng ``x_seed`` (default
+    ``seed + M``).
+    """
+    if K % G or K % 8:
+        raise ValueError("K must be a multiple of G and of 8")
+    rng = np.random.default_rng(seed)
+    W = rng.normal(0.0, 0.02, size=(K, N)).astype(np.float32)
+    ng = K // G
+    if act_order:
+        g_idx = rng.permutation(np.repeat(np.arange(ng), G)).astype(np.int32)
+    else:
+        g_idx = (np.arange(K) // G).astype(np.int32)
+    wmin = np.zeros((ng, N), dtype=np.float32)
+    wmax = np.zeros((ng, N), dtype=np.float32)
+    for g in range(ng):
+        wmin[g] = np.min(W[g_idx == g], axis=0)
+        wmax[g] = np.max(W[g_idx == g], axis=0)
+    scales = ((wmax - wmin) / np.float32(15.0)).astype(np.float16)   # [K/G, N]
+    s32 = scales.astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        z = np.where(s32 == 0, np.float32(0), np.rint(-wmin / s32))
+    z = np.clip(z, 0, 15)
+    zeros = z.astype(np.float16)
+    u = np.clip(_quantise(W, s32[g_idx], -(1 << 20), 1 << 20) + z[g_idx].astype(np.int64), 0, 15)
+    qweight = pack_q4(u)
+    xr = np.random.default_rng(seed + M if x_seed is None else x_seed)
+    X = xr.standard_normal((M, K)).astype(np.float16)
+    return {"X": X, "qweight": qweight, "scales": scales, "zeros": zeros, "g_idx": g_idx,
+            "u": u, "W": W, "M": M, "K": K, "N": N, "G": G}
 
 
 def gen_w8a8(M: int, K: int, N: int, seed: int) -> dict:

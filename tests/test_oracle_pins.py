@@ -295,3 +295,71 @@ def test_w8a8_epilogue_ties_through_path():
     acc = np.array([[257, 259, 514, 518, -257]], np.int32)
     y = oracle.bf16_bits_to_f32(oracle.w8a8_epilogue(acc, np.ones(1, np.float32), np.ones(5, np.float32)))
     assert y.tolist() == [[256.0, 260.0, 512.0, 520.0, -256.0]]
+
+
+# ------------------------------------------------- asymmetric 4-bit (AWQ) --
+
+def test_q4_zp_worked_examples():
+    for name, words, G, zeros, scales, x, y in read_golden("q4_zp_worked.txt"):
+        w = np.array([int(h, 16) for h in words.split()], dtype=np.uint32)
+        qw = w.view(np.int32).reshape(-1, 1)
+        z = np.array([float(v) for v in zeros.split()]).reshape(-1, 1)
+        s = np.array([float(v) for v in scales.split()]).reshape(-1, 1)
+        xv = np.array([float(v) for v in x.split()]).reshape(1, -1)
+        got = oracle.gemm_q4_zp(xv, qw, s, z, None, int(G))
+        assert got.shape == (1, 1)
+        assert got[0, 0] == float(y), name
+
+
+def test_q4_zp_unsigned_nibbles_closed_form():
+    # nibble j of 0x76543210 is j; of 0xFEDCBA98 it is 8 + j.
+    w = np.array([0x76543210, 0xFEDCBA98], dtype=np.uint32).view(np.int32).reshape(2, 1)
+    assert np.array_equal(oracle.unpack_u4(w)[:, 0], np.arange(16))
+    assert np.array_equal(oracle.unpack_q4(w)[:, 0], np.arange(16) - 8)
+
+
+def test_q4_zp_zero_eight_is_the_symmetric_form():
+    # With every zero 8 the asymmetric form is the symmetric one (u = q + 8).
+    d = synth.gen_q4_group(3, 512, 40, 128, seed=61, act_order=True)
+    z = np.full_like(d["scales"], 8.0)
+    a = oracle.gemm_q4_zp(d["X"], d["qweight"], d["scales"], z, d["g_idx"], 128)
+    b = oracle.gemm_q4_group(d["X"], d["qweight"], d["scales"], d["g_idx"], 128)
+    assert np.array_equal(a, b)
+
+
+def test_q4_zp_shift_invariance():
+    # Adding the same constant to every value and zero of a group leaves W.
+    rng = np.random.default_rng(62)
+    K, N, G = 128, 8, 32
+    u = rng.integers(0, 14, size=(K, N))
+    z = rng.integers(0, 14, size=(K // G, N)).astype(np.float64)
+    s = rng.uniform(0.01, 0.1, size=(K // G, N))
+    x = rng.standard_normal((2, K))
+    a = oracle.gemm_q4_zp(x, synth.pack_q4(u), s, z, None, G)
+    b = oracle.gemm_q4_zp(x, synth.pack_q4(u + 1), s, z + 1, None, G)
+    assert np.allclose(a, b, rtol=1e-13, atol=1e-13)
+
+
+def test_q4_zp_group_index_and_column_brute_force():
+    # Tiny case summed term by term with exact rationals (scales and zeros
+    # picked as dyadic values), against the fp64 oracle.
+    rng = np.random.default_rng(63)
+    K, N, G = 16, 3, 8
+    u = rng.integers(0, 16, size=(K, N))
+    z = rng.integers(0, 16, size=(K // G, N)) / 2.0
+    s = rng.integers(1, 9, size=(K // G, N)) / 8.0
+    x = rng.integers(-3, 4, size=(1, K)).astype(np.float64)
+    got = oracle.gemm_q4_zp(x, synth.pack_q4(u), s, z, None, G)[0]
+    for n in range(N):
+        acc = Fraction(0)
+        for k in range(K):
+            g = k // G
+            acc += Fraction(x[0, k]) * (Fraction(int(u[k, n])) - Fraction(z[g, n])) * Fraction(s[g, n])
+        assert got[n] == float(acc), n
+
+
+def test_q4_zp_generator_roundtrip_bound():
+    d = synth.gen_q4_zp(1, 512, 64, 64, seed=64)
+    W = oracle.dequant_q4_zp(oracle.unpack_u4(d["qweight"]), d["scales"], d["zeros"], None, 64)
+    s = d["scales"].astype(np.float64)[np.arange(512) // 64]
+    assert np.all(np.abs(W - d["W"]) <= s * (0.5 + 1e-3) + 1e-12)
