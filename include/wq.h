@@ -162,6 +162,21 @@ int wq_prepack_q4(const int32_t* qweight, const int32_t* perm, void* packed, int
 int wq_gemm_q4_group(const void* X, const void* packed, const void* scales, void* Y, int M, int K,
                      int N, int G, void* stream);
 
+/* Asymmetric (AWQ-style) group-wise 4-bit GEMM:
+ *   Y[m, n] = sum_k X[m, k] * (u[k, n] - zero[g, n]) * scale[g, n],
+ *   g = g_idx[k] (through the row order inside the packed weight) or k / G,
+ * with u the stored unsigned nibble 0..15 (the same packed weight as
+ * wq_gemm_q4_group: wq_prepack_q4 stores the nibbles as given).
+ * ("Quantization CUDA", tom-jerr.github.io, section "量化粒度": x = S (q - Z),
+ * each group its own S and Z; section "Marlin 格式": the asymmetric step
+ * W_fp16 = (W_int4 - Zero) * Scale.)
+ * X [M, K] fp16; scales and zeros [K/G, N] fp16 (zeros as values, e.g. the
+ * integers 0..15); Y [M, N] fp16, written (fp32 accumulation; the zero is
+ * applied once per group to the accumulated sums).
+ * Rules: as wq_gemm_q4_group; zeros 16-byte aligned. */
+int wq_gemm_q4_group_zp(const void* X, const void* packed, const void* scales, const void* zeros,
+                        void* Y, int M, int K, int N, int G, void* stream);
+
 /* ----------------------------------------------------------------- W8A8 -- */
 
 /* W8A8 dynamic-quantisation GEMM:

@@ -83,6 +83,10 @@ def test_q4_validation(L):
     assert f(P, P, P, P, 0, 4096, 11008, 128, None) == wq.WQ_ERR_SHAPE
     assert f(P, P, P, P, 1, 32768 + 128, 64, 128, None) == wq.WQ_ERR_SHAPE   # K bound
     assert f(P, P_MIS, P, P, 1, 4096, 11008, 128, None) == wq.WQ_ERR_ALIGN
+    z = L.wq_gemm_q4_group_zp
+    assert z(P, P, P, None, P, 1, 4096, 11008, 128, None) == wq.WQ_ERR_NULL      # zeros
+    assert z(P, P, P, P, P, 1, 4096, 11006, 128, None) == wq.WQ_ERR_SHAPE
+    assert z(P, P, P, P_MIS, P, 1, 4096, 11008, 128, None) == wq.WQ_ERR_ALIGN
     g = L.wq_prepack_q4
     assert g(P, None, P, 12, 16, 32, None) == wq.WQ_ERR_SHAPE
     assert g(P, None, None, 64, 16, 32, None) == wq.WQ_ERR_NULL

@@ -307,6 +307,50 @@ def test_q4_integer_exact(wq):
     assert np.array_equal(Y, ref)
 
 
+# ====================================================== asymmetric 4-bit ==
+
+@pytest.mark.parametrize("M,K,N,G,act", [
+    (1, 4096, 11008, 128, False),   # AWQ-style layer shape, no act-order
+    (1, 4096, 4096, 64, False),     # group 64
+    (4, 2048, 1024, 32, False),     # group 32: four scale and zero loads per block
+    (8, 1024, 528, 128, False),
+    (3, 1024, 260, 128, True),      # zeros with an act-order row table; ragged N
+    (12, 512, 1028, 128, False),    # two row chunks (8 + 4)
+])
+def test_q4_zp_vs_oracle(wq, M, K, N, G, act):
+    d = synth.gen_q4_zp(M, K, N, G, seed=synth.SEEDS["q4_zp"] + K + N, act_order=act)
+    packed, _ = wq.prepare_q4(cu(d["qweight"]), d["g_idx"] if act else None, G)
+    Y = wq.gemm_q4_group_zp(cu(d["X"]), packed, cu(d["scales"]), cu(d["zeros"]), G)
+    ref = oracle.gemm_q4_zp(d["X"], d["qweight"], d["scales"], d["zeros"], d["g_idx"], G)
+    assert_tol(host(Y), ref, f"q4 zp {M}x{K}x{N} G{G} act={act}")
+
+
+def test_q4_zp_integer_exact_gpu(wq):
+    # Scales 1, integer zeros and small integer X: every fp32 partial sum is an
+    # exact integer, so the result equals the oracle's after one fp16 rounding.
+    rng = np.random.default_rng(65)
+    M, K, N, G = 2, 1024, 64, 128
+    u = rng.integers(0, 16, size=(K, N))
+    z = rng.integers(0, 16, size=(K // G, N)).astype(np.float16)
+    s = np.ones((K // G, N), np.float16)
+    X = rng.integers(-2, 3, size=(M, K)).astype(np.float16)
+    qw = synth.pack_q4(u)
+    packed, _ = wq.prepare_q4(cu(qw), None, G)
+    Y = host(wq.gemm_q4_group_zp(cu(X), packed, cu(s), cu(z), G))
+    ref = oracle.gemm_q4_zp(X, qw, s, z, None, G).astype(np.float16).astype(np.float64)
+    assert np.array_equal(Y, ref)
+
+
+def test_q4_zp_zero_eight_matches_symmetric_kernel(wq):
+    # The same packed weight through both entry points: zeros of 8 reproduce
+    # the symmetric product bit for bit (same kernel, same order of sums).
+    d = synth.gen_q4_group(4, 2048, 512, 128, seed=66, act_order=True)
+    packed, _ = wq.prepare_q4(cu(d["qweight"]), d["g_idx"], 128)
+    X, S = cu(d["X"]), cu(d["scales"])
+    z8 = torch.full_like(S, 8.0)
+    assert torch.equal(wq.gemm_q4_group_zp(X, packed, S, z8, 128), wq.gemm_q4_group(X, packed, S, 128))
+
+
 # ================================================================== W8A8 ==
 
 def _w8a8_check(wq, d):

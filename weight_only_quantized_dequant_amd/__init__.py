@@ -42,6 +42,7 @@ _SIGNATURES = {
     "wq_q4_act_order_perm": (_i, [_vp, _i, _i, _vp, _vp]),
     "wq_prepack_q4": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
     "wq_gemm_q4_group": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
+    "wq_gemm_q4_group_zp": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "wq_gemm_w8a8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
     "wq_unpack_q3": (_i, [_vp, _vp, _i, _i, _vp]),
     "wq_unpack_q8": (_i, [_vp, _vp, _i, _i, _vp]),
@@ -274,6 +275,26 @@ def gemm_q4_group(X, packed, scales, group_size=128, Y=None):
     st = lib().wq_gemm_q4_group(_ptr(X2), _ptr(packed), _ptr(scales), _ptr(Y), M, K, N, group_size,
                                 _stream(dev))
     _check("wq_gemm_q4_group", st)
+    return Y.reshape(N) if squeeze else Y
+
+
+def gemm_q4_group_zp(X, packed, scales, zeros, group_size=128, Y=None):
+    """Y[m, n] = sum_k X[m, k] * (u[k, n] - zero[g, n]) * scale[g, n] (asymmetric 4-bit)."""
+    squeeze = X.dim() == 1
+    X2 = X.reshape(1, -1) if squeeze else X
+    M, K = X2.shape
+    N = scales.shape[1]
+    dev = X.device
+    _need(X2, "X", torch.float16, (M, K), dev)
+    _need_packed(packed, WQ_OP_Q4G, K, N, group_size, dev)
+    _need(scales, "scales", torch.float16, (K // group_size, N), dev)
+    _need(zeros, "zeros", torch.float16, (K // group_size, N), dev)
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    _need(Y, "Y", torch.float16, (M, N), dev)
+    st = lib().wq_gemm_q4_group_zp(_ptr(X2), _ptr(packed), _ptr(scales), _ptr(zeros), _ptr(Y), M, K,
+                                   N, group_size, _stream(dev))
+    _check("wq_gemm_q4_group_zp", st)
     return Y.reshape(N) if squeeze else Y
 
 

@@ -125,11 +125,14 @@ __global__ __launch_bounds__(kThreads) void q4_prepack_kernel(const uint32_t* __
 // barrier at the end, then the workgroup sums the waves and writes Y.
 // NSC: scale loads per block (4 for G = 32, 2 for G = 64, 1 for G >= 128).
 // ---------------------------------------------------------------------------
-template <int MT, int NSC>
+// ZP: asymmetric form, w = (u - zero) * scale with an fp16 zero per (group,
+// column) ("Quantization CUDA", tom-jerr.github.io, sections "量化粒度" and
+// "Marlin 格式"); without it the offset is the fixed 8 of the symmetric codes.
+template <int MT, int NSC, bool ZP>
 __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
     const _Float16* __restrict__ X, const uint8_t* __restrict__ Wp,
-    const _Float16* __restrict__ scales, _Float16* __restrict__ Y, int M, int K, int N, int G,
-    int nb, int npanels, int packed_bytes) {
+    const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
+    _Float16* __restrict__ Y, int M, int K, int N, int G, int nb, int npanels, int packed_bytes) {
   typedef _Float16 h8 __attribute__((ext_vector_type(8)));
   typedef float f4 __attribute__((ext_vector_type(4)));
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -156,26 +159,31 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
 
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wp, packed_bytes);
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, (K / G) * N * 2);
+  const __amdgpu_buffer_rsrc_t zr = make_rsrc(ZP ? zeros : scales, (K / G) * N * 2);
   const int col = lane & 15;
 
   int lbpg = 0;  // log2(bpg): G is a power of two
   while ((1 << lbpg) < bpg) ++lbpg;
 
-  // Ring buffers: one 16-byte word quadruple and NSC scale bits per block.
+  // Ring buffers: one 16-byte word quadruple, NSC scale bits and (ZP) NSC
+  // zero bits per block.
+  constexpr int NZ = ZP ? NSC : 1;
   u32x4 wb0, wb1, wb2, wb3;
   uint32_t sc0[NSC], sc1[NSC], sc2[NSC], sc3[NSC];
+  uint32_t zp0[NZ], zp1[NZ], zp2[NZ], zp3[NZ];
   // Load cursor (panel of the run, block) walks the wave's blocks in order;
   // past the end it loads nothing (out-of-range offsets).
   int lp = nbw > 0 ? 0 : npr, lb = blo;
   int woff = ((p_begin * nb + blo) * 64 + lane) * 16;
-  auto load_item = [&](u32x4& w, uint32_t (&sc)[NSC]) {
+  auto load_item = [&](u32x4& w, uint32_t (&sc)[NSC], uint32_t (&zq)[NZ]) {
     const bool ok = lp < npr;
     const int n = (p_begin + lp) * kQ4Panel + col;
 #pragma unroll
     for (int k = 0; k < NSC; ++k) {
       const int g = NSC == 1 ? (lb >> lbpg) : lb * NSC + k;  // the group step k closes
-      sc[k] = __builtin_amdgcn_raw_buffer_load_b16(sr, (ok && n < N) ? (g * N + n) * 2 : kOutOfRange,
-                                                   0, 0);
+      const int off = (ok && n < N) ? (g * N + n) * 2 : kOutOfRange;
+      sc[k] = __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0);
+      if constexpr (ZP) zq[k] = __builtin_amdgcn_raw_buffer_load_b16(zr, off, 0, 0);
     }
     // The weights last: waiting for them covers the scales of the block.
     w = buffer_stream(wr, ok ? woff : kOutOfRange);
@@ -229,10 +237,10 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
   {
     u32x4 pv[CR], xq[CR][MT];
     stage_load(t, pv, xq);
-    load_item(wb0, sc0);
-    load_item(wb1, sc1);
-    load_item(wb2, sc2);
-    load_item(wb3, sc3);
+    load_item(wb0, sc0, zp0);
+    load_item(wb1, sc1, zp1);
+    load_item(wb2, sc2, zp2);
+    load_item(wb3, sc3, zp3);
     // Rows m < MT beyond K (block padding): zero.  The reduction tiles: zero.
     uint32_t* xz = reinterpret_cast<uint32_t*>(xa);
     const int padw = (rs - K) / 2;  // words per row past K
@@ -266,7 +274,7 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) apf[j] = *reinterpret_cast<const h8*>(xrow + (16 * blo + 4 * j) * 8);
   }
-  auto compute = [&](const u32x4& w, const uint32_t (&sc)[NSC]) {
+  auto compute = [&](const u32x4& w, const uint32_t (&sc)[NSC], const uint32_t (&zq)[NZ]) {
     const int pi = cp, b = cb;
     h8 a[4];
 #pragma unroll
@@ -296,9 +304,12 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
       }
       if (close) {
         const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sc[k]);
+        // -offset * 2^-24: the codes sit in the products as u * 2^-24.
+        float zoff = -8.0f / kTwo24;
+        if constexpr (ZP) zoff = (float)__builtin_bit_cast(_Float16, (uint16_t)zq[k]) * (-1.0f / kTwo24);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          tot[r] = __builtin_fmaf(s, __builtin_fmaf(S0[r] + S1[r], -8.0f / kTwo24, C0[r] + C1[r]), tot[r]);
+          tot[r] = __builtin_fmaf(s, __builtin_fmaf(S0[r] + S1[r], zoff, C0[r] + C1[r]), tot[r]);
           C0[r] = C1[r] = S0[r] = S1[r] = 0.0f;
         }
       }
@@ -315,17 +326,17 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
       ++cp;
     }
   };
-  auto step = [&](int q, u32x4& w, uint32_t (&sc)[NSC]) {
-    if (q < nitems) compute(w, sc);
+  auto step = [&](int q, u32x4& w, uint32_t (&sc)[NSC], uint32_t (&zq)[NZ]) {
+    if (q < nitems) compute(w, sc, zq);
     // Unconditional (out-of-range past the end), so the loads of every ring
     // slot keep one issue order and each wait covers just its own block.
-    load_item(w, sc);
+    load_item(w, sc, zq);
   };
   for (int q = 0; q < nitems; q += kQ4Ring) {
-    step(q, wb0, sc0);
-    step(q + 1, wb1, sc1);
-    step(q + 2, wb2, sc2);
-    step(q + 3, wb3, sc3);
+    step(q, wb0, sc0, zp0);
+    step(q + 1, wb1, sc1, zp1);
+    step(q + 2, wb2, sc2, zp2);
+    step(q + 3, wb3, sc3, zp3);
   }
   __syncthreads();
   for (int r = t; r < npr * MT * 16; r += kQ4Threads) {
@@ -392,35 +403,46 @@ hipError_t launch_q4_unpack(const void* packed, const int32_t* perm, int8_t* cod
   return hipGetLastError();
 }
 
-template <int MT, int NSC>
-static hipError_t launch_q4_t(const void* X, const void* packed, const void* scales, void* Y,
-                              int M, int K, int N, int G, const PanelPlan& p, hipStream_t s) {
+template <int MT, int NSC, bool ZP>
+static hipError_t launch_q4_t(const void* X, const void* packed, const void* scales,
+                              const void* zeros, void* Y, int M, int K, int N, int G,
+                              const PanelPlan& p, hipStream_t s) {
   const int cus = device_cus();
   int grid = p.npanels < cus ? p.npanels : cus;
   if ((p.npanels + grid - 1) / grid > kQ4MaxRun) grid = (p.npanels + kQ4MaxRun - 1) / kQ4MaxRun;
   const size_t lds = ((size_t)p.u * kQ4Block + kQ4RowPad) * MT * 2 + (size_t)kQ4MaxRun * kQ4Waves * MT * 16 * 4;
   if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&q4_mfma_kernel<MT, NSC>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&q4_mfma_kernel<MT, NSC, ZP>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((q4_mfma_kernel<MT, NSC>), dim3(grid), dim3(kQ4Threads), lds, s,
+  hipLaunchKernelGGL((q4_mfma_kernel<MT, NSC, ZP>), dim3(grid), dim3(kQ4Threads), lds, s,
                      reinterpret_cast<const _Float16*>(X), reinterpret_cast<const uint8_t*>(packed),
-                     reinterpret_cast<const _Float16*>(scales), reinterpret_cast<_Float16*>(Y), M,
+                     reinterpret_cast<const _Float16*>(scales),
+                     reinterpret_cast<const _Float16*>(zeros), reinterpret_cast<_Float16*>(Y), M,
                      K, N, G, p.u, p.npanels, (int)q4_block_bytes(p));
   return hipGetLastError();
 }
 
-template <int MT>
-static hipError_t launch_q4_mt(const void* X, const void* packed, const void* scales, void* Y,
-                               int M, int K, int N, int G, const PanelPlan& p, hipStream_t s) {
-  if (G == 32) return launch_q4_t<MT, 4>(X, packed, scales, Y, M, K, N, G, p, s);
-  if (G == 64) return launch_q4_t<MT, 2>(X, packed, scales, Y, M, K, N, G, p, s);
-  return launch_q4_t<MT, 1>(X, packed, scales, Y, M, K, N, G, p, s);
+template <int MT, bool ZP>
+static hipError_t launch_q4_zp(const void* X, const void* packed, const void* scales,
+                               const void* zeros, void* Y, int M, int K, int N, int G,
+                               const PanelPlan& p, hipStream_t s) {
+  if (G == 32) return launch_q4_t<MT, 4, ZP>(X, packed, scales, zeros, Y, M, K, N, G, p, s);
+  if (G == 64) return launch_q4_t<MT, 2, ZP>(X, packed, scales, zeros, Y, M, K, N, G, p, s);
+  return launch_q4_t<MT, 1, ZP>(X, packed, scales, zeros, Y, M, K, N, G, p, s);
 }
 
-hipError_t launch_q4_group(const void* X, const void* packed, const void* scales, void* Y, int M,
-                           int K, int N, int G, hipStream_t s) {
+template <int MT>
+static hipError_t launch_q4_mt(const void* X, const void* packed, const void* scales,
+                               const void* zeros, void* Y, int M, int K, int N, int G,
+                               const PanelPlan& p, hipStream_t s) {
+  return zeros ? launch_q4_zp<MT, true>(X, packed, scales, zeros, Y, M, K, N, G, p, s)
+               : launch_q4_zp<MT, false>(X, packed, scales, zeros, Y, M, K, N, G, p, s);
+}
+
+hipError_t launch_q4_group(const void* X, const void* packed, const void* scales,
+                           const void* zeros, void* Y, int M, int K, int N, int G, hipStream_t s) {
   const PanelPlan p = plan_q4(K, N, G);
   const int mtmax = q4_max_mt(K);
   for (int m0 = 0; m0 < M; m0 += mtmax) {
@@ -430,10 +452,10 @@ hipError_t launch_q4_group(const void* X, const void* packed, const void* scales
     void* Yc = reinterpret_cast<char*>(Y) + (size_t)m0 * N * 2;
     hipError_t e;
     switch (mt) {
-      case 1: e = launch_q4_mt<1>(Xc, packed, scales, Yc, mc, K, N, G, p, s); break;
-      case 2: e = launch_q4_mt<2>(Xc, packed, scales, Yc, mc, K, N, G, p, s); break;
-      case 4: e = launch_q4_mt<4>(Xc, packed, scales, Yc, mc, K, N, G, p, s); break;
-      default: e = launch_q4_mt<8>(Xc, packed, scales, Yc, mc, K, N, G, p, s); break;
+      case 1: e = launch_q4_mt<1>(Xc, packed, scales, zeros, Yc, mc, K, N, G, p, s); break;
+      case 2: e = launch_q4_mt<2>(Xc, packed, scales, zeros, Yc, mc, K, N, G, p, s); break;
+      case 4: e = launch_q4_mt<4>(Xc, packed, scales, zeros, Yc, mc, K, N, G, p, s); break;
+      default: e = launch_q4_mt<8>(Xc, packed, scales, zeros, Yc, mc, K, N, G, p, s); break;
     }
     if (e != hipSuccess) return e;
   }

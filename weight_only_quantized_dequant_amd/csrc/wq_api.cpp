@@ -174,7 +174,18 @@ int wq_gemm_q4_group(const void* X, const void* packed, const void* scales, void
   if (M < 1) return WQ_ERR_SHAPE;
   if ((long long)M * K * 2 > kMaxBytes) return WQ_ERR_SHAPE;
   if (!aligned16(X) || !aligned16(packed) || !aligned16(scales)) return WQ_ERR_ALIGN;
-  return hip_status(wq::launch_q4_group(X, packed, scales, Y, M, K, N, G, as_stream(stream)));
+  return hip_status(wq::launch_q4_group(X, packed, scales, nullptr, Y, M, K, N, G, as_stream(stream)));
+}
+
+int wq_gemm_q4_group_zp(const void* X, const void* packed, const void* scales, const void* zeros,
+                        void* Y, int M, int K, int N, int G, void* stream) {
+  if (!X || !packed || !scales || !zeros || !Y) return WQ_ERR_NULL;
+  if (int st = check_q4(K, N, G)) return st;
+  if (M < 1) return WQ_ERR_SHAPE;
+  if ((long long)M * K * 2 > kMaxBytes) return WQ_ERR_SHAPE;
+  if (!aligned16(X) || !aligned16(packed) || !aligned16(scales) || !aligned16(zeros))
+    return WQ_ERR_ALIGN;
+  return hip_status(wq::launch_q4_group(X, packed, scales, zeros, Y, M, K, N, G, as_stream(stream)));
 }
 
 int wq_unpack_q4(const void* packed, const int32_t* perm, int8_t* codes, int K, int N, int G,

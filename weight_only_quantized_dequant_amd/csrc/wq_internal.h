@@ -53,8 +53,9 @@ hipError_t launch_q3_unpack(const void* packed, int8_t* codes, int K, int N, hip
 
 hipError_t launch_q4_prepack(const int32_t* qw, const int32_t* perm, void* packed, int K, int N,
                              int G, hipStream_t s);
-hipError_t launch_q4_group(const void* X, const void* packed, const void* scales, void* Y, int M,
-                           int K, int N, int G, hipStream_t s);
+// zeros: nullptr for the symmetric codes (offset 8), else fp16 [K/G, N].
+hipError_t launch_q4_group(const void* X, const void* packed, const void* scales,
+                           const void* zeros, void* Y, int M, int K, int N, int G, hipStream_t s);
 hipError_t launch_q4_unpack(const void* packed, const int32_t* perm, int8_t* codes, int K, int N,
                             int G, hipStream_t s);
 
