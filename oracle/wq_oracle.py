@@ -24,6 +24,9 @@ Sources (page title, then section):
     the result is stored in bf16;
   - "Int8 Weight Only Quantization": Y = X.(Wint*Sw) with float multiply and
     fp32 accumulation;
+  - "Smoothquant": Y = (X diag(s)^-1) . (diag(s) W): the activations are
+    divided by a per-input-channel factor s and the matching weight rows
+    multiplied by it, before both are quantised to int8;
   - "量化粒度" (granularity): x = S*(q - Z); per-channel scales for weights,
     per-token for activations, group-wise (group 128) for int4;
   - "Weight Store" / "Int4 Weight Only Quantization": int4 codes are packed
@@ -53,6 +56,9 @@ design notes):
   an all-zero row gets ``Sx = 0`` and all-zero codes.
 * The epilogue is ``bf16_rne(f32(f32(Sx * f32(acc)) * Sw))``: two separately
   rounded fp32 multiplies, left to right, then round-to-nearest-even to bf16.
+* SmoothQuant's ``X diag(s)^-1`` is one IEEE fp32 division per element,
+  ``X[m, k] / s[k]``, before the per-row quantiser; ``diag(s) W`` is folded
+  into the weight offline (fp32 multiply) before it is quantised.
 """
 from __future__ import annotations
 
@@ -63,7 +69,8 @@ __all__ = [
     "dequant_q4_group", "dequant_q4_zp", "matvec_q3", "gemm_q8_group", "gemm_q4_group",
     "gemm_q4_zp",
     "quantize_rows_int8", "w8a8_accumulate", "w8a8_epilogue",
-    "bf16_rne_bits", "bf16_bits_to_f32", "gemm_w8a8",
+    "bf16_rne_bits", "bf16_bits_to_f32", "gemm_w8a8", "smooth_activations",
+    "smooth_weight", "gemm_w8a8_smooth",
 ]
 
 
@@ -262,3 +269,23 @@ def gemm_w8a8(X: np.ndarray, Wq: np.ndarray, Sw: np.ndarray) -> dict:
     y_exact = (Sx.astype(np.float64)[:, None] * acc.astype(np.float64)
                * np.asarray(Sw, np.float64)[None, :])
     return {"Xq": Xq, "Sx": Sx, "acc": acc, "y_bits": y_bits, "y_exact": y_exact}
+
+
+# --------------------------------------------------------------------------
+# SmoothQuant folding around the W8A8 step
+# --------------------------------------------------------------------------
+
+def smooth_activations(X: np.ndarray, smooth: np.ndarray) -> np.ndarray:
+    """``X . diag(s)^-1`` in fp32: ``X[m, k] / s[k]``, one IEEE division each."""
+    X = np.atleast_2d(np.asarray(X, dtype=np.float32))
+    return (X / np.asarray(smooth, dtype=np.float32)[None, :]).astype(np.float32)
+
+
+def smooth_weight(W: np.ndarray, smooth: np.ndarray) -> np.ndarray:
+    """``diag(s) . W`` in fp32 for W indexed ``[K, N]`` (done once, offline)."""
+    return (np.asarray(smooth, np.float32)[:, None] * np.asarray(W, np.float32)).astype(np.float32)
+
+
+def gemm_w8a8_smooth(X: np.ndarray, smooth: np.ndarray, Wq: np.ndarray, Sw: np.ndarray) -> dict:
+    """The W8A8 step on ``X . diag(s)^-1``; ``Wq, Sw`` quantise ``diag(s) . W``."""
+    return gemm_w8a8(smooth_activations(X, smooth), Wq, Sw)

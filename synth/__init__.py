@@ -28,7 +28,7 @@ import numpy as np
 
 __all__ = [
     "pack_q3", "pack_q4", "gen_q3", "gen_q8_group", "gen_q4_group",
-    "gen_w8a8", "gen_q4_zp", "SEEDS",
+    "gen_w8a8", "gen_q4_zp", "gen_w8a8_smooth", "SEEDS",
 ]
 
 # Seeds of the named workloads (the tests and the benchmark use these).
@@ -42,6 +42,7 @@ SEEDS = {
     "q4_group_actorder": 1300,   # weights; activations use 1300 + M
     "q4_zp": 1600,               # asymmetric 4-bit; activations use 1600 + M
     "w8a8_256x8192x8192": 1400,
+    "w8a8_smooth": 1700,
 }
 
 
@@ -228,3 +229,33 @@ def gen_w8a8(M: int, K: int, N: int, seed: int) -> dict:
     Wq = _quantise(W, Sw[None, :], -127, 127).astype(np.int8)
     Wq = np.ascontiguousarray(Wq.T)                                # [N, K]
     return {"X": X, "Wq": Wq, "Sw": Sw, "M": M, "K": K, "N": N}
+
+
+def gen_w8a8_smooth(M: int, K: int, N: int, seed: int, n_outlier: int = 8,
+                    outlier_scale: float = 20.0, alpha: float = 0.5) -> dict:
+    """W8A8 inputs with outlier activation channels, and a SmoothQuant factor.
+
+    Draw order: X ~ N(0,1) fp32 [M,K]; ``n_outlier`` distinct channels
+    (``rng.choice``) of X multiplied by ``outlier_scale`` (activation outliers
+    sit in a few fixed channels); W ~ N(0, 0.02) fp32 [K,N].  The factor is
+    ``s[k] = max|X[:, k]|**alpha / max|W[k, :]|**(1 - alpha)`` in fp32
+    (the usual migration-strength choice; alpha = 0.5).  The weight is folded
+    and quantised offline: ``Ws = s[:, None] * W``, ``Sw = colabsmax(Ws)/127``,
+    ``Wq = clip(rint(Ws/Sw), -127, 127)`` stored ``[N, K]``.  ``Wq0, Sw0`` are
+    the same quantisation of W itself (no smoothing), for comparison.
+    """
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((M, K)).astype(np.float32)
+    cols = rng.choice(K, size=n_outlier, replace=False)
+    X[:, cols] *= np.float32(outlier_scale)
+    W = rng.normal(0.0, 0.02, size=(K, N)).astype(np.float32)
+    ax = np.max(np.abs(X), axis=0).astype(np.float32)
+    aw = np.max(np.abs(W), axis=1).astype(np.float32)
+    smooth = (ax ** np.float32(alpha) / aw ** np.float32(1.0 - alpha)).astype(np.float32)
+    Ws = (smooth[:, None] * W).astype(np.float32)
+    Sw = _absmax_scale(Ws, axis=0, qmax=127.0)
+    Wq = np.ascontiguousarray(_quantise(Ws, Sw[None, :], -127, 127).astype(np.int8).T)
+    Sw0 = _absmax_scale(W, axis=0, qmax=127.0)
+    Wq0 = np.ascontiguousarray(_quantise(W, Sw0[None, :], -127, 127).astype(np.int8).T)
+    return {"X": X, "W": W, "smooth": smooth, "Wq": Wq, "Sw": Sw, "Wq0": Wq0, "Sw0": Sw0,
+            "outlier_cols": cols, "M": M, "K": K, "N": N}

@@ -363,3 +363,48 @@ def test_q4_zp_generator_roundtrip_bound():
     W = oracle.dequant_q4_zp(oracle.unpack_u4(d["qweight"]), d["scales"], d["zeros"], None, 64)
     s = d["scales"].astype(np.float64)[np.arange(512) // 64]
     assert np.all(np.abs(W - d["W"]) <= s * (0.5 + 1e-3) + 1e-12)
+
+
+# ------------------------------------------------------------ SmoothQuant --
+
+def test_smooth_ones_is_plain_w8a8():
+    d = synth.gen_w8a8(5, 256, 32, seed=71)
+    a = oracle.gemm_w8a8_smooth(d["X"], np.ones(256, np.float32), d["Wq"], d["Sw"])
+    b = oracle.gemm_w8a8(d["X"], d["Wq"], d["Sw"])
+    for key in ("Xq", "Sx", "acc", "y_bits"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_smooth_identity_exact_case():
+    # (X diag(s)^-1)(diag(s) W) = X W.  Built so that every step is exact:
+    # s = powers of two, X / s integers with row max 127 (Sx = 1), s W
+    # integers with column max 127 (Sw = 1); the result must be X . W.
+    rng = np.random.default_rng(72)
+    M, K, N = 4, 64, 16
+    s = (2.0 ** rng.integers(-3, 4, size=K)).astype(np.float32)
+    Xs = rng.integers(-127, 128, size=(M, K))
+    Xs[:, 0] = 127
+    Ws = rng.integers(-127, 128, size=(K, N))
+    Ws[1, :] = -127
+    X = (Xs * s[None, :]).astype(np.float32)
+    W = (Ws / s[:, None]).astype(np.float32)
+    folded = oracle.smooth_weight(W, s)
+    assert np.array_equal(folded, Ws.astype(np.float32))
+    Wq = np.ascontiguousarray(Ws.T.astype(np.int8))
+    r = oracle.gemm_w8a8_smooth(X, s, Wq, np.ones(N, np.float32))
+    assert np.array_equal(r["Sx"], np.ones(M, np.float32))
+    assert np.array_equal(r["Xq"], Xs.astype(np.int8))
+    assert np.array_equal(r["y_exact"], X.astype(np.float64) @ W.astype(np.float64))
+
+
+def test_smooth_reduces_error_with_outlier_channels():
+    # Few activation channels 20x larger: per-token int8 quantisation of X
+    # crushes the other channels; dividing them out (and folding s into W)
+    # brings the product much closer to X . W.
+    d = synth.gen_w8a8_smooth(32, 1024, 64, seed=synth.SEEDS["w8a8_smooth"])
+    ref = d["X"].astype(np.float64) @ d["W"].astype(np.float64)
+    plain = oracle.gemm_w8a8(d["X"], d["Wq0"], d["Sw0"])["y_exact"]
+    smooth = oracle.gemm_w8a8_smooth(d["X"], d["smooth"], d["Wq"], d["Sw"])["y_exact"]
+    e_plain = np.linalg.norm(plain - ref) / np.linalg.norm(ref)
+    e_smooth = np.linalg.norm(smooth - ref) / np.linalg.norm(ref)
+    assert e_smooth < 0.5 * e_plain, (e_plain, e_smooth)
