@@ -179,24 +179,31 @@ def wl_q4zp(wq, torch, dev, M, G=128):
     return w
 
 
-def wl_w8a8(wq, torch, dev):
+def wl_w8a8(wq, torch, dev, smooth=False):
     import synth
     M, K, N = 256, 8192, 8192
-    # quantiser: read X fp32, write Xq + Sx; GEMM: read Xq, Wq, Sx, Sw, write Y
+    # quantiser: read X fp32 (and s), write Xq + Sx; GEMM: read Xq, Wq, Sx, Sw, write Y
     nbytes = (M * K * 4 + M * K + M * 4) + (M * K + N * K + M * 4 + N * 4 + M * N * 2)
-    d = synth.gen_w8a8(M, K, N, seed=synth.SEEDS["w8a8_256x8192x8192"])
+    if smooth:
+        nbytes += K * 4
+        d = synth.gen_w8a8_smooth(M, K, N, seed=synth.SEEDS["w8a8_smooth"])
+    else:
+        d = synth.gen_w8a8(M, K, N, seed=synth.SEEDS["w8a8_256x8192x8192"])
 
     def make(R):
         base = [torch.from_numpy(a).to(dev) for a in (d["X"], d["Wq"], d["Sw"])]
+        extra = [torch.from_numpy(d["smooth"]).to(dev)] if smooth else []
         return [[t.clone() for t in base] + [torch.empty((M, N), dtype=torch.bfloat16, device=dev),
                                              torch.empty((M, K), dtype=torch.int8, device=dev),
                                              torch.empty(M, dtype=torch.float32, device=dev)]
+                + [t.clone() for t in extra]
                 for _ in range(R)]
 
     def run(c):
-        wq.gemm_w8a8(c[0], c[1], c[2], Y=c[3], Xq=c[4], Sx=c[5])
+        wq.gemm_w8a8(c[0], c[1], c[2], Y=c[3], Xq=c[4], Sx=c[5], smooth=c[6] if smooth else None)
 
-    w = Workload(f"w8a8_dynamic M={M} K={K} N={N}", nbytes, make, run, flops=2 * M * K * N)
+    kind = "w8a8_smoothquant" if smooth else "w8a8_dynamic"
+    w = Workload(f"{kind} M={M} K={K} N={N}", nbytes, make, run, flops=2 * M * K * N)
     w.peak_tops = INT8_PEAK_TOPS
     w.oracle = lambda: __import__("oracle").gemm_w8a8(d["X"], d["Wq"], d["Sw"])
     return w
@@ -280,7 +287,7 @@ def main():
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="q8",
-                    help="q8 (headline) | q8_m* | q3_* | q4_m* | q4zp_m* | q4zp_g64_m* | w8a8 (single line)")
+                    help="q8 (headline) | q8_m* | q3_* | q4_m* | q4zp_m* | q4zp_g64_m* | w8a8 | w8a8_smooth (single line)")
     ap.add_argument("--eager", action="store_true",
                     help="launch every timed step from Python instead of replaying a captured graph")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -324,6 +331,8 @@ def main():
             return wl_q4zp(wq, torch, dev, int(name[len("q4zp_m"):]))
         if name == "w8a8":
             return wl_w8a8(wq, torch, dev)
+        if name == "w8a8_smooth":
+            return wl_w8a8(wq, torch, dev, smooth=True)
         raise SystemExit(f"unknown workload {name}")
 
     w = make(args.workload)
@@ -346,9 +355,10 @@ def main():
     if not args.headline_only:
         sec = {}
         for name in ("q3_f32_1024", "q3_f16_4096x4096", "q3_f16_4096x11008", "q3_f16_11008x4096",
-                     "q4_m1", "q4_m2", "q4_m4", "q4_m8", "q4zp_m1", "q4zp_g64_m1", "q8_m512", "w8a8"):
+                     "q4_m1", "q4_m2", "q4_m4", "q4_m8", "q4zp_m1", "q4zp_g64_m1", "q8_m512", "w8a8", "w8a8_smooth"):
             sw = make(name)
-            sms, sR = time_workload(torch, sw, 300 if name != "w8a8" else 100, 30 if name != "w8a8" else 10)
+            big = name.startswith("w8a8")
+            sms, sR = time_workload(torch, sw, 100 if big else 300, 10 if big else 30)
             e = {"us_per_call": round(sms * 1e3, 3), "GB_per_s": round(sw.nbytes / (sms * 1e-3) / 1e9, 1),
                  "pct_hbm_peak": round(100 * sw.nbytes / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                  "rotation_copies": sR, "algorithmic_bytes": sw.nbytes}

@@ -195,6 +195,18 @@ int wq_gemm_q4_group_zp(const void* X, const void* packed, const void* scales, c
 int wq_gemm_w8a8(const float* X, const int8_t* Wq, const float* Sw, void* Y, int8_t* Xq,
                  float* Sx, int32_t* acc_out, int M, int K, int N, void* stream);
 
+/* SmoothQuant around the same W8A8 step:  Y = (X diag(s)^-1) . (diag(s) W).
+ * The activation side runs here: the row quantiser works on X[m, k] / s[k]
+ * (one IEEE fp32 division per element) and writes Xq and Sx of that matrix;
+ * everything else is wq_gemm_w8a8.  The weight side is folded offline: Wq and
+ * Sw must quantise diag(s) W (rows of W indexed by k scaled by s[k]).
+ * ("Quantization CUDA", tom-jerr.github.io, section "Smoothquant".)
+ * smooth [K] fp32, s[k] > 0, 16-byte aligned; other arguments and rules as
+ * wq_gemm_w8a8. */
+int wq_gemm_w8a8_smooth(const float* X, const float* smooth, const int8_t* Wq, const float* Sw,
+                        void* Y, int8_t* Xq, float* Sx, int32_t* acc_out, int M, int K, int N,
+                        void* stream);
+
 /* ------------------------------------------------------ bit-exact checks -- */
 
 /* Write the signed codes a packed weight holds as int8 [K, N], through the

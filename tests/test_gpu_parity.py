@@ -397,3 +397,32 @@ def test_w8a8_ties_and_zero_row(wq):
     assert y[0, :4].tolist() == [256.0, 260.0, 512.0, 520.0]
     assert Xq.cpu().numpy()[1, :4].tolist() == [127, 2, -4, 0]
     assert Sx.cpu().numpy()[2] == 0 and np.all(Xq.cpu().numpy()[2] == 0) and np.all(y[2] == 0)
+
+
+# ----------------------------------------------------- SmoothQuant (W8A8) --
+
+@pytest.mark.parametrize("M,K,N", [(32, 1024, 64), (130, 256, 528), (7, 12288, 96),
+                                   (256, 8192, 8192)])
+def test_w8a8_smooth_bit_exact(wq, M, K, N):
+    # Outlier activation channels; the quantiser divides X by s, the GEMM is
+    # the plain W8A8 one on diag(s) W.  Codes, scales, accumulators and bf16
+    # output bits all equal the oracle's.  K = 12288 takes the quantiser's
+    # two-pass path (rows longer than one register block).
+    d = synth.gen_w8a8_smooth(M, K, N, seed=synth.SEEDS["w8a8_smooth"] + M + K + N)
+    Y, Xq, Sx, acc = wq.gemm_w8a8(cu(d["X"]), cu(d["Wq"]), cu(d["Sw"]), want_acc=True,
+                                  smooth=cu(d["smooth"]))
+    torch.cuda.synchronize()
+    r = oracle.gemm_w8a8_smooth(d["X"], d["smooth"], d["Wq"], d["Sw"])
+    assert np.array_equal(Xq.cpu().numpy(), r["Xq"])
+    assert np.array_equal(Sx.cpu().numpy().view(np.uint32), r["Sx"].view(np.uint32))
+    assert np.array_equal(acc.cpu().numpy(), r["acc"])
+    assert np.array_equal(Y.view(torch.int16).cpu().numpy().view(np.uint16), r["y_bits"])
+
+
+def test_w8a8_smooth_ones_equals_plain(wq):
+    d = synth.gen_w8a8(64, 640, 64, seed=73)
+    X, Wq, Sw = cu(d["X"]), cu(d["Wq"]), cu(d["Sw"])
+    a = wq.gemm_w8a8(X, Wq, Sw, want_acc=True, smooth=torch.ones(640, dtype=torch.float32, device=dev()))
+    b = wq.gemm_w8a8(X, Wq, Sw, want_acc=True)
+    for t1, t2 in zip(a, b):
+        assert torch.equal(t1, t2)

@@ -44,6 +44,7 @@ _SIGNATURES = {
     "wq_gemm_q4_group": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "wq_gemm_q4_group_zp": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "wq_gemm_w8a8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
+    "wq_gemm_w8a8_smooth": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
     "wq_unpack_q3": (_i, [_vp, _vp, _i, _i, _vp]),
     "wq_unpack_q8": (_i, [_vp, _vp, _i, _i, _vp]),
     "wq_unpack_q4": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
@@ -311,8 +312,13 @@ def unpack_q4(packed, K: int, N: int, group_size: int = 128, perm=None):
 
 # ------------------------------------------------------------------ W8A8 --
 
-def gemm_w8a8(X, Wq, Sw, want_acc=False, Y=None, Xq=None, Sx=None, acc=None):
-    """Dynamic W8A8: returns ``(Y bf16 [M,N], Xq int8 [M,K], Sx fp32 [M], acc int32 | None)``."""
+def gemm_w8a8(X, Wq, Sw, want_acc=False, Y=None, Xq=None, Sx=None, acc=None, smooth=None):
+    """Dynamic W8A8: returns ``(Y bf16 [M,N], Xq int8 [M,K], Sx fp32 [M], acc int32 | None)``.
+
+    With ``smooth`` (fp32 [K]) the SmoothQuant entry point runs instead: X is
+    divided by it per input channel before quantisation, and Wq, Sw must
+    quantise ``diag(smooth) . W``.
+    """
     M, K = X.shape
     N = Wq.shape[0]
     dev = X.device
@@ -329,6 +335,12 @@ def gemm_w8a8(X, Wq, Sw, want_acc=False, Y=None, Xq=None, Sx=None, acc=None):
     _need(Sx, "Sx", torch.float32, (M,), dev)
     if acc is not None:
         _need(acc, "acc", torch.int32, (M, N), dev)
+    if smooth is not None:
+        _need(smooth, "smooth", torch.float32, (K,), dev)
+        st = lib().wq_gemm_w8a8_smooth(_ptr(X), _ptr(smooth), _ptr(Wq), _ptr(Sw), _ptr(Y), _ptr(Xq),
+                                       _ptr(Sx), _ptr(acc), M, K, N, _stream(dev))
+        _check("wq_gemm_w8a8_smooth", st)
+        return Y, Xq, Sx, acc
     st = lib().wq_gemm_w8a8(_ptr(X), _ptr(Wq), _ptr(Sw), _ptr(Y), _ptr(Xq), _ptr(Sx), _ptr(acc),
                             M, K, N, _stream(dev))
     _check("wq_gemm_w8a8", st)

@@ -207,7 +207,22 @@ int wq_gemm_w8a8(const float* X, const int8_t* Wq, const float* Sw, void* Y, int
   if (!aligned16(X) || !aligned16(Wq) || !aligned16(Xq) || !aligned16(Sw) || !aligned16(Y) ||
       !aligned16(acc_out))
     return WQ_ERR_ALIGN;
-  return hip_status(wq::launch_w8a8(X, Wq, Sw, Y, Xq, Sx, acc_out, M, K, N, as_stream(stream)));
+  return hip_status(wq::launch_w8a8(X, nullptr, Wq, Sw, Y, Xq, Sx, acc_out, M, K, N, as_stream(stream)));
+}
+
+int wq_gemm_w8a8_smooth(const float* X, const float* smooth, const int8_t* Wq, const float* Sw,
+                        void* Y, int8_t* Xq, float* Sx, int32_t* acc_out, int M, int K, int N,
+                        void* stream) {
+  if (!smooth) return WQ_ERR_NULL;
+  if (!aligned16(smooth)) return WQ_ERR_ALIGN;
+  if (!X || !Wq || !Sw || !Y || !Xq || !Sx) return WQ_ERR_NULL;
+  if (M < 1 || K < 64 || N < 16 || K % 64 || N % 16) return WQ_ERR_SHAPE;
+  if ((long long)K * 127 * 127 >= (1LL << 31)) return WQ_ERR_SHAPE;
+  if ((long long)M * K > kMaxBytes || (long long)N * K > kMaxBytes) return WQ_ERR_SHAPE;
+  if (!aligned16(X) || !aligned16(Wq) || !aligned16(Xq) || !aligned16(Sw) || !aligned16(Y) ||
+      !aligned16(acc_out))
+    return WQ_ERR_ALIGN;
+  return hip_status(wq::launch_w8a8(X, smooth, Wq, Sw, Y, Xq, Sx, acc_out, M, K, N, as_stream(stream)));
 }
 
 // ------------------------------------------------------------------- misc --

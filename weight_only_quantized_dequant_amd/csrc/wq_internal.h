@@ -59,7 +59,9 @@ hipError_t launch_q4_group(const void* X, const void* packed, const void* scales
 hipError_t launch_q4_unpack(const void* packed, const int32_t* perm, int8_t* codes, int K, int N,
                             int G, hipStream_t s);
 
-hipError_t launch_w8a8(const float* X, const int8_t* Wq, const float* Sw, void* Y, int8_t* Xq,
-                       float* Sx, int32_t* acc_out, int M, int K, int N, hipStream_t s);
+// smooth: nullptr, or the SmoothQuant factor s [K] (X is divided by it).
+hipError_t launch_w8a8(const float* X, const float* smooth, const int8_t* Wq, const float* Sw,
+                       void* Y, int8_t* Xq, float* Sx, int32_t* acc_out, int M, int K, int N,
+                       hipStream_t s);
 
 }  // namespace wq
