@@ -24,6 +24,11 @@ Sources (page title, then section):
     the result is stored in bf16;
   - "Int8 Weight Only Quantization": Y = X.(Wint*Sw) with float multiply and
     fp32 accumulation;
+  - "LLM.int8()": mixed-precision decomposition: columns of the activation
+    matrix holding a value beyond a magnitude threshold (e.g. 6.0) and the
+    matching weight rows are taken out and multiplied in 16-bit floating
+    point; the rest is quantised to int8 (activations per token, weights per
+    output channel) and multiplied in int8; the two results are added;
   - "Smoothquant": Y = (X diag(s)^-1) . (diag(s) W): the activations are
     divided by a per-input-channel factor s and the matching weight rows
     multiplied by it, before both are quantised to int8;
@@ -56,6 +61,16 @@ design notes):
   an all-zero row gets ``Sx = 0`` and all-zero codes.
 * The epilogue is ``bf16_rne(f32(f32(Sx * f32(acc)) * Sw))``: two separately
   rounded fp32 multiplies, left to right, then round-to-nearest-even to bf16.
+* LLM.int8(): X is fp16; a column k is an outlier column when
+  ``max_m |X[m, k]| > threshold``; the weight is stored only as per-channel
+  int8 (``Wq [N, K]``, ``Sw [N]``), so the 16-bit side multiplies the fp16
+  outlier columns of X with the int8 rows of those columns and scales by Sw
+  (the dequantised rows, without a separate fp16 copy of the weight).  Both
+  parts are summed in fp32 and rounded once:
+  ``y = fp16_rne(f32(f32(f32(Sx * f32(acc)) + o) * Sw))`` with
+  ``o = sum_j f32(X[m, k_j]) * Wq[n, k_j]`` added in ascending k_j (each
+  product is exact in fp32).  The int8 side quantises the rows of X with the
+  outlier columns set to zero.
 * SmoothQuant's ``X diag(s)^-1`` is one IEEE fp32 division per element,
   ``X[m, k] / s[k]``, before the per-row quantiser; ``diag(s) W`` is folded
   into the weight offline (fp32 multiply) before it is quantised.
@@ -70,7 +85,7 @@ __all__ = [
     "gemm_q4_zp",
     "quantize_rows_int8", "w8a8_accumulate", "w8a8_epilogue",
     "bf16_rne_bits", "bf16_bits_to_f32", "gemm_w8a8", "smooth_activations",
-    "smooth_weight", "gemm_w8a8_smooth",
+    "smooth_weight", "gemm_w8a8_smooth", "fp16_rne", "int8_mixed_decompose",
 ]
 
 
@@ -289,3 +304,42 @@ def smooth_weight(W: np.ndarray, smooth: np.ndarray) -> np.ndarray:
 def gemm_w8a8_smooth(X: np.ndarray, smooth: np.ndarray, Wq: np.ndarray, Sw: np.ndarray) -> dict:
     """The W8A8 step on ``X . diag(s)^-1``; ``Wq, Sw`` quantise ``diag(s) . W``."""
     return gemm_w8a8(smooth_activations(X, smooth), Wq, Sw)
+
+
+# --------------------------------------------------------------------------
+# LLM.int8() mixed-precision decomposition
+# --------------------------------------------------------------------------
+
+def fp16_rne(a: np.ndarray) -> np.ndarray:
+    """fp32 -> fp16, round to nearest even (numpy's conversion)."""
+    return np.asarray(a, dtype=np.float32).astype(np.float16)
+
+
+def int8_mixed_decompose(X: np.ndarray, Wq: np.ndarray, Sw: np.ndarray, threshold: float) -> dict:
+    """LLM.int8()-style product of fp16 X [M, K] with the per-channel int8 weight.
+
+    Returns the column maxima ``colmax`` (fp32), the outlier columns ``cols``
+    (ascending), the int8 side's ``Xq, Sx, acc``, the fp32 outlier sums ``o``,
+    the fp16 output ``y16`` and the unrounded fp64 ``y_exact``.
+    """
+    X = np.atleast_2d(np.asarray(X, dtype=np.float16)).astype(np.float32)
+    Wq = np.asarray(Wq, dtype=np.int8)
+    Sw = np.asarray(Sw, dtype=np.float32)
+    colmax = np.max(np.abs(X), axis=0).astype(np.float32)
+    cols = np.nonzero(colmax > np.float32(threshold))[0]
+    Xr = X.copy()
+    Xr[:, cols] = 0
+    Xq, Sx = quantize_rows_int8(Xr)
+    acc = w8a8_accumulate(Xq, Wq)
+    M, N = X.shape[0], Wq.shape[0]
+    o = np.zeros((M, N), dtype=np.float32)
+    for k in cols:                                    # ascending, one fp32 add each
+        o = (o + (X[:, k:k + 1] * Wq[:, k].astype(np.float32)[None, :]).astype(np.float32)).astype(np.float32)
+    t = (Sx[:, None] * acc.astype(np.float32)).astype(np.float32)
+    u = (t + o).astype(np.float32)
+    y = (u * Sw[None, :]).astype(np.float32)
+    y_exact = Sw.astype(np.float64)[None, :] * (
+        Sx.astype(np.float64)[:, None] * acc.astype(np.float64)
+        + X[:, cols].astype(np.float64) @ Wq[:, cols].astype(np.float64).T)
+    return {"colmax": colmax, "cols": cols.astype(np.int32), "Xq": Xq, "Sx": Sx, "acc": acc,
+            "o": o, "y16": fp16_rne(y), "y_exact": y_exact}

@@ -28,7 +28,7 @@ import numpy as np
 
 __all__ = [
     "pack_q3", "pack_q4", "gen_q3", "gen_q8_group", "gen_q4_group",
-    "gen_w8a8", "gen_q4_zp", "gen_w8a8_smooth", "SEEDS",
+    "gen_w8a8", "gen_q4_zp", "gen_w8a8_smooth", "gen_int8_mixed", "SEEDS",
 ]
 
 # Seeds of the named workloads (the tests and the benchmark use these).
@@ -43,6 +43,7 @@ SEEDS = {
     "q4_zp": 1600,               # asymmetric 4-bit; activations use 1600 + M
     "w8a8_256x8192x8192": 1400,
     "w8a8_smooth": 1700,
+    "int8_mixed": 1800,
 }
 
 
@@ -259,3 +260,25 @@ def gen_w8a8_smooth(M: int, K: int, N: int, seed: int, n_outlier: int = 8,
     Wq0 = np.ascontiguousarray(_quantise(W, Sw0[None, :], -127, 127).astype(np.int8).T)
     return {"X": X, "W": W, "smooth": smooth, "Wq": Wq, "Sw": Sw, "Wq0": Wq0, "Sw0": Sw0,
             "outlier_cols": cols, "M": M, "K": K, "N": N}
+
+
+def gen_int8_mixed(M: int, K: int, N: int, seed: int, n_outlier: int = 8,
+                   outlier_scale: float = 20.0) -> dict:
+    """LLM.int8()-style inputs: fp16 activations with a few outlier channels.
+
+    Draw order: X ~ N(0,1) [M,K]; ``n_outlier`` distinct channels
+    (``rng.choice``) multiplied by ``outlier_scale`` (most of their values
+    then exceed 6); X rounded to fp16.  W ~ N(0, 0.02) fp32 [K,N], quantised
+    offline per output channel: ``Sw = colabsmax/127``,
+    ``Wq = clip(rint(W/Sw), -127, 127)`` stored ``[N, K]``.
+    """
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((M, K)).astype(np.float32)
+    cols = np.sort(rng.choice(K, size=n_outlier, replace=False))
+    X[:, cols] *= np.float32(outlier_scale)
+    X = X.astype(np.float16)
+    W = rng.normal(0.0, 0.02, size=(K, N)).astype(np.float32)
+    Sw = _absmax_scale(W, axis=0, qmax=127.0)
+    Wq = np.ascontiguousarray(_quantise(W, Sw[None, :], -127, 127).astype(np.int8).T)
+    return {"X": X, "W": W, "Wq": Wq, "Sw": Sw, "outlier_cols": cols.astype(np.int32),
+            "M": M, "K": K, "N": N}

@@ -408,3 +408,61 @@ def test_smooth_reduces_error_with_outlier_channels():
     e_plain = np.linalg.norm(plain - ref) / np.linalg.norm(ref)
     e_smooth = np.linalg.norm(smooth - ref) / np.linalg.norm(ref)
     assert e_smooth < 0.5 * e_plain, (e_plain, e_smooth)
+
+
+# -------------------------------------------------------------- LLM.int8() --
+
+def test_mixed_no_outliers_is_plain_w8a8():
+    # Above every value: no column is taken out, the int8 side is W8A8.
+    d = synth.gen_w8a8(6, 256, 32, seed=81)
+    X16 = d["X"].astype(np.float16)
+    r = oracle.int8_mixed_decompose(X16, d["Wq"], d["Sw"], threshold=1e30)
+    p = oracle.gemm_w8a8(X16.astype(np.float32), d["Wq"], d["Sw"])
+    assert r["cols"].size == 0
+    for key in ("Xq", "Sx", "acc"):
+        assert np.array_equal(r[key], p[key]), key
+    assert np.array_equal(r["y_exact"], p["y_exact"])
+
+
+def test_mixed_all_outliers_is_the_16bit_product():
+    # Below every magnitude: every column is 16-bit, the int8 side is empty
+    # and y is X . (Wq * Sw) exactly (integer-valued case, exact in fp32).
+    rng = np.random.default_rng(82)
+    M, K, N = 3, 64, 16
+    X = rng.integers(-4, 5, size=(M, K)).astype(np.float16)
+    X[:, 0] = 1                                       # no all-zero column
+    Wq = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    Sw = np.full(N, 0.5, np.float32)
+    r = oracle.int8_mixed_decompose(X, Wq, Sw, threshold=-1.0)
+    assert r["cols"].size == K and np.all(r["Xq"] == 0) and np.all(r["Sx"] == 0)
+    ref = X.astype(np.float64) @ (Wq.astype(np.float64) * 0.5).T
+    assert np.array_equal(r["y_exact"], ref)
+    assert np.array_equal(r["y16"].astype(np.float64), ref.astype(np.float16).astype(np.float64))
+
+
+def test_mixed_worked_example():
+    # One row, K = 4, threshold 6: only column 2 (value 8) exceeds it.
+    #   regular part x = [127/32, 1/32, 0, 2/32]: absmax 127/32, so
+    #   Sx = 1/32 and Xq = [127, 1, 0, 2];
+    #   n = 0, w = [1, 2, 3, 4]: acc = 127 + 2 + 8 = 137, o = 8 * 3 = 24,
+    #          y = (137/32 + 24) * 0.25 = 28.28125 * 0.25 = 7.0703125;
+    #   n = 1, w = [0, 0, -1, 0]: acc = 0, o = -8, y = -8 * 2 = -16.
+    X = np.array([[127.0 / 32, 1.0 / 32, 8.0, 2.0 / 32]], np.float16)
+    Wq = np.array([[1, 2, 3, 4], [0, 0, -1, 0]], np.int8)
+    Sw = np.array([0.25, 2.0], np.float32)
+    r = oracle.int8_mixed_decompose(X, Wq, Sw, threshold=6.0)
+    assert r["cols"].tolist() == [2]
+    assert r["Xq"].tolist() == [[127, 1, 0, 2]] and r["Sx"].tolist() == [1.0 / 32]
+    assert r["acc"].tolist() == [[137, 0]] and r["o"].tolist() == [[24.0, -8.0]]
+    assert r["y16"].astype(np.float64).tolist() == [[7.0703125, -16.0]]
+
+
+def test_mixed_reduces_error_with_outlier_channels():
+    d = synth.gen_int8_mixed(32, 1024, 64, seed=synth.SEEDS["int8_mixed"])
+    ref = d["X"].astype(np.float64) @ d["W"].astype(np.float64)
+    plain = oracle.gemm_w8a8(d["X"].astype(np.float32), d["Wq"], d["Sw"])["y_exact"]
+    mixed = oracle.int8_mixed_decompose(d["X"], d["Wq"], d["Sw"], 6.0)
+    assert np.array_equal(mixed["cols"], d["outlier_cols"])
+    e_plain = np.linalg.norm(plain - ref) / np.linalg.norm(ref)
+    e_mixed = np.linalg.norm(mixed["y_exact"] - ref) / np.linalg.norm(ref)
+    assert e_mixed < 0.5 * e_plain, (e_plain, e_mixed)
