@@ -157,6 +157,28 @@ def wl_q4(wq, torch, dev, M):
     return w
 
 
+def wl_int8_mixed(wq, torch, dev):
+    import synth
+    M, K, N = 256, 8192, 8192
+    # column maxima: read X fp16, write colmax; quantiser: read X, colmax, write Xq, Sx;
+    # GEMM: read Xq, Wq, Sx, Sw, write Y fp16 (the outlier columns are a few KB)
+    nbytes = (2 * M * K + 4 * K) + (2 * M * K + 4 * K + M * K + 4 * M) + (M * K + N * K + 4 * M + 4 * N + 2 * M * N)
+    d = synth.gen_int8_mixed(M, K, N, seed=synth.SEEDS["int8_mixed"])
+
+    def make(R):
+        base = [torch.from_numpy(a).to(dev) for a in (d["X"], d["Wq"], d["Sw"])]
+        return [[t.clone() for t in base] + [torch.empty((M, N), dtype=torch.float16, device=dev)]
+                for _ in range(R)]
+
+    def run(c):
+        wq.gemm_int8_mixed(c[0], c[1], c[2], 6.0, Y=c[3])
+
+    w = Workload(f"int8_mixed_decomposition M={M} K={K} N={N} outlier_cols=8", nbytes, make, run,
+                 flops=2 * M * K * N)
+    w.peak_tops = INT8_PEAK_TOPS
+    return w
+
+
 def wl_q4zp(wq, torch, dev, M, G=128):
     import synth
     K, N = 4096, 11008
@@ -287,7 +309,7 @@ def main():
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="q8",
-                    help="q8 (headline) | q8_m* | q3_* | q4_m* | q4zp_m* | q4zp_g64_m* | w8a8 | w8a8_smooth (single line)")
+                    help="q8 (headline) | q8_m* | q3_* | q4_m* | q4zp_m* | q4zp_g64_m* | w8a8 | w8a8_smooth | int8_mixed (single line)")
     ap.add_argument("--eager", action="store_true",
                     help="launch every timed step from Python instead of replaying a captured graph")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -333,6 +355,8 @@ def main():
             return wl_w8a8(wq, torch, dev)
         if name == "w8a8_smooth":
             return wl_w8a8(wq, torch, dev, smooth=True)
+        if name == "int8_mixed":
+            return wl_int8_mixed(wq, torch, dev)
         raise SystemExit(f"unknown workload {name}")
 
     w = make(args.workload)
@@ -355,9 +379,9 @@ def main():
     if not args.headline_only:
         sec = {}
         for name in ("q3_f32_1024", "q3_f16_4096x4096", "q3_f16_4096x11008", "q3_f16_11008x4096",
-                     "q4_m1", "q4_m2", "q4_m4", "q4_m8", "q4zp_m1", "q4zp_g64_m1", "q8_m512", "w8a8", "w8a8_smooth"):
+                     "q4_m1", "q4_m2", "q4_m4", "q4_m8", "q4zp_m1", "q4zp_g64_m1", "q8_m512", "w8a8", "w8a8_smooth", "int8_mixed"):
             sw = make(name)
-            big = name.startswith("w8a8")
+            big = name.startswith("w8a8") or name == "int8_mixed"
             sms, sR = time_workload(torch, sw, 100 if big else 300, 10 if big else 30)
             e = {"us_per_call": round(sms * 1e3, 3), "GB_per_s": round(sw.nbytes / (sms * 1e-3) / 1e9, 1),
                  "pct_hbm_peak": round(100 * sw.nbytes / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),

@@ -207,6 +207,29 @@ int wq_gemm_w8a8_smooth(const float* X, const float* smooth, const int8_t* Wq, c
                         void* Y, int8_t* Xq, float* Sx, int32_t* acc_out, int M, int K, int N,
                         void* stream);
 
+/* LLM.int8()-style mixed-precision decomposition of Y = X . W:
+ *   colmax[k] = max_m |X[m, k]|;  column k is an outlier when colmax[k] > threshold;
+ *   the int8 side quantises each row of X with the outlier columns set to 0
+ *   (Xq, Sx as wq_gemm_w8a8) and forms acc = Xq . Wq^T (exact int32);
+ *   the 16-bit side sums o[m, n] = x[m, k] * Wq[n, k] over the outlier
+ *   columns in ascending k (fp32; each product exact);
+ *   Y[m, n] = fp16_rne( (Sx[m] * float(acc) + o) * Sw[n] ), each fp32
+ *   operation rounded on its own.
+ * ("Quantization CUDA", tom-jerr.github.io, section "LLM.int8()": outlier
+ * columns by a magnitude threshold such as 6.0, int8 vector-wise product of
+ * the rest, 16-bit product of the outlier columns, the two added.  The weight
+ * is kept only as per-channel int8: its outlier rows enter the 16-bit side
+ * as the codes times Sw.)
+ * X [M, K] fp16; Wq [N, K] int8; Sw [N] fp32; Y [M, N] fp16, written;
+ * Xq [M, K] int8, Sx [M] fp32, colmax [K] fp32, outlier_cols [K] int32 (the
+ * first *n_outlier entries, ascending) and n_outlier [1] int32: written;
+ * acc_out as wq_gemm_w8a8.  Three launches on `stream`.
+ * Rules: as wq_gemm_w8a8; threshold not NaN; X, Wq, Sw, Y, Xq, colmax and
+ * acc_out (when given) 16-byte aligned. */
+int wq_gemm_int8_mixed(const void* X, const int8_t* Wq, const float* Sw, float threshold, void* Y,
+                       int8_t* Xq, float* Sx, float* colmax, int32_t* outlier_cols,
+                       int32_t* n_outlier, int32_t* acc_out, int M, int K, int N, void* stream);
+
 /* ------------------------------------------------------ bit-exact checks -- */
 
 /* Write the signed codes a packed weight holds as int8 [K, N], through the

@@ -426,3 +426,46 @@ def test_w8a8_smooth_ones_equals_plain(wq):
     b = wq.gemm_w8a8(X, Wq, Sw, want_acc=True)
     for t1, t2 in zip(a, b):
         assert torch.equal(t1, t2)
+
+
+# ------------------------------------------------ LLM.int8() decomposition --
+
+def _mixed_check(wq, X16, Wq, Sw, threshold):
+    Y, Xq, Sx, colmax, cols, n_out, acc = wq.gemm_int8_mixed(cu(X16), cu(Wq), cu(Sw), threshold,
+                                                              want_acc=True)
+    torch.cuda.synchronize()
+    r = oracle.int8_mixed_decompose(X16, Wq, Sw, threshold)
+    assert np.array_equal(colmax.cpu().numpy().view(np.uint32), r["colmax"].view(np.uint32))
+    assert int(n_out.item()) == r["cols"].size
+    assert np.array_equal(cols.cpu().numpy()[:r["cols"].size], r["cols"])
+    assert np.array_equal(Xq.cpu().numpy(), r["Xq"])
+    assert np.array_equal(Sx.cpu().numpy().view(np.uint32), r["Sx"].view(np.uint32))
+    assert np.array_equal(acc.cpu().numpy(), r["acc"])
+    assert np.array_equal(Y.view(torch.int16).cpu().numpy().view(np.uint16), r["y16"].view(np.uint16))
+    return r
+
+
+@pytest.mark.parametrize("M,K,N,nout", [(32, 1024, 64, 8), (130, 256, 528, 3), (7, 2048, 96, 0),
+                                        (256, 8192, 8192, 8)])
+def test_int8_mixed_bit_exact(wq, M, K, N, nout):
+    # Outlier channels 20x (beyond 6.0); every output of the decomposition
+    # (column maxima, the outlier list, codes, scales, int32, fp16 bits)
+    # equals the oracle's.
+    d = synth.gen_int8_mixed(M, K, N, seed=synth.SEEDS["int8_mixed"] + M + K + N, n_outlier=nout)
+    r = _mixed_check(wq, d["X"], d["Wq"], d["Sw"], 6.0)
+    assert np.array_equal(r["cols"], d["outlier_cols"])
+
+
+def test_int8_mixed_thresholds_and_zero_rows(wq):
+    rng = np.random.default_rng(83)
+    M, K, N = 5, 128, 32
+    X = rng.standard_normal((M, K)).astype(np.float16)
+    X[:, 7] = 40.0                       # an outlier column
+    X[3, :] = 0
+    X[3, 7] = 9.0                        # row 3: only its outlier value is non-zero
+    Wq = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    Sw = rng.uniform(0.001, 0.01, size=N).astype(np.float32)
+    r = _mixed_check(wq, X, Wq, Sw, 6.0)
+    assert r["cols"].tolist() == [7] and r["Sx"][3] == 0
+    _mixed_check(wq, X, Wq, Sw, 1e30)    # nothing taken out
+    _mixed_check(wq, X, Wq, Sw, -1.0)    # every column taken out
