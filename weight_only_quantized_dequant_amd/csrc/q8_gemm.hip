@@ -9,22 +9,26 @@
 // and "技术实现细节": tiles of the int8 weight are dequantised on chip and never
 // written back as floating point, one fp32 scale per 128 rows of K per column).
 //
-// Tiles.  A workgroup owns a 64 x 128 tile of Y and walks K in stages of 64
-// rows.  Per stage, direct-to-LDS buffer loads bring the X tile (fp16,
-// 64 x 64), the int8 codes of the weight tile (64 rows x 128 columns, as the
-// 16-byte pieces of the packed layout: one row of one 16-column chunk) and
-// the stage's row of scales into a ring of kStages slots.  The codes of a
-// stage are converted once per workgroup into an fp16 tile [n][k] (exact
-// integers, via the fp16 magic number 1024 and one packed add), which the
-// eight waves read as v_mfma_f32_16x16x32_f16 operands.  Each wave keeps a
-// 32 x 32 accumulator for the current group and a running total; at the end
-// of a group the total takes accumulator * scale (fp32) and the accumulator
-// restarts, so the products are exact and every rounding is an fp32 one, as
-// in the small-batch kernel.
+// Tiles.  A workgroup (4 waves) owns a 32 x 128 tile of Y and walks K in
+// stages of 128 rows.  Per stage, direct-to-LDS buffer loads bring the X tile
+// (fp16, 32 x 128), the int8 codes of the weight tile (128 rows x 128
+// columns, as the 16-byte pieces of the packed layout: one row of one
+// 16-column chunk) and the scale rows of the stage's groups into a ring of
+// kStages slots (75 KB: two workgroups fit on a CU).  Each wave builds its
+// v_mfma_f32_16x16x32_f16 operands for a 16 x 64 sub-tile in registers,
+// straight from the int8 stage: one v_perm_b32 turns two code bytes into two
+// zero-exponent fp16s (the exact subnormals u 2^-24, u = q + 128), and one
+// more matrix-core product per k32 step against a constant operand of
+// 128 2^-24 gives the offset term.  Each wave keeps the current group's sums
+// and a running total; at the end of a group the total takes
+// (sums - offset term) * scale in fp32 and the next group starts from zero,
+// so the products are exact and every rounding is an fp32 one, as in the
+// small-batch kernel.  The result is scaled by 2^24 and rounded once to
+// fp16.
 //
-// X rows and stage rows are 128-byte rows of 8 16-byte chunks; chunk c of
-// row r sits at position c ^ ((r >> 1) & 7), which keeps the 16 rows of one
-// fragment read on distinct LDS banks.
+// X rows of a stage are 256 bytes, 16 chunks of 16; chunk c of row r sits at
+// position c ^ (r % 16), which keeps the 16 rows of one fragment read on
+// distinct LDS banks.
 #include "wq_device.hpp"
 #include "wq_internal.h"
 
@@ -35,13 +39,13 @@ namespace {
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
-constexpr int kBM = 64, kBN = 128, kBK = 128, kStages = 3, kThreadsG = 256;
+constexpr int kBM = 32, kBN = 128, kBK = 128, kStages = 3, kThreadsG = 256;
 constexpr int kRowA = kBK * 2;                   // 256 bytes: one fp16 row of X per stage
 constexpr int kStageA = kBM * kRowA;             // X tile, fp16 [m][k], 16 KB
 constexpr int kStageB = kBK * kBN;               // codes: 128 rows x 8 chunks of 16 bytes
 constexpr int kStageS = 1024;                    // two scale rows of 128 columns
 constexpr int kStage = kStageA + kStageB + kStageS;
-constexpr int kLoads = 8;                        // direct-to-LDS loads per stage per wave
+constexpr int kLoads = 6;                        // direct-to-LDS loads per stage per wave
 
 // X rows of a stage are 16 chunks of 16 bytes; chunk c of row r sits at
 // position c ^ (r % 16), so the 16 rows of one fragment read hit distinct
@@ -79,7 +83,7 @@ __device__ __forceinline__ void lds_barrier() {
 // matrix-core operand of block j, so block j, operand column t holds weight
 // column 16 (t / 4) + 4 (t % 4) + j; the transposed result then gives lane l
 // the 16 consecutive columns 16 (l / 16) + 4 r + j (r, j = 0..3) of one row.
-__global__ __launch_bounds__(kThreadsG) void q8_gemm_kernel(
+__global__ __launch_bounds__(kThreadsG, 2) void q8_gemm_kernel(
     const _Float16* __restrict__ X, const uint8_t* __restrict__ Wp,
     const float* __restrict__ scales, _Float16* __restrict__ Y, int M, int K, int N, int G, int u,
     int nta, int cpp, int packed_bytes, int mtiles, int ntiles) {
@@ -102,10 +106,10 @@ __global__ __launch_bounds__(kThreadsG) void q8_gemm_kernel(
 
   // X: load t of wave w fills stage rows 4 (4 w + t) .. + 3; lane l brings
   // row 4 (4 w + t) + l / 16, chunk position l % 16.
-  int a_off[4];
+  int a_off[2];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int row = 4 * (4 * wave + t) + (lane >> 4);
+  for (int t = 0; t < 2; ++t) {
+    const int row = 4 * (2 * wave + t) + (lane >> 4);
     a_off[t] = m0 + row < M ? (m0 + row) * K * 2 + 16 * swz(row, lane & 15) : -1;
   }
   // Codes: load t of wave w fills slots 64 (4 w + t) ..: i = 2 w + t / 2,
@@ -142,10 +146,10 @@ __global__ __launch_bounds__(kThreadsG) void q8_gemm_kernel(
     const int k0 = kt * kBK;
     lds_u8* base = (lds_u8*)smem + slot * kStage;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 2; ++t)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xr, (__attribute__((address_space(3))) void*)(base + 1024 * (4 * wave + t)), 16,
-          (a_off[t] >= 0 && k0 + 8 * swz(4 * (4 * wave + t) + (lane >> 4), lane & 15) < K)
+          xr, (__attribute__((address_space(3))) void*)(base + 1024 * (2 * wave + t)), 16,
+          (a_off[t] >= 0 && k0 + 8 * swz(4 * (2 * wave + t) + (lane >> 4), lane & 15) < K)
               ? a_off[t] + 2 * k0 : kOutOfRange,
           0, 0, 0);
 #pragma unroll
@@ -170,7 +174,7 @@ __global__ __launch_bounds__(kThreadsG) void q8_gemm_kernel(
     }
   };
 
-  const int wm = wave >> 1, wn = wave & 1;  // 2 x 2 waves, each 32 rows x 64 columns
+  const int wm = wave >> 1, wn = wave & 1;  // 2 x 2 waves, each 16 rows x 64 columns
   const int fr = lane & 15, fq = lane >> 4;
   const int fp = fr >> 2, fd = fr & 3;
   // Byte offset of this lane's code word in the stage for e = 0, k32 step h
@@ -178,12 +182,12 @@ __global__ __launch_bounds__(kThreadsG) void q8_gemm_kernel(
   // LDS byte offsets (within a stage) of this lane's fragment reads, per k32
   // step h: X rows wm 32 + 16 i + l % 16; the code word of row e = 0 (row e
   // adds 2048: 8 i + c grows by 8).
-  int a_lds[4][2], b_lds[4];
+  int a_lds[4][1], b_lds[4];
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = wm * 32 + 16 * i + fr;
+    for (int i = 0; i < 1; ++i) {
+      const int row = wm * 16 + 16 * i + fr;
       a_lds[h][i] = row * kRowA + 16 * swz(row, 4 * h + fq);
     }
     b_lds[h] = kStageA + (16 * (4 * wn + fp) + fq + 4 * (h ^ fp)) * 16 + 4 * fd;
@@ -193,9 +197,9 @@ __global__ __launch_bounds__(kThreadsG) void q8_gemm_kernel(
   // xacc: the same sums with every u = 128, i.e. 128 2^-24 sum(x), one
   // matrix-core product per row block against a constant operand; at the end
   // of a group tot += (acc - xacc) * scale, all in units of 2^-24.
-  f32x4 acc[2][4], tot[2][4], xacc[2];
+  f32x4 acc[1][4], tot[1][4], xacc[1];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 1; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) tot[i][j] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
   const h8 c128 = __builtin_bit_cast(h8, (u32x4){0x00800080u, 0x00800080u, 0x00800080u, 0x00800080u});
@@ -204,12 +208,12 @@ __global__ __launch_bounds__(kThreadsG) void q8_gemm_kernel(
   // the low byte of an fp16 whose other bits are zero (the subnormal u 2^-24),
   // two rows per register, one v_perm_b32 per register.
   struct Step {
-    h8 a[2];
+    h8 a[1];
     uint32_t D[8];
   };
   auto read_step = [&](const unsigned char* S, int h, Step& st) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) st.a[i] = *reinterpret_cast<const h8*>(S + a_lds[h][i]);
+    for (int i = 0; i < 1; ++i) st.a[i] = *reinterpret_cast<const h8*>(S + a_lds[h][i]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) st.D[e] = *reinterpret_cast<const uint32_t*>(S + b_lds[h] + 2048 * e);
   };
@@ -229,7 +233,7 @@ __global__ __launch_bounds__(kThreadsG) void q8_gemm_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) v[r] = *reinterpret_cast<const f32x4*>(sc + 16 * r);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 1; ++i) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -258,7 +262,7 @@ __global__ __launch_bounds__(kThreadsG) void q8_gemm_kernel(
       const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
       if ((h == 0 && start0) || (h == 2 && mid)) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < 1; ++i) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[h & 1][j], st[h & 1].a[i], zero, 0, 0, 0);
@@ -266,7 +270,7 @@ __global__ __launch_bounds__(kThreadsG) void q8_gemm_kernel(
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < 1; ++i) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[h & 1][j], st[h & 1].a[i], acc[i][j], 0, 0, 0);
@@ -302,8 +306,8 @@ __global__ __launch_bounds__(kThreadsG) void q8_gemm_kernel(
   }
 
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int m = m0 + wm * 32 + 16 * i + fr;
+  for (int i = 0; i < 1; ++i) {
+    const int m = m0 + wm * 16 + 16 * i + fr;
     const int n = n0 + wn * 64 + 16 * fq;
     if (m >= M || n >= N) continue;
     uint32_t w[8];
