@@ -20,6 +20,10 @@ Extra fields on the single JSON line:
   was taken on the current kernel source, else null.
 * cpu_baseline: the CPU oracle (numpy, fp64) timed on this host on the same
   workload, repeated for a bounded ~10 s.
+* calibration (headline only): an empty kernel with the GEMV's grid (the
+  dispatch floor) and a kernel that only streams each copy's packed weight
+  once with the GEMV's loads (the achievable time for those bytes here), on
+  the same rotation and graph replay.
 * secondary (unless --headline-only): the other workloads of the library,
   each as microseconds per call and GB/s (or TOPS) with the same method.
 """
@@ -279,6 +283,31 @@ def time_workload(torch, w, steps, warmup, R=None, eager=False):
     return ms, R
 
 
+def calibration(wq, torch, w, steps, warmup, gemv_ms):
+    """Dispatch floor and achievable streaming time for the headline workload.
+
+    Same rotation and graph replay as the GEMV: (a) an empty kernel with the
+    GEMV's grid (256 x 512 threads), (b) a kernel that only reads each copy's
+    packed weight once with the GEMV's loads.  The GEMV moves the same weight
+    plus 2.6% more bytes, so (b) is a lower bound for it on this GPU.
+    """
+    dev = torch.device("cuda:0")
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def run_stream(c):
+        wq.calib_stream_read(c[1], sink)
+
+    sw = Workload("stream read of the packed weight", w.nbytes, w.make, run_stream)
+    s_ms, R = time_workload(torch, sw, steps, warmup)
+    ew = Workload("empty kernel", 0, lambda R: [[None]], lambda c: wq.calib_empty(sink, 256, 512))
+    e_ms, _ = time_workload(torch, ew, steps, warmup, R=1)
+    wbytes = w.make(1)[0][1].numel()
+    return {"empty_kernel_us": round(e_ms * 1e3, 3), "stream_read_us": round(s_ms * 1e3, 3),
+            "stream_read_bytes": wbytes, "stream_read_GB_per_s": round(wbytes / (s_ms * 1e-3) / 1e9, 1),
+            "stream_read_pct_hbm_peak": round(100 * wbytes / (s_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+            "gemv_time_over_stream_time": round(s_ms / gemv_ms, 4), "rotation_copies": R}
+
+
 def cpu_baseline(w, budget_s=10.0):
     """Time the CPU oracle on the same workload, repeated for about budget_s."""
     try:
@@ -308,6 +337,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-calibration", action="store_true",
+                    help="skip the empty-kernel and bare-stream reference timings")
     ap.add_argument("--workload", default="q8",
                     help="q8 (headline) | q8_m* | q3_* | q4_m* | q4zp_m* | q4zp_g64_m* | w8a8 | w8a8_smooth | int8_mixed (single line)")
     ap.add_argument("--eager", action="store_true",
@@ -376,6 +407,8 @@ def main():
     out["roofline"] = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                        "algorithmic_bytes_per_launch": w.nbytes}
+    if args.workload == "q8" and not args.no_calibration:
+        out["calibration"] = calibration(wq, torch, w, args.steps, args.warmup, ms)
     if not args.headline_only:
         sec = {}
         for name in ("q3_f32_1024", "q3_f16_4096x4096", "q3_f16_4096x11008", "q3_f16_11008x4096",

@@ -242,6 +242,22 @@ int wq_unpack_q8(const void* packed, int8_t* codes, int K, int N, void* stream);
 int wq_unpack_q4(const void* packed, const int32_t* perm, int8_t* codes, int K, int N, int G,
                  void* stream);
 
+/* ---------------------------------------------------- measurement only -- */
+
+/* References for timing the streaming products; neither computes anything.
+ * wq_calib_empty: one launch of an empty kernel, grid x threads (1..1024),
+ *   that touches no memory: the dispatch floor of a launch.
+ * wq_calib_stream_read: one launch that reads bytes [0, bytes) of buf once
+ *   with the int8 GEMV's weight-stream loads (512-thread workgroups, eight
+ *   16-byte non-temporal buffer loads per thread, 64 KiB per workgroup) and
+ *   discards them: the achievable time for any kernel that reads those bytes.
+ *   buf: device, 16-byte aligned; bytes % 16 == 0, 16 <= bytes < 2^31.
+ *   sink: device uint32 [1]; written only if the xor of all words read
+ *   equals 0x9E3779B9 (its value carries no meaning).
+ * Errors: WQ_ERR_NULL, WQ_ERR_SHAPE, WQ_ERR_ALIGN, WQ_ERR_HIP as above. */
+int wq_calib_empty(int grid, int threads, uint32_t* sink, void* stream);
+int wq_calib_stream_read(const void* buf, long long bytes, uint32_t* sink, void* stream);
+
 /* Static text for a status code. */
 const char* wq_status_str(int status);
 

@@ -143,3 +143,16 @@ def test_act_order_perm_host():
         wq.q4_act_order_perm(bad, K, G)
     with pytest.raises(wq.WQError):
         wq.q4_act_order_perm(np.full(K, 9, np.int32), K, G)
+
+
+def test_calibration_validation(L):
+    assert L.wq_calib_empty(256, 512, None, None) == wq.WQ_ERR_NULL
+    assert L.wq_calib_empty(0, 512, P, None) == wq.WQ_ERR_SHAPE
+    assert L.wq_calib_empty(256, 2048, P, None) == wq.WQ_ERR_SHAPE
+    f = L.wq_calib_stream_read
+    assert f(None, 1 << 20, P, None) == wq.WQ_ERR_NULL
+    assert f(P, 1 << 20, None, None) == wq.WQ_ERR_NULL
+    assert f(P, 1000, P, None) == wq.WQ_ERR_SHAPE          # bytes % 16
+    assert f(P, 0, P, None) == wq.WQ_ERR_SHAPE
+    assert f(P, 1 << 31, P, None) == wq.WQ_ERR_SHAPE        # 32-bit buffer offsets
+    assert f(P_MIS, 1 << 20, P, None) == wq.WQ_ERR_ALIGN

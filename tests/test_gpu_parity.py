@@ -469,3 +469,23 @@ def test_int8_mixed_thresholds_and_zero_rows(wq):
     assert r["cols"].tolist() == [7] and r["Sx"][3] == 0
     _mixed_check(wq, X, Wq, Sw, 1e30)    # nothing taken out
     _mixed_check(wq, X, Wq, Sw, -1.0)    # every column taken out
+
+
+# ============================================================ measurement ==
+
+@pytest.mark.parametrize("nbytes,pos", [(1 << 24, 0), (1 << 24, (1 << 24) - 4), (65536 * 3 + 48, 65536 * 3 + 36),
+                                        (4096, 2052)])
+def test_calib_stream_reads_every_byte(wq, nbytes, pos):
+    """The bare-stream reference reads each word of the buffer: a single
+    non-zero word equal to the sink's trigger value, anywhere (ragged tails
+    included), is seen by exactly the thread whose loads cover it."""
+    buf = torch.zeros(nbytes // 4, dtype=torch.int32, device=dev())
+    sink = torch.zeros(1, dtype=torch.int32, device=dev())
+    wq.calib_stream_read(buf, sink)
+    wq.calib_empty(sink, 256, 512)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0
+    buf[pos // 4] = np.int32(np.uint32(0x9E3779B9).view(np.int32))
+    wq.calib_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) & 0xFFFFFFFF == 0x9E3779B9

@@ -14,6 +14,7 @@ products read a packed copy of the weight made once by ``prepack_*``:
   (``prepare_q4(qweight, g_idx, G)`` does the act-order preparation in one go)
 * ``gemm_w8a8(X, Wq, Sw, want_acc=False)``  -> (Y bf16, Xq, Sx, acc | None)
 * ``unpack_q3`` / ``unpack_q8`` / ``unpack_q4``: codes held by a packed weight
+* ``calib_empty`` / ``calib_stream_read``: timing references (no product)
 """
 from __future__ import annotations
 
@@ -50,6 +51,8 @@ _SIGNATURES = {
     "wq_unpack_q3": (_i, [_vp, _vp, _i, _i, _vp]),
     "wq_unpack_q8": (_i, [_vp, _vp, _i, _i, _vp]),
     "wq_unpack_q4": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
+    "wq_calib_empty": (_i, [_i, _i, _vp, _vp]),
+    "wq_calib_stream_read": (_i, [_vp, ctypes.c_longlong, _vp, _vp]),
     "wq_status_str": (ctypes.c_char_p, [_i]),
     "wq_last_hip_error": (_i, []),
 }
@@ -376,3 +379,23 @@ def gemm_int8_mixed(X, Wq, Sw, threshold=6.0, want_acc=False, Y=None):
                                   N, _stream(dev))
     _check("wq_gemm_int8_mixed", st)
     return Y, Xq, Sx, colmax, cols, n_out, acc
+
+
+# ---------------------------------------------------------- measurement --
+
+def calib_empty(sink, grid: int = 256, threads: int = 512):
+    """One launch of an empty kernel (the dispatch floor); sink: int32 [1] on the device."""
+    dev = sink.device
+    _need(sink, "sink", torch.int32, (1,), dev)
+    _check("wq_calib_empty", lib().wq_calib_empty(grid, threads, _ptr(sink), _stream(dev)))
+
+
+def calib_stream_read(buf, sink):
+    """One launch that only reads the bytes of ``buf`` once (the int8 GEMV's loads)."""
+    dev = buf.device
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    _need(sink, "sink", torch.int32, (1,), dev)
+    nbytes = buf.numel() * buf.element_size()
+    _check("wq_calib_stream_read",
+           lib().wq_calib_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(dev)))

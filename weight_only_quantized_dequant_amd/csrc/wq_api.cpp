@@ -241,6 +241,21 @@ int wq_gemm_int8_mixed(const void* X, const int8_t* Wq, const float* Sw, float t
                                           n_outlier, acc_out, M, K, N, as_stream(stream)));
 }
 
+// ------------------------------------------------------ measurement only --
+
+int wq_calib_empty(int grid, int threads, uint32_t* sink, void* stream) {
+  if (!sink) return WQ_ERR_NULL;
+  if (grid < 1 || threads < 1 || threads > 1024) return WQ_ERR_SHAPE;
+  return hip_status(wq::launch_calib_empty(grid, threads, sink, as_stream(stream)));
+}
+
+int wq_calib_stream_read(const void* buf, long long bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink) return WQ_ERR_NULL;
+  if (bytes < 16 || bytes % 16 || bytes > kMaxBytes) return WQ_ERR_SHAPE;
+  if (!aligned16(buf)) return WQ_ERR_ALIGN;
+  return hip_status(wq::launch_calib_stream(buf, (int)bytes, sink, as_stream(stream)));
+}
+
 // ------------------------------------------------------------------- misc --
 
 const char* wq_status_str(int status) {

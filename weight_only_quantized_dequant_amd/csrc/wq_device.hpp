@@ -21,7 +21,6 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr uint32_t kMagic2 = 0x64006400u;  // fp16 1024.0 in both halves
 constexpr float kTwo24 = 16777216.0f;      // 2^24: undoes the subnormal scale
 
 __device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
@@ -29,12 +28,6 @@ __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uin
 // Takes its argument by value on purpose: __builtin_bit_cast applied directly
 // to an element of an ext_vector_type reads the vector's first element.
 __device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
-
-// 128-bit load of packed weights that are read exactly once: non-temporal, so
-// they do not push the activations, scales or partial sums out of the caches.
-__device__ __forceinline__ u32x4 load_stream(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
 
 // Buffer-resource view of a read-only array of `bytes` bytes (< 2^31).  A
 // raw buffer load whose offset falls outside the range returns zeros, which
@@ -51,24 +44,6 @@ constexpr int kOutOfRange = 0x7FFFFFF0;
 
 __device__ __forceinline__ float dot2(h2 a, h2 b, float c) {
   return __builtin_amdgcn_fdot2(a, b, c, false);
-}
-
-// (t & mask) | magic in one v_and_or_b32.  gfx9 VOP3 encodings take no
-// literal operand, so left to itself the compiler splits this into an AND and
-// an OR with literals; here the mask lives in an SGPR and the magic constant
-// in a VGPR.
-__device__ __forceinline__ uint32_t and_or(uint32_t t, uint32_t mask, uint32_t magic) {
-  uint32_t d;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(t), "s"(mask), "v"(magic));
-  return d;
-}
-
-// (1024 + v * 2^p) * 2^-p - (1024 * 2^-p + off)  ==  v - off, exactly.
-__device__ __forceinline__ h2 magic_fma(uint32_t t, _Float16 s_lo, _Float16 s_hi,
-                                        _Float16 b_lo, _Float16 b_hi) {
-  h2 s = {s_lo, s_hi};
-  h2 b = {b_lo, b_hi};
-  return __builtin_elementwise_fma(as_h2(t), s, b);
 }
 
 // ---------------------------------------------------------------------------
@@ -100,72 +75,6 @@ __device__ __forceinline__ uint32_t q3_window(uint32_t w0, uint32_t w1, uint32_t
   else return w2 >> (SRC - 64);
 }
 
-template <int P>
-__device__ __forceinline__ h2 q3_pair_value(uint32_t w0, uint32_t w1, uint32_t w2) {
-  constexpr Q3Pair q = q3_pair(P);
-  constexpr uint32_t mask = (7u << q.pa) | (7u << (16 + q.pb));
-  const uint32_t t = and_or(q3_window<q.src>(w0, w1, w2), mask, kMagic2);
-  constexpr float sa = 1.0f / (1 << q.pa), sb = 1.0f / (1 << q.pb);
-  return magic_fma(t, (_Float16)sa, (_Float16)sb, (_Float16)(-1024.0f * sa),
-                   (_Float16)(-1024.0f * sb));
-}
-
-// All 16 pairs of one block: out[P] = (code a_P, code b_P) as exact fp16.
-__device__ __forceinline__ void q3_block_pairs(uint32_t w0, uint32_t w1, uint32_t w2, h2 out[16]) {
-  out[0] = q3_pair_value<0>(w0, w1, w2);
-  out[1] = q3_pair_value<1>(w0, w1, w2);
-  out[2] = q3_pair_value<2>(w0, w1, w2);
-  out[3] = q3_pair_value<3>(w0, w1, w2);
-  out[4] = q3_pair_value<4>(w0, w1, w2);
-  out[5] = q3_pair_value<5>(w0, w1, w2);
-  out[6] = q3_pair_value<6>(w0, w1, w2);
-  out[7] = q3_pair_value<7>(w0, w1, w2);
-  out[8] = q3_pair_value<8>(w0, w1, w2);
-  out[9] = q3_pair_value<9>(w0, w1, w2);
-  out[10] = q3_pair_value<10>(w0, w1, w2);
-  out[11] = q3_pair_value<11>(w0, w1, w2);
-  out[12] = q3_pair_value<12>(w0, w1, w2);
-  out[13] = q3_pair_value<13>(w0, w1, w2);
-  out[14] = q3_pair_value<14>(w0, w1, w2);
-  out[15] = q3_pair_value<15>(w0, w1, w2);
-}
-
-// ---------------------------------------------------------------------------
-// 4-bit: word w holds rows 8r+j (j = 0..7) of one column in nibble j as
-// u = q + 8.  Pairs (j, j+4) for j = 0..3: nibbles j and j+4 are 16 bits
-// apart, so one mask puts them into the two mantissas (j = 0, 1 directly;
-// j = 2, 3 after w >> 8).  out[j] = (q_j, q_{j+4}).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void q4_word_pairs(uint32_t w, h2 out[4]) {
-  const uint32_t w8 = w >> 8;
-  const _Float16 one = 1.0f, sixteenth = 0.0625f, m1032 = -1032.0f, m72 = -72.0f;
-  out[0] = magic_fma(and_or(w, 0x000F000Fu, kMagic2), one, one, m1032, m1032);
-  out[1] = magic_fma(and_or(w, 0x00F000F0u, kMagic2), sixteenth, sixteenth, m72, m72);
-  out[2] = magic_fma(and_or(w8, 0x000F000Fu, kMagic2), one, one, m1032, m1032);
-  out[3] = magic_fma(and_or(w8, 0x00F000F0u, kMagic2), sixteenth, sixteenth, m72, m72);
-}
-
-// ---------------------------------------------------------------------------
-// int8: words ra, rb hold 4 consecutive columns of rows k and k+1.  out[c] =
-// (q[k][c], q[k+1][c]) for c = 0..3.  XOR 0x80 turns each signed byte into
-// q + 128; v_perm_b32 interleaves the two rows; the magic constant and one
-// packed add of -1152 give q exactly.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void q8_rowpair_pairs(uint32_t ra, uint32_t rb, h2 out[4]) {
-  const uint32_t ua = ra ^ 0x80808080u, ub = rb ^ 0x80808080u;
-  const uint32_t t0 = __builtin_amdgcn_perm(ua, ub, 0x01000504u);  // a.b0 a.b1 b.b0 b.b1
-  const uint32_t t1 = __builtin_amdgcn_perm(ua, ub, 0x03020706u);  // a.b2 a.b3 b.b2 b.b3
-  const uint32_t p0 = (t0 & 0x00FF00FFu) | kMagic2;
-  const uint32_t p1 = __builtin_amdgcn_perm(t0, 0x64646464u, 0x00070005u);
-  const uint32_t p2 = (t1 & 0x00FF00FFu) | kMagic2;
-  const uint32_t p3 = __builtin_amdgcn_perm(t1, 0x64646464u, 0x00070005u);
-  const h2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
-  out[0] = as_h2(p0) + bias;
-  out[1] = as_h2(p1) + bias;
-  out[2] = as_h2(p2) + bias;
-  out[3] = as_h2(p3) + bias;
-}
-
 // ---------------------------------------------------------------------------
 // Subnormal-pair extractors (the fast path).  Values are in units of 2^-24.
 // ---------------------------------------------------------------------------
@@ -178,17 +87,6 @@ __device__ __forceinline__ void q8_pairs_sub(uint32_t ra, uint32_t rb, h2 out[4]
   out[1] = as_h2(__builtin_amdgcn_perm(ra, rb, 0x0c010c05u));
   out[2] = as_h2(__builtin_amdgcn_perm(ra, rb, 0x0c020c06u));
   out[3] = as_h2(__builtin_amdgcn_perm(ra, rb, 0x0c030c07u));
-}
-
-// 4-bit, u = q + 8: pairs (j, j+4).  out[0], out[2]: (u_j, u_j+4) * 2^-24
-// (j = 0, 2); out[1], out[3]: (u_j, u_j+4) * 2^-20 (j = 1, 3; nibble at bit 4
-// of each half).
-__device__ __forceinline__ void q4_pairs_sub(uint32_t w, h2 out[4]) {
-  const uint32_t w8 = w >> 8;
-  out[0] = as_h2(w & 0x000F000Fu);
-  out[1] = as_h2(w & 0x00F000F0u);
-  out[2] = as_h2(w8 & 0x000F000Fu);
-  out[3] = as_h2(w8 & 0x00F000F0u);
 }
 
 // 3-bit: pair P of q3_pair(P) as (c_a * 2^pa, c_b * 2^pb) * 2^-24.
@@ -324,30 +222,6 @@ __device__ __forceinline__ int bfly_base(int lane, bool& owner) {
     }
   }
   return base;
-}
-
-// ---------------------------------------------------------------------------
-// Split-K completion.  Every workgroup of a column tile stores its fp32
-// partials, then arrives on the tile's counter; the last to arrive sees every
-// partial (agent-scope release by the writers, acquire by the reader), sums
-// them in a fixed order and resets the counter to zero for the next call.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ bool splitk_arrive(unsigned* counter, int S, int* flag_smem) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev =
-        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    *flag_smem = (prev == (unsigned)(S - 1));
-  }
-  __syncthreads();
-  const bool last = *flag_smem != 0;
-  if (last) __threadfence();
-  return last;
-}
-
-__device__ __forceinline__ void splitk_reset(unsigned* counter) {
-  if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace wq

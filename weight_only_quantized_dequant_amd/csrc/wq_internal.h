@@ -69,4 +69,9 @@ hipError_t launch_int8_mixed(const void* X16, const int8_t* Wq, const float* Sw,
                              void* Y, int8_t* Xq, float* Sx, float* colmax, int32_t* out_cols,
                              int32_t* n_out, int32_t* acc_out, int M, int K, int N, hipStream_t s);
 
+// Measurement references (calib.hip): a launch that does nothing, and one that
+// only streams `bytes` of `buf` with the int8 GEMV's loads and grid shape.
+hipError_t launch_calib_empty(int grid, int threads, uint32_t* sink, hipStream_t s);
+hipError_t launch_calib_stream(const void* buf, int bytes, uint32_t* sink, hipStream_t s);
+
 }  // namespace wq
