@@ -52,21 +52,6 @@ constexpr int kLoads = 6;                        // direct-to-LDS loads per stag
 // LDS banks.
 __device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 15); }
 
-template <int VM>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(VM >= 0 && VM < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// All LDS reads of this wave done, then a workgroup barrier; the empty asm
-// statements keep the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 }  // namespace
 
 // Codes of a stage in LDS: the 16-byte piece of row r = 8 o + i (o = 0..15,

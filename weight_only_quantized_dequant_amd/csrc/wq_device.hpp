@@ -46,6 +46,25 @@ __device__ __forceinline__ float dot2(h2 a, h2 b, float c) {
   return __builtin_amdgcn_fdot2(a, b, c, false);
 }
 
+// s_waitcnt with vmcnt = VM and the other counters left alone.
+template <int VM>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// This wave's LDS accesses done, then a workgroup barrier.  Unlike
+// __syncthreads() it does not wait for outstanding global loads, so a ring
+// of weight loads stays in flight across it (each later use of a loaded
+// register still gets its own vmcnt wait from the compiler).  The empty asm
+// statements keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------
 // 3-bit: one 32-row block of one column is three int32 words w0, w1, w2 = the
 // 96-bit value V; code i sits at bits 3i..3i+2 of V.  The 32 codes are read
