@@ -18,10 +18,11 @@
 // are zero lanes of the operand).  A code u (0..15) enters the cores as the
 // fp16 subnormal with mantissa u, i.e. exactly u * 2^-24, so each product
 // x * u * 2^-24 is exact in the fp32 accumulator.  Per group g the tile
-//   C = sum_k x[m, k] u[k, n] 2^-24,   S = sum_k x[m, k]   (a second MFMA
-// against a constant operand of ones) gives the group's share
-//   scale[g, n] * (C - 8 * 2^-24 * S)
-// of Y / 2^24: the (u - 8) offset is applied once per group, not per code.
+//   C = sum_k x[m, k] u[k, n] 2^-24   and the group sum  S = sum_k x[m, k]
+// give the group's share  scale[g, n] * (C - 8 * 2^-24 * S)  of Y / 2^24:
+// the (u - 8) offset is applied once per group, not per code.  S depends on
+// X only, so each workgroup computes it once per (row, group) from the X it
+// staged in LDS and every panel reuses it.
 //
 // Layout.  Panels of 16 columns; a panel's rows (group order) are cut into
 // blocks of 128, zero-padded to a whole block.  Block (panel p, block b) is
@@ -140,6 +141,7 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
   const int xhalves = rs * MT;                                          // halves of X in LDS
   _Float16* xa = reinterpret_cast<_Float16*>(smem);                     // [MT][octet][8], padded rows
   float* red = reinterpret_cast<float*>(smem + (size_t)xhalves * 2);  // [run][wave][MT][16]
+  float* sg = red + kQ4MaxRun * kQ4Waves * MT * 16;                    // [K / G][8] group sums
 
   const int t = threadIdx.x, lane = t & 63;
   // Uniform across the wave: keeps the block range and cursors in scalar
@@ -255,17 +257,39 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
   }
   __syncthreads();
 
-  const h8 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f,
-                   (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
-  // Operand rows past MT read row MT - 1: rows of the product depend only on
-  // their own row of X, and rows >= MT are never stored.
+  // Group sums of the wave's own groups: sg[g][m] = sum of the G halves of
+  // group g (group order: octets g G / 8 .. (g + 1) G / 8 - 1) in row m < MT.
+  // Eight lanes share one sum: part p adds octets p, p + 8, ... with v_dot2
+  // against ones, then a 3-step butterfly over the eight lanes (a fixed
+  // order, so the result is bitwise reproducible).  Only this wave reads
+  // these entries, after its own writes: no workgroup barrier.  Entries of
+  // rows m >= MT are never written; they only meet output rows that are
+  // never stored.
+  {
+    const h2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+    const int octs = G / 8, part = lane & 7;
+    const int g0 = blo * kQ4Block / G, ng = nbw * kQ4Block / G;
+    for (int task = lane >> 3; task < ng * MT; task += 8) {
+      const int g = g0 + task / MT, m = task % MT;
+      const _Float16* row = xa + (size_t)m * rs + (size_t)g * G;
+      float acc = 0.0f;
+      for (int o = part; o < octs; o += 8) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(row + 8 * o);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = dot2(as_h2(v[e]), one2, acc);
+      }
+      float sv[1] = {acc};
+      bfly<1, 2, 0>(sv, lane);
+      if (part == 0) sg[g * 8 + m] = sv[0];
+    }
+  }
+
   const int am = (lane & 15) < MT ? (lane & 15) : MT - 1, aq = lane >> 4;
   const _Float16* xrow = xa + (size_t)am * rs + aq * 8;
-  f4 C0 = {0.0f, 0.0f, 0.0f, 0.0f}, C1 = C0, S0 = C0, S1 = C0, tot = C0;
+  f4 C0 = {0.0f, 0.0f, 0.0f, 0.0f}, C1 = C0, tot = C0;
 
-  // One block: 4 MFMA steps (and 4 against the ones, two chains each) and the
-  // group closes; at the wave's last block of a panel its partial tile goes
-  // to LDS.
+  // One block: 4 MFMA steps (two chains) and the group closes; at the wave's
+  // last block of a panel its partial tile goes to LDS.
   int cp = 0, cb = blo;  // compute cursor: panel of the run, block
   // Operands of X for the block about to be multiplied, read one block ahead
   // (X is the same for every panel, so after a wave's last block comes blo).
@@ -287,30 +311,31 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
       h2 pr[4];
       q4_mfma_pairs(w[j], pr);
       const h8 bv = {pr[0].x, pr[0].y, pr[1].x, pr[1].y, pr[2].x, pr[2].y, pr[3].x, pr[3].y};
-      if (j & 1) {
+      if (j & 1)
         C1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], bv, C1, 0, 0, 0);
-        S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], ones, S1, 0, 0, 0);
-      } else {
+      else
         C0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], bv, C0, 0, 0, 0);
-        S0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], ones, S0, 0, 0, 0);
-      }
       bool close;
-      int k = 0;
+      int k = 0, g;
       if constexpr (NSC > 1) {
         close = ((j + 1) % (4 / NSC)) == 0;
         k = j / (4 / NSC);
+        g = b * NSC + k;
       } else {
         close = j == 3 && ((b + 1) & (bpg - 1)) == 0;
+        g = b >> lbpg;
       }
       if (close) {
         const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sc[k]);
         // -offset * 2^-24: the codes sit in the products as u * 2^-24.
         float zoff = -8.0f / kTwo24;
         if constexpr (ZP) zoff = (float)__builtin_bit_cast(_Float16, (uint16_t)zq[k]) * (-1.0f / kTwo24);
+        // Group sums of this lane's rows 4 (lane / 16) + r.
+        const f4 S = *reinterpret_cast<const f4*>(sg + g * 8 + 4 * aq);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          tot[r] = __builtin_fmaf(s, __builtin_fmaf(S0[r] + S1[r], zoff, C0[r] + C1[r]), tot[r]);
-          C0[r] = C1[r] = S0[r] = S1[r] = 0.0f;
+          tot[r] = __builtin_fmaf(s, __builtin_fmaf(S[r], zoff, C0[r] + C1[r]), tot[r]);
+          C0[r] = C1[r] = 0.0f;
         }
       }
     }
@@ -410,7 +435,8 @@ static hipError_t launch_q4_t(const void* X, const void* packed, const void* sca
   const int cus = device_cus();
   int grid = p.npanels < cus ? p.npanels : cus;
   if ((p.npanels + grid - 1) / grid > kQ4MaxRun) grid = (p.npanels + kQ4MaxRun - 1) / kQ4MaxRun;
-  const size_t lds = ((size_t)p.u * kQ4Block + kQ4RowPad) * MT * 2 + (size_t)kQ4MaxRun * kQ4Waves * MT * 16 * 4;
+  const size_t lds = ((size_t)p.u * kQ4Block + kQ4RowPad) * MT * 2 +
+                     (size_t)kQ4MaxRun * kQ4Waves * MT * 16 * 4 + (size_t)(K / G) * 8 * 4;
   if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&q4_mfma_kernel<MT, NSC, ZP>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
