@@ -216,6 +216,19 @@ def test_q3_vs_oracle(wq, K, N, dt, seed):
     assert_tol(host(y), ref, f"q3 {dt} {K}x{N}")
 
 
+@pytest.mark.parametrize("K,N,dt", [
+    (64, 8208, "f16"),     # 2052 four-column panels: runs of 8 panels over 257 workgroups
+    (128, 3076, "f32"),    # 769 panels: runs of 3 and 4
+    (32768, 64, "f16"),    # x fills 64 KB of LDS next to the per-panel partial sums
+    (16384, 132, "f32"),
+])
+def test_q3_long_runs_and_long_k(wq, K, N, dt):
+    d = synth.gen_q3(K, N, seed=K + N, dtype=dt)
+    y = wq.matvec_q3(cu(d["x"]), wq.prepack_q3(cu(d["qweight"]), K), cu(d["scales"]), cu(d["zeros"]))
+    ref = oracle.matvec_q3(d["x"], d["qweight"], d["scales"], d["zeros"])
+    assert_tol(host(y), ref, f"q3 {dt} {K}x{N}")
+
+
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 def test_q3_integer_exact_and_zero_codes(wq, dt):
     K, N = 1024, 516

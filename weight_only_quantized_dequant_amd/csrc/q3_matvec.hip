@@ -26,6 +26,10 @@
 
 namespace wq {
 
+// Panels a workgroup walks at most: each keeps its waves' partial sums in
+// its own LDS slot until the single reduction at the end.
+constexpr int kQ3MaxRun = 8;
+
 // Threads of the product's workgroup: 8 waves (two per SIMD, one wave's
 // arithmetic overlapping another's loads) for the large shapes, 4 waves for
 // the small ones, where the shorter per-wave staging wins.
@@ -103,7 +107,7 @@ __global__ __launch_bounds__(THREADS) void q3_panel_kernel(
   constexpr int UB = 1;  // 32-row blocks per streamed unit
   constexpr int NW = THREADS / 64;
   __shared__ float xsum_w[NW];
-  __shared__ float red[NW][CPP][4];
+  __shared__ float red[kQ3MaxRun][NW][CPP][4];
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   // This workgroup's contiguous run of panels; a unit is UB blocks of a panel.
@@ -211,7 +215,7 @@ __global__ __launch_bounds__(THREADS) void q3_panel_kernel(
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) my_sum += __shfl_xor(my_sum, o);
-  if (lane == 0) xsum_w[wave] = my_sum;  // read after the first panel's barrier
+  if (lane == 0) xsum_w[wave] = my_sum;  // read after the final barrier
   // The wave's own LDS writes are done before its lanes read each other's.
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   asm volatile("" ::: "memory");
@@ -224,11 +228,12 @@ __global__ __launch_bounds__(THREADS) void q3_panel_kernel(
     for (int j = 0; j < 4; ++j) acc[a][j] = 0.0f;
 
   // One unit: multiply the buffer `w`, refill `pre` with unit q + 2; at the
-  // last unit of a panel, reduce and write the panel's P outputs.
+  // last unit of a panel, reduce over the wave and leave the wave's partial
+  // sums of the panel's P columns in LDS.
   int cpi = 0, cu = 0;  // compute cursor: panel of the run, unit
   auto step = [&](int q, const u32x4 (&w)[UB][3], u32x4 (&pre)[UB][3]) {
     if (q >= nunits) return;
-    const int panel = p_begin + cpi, i0 = cu * UB;
+    const int pr_i = cpi, i0 = cu * UB;
     const bool last = cu == nr - 1;
     if (++cu == nr) {
       cu = 0;
@@ -282,40 +287,43 @@ __global__ __launch_bounds__(THREADS) void q3_panel_kernel(
         acc[0][j] = 0.0f;
       }
     }
-    // Over the slots of a chunk, then y = scale * A - zero * sum(x).
+    // Over the slots of a chunk that share this wave.
     bfly<4, 5, LOWBIT>(v, lane);
     bool owner;
     const int base = bfly_base<4, LOWBIT>(lane, owner);
     constexpr int LEFT = bfly_left<4, LOWBIT>();
     if (owner) {
 #pragma unroll
-      for (int j = 0; j < LEFT; ++j) red[wave][c][base + j] = v[j];
+      for (int j = 0; j < LEFT; ++j) red[pr_i][wave][c][base + j] = v[j];
     }
-    __syncthreads();
-    if (t < P) {
-      float xsum = 0.0f;
-#pragma unroll
-      for (int w2 = 0; w2 < NW; ++w2) xsum += xsum_w[w2];
-      const int rc = t / 4, j = t % 4;
-      const int n = panel * P + t;
-      float A = 0.0f;
-#pragma unroll
-      for (int w2 = 0; w2 < NW; ++w2) A += red[w2][rc][j];
-      if constexpr (F16) {
-        const float sc = (float)reinterpret_cast<const _Float16*>(sv)[n];
-        const float ze = (float)reinterpret_cast<const _Float16*>(zv)[n];
-        reinterpret_cast<_Float16*>(yv)[n] = (_Float16)(sc * A - ze * xsum);
-      } else {
-        const float sc = reinterpret_cast<const float*>(sv)[n];
-        const float ze = reinterpret_cast<const float*>(zv)[n];
-        reinterpret_cast<float*>(yv)[n] = sc * A - ze * xsum;
-      }
-    }
-    __syncthreads();  // red is rewritten by the next panel
   };
   for (int q = 0; q < nunits; q += 2) {
     step(q, w0, w0);
     step(q + 1, w1, w1);
+  }
+
+  // 5. Over the waves, then y = scale * A - zero * sum(x), for every panel of
+  //    the run at once.
+  __syncthreads();
+  float xsum = 0.0f;
+#pragma unroll
+  for (int w2 = 0; w2 < NW; ++w2) xsum += xsum_w[w2];
+  for (int r = t; r < (p_end - p_begin) * P; r += THREADS) {
+    const int pi = r / P, tt = r % P;
+    const int rc = tt / 4, j = tt % 4;
+    const int n = (p_begin + pi) * P + tt;
+    float A = 0.0f;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) A += red[pi][w2][rc][j];
+    if constexpr (F16) {
+      const float sc = (float)reinterpret_cast<const _Float16*>(sv)[n];
+      const float ze = (float)reinterpret_cast<const _Float16*>(zv)[n];
+      reinterpret_cast<_Float16*>(yv)[n] = (_Float16)(sc * A - ze * xsum);
+    } else {
+      const float sc = reinterpret_cast<const float*>(sv)[n];
+      const float ze = reinterpret_cast<const float*>(zv)[n];
+      reinterpret_cast<float*>(yv)[n] = sc * A - ze * xsum;
+    }
   }
 }
 
@@ -377,7 +385,16 @@ static hipError_t launch_q3_t(const void* x, const void* packed, const void* sca
                               hipStream_t s) {
   const size_t lds = (size_t)(K / 2) * (F16 ? 4 : 8);
   const int cus = device_cus();
-  const int grid = p.npanels < cus ? p.npanels : cus;
+  int grid = p.npanels < cus ? p.npanels : cus;
+  if ((p.npanels + grid - 1) / grid > kQ3MaxRun) grid = (p.npanels + kQ3MaxRun - 1) / kQ3MaxRun;
+  // Static LDS (the per-panel partial sums) plus x may pass 64 KB.
+  constexpr size_t kStatic = sizeof(float) * ((size_t)kQ3MaxRun * (THREADS / 64) * CPP * 4 + THREADS / 64);
+  if (lds + kStatic > 65536) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&q3_panel_kernel<F16, CPP, THREADS>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((q3_panel_kernel<F16, CPP, THREADS>), dim3(grid), dim3(THREADS), lds, s, x,
                      reinterpret_cast<const uint8_t*>(packed), scales, zeros, y, K, N, p.u, p.nsa,
                      p.npanels, (int)p.packed_bytes);
