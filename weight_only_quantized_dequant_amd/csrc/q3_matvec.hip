@@ -167,6 +167,27 @@ __global__ __launch_bounds__(THREADS) void q3_panel_kernel(
   load_unit(w0);
   load_unit(w1);
 
+  // The scale and zero of output column p_begin * P + t (a run has at most
+  // 32 * kQ3MaxRun <= THREADS outputs), loaded now and used at the end.
+  // Issued after the first units, so waiting for those does not wait for them.
+  static_assert(32 * kQ3MaxRun <= 256, "one output per thread");
+  const int nout = (p_end - p_begin) * P;
+  float out_sc = 0.0f, out_ze = 0.0f;
+  {
+    // Buffer loads: they count in vmcnt only (a flat load would also hold up
+    // every later LDS wait).
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(sv, N * (F16 ? 2 : 4));
+    const __amdgpu_buffer_rsrc_t zr = make_rsrc(zv, N * (F16 ? 2 : 4));
+    const int off = t < nout ? (p_begin * P + t) * (F16 ? 2 : 4) : kOutOfRange;
+    if constexpr (F16) {
+      out_sc = (float)__builtin_bit_cast(_Float16, (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0));
+      out_ze = (float)__builtin_bit_cast(_Float16, (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(zr, off, 0, 0));
+    } else {
+      out_sc = as_f32(__builtin_amdgcn_raw_buffer_load_b32(sr, off, 0, 0));
+      out_ze = as_f32(__builtin_amdgcn_raw_buffer_load_b32(zr, off, 0, 0));
+    }
+  }
+
   // 3. Pairs into LDS in code-pair order (pre-scaled), and sum_k x[k].
   float my_sum = 0.0f;
   auto stage_block = [&](int blk, const u32x4* raw) {
@@ -308,22 +329,17 @@ __global__ __launch_bounds__(THREADS) void q3_panel_kernel(
   float xsum = 0.0f;
 #pragma unroll
   for (int w2 = 0; w2 < NW; ++w2) xsum += xsum_w[w2];
-  for (int r = t; r < (p_end - p_begin) * P; r += THREADS) {
-    const int pi = r / P, tt = r % P;
+  if (t < nout) {
+    const int pi = t / P, tt = t % P;
     const int rc = tt / 4, j = tt % 4;
-    const int n = (p_begin + pi) * P + tt;
+    const int n = p_begin * P + t;
     float A = 0.0f;
 #pragma unroll
     for (int w2 = 0; w2 < NW; ++w2) A += red[pi][w2][rc][j];
-    if constexpr (F16) {
-      const float sc = (float)reinterpret_cast<const _Float16*>(sv)[n];
-      const float ze = (float)reinterpret_cast<const _Float16*>(zv)[n];
-      reinterpret_cast<_Float16*>(yv)[n] = (_Float16)(sc * A - ze * xsum);
-    } else {
-      const float sc = reinterpret_cast<const float*>(sv)[n];
-      const float ze = reinterpret_cast<const float*>(zv)[n];
-      reinterpret_cast<float*>(yv)[n] = sc * A - ze * xsum;
-    }
+    if constexpr (F16)
+      reinterpret_cast<_Float16*>(yv)[n] = (_Float16)(out_sc * A - out_ze * xsum);
+    else
+      reinterpret_cast<float*>(yv)[n] = out_sc * A - out_ze * xsum;
   }
 }
 
