@@ -55,6 +55,13 @@ design notes):
 * The asymmetric 4-bit form takes the unsigned nibble ``u`` (0..15) as the
   integer value and one fp16 zero and one fp16 scale per (group, column),
   both as given: ``w = (u - zero) * scale``.
+* 2-bit codes, which "GPTQ CUDA kernel walkthrough" names only as a lower
+  bit width still to support (its closing outlook): 16 per int32 along K,
+  row ``16r + j`` in bits ``2j..2j+1`` of word ``r`` (the 4-bit order with
+  2-bit fields), unsigned 0..3, rebuilt in the same asymmetric group-wise
+  form ``w = (u - zero) * scale`` ("Quantization CUDA", "量化粒度":
+  x = S*(q - Z) per group), since a symmetric 2-bit grid has no zero-centred
+  form worth using.
 * Outputs are overwritten (no accumulate into the caller's buffer), no bias.
 * The activation quantiser divides (``absmax / 127`` then ``x / Sx``) in fp32
   with IEEE round-to-nearest, rounds half to even and clamps to [-127, 127];
@@ -82,7 +89,7 @@ import numpy as np
 __all__ = [
     "bits_le", "unpack_q3", "unpack_u4", "unpack_q4", "dequant_q3", "dequant_q8_group",
     "dequant_q4_group", "dequant_q4_zp", "matvec_q3", "gemm_q8_group", "gemm_q4_group",
-    "gemm_q4_zp",
+    "gemm_q4_zp", "unpack_u2", "gemm_q2_zp",
     "quantize_rows_int8", "w8a8_accumulate", "w8a8_epilogue",
     "bf16_rne_bits", "bf16_bits_to_f32", "gemm_w8a8", "smooth_activations",
     "smooth_weight", "gemm_w8a8_smooth", "fp16_rne", "int8_mixed_decompose",
@@ -135,6 +142,19 @@ def unpack_u4(qweight: np.ndarray) -> np.ndarray:
 def unpack_q4(qweight: np.ndarray) -> np.ndarray:
     """Signed 4-bit codes ``[K, N]`` (-8..7): the unsigned value u minus 8."""
     return unpack_u4(qweight) - 8
+
+
+def unpack_u2(qweight: np.ndarray) -> np.ndarray:
+    """Unsigned 2-bit values ``[K, N]`` (0..3) from int32 ``[K/16, N]``.
+
+    Row 16r + j is bits 2j, 2j+1 of word r.
+    """
+    qweight = np.asarray(qweight)
+    R, N = qweight.shape
+    b = bits_le(qweight).astype(np.int64)             # [R, N, 32]
+    pair = b.reshape(R, N, 16, 2)
+    u = pair[..., 0] + 2 * pair[..., 1]               # [R, N, 16]
+    return u.transpose(0, 2, 1).reshape(R * 16, N)
 
 
 # --------------------------------------------------------------------------
@@ -202,6 +222,17 @@ def gemm_q4_zp(X: np.ndarray, qweight: np.ndarray, scales: np.ndarray, zeros: np
                g_idx: np.ndarray | None, G: int) -> np.ndarray:
     """``Y = X . W`` with W the dequantised asymmetric 4-bit weight; fp64."""
     W = dequant_q4_zp(unpack_u4(qweight), scales, zeros, g_idx, G)
+    return np.atleast_2d(np.asarray(X).astype(np.float64)) @ W
+
+
+def gemm_q2_zp(X: np.ndarray, qweight: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
+               g_idx: np.ndarray | None, G: int) -> np.ndarray:
+    """``Y = X . W`` with W the dequantised asymmetric 2-bit weight; fp64.
+
+    The same group-wise rebuild as the asymmetric 4-bit weight,
+    ``(u - zero[g, n]) * scale[g, n]``, on the 2-bit values.
+    """
+    W = dequant_q4_zp(unpack_u2(qweight), scales, zeros, g_idx, G)
     return np.atleast_2d(np.asarray(X).astype(np.float64)) @ W
 
 

@@ -29,6 +29,7 @@ import numpy as np
 __all__ = [
     "pack_q3", "pack_q4", "gen_q3", "gen_q8_group", "gen_q4_group",
     "gen_w8a8", "gen_q4_zp", "gen_w8a8_smooth", "gen_int8_mixed", "SEEDS",
+    "pack_q2", "gen_q2_zp",
 ]
 
 # Seeds of the named workloads (the tests and the benchmark use these).
@@ -44,6 +45,7 @@ SEEDS = {
     "w8a8_256x8192x8192": 1400,
     "w8a8_smooth": 1700,
     "int8_mixed": 1800,
+    "q2_zp": 1900,               # asymmetric 2-bit; activations use 1900 + M
 }
 
 
@@ -78,6 +80,21 @@ def pack_q4(u: np.ndarray) -> np.ndarray:
     words = np.zeros((K // 8, N), dtype=np.uint32)
     for j in range(8):
         words |= v[:, j, :] << np.uint32(4 * j)
+    return words.view(np.int32)
+
+
+def pack_q2(u: np.ndarray) -> np.ndarray:
+    """Pack unsigned 2-bit values ``[K, N]`` (0..3, K % 16 == 0) into int32 words."""
+    u = np.asarray(u)
+    K, N = u.shape
+    if K % 16:
+        raise ValueError("K must be a multiple of 16")
+    if u.min(initial=0) < 0 or u.max(initial=0) > 3:
+        raise ValueError("2-bit values must lie in 0..3")
+    v = u.astype(np.uint32).reshape(K // 16, 16, N)
+    words = np.zeros((K // 16, N), dtype=np.uint32)
+    for j in range(16):
+        words |= v[:, j, :] << np.uint32(2 * j)
     return words.view(np.int32)
 
 
@@ -208,6 +225,47 @@ def gen_q4_zp(M: int, K: int, N: int, G: int, seed: int, act_order: bool = False
     zeros = z.astype(np.float16)
     u = np.clip(_quantise(W, s32[g_idx], -(1 << 20), 1 << 20) + z[g_idx].astype(np.int64), 0, 15)
     qweight = pack_q4(u)
+    xr = np.random.default_rng(seed + M if x_seed is None else x_seed)
+    X = xr.standard_normal((M, K)).astype(np.float16)
+    return {"X": X, "qweight": qweight, "scales": scales, "zeros": zeros, "g_idx": g_idx,
+            "u": u, "W": W, "M": M, "K": K, "N": N, "G": G}
+
+
+def gen_q2_zp(M: int, K: int, N: int, G: int, seed: int, act_order: bool = False,
+              x_seed: int | None = None) -> dict:
+    """Asymmetric 2-bit group-wise inputs: unsigned values 0..3, a zero point
+    and a scale per (group, column).
+
+    Draw order (weight rng ``seed``): W ~ N(0, 0.02) fp32 [K,N]; then, with
+    act-order, ``g_idx = permutation(repeat(arange(K/G), G))`` (else
+    ``k // G``).  Per (group, column): ``scale = fp16((max - min) / 3)`` over
+    the group's rows, ``zero = clip(rint(-min / fp32(scale)), 0, 3)`` (an
+    integer, stored fp16) and ``u = clip(rint(W / fp32(scale)) + zero, 0, 3)``,
+    packed as :func:`pack_q2`.  X ~ N(0,1) fp16 [M,K] from rng ``x_seed``
+    (default ``seed + M``).
+    """
+    if K % G or K % 16:
+        raise ValueError("K must be a multiple of G and of 16")
+    rng = np.random.default_rng(seed)
+    W = rng.normal(0.0, 0.02, size=(K, N)).astype(np.float32)
+    ng = K // G
+    if act_order:
+        g_idx = rng.permutation(np.repeat(np.arange(ng), G)).astype(np.int32)
+    else:
+        g_idx = (np.arange(K) // G).astype(np.int32)
+    wmin = np.zeros((ng, N), dtype=np.float32)
+    wmax = np.zeros((ng, N), dtype=np.float32)
+    for g in range(ng):
+        wmin[g] = np.min(W[g_idx == g], axis=0)
+        wmax[g] = np.max(W[g_idx == g], axis=0)
+    scales = ((wmax - wmin) / np.float32(3.0)).astype(np.float16)
+    s32 = scales.astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        z = np.where(s32 == 0, np.float32(0), np.rint(-wmin / s32))
+    z = np.clip(z, 0, 3)
+    zeros = z.astype(np.float16)
+    u = np.clip(_quantise(W, s32[g_idx], -(1 << 20), 1 << 20) + z[g_idx].astype(np.int64), 0, 3)
+    qweight = pack_q2(u)
     xr = np.random.default_rng(seed + M if x_seed is None else x_seed)
     X = xr.standard_normal((M, K)).astype(np.float16)
     return {"X": X, "qweight": qweight, "scales": scales, "zeros": zeros, "g_idx": g_idx,

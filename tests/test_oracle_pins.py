@@ -365,6 +365,65 @@ def test_q4_zp_generator_roundtrip_bound():
     assert np.all(np.abs(W - d["W"]) <= s * (0.5 + 1e-3) + 1e-12)
 
 
+# ------------------------------------------------------ asymmetric 2-bit --
+
+def test_q2_zp_worked_examples():
+    for name, words, G, zeros, scales, x, y in read_golden("q2_zp_worked.txt"):
+        w = np.array([int(h, 16) for h in words.split()], dtype=np.uint32)
+        qw = w.view(np.int32).reshape(-1, 1)
+        z = np.array([float(v) for v in zeros.split()]).reshape(-1, 1)
+        s = np.array([float(v) for v in scales.split()]).reshape(-1, 1)
+        xv = np.array([float(v) for v in x.split()]).reshape(1, -1)
+        got = oracle.gemm_q2_zp(xv, qw, s, z, None, int(G))
+        assert got.shape == (1, 1)
+        assert got[0, 0] == float(y), name
+
+
+def test_q2_closed_form_words():
+    w = np.array([0xE4E4E4E4, 0x1B1B1B1B, 0xC0000000, 0x00000001], dtype=np.uint32)
+    u = oracle.unpack_u2(w.view(np.int32).reshape(4, 1))[:, 0]
+    assert np.array_equal(u[0:16], np.arange(16) % 4)
+    assert np.array_equal(u[16:32], 3 - np.arange(16) % 4)
+    assert np.array_equal(u[32:48], np.r_[np.zeros(15, int), 3])
+    assert np.array_equal(u[48:64], np.r_[1, np.zeros(15, int)])
+
+
+def test_q2_roundtrip_and_generator_bound():
+    rng = np.random.default_rng(65)
+    u = rng.integers(0, 4, size=(96, 7))
+    assert np.array_equal(oracle.unpack_u2(synth.pack_q2(u)), u)
+    d = synth.gen_q2_zp(1, 512, 48, 128, seed=66, act_order=True)
+    assert np.array_equal(oracle.unpack_u2(d["qweight"]), d["u"])
+    W = oracle.dequant_q4_zp(d["u"], d["scales"], d["zeros"], d["g_idx"], 128)
+    s = d["scales"].astype(np.float64)[d["g_idx"]]
+    assert np.all(np.abs(W - d["W"]) <= s * (0.5 + 1e-3) + 1e-12)
+
+
+def test_q2_matches_the_same_values_as_4bit():
+    # The same unsigned values packed as 2-bit and as 4-bit fields go through
+    # two independent unpackers into the same asymmetric rebuild.
+    d = synth.gen_q2_zp(3, 256, 24, 64, seed=67, act_order=True)
+    a = oracle.gemm_q2_zp(d["X"], d["qweight"], d["scales"], d["zeros"], d["g_idx"], 64)
+    b = oracle.gemm_q4_zp(d["X"], synth.pack_q4(d["u"]), d["scales"], d["zeros"], d["g_idx"], 64)
+    assert np.array_equal(a, b)
+
+
+def test_q2_group_brute_force():
+    rng = np.random.default_rng(68)
+    K, N, G = 32, 3, 16
+    u = rng.integers(0, 4, size=(K, N))
+    z = rng.integers(0, 7, size=(K // G, N)) / 2.0
+    s = rng.integers(1, 9, size=(K // G, N)) / 8.0
+    x = rng.integers(-3, 4, size=(1, K)).astype(np.float64)
+    got = oracle.gemm_q2_zp(x, synth.pack_q2(u), s, z, None, G)[0]
+    for n in range(N):
+        acc = Fraction(0)
+        for k in range(K):
+            g = k // G
+            acc += Fraction(x[0, k]) * (Fraction(int(u[k, n])) - Fraction(z[g, n])) * Fraction(s[g, n])
+        assert got[n] == float(acc), n
+
+
 # ------------------------------------------------------------ SmoothQuant --
 
 def test_smooth_ones_is_plain_w8a8():
