@@ -205,6 +205,28 @@ def wl_q4zp(wq, torch, dev, M, G=128):
     return w
 
 
+def wl_q2(wq, torch, dev, M, G=128):
+    import synth
+    K, N = 4096, 11008
+    # packed codes + scales + zeros + the uint16 row table + X + Y
+    nbytes = (K // 16) * N * 4 + 2 * (K // G) * N * 2 + K * 2 + M * K * 2 + M * N * 2
+    d = synth.gen_q2_zp(M, K, N, G, seed=synth.SEEDS["q2_zp"])
+
+    def make(R):
+        packed, _ = wq.prepare_q2(torch.from_numpy(d["qweight"]).to(dev), None, G)
+        base = [torch.from_numpy(d["X"]).to(dev), packed, torch.from_numpy(d["scales"]).to(dev),
+                torch.from_numpy(d["zeros"]).to(dev)]
+        return [[t.clone() for t in base] + [torch.empty((M, N), dtype=torch.float16, device=dev)]
+                for _ in range(R)]
+
+    def run(c):
+        wq.gemm_q2_group_zp(c[0], c[1], c[2], c[3], G, Y=c[4])
+
+    w = Workload(f"q2_zp_asymmetric M={M} K={K} N={N} G={G}", nbytes, make, run)
+    w.oracle = lambda: __import__("oracle").gemm_q2_zp(d["X"], d["qweight"], d["scales"], d["zeros"], None, G)
+    return w
+
+
 def wl_w8a8(wq, torch, dev, smooth=False):
     import synth
     M, K, N = 256, 8192, 8192
@@ -340,7 +362,7 @@ def main():
     ap.add_argument("--no-calibration", action="store_true",
                     help="skip the empty-kernel and bare-stream reference timings")
     ap.add_argument("--workload", default="q8",
-                    help="q8 (headline) | q8_m* | q3_* | q4_m* | q4zp_m* | q4zp_g64_m* | w8a8 | w8a8_smooth | int8_mixed (single line)")
+                    help="q8 (headline) | q8_m* | q3_* | q4_m* | q4zp_m* | q4zp_g64_m* | q2_m* | w8a8 | w8a8_smooth | int8_mixed (single line)")
     ap.add_argument("--eager", action="store_true",
                     help="launch every timed step from Python instead of replaying a captured graph")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -382,6 +404,8 @@ def main():
             return wl_q4zp(wq, torch, dev, int(name[len("q4zp_g64_m"):]), 64)
         if name.startswith("q4zp_m"):
             return wl_q4zp(wq, torch, dev, int(name[len("q4zp_m"):]))
+        if name.startswith("q2_m"):
+            return wl_q2(wq, torch, dev, int(name[len("q2_m"):]))
         if name == "w8a8":
             return wl_w8a8(wq, torch, dev)
         if name == "w8a8_smooth":
@@ -412,7 +436,7 @@ def main():
     if not args.headline_only:
         sec = {}
         for name in ("q3_f32_1024", "q3_f16_4096x4096", "q3_f16_4096x11008", "q3_f16_11008x4096",
-                     "q4_m1", "q4_m2", "q4_m4", "q4_m8", "q4zp_m1", "q4zp_g64_m1", "q8_m512", "w8a8", "w8a8_smooth", "int8_mixed"):
+                     "q4_m1", "q4_m2", "q4_m4", "q4_m8", "q4zp_m1", "q4zp_g64_m1", "q2_m1", "q2_m8", "q8_m512", "w8a8", "w8a8_smooth", "int8_mixed"):
             sw = make(name)
             big = name.startswith("w8a8") or name == "int8_mixed"
             sms, sR = time_workload(torch, sw, 100 if big else 300, 10 if big else 30)

@@ -84,11 +84,12 @@ typedef enum wq_dtype {
 typedef enum wq_op {
   WQ_OP_Q3 = 0,   /* 3-bit matvec              */
   WQ_OP_Q4G = 1,  /* 4-bit group-wise GEMM      */
-  WQ_OP_Q8G = 2   /* int8 group-wise GEMV/GEMM  */
+  WQ_OP_Q8G = 2,  /* int8 group-wise GEMV/GEMM  */
+  WQ_OP_Q2G = 3   /* 2-bit group-wise GEMM      */
 } wq_op_t;
 
 /* Bytes of the packed weight for `op` at this shape (G is used by
- * WQ_OP_Q4G only).  Returns 0 for an invalid op or shape.  Pure function. */
+ * WQ_OP_Q4G and WQ_OP_Q2G only).  Returns 0 for an invalid op or shape.  Pure function. */
 size_t wq_packed_bytes(int op, int K, int N, int G);
 
 /* ---------------------------------------------------------------- 3-bit -- */
@@ -177,6 +178,31 @@ int wq_gemm_q4_group(const void* X, const void* packed, const void* scales, void
 int wq_gemm_q4_group_zp(const void* X, const void* packed, const void* scales, const void* zeros,
                         void* Y, int M, int K, int N, int G, void* stream);
 
+/* ---------------------------------------------------------------- 2-bit -- */
+
+/* Re-lay out a 2-bit weight qweight [K/16, N] int32 (row 16r + j in bits
+ * 2j, 2j+1 of word r, unsigned values 0..3), its rows taken in the order
+ * perm lists (device array [K], from wq_q4_act_order_perm, or NULL for the
+ * stored order).  packed: wq_packed_bytes(WQ_OP_Q2G, K, N, G) bytes, written;
+ * it also holds the inverse of perm as a table of K uint16.
+ * Rules: K % G == 0, G a power of two >= 32, K <= 32768, N % 4 == 0. */
+int wq_prepack_q2(const int32_t* qweight, const int32_t* perm, void* packed, int K, int N, int G,
+                  void* stream);
+
+/* Asymmetric group-wise 2-bit GEMM:
+ *   Y[m, n] = sum_k X[m, k] * (u[k, n] - zero[g, n]) * scale[g, n],
+ *   g = g_idx[k] (through the row order inside the packed weight) or k / G,
+ * u the stored value 0..3.  ("GPTQ CUDA kernel walkthrough", yelogs.com:
+ * 2-bit codes as a lower bit width to support; "Quantization CUDA",
+ * tom-jerr.github.io, section "量化粒度": x = S (q - Z), each group its own S
+ * and Z.)  X [M, K] fp16; packed: from wq_prepack_q2; scales and zeros
+ * [K/G, N] fp16; Y [M, N] fp16, written (fp32 accumulation; the zero is
+ * applied once per group to the accumulated sums).
+ * Rules: as wq_prepack_q2, M >= 1; X, packed, scales and zeros 16-byte
+ * aligned. */
+int wq_gemm_q2_group_zp(const void* X, const void* packed, const void* scales, const void* zeros,
+                        void* Y, int M, int K, int N, int G, void* stream);
+
 /* ----------------------------------------------------------------- W8A8 -- */
 
 /* W8A8 dynamic-quantisation GEMM:
@@ -240,6 +266,9 @@ int wq_gemm_int8_mixed(const void* X, const int8_t* Wq, const float* Sw, float t
 int wq_unpack_q3(const void* packed, int8_t* codes, int K, int N, void* stream);
 int wq_unpack_q8(const void* packed, int8_t* codes, int K, int N, void* stream);
 int wq_unpack_q4(const void* packed, const int32_t* perm, int8_t* codes, int K, int N, int G,
+                 void* stream);
+/* wq_unpack_q2: the values u (0..3) in the original row order. */
+int wq_unpack_q2(const void* packed, const int32_t* perm, int8_t* codes, int K, int N, int G,
                  void* stream);
 
 /* ---------------------------------------------------- measurement only -- */

@@ -92,6 +92,22 @@ def test_q4_validation(L):
     assert g(P, None, None, 64, 16, 32, None) == wq.WQ_ERR_NULL
 
 
+def test_q2_validation(L):
+    assert L.wq_packed_bytes(wq.WQ_OP_Q2G, 4096, 11008, 128) == 4096 // 16 * 11008 * 4 + 4096 * 2
+    assert L.wq_packed_bytes(wq.WQ_OP_Q2G, 4096, 11008, 96) == 0
+    f = L.wq_gemm_q2_group_zp
+    assert f(P, P, P, None, P, 1, 4096, 11008, 128, None) == wq.WQ_ERR_NULL      # zeros
+    assert f(P, P, P, P, P, 1, 4096, 11006, 128, None) == wq.WQ_ERR_SHAPE       # N % 4
+    assert f(P, P, P, P, P, 1, 4000, 11008, 128, None) == wq.WQ_ERR_SHAPE       # K % G
+    assert f(P, P, P, P, P, 1, 4096, 11008, 16, None) == wq.WQ_ERR_SHAPE        # G >= 32
+    assert f(P, P, P, P, P, 0, 4096, 11008, 128, None) == wq.WQ_ERR_SHAPE       # M
+    assert f(P, P, P, P, P, 1, 32768 + 128, 64, 128, None) == wq.WQ_ERR_SHAPE   # K bound
+    assert f(P, P, P, P_MIS, P, 1, 4096, 11008, 128, None) == wq.WQ_ERR_ALIGN
+    assert L.wq_prepack_q2(P, None, None, 64, 16, 32, None) == wq.WQ_ERR_NULL
+    assert L.wq_prepack_q2(P, None, P, 48, 16, 32, None) == wq.WQ_ERR_SHAPE
+    assert L.wq_unpack_q2(None, None, P, 64, 64, 32, None) == wq.WQ_ERR_NULL
+
+
 def test_w8a8_validation(L):
     f = L.wq_gemm_w8a8
     assert f(P, P, P, P, P, None, None, 256, 8192, 8192, None) == wq.WQ_ERR_NULL

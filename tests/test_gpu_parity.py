@@ -364,6 +364,64 @@ def test_q4_zp_zero_eight_matches_symmetric_kernel(wq):
     assert torch.equal(wq.gemm_q4_group_zp(X, packed, S, z8, 128), wq.gemm_q4_group(X, packed, S, 128))
 
 
+# ================================================================= 2-bit ==
+
+@pytest.mark.parametrize("K,N,G,act", [(4096, 11008, 128, True), (4096, 11008, 128, False)])
+def test_unpack_q2_bit_exact(wq, K, N, G, act):
+    d = synth.gen_q2_zp(1, K, N, G, seed=71 + int(act), act_order=act)
+    packed, perm = wq.prepare_q2(cu(d["qweight"]), d["g_idx"] if act else None, G)
+    u = wq.unpack_q2(packed, K, N, G, perm)
+    torch.cuda.synchronize()
+    assert np.array_equal(u.cpu().numpy().astype(np.int64), oracle.unpack_u2(d["qweight"]))
+
+
+@pytest.mark.parametrize("M,K,N,G,act", [
+    (1, 4096, 11008, 128, True), (2, 4096, 11008, 128, False), (4, 4096, 11008, 64, True),
+    (8, 4096, 11008, 256, False), (1, 4096, 4096, 32, True),
+    (3, 544, 20, 32, False),       # ragged: a partial 256-row block, N % 16 != 0
+    (5, 1280, 132, 128, True),     # two groups per block, 9 panels
+    (1, 8192, 64, 512, False),     # a group spans two blocks
+])
+def test_q2_vs_oracle(wq, M, K, N, G, act):
+    d = synth.gen_q2_zp(M, K, N, G, seed=synth.SEEDS["q2_zp"] + K + N + G, act_order=act)
+    packed, _ = wq.prepare_q2(cu(d["qweight"]), d["g_idx"] if act else None, G)
+    Y = wq.gemm_q2_group_zp(cu(d["X"]), packed, cu(d["scales"]), cu(d["zeros"]), G)
+    ref = oracle.gemm_q2_zp(d["X"], d["qweight"], d["scales"], d["zeros"], d["g_idx"], G)
+    assert_tol(host(Y), ref, f"q2 {M}x{K}x{N} G{G} act={act}")
+
+
+def test_q2_integer_exact_and_one_hot(wq):
+    # Scales 1, integer zeros and small integer X: every fp32 partial sum is an
+    # exact integer, so the result equals the oracle's after one fp16 rounding.
+    rng = np.random.default_rng(72)
+    M, K, N, G = 3, 1024, 48, 64
+    u = rng.integers(0, 4, size=(K, N))
+    z = rng.integers(0, 4, size=(K // G, N)).astype(np.float16)
+    s = np.ones((K // G, N), np.float16)
+    X = rng.integers(-3, 4, size=(M, K)).astype(np.float16)
+    g_idx = rng.permutation(np.repeat(np.arange(K // G), G)).astype(np.int32)
+    qw = synth.pack_q2(u)
+    packed, _ = wq.prepare_q2(cu(qw), g_idx, G)
+    Y = host(wq.gemm_q2_group_zp(cu(X), packed, cu(s), cu(z), G))
+    ref = oracle.gemm_q2_zp(X, qw, s, z, g_idx, G).astype(np.float16).astype(np.float64)
+    assert np.array_equal(Y, ref)
+    # One-hot rows: y[n] = u[k, n] - zero[g_idx[k], n] exactly, row by row.
+    for k in (0, 7, 8, 15, 31, 32, 255, 256, 700, 1023):
+        x = np.zeros((1, K), np.float16)
+        x[0, k] = 1
+        y = host(wq.gemm_q2_group_zp(cu(x), packed, cu(s), cu(z), G))[0]
+        assert np.array_equal(y, u[k].astype(np.float64) - z[g_idx[k]].astype(np.float64)), k
+
+
+def test_q2_deterministic(wq):
+    d = synth.gen_q2_zp(2, 4096, 1024, 128, seed=73, act_order=True)
+    packed, _ = wq.prepare_q2(cu(d["qweight"]), d["g_idx"], 128)
+    X, S, Z = cu(d["X"]), cu(d["scales"]), cu(d["zeros"])
+    first = wq.gemm_q2_group_zp(X, packed, S, Z, 128)
+    for _ in range(20):
+        assert torch.equal(wq.gemm_q2_group_zp(X, packed, S, Z, 128), first)
+
+
 # ================================================================== W8A8 ==
 
 def _w8a8_check(wq, d):

@@ -12,6 +12,8 @@ products read a packed copy of the weight made once by ``prepack_*``:
 * ``q4_act_order_perm(g_idx, K, G)`` -> (perm, invperm) host int32 arrays
 * ``prepack_q4(qweight, perm, G)`` / ``gemm_q4_group(X, packed, scales, invperm, G)`` -> Y
   (``prepare_q4(qweight, g_idx, G)`` does the act-order preparation in one go)
+* ``prepare_q2(qweight, g_idx, G)`` / ``gemm_q2_group_zp(X, packed, scales, zeros, G)`` -> Y
+  (asymmetric 2-bit, 16 codes per int32 along K)
 * ``gemm_w8a8(X, Wq, Sw, want_acc=False)``  -> (Y bf16, Xq, Sx, acc | None)
 * ``unpack_q3`` / ``unpack_q8`` / ``unpack_q4``: codes held by a packed weight
 * ``calib_empty`` / ``calib_stream_read``: timing references (no product)
@@ -31,7 +33,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "wq.h")
 
 WQ_OK, WQ_ERR_NULL, WQ_ERR_SHAPE, WQ_ERR_ALIGN, WQ_ERR_DTYPE, WQ_ERR_HIP = 0, 1, 2, 3, 4, 6
 WQ_F32, WQ_F16 = 0, 1
-WQ_OP_Q3, WQ_OP_Q4G, WQ_OP_Q8G = 0, 1, 2
+WQ_OP_Q3, WQ_OP_Q4G, WQ_OP_Q8G, WQ_OP_Q2G = 0, 1, 2, 3
 
 _vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 _SIGNATURES = {
@@ -48,6 +50,9 @@ _SIGNATURES = {
     "wq_gemm_w8a8_smooth": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
     "wq_gemm_int8_mixed": (_i, [_vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _i, _i, _i, _vp]),
+    "wq_prepack_q2": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
+    "wq_gemm_q2_group_zp": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
+    "wq_unpack_q2": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
     "wq_unpack_q3": (_i, [_vp, _vp, _i, _i, _vp]),
     "wq_unpack_q8": (_i, [_vp, _vp, _i, _i, _vp]),
     "wq_unpack_q4": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
@@ -311,6 +316,64 @@ def unpack_q4(packed, K: int, N: int, group_size: int = 128, perm=None):
         _need(perm, "perm", torch.int32, (K,), dev)
     codes = torch.empty((K, N), dtype=torch.int8, device=dev)
     _check("wq_unpack_q4", lib().wq_unpack_q4(_ptr(packed), _ptr(perm), _ptr(codes), K, N,
+                                              group_size, _stream(dev)))
+    return codes
+
+
+# ----------------------------------------------------------------- 2-bit --
+
+def prepack_q2(qweight, perm=None, group_size=128):
+    """Device: re-lay out a 2-bit weight [K/16, N], rows in ``perm`` order (or as stored)."""
+    R, N = qweight.shape
+    K = 16 * R
+    dev = qweight.device
+    _need(qweight, "qweight", torch.int32, (R, N), dev)
+    if perm is not None:
+        _need(perm, "perm", torch.int32, (K,), dev)
+    out = _packed(WQ_OP_Q2G, K, N, group_size, dev)
+    st = lib().wq_prepack_q2(_ptr(qweight), _ptr(perm), _ptr(out), K, N, group_size, _stream(dev))
+    _check("wq_prepack_q2", st)
+    return out
+
+
+def prepare_q2(qweight, g_idx, group_size=128):
+    """Act-order preparation and re-layout of a 2-bit weight: ``(packed, perm_dev)``."""
+    if g_idx is None:
+        return prepack_q2(qweight, None, group_size), None
+    K = 16 * qweight.shape[0]
+    perm, _ = q4_act_order_perm(g_idx, K, group_size)
+    perm_d = torch.from_numpy(perm).to(qweight.device)
+    return prepack_q2(qweight, perm_d, group_size), perm_d
+
+
+def gemm_q2_group_zp(X, packed, scales, zeros, group_size=128, Y=None):
+    """Y[m, n] = sum_k X[m, k] * (u[k, n] - zero[g, n]) * scale[g, n] (asymmetric 2-bit)."""
+    squeeze = X.dim() == 1
+    X2 = X.reshape(1, -1) if squeeze else X
+    M, K = X2.shape
+    N = scales.shape[1]
+    dev = X.device
+    _need(X2, "X", torch.float16, (M, K), dev)
+    _need_packed(packed, WQ_OP_Q2G, K, N, group_size, dev)
+    _need(scales, "scales", torch.float16, (K // group_size, N), dev)
+    _need(zeros, "zeros", torch.float16, (K // group_size, N), dev)
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    _need(Y, "Y", torch.float16, (M, N), dev)
+    st = lib().wq_gemm_q2_group_zp(_ptr(X2), _ptr(packed), _ptr(scales), _ptr(zeros), _ptr(Y), M, K,
+                                   N, group_size, _stream(dev))
+    _check("wq_gemm_q2_group_zp", st)
+    return Y.reshape(N) if squeeze else Y
+
+
+def unpack_q2(packed, K: int, N: int, group_size: int = 128, perm=None):
+    """The values u (0..3) a packed 2-bit weight holds, in the original row order."""
+    dev = packed.device
+    _need_packed(packed, WQ_OP_Q2G, K, N, group_size, dev)
+    if perm is not None:
+        _need(perm, "perm", torch.int32, (K,), dev)
+    codes = torch.empty((K, N), dtype=torch.int8, device=dev)
+    _check("wq_unpack_q2", lib().wq_unpack_q2(_ptr(packed), _ptr(perm), _ptr(codes), K, N,
                                               group_size, _stream(dev)))
     return codes
 

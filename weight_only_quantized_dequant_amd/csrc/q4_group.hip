@@ -29,13 +29,23 @@
 // 1 KB: lane l owns 16 bytes = 4 words, word j holding the 8 codes of column
 // 16 p + l % 16, rows 128 b + 32 j + 8 (l / 16) .. +7, row +e in nibble e —
 // the B operand of MFMA step j of the block, one 1 KB load per wave.
+//
+// 2-bit codes (named on "GPTQ CUDA kernel walkthrough", yelogs.com, as a
+// lower bit width to support) run through the same kernel in the asymmetric
+// form: blocks of 256 rows, word j of a lane holding the 16 codes of steps
+// 2j and 2j + 1 (rows 256 b + 64 j + 8 (l / 16) + e and 32 rows further),
+// placed so that (w >> 2i) & 0x00030003 is the operand pair i: pairs 0..3
+// are step 2j's rows (e, e + 4), pairs 4..7 step 2j + 1's.
 #include "wq_device.hpp"
 #include "wq_internal.h"
 
 namespace wq {
 
 constexpr int kQ4Panel = 16;   // columns per panel (one MFMA tile)
-constexpr int kQ4Block = 128;  // rows per block (4 MFMA steps of 32)
+constexpr int kQ4Block = 128;  // rows per 4-bit block (4 MFMA steps of 32)
+// Rows per 1 KB block: 128 four-bit or 256 two-bit codes per 16 columns.
+template <int BITS>
+constexpr int block_rows() { return BITS == 4 ? 128 : 256; }
 constexpr int kQ4Ring = 4;     // blocks in flight per wave
 constexpr int kQ4MaxRun = 8;   // panels a workgroup walks at most
 constexpr int kQ4Threads = 512;             // 8 waves: two per SIMD
@@ -49,23 +59,31 @@ constexpr int kQ4RowPad = 32;
 // packed weight is the blocks, then the row table: K uint16, entry k = the
 // group-order row of original row k (the inverse of perm), padded to 16 B.
 static size_t q4_block_bytes(const PanelPlan& p) { return (size_t)p.npanels * p.u * 1024; }
-PanelPlan plan_q4(int K, int N, int G) {
-  (void)G;
+static PanelPlan plan_blocks(int K, int N, int rows) {
   PanelPlan p{};
   p.P = kQ4Panel;
   p.cpp = 0;
   p.npanels = (N + kQ4Panel - 1) / kQ4Panel;
-  p.u = (K + kQ4Block - 1) / kQ4Block;
+  p.u = (K + rows - 1) / rows;
   p.nsa = 0;
   p.bw = 0;
   p.packed_bytes = q4_block_bytes(p) + ((size_t)K * 2 + 15) / 16 * 16;
   return p;
 }
+PanelPlan plan_q4(int K, int N, int G) {
+  (void)G;
+  return plan_blocks(K, N, block_rows<4>());
+}
+// 2-bit: the same structure with 256-row blocks.
+PanelPlan plan_q2(int K, int N, int G) {
+  (void)G;
+  return plan_blocks(K, N, block_rows<2>());
+}
 
-// Rows of X staged per launch: the LDS copies of X (MT rows of u * 128
-// halves plus padding) stay <= 96 KB.
-int q4_max_mt(int K) {
-  const size_t kb = (size_t)(K + kQ4Block - 1) / kQ4Block * kQ4Block + kQ4RowPad;
+// Rows of X staged per launch: the LDS copies of X (MT rows of the padded
+// block rows plus padding) stay <= 96 KB.
+static int max_mt(int K, int rows) {
+  const size_t kb = (size_t)(K + rows - 1) / rows * rows + kQ4RowPad;
   int mt = 8;
   while (mt > 1 && (size_t)mt * kb * 2 > 98304) mt /= 2;
   return mt;
@@ -79,6 +97,16 @@ __device__ __forceinline__ void q4_mfma_pairs(uint32_t w, h2 out[4]) {
   out[2] = as_h2((w >> 8) & 0x000F000Fu);
   out[3] = as_h2((w >> 12) & 0x000F000Fu);
 }
+// 2-bit: the operand of step 2j + H of word j: pairs 4H .. 4H + 3, i.e.
+// (w >> 2i) & 0x00030003, each half an exact subnormal u * 2^-24.
+template <int H>
+__device__ __forceinline__ void q2_mfma_pairs(uint32_t w, h2 out[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = as_h2((w >> (2 * (4 * H + i))) & 0x00030003u);
+}
+// Code position (0..15) of row e of step 2j + H inside word j.
+__host__ __device__ constexpr int q2_pos(int h, int e) { return e < 4 ? e + 4 * h : e + 4 + 4 * h; }
+
 // Position of row e (0..7) of an octet among the 8 halves of an operand.
 __device__ __forceinline__ int q4_pos(int e) { return 2 * (e & 3) + (e >> 2); }
 
@@ -117,6 +145,42 @@ __global__ __launch_bounds__(kThreads) void q4_prepack_kernel(const uint32_t* __
   }
 }
 
+// 2-bit: qw [K/16, N], row 16 r + j in bits 2j, 2j + 1 of word r.  Piece
+// (panel, block b, lane l), word j: the rows of steps 2j + h (h = 0, 1),
+// 256 b + 64 j + 32 h + 8 (l / 16) + e, at code position q2_pos(h, e).
+__global__ __launch_bounds__(kThreads) void q2_prepack_kernel(const uint32_t* __restrict__ qw,
+                                                              const int* __restrict__ perm,
+                                                              uint32_t* __restrict__ out,
+                                                              uint16_t* __restrict__ table, int K,
+                                                              int N, int nb, int npanels) {
+  constexpr int BR = block_rows<2>();
+  const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  for (size_t i = idx; i < (size_t)K; i += (size_t)gridDim.x * kThreads)
+    table[perm ? perm[i] : (int)i] = (uint16_t)i;
+  if (idx >= (size_t)npanels * nb * 64) return;
+  const int l = (int)(idx % 64);
+  const size_t pb = idx / 64;
+  const int b = (int)(pb % nb), panel = (int)(pb / nb);
+  const int n = panel * kQ4Panel + l % 16;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t word = 0;  // padding rows and columns: u = 0, met by x = 0 or dropped
+    if (n < N) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = BR * b + 64 * j + 32 * h + 8 * (l / 16) + e;
+          if (i >= K) continue;
+          const int src = perm ? perm[i] : i;
+          const uint32_t sw = qw[(size_t)(src >> 4) * N + n];
+          word |= ((sw >> (2 * (src & 15))) & 3u) << (2 * q2_pos(h, e));
+        }
+    }
+    out[idx * 4 + j] = word;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // The fused product.
 //
@@ -129,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void q4_prepack_kernel(const uint32_t* __
 // ZP: asymmetric form, w = (u - zero) * scale with an fp16 zero per (group,
 // column) ("Quantization CUDA", tom-jerr.github.io, sections "量化粒度" and
 // "Marlin 格式"); without it the offset is the fixed 8 of the symmetric codes.
-template <int MT, int NSC, bool ZP>
+template <int MT, int NSC, bool ZP, int BITS>
 __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
     const _Float16* __restrict__ X, const uint8_t* __restrict__ Wp,
     const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
@@ -137,11 +201,14 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
   typedef _Float16 h8 __attribute__((ext_vector_type(8)));
   typedef float f4 __attribute__((ext_vector_type(4)));
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int rs = nb * kQ4Block + kQ4RowPad;                           // halves per LDS row of X
+  constexpr int BR = block_rows<BITS>();  // rows per block
+  constexpr int SPB = BR / 32;            // MFMA steps per block
+  static_assert(BITS == 4 || ZP, "2-bit codes come with zero points");
+  const int rs = nb * BR + kQ4RowPad;                                  // halves per LDS row of X
   const int xhalves = rs * MT;                                          // halves of X in LDS
   _Float16* xa = reinterpret_cast<_Float16*>(smem);                     // [MT][octet][8], padded rows
   float* red = reinterpret_cast<float*>(smem + (size_t)xhalves * 2);  // [run][wave][MT][16]
-  float* sg = red + kQ4MaxRun * kQ4Waves * MT * 16;                    // [K / G][8] group sums
+  float* sg = red + kQ4MaxRun * kQ4Waves * MT * 16;  // [groups of nb * BR rows][8] group sums
 
   const int t = threadIdx.x, lane = t & 63;
   // Uniform across the wave: keeps the block range and cursors in scalar
@@ -153,7 +220,7 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
 
   // Blocks of this wave: a group-aligned contiguous range.
   const int spg = G / 32;  // MFMA steps per group
-  const int bpg = G >= kQ4Block ? G / kQ4Block : 1;
+  const int bpg = G >= BR ? G / BR : 1;
   const int nsplit = nb / bpg;
   const int blo = (wave * nsplit / kQ4Waves) * bpg, bhi = ((wave + 1) * nsplit / kQ4Waves) * bpg;
   const int nbw = bhi - blo;
@@ -268,7 +335,7 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
   {
     const h2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
     const int octs = G / 8, part = lane & 7;
-    const int g0 = blo * kQ4Block / G, ng = nbw * kQ4Block / G;
+    const int g0 = blo * BR / G, ng = nbw * BR / G;
     for (int task = lane >> 3; task < ng * MT; task += 8) {
       const int g = g0 + task / MT, m = task % MT;
       const _Float16* row = xa + (size_t)m * rs + (size_t)g * G;
@@ -293,36 +360,34 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
   int cp = 0, cb = blo;  // compute cursor: panel of the run, block
   // Operands of X for the block about to be multiplied, read one block ahead
   // (X is the same for every panel, so after a wave's last block comes blo).
-  h8 apf[4];
+  h8 apf[SPB];
   if (nbw > 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) apf[j] = *reinterpret_cast<const h8*>(xrow + (16 * blo + 4 * j) * 8);
+    for (int j = 0; j < SPB; ++j) apf[j] = *reinterpret_cast<const h8*>(xrow + ((BR / 8) * blo + 4 * j) * 8);
   }
   auto compute = [&](const u32x4& w, const uint32_t (&sc)[NSC], const uint32_t (&zq)[NZ]) {
     const int pi = cp, b = cb;
-    h8 a[4];
+    h8 a[SPB];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) a[j] = apf[j];
+    for (int j = 0; j < SPB; ++j) a[j] = apf[j];
     const int bn = b + 1 == bhi ? blo : b + 1;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) apf[j] = *reinterpret_cast<const h8*>(xrow + (16 * bn + 4 * j) * 8);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      h2 pr[4];
-      q4_mfma_pairs(w[j], pr);
+    for (int j = 0; j < SPB; ++j) apf[j] = *reinterpret_cast<const h8*>(xrow + ((BR / 8) * bn + 4 * j) * 8);
+    // MFMA step st of the block; the group it completes, if any, closes.
+    auto mstep = [&](int st, const h2 (&pr)[4]) {
       const h8 bv = {pr[0].x, pr[0].y, pr[1].x, pr[1].y, pr[2].x, pr[2].y, pr[3].x, pr[3].y};
-      if (j & 1)
-        C1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], bv, C1, 0, 0, 0);
+      if (st & 1)
+        C1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[st], bv, C1, 0, 0, 0);
       else
-        C0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], bv, C0, 0, 0, 0);
+        C0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[st], bv, C0, 0, 0, 0);
       bool close;
       int k = 0, g;
       if constexpr (NSC > 1) {
-        close = ((j + 1) % (4 / NSC)) == 0;
-        k = j / (4 / NSC);
+        close = ((st + 1) % (SPB / NSC)) == 0;
+        k = st / (SPB / NSC);
         g = b * NSC + k;
       } else {
-        close = j == 3 && ((b + 1) & (bpg - 1)) == 0;
+        close = st == SPB - 1 && ((b + 1) & (bpg - 1)) == 0;
         g = b >> lbpg;
       }
       if (close) {
@@ -337,6 +402,19 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
           tot[r] = __builtin_fmaf(s, __builtin_fmaf(S[r], zoff, C0[r] + C1[r]), tot[r]);
           C0[r] = C1[r] = 0.0f;
         }
+      }
+    };
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      h2 pr[4];
+      if constexpr (BITS == 4) {
+        q4_mfma_pairs(w[j], pr);
+        mstep(j, pr);
+      } else {
+        q2_mfma_pairs<0>(w[j], pr);
+        mstep(2 * j, pr);
+        q2_mfma_pairs<1>(w[j], pr);
+        mstep(2 * j + 1, pr);
       }
     }
     if (++cb == bhi) {
@@ -406,6 +484,42 @@ __global__ __launch_bounds__(kThreads) void q4_unpack_kernel(const uint8_t* __re
   }
 }
 
+// 2-bit: each piece through q2_mfma_pairs back to the values u (0..3) in the
+// original row order.
+__global__ __launch_bounds__(kThreads) void q2_unpack_kernel(const uint8_t* __restrict__ Wp,
+                                                             const int* __restrict__ perm,
+                                                             int8_t* __restrict__ codes, int K,
+                                                             int N, int nb, int npanels) {
+  constexpr int BR = block_rows<2>();
+  const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= (size_t)npanels * nb * 64) return;
+  const int l = (int)(idx % 64);
+  const size_t pb = idx / 64;
+  const int b = (int)(pb % nb), panel = (int)(pb / nb);
+  const int n = panel * kQ4Panel + l % 16;
+  if (n >= N) return;
+  const u32x4 w = *reinterpret_cast<const u32x4*>(Wp + idx * 16);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      h2 pr[4];
+      if (h == 0)
+        q2_mfma_pairs<0>(w[j], pr);
+      else
+        q2_mfma_pairs<1>(w[j], pr);
+      const int i0 = BR * b + 64 * j + 32 * h + 8 * (l / 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t bits = as_u32(pr[e]);
+        const int ia = i0 + e, ib = i0 + e + 4;
+        if (ia < K) codes[(size_t)(perm ? perm[ia] : ia) * N + n] = (int8_t)(bits & 0xFFFFu);
+        if (ib < K) codes[(size_t)(perm ? perm[ib] : ib) * N + n] = (int8_t)(bits >> 16);
+      }
+    }
+  }
+}
+
 hipError_t launch_q4_prepack(const int32_t* qw, const int32_t* perm, void* out, int K, int N, int G,
                              hipStream_t s) {
   const PanelPlan p = plan_q4(K, N, G);
@@ -428,21 +542,48 @@ hipError_t launch_q4_unpack(const void* packed, const int32_t* perm, int8_t* cod
   return hipGetLastError();
 }
 
-template <int MT, int NSC, bool ZP>
+hipError_t launch_q2_prepack(const int32_t* qw, const int32_t* perm, void* out, int K, int N, int G,
+                             hipStream_t s) {
+  const PanelPlan p = plan_q2(K, N, G);
+  const size_t total = (size_t)p.npanels * p.u * 64;
+  hipLaunchKernelGGL(q2_prepack_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, reinterpret_cast<const uint32_t*>(qw), perm,
+                     reinterpret_cast<uint32_t*>(out),
+                     reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(out) + q4_block_bytes(p)), K,
+                     N, p.u, p.npanels);
+  return hipGetLastError();
+}
+
+hipError_t launch_q2_unpack(const void* packed, const int32_t* perm, int8_t* codes, int K, int N,
+                            int G, hipStream_t s) {
+  const PanelPlan p = plan_q2(K, N, G);
+  const size_t total = (size_t)p.npanels * p.u * 64;
+  hipLaunchKernelGGL(q2_unpack_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, reinterpret_cast<const uint8_t*>(packed), perm, codes, K,
+                     N, p.u, p.npanels);
+  return hipGetLastError();
+}
+
+template <int MT, int NSC, bool ZP, int BITS>
 static hipError_t launch_q4_t(const void* X, const void* packed, const void* scales,
                               const void* zeros, void* Y, int M, int K, int N, int G,
                               const PanelPlan& p, hipStream_t s) {
+  constexpr int BR = block_rows<BITS>();
   const int cus = device_cus();
   int grid = p.npanels < cus ? p.npanels : cus;
   if ((p.npanels + grid - 1) / grid > kQ4MaxRun) grid = (p.npanels + kQ4MaxRun - 1) / kQ4MaxRun;
-  const size_t lds = ((size_t)p.u * kQ4Block + kQ4RowPad) * MT * 2 +
-                     (size_t)kQ4MaxRun * kQ4Waves * MT * 16 * 4 + (size_t)(K / G) * 8 * 4;
+  // Group sums: one entry per group of the padded rows p.u * BR (a ragged
+  // last block closes groups past K / G, whose rows are all padding).
+  const size_t ngroups = ((size_t)p.u * BR + G - 1) / G;
+  const size_t lds = ((size_t)p.u * BR + kQ4RowPad) * MT * 2 +
+                     (size_t)kQ4MaxRun * kQ4Waves * MT * 16 * 4 + ngroups * 8 * 4;
   if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&q4_mfma_kernel<MT, NSC, ZP>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&q4_mfma_kernel<MT, NSC, ZP, BITS>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((q4_mfma_kernel<MT, NSC, ZP>), dim3(grid), dim3(kQ4Threads), lds, s,
+  hipLaunchKernelGGL((q4_mfma_kernel<MT, NSC, ZP, BITS>), dim3(grid), dim3(kQ4Threads), lds, s,
                      reinterpret_cast<const _Float16*>(X), reinterpret_cast<const uint8_t*>(packed),
                      reinterpret_cast<const _Float16*>(scales),
                      reinterpret_cast<const _Float16*>(zeros), reinterpret_cast<_Float16*>(Y), M,
@@ -450,27 +591,39 @@ static hipError_t launch_q4_t(const void* X, const void* packed, const void* sca
   return hipGetLastError();
 }
 
-template <int MT, bool ZP>
+// Closes per block (NSC): groups of G rows in a block of BR rows, at least 1.
+template <int MT, bool ZP, int BITS>
 static hipError_t launch_q4_zp(const void* X, const void* packed, const void* scales,
                                const void* zeros, void* Y, int M, int K, int N, int G,
                                const PanelPlan& p, hipStream_t s) {
-  if (G == 32) return launch_q4_t<MT, 4, ZP>(X, packed, scales, zeros, Y, M, K, N, G, p, s);
-  if (G == 64) return launch_q4_t<MT, 2, ZP>(X, packed, scales, zeros, Y, M, K, N, G, p, s);
-  return launch_q4_t<MT, 1, ZP>(X, packed, scales, zeros, Y, M, K, N, G, p, s);
+  constexpr int BR = block_rows<BITS>();
+  const int nsc = G >= BR ? 1 : BR / G;
+  if constexpr (BITS == 2) {
+    if (nsc == 8) return launch_q4_t<MT, 8, ZP, BITS>(X, packed, scales, zeros, Y, M, K, N, G, p, s);
+  }
+  if (nsc == 4) return launch_q4_t<MT, 4, ZP, BITS>(X, packed, scales, zeros, Y, M, K, N, G, p, s);
+  if (nsc == 2) return launch_q4_t<MT, 2, ZP, BITS>(X, packed, scales, zeros, Y, M, K, N, G, p, s);
+  return launch_q4_t<MT, 1, ZP, BITS>(X, packed, scales, zeros, Y, M, K, N, G, p, s);
 }
 
-template <int MT>
+template <int MT, int BITS>
 static hipError_t launch_q4_mt(const void* X, const void* packed, const void* scales,
                                const void* zeros, void* Y, int M, int K, int N, int G,
                                const PanelPlan& p, hipStream_t s) {
-  return zeros ? launch_q4_zp<MT, true>(X, packed, scales, zeros, Y, M, K, N, G, p, s)
-               : launch_q4_zp<MT, false>(X, packed, scales, zeros, Y, M, K, N, G, p, s);
+  if constexpr (BITS == 2)
+    return launch_q4_zp<MT, true, 2>(X, packed, scales, zeros, Y, M, K, N, G, p, s);
+  else
+    return zeros ? launch_q4_zp<MT, true, 4>(X, packed, scales, zeros, Y, M, K, N, G, p, s)
+                 : launch_q4_zp<MT, false, 4>(X, packed, scales, zeros, Y, M, K, N, G, p, s);
 }
 
-hipError_t launch_q4_group(const void* X, const void* packed, const void* scales,
-                           const void* zeros, void* Y, int M, int K, int N, int G, hipStream_t s) {
-  const PanelPlan p = plan_q4(K, N, G);
-  const int mtmax = q4_max_mt(K);
+template <int BITS>
+static hipError_t launch_blocks(const void* X, const void* packed, const void* scales,
+                                const void* zeros, void* Y, int M, int K, int N, int G,
+                                hipStream_t s) {
+  constexpr int BR = block_rows<BITS>();
+  const PanelPlan p = plan_blocks(K, N, BR);
+  const int mtmax = max_mt(K, BR);
   for (int m0 = 0; m0 < M; m0 += mtmax) {
     const int mc = (M - m0) < mtmax ? (M - m0) : mtmax;
     const int mt = mc == 1 ? 1 : (mc == 2 ? 2 : (mc <= 4 ? 4 : 8));
@@ -478,14 +631,24 @@ hipError_t launch_q4_group(const void* X, const void* packed, const void* scales
     void* Yc = reinterpret_cast<char*>(Y) + (size_t)m0 * N * 2;
     hipError_t e;
     switch (mt) {
-      case 1: e = launch_q4_mt<1>(Xc, packed, scales, zeros, Yc, mc, K, N, G, p, s); break;
-      case 2: e = launch_q4_mt<2>(Xc, packed, scales, zeros, Yc, mc, K, N, G, p, s); break;
-      case 4: e = launch_q4_mt<4>(Xc, packed, scales, zeros, Yc, mc, K, N, G, p, s); break;
-      default: e = launch_q4_mt<8>(Xc, packed, scales, zeros, Yc, mc, K, N, G, p, s); break;
+      case 1: e = launch_q4_mt<1, BITS>(Xc, packed, scales, zeros, Yc, mc, K, N, G, p, s); break;
+      case 2: e = launch_q4_mt<2, BITS>(Xc, packed, scales, zeros, Yc, mc, K, N, G, p, s); break;
+      case 4: e = launch_q4_mt<4, BITS>(Xc, packed, scales, zeros, Yc, mc, K, N, G, p, s); break;
+      default: e = launch_q4_mt<8, BITS>(Xc, packed, scales, zeros, Yc, mc, K, N, G, p, s); break;
     }
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t launch_q4_group(const void* X, const void* packed, const void* scales,
+                           const void* zeros, void* Y, int M, int K, int N, int G, hipStream_t s) {
+  return launch_blocks<4>(X, packed, scales, zeros, Y, M, K, N, G, s);
+}
+
+hipError_t launch_q2_group(const void* X, const void* packed, const void* scales,
+                           const void* zeros, void* Y, int M, int K, int N, int G, hipStream_t s) {
+  return launch_blocks<2>(X, packed, scales, zeros, Y, M, K, N, G, s);
 }
 
 }  // namespace wq

@@ -63,6 +63,14 @@ int check_q4(int K, int N, int G) {
   return WQ_OK;
 }
 
+// 2-bit: the 4-bit limits; the packed weight is a quarter of K*N bytes.
+int check_q2(int K, int N, int G) {
+  if (G < 32 || !pow2(G) || K < G || K % G || N < 4 || N % 4) return WQ_ERR_SHAPE;
+  if (K > 32768) return WQ_ERR_SHAPE;  // X staged in LDS; 16-bit row table
+  if ((long long)(K / 16) * N * 4 > kMaxBytes / 2) return WQ_ERR_SHAPE;
+  return WQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -72,6 +80,7 @@ size_t wq_packed_bytes(int op, int K, int N, int G) {
     case WQ_OP_Q3: return check_q3(K, N) ? 0 : wq::plan_q3(K, N).packed_bytes;
     case WQ_OP_Q4G: return check_q4(K, N, G) ? 0 : wq::plan_q4(K, N, G).packed_bytes;
     case WQ_OP_Q8G: return check_q8(K, N) ? 0 : wq::plan_q8(K, N).packed_bytes;
+    case WQ_OP_Q2G: return check_q2(K, N, G) ? 0 : wq::plan_q2(K, N, G).packed_bytes;
     default: return 0;
   }
 }
@@ -194,6 +203,35 @@ int wq_unpack_q4(const void* packed, const int32_t* perm, int8_t* codes, int K, 
   if (int st = check_q4(K, N, G)) return st;
   if (!aligned16(packed)) return WQ_ERR_ALIGN;
   return hip_status(wq::launch_q4_unpack(packed, perm, codes, K, N, G, as_stream(stream)));
+}
+
+// ------------------------------------------------------------------ 2-bit --
+
+int wq_prepack_q2(const int32_t* qweight, const int32_t* perm, void* packed, int K, int N, int G,
+                  void* stream) {
+  if (!qweight || !packed) return WQ_ERR_NULL;
+  if (int st = check_q2(K, N, G)) return st;
+  if (!aligned16(qweight) || !aligned16(packed)) return WQ_ERR_ALIGN;
+  return hip_status(wq::launch_q2_prepack(qweight, perm, packed, K, N, G, as_stream(stream)));
+}
+
+int wq_gemm_q2_group_zp(const void* X, const void* packed, const void* scales, const void* zeros,
+                        void* Y, int M, int K, int N, int G, void* stream) {
+  if (!X || !packed || !scales || !zeros || !Y) return WQ_ERR_NULL;
+  if (int st = check_q2(K, N, G)) return st;
+  if (M < 1) return WQ_ERR_SHAPE;
+  if ((long long)M * K * 2 > kMaxBytes) return WQ_ERR_SHAPE;
+  if (!aligned16(X) || !aligned16(packed) || !aligned16(scales) || !aligned16(zeros))
+    return WQ_ERR_ALIGN;
+  return hip_status(wq::launch_q2_group(X, packed, scales, zeros, Y, M, K, N, G, as_stream(stream)));
+}
+
+int wq_unpack_q2(const void* packed, const int32_t* perm, int8_t* codes, int K, int N, int G,
+                 void* stream) {
+  if (!packed || !codes) return WQ_ERR_NULL;
+  if (int st = check_q2(K, N, G)) return st;
+  if (!aligned16(packed)) return WQ_ERR_ALIGN;
+  return hip_status(wq::launch_q2_unpack(packed, perm, codes, K, N, G, as_stream(stream)));
 }
 
 // ------------------------------------------------------------------- W8A8 --

@@ -34,8 +34,8 @@ struct PanelPlan {
 
 PanelPlan plan_q8(int K, int N);
 PanelPlan plan_q4(int K, int N, int G);
+PanelPlan plan_q2(int K, int N, int G);
 PanelPlan plan_q3(int K, int N);
-int q4_max_mt(int K);
 
 hipError_t launch_q8_prepack(const int8_t* W, void* packed, int K, int N, hipStream_t s);
 hipError_t launch_q8_group(const void* X, const void* packed, const float* scales, void* Y, int M,
@@ -57,6 +57,13 @@ hipError_t launch_q4_prepack(const int32_t* qw, const int32_t* perm, void* packe
 hipError_t launch_q4_group(const void* X, const void* packed, const void* scales,
                            const void* zeros, void* Y, int M, int K, int N, int G, hipStream_t s);
 hipError_t launch_q4_unpack(const void* packed, const int32_t* perm, int8_t* codes, int K, int N,
+                            int G, hipStream_t s);
+// 2-bit, asymmetric only (zeros required): the 4-bit kernel with 256-row blocks.
+hipError_t launch_q2_prepack(const int32_t* qw, const int32_t* perm, void* packed, int K, int N,
+                             int G, hipStream_t s);
+hipError_t launch_q2_group(const void* X, const void* packed, const void* scales,
+                           const void* zeros, void* Y, int M, int K, int N, int G, hipStream_t s);
+hipError_t launch_q2_unpack(const void* packed, const int32_t* perm, int8_t* codes, int K, int N,
                             int G, hipStream_t s);
 
 // smooth: nullptr, or the SmoothQuant factor s [K] (X is divided by it).
