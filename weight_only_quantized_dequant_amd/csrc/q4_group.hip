@@ -97,12 +97,23 @@ __device__ __forceinline__ void q4_mfma_pairs(uint32_t w, h2 out[4]) {
   out[2] = as_h2((w >> 8) & 0x000F000Fu);
   out[3] = as_h2((w >> 12) & 0x000F000Fu);
 }
+// The same four pairs as one MFMA operand (built in place, no moves).
+__device__ __forceinline__ u32x4 q4_mfma_operand(uint32_t w) {
+  return u32x4{w & 0x000F000Fu, (w >> 4) & 0x000F000Fu, (w >> 8) & 0x000F000Fu,
+               (w >> 12) & 0x000F000Fu};
+}
 // 2-bit: the operand of step 2j + H of word j: pairs 4H .. 4H + 3, i.e.
 // (w >> 2i) & 0x00030003, each half an exact subnormal u * 2^-24.
 template <int H>
 __device__ __forceinline__ void q2_mfma_pairs(uint32_t w, h2 out[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) out[i] = as_h2((w >> (2 * (4 * H + i))) & 0x00030003u);
+}
+template <int H>
+__device__ __forceinline__ u32x4 q2_mfma_operand(uint32_t w) {
+  constexpr int b = 8 * H;
+  return u32x4{(w >> b) & 0x00030003u, (w >> (b + 2)) & 0x00030003u,
+               (w >> (b + 4)) & 0x00030003u, (w >> (b + 6)) & 0x00030003u};
 }
 // Code position (0..15) of row e of step 2j + H inside word j.
 __host__ __device__ constexpr int q2_pos(int h, int e) { return e < 4 ? e + 4 * h : e + 4 + 4 * h; }
@@ -358,24 +369,23 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
   // One block: 4 MFMA steps (two chains) and the group closes; at the wave's
   // last block of a panel its partial tile goes to LDS.
   int cp = 0, cb = blo;  // compute cursor: panel of the run, block
-  // Operands of X for the block about to be multiplied, read one block ahead
-  // (X is the same for every panel, so after a wave's last block comes blo).
-  h8 apf[SPB];
+  // Operands of X, read one block ahead into the other of two buffers (X is
+  // the same for every panel, so after a wave's last block comes blo).  The
+  // ring below alternates the buffers, so no operand is ever copied.
+  h8 xa0[SPB], xa1[SPB];
   if (nbw > 0) {
 #pragma unroll
-    for (int j = 0; j < SPB; ++j) apf[j] = *reinterpret_cast<const h8*>(xrow + ((BR / 8) * blo + 4 * j) * 8);
+    for (int j = 0; j < SPB; ++j) xa0[j] = *reinterpret_cast<const h8*>(xrow + ((BR / 8) * blo + 4 * j) * 8);
   }
-  auto compute = [&](const u32x4& w, const uint32_t (&sc)[NSC], const uint32_t (&zq)[NZ]) {
+  auto compute = [&](const u32x4& w, const uint32_t (&sc)[NSC], const uint32_t (&zq)[NZ],
+                     const h8 (&a)[SPB], h8 (&nxt)[SPB]) {
     const int pi = cp, b = cb;
-    h8 a[SPB];
-#pragma unroll
-    for (int j = 0; j < SPB; ++j) a[j] = apf[j];
     const int bn = b + 1 == bhi ? blo : b + 1;
 #pragma unroll
-    for (int j = 0; j < SPB; ++j) apf[j] = *reinterpret_cast<const h8*>(xrow + ((BR / 8) * bn + 4 * j) * 8);
+    for (int j = 0; j < SPB; ++j) nxt[j] = *reinterpret_cast<const h8*>(xrow + ((BR / 8) * bn + 4 * j) * 8);
     // MFMA step st of the block; the group it completes, if any, closes.
-    auto mstep = [&](int st, const h2 (&pr)[4]) {
-      const h8 bv = {pr[0].x, pr[0].y, pr[1].x, pr[1].y, pr[2].x, pr[2].y, pr[3].x, pr[3].y};
+    auto mstep = [&](int st, const u32x4 bw) {
+      const h8 bv = __builtin_bit_cast(h8, bw);
       if (st & 1)
         C1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[st], bv, C1, 0, 0, 0);
       else
@@ -406,15 +416,11 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
     };
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      h2 pr[4];
       if constexpr (BITS == 4) {
-        q4_mfma_pairs(w[j], pr);
-        mstep(j, pr);
+        mstep(j, q4_mfma_operand(w[j]));
       } else {
-        q2_mfma_pairs<0>(w[j], pr);
-        mstep(2 * j, pr);
-        q2_mfma_pairs<1>(w[j], pr);
-        mstep(2 * j + 1, pr);
+        mstep(2 * j, q2_mfma_operand<0>(w[j]));
+        mstep(2 * j + 1, q2_mfma_operand<1>(w[j]));
       }
     }
     if (++cb == bhi) {
@@ -429,17 +435,18 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
       ++cp;
     }
   };
-  auto step = [&](int q, u32x4& w, uint32_t (&sc)[NSC], uint32_t (&zq)[NZ]) {
-    if (q < nitems) compute(w, sc, zq);
+  auto step = [&](int q, u32x4& w, uint32_t (&sc)[NSC], uint32_t (&zq)[NZ], const h8 (&a)[SPB],
+                  h8 (&nxt)[SPB]) {
+    if (q < nitems) compute(w, sc, zq, a, nxt);
     // Unconditional (out-of-range past the end), so the loads of every ring
     // slot keep one issue order and each wait covers just its own block.
     load_item(w, sc, zq);
   };
   for (int q = 0; q < nitems; q += kQ4Ring) {
-    step(q, wb0, sc0, zp0);
-    step(q + 1, wb1, sc1, zp1);
-    step(q + 2, wb2, sc2, zp2);
-    step(q + 3, wb3, sc3, zp3);
+    step(q, wb0, sc0, zp0, xa0, xa1);
+    step(q + 1, wb1, sc1, zp1, xa1, xa0);
+    step(q + 2, wb2, sc2, zp2, xa0, xa1);
+    step(q + 3, wb3, sc3, zp3, xa1, xa0);
   }
   __syncthreads();
   for (int r = t; r < npr * MT * 16; r += kQ4Threads) {
