@@ -369,7 +369,7 @@ def main():
                     help="only run a plain 256 MiB device-to-device copy 5 times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1 (each GPU would take its own share of the columns)"}))
         sys.exit(2)
 
     import torch
@@ -422,7 +422,7 @@ def main():
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": getattr(w, "dtype", "see workload"), "data": "synthetic (seeded, see DESIGN.md)",
+        "dtype": getattr(w, "dtype", "see workload"), "data": "synthetic (seeded: N(0,1) activations, N(0,0.02) weights quantised offline)",
         "config": dict(getattr(w, "config", {"workload": w.name}), rotation_copies=R,
                        pct_of_hbm_peak=round(100 * gbs / HBM_PEAK_GBS, 2)),
     }
