@@ -285,6 +285,7 @@ def test_q4_act_order_headline(wq, M):
     (1, 128, 4, 32, True), (3, 384, 260, 64, True), (5, 1024, 1028, 128, False),
     (9, 512, 516, 128, True), (2, 2048, 256, 32, False), (16, 256, 64, 128, True),
     (1, 4096, 4096, 128, True), (4, 11008, 4096, 128, True), (1, 544, 1024, 32, True),
+    (2, 2048, 264, 256, True), (1, 4096, 1024, 512, False),   # groups spanning 2 and 4 blocks
 ])
 def test_q4_small_ragged(wq, M, K, N, G, act):
     d = synth.gen_q4_group(M, K, N, G, seed=60 + M + K, act_order=act)
@@ -329,6 +330,7 @@ def test_q4_integer_exact(wq):
     (8, 1024, 528, 128, False),
     (3, 1024, 260, 128, True),      # zeros with an act-order row table; ragged N
     (12, 512, 1028, 128, False),    # two row chunks (8 + 4)
+    (3, 2048, 132, 256, True),      # a group spans two blocks
 ])
 def test_q4_zp_vs_oracle(wq, M, K, N, G, act):
     d = synth.gen_q4_zp(M, K, N, G, seed=synth.SEEDS["q4_zp"] + K + N, act_order=act)

@@ -199,7 +199,9 @@ __global__ __launch_bounds__(kThreads) void q2_prepack_kernel(const uint32_t* __
 // panel's blocks into contiguous, group-aligned ranges and keep kQ4Ring
 // blocks in flight.  Each wave leaves its partial tile per panel in LDS; one
 // barrier at the end, then the workgroup sums the waves and writes Y.
-// NSC: scale loads per block (4 for G = 32, 2 for G = 64, 1 for G >= 128).
+// NSC: groups that close in each block (BR / G: 1 .. 8), or 0 when a group
+// spans several blocks (G > BR); one scale (and zero) load per group closed,
+// one per block when NSC = 0.
 // ---------------------------------------------------------------------------
 // ZP: asymmetric form, w = (u - zero) * scale with an fp16 zero per (group,
 // column) ("Quantization CUDA", tom-jerr.github.io, sections "量化粒度" and
@@ -247,20 +249,21 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
 
   // Ring buffers: one 16-byte word quadruple, NSC scale bits and (ZP) NSC
   // zero bits per block.
-  constexpr int NZ = ZP ? NSC : 1;
+  constexpr int NL = NSC == 0 ? 1 : NSC;  // scale loads per block
+  constexpr int NZ = ZP ? NL : 1;
   u32x4 wb0, wb1, wb2, wb3;
-  uint32_t sc0[NSC], sc1[NSC], sc2[NSC], sc3[NSC];
+  uint32_t sc0[NL], sc1[NL], sc2[NL], sc3[NL];
   uint32_t zp0[NZ], zp1[NZ], zp2[NZ], zp3[NZ];
   // Load cursor (panel of the run, block) walks the wave's blocks in order;
   // past the end it loads nothing (out-of-range offsets).
   int lp = nbw > 0 ? 0 : npr, lb = blo;
   int woff = ((p_begin * nb + blo) * 64 + lane) * 16;
-  auto load_item = [&](u32x4& w, uint32_t (&sc)[NSC], uint32_t (&zq)[NZ]) {
+  auto load_item = [&](u32x4& w, uint32_t (&sc)[NL], uint32_t (&zq)[NZ]) {
     const bool ok = lp < npr;
     const int n = (p_begin + lp) * kQ4Panel + col;
 #pragma unroll
-    for (int k = 0; k < NSC; ++k) {
-      const int g = NSC == 1 ? (lb >> lbpg) : lb * NSC + k;  // the group step k closes
+    for (int k = 0; k < NL; ++k) {
+      const int g = NSC == 0 ? (lb >> lbpg) : lb * NSC + k;  // the group closed k-th in the block
       const int off = (ok && n < N) ? (g * N + n) * 2 : kOutOfRange;
       sc[k] = __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0);
       if constexpr (ZP) zq[k] = __builtin_amdgcn_raw_buffer_load_b16(zr, off, 0, 0);
@@ -377,28 +380,45 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
 #pragma unroll
     for (int j = 0; j < SPB; ++j) xa0[j] = *reinterpret_cast<const h8*>(xrow + ((BR / 8) * blo + 4 * j) * 8);
   }
-  auto compute = [&](const u32x4& w, const uint32_t (&sc)[NSC], const uint32_t (&zq)[NZ],
+  auto compute = [&](const u32x4& w, const uint32_t (&sc)[NL], const uint32_t (&zq)[NZ],
                      const h8 (&a)[SPB], h8 (&nxt)[SPB]) {
     const int pi = cp, b = cb;
     const int bn = b + 1 == bhi ? blo : b + 1;
 #pragma unroll
     for (int j = 0; j < SPB; ++j) nxt[j] = *reinterpret_cast<const h8*>(xrow + ((BR / 8) * bn + 4 * j) * 8);
     // MFMA step st of the block; the group it completes, if any, closes.
+    // With whole groups in a block (NSC >= 1) the first two steps of a group
+    // start their chains from the constant 0 operand, so nothing is zeroed at
+    // a close; groups spanning blocks (NSC = 0) zero both chains at a close.
+    constexpr int SPG = NSC == 0 ? SPB : SPB / NSC;  // steps per group (in the block)
+    const f4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
     auto mstep = [&](int st, const u32x4 bw) {
       const h8 bv = __builtin_bit_cast(h8, bw);
-      if (st & 1)
-        C1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[st], bv, C1, 0, 0, 0);
-      else
-        C0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[st], bv, C0, 0, 0, 0);
+      const int t = st % SPG;
+      if constexpr (NSC == 0) {
+        if (st & 1)
+          C1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[st], bv, C1, 0, 0, 0);
+        else
+          C0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[st], bv, C0, 0, 0, 0);
+      } else {
+        if (t == 0)
+          C0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[st], bv, zero4, 0, 0, 0);
+        else if (t == 1)
+          C1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[st], bv, zero4, 0, 0, 0);
+        else if (t & 1)
+          C1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[st], bv, C1, 0, 0, 0);
+        else
+          C0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[st], bv, C0, 0, 0, 0);
+      }
       bool close;
       int k = 0, g;
-      if constexpr (NSC > 1) {
-        close = ((st + 1) % (SPB / NSC)) == 0;
-        k = st / (SPB / NSC);
-        g = b * NSC + k;
-      } else {
+      if constexpr (NSC == 0) {
         close = st == SPB - 1 && ((b + 1) & (bpg - 1)) == 0;
         g = b >> lbpg;
+      } else {
+        close = t == SPG - 1;
+        k = st / SPG;
+        g = b * NSC + k;
       }
       if (close) {
         const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sc[k]);
@@ -409,8 +429,9 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
         const f4 S = *reinterpret_cast<const f4*>(sg + g * 8 + 4 * aq);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          tot[r] = __builtin_fmaf(s, __builtin_fmaf(S[r], zoff, C0[r] + C1[r]), tot[r]);
-          C0[r] = C1[r] = 0.0f;
+          const float c = SPG == 1 ? C0[r] : C0[r] + C1[r];
+          tot[r] = __builtin_fmaf(s, __builtin_fmaf(S[r], zoff, c), tot[r]);
+          if constexpr (NSC == 0) C0[r] = C1[r] = 0.0f;
         }
       }
     };
@@ -435,7 +456,7 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
       ++cp;
     }
   };
-  auto step = [&](int q, u32x4& w, uint32_t (&sc)[NSC], uint32_t (&zq)[NZ], const h8 (&a)[SPB],
+  auto step = [&](int q, u32x4& w, uint32_t (&sc)[NL], uint32_t (&zq)[NZ], const h8 (&a)[SPB],
                   h8 (&nxt)[SPB]) {
     if (q < nitems) compute(w, sc, zq, a, nxt);
     // Unconditional (out-of-range past the end), so the loads of every ring
@@ -598,19 +619,21 @@ static hipError_t launch_q4_t(const void* X, const void* packed, const void* sca
   return hipGetLastError();
 }
 
-// Closes per block (NSC): groups of G rows in a block of BR rows, at least 1.
+// Groups closed per block (NSC): BR / G for G <= BR, 0 for groups spanning
+// several blocks.
 template <int MT, bool ZP, int BITS>
 static hipError_t launch_q4_zp(const void* X, const void* packed, const void* scales,
                                const void* zeros, void* Y, int M, int K, int N, int G,
                                const PanelPlan& p, hipStream_t s) {
   constexpr int BR = block_rows<BITS>();
-  const int nsc = G >= BR ? 1 : BR / G;
+  const int nsc = G > BR ? 0 : BR / G;
   if constexpr (BITS == 2) {
     if (nsc == 8) return launch_q4_t<MT, 8, ZP, BITS>(X, packed, scales, zeros, Y, M, K, N, G, p, s);
   }
   if (nsc == 4) return launch_q4_t<MT, 4, ZP, BITS>(X, packed, scales, zeros, Y, M, K, N, G, p, s);
   if (nsc == 2) return launch_q4_t<MT, 2, ZP, BITS>(X, packed, scales, zeros, Y, M, K, N, G, p, s);
-  return launch_q4_t<MT, 1, ZP, BITS>(X, packed, scales, zeros, Y, M, K, N, G, p, s);
+  if (nsc == 1) return launch_q4_t<MT, 1, ZP, BITS>(X, packed, scales, zeros, Y, M, K, N, G, p, s);
+  return launch_q4_t<MT, 0, ZP, BITS>(X, packed, scales, zeros, Y, M, K, N, G, p, s);
 }
 
 template <int MT, int BITS>
