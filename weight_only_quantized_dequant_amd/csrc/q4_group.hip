@@ -227,8 +227,14 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
   // Uniform across the wave: keeps the block range and cursors in scalar
   // registers and their branches scalar.
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int p_begin = (int)((long long)blockIdx.x * npanels / gridDim.x);
-  const int p_end = (int)((long long)(blockIdx.x + 1) * npanels / gridDim.x);
+  // Workgroups b and b + 8 run on the same XCD (dispatch is round-robin over
+  // the 8 XCDs).  Each XCD takes a contiguous range of panel runs, so a
+  // 128-byte line of a scale or zero row (64 columns: four panels) is
+  // fetched into one XCD's L2, not into up to four.
+  const int G8 = gridDim.x % 8 == 0 ? gridDim.x / 8 : 0;
+  const int run = G8 ? (int)(blockIdx.x % 8) * G8 + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+  const int p_begin = (int)((long long)run * npanels / gridDim.x);
+  const int p_end = (int)((long long)(run + 1) * npanels / gridDim.x);
   const int npr = p_end - p_begin;
 
   // Blocks of this wave: a group-aligned contiguous range.
