@@ -544,6 +544,44 @@ def test_int8_mixed_thresholds_and_zero_rows(wq):
     _mixed_check(wq, X, Wq, Sw, -1.0)    # every column taken out
 
 
+# ====================================================== large activations ==
+
+def _with_large_entries(x, rows, value=60000.0):
+    x = np.array(x, copy=True)
+    for i, k in enumerate(rows):
+        x[..., k] = value if i % 2 == 0 else -value
+    return x
+
+
+def test_large_fp16_activations_all_paths(wq):
+    """fp16 activations near the top of the fp16 range (60000) at a few rows,
+    the rest N(0,1): every weight-only path stays finite and within the
+    tolerance (outputs stay inside the fp16 range)."""
+    rows = (3, 100, 517, 1000)
+    d = synth.gen_q3(1024, 256, seed=81, dtype="f16")
+    x = _with_large_entries(d["x"], rows).astype(np.float16)
+    y = wq.matvec_q3(cu(x), wq.prepack_q3(cu(d["qweight"]), 1024), cu(d["scales"]), cu(d["zeros"]))
+    assert_tol(host(y), oracle.matvec_q3(x, d["qweight"], d["scales"], d["zeros"]), "q3 f16 large x")
+
+    d = synth.gen_q8_group(2, 1024, 256, 128, seed=82)
+    X = _with_large_entries(d["X"], rows).astype(np.float16)
+    y = wq.gemm_q8_group(cu(X), wq.prepack_q8(cu(d["q"])), cu(d["scales"]), 128)
+    assert_tol(host(y), oracle.gemm_q8_group(X, d["q"], d["scales"], 128), "q8 large x")
+
+    d = synth.gen_q4_group(2, 1024, 256, 128, seed=83, act_order=True)
+    X = _with_large_entries(d["X"], rows).astype(np.float16)
+    packed, _ = wq.prepare_q4(cu(d["qweight"]), d["g_idx"], 128)
+    y = wq.gemm_q4_group(cu(X), packed, cu(d["scales"]), 128)
+    assert_tol(host(y), oracle.gemm_q4_group(X, d["qweight"], d["scales"], d["g_idx"], 128), "q4 large x")
+
+    d = synth.gen_q2_zp(2, 1024, 256, 128, seed=84, act_order=True)
+    X = _with_large_entries(d["X"], rows).astype(np.float16)
+    packed, _ = wq.prepare_q2(cu(d["qweight"]), d["g_idx"], 128)
+    y = wq.gemm_q2_group_zp(cu(X), packed, cu(d["scales"]), cu(d["zeros"]), 128)
+    assert_tol(host(y), oracle.gemm_q2_zp(X, d["qweight"], d["scales"], d["zeros"], d["g_idx"], 128),
+               "q2 large x")
+
+
 # ============================================================ measurement ==
 
 @pytest.mark.parametrize("nbytes,pos", [(1 << 24, 0), (1 << 24, (1 << 24) - 4), (65536 * 3 + 48, 65536 * 3 + 36),

@@ -26,6 +26,19 @@
 
 namespace wq {
 
+// fp16 activations: a pair is pre-scaled by 2^(cls - pa - kQ3XShift) and
+// 2^(cls - pb - kQ3XShift), never by more than 1, so no finite fp16 x
+// overflows (pre-scaling up by 2^(cls - p) alone would reach 4 x and turn
+// |x| > 16376 into infinity); the 2^kQ3XShift returns in the final rescale.
+constexpr int kQ3XShift = 2;
+constexpr bool q3_prescale_at_most_one() {
+  for (int P = 0; P < 16; ++P)
+    if (q3_class(P) - q3_pair(P).pa > kQ3XShift || q3_class(P) - q3_pair(P).pb > kQ3XShift)
+      return false;
+  return true;
+}
+static_assert(q3_prescale_at_most_one(), "a pre-scale factor would exceed 1");
+
 // Panels a workgroup walks at most: each keeps its waves' partial sums in
 // its own LDS slot until the single reduction at the end.
 constexpr int kQ3MaxRun = 8;
@@ -210,10 +223,10 @@ __global__ __launch_bounds__(THREADS) void q3_panel_kernel(
     for (int P = 0; P < 16; ++P) {
       const Q3Pair q = q3_pair(P);
       if constexpr (F16) {
-        // class = max(pa, pb): the half with the smaller offset is divided by 2^d.
+        // class = max(pa, pb): both products carry 2^(cls - 24 - kQ3XShift).
         const int cls = q3_class(P);
-        const h2 hv = {(_Float16)__builtin_ldexpf(xs[q.a], cls - q.pa),
-                       (_Float16)__builtin_ldexpf(xs[q.b], cls - q.pb)};
+        const h2 hv = {(_Float16)__builtin_ldexpf(xs[q.a], cls - q.pa - kQ3XShift),
+                       (_Float16)__builtin_ldexpf(xs[q.b], cls - q.pb - kQ3XShift)};
         xp[blk * 16 + P] = as_u32(hv);
       } else {
         // fp32: undo the 2^(p - 24) of each subnormal code in the activation.
@@ -299,7 +312,7 @@ __global__ __launch_bounds__(THREADS) void q3_panel_kernel(
         float a = 0.0f;
 #pragma unroll
         for (int sl = 0; sl < NACC; ++sl) {
-          a = __builtin_fmaf(acc[sl][j], __builtin_ldexpf(1.0f, 24 - q3_slot_class(sl)), a);
+          a = __builtin_fmaf(acc[sl][j], __builtin_ldexpf(1.0f, 24 + kQ3XShift - q3_slot_class(sl)), a);
           acc[sl][j] = 0.0f;
         }
         v[j] = a;
