@@ -238,7 +238,6 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
   const int npr = p_end - p_begin;
 
   // Blocks of this wave: a group-aligned contiguous range.
-  const int spg = G / 32;  // MFMA steps per group
   const int bpg = G >= BR ? G / BR : 1;
   const int nsplit = nb / bpg;
   const int blo = (wave * nsplit / kQ4Waves) * bpg, bhi = ((wave + 1) * nsplit / kQ4Waves) * bpg;
@@ -253,8 +252,8 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
   int lbpg = 0;  // log2(bpg): G is a power of two
   while ((1 << lbpg) < bpg) ++lbpg;
 
-  // Ring buffers: one 16-byte word quadruple, NSC scale bits and (ZP) NSC
-  // zero bits per block.
+  // Ring buffers: one 16-byte word quadruple, NL scale bits and (ZP) NL zero
+  // bits per block.
   constexpr int NL = NSC == 0 ? 1 : NSC;  // scale loads per block
   constexpr int NZ = ZP ? NL : 1;
   u32x4 wb0, wb1, wb2, wb3;
@@ -375,8 +374,8 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
   const _Float16* xrow = xa + (size_t)am * rs + aq * 8;
   f4 C0 = {0.0f, 0.0f, 0.0f, 0.0f}, C1 = C0, tot = C0;
 
-  // One block: 4 MFMA steps (two chains) and the group closes; at the wave's
-  // last block of a panel its partial tile goes to LDS.
+  // One block: SPB MFMA steps (two chains) and the groups they close; at the
+  // wave's last block of a panel its partial tile goes to LDS.
   int cp = 0, cb = blo;  // compute cursor: panel of the run, block
   // Operands of X, read one block ahead into the other of two buffers (X is
   // the same for every panel, so after a wave's last block comes blo).  The
@@ -400,18 +399,18 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
     const f4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
     auto mstep = [&](int st, const u32x4 bw) {
       const h8 bv = __builtin_bit_cast(h8, bw);
-      const int t = st % SPG;
+      const int ts = st % SPG;  // step within its group
       if constexpr (NSC == 0) {
         if (st & 1)
           C1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[st], bv, C1, 0, 0, 0);
         else
           C0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[st], bv, C0, 0, 0, 0);
       } else {
-        if (t == 0)
+        if (ts == 0)
           C0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[st], bv, zero4, 0, 0, 0);
-        else if (t == 1)
+        else if (ts == 1)
           C1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[st], bv, zero4, 0, 0, 0);
-        else if (t & 1)
+        else if (ts & 1)
           C1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[st], bv, C1, 0, 0, 0);
         else
           C0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[st], bv, C0, 0, 0, 0);
@@ -422,7 +421,7 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
         close = st == SPB - 1 && ((b + 1) & (bpg - 1)) == 0;
         g = b >> lbpg;
       } else {
-        close = t == SPG - 1;
+        close = ts == SPG - 1;
         k = st / SPG;
         g = b * NSC + k;
       }
