@@ -327,7 +327,7 @@ def calibration(wq, torch, w, steps, warmup, gemv_ms):
     return {"empty_kernel_us": round(e_ms * 1e3, 3), "stream_read_us": round(s_ms * 1e3, 3),
             "stream_read_bytes": wbytes, "stream_read_GB_per_s": round(wbytes / (s_ms * 1e-3) / 1e9, 1),
             "stream_read_pct_hbm_peak": round(100 * wbytes / (s_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
-            "gemv_time_over_stream_time": round(s_ms / gemv_ms, 4), "rotation_copies": R}
+            "share_of_stream_ceiling": round(s_ms / gemv_ms, 4), "rotation_copies": R}
 
 
 def cpu_baseline(w, budget_s=10.0):
