@@ -343,7 +343,7 @@ def cpu_baseline(w, budget_s=10.0):
         w.oracle()
         n += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or n >= 200:
+        if el >= budget_s or n >= 2000:
             break
     per = el / n
     return {"value": round(w.nbytes / per / 1e9, 4), "unit": "GB/s", "cores": threads,
