@@ -45,8 +45,13 @@ constexpr int kQ3MaxRun = 8;
 
 // Threads of the product's workgroup: 8 waves (two per SIMD, one wave's
 // arithmetic overlapping another's loads) for the large shapes, 4 waves for
-// the small ones, where the shorter per-wave staging wins.
-static int q3_threads(int K, int N) { return (K >= 8192 || N >= 8192) ? 512 : 256; }
+// the small ones, where the shorter per-wave staging wins, and a single wave
+// when one wave's slots already cover K with one block each (the other waves
+// would idle and still wait at the barrier).
+static int q3_threads(int K, int N, int cpp) {
+  if (K / 32 <= 64 / cpp && N <= 4096) return 64;
+  return (K >= 8192 || N >= 8192) ? 512 : 256;
+}
 
 // Widest panel whose count spreads over kTargetCUs compute units in whole
 // rounds with at most 12% idle (each workgroup then walks a contiguous run of
@@ -67,7 +72,7 @@ PanelPlan plan_q3(int K, int N) {
   p.P = panel_width_3(N);
   p.cpp = p.P / 4;
   p.npanels = N / p.P;
-  p.threads = q3_threads(K, N);
+  p.threads = q3_threads(K, N, p.cpp);
   const int ns = p.threads / p.cpp;
   const int ku = K / 32;  // blocks
   p.u = (ku + ns - 1) / ns;
@@ -183,7 +188,7 @@ __global__ __launch_bounds__(THREADS) void q3_panel_kernel(
   // The scale and zero of output column p_begin * P + t (a run has at most
   // 32 * kQ3MaxRun <= THREADS outputs), loaded now and used at the end.
   // Issued after the first units, so waiting for those does not wait for them.
-  static_assert(32 * kQ3MaxRun <= 256, "one output per thread");
+  // (launch_q3_t bounds the run so that a run's outputs never exceed THREADS.)
   const int nout = (p_end - p_begin) * P;
   float out_sc = 0.0f, out_ze = 0.0f;
   {
@@ -415,7 +420,10 @@ static hipError_t launch_q3_t(const void* x, const void* packed, const void* sca
   const size_t lds = (size_t)(K / 2) * (F16 ? 4 : 8);
   const int cus = device_cus();
   int grid = p.npanels < cus ? p.npanels : cus;
-  if ((p.npanels + grid - 1) / grid > kQ3MaxRun) grid = (p.npanels + kQ3MaxRun - 1) / kQ3MaxRun;
+  // Runs of at most kQ3MaxRun panels and at most THREADS outputs (one per
+  // thread in the final step).
+  const int max_run = (THREADS / (4 * CPP)) < kQ3MaxRun ? THREADS / (4 * CPP) : kQ3MaxRun;
+  if ((p.npanels + grid - 1) / grid > max_run) grid = (p.npanels + max_run - 1) / max_run;
   // Static LDS (the per-panel partial sums) plus x may pass 64 KB.
   constexpr size_t kStatic = sizeof(float) * ((size_t)kQ3MaxRun * (THREADS / 64) * CPP * 4 + THREADS / 64);
   if (lds + kStatic > 65536) {
@@ -437,8 +445,9 @@ template <bool F16, int CPP>
 static hipError_t launch_q3_ub(const void* x, const void* packed, const void* scales,
                                const void* zeros, void* y, int K, int N, const PanelPlan& p,
                                hipStream_t s) {
-  return p.threads == 512 ? launch_q3_t<F16, CPP, 512>(x, packed, scales, zeros, y, K, N, p, s)
-                          : launch_q3_t<F16, CPP, 256>(x, packed, scales, zeros, y, K, N, p, s);
+  if (p.threads == 512) return launch_q3_t<F16, CPP, 512>(x, packed, scales, zeros, y, K, N, p, s);
+  if (p.threads == 256) return launch_q3_t<F16, CPP, 256>(x, packed, scales, zeros, y, K, N, p, s);
+  return launch_q3_t<F16, CPP, 64>(x, packed, scales, zeros, y, K, N, p, s);
 }
 
 template <bool F16>
