@@ -25,7 +25,9 @@ Extra fields on the single JSON line:
   once with the GEMV's loads (the achievable time for those bytes here), on
   the same rotation and graph replay.
 * secondary (unless --headline-only): the other workloads of the library,
-  each as microseconds per call and GB/s (or TOPS) with the same method.
+  each as microseconds per call and GB/s (or TOPS) with the same method, and
+  (unless --no-calibration) the time of a bare stream of the same weight
+  bytes on the same rotation, with the kernel's share of it.
 """
 from __future__ import annotations
 
@@ -443,6 +445,16 @@ def main():
             e = {"us_per_call": round(sms * 1e3, 3), "GB_per_s": round(sw.nbytes / (sms * 1e-3) / 1e9, 1),
                  "pct_hbm_peak": round(100 * sw.nbytes / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                  "rotation_copies": sR, "algorithmic_bytes": sw.nbytes}
+            if not args.no_calibration:
+                # The same rotation, a kernel that only reads each copy's weight
+                # (slot 1 of every argument set) once: the time any kernel that
+                # moves those bytes needs here.
+                sink = torch.zeros(1, dtype=torch.int32, device=dev)
+                ref = Workload("weight stream", sw.nbytes, sw.make,
+                               lambda c: wq.calib_stream_read(c[1], sink))
+                rms, _ = time_workload(torch, ref, 100 if big else 300, 10 if big else 30)
+                e["weight_stream_us"] = round(rms * 1e3, 3)
+                e["share_of_stream_ceiling"] = round(rms / sms, 4)
             if sw.flops:
                 e["TOPS"] = round(sw.flops / (sms * 1e-3) / 1e12, 1)
                 e["pct_mfma_peak"] = round(100 * sw.flops / (sms * 1e-3) / 1e12 / sw.peak_tops, 2)
