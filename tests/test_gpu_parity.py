@@ -59,8 +59,12 @@ def assert_tol(y, y_exact, what=""):
     (1, 256, 16, 128), (1, 384, 272, 128), (2, 512, 1024, 64), (3, 640, 528, 128),
     (4, 4096, 1040, 128), (5, 1024, 256, 32), (8, 2048, 4096, 128), (9, 768, 784, 128),
     (16, 256, 512, 256),
-    (1, 8192, 512, 256),         # scale folded after the reduction, two batches per slot
-    (1, 8192, 1024, 128),        # two groups per quarter-wave: scale per batch
+    (1, 8192, 512, 256),         # group scale folded after the quarter-wave sums, two chunks
+    (1, 8192, 1024, 128),        # two chunks of 4096 rows, folded scales
+    (1, 4608, 256, 512),         # a ragged second chunk (512 of 4096 rows)
+    (1, 1152, 256, 96),          # group of 96 rows: a scale per piece, one row
+    (6, 8192, 512, 128),         # 8-row pass, activations restaged in LDS per chunk
+    (7, 4224, 272, 64),          # 8-row pass, ragged chunk, scale per piece
 ])
 def test_q8_group_vs_oracle(wq, M, K, N, G):
     d = synth.gen_q8_group(M, K, N, G, seed=1100 if (M, K, N) == (1, 4096, 4096) else 7 + M + K + N)
@@ -127,7 +131,7 @@ def test_unpack_q8_bit_exact(wq, K, N):
 
 
 def test_q8_wide_panels_and_long_k(wq):
-    # N >= 8192 switches to 32-column panels; K = 11008 gives 48-row slot spans.
+    # Wide N, and K = 11008 (two chunks of 4096 rows and a ragged third).
     for (M, K, N) in ((1, 4096, 11008), (2, 11008, 4096), (3, 1024, 8192)):
         d = synth.gen_q8_group(M, K, N, 128, seed=M + K)
         Y = wq.gemm_q8_group(cu(d["X"]), wq.prepack_q8(cu(d["q"])), cu(d["scales"]), 128)
@@ -135,13 +139,13 @@ def test_q8_wide_panels_and_long_k(wq):
 
 
 # From 32 rows of X on (groups a multiple of 64 rows) the int8 product runs
-# on the matrix cores: 64 x 128 output tiles, K in stages of 64 rows.
+# on the matrix cores: 32 x 128 output tiles, K in stages of 128 rows.
 @pytest.mark.parametrize("M,K,N,G", [
     (32, 4096, 4096, 128),     # first row count on the tiled path
     (100, 1088, 4112, 64),     # ragged row and column tiles, 17 stages
     (64, 64, 128, 64),         # a single stage
-    (40, 11008, 4096, 128),    # 24-row slots of the packed layout straddle stages
-    (72, 4096, 8192, 128),     # 32-column panels (two 16-column chunks each)
+    (40, 11008, 4096, 128),    # a ragged last stage (K = 86 stages of 128)
+    (72, 4096, 8192, 128),     # wide N
     (33, 1152, 384, 192),      # groups of three stages
     (130, 512, 1024, 512),     # one group over all of K; three row tiles
 ])

@@ -12,14 +12,16 @@
 // Tiles.  A workgroup (4 waves) owns a 32 x 128 tile of Y and walks K in
 // stages of 128 rows.  Per stage, direct-to-LDS buffer loads bring the X tile
 // (fp16, 32 x 128), the int8 codes of the weight tile (128 rows x 128
-// columns, as the 16-byte pieces of the packed layout: one row of one
-// 16-column chunk) and the scale rows of the stage's groups into a ring of
-// kStages slots (75 KB: two workgroups fit on a CU).  Each wave builds its
+// columns: 16 pieces of each of 64 column pairs of the packed layout, 8 rows
+// x 2 columns per piece) and the scale rows of the stage's groups into a ring
+// of kStages slots (75 KB: two workgroups fit on a CU).  Each wave builds its
 // v_mfma_f32_16x16x32_f16 operands for a 16 x 64 sub-tile in registers,
-// straight from the int8 stage: one v_perm_b32 turns two code bytes into two
-// zero-exponent fp16s (the exact subnormals u 2^-24, u = q + 128), and one
-// more matrix-core product per k32 step against a constant operand of
-// 128 2^-24 gives the offset term.  Each wave keeps the current group's sums
+// straight from the int8 stage: a piece is the 8 rows of one k32 octet for
+// two columns, and one v_perm_b32 per word turns a column's two code bytes
+// into two zero-exponent fp16s (the exact subnormals u 2^-24, u = q + 128),
+// so one 16-byte LDS read gives the operands of two columns.  One more
+// matrix-core product per k32 step against a constant operand of 128 2^-24
+// gives the offset term.  Each wave keeps the current group's sums
 // and a running total; at the end of a group the total takes
 // (sums - offset term) * scale in fp32 and the next group starts from zero,
 // so the products are exact and every rounding is an fp32 one, as in the
@@ -54,24 +56,24 @@ __device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 15); }
 
 }  // namespace
 
-// Codes of a stage in LDS: the 16-byte piece of row r = 8 o + i (o = 0..15,
-// i = 0..7), chunk c (16 columns) sits at slot 16 (8 i + c) + (o ^ 4 (c % 4)).
-// A direct-to-LDS load writes 64 consecutive slots, so its 16 lanes of one
-// (i, c) read 16 pieces of consecutive octets o, which are adjacent in the
-// packed layout whenever one of its slots spans 8 rows; and the 64 lanes of
-// a fragment read (below) hit 64 distinct banks.
+// Codes of a stage in LDS: piece b (rows 8 b .. 8 b + 7 of the stage,
+// b = 0..15) of the tile's column pair p (0..63) sits at slot
+// 16 p + (b ^ (p % 16)).  A direct-to-LDS load writes 64 consecutive slots:
+// 4 pairs x 16 pieces, i.e. four 256-byte runs of the packed weight.  The
+// swizzle keeps the 16 lanes of one fragment read (16 pairs, one piece
+// each) on distinct banks.
 //
-// Fragments.  Lane l of a wave with columns w0 .. w0 + 63 takes, for the
-// k32 step h, rows 32 h + 8 (l / 16) + e (e = 0..7) of chunk w0 / 16 + p and
-// the 4-byte word d of each (p = (l % 16) / 4, d = l % 4): 4 columns
-// 16 p + 4 d + j (j = 0..3), 8 rows each.  Column j of that word goes to the
-// matrix-core operand of block j, so block j, operand column t holds weight
-// column 16 (t / 4) + 4 (t % 4) + j; the transposed result then gives lane l
-// the 16 consecutive columns 16 (l / 16) + 4 r + j (r, j = 0..3) of one row.
+// Fragments.  Lane l of a wave with columns w0 .. w0 + 63 (pairs w0 / 2 ..)
+// takes, for the k32 step h and half H (0, 1), piece 4 h + l / 16 of pair
+// w0 / 2 + 16 H + l % 16: the 8 rows 32 h + 8 (l / 16) + e of two columns.
+// Column c of it goes to the matrix-core operand of block 2 H + c, so block
+// 2 H + c, operand column t holds weight column w0 + 32 H + 2 t + c; the
+// transposed result then gives lane l, per half, the 8 consecutive columns
+// w0 + 32 H + 8 (l / 16) + 2 r + c (r = 0..3, c = 0, 1) of one row.
 __global__ __launch_bounds__(kThreadsG, 2) void q8_gemm_kernel(
     const _Float16* __restrict__ X, const uint8_t* __restrict__ Wp,
-    const float* __restrict__ scales, _Float16* __restrict__ Y, int M, int K, int N, int G, int u,
-    int nta, int cpp, int packed_bytes, int mtiles, int ntiles) {
+    const float* __restrict__ scales, _Float16* __restrict__ Y, int M, int K, int N, int G, int KB,
+    int mtiles, int ntiles) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStage];
 
   // Workgroups b and b + 8 run on the same XCD: the M tiles that share a
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(kThreadsG, 2) void q8_gemm_kernel(
   const int nk = (K + kBK - 1) / kBK;
 
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, M * K * 2);
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wp, packed_bytes);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wp, K * N);
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, (K / G) * N * 4);
 
   // X: load t of wave w fills stage rows 4 (4 w + t) .. + 3; lane l brings
@@ -97,31 +99,18 @@ __global__ __launch_bounds__(kThreadsG, 2) void q8_gemm_kernel(
     const int row = 4 * (2 * wave + t) + (lane >> 4);
     a_off[t] = m0 + row < M ? (m0 + row) * K * 2 + 16 * swz(row, lane & 15) : -1;
   }
-  // Codes: load t of wave w fills slots 64 (4 w + t) ..: i = 2 w + t / 2,
-  // chunk c = 4 (t % 2) + l / 16, octet o = (l % 16) ^ 4 (c % 4).  The piece of
-  // row k, 16-column chunk q sits at ((panel u + k % u) nta + (k / u) cpp +
-  // q % cpp) 16, panel = q / cpp; (bs, bi) track (k / u, k % u) per row.
-  const int b_oct = (lane & 15) ^ (4 * ((lane >> 4) & 3));
-  int b_base[2];  // chunk part of the piece offset
-  bool b_live[2];
+  // Codes: load t of wave w fills slots 64 (4 w + t) .. + 63, i.e. pair
+  // p = 4 (4 w + t) + l / 16 of the tile, the piece that slot 16 p + l % 16
+  // holds: b = (l % 16) ^ (p % 16), with p % 16 = 4 t + l / 16.
+  int b_off[4], b_sw[4];
+  bool b_live[4];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int q = n0 / 16 + 4 * t + (lane >> 4);
-    b_live[t] = q < N / 16;
-    b_base[t] = b_live[t] ? ((q / cpp) * u * nta + q % cpp) * 16 : 0;
+  for (int t = 0; t < 4; ++t) {
+    const int pg = n0 / 2 + 4 * (4 * wave + t) + (lane >> 4);
+    b_live[t] = pg < N / 2;
+    b_off[t] = b_live[t] ? pg * KB * 16 : 0;
+    b_sw[t] = (lane & 15) ^ (4 * t + (lane >> 4));
   }
-  // Row part (k % u) nta 16 + (k / u) cpp 16 of the two rows, kept up to date
-  // from stage to stage without multiplies.
-  int bi[2], b_rowoff[2], brow[2];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    brow[r] = 8 * b_oct + 2 * wave + r;  // row within the stage
-    bi[r] = brow[r] % u;
-    b_rowoff[r] = (bi[r] * nta + (brow[r] / u) * cpp) * 16;
-  }
-  const int step_i = kBK % u;
-  const int step_off = (step_i * nta + (kBK / u) * cpp) * 16;  // no wrap of k % u
-  const int wrap_off = (cpp - u * nta) * 16;                   // extra when k % u wraps
   // Scales (wave 0): lanes 0..31 columns n0 + 4 l .. + 3 of the group of the
   // stage's first row, lanes 32..63 the same columns of the group of row 64.
   const int s_col = n0 + 4 * (lane & 31);
@@ -139,17 +128,10 @@ __global__ __launch_bounds__(kThreadsG, 2) void q8_gemm_kernel(
           0, 0, 0);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int r = t >> 1, c = t & 1;
+      const int b = kt * 16 + b_sw[t];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           wr, (__attribute__((address_space(3))) void*)(base + kStageA + 1024 * (4 * wave + t)), 16,
-          (b_live[c] && k0 + brow[r] < K) ? b_base[c] + b_rowoff[r] : kOutOfRange, 0, 0, 0);
-    }
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      bi[r] += step_i;
-      const bool wrap = bi[r] >= u;
-      bi[r] -= wrap ? u : 0;
-      b_rowoff[r] += step_off + (wrap ? wrap_off : 0);
+          (b_live[t] && b < KB) ? b_off[t] + 16 * b : kOutOfRange, 0, 0, 0);
     }
     if (wave == 0) {
       const int g = (k0 + (lane >= 32 ? 64 : 0)) / G;
@@ -161,13 +143,10 @@ __global__ __launch_bounds__(kThreadsG, 2) void q8_gemm_kernel(
 
   const int wm = wave >> 1, wn = wave & 1;  // 2 x 2 waves, each 16 rows x 64 columns
   const int fr = lane & 15, fq = lane >> 4;
-  const int fp = fr >> 2, fd = fr & 3;
-  // Byte offset of this lane's code word in the stage for e = 0, k32 step h
-  // (e adds 2048: 8 i + c grows by 8).
   // LDS byte offsets (within a stage) of this lane's fragment reads, per k32
-  // step h: X rows wm 32 + 16 i + l % 16; the code word of row e = 0 (row e
-  // adds 2048: 8 i + c grows by 8).
-  int a_lds[4][1], b_lds[4];
+  // step h: X row wm 16 + l % 16; the piece 4 h + l / 16 of pair
+  // 32 wn + 16 H + l % 16 (whose p % 16 is l % 16).
+  int a_lds[4][1], b_lds[4][2];
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
 #pragma unroll
@@ -175,7 +154,9 @@ __global__ __launch_bounds__(kThreadsG, 2) void q8_gemm_kernel(
       const int row = wm * 16 + 16 * i + fr;
       a_lds[h][i] = row * kRowA + 16 * swz(row, 4 * h + fq);
     }
-    b_lds[h] = kStageA + (16 * (4 * wn + fp) + fq + 4 * (h ^ fp)) * 16 + 4 * fd;
+#pragma unroll
+    for (int H = 0; H < 2; ++H)
+      b_lds[h][H] = kStageA + (16 * (32 * wn + 16 * H + fr) + ((4 * h + fq) ^ fr)) * 16;
   }
 
   // acc: this group's sums of x * u (u = q + 128, as fp16 subnormals u 2^-24);
@@ -189,41 +170,48 @@ __global__ __launch_bounds__(kThreadsG, 2) void q8_gemm_kernel(
     for (int j = 0; j < 4; ++j) tot[i][j] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
   const h8 c128 = __builtin_bit_cast(h8, (u32x4){0x00800080u, 0x00800080u, 0x00800080u, 0x00800080u});
 
-  // One k32 step of the stage in slot S: LDS reads; then each code byte into
-  // the low byte of an fp16 whose other bits are zero (the subnormal u 2^-24),
-  // two rows per register, one v_perm_b32 per register.
+  // One k32 step of the stage in slot S: LDS reads; then each column's two
+  // code bytes of a word into the low bytes of two fp16s whose other bits are
+  // zero (the subnormals u 2^-24), one v_perm_b32 per register.
   struct Step {
     h8 a[1];
-    uint32_t D[8];
+    u32x4 B[2];
   };
   auto read_step = [&](const unsigned char* S, int h, Step& st) {
 #pragma unroll
     for (int i = 0; i < 1; ++i) st.a[i] = *reinterpret_cast<const h8*>(S + a_lds[h][i]);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) st.D[e] = *reinterpret_cast<const uint32_t*>(S + b_lds[h] + 2048 * e);
+    for (int H = 0; H < 2; ++H) st.B[H] = *reinterpret_cast<const u32x4*>(S + b_lds[h][H]);
   };
   auto convert = [&](const Step& st, h8 b[4]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t sel = 0x0C000C00u | ((4u + j) << 16) | (uint32_t)j;
-      const u32x4 w = {__builtin_amdgcn_perm(st.D[1], st.D[0], sel), __builtin_amdgcn_perm(st.D[3], st.D[2], sel),
-                       __builtin_amdgcn_perm(st.D[5], st.D[4], sel), __builtin_amdgcn_perm(st.D[7], st.D[6], sel)};
-      b[j] = __builtin_bit_cast(h8, w);
+    for (int H = 0; H < 2; ++H) {
+      const u32x4 w = st.B[H];
+      const u32x4 c0 = {q8_col_pair<0>(w[0]), q8_col_pair<0>(w[1]), q8_col_pair<0>(w[2]), q8_col_pair<0>(w[3])};
+      const u32x4 c1 = {q8_col_pair<1>(w[0]), q8_col_pair<1>(w[1]), q8_col_pair<1>(w[2]), q8_col_pair<1>(w[3])};
+      b[2 * H] = __builtin_bit_cast(h8, c0);
+      b[2 * H + 1] = __builtin_bit_cast(h8, c1);
     }
   };
   auto group_end = [&](const unsigned char* S, int h) {
-    // 16 scales of this lane's columns, v[r][j] for column 16 (l / 16) + 4 r + j.
-    const unsigned char* sc = S + kStageA + kStageB + 512 * (h >> 1) + 4 * (wn * 64 + 16 * fq);
-    f32x4 v[4];
+    // Scales of this lane's columns: v[H][0..1] for columns
+    // 64 wn + 32 H + 8 (l / 16) + 0 .. 7 of the tile.
+    const unsigned char* sc = S + kStageA + kStageB + 512 * (h >> 1) + 4 * (wn * 64 + 8 * fq);
+    f32x4 v[2][2];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] = *reinterpret_cast<const f32x4*>(sc + 16 * r);
+    for (int H = 0; H < 2; ++H)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) v[H][e] = *reinterpret_cast<const f32x4*>(sc + 128 * H + 16 * e);
 #pragma unroll
     for (int i = 0; i < 1; ++i) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        const int H = j >> 1, c = j & 1;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          tot[i][j][r] = __builtin_fmaf(acc[i][j][r] - xacc[i][r], v[r][j], tot[i][j][r]);
+        for (int r = 0; r < 4; ++r) {
+          const int e = 2 * r + c;  // column 8 (l / 16) + e of half H
+          tot[i][j][r] = __builtin_fmaf(acc[i][j][r] - xacc[i][r], v[H][e >> 2][e & 3], tot[i][j][r]);
+        }
       }
     }
   };
@@ -293,19 +281,19 @@ __global__ __launch_bounds__(kThreadsG, 2) void q8_gemm_kernel(
 #pragma unroll
   for (int i = 0; i < 1; ++i) {
     const int m = m0 + wm * 16 + 16 * i + fr;
-    const int n = n0 + wn * 64 + 16 * fq;
-    if (m >= M || n >= N) continue;
-    uint32_t w[8];
+    if (m >= M) continue;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const h2 lo = {(_Float16)(tot[i][0][r] * kTwo24), (_Float16)(tot[i][1][r] * kTwo24)};
-      const h2 hi = {(_Float16)(tot[i][2][r] * kTwo24), (_Float16)(tot[i][3][r] * kTwo24)};
-      w[2 * r] = as_u32(lo);
-      w[2 * r + 1] = as_u32(hi);
+    for (int H = 0; H < 2; ++H) {
+      const int n = n0 + wn * 64 + 32 * H + 8 * fq;
+      if (n >= N) continue;
+      uint32_t w[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const h2 pr = {(_Float16)(tot[i][2 * H][r] * kTwo24), (_Float16)(tot[i][2 * H + 1][r] * kTwo24)};
+        w[r] = as_u32(pr);
+      }
+      *reinterpret_cast<uint4*>(Y + (size_t)m * N + n) = make_uint4(w[0], w[1], w[2], w[3]);
     }
-    uint4* dst = reinterpret_cast<uint4*>(Y + (size_t)m * N + n);
-    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
   }
 }
 
@@ -318,13 +306,11 @@ bool q8_gemm_supported(int M, int K, int N, int G) {
 
 hipError_t launch_q8_gemm(const void* X, const void* packed, const float* scales, void* Y, int M,
                           int K, int N, int G, hipStream_t s) {
-  const PanelPlan p = plan_q8(K, N);
   const int mtiles = (M + kBM - 1) / kBM, ntiles = (N + kBN - 1) / kBN;
   const int grid = (ntiles + 7) / 8 * 8 * mtiles;
   hipLaunchKernelGGL(q8_gemm_kernel, dim3(grid), dim3(kThreadsG), 0, s,
                      reinterpret_cast<const _Float16*>(X), reinterpret_cast<const uint8_t*>(packed),
-                     scales, reinterpret_cast<_Float16*>(Y), M, K, N, G, p.u, p.nsa * p.cpp, p.cpp,
-                     (int)p.packed_bytes, mtiles, ntiles);
+                     scales, reinterpret_cast<_Float16*>(Y), M, K, N, G, K / 8, mtiles, ntiles);
   return hipGetLastError();
 }
 

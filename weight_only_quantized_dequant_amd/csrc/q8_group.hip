@@ -10,15 +10,20 @@
 // rows of K per column).
 //
 // Layout.  The [K, N] weight is re-laid out once, offline (wq_prepack_q8),
-// into column panels of P = 16*CPP columns.  A workgroup owns one panel over
-// the whole of K, so no partial sum ever leaves the workgroup.  Inside a
-// panel, thread t = s*CPP + c takes the 16 columns of chunk c and the u rows
-// of slot s, in batches of 8 rows; the packed order puts the 16-byte piece
-// that thread t reads at step i at ((panel*u + i) * active_threads + t) * 16,
-// so every wave load is 1 KB of contiguous memory.  Codes are stored biased
-// (u = q + 128): the bias is removed with one per-batch sum of x, and the
-// biased byte goes straight into an fp16 mantissa as a subnormal (see
-// q8_pairs_sub).
+// into column pairs: pair q (columns 2q, 2q + 1) is K/8 contiguous 16-byte
+// pieces, piece b holding rows 8b .. 8b + 7.  Word d of a piece holds rows
+// 2d and 2d + 1 of column 2q in bytes 0 and 1, and the same rows of column
+// 2q + 1 in bytes 2 and 3, so one v_perm_b32 puts a column's two rows into
+// an fp16 pair (q8_col_pair).  Codes are stored biased (u = q + 128): the
+// bias is removed with one sum of x per piece, and the biased byte goes
+// straight into an fp16 mantissa as a subnormal, u * 2^-24, so every
+// product x * u * 2^-24 is exact in fp32.
+//
+// The product.  A wave owns one column pair over all of K, so no partial sum
+// ever leaves the wave: at step i lane l takes piece 64 i + l of its pair
+// (the wave reads 1 KB of contiguous memory per step), and one cross-lane
+// reduction at the end gives the two outputs.  Eight waves (a 16-column
+// panel) share the activations, staged once per 4096 rows in LDS.
 #include "wq_device.hpp"
 #include "wq_internal.h"
 
@@ -27,286 +32,249 @@ namespace wq {
 // 512 threads (8 wave64s, two per SIMD): while one wave of a SIMD converts
 // its codes the other's loads are still landing.
 constexpr int kQ8Threads = 512;
-constexpr int kQ8Batch = 8;  // rows per batch (never straddles a group: G % 32 == 0)
+constexpr int kQ8Steps = 8;                    // pieces per lane per chunk
+constexpr int kQ8Chunk = 64 * kQ8Steps * 8;    // rows of K per chunk: 4096
 // From this many rows of X on, the product runs as a tiled matrix-core GEMM
-// (q8_gemm.hip) instead of one streaming pass over the weight per 4 rows.
+// (q8_gemm.hip) instead of one streaming pass over the weight per 8 rows.
 constexpr int kQ8GemmMinRows = 32;
 
-// Panel plan: a pure function of (K, N); prepack and product agree on it.
+// Panel plan: 16-column panels (8 column pairs); u = pieces per pair.
 PanelPlan plan_q8(int K, int N) {
   PanelPlan p{};
-  p.P = (N % 32 == 0 && N / 32 >= 256) ? 32 : 16;
-  p.cpp = p.P / 16;
-  p.npanels = N / p.P;
-  const int ns = kQ8Threads / p.cpp;
-  p.u = kQ8Batch * ((K + kQ8Batch * ns - 1) / (kQ8Batch * ns));  // rows per slot
-  p.nsa = (K + p.u - 1) / p.u;                                     // slots in use
-  p.packed_bytes = (size_t)p.npanels * p.u * p.nsa * p.cpp * 16;
+  p.P = 16;
+  p.cpp = 1;
+  p.npanels = N / 16;
+  p.u = K / 8;
+  p.nsa = 0;
+  p.packed_bytes = (size_t)K * N;
   return p;
 }
 
 // ---------------------------------------------------------------------------
-// Offline re-layout: one thread per 16-byte output piece.
+// Offline re-layout: one thread per 16-byte piece (pair q, rows 8b .. 8b + 7).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void q8_prepack_kernel(const int8_t* __restrict__ W,
                                                               uint32_t* __restrict__ out, int K,
-                                                              int N, PanelPlan p) {
+                                                              int N) {
+  const int KB = K / 8;
   const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
-  const int nta = p.nsa * p.cpp;
-  const size_t total = (size_t)p.npanels * p.u * nta;
-  if (idx >= total) return;
-  const int t = (int)(idx % nta);
-  const size_t pi = idx / nta;
-  const int i = (int)(pi % p.u), panel = (int)(pi / p.u);
-  const int s = t / p.cpp, c = t % p.cpp;
-  const int row = s * p.u + i;
-  const int col0 = panel * p.P + 16 * c;
-  uint32_t v[4] = {0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u};  // padding rows: q = 0
-  if (row < K) {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(W + (size_t)row * N + col0);
+  if (idx >= (size_t)(N / 2) * KB) return;
+  const int q = (int)(idx / KB), b = (int)(idx % KB);
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(W) + (size_t)8 * b * N + 2 * q;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) v[d] = src[d] ^ 0x80808080u;
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t r0 = *reinterpret_cast<const uint16_t*>(src + (size_t)(2 * d) * N);
+    const uint32_t r1 = *reinterpret_cast<const uint16_t*>(src + (size_t)(2 * d + 1) * N);
+    // bytes: row 2d col 0, row 2d+1 col 0, row 2d col 1, row 2d+1 col 1
+    const uint32_t v = (r0 & 0xFFu) | ((r1 & 0xFFu) << 8) | ((r0 >> 8) << 16) | ((r1 >> 8) << 24);
+    out[idx * 4 + d] = v ^ 0x80808080u;
   }
-#pragma unroll
-  for (int d = 0; d < 4; ++d) out[idx * 4 + d] = v[d];
 }
 
 // ---------------------------------------------------------------------------
-// The fused product.
+// The fused product, MT rows of X per pass.
 // ---------------------------------------------------------------------------
-// FOLD (M = 1, 16-column panels, 16 u == G): the 16 lanes of a quarter-wave
-// hold the rows of one group, so their sums are reduced first and the
-// group's scale is applied once per column on the reduced value: one 4-byte
-// scale load per lane instead of four 16-byte loads, and one multiply.
-template <int MT, int CPP, bool FOLD>
-__global__ __launch_bounds__(kQ8Threads) void q8_panel_kernel(
+// FOLD (MT = 1, G a multiple of 128): the 16 lanes of a quarter-wave hold 128
+// consecutive rows at every step, i.e. part of one group.  A wave's 16 step
+// values (8 steps x 2 columns) are summed over the quarter with a halving
+// butterfly, which leaves lane l with step (l % 16) / 2 and column l % 2; the
+// group's scale is then applied once, with one 4-byte load per lane per 4096
+// rows.  Otherwise each piece's two sums take their scales (one 8-byte load
+// per piece) before they are added up.
+template <int MT, bool FOLD>
+__global__ __launch_bounds__(kQ8Threads) void q8_pair_kernel(
     const _Float16* __restrict__ X, const uint8_t* __restrict__ Wp,
-    const float* __restrict__ scales, _Float16* __restrict__ Y, int M, int K, int N, int G,
-    int u, int nsa, int packed_bytes) {
-  constexpr int P = 16 * CPP;
-  constexpr int V = 16 * MT;                // results per chunk: [m][16 columns]
-  constexpr int LOWBIT = CPP == 1 ? 0 : 1;  // lane bit 0 selects the chunk when CPP == 2
-  constexpr int LEFT = bfly_left<V, LOWBIT>();
-  constexpr int RB = kQ8Batch;
-  static_assert(!FOLD || (MT == 1 && CPP == 1), "FOLD needs one row and 16-column panels");
-  __shared__ float red[kQ8Threads / 64][CPP][V];
+    const float* __restrict__ scales, _Float16* __restrict__ Y, int M, int K, int N, int G) {
+  static_assert(!FOLD || MT == 1, "FOLD takes one row of X");
+  __shared__ u32x4 xs[MT][kQ8Threads];  // rows r0 .. r0 + 4095 of the MT rows of X
 
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   // Workgroups b and b + 8 run on the same XCD (dispatch is round-robin over
   // the 8 XCDs).  When the panel count allows, they take neighbouring panels,
   // which share the 128-byte lines of the fp32 scale rows, so each line is
   // fetched into one XCD's L2 only.
   const int bid = blockIdx.x;
   const int panel = (gridDim.x % 16 == 0) ? (bid & ~15) + 2 * (bid & 7) + ((bid >> 3) & 1) : bid;
-  const int nta = nsa * CPP;
-  const int c = t % CPP, s = t / CPP;
-  const bool active = t < nta;
-  const int col0 = panel * P + 16 * c;
+  const int q = panel * 8 + wave;  // this wave's column pair
+  const int KB = K / 8;            // pieces per pair
 
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wp, packed_bytes);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wp, K * N);
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, M * K * 2);
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, (K / G) * N * 4);
   const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
-  float accT[MT][16];
+  float tot[MT][2];
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) accT[m][j] = 0.0f;
+  for (int m = 0; m < MT; ++m) tot[m][0] = tot[m][1] = 0.0f;
+  float ftot = 0.0f;
 
-  // FOLD: this lane's scale, group (s u) / G, column col0 + lane % 16.
-  float fold_scale = 0.0f;
-  if constexpr (FOLD) {
-    const bool live0 = active && s * u < K;
-    fold_scale = __builtin_bit_cast(
-        float, __builtin_amdgcn_raw_buffer_load_b32(
-                   sr, live0 ? (((s * u) / G) * N + col0 + (lane & 15)) * 4 : kOutOfRange, 0, 0));
-  }
-
-  const int nb = u / RB;
-  for (int b = 0; b < nb; ++b) {
-    const int row0 = s * u + RB * b;
-    const bool live = active && row0 < K;
-    // Activations of these 8 rows: one 128-bit load per row of X.
-    u32x4 xv[MT];
+  for (int r0 = 0; r0 < K; r0 += kQ8Chunk) {
+    const int b0 = r0 / 8;
+    // Activations first (rows r0 + 8t .. + 7; zero past K and for m >= M),
+    // then the scales, then the weight stream, so waiting for the activations
+    // leaves the rest in flight.
+    u32x4 xg[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
-      xv[m] = __builtin_amdgcn_raw_buffer_load_b128(
-          xr, (live && m < M) ? ((m * K + row0) * 2) : kOutOfRange, 0, 0);
-    // The weight stream: 8 rows x 16 columns; 1 KB contiguous per wave load.
-    u32x4 w[RB];
-    const int wbase = ((panel * u + RB * b) * nta + t) * 16;
+      xg[m] = __builtin_amdgcn_raw_buffer_load_b128(
+          xr, (m < M && r0 + 8 * t < K) ? (m * K + r0 + 8 * t) * 2 : kOutOfRange, 0, 0);
+    constexpr int NS = FOLD ? 1 : kQ8Steps;  // scale loads per lane per chunk
+    float fs = 0.0f;
+    u32x2 sc[NS];
+    if constexpr (FOLD) {
+      // Lane l's value after the butterfly: step (l % 16) / 2, column l % 2,
+      // rows r0 + 512 step + 128 (l / 16) .. + 127, one group.
+      const int row = r0 + 512 * ((lane & 15) >> 1) + 128 * (lane >> 4);
+      fs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                         sr, row < K ? ((row / G) * N + 2 * q + (lane & 1)) * 4 : kOutOfRange,
+                                         0, 0));
+    } else {
 #pragma unroll
-    for (int i = 0; i < RB; ++i) w[i] = buffer_stream(wr, active ? wbase + i * nta * 16 : kOutOfRange);
-    f32x4 sc[4];
-    if constexpr (!FOLD) {
-      const int soff = live ? ((row0 / G) * N + col0) * 4 : kOutOfRange;
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-        sc[d] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, soff + 16 * d, 0, 0));
+      for (int i = 0; i < kQ8Steps; ++i) {
+        const int b = b0 + 64 * i + lane;
+        sc[i] = __builtin_amdgcn_raw_buffer_load_b64(
+            sr, b < KB ? (((8 * b) / G) * N + 2 * q) * 4 : kOutOfRange, 0, 0);
+      }
     }
+    u32x4 w[kQ8Steps];
+#pragma unroll
+    for (int i = 0; i < kQ8Steps; ++i) {
+      const int b = b0 + 64 * i + lane;
+      w[i] = buffer_stream(wr, b < KB ? (q * KB + b) * 16 : kOutOfRange);
+    }
+    wait_vmcnt<kQ8Steps + NS>();  // the activations have landed
+    if (r0 > 0) lds_barrier();     // every wave is done with the previous chunk
+#pragma unroll
+    for (int m = 0; m < MT; ++m) xs[m][t] = xg[m];
+    lds_barrier();
 
-    // The codes are u = q + 128, so every column starts at -128 * sum(x),
-    // in the 2^-24 units of the subnormal products.
-    float acc[MT][16];
+    float v[2 * kQ8Steps];
+#pragma unroll
+    for (int i = 0; i < kQ8Steps; ++i) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const u32x4 xv = xs[m][64 * i + lane];
+        // u = q + 128: both columns start at -128 * sum(x), in 2^-24 units.
+        float xsum = 0.0f;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) xsum = dot2(as_h2(xv[d]), ones, xsum);
+        const float bias = xsum * (-128.0f / kTwo24);
+        float a0 = bias, a1 = bias;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          a0 = dot2(as_h2(q8_col_pair<0>(w[i][d])), as_h2(xv[d]), a0);
+          a1 = dot2(as_h2(q8_col_pair<1>(w[i][d])), as_h2(xv[d]), a1);
+        }
+        if constexpr (FOLD) {
+          v[2 * i] = a0;
+          v[2 * i + 1] = a1;
+        } else {
+          tot[m][0] = __builtin_fmaf(a0, as_f32(sc[i][0]), tot[m][0]);
+          tot[m][1] = __builtin_fmaf(a1, as_f32(sc[i][1]), tot[m][1]);
+        }
+      }
+    }
+    if constexpr (FOLD) {
+      bfly<2 * kQ8Steps, 3, 0>(v, lane);
+      ftot = __builtin_fmaf(v[0], fs, ftot);
+    }
+  }
+
+  if constexpr (FOLD) {
+    // Sum over the steps and quarters (lane bits 5..1); lane l < 2 holds
+    // column 2q + l.
+    float r[1] = {ftot};
+    bfly<1, 5, 1>(r, lane);
+    if (lane < 2) Y[2 * q + lane] = (_Float16)(r[0] * kTwo24);
+  } else {
+    // Value j = 2m + c per lane, reduced over the whole wave.
+    constexpr int V = 2 * MT;
+    float r[V];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      float xs = 0.0f;
-#pragma unroll
-      for (int q = 0; q < RB / 2; ++q) xs = dot2(as_h2(xv[m][q]), ones, xs);
-      const float b0 = xs * (-128.0f / kTwo24);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[m][j] = b0;
+      r[2 * m] = tot[m][0];
+      r[2 * m + 1] = tot[m][1];
     }
-#pragma unroll
-    for (int q = 0; q < RB / 2; ++q) {  // row pair (2q, 2q + 1)
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        h2 pr[4];
-        q8_pairs_sub(w[2 * q][d], w[2 * q + 1][d], pr);
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-          for (int m = 0; m < MT; ++m)
-            acc[m][4 * d + cc] = dot2(pr[cc], as_h2(xv[m][q]), acc[m][4 * d + cc]);
-      }
-    }
-    // One group per batch: scale once (FOLD: after the reduction below).
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        if constexpr (FOLD)
-          accT[m][j] += acc[m][j];
-        else
-          accT[m][j] = __builtin_fmaf(acc[m][j], sc[j >> 2][j & 3], accT[m][j]);
-      }
-  }
-
-  // Reduce over the slots of a chunk: the lanes of a wave, then the waves.
-  float v[V];
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) v[m * 16 + j] = accT[m][j];
-  if constexpr (FOLD) {
-    // Lane bits 3..0 first: lane l keeps column l % 16 of its quarter-wave's
-    // group; scale it; then bits 5 and 4 add the wave's four groups.
-    bfly<16, 3, 0>(v, lane);
-    v[0] *= fold_scale;
-    bfly<1, 5, 4>(v, lane);
-    if (lane < 16) red[wave][0][lane] = v[0];
-  } else {
-    bfly<V, 5, LOWBIT>(v, lane);
+    bfly<V, 5, 0>(r, lane);
     bool owner;
-    const int base = bfly_base<V, LOWBIT>(lane, owner);
+    const int base = bfly_base<V, 0>(lane, owner);
+    constexpr int LEFT = bfly_left<V, 0>();
     if (owner) {
 #pragma unroll
-      for (int j = 0; j < LEFT; ++j) red[wave][c][base + j] = v[j];
+      for (int j = 0; j < LEFT; ++j) {
+        const int m = (base + j) >> 1, c = (base + j) & 1;
+        if (m < M) Y[(size_t)m * N + 2 * q + c] = (_Float16)(r[j] * kTwo24);
+      }
     }
-  }
-  __syncthreads();
-  for (int r = t; r < CPP * V; r += kQ8Threads) {
-    const int rc = r / V, idx = r % V;
-    const int m = idx / 16, col = panel * P + 16 * rc + (idx % 16);
-    float sum = 0.0f;
-#pragma unroll
-    for (int w2 = 0; w2 < kQ8Threads / 64; ++w2) sum += red[w2][rc][idx];
-    if (m < M) Y[(size_t)m * N + col] = (_Float16)(sum * kTwo24);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Bit-exact check of the packed layout: rows (2q, 2q+1) of a slot go through
-// q8_pairs_sub and are written back as signed codes.
+// Bit-exact check of the packed layout: every piece through q8_col_pair,
+// written back as signed codes in [K, N].
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void q8_unpack_kernel(const uint8_t* __restrict__ Wp,
                                                              int8_t* __restrict__ codes, int K,
-                                                             int N, PanelPlan p) {
-  const int nta = p.nsa * p.cpp;
+                                                             int N) {
+  const int KB = K / 8;
   const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
-  const size_t total = (size_t)p.npanels * (p.u / 2) * nta;
-  if (idx >= total) return;
-  const int t = (int)(idx % nta);
-  const size_t pi = idx / nta;
-  const int q = (int)(pi % (p.u / 2)), panel = (int)(pi / (p.u / 2));
-  const int s = t / p.cpp, c = t % p.cpp;
-  const int row = s * p.u + 2 * q;
-  const int col0 = panel * p.P + 16 * c;
-  const u32x4 a = *reinterpret_cast<const u32x4*>(Wp + (((size_t)panel * p.u + 2 * q) * nta + t) * 16);
-  const u32x4 b =
-      *reinterpret_cast<const u32x4*>(Wp + (((size_t)panel * p.u + 2 * q + 1) * nta + t) * 16);
+  if (idx >= (size_t)(N / 2) * KB) return;
+  const int q = (int)(idx / KB), b = (int)(idx % KB);
+  const u32x4 w = *reinterpret_cast<const u32x4*>(Wp + idx * 16);
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    h2 pr[4];
-    q8_pairs_sub(a[d], b[d], pr);
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const uint32_t bits = as_u32(pr[cc]);
-      const int ua = (int)(bits & 0xFFFFu), ub = (int)(bits >> 16);
-      const int col = col0 + 4 * d + cc;
-      if (row < K) codes[(size_t)row * N + col] = (int8_t)(ua - 128);
-      if (row + 1 < K) codes[(size_t)(row + 1) * N + col] = (int8_t)(ub - 128);
-    }
+    const uint32_t c0 = q8_col_pair<0>(w[d]), c1 = q8_col_pair<1>(w[d]);
+    const size_t row = (size_t)8 * b + 2 * d;
+    codes[row * N + 2 * q] = (int8_t)((int)(c0 & 0xFFFFu) - 128);
+    codes[(row + 1) * N + 2 * q] = (int8_t)((int)(c0 >> 16) - 128);
+    codes[row * N + 2 * q + 1] = (int8_t)((int)(c1 & 0xFFFFu) - 128);
+    codes[(row + 1) * N + 2 * q + 1] = (int8_t)((int)(c1 >> 16) - 128);
   }
 }
 
 hipError_t launch_q8_prepack(const int8_t* W, void* packed, int K, int N, hipStream_t s) {
-  const PanelPlan p = plan_q8(K, N);
-  const size_t total = (size_t)p.npanels * p.u * p.nsa * p.cpp;
+  const size_t total = (size_t)(N / 2) * (K / 8);
   hipLaunchKernelGGL(q8_prepack_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, s, W, reinterpret_cast<uint32_t*>(packed), K, N, p);
+                     dim3(kThreads), 0, s, W, reinterpret_cast<uint32_t*>(packed), K, N);
   return hipGetLastError();
 }
 
 hipError_t launch_q8_unpack(const void* packed, int8_t* codes, int K, int N, hipStream_t s) {
-  const PanelPlan p = plan_q8(K, N);
-  const size_t total = (size_t)p.npanels * (p.u / 2) * p.nsa * p.cpp;
+  const size_t total = (size_t)(N / 2) * (K / 8);
   hipLaunchKernelGGL(q8_unpack_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, s, reinterpret_cast<const uint8_t*>(packed), codes, K, N,
-                     p);
+                     dim3(kThreads), 0, s, reinterpret_cast<const uint8_t*>(packed), codes, K, N);
   return hipGetLastError();
 }
 
-template <int MT, int CPP, bool FOLD = false>
+template <int MT, bool FOLD = false>
 static hipError_t launch_q8_t(const void* X, const void* packed, const float* scales, void* Y,
-                              int M, int K, int N, int G, const PanelPlan& p, hipStream_t s) {
-  hipLaunchKernelGGL((q8_panel_kernel<MT, CPP, FOLD>), dim3(p.npanels), dim3(kQ8Threads), 0, s,
+                              int M, int K, int N, int G, hipStream_t s) {
+  hipLaunchKernelGGL((q8_pair_kernel<MT, FOLD>), dim3(N / 16), dim3(kQ8Threads), 0, s,
                      reinterpret_cast<const _Float16*>(X), reinterpret_cast<const uint8_t*>(packed),
-                     scales, reinterpret_cast<_Float16*>(Y), M, K, N, G, p.u, p.nsa,
-                     (int)p.packed_bytes);
+                     scales, reinterpret_cast<_Float16*>(Y), M, K, N, G);
   return hipGetLastError();
-}
-
-template <int MT>
-static hipError_t launch_q8_mt(const void* X, const void* packed, const float* scales, void* Y,
-                               int M, int K, int N, int G, const PanelPlan& p, hipStream_t s) {
-  if constexpr (MT == 1) {
-    if (p.cpp == 1 && 16 * p.u == G)
-      return launch_q8_t<1, 1, true>(X, packed, scales, Y, M, K, N, G, p, s);
-  }
-  return p.cpp == 1 ? launch_q8_t<MT, 1>(X, packed, scales, Y, M, K, N, G, p, s)
-                    : launch_q8_t<MT, 2>(X, packed, scales, Y, M, K, N, G, p, s);
 }
 
 hipError_t launch_q8_group(const void* X, const void* packed, const float* scales, void* Y, int M,
                            int K, int N, int G, hipStream_t s) {
   if (M >= kQ8GemmMinRows && q8_gemm_supported(M, K, N, G))
     return launch_q8_gemm(X, packed, scales, Y, M, K, N, G, s);
-  const PanelPlan p = plan_q8(K, N);
-  // Rows of X beyond 4 run as further launches over the same panels (the
-  // accumulators of 4 rows x 16 columns x 2 fill the register budget of a
-  // 512-thread workgroup).
-  for (int m0 = 0; m0 < M; m0 += 4) {
-    const int mc = (M - m0) < 4 ? (M - m0) : 4;
+  // Rows of X beyond 8 run as further launches over the same weight.
+  for (int m0 = 0; m0 < M; m0 += 8) {
+    const int mc = (M - m0) < 8 ? (M - m0) : 8;
     const void* Xc = reinterpret_cast<const char*>(X) + (size_t)m0 * K * 2;
     void* Yc = reinterpret_cast<char*>(Y) + (size_t)m0 * N * 2;
     hipError_t e;
-    switch (mc) {
-      case 1: e = launch_q8_mt<1>(Xc, packed, scales, Yc, mc, K, N, G, p, s); break;
-      case 2: e = launch_q8_mt<2>(Xc, packed, scales, Yc, mc, K, N, G, p, s); break;
-      default: e = launch_q8_mt<4>(Xc, packed, scales, Yc, mc, K, N, G, p, s); break;
-    }
+    if (mc == 1)
+      e = G % 128 == 0 ? launch_q8_t<1, true>(Xc, packed, scales, Yc, mc, K, N, G, s)
+                       : launch_q8_t<1>(Xc, packed, scales, Yc, mc, K, N, G, s);
+    else if (mc == 2)
+      e = launch_q8_t<2>(Xc, packed, scales, Yc, mc, K, N, G, s);
+    else if (mc <= 4)
+      e = launch_q8_t<4>(Xc, packed, scales, Yc, mc, K, N, G, s);
+    else
+      e = launch_q8_t<8>(Xc, packed, scales, Yc, mc, K, N, G, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -19,6 +19,7 @@ namespace wq {
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kTwo24 = 16777216.0f;      // 2^24: undoes the subnormal scale
@@ -98,14 +99,13 @@ __device__ __forceinline__ uint32_t q3_window(uint32_t w0, uint32_t w1, uint32_t
 // Subnormal-pair extractors (the fast path).  Values are in units of 2^-24.
 // ---------------------------------------------------------------------------
 
-// int8, stored biased as u = q + 128: words ra, rb hold 4 consecutive
-// columns of rows k and k+1; out[c] = (u[k][c], u[k+1][c]) * 2^-24.  One
-// v_perm_b32 per pair (byte c of each row into the low byte of each half).
-__device__ __forceinline__ void q8_pairs_sub(uint32_t ra, uint32_t rb, h2 out[4]) {
-  out[0] = as_h2(__builtin_amdgcn_perm(ra, rb, 0x0c000c04u));
-  out[1] = as_h2(__builtin_amdgcn_perm(ra, rb, 0x0c010c05u));
-  out[2] = as_h2(__builtin_amdgcn_perm(ra, rb, 0x0c020c06u));
-  out[3] = as_h2(__builtin_amdgcn_perm(ra, rb, 0x0c030c07u));
+// int8, stored biased as u = q + 128, in the column-pair layout: byte 0 and
+// byte 1 of word w are two consecutive rows of one column, bytes 2 and 3 the
+// same rows of the next column.  C selects the column; the result is its two
+// rows as (u_lo, u_hi) * 2^-24, one v_perm_b32.
+template <int C>
+__device__ __forceinline__ uint32_t q8_col_pair(uint32_t w) {
+  return __builtin_amdgcn_perm(0u, w, C ? 0x0c030c02u : 0x0c010c00u);
 }
 
 // 3-bit: pair P of q3_pair(P) as (c_a * 2^pa, c_b * 2^pb) * 2^-24.
