@@ -63,6 +63,7 @@ def assert_tol(y, y_exact, what=""):
     (1, 8192, 1024, 128),        # two chunks of 4096 rows, folded scales
     (1, 4608, 256, 512),         # a ragged second chunk (512 of 4096 rows)
     (1, 1152, 256, 96),          # group of 96 rows: a scale per piece, one row
+    (1, 1536, 256, 384),         # group of 384 rows (not a power of two): a scale per piece
     (6, 8192, 512, 128),         # 8-row pass, activations restaged in LDS per chunk
     (7, 4224, 272, 64),          # 8-row pass, ragged chunk, scale per piece
 ])

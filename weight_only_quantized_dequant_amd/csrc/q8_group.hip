@@ -74,8 +74,9 @@ __global__ __launch_bounds__(kThreads) void q8_prepack_kernel(const int8_t* __re
 // ---------------------------------------------------------------------------
 // The fused product, MT rows of X per pass.
 // ---------------------------------------------------------------------------
-// FOLD (MT = 1, G a multiple of 128): the 16 lanes of a quarter-wave hold 128
-// consecutive rows at every step, i.e. part of one group.  A wave's 16 step
+// FOLD (MT = 1, G a power of two >= 128, log2 G = gsh): the 16 lanes of a
+// quarter-wave hold 128 consecutive rows at every step, i.e. part of one
+// group.  A wave's 16 step
 // values (8 steps x 2 columns) are summed over the quarter with a halving
 // butterfly, which leaves lane l with step (l % 16) / 2 and column l % 2; the
 // group's scale is then applied once, with one 4-byte load per lane per 4096
@@ -84,7 +85,8 @@ __global__ __launch_bounds__(kThreads) void q8_prepack_kernel(const int8_t* __re
 template <int MT, bool FOLD>
 __global__ __launch_bounds__(kQ8Threads) void q8_pair_kernel(
     const _Float16* __restrict__ X, const uint8_t* __restrict__ Wp,
-    const float* __restrict__ scales, _Float16* __restrict__ Y, int M, int K, int N, int G) {
+    const float* __restrict__ scales, _Float16* __restrict__ Y, int M, int K, int N, int G,
+    int gsh) {
   static_assert(!FOLD || MT == 1, "FOLD takes one row of X");
   __shared__ u32x4 xs[MT][kQ8Threads];  // rows r0 .. r0 + 4095 of the MT rows of X
 
@@ -127,7 +129,7 @@ __global__ __launch_bounds__(kQ8Threads) void q8_pair_kernel(
       // rows r0 + 512 step + 128 (l / 16) .. + 127, one group.
       const int row = r0 + 512 * ((lane & 15) >> 1) + 128 * (lane >> 4);
       fs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                         sr, row < K ? ((row / G) * N + 2 * q + (lane & 1)) * 4 : kOutOfRange,
+                                         sr, row < K ? ((row >> gsh) * N + 2 * q + (lane & 1)) * 4 : kOutOfRange,
                                          0, 0));
     } else {
 #pragma unroll
@@ -149,22 +151,34 @@ __global__ __launch_bounds__(kQ8Threads) void q8_pair_kernel(
     for (int m = 0; m < MT; ++m) xs[m][t] = xg[m];
     lds_barrier();
 
+    // The activations of every step and their sums first: they do not wait
+    // for the weights.  u = q + 128: both columns of a piece start at
+    // -128 * sum(x), in 2^-24 units.
+    u32x4 xv[kQ8Steps][MT];
+    float bias[kQ8Steps][MT];
+#pragma unroll
+    for (int i = 0; i < kQ8Steps; ++i)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) xv[i][m] = xs[m][64 * i + lane];
+#pragma unroll
+    for (int i = 0; i < kQ8Steps; ++i)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        float xsum = 0.0f;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) xsum = dot2(as_h2(xv[i][m][d]), ones, xsum);
+        bias[i][m] = xsum * (-128.0f / kTwo24);
+      }
     float v[2 * kQ8Steps];
 #pragma unroll
     for (int i = 0; i < kQ8Steps; ++i) {
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        const u32x4 xv = xs[m][64 * i + lane];
-        // u = q + 128: both columns start at -128 * sum(x), in 2^-24 units.
-        float xsum = 0.0f;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) xsum = dot2(as_h2(xv[d]), ones, xsum);
-        const float bias = xsum * (-128.0f / kTwo24);
-        float a0 = bias, a1 = bias;
+        float a0 = bias[i][m], a1 = bias[i][m];
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          a0 = dot2(as_h2(q8_col_pair<0>(w[i][d])), as_h2(xv[d]), a0);
-          a1 = dot2(as_h2(q8_col_pair<1>(w[i][d])), as_h2(xv[d]), a1);
+          a0 = dot2(as_h2(q8_col_pair<0>(w[i][d])), as_h2(xv[i][m][d]), a0);
+          a1 = dot2(as_h2(q8_col_pair<1>(w[i][d])), as_h2(xv[i][m][d]), a1);
         }
         if constexpr (FOLD) {
           v[2 * i] = a0;
@@ -250,9 +264,11 @@ hipError_t launch_q8_unpack(const void* packed, int8_t* codes, int K, int N, hip
 template <int MT, bool FOLD = false>
 static hipError_t launch_q8_t(const void* X, const void* packed, const float* scales, void* Y,
                               int M, int K, int N, int G, hipStream_t s) {
+  int gsh = 0;
+  while ((1 << gsh) < G) ++gsh;
   hipLaunchKernelGGL((q8_pair_kernel<MT, FOLD>), dim3(N / 16), dim3(kQ8Threads), 0, s,
                      reinterpret_cast<const _Float16*>(X), reinterpret_cast<const uint8_t*>(packed),
-                     scales, reinterpret_cast<_Float16*>(Y), M, K, N, G);
+                     scales, reinterpret_cast<_Float16*>(Y), M, K, N, G, gsh);
   return hipGetLastError();
 }
 
@@ -267,7 +283,7 @@ hipError_t launch_q8_group(const void* X, const void* packed, const float* scale
     void* Yc = reinterpret_cast<char*>(Y) + (size_t)m0 * N * 2;
     hipError_t e;
     if (mc == 1)
-      e = G % 128 == 0 ? launch_q8_t<1, true>(Xc, packed, scales, Yc, mc, K, N, G, s)
+      e = (G >= 128 && (G & (G - 1)) == 0) ? launch_q8_t<1, true>(Xc, packed, scales, Yc, mc, K, N, G, s)
                        : launch_q8_t<1>(Xc, packed, scales, Yc, mc, K, N, G, s);
     else if (mc == 2)
       e = launch_q8_t<2>(Xc, packed, scales, Yc, mc, K, N, G, s);
