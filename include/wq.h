@@ -113,8 +113,9 @@ int wq_matvec_q3(const void* x, const void* packed, const void* scales, const vo
 
 /* ----------------------------------------------------------------- int8 -- */
 
-/* Re-lay out a group-wise int8 weight qweight [K, N] (codes -127..127).
- * packed: wq_packed_bytes(WQ_OP_Q8G, K, N, G) bytes, written.
+/* Re-lay out a group-wise int8 weight qweight [K, N] (codes -127..127) into
+ * column pairs of 16-byte pieces (8 rows x 2 columns, K/8 pieces per pair).
+ * packed: wq_packed_bytes(WQ_OP_Q8G, K, N, G) = K * N bytes, written.
  * Rules: K % 32 == 0, N % 16 == 0. */
 int wq_prepack_q8(const int8_t* qweight, void* packed, int K, int N, void* stream);
 
@@ -124,7 +125,7 @@ int wq_prepack_q8(const int8_t* qweight, void* packed, int K, int N, void* strea
  * Y [M, N] fp16, written (fp32 accumulation, one round to nearest even).
  * Evaluated per group as scale * (sum of X * q), exact products, fp32 sums.
  * M < 32, or G not a multiple of 64: streaming passes over the packed weight
- * (one per 4 rows of X).  Otherwise one tiled matrix-core launch (32 x 128
+ * (one per 8 rows of X).  Otherwise one tiled matrix-core launch (32 x 128
  * output tiles) that reads the same packed weight.
  * ("Quantization CUDA", tom-jerr.github.io, "Int8 Weight Only Quantization";
  * "融合反量化与GEMM：LLM推理的CUDA内核优化实践", zingnex.cn, "技术实现细节".)
