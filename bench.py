@@ -111,7 +111,7 @@ def wl_q8(wq, torch, dev, M=1):
     def run(c):
         wq.gemm_q8_group(c[0], c[1], c[2], G, Y=c[3])
 
-    kind = "gemv" if M == 1 else "gemm"
+    kind = "gemv" if M == 1 else "streaming" if M < 32 else "gemm"
     w = Workload(f"q8_group_{kind} M={M} K={K} N={N} G={G}", nbytes, make, run,
                  flops=0 if M == 1 else 2 * M * K * N)
     w.peak_tops = FP16_PEAK_TFLOPS
@@ -438,7 +438,8 @@ def main():
     if not args.headline_only:
         sec = {}
         for name in ("q3_f32_1024", "q3_f16_4096x4096", "q3_f16_4096x11008", "q3_f16_11008x4096",
-                     "q4_m1", "q4_m2", "q4_m4", "q4_m8", "q4zp_m1", "q4zp_g64_m1", "q2_m1", "q2_m8", "q8_m512", "w8a8", "w8a8_smooth", "int8_mixed"):
+                     "q4_m1", "q4_m2", "q4_m4", "q4_m8", "q4zp_m1", "q4zp_g64_m1", "q2_m1", "q2_m8", "q8_m2", "q8_m8",
+                     "q8_m512", "w8a8", "w8a8_smooth", "int8_mixed"):
             sw = make(name)
             big = name.startswith("w8a8") or name == "int8_mixed"
             sms, sR = time_workload(torch, sw, 100 if big else 300, 10 if big else 30)
