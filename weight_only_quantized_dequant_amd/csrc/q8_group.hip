@@ -76,12 +76,30 @@ __global__ __launch_bounds__(kThreads) void q8_prepack_kernel(const int8_t* __re
 // ---------------------------------------------------------------------------
 // FOLD (MT = 1, G a power of two >= 128, log2 G = gsh): the 16 lanes of a
 // quarter-wave hold 128 consecutive rows at every step, i.e. part of one
-// group.  A wave's 16 step
-// values (8 steps x 2 columns) are summed over the quarter with a halving
-// butterfly, which leaves lane l with step (l % 16) / 2 and column l % 2; the
-// group's scale is then applied once, with one 4-byte load per lane per 4096
-// rows.  Otherwise each piece's two sums take their scales (one 8-byte load
-// per piece) before they are added up.
+// group, so a quarter needs 16 scales per 4096 rows (8 steps x 2 columns).
+// Lane j of the quarter loads the one of step j / 2, column j % 2 (one 4-byte
+// load per lane), and a DPP row broadcast hands it to the other 15 lanes as
+// each step value is scaled.  Otherwise each piece's two sums take their
+// scales (one 8-byte load per piece) before they are added up.
+// Lane J of each 16-lane row, to every lane of the row (DPP row_newbcast).
+template <int J>
+__device__ __forceinline__ float q8_row_share(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + J, 0xF, 0xF, false));
+}
+// t_c += v[j] * (scale j of the quarter) for the 16 step values, j = 2i + c.
+template <int J = 0>
+__device__ __forceinline__ void q8_fold_scales(const float* v, float fs, float& t0, float& t1) {
+  if constexpr (J < 2 * kQ8Steps) {
+    const float sj = q8_row_share<J>(fs);
+    if constexpr (J & 1)
+      t1 = __builtin_fmaf(v[J], sj, t1);
+    else
+      t0 = __builtin_fmaf(v[J], sj, t0);
+    q8_fold_scales<J + 1>(v, fs, t0, t1);
+  }
+}
+
 template <int MT, bool FOLD>
 __global__ __launch_bounds__(kQ8Threads) void q8_pair_kernel(
     const _Float16* __restrict__ X, const uint8_t* __restrict__ Wp,
@@ -109,7 +127,6 @@ __global__ __launch_bounds__(kQ8Threads) void q8_pair_kernel(
   float tot[MT][2];
 #pragma unroll
   for (int m = 0; m < MT; ++m) tot[m][0] = tot[m][1] = 0.0f;
-  float ftot = 0.0f;
 
   for (int r0 = 0; r0 < K; r0 += kQ8Chunk) {
     const int b0 = r0 / 8;
@@ -125,8 +142,8 @@ __global__ __launch_bounds__(kQ8Threads) void q8_pair_kernel(
     float fs = 0.0f;
     u32x2 sc[NS];
     if constexpr (FOLD) {
-      // Lane l's value after the butterfly: step (l % 16) / 2, column l % 2,
-      // rows r0 + 512 step + 128 (l / 16) .. + 127, one group.
+      // Lane l's scale: step (l % 16) / 2, column l % 2, the group of rows
+      // r0 + 512 step + 128 (l / 16) .. + 127.
       const int row = r0 + 512 * ((lane & 15) >> 1) + 128 * (lane >> 4);
       fs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                          sr, row < K ? ((row >> gsh) * N + 2 * q + (lane & 1)) * 4 : kOutOfRange,
@@ -190,18 +207,11 @@ __global__ __launch_bounds__(kQ8Threads) void q8_pair_kernel(
       }
     }
     if constexpr (FOLD) {
-      bfly<2 * kQ8Steps, 3, 0>(v, lane);
-      ftot = __builtin_fmaf(v[0], fs, ftot);
+      q8_fold_scales(v, fs, tot[0][0], tot[0][1]);
     }
   }
 
-  if constexpr (FOLD) {
-    // Sum over the steps and quarters (lane bits 5..1); lane l < 2 holds
-    // column 2q + l.
-    float r[1] = {ftot};
-    bfly<1, 5, 1>(r, lane);
-    if (lane < 2) Y[2 * q + lane] = (_Float16)(r[0] * kTwo24);
-  } else {
+  {
     // Value j = 2m + c per lane, reduced over the whole wave.
     constexpr int V = 2 * MT;
     float r[V];
