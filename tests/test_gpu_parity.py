@@ -56,6 +56,7 @@ def assert_tol(y, y_exact, what=""):
 
 @pytest.mark.parametrize("M,K,N,G", [
     (1, 4096, 4096, 128),        # the headline GEMV
+    (2, 4096, 4096, 128), (8, 4096, 4096, 128),  # the streaming lines the bench times
     (1, 256, 16, 128), (1, 384, 272, 128), (2, 512, 1024, 64), (3, 640, 528, 128),
     (4, 4096, 1040, 128), (5, 1024, 256, 32), (8, 2048, 4096, 128), (9, 768, 784, 128),
     (16, 256, 512, 256),
