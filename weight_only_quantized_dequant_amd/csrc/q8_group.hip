@@ -81,6 +81,16 @@ __global__ __launch_bounds__(kThreads) void q8_prepack_kernel(const int8_t* __re
 // load per lane), and a DPP row broadcast hands it to the other 15 lanes as
 // each step value is scaled.  Otherwise each piece's two sums take their
 // scales (one 8-byte load per piece) before they are added up.
+// u = q + 128: both columns of a piece start at -128 * sum(x) over the
+// piece's 8 activations, in 2^-24 units.
+__device__ __forceinline__ float q8_piece_bias(const u32x4 x) {
+  const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+  float s = 0.0f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) s = dot2(as_h2(x[d]), ones, s);
+  return s * (-128.0f / kTwo24);
+}
+
 // Lane J of each 16-lane row, to every lane of the row (DPP row_newbcast).
 template <int J>
 __device__ __forceinline__ float q8_row_share(float x) {
@@ -107,6 +117,11 @@ __global__ __launch_bounds__(kQ8Threads) void q8_pair_kernel(
     int gsh) {
   static_assert(!FOLD || MT == 1, "FOLD takes one row of X");
   __shared__ u32x4 xs[MT][kQ8Threads];  // rows r0 .. r0 + 4095 of the MT rows of X
+  // With several rows of X, each piece's sum of x is formed once, by the
+  // thread that stages it, for all eight waves (MT > 1 only: at one row the
+  // sums are cheaper inside each wave, off the path to the barrier).
+  constexpr bool XB = MT > 1;
+  __shared__ float xb[XB ? MT : 1][kQ8Threads];  // -128 * 2^-24 * (sum of a piece's 8 x)
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -122,7 +137,6 @@ __global__ __launch_bounds__(kQ8Threads) void q8_pair_kernel(
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wp, K * N);
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, M * K * 2);
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, (K / G) * N * 4);
-  const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
   float tot[MT][2];
 #pragma unroll
@@ -165,27 +179,29 @@ __global__ __launch_bounds__(kQ8Threads) void q8_pair_kernel(
     wait_vmcnt<kQ8Steps + NS>();  // the activations have landed
     if (r0 > 0) lds_barrier();     // every wave is done with the previous chunk
 #pragma unroll
-    for (int m = 0; m < MT; ++m) xs[m][t] = xg[m];
+    for (int m = 0; m < MT; ++m) {
+      xs[m][t] = xg[m];
+      if constexpr (XB) xb[m][t] = q8_piece_bias(xg[m]);
+    }
     lds_barrier();
 
-    // The activations of every step and their sums first: they do not wait
-    // for the weights.  u = q + 128: both columns of a piece start at
-    // -128 * sum(x), in 2^-24 units.
+    // The activations of every step and their piece sums first: they do
+    // not wait for the weights.
     u32x4 xv[kQ8Steps][MT];
     float bias[kQ8Steps][MT];
 #pragma unroll
     for (int i = 0; i < kQ8Steps; ++i)
 #pragma unroll
-      for (int m = 0; m < MT; ++m) xv[i][m] = xs[m][64 * i + lane];
-#pragma unroll
-    for (int i = 0; i < kQ8Steps; ++i)
-#pragma unroll
       for (int m = 0; m < MT; ++m) {
-        float xsum = 0.0f;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) xsum = dot2(as_h2(xv[i][m][d]), ones, xsum);
-        bias[i][m] = xsum * (-128.0f / kTwo24);
+        xv[i][m] = xs[m][64 * i + lane];
+        if constexpr (XB) bias[i][m] = xb[m][64 * i + lane];
       }
+    if constexpr (!XB) {
+#pragma unroll
+      for (int i = 0; i < kQ8Steps; ++i)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) bias[i][m] = q8_piece_bias(xv[i][m]);
+    }
     float v[2 * kQ8Steps];
 #pragma unroll
     for (int i = 0; i < kQ8Steps; ++i) {
