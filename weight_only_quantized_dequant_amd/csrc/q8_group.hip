@@ -74,13 +74,13 @@ __global__ __launch_bounds__(kThreads) void q8_prepack_kernel(const int8_t* __re
 // ---------------------------------------------------------------------------
 // The fused product, MT rows of X per pass.
 // ---------------------------------------------------------------------------
-// FOLD (MT = 1, G a power of two >= 128, log2 G = gsh): the 16 lanes of a
-// quarter-wave hold 128 consecutive rows at every step, i.e. part of one
-// group, so a quarter needs 16 scales per 4096 rows (8 steps x 2 columns).
-// Lane j of the quarter loads the one of step j / 2, column j % 2 (one 4-byte
-// load per lane), and a DPP row broadcast hands it to the other 15 lanes as
-// each step value is scaled.  Otherwise each piece's two sums take their
-// scales (one 8-byte load per piece) before they are added up.
+// FOLD (one or two rows of X, G a power of two >= 128, log2 G = gsh): the
+// 16 lanes of a quarter-wave hold 128 consecutive rows at every step, i.e.
+// part of one group, so a quarter needs 16 scales per 4096 rows (8 steps x 2
+// columns).  Lane j of the quarter loads the one of step j / 2, column j % 2
+// (one 4-byte load per lane), and DPP row broadcasts hand all 16 to every
+// lane of the quarter as soon as it lands, before the weights.  Otherwise
+// each piece's two sums take their scales (one 8-byte load per piece).
 // u = q + 128: both columns of a piece start at -128 * sum(x) over the
 // piece's 8 activations, in 2^-24 units.
 __device__ __forceinline__ float q8_piece_bias(const u32x4 x) {
@@ -97,16 +97,12 @@ __device__ __forceinline__ float q8_row_share(float x) {
   return __builtin_bit_cast(
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + J, 0xF, 0xF, false));
 }
-// t_c += v[j] * (scale j of the quarter) for the 16 step values, j = 2i + c.
+// s[j] = lane j's value of this lane's 16-lane row, j = 0 .. 15.
 template <int J = 0>
-__device__ __forceinline__ void q8_fold_scales(const float* v, float fs, float& t0, float& t1) {
+__device__ __forceinline__ void q8_row_all(float x, float (&s)[2 * kQ8Steps]) {
   if constexpr (J < 2 * kQ8Steps) {
-    const float sj = q8_row_share<J>(fs);
-    if constexpr (J & 1)
-      t1 = __builtin_fmaf(v[J], sj, t1);
-    else
-      t0 = __builtin_fmaf(v[J], sj, t0);
-    q8_fold_scales<J + 1>(v, fs, t0, t1);
+    s[J] = q8_row_share<J>(x);
+    q8_row_all<J + 1>(x, s);
   }
 }
 
@@ -115,7 +111,6 @@ __global__ __launch_bounds__(kQ8Threads) void q8_pair_kernel(
     const _Float16* __restrict__ X, const uint8_t* __restrict__ Wp,
     const float* __restrict__ scales, _Float16* __restrict__ Y, int M, int K, int N, int G,
     int gsh) {
-  static_assert(!FOLD || MT == 1, "FOLD takes one row of X");
   __shared__ u32x4 xs[MT][kQ8Threads];  // rows r0 .. r0 + 4095 of the MT rows of X
   // With several rows of X, each piece's sum of x is formed once, by the
   // thread that stages it, for all eight waves (MT > 1 only: at one row the
@@ -202,7 +197,10 @@ __global__ __launch_bounds__(kQ8Threads) void q8_pair_kernel(
 #pragma unroll
         for (int m = 0; m < MT; ++m) bias[i][m] = q8_piece_bias(xv[i][m]);
     }
-    float v[2 * kQ8Steps];
+    // The quarter's 16 scales in every lane (FOLD): scale of step i,
+    // column c at fsq[2i + c].
+    float fsq[2 * kQ8Steps];
+    if constexpr (FOLD) q8_row_all(fs, fsq);
 #pragma unroll
     for (int i = 0; i < kQ8Steps; ++i) {
 #pragma unroll
@@ -213,17 +211,11 @@ __global__ __launch_bounds__(kQ8Threads) void q8_pair_kernel(
           a0 = dot2(as_h2(q8_col_pair<0>(w[i][d])), as_h2(xv[i][m][d]), a0);
           a1 = dot2(as_h2(q8_col_pair<1>(w[i][d])), as_h2(xv[i][m][d]), a1);
         }
-        if constexpr (FOLD) {
-          v[2 * i] = a0;
-          v[2 * i + 1] = a1;
-        } else {
-          tot[m][0] = __builtin_fmaf(a0, as_f32(sc[i][0]), tot[m][0]);
-          tot[m][1] = __builtin_fmaf(a1, as_f32(sc[i][1]), tot[m][1]);
-        }
+        const float s0 = FOLD ? fsq[2 * i] : as_f32(sc[i][0]);
+        const float s1 = FOLD ? fsq[2 * i + 1] : as_f32(sc[i][1]);
+        tot[m][0] = __builtin_fmaf(a0, s0, tot[m][0]);
+        tot[m][1] = __builtin_fmaf(a1, s1, tot[m][1]);
       }
-    }
-    if constexpr (FOLD) {
-      q8_fold_scales(v, fs, tot[0][0], tot[0][1]);
     }
   }
 
@@ -308,12 +300,14 @@ hipError_t launch_q8_group(const void* X, const void* packed, const float* scale
     const void* Xc = reinterpret_cast<const char*>(X) + (size_t)m0 * K * 2;
     void* Yc = reinterpret_cast<char*>(Y) + (size_t)m0 * N * 2;
     hipError_t e;
+    const bool fold = G >= 128 && (G & (G - 1)) == 0;
     if (mc == 1)
-      e = (G >= 128 && (G & (G - 1)) == 0) ? launch_q8_t<1, true>(Xc, packed, scales, Yc, mc, K, N, G, s)
-                       : launch_q8_t<1>(Xc, packed, scales, Yc, mc, K, N, G, s);
+      e = fold ? launch_q8_t<1, true>(Xc, packed, scales, Yc, mc, K, N, G, s)
+               : launch_q8_t<1>(Xc, packed, scales, Yc, mc, K, N, G, s);
     else if (mc == 2)
-      e = launch_q8_t<2>(Xc, packed, scales, Yc, mc, K, N, G, s);
-    else if (mc <= 4)
+      e = fold ? launch_q8_t<2, true>(Xc, packed, scales, Yc, mc, K, N, G, s)
+               : launch_q8_t<2>(Xc, packed, scales, Yc, mc, K, N, G, s);
+    else if (mc <= 4)  // per-piece scales: measured faster than the fold from 4 rows on
       e = launch_q8_t<4>(Xc, packed, scales, Yc, mc, K, N, G, s);
     else
       e = launch_q8_t<8>(Xc, packed, scales, Yc, mc, K, N, G, s);
