@@ -12,14 +12,20 @@ served by the 256 MB Infinity Cache or the L2s, the argument set is
 replicated R times (R * bytes >= 512 MB) and the steps cycle through the
 copies.  Time is taken with HIP events on the stream the kernels are
 launched on, bracketing exactly `--steps` calls after `--warmup` untimed
-ones.
+ones.  Before each timed region a pre-roll of one call per copy evicts the
+copies the timed calls read, and a spin kernel keeps the GPU busy until all
+timed calls are queued, so the events see the kernels back to back.  The
+timed region is repeated (--trials) and the median is reported.
 
 Extra fields on the single JSON line:
 * roofline: the dominant (only) kernel's bandwidth against 8 TB/s; "traffic"
   comes from the rocprofv3 counter summary committed under profiles/ when it
   was taken on the current kernel source, else null.
 * cpu_baseline: the CPU oracle (numpy, fp64) timed on this host on the same
-  workload, repeated for a bounded ~10 s.
+  workload, in child processes started before the GPU is touched: one leg
+  with the job's BLAS thread count and one with a single thread, each about
+  8 s of calls timed one by one (median), with the host's visible cores and
+  CPU model.
 * calibration (headline only): an empty kernel with the GEMV's grid (the
   dispatch floor) and a kernel that only streams each copy's packed weight
   once with the GEMV's loads (the achievable time for those bytes here), on
@@ -259,52 +265,96 @@ def wl_w8a8(wq, torch, dev, smooth=False):
     return w
 
 
-def time_workload(torch, w, steps, warmup, R=None, eager=False):
-    """Average time of one step over exactly `steps` back-to-back steps.
+def _median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
 
-    The steps are captured once into a HIP graph (each one a separate call on
-    the next copy of the arguments), so what is timed is the GPU work, not the
-    Python argument checks of each call.  HIP events bracket one replay of the
-    graph on the stream it runs on.
+
+_SPIN_CYCLES_PER_MS = None
+
+
+def _spin_rate(torch):
+    """Cycles per millisecond of torch's spin kernel on this GPU (measured once)."""
+    global _SPIN_CYCLES_PER_MS
+    if _SPIN_CYCLES_PER_MS is None:
+        torch.cuda._sleep(1000)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.cuda._sleep(2_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        _SPIN_CYCLES_PER_MS = 2_000_000 / a.elapsed_time(b)
+    return _SPIN_CYCLES_PER_MS
+
+
+def time_workload(torch, w, steps, warmup, R=None, trials=None, method="eager"):
+    """Time of one step: the median over trials of exactly `steps` back-to-back steps.
+
+    Every trial, on the current stream (the one the library launches on):
+    1. a pre-roll, one call on each of the R copies, replayed from a captured
+       graph: when timed call i runs, the R - 1 other copies (>= 512 MB for
+       the streaming workloads) have been read since copy i was, so its
+       weights come from HBM, not from the 256 MB Infinity Cache or the L2s;
+    2. a spin kernel that holds the GPU for twice the host time of issuing
+       `steps` calls (measured on an untimed pass), so the timed calls are
+       all queued before the first one starts;
+    3. the start event, exactly `steps` calls (call i on copy i mod R) issued
+       one by one through the library, the end event.
+    The step time is the events' elapsed time over `steps`; the median over
+    trials is returned.  method="graph" instead replays a captured graph of
+    the `steps` calls between the events (each replay then adds a fixed
+    cost of several microseconds on the GPU).
+    Returns (median ms per step, R, per-trial ms per step).
     """
     R = R or _rotation(w.nbytes)
     copies = w.make(R)
     for i in range(warmup):
         w.run(copies[i % R])
     torch.cuda.synchronize()
-    if eager:
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        start.record()
-        for i in range(steps):
-            w.run(copies[i % R])
-        end.record()
-        torch.cuda.synchronize()
-        ms = start.elapsed_time(end) / steps
-        del copies
-        torch.cuda.empty_cache()
-        return ms, R
-    stream = torch.cuda.Stream()
-    stream.wait_stream(torch.cuda.current_stream())
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(stream):
+    if trials is None:
+        trials = 11 if steps <= 500 else 5
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    preroll, timed = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
         w.run(copies[0])  # first call on the side stream, outside the capture
         torch.cuda.current_stream().synchronize()
-        with torch.cuda.graph(graph, stream=stream):
+        with torch.cuda.graph(preroll, stream=side):
+            for i in range(R):
+                w.run(copies[i])
+        if method == "graph":
+            with torch.cuda.graph(timed, stream=side):
+                for i in range(steps):
+                    w.run(copies[i % R])
+    torch.cuda.synchronize()
+    preroll.replay()  # untimed: the first replay of a graph uploads it
+    if method == "graph":
+        timed.replay()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        w.run(copies[i % R])
+    host_ms = (time.perf_counter() - t0) * 1e3
+    torch.cuda.synchronize()
+    spin = int(_spin_rate(torch) * (2.0 * host_ms + 0.2))
+    per = []
+    for _ in range(trials):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        preroll.replay()
+        torch.cuda._sleep(spin)
+        start.record()
+        if method == "graph":
+            timed.replay()
+        else:
             for i in range(steps):
                 w.run(copies[i % R])
-    torch.cuda.synchronize()
-    graph.replay()  # untimed: first replay uploads the graph
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        start.record(stream)
-        graph.replay()
-        end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
-    del graph, copies
+        end.record()
+        torch.cuda.synchronize()
+        per.append(start.elapsed_time(end) / steps)
+    del preroll, timed, copies
     torch.cuda.empty_cache()
-    return ms, R
+    return _median(per), R, per
 
 
 def calibration(wq, torch, w, steps, warmup, gemv_ms):
@@ -322,9 +372,9 @@ def calibration(wq, torch, w, steps, warmup, gemv_ms):
         wq.calib_stream_read(c[1], sink)
 
     sw = Workload("stream read of the packed weight", w.nbytes, w.make, run_stream)
-    s_ms, R = time_workload(torch, sw, steps, warmup)
-    ew = Workload("empty kernel", 0, lambda R: [[None]], lambda c: wq.calib_empty(sink, 256, 512))
-    e_ms, _ = time_workload(torch, ew, steps, warmup, R=1)
+    s_ms, R, _ = time_workload(torch, sw, steps, warmup)
+    ew = Workload("empty kernel", 0, lambda R: [[None]] * R, lambda c: wq.calib_empty(sink, 256, 512))
+    e_ms, _, _ = time_workload(torch, ew, steps, warmup, R=1)
     wbytes = w.make(1)[0][1].numel()
     return {"empty_kernel_us": round(e_ms * 1e3, 3), "stream_read_us": round(s_ms * 1e3, 3),
             "stream_read_bytes": wbytes, "stream_read_GB_per_s": round(wbytes / (s_ms * 1e-3) / 1e9, 1),
@@ -332,26 +382,111 @@ def calibration(wq, torch, w, steps, warmup, gemv_ms):
             "share_of_stream_ceiling": round(s_ms / gemv_ms, 4), "rotation_copies": R}
 
 
-def cpu_baseline(w, budget_s=10.0):
-    """Time the CPU oracle on the same workload, repeated for about budget_s."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_leg(name, budget_s):
+    """Run in a child process: time the oracle on workload `name` (no GPU).
+
+    The BLAS thread count comes from the environment the parent set before
+    this interpreter (and numpy) started.  Each oracle call is timed on its
+    own; the median is reported.
+    """
+    w = _make_workload(name, None, None, None)
+    w.oracle()  # untimed: first touch of the inputs
+    per = []
+    t_end = time.perf_counter() + budget_s
+    while time.perf_counter() < t_end and len(per) < 2000:
+        t0 = time.perf_counter()
+        w.oracle()
+        per.append(time.perf_counter() - t0)
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    t0 = time.perf_counter()
-    n = 0
-    while True:
-        w.oracle()
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or n >= 2000:
-            break
-    per = el / n
-    return {"value": round(w.nbytes / per / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{n} full oracle calls ({w.name}: unpack, fp64 dequantise, fp64 matmul), "
-                      f"{per * 1e3:.1f} ms each"}
+        blas = None
+    print(json.dumps({"median_s": _median(per), "calls": len(per), "blas_threads": blas,
+                      "nbytes": w.nbytes, "name": w.name}))
+
+
+def cpu_baseline(name, budget_s=8.0):
+    """The CPU oracle on the same workload, in two child processes.
+
+    One leg with the BLAS thread count the job is given (OMP_NUM_THREADS when
+    set, else every core this process may run on), one with a single thread;
+    each is about budget_s of oracle calls, timed one by one (median).
+    Thread counts are fixed in the child's environment before numpy loads.
+    """
+    import subprocess
+    visible = len(os.sched_getaffinity(0))
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    threads_all = int(share) if share.isdigit() and int(share) > 0 else visible
+    legs = {}
+    for threads in (threads_all, 1):
+        env = dict(os.environ)
+        for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS",
+                    "BLIS_NUM_THREADS", "NUMEXPR_NUM_THREADS"):
+            env[var] = str(threads)
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-leg", name,
+                            "--cpu-budget", str(budget_s)],
+                           env=env, capture_output=True, text=True, timeout=budget_s * 6 + 300)
+        if r.returncode != 0:
+            raise RuntimeError(f"CPU oracle leg failed ({threads} threads): {r.stderr[-2000:]}")
+        legs[threads] = json.loads(r.stdout.strip().splitlines()[-1])
+    full, one = legs[threads_all], legs[1]
+    nbytes = full["nbytes"]
+    return {"value": round(nbytes / full["median_s"] / 1e9, 4), "unit": "GB/s",
+            "cores": full["blas_threads"] or threads_all, "kind": "oracle",
+            "sample": (f"{full['calls']} oracle calls ({full['name']}: unpack, fp64 dequantise, fp64 "
+                       f"matmul), median {full['median_s'] * 1e3:.2f} ms each; the dequantise step "
+                       f"runs on one thread, the matmul on the BLAS threads"),
+            "single_thread": {"value": round(nbytes / one["median_s"] / 1e9, 4), "unit": "GB/s",
+                              "cores": 1, "calls": one["calls"],
+                              "median_ms": round(one["median_s"] * 1e3, 3)},
+            "median_ms": round(full["median_s"] * 1e3, 3),
+            "host_cores_visible": visible, "cpu_model": _cpu_model()}
+
+
+def _make_workload(name, wq, torch, dev):
+    """The named workload (wq/torch/dev may be None when only the oracle is used)."""
+    if name == "q8":
+        return wl_q8(wq, torch, dev)
+    if name.startswith("q8_m"):
+        return wl_q8(wq, torch, dev, int(name[4:]))
+    if name == "q3_f32_1024":
+        return wl_q3(wq, torch, dev, 1024, 1024, "f32", 1000)
+    if name.startswith("q3_f16_"):
+        K, N = (int(v) for v in name[len("q3_f16_"):].split("x"))
+        seed = {(4096, 4096): 1200, (4096, 11008): 1201, (11008, 4096): 1202}.get((K, N), 1203)
+        return wl_q3(wq, torch, dev, K, N, "f16", seed)
+    if name.startswith("q4_m"):
+        return wl_q4(wq, torch, dev, int(name[4:]))
+    if name.startswith("q4zp_g64_m"):
+        return wl_q4zp(wq, torch, dev, int(name[len("q4zp_g64_m"):]), 64)
+    if name.startswith("q4zp_m"):
+        return wl_q4zp(wq, torch, dev, int(name[len("q4zp_m"):]))
+    if name.startswith("q2_m"):
+        return wl_q2(wq, torch, dev, int(name[len("q2_m"):]))
+    if name == "w8a8":
+        return wl_w8a8(wq, torch, dev)
+    if name == "w8a8_smooth":
+        return wl_w8a8(wq, torch, dev, smooth=True)
+    if name == "int8_mixed":
+        return wl_int8_mixed(wq, torch, dev)
+    raise SystemExit(f"unknown workload {name}")
+
+
+SECONDARY = ("q3_f32_1024", "q3_f16_4096x4096", "q3_f16_4096x11008", "q3_f16_11008x4096",
+             "q4_m1", "q4_m2", "q4_m4", "q4_m8", "q4zp_m1", "q4zp_g64_m1", "q2_m1", "q2_m8",
+             "q8_m2", "q8_m8", "q8_m512", "w8a8", "w8a8_smooth", "int8_mixed")
 
 
 def main():
@@ -359,20 +494,32 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--trials", type=int, default=None,
+                    help="timed trials of exactly --steps steps each (median reported); "
+                         "default 11, or 5 above 500 steps")
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-calibration", action="store_true",
                     help="skip the empty-kernel and bare-stream reference timings")
     ap.add_argument("--workload", default="q8",
                     help="q8 (headline) | q8_m* | q3_* | q4_m* | q4zp_m* | q4zp_g64_m* | q2_m* | w8a8 | w8a8_smooth | int8_mixed (single line)")
-    ap.add_argument("--eager", action="store_true",
-                    help="launch every timed step from Python instead of replaying a captured graph")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay a captured graph of the timed steps instead of issuing them one by one")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (counter calibration)")
+    ap.add_argument("--cpu-leg", default=None, help=argparse.SUPPRESS)
+    ap.add_argument("--cpu-budget", type=float, default=8.0, help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.cpu_leg:
+        cpu_leg(args.cpu_leg, args.cpu_budget)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1 (each GPU would take its own share of the columns)"}))
         sys.exit(2)
+
+    # The CPU oracle legs run first, in child processes, before this process
+    # touches the GPU.
+    cpu = None if args.no_cpu_baseline or args.calibrate_copy else cpu_baseline(args.workload)
 
     import torch
     dev = torch.device("cuda:0")
@@ -390,34 +537,11 @@ def main():
     wq.lib()
 
     def make(name):
-        if name == "q8":
-            return wl_q8(wq, torch, dev)
-        if name.startswith("q8_m"):
-            return wl_q8(wq, torch, dev, int(name[4:]))
-        if name == "q3_f32_1024":
-            return wl_q3(wq, torch, dev, 1024, 1024, "f32", 1000)
-        if name.startswith("q3_f16_"):
-            K, N = (int(v) for v in name[len("q3_f16_"):].split("x"))
-            seed = {(4096, 4096): 1200, (4096, 11008): 1201, (11008, 4096): 1202}.get((K, N), 1203)
-            return wl_q3(wq, torch, dev, K, N, "f16", seed)
-        if name.startswith("q4_m"):
-            return wl_q4(wq, torch, dev, int(name[4:]))
-        if name.startswith("q4zp_g64_m"):
-            return wl_q4zp(wq, torch, dev, int(name[len("q4zp_g64_m"):]), 64)
-        if name.startswith("q4zp_m"):
-            return wl_q4zp(wq, torch, dev, int(name[len("q4zp_m"):]))
-        if name.startswith("q2_m"):
-            return wl_q2(wq, torch, dev, int(name[len("q2_m"):]))
-        if name == "w8a8":
-            return wl_w8a8(wq, torch, dev)
-        if name == "w8a8_smooth":
-            return wl_w8a8(wq, torch, dev, smooth=True)
-        if name == "int8_mixed":
-            return wl_int8_mixed(wq, torch, dev)
-        raise SystemExit(f"unknown workload {name}")
+        return _make_workload(name, wq, torch, dev)
 
     w = make(args.workload)
-    ms, R = time_workload(torch, w, args.steps, args.warmup, eager=args.eager)
+    ms, R, per = time_workload(torch, w, args.steps, args.warmup, trials=args.trials,
+                               method="graph" if args.graph else "eager")
     gbs = w.nbytes / (ms * 1e-3) / 1e9
     out = {
         "metric": "Achieved HBM GB/s (% of 8 TB/s) for M=1 fused-dequant GEMV, K=N=4096",
@@ -427,6 +551,13 @@ def main():
         "dtype": getattr(w, "dtype", "see workload"), "data": "synthetic (seeded: N(0,1) activations, N(0,0.02) weights quantised offline)",
         "config": dict(getattr(w, "config", {"workload": w.name}), rotation_copies=R,
                        pct_of_hbm_peak=round(100 * gbs / HBM_PEAK_GBS, 2)),
+        "timing": {"trials": len(per), "steps_per_trial": args.steps, "statistic": "median",
+                   "per_trial_us_per_step": [round(t * 1e3, 3) for t in per],
+                   "method": ("HIP events around exactly `steps` calls on the launch stream, queued "
+                              "behind a spin kernel, after a pre-roll of one call per rotated copy"
+                              if not args.graph else
+                              "HIP events around one replay of a graph of exactly `steps` calls, "
+                              "after a pre-roll of one call per rotated copy")},
     }
     kern = "q8_group" if args.workload == "q8" else None
     traffic = committed_traffic(kern, "4096") if kern else None
@@ -437,12 +568,11 @@ def main():
         out["calibration"] = calibration(wq, torch, w, args.steps, args.warmup, ms)
     if not args.headline_only:
         sec = {}
-        for name in ("q3_f32_1024", "q3_f16_4096x4096", "q3_f16_4096x11008", "q3_f16_11008x4096",
-                     "q4_m1", "q4_m2", "q4_m4", "q4_m8", "q4zp_m1", "q4zp_g64_m1", "q2_m1", "q2_m8", "q8_m2", "q8_m8",
-                     "q8_m512", "w8a8", "w8a8_smooth", "int8_mixed"):
+        for name in SECONDARY:
             sw = make(name)
             big = name.startswith("w8a8") or name == "int8_mixed"
-            sms, sR = time_workload(torch, sw, 100 if big else 300, 10 if big else 30)
+            st, wu = (100, 10) if big else (300, 30)
+            sms, sR, _ = time_workload(torch, sw, st, wu, trials=5)
             e = {"us_per_call": round(sms * 1e3, 3), "GB_per_s": round(sw.nbytes / (sms * 1e-3) / 1e9, 1),
                  "pct_hbm_peak": round(100 * sw.nbytes / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                  "rotation_copies": sR, "algorithmic_bytes": sw.nbytes}
@@ -453,7 +583,7 @@ def main():
                 sink = torch.zeros(1, dtype=torch.int32, device=dev)
                 ref = Workload("weight stream", sw.nbytes, sw.make,
                                lambda c: wq.calib_stream_read(c[1], sink))
-                rms, _ = time_workload(torch, ref, 100 if big else 300, 10 if big else 30)
+                rms, _, _ = time_workload(torch, ref, st, wu, trials=5)
                 e["weight_stream_us"] = round(rms * 1e3, 3)
                 e["share_of_stream_ceiling"] = round(rms / sms, 4)
             if sw.flops:
@@ -462,8 +592,8 @@ def main():
             sec[sw.name] = e
             del sw
         out["secondary"] = sec
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out))
 
 
