@@ -172,22 +172,25 @@ def wl_q4(wq, torch, dev, M):
 def wl_int8_mixed(wq, torch, dev):
     import synth
     M, K, N = 256, 8192, 8192
-    # column maxima: read X fp16, write colmax; quantiser: read X, colmax, write Xq, Sx;
-    # GEMM: read Xq, Wq, Sx, Sw, write Y fp16 (the outlier columns are a few KB)
-    nbytes = (2 * M * K + 4 * K) + (2 * M * K + 4 * K + M * K + 4 * M) + (M * K + N * K + 4 * M + 4 * N + 2 * M * N)
+    # column scan: read X fp16, write colmax + mask; quantiser: read X and W
+    # fp16 (and the mask), write Xq, Sx, Wq, Sw; GEMM: read Xq, Wq, Sx, Sw,
+    # write Y fp16 (the outlier columns of X and W are a few KB)
+    nbytes = ((2 * M * K + 4 * K + K // 8) + (2 * M * K + 2 * N * K + M * K + 4 * M + N * K + 4 * N)
+              + (M * K + N * K + 4 * M + 4 * N + 2 * M * N))
     d = synth.gen_int8_mixed(M, K, N, seed=synth.SEEDS["int8_mixed"])
 
     def make(R):
-        base = [torch.from_numpy(a).to(dev) for a in (d["X"], d["Wq"], d["Sw"])]
+        base = [torch.from_numpy(a).to(dev) for a in (d["X"], d["W16"])]
         return [[t.clone() for t in base] + [torch.empty((M, N), dtype=torch.float16, device=dev)]
                 for _ in range(R)]
 
     def run(c):
-        wq.gemm_int8_mixed(c[0], c[1], c[2], 6.0, Y=c[3])
+        wq.gemm_int8_mixed(c[0], c[1], 6.0, Y=c[2])
 
     w = Workload(f"int8_mixed_decomposition M={M} K={K} N={N} outlier_cols=8", nbytes, make, run,
                  flops=2 * M * K * N)
     w.peak_tops = INT8_PEAK_TOPS
+    w.oracle = lambda: __import__("oracle").int8_mixed_decompose(d["X"], d["W16"], 6.0)
     return w
 
 

@@ -234,28 +234,38 @@ int wq_gemm_w8a8_smooth(const float* X, const float* smooth, const int8_t* Wq, c
                         void* Y, int8_t* Xq, float* Sx, int32_t* acc_out, int M, int K, int N,
                         void* stream);
 
-/* LLM.int8()-style mixed-precision decomposition of Y = X . W:
+/* LLM.int8() mixed-precision decomposition of Y = X . W^T
+ * ("Quantization CUDA", tom-jerr.github.io, section "LLM.int8()": the
+ * activations are scanned against a magnitude threshold such as 6.0; the
+ * columns of X holding such values and the matching weight entries stay in
+ * fp16 and are multiplied in fp16; the rest of X is quantised per token and
+ * the rest of W per output channel to int8 and multiplied in int8; the int8
+ * result, rescaled, and the fp16 product are added):
  *   colmax[k] = max_m |X[m, k]|;  column k is an outlier when colmax[k] > threshold;
- *   the int8 side quantises each row of X with the outlier columns set to 0
- *   (Xq, Sx as wq_gemm_w8a8) and forms acc = Xq . Wq^T (exact int32);
- *   the 16-bit side sums o[m, n] = x[m, k] * Wq[n, k] over the outlier
- *   columns in ascending k (fp32; each product exact);
- *   Y[m, n] = fp16_rne( (Sx[m] * float(acc) + o) * Sw[n] ), each fp32
- *   operation rounded on its own.
- * ("Quantization CUDA", tom-jerr.github.io, section "LLM.int8()": outlier
- * columns by a magnitude threshold such as 6.0, int8 vector-wise product of
- * the rest, 16-bit product of the outlier columns, the two added.  The weight
- * is kept only as per-channel int8: its outlier rows enter the 16-bit side
- * as the codes times Sw.)
- * X [M, K] fp16; Wq [N, K] int8; Sw [N] fp32; Y [M, N] fp16, written;
- * Xq [M, K] int8, Sx [M] fp32, colmax [K] fp32, outlier_cols [K] int32 (the
- * first *n_outlier entries, ascending) and n_outlier [1] int32: written;
- * acc_out as wq_gemm_w8a8.  Three launches on `stream`.
- * Rules: as wq_gemm_w8a8; threshold not NaN; X, Wq, Sw, Y, Xq, colmax and
- * acc_out (when given) 16-byte aligned. */
-int wq_gemm_int8_mixed(const void* X, const int8_t* Wq, const float* Sw, float threshold, void* Y,
-                       int8_t* Xq, float* Sx, float* colmax, int32_t* outlier_cols,
-                       int32_t* n_outlier, int32_t* acc_out, int M, int K, int N, void* stream);
+ *   Xq, Sx: each row of X with the outlier columns set to 0, quantised as in
+ *     wq_gemm_w8a8 (Sx = absmax / 127, codes clamp(rint(x / Sx), -127, 127));
+ *   Wq, Sw: each row n of W (output channel n) with the outlier columns set
+ *     to 0, quantised by the same rule (Sw over the regular columns only);
+ *   acc = Xq . Wq^T (exact int32);
+ *   o[m, n] = sum over outlier columns k of X[m, k] * W[n, k] (fp32; each
+ *     product of two fp16 values is exact);
+ *   Y[m, n] = fp16_rne( (Sx[m] * float(acc)) * Sw[n] + o[m, n] ).
+ * X [M, K] fp16; W [N, K] fp16 (K contiguous, row n = output channel n);
+ * Y [M, N] fp16, written.  Written as well: Xq [M, K] int8, Sx [M] fp32,
+ * Wq [N, K] int8, Sw [N] fp32 (the quantised regular part), colmax [K] fp32,
+ * outlier_mask [K / 32] uint32 (bit k % 32 of word k / 32 set for an outlier
+ * column), outlier_cols [K] int32 (the first *n_outlier entries, ascending)
+ * and n_outlier [1] int32; acc_out as wq_gemm_w8a8.  The weight is read in
+ * fp16 and quantised on every call because its split depends on X.  Three
+ * launches on `stream` (column scan; quantiser of the rows of X and W and
+ * the outlier list; GEMM with the fp16 side in its epilogue).
+ * Rules: M >= 1, K % 64 == 0, N % 16 == 0, K * 127 * 127 < 2^31, threshold
+ * not NaN; X, W, Y, Xq, Wq, Sw, colmax, outlier_mask and acc_out (when
+ * given) 16-byte aligned. */
+int wq_gemm_int8_mixed(const void* X, const void* W, float threshold, void* Y, int8_t* Xq,
+                       float* Sx, int8_t* Wq, float* Sw, float* colmax, uint32_t* outlier_mask,
+                       int32_t* outlier_cols, int32_t* n_outlier, int32_t* acc_out, int M, int K,
+                       int N, void* stream);
 
 /* ------------------------------------------------------ bit-exact checks -- */
 

@@ -68,16 +68,14 @@ design notes):
   an all-zero row gets ``Sx = 0`` and all-zero codes.
 * The epilogue is ``bf16_rne(f32(f32(Sx * f32(acc)) * Sw))``: two separately
   rounded fp32 multiplies, left to right, then round-to-nearest-even to bf16.
-* LLM.int8(): X is fp16; a column k is an outlier column when
-  ``max_m |X[m, k]| > threshold``; the weight is stored only as per-channel
-  int8 (``Wq [N, K]``, ``Sw [N]``), so the 16-bit side multiplies the fp16
-  outlier columns of X with the int8 rows of those columns and scales by Sw
-  (the dequantised rows, without a separate fp16 copy of the weight).  Both
-  parts are summed in fp32 and rounded once:
-  ``y = fp16_rne(f32(f32(f32(Sx * f32(acc)) + o) * Sw))`` with
-  ``o = sum_j f32(X[m, k_j]) * Wq[n, k_j]`` added in ascending k_j (each
-  product is exact in fp32).  The int8 side quantises the rows of X with the
-  outlier columns set to zero.
+* LLM.int8(): X is fp16 and the weight is given in fp16, ``W16 [N, K]``; a
+  column k is an outlier column when ``max_m |X[m, k]| > threshold``.  The
+  16-bit side multiplies the fp16 outlier columns of X with the fp16 weight
+  entries of the same k; the int8 side quantises the rest of X per row and
+  the rest of W per output channel (the scales are taken over the regular
+  columns only), multiplies exactly in int32 and rescales.  The output is
+  the exact sum of the two parts (fp64); the GPU's fp16 output is compared
+  with it at the floating-point tolerance, not bit for bit.
 * SmoothQuant's ``X diag(s)^-1`` is one IEEE fp32 division per element,
   ``X[m, k] / s[k]``, before the per-row quantiser; ``diag(s) W`` is folded
   into the weight offline (fp32 multiply) before it is quantised.
@@ -92,7 +90,7 @@ __all__ = [
     "gemm_q4_zp", "unpack_u2", "gemm_q2_zp",
     "quantize_rows_int8", "w8a8_accumulate", "w8a8_epilogue",
     "bf16_rne_bits", "bf16_bits_to_f32", "gemm_w8a8", "smooth_activations",
-    "smooth_weight", "gemm_w8a8_smooth", "fp16_rne", "int8_mixed_decompose",
+    "smooth_weight", "gemm_w8a8_smooth", "int8_mixed_decompose",
 ]
 
 
@@ -341,36 +339,42 @@ def gemm_w8a8_smooth(X: np.ndarray, smooth: np.ndarray, Wq: np.ndarray, Sw: np.n
 # LLM.int8() mixed-precision decomposition
 # --------------------------------------------------------------------------
 
-def fp16_rne(a: np.ndarray) -> np.ndarray:
-    """fp32 -> fp16, round to nearest even (numpy's conversion)."""
-    return np.asarray(a, dtype=np.float32).astype(np.float16)
+def int8_mixed_decompose(X: np.ndarray, W16: np.ndarray, threshold: float) -> dict:
+    """LLM.int8() mixed-precision decomposition of ``Y = X . W^T``.
 
+    "Quantization CUDA" (tom-jerr.github.io), section "LLM.int8()", step by
+    step, with ``X`` fp16 ``[M, K]`` and the fp16 weight ``W16`` ``[N, K]``
+    (K contiguous; row n is output channel n):
 
-def int8_mixed_decompose(X: np.ndarray, Wq: np.ndarray, Sw: np.ndarray, threshold: float) -> dict:
-    """LLM.int8()-style product of fp16 X [M, K] with the per-channel int8 weight.
+    1. scan the activations: ``colmax[k] = max_m |X[m, k]|``; column k is an
+       outlier column when ``colmax[k] > threshold``;
+    2. split: the outlier part is those columns of X and the matching
+       (k-indexed) weight entries ``W16[:, k]``; the regular part is the rest;
+    3. int8 side: the regular part of X is quantised per token (row) and the
+       regular part of W per output channel (row of ``W16``), both with the
+       symmetric absmax/127 rule of ``quantize_rows_int8`` over the regular
+       columns only; ``acc = Xq . Wq^T`` exactly in int32;
+    4. 16-bit side: the outlier part stays in fp16 and is multiplied as is;
+    5. the int8 result, dequantised (``Sx[m] * acc * Sw[n]``), plus the
+       16-bit product is the output.
 
-    Returns the column maxima ``colmax`` (fp32), the outlier columns ``cols``
-    (ascending), the int8 side's ``Xq, Sx, acc``, the fp32 outlier sums ``o``,
-    the fp16 output ``y16`` and the unrounded fp64 ``y_exact``.
+    Returns ``colmax`` (fp32), ``cols`` (ascending), ``Xq, Sx``, ``Wq, Sw``,
+    ``acc``, the two parts in fp64 (``y_int8``, ``y_fp16``) and their exact
+    sum ``y_exact``.
     """
     X = np.atleast_2d(np.asarray(X, dtype=np.float16)).astype(np.float32)
-    Wq = np.asarray(Wq, dtype=np.int8)
-    Sw = np.asarray(Sw, dtype=np.float32)
+    W = np.atleast_2d(np.asarray(W16, dtype=np.float16)).astype(np.float32)
+    if X.shape[1] != W.shape[1]:
+        raise ValueError("X and W16 must share K")
     colmax = np.max(np.abs(X), axis=0).astype(np.float32)
-    cols = np.nonzero(colmax > np.float32(threshold))[0]
-    Xr = X.copy()
-    Xr[:, cols] = 0
+    outlier = colmax > np.float32(threshold)
+    cols = np.nonzero(outlier)[0]
+    Xr = np.where(outlier[None, :], np.float32(0), X)
+    Wr = np.where(outlier[None, :], np.float32(0), W)
     Xq, Sx = quantize_rows_int8(Xr)
+    Wq, Sw = quantize_rows_int8(Wr)
     acc = w8a8_accumulate(Xq, Wq)
-    M, N = X.shape[0], Wq.shape[0]
-    o = np.zeros((M, N), dtype=np.float32)
-    for k in cols:                                    # ascending, one fp32 add each
-        o = (o + (X[:, k:k + 1] * Wq[:, k].astype(np.float32)[None, :]).astype(np.float32)).astype(np.float32)
-    t = (Sx[:, None] * acc.astype(np.float32)).astype(np.float32)
-    u = (t + o).astype(np.float32)
-    y = (u * Sw[None, :]).astype(np.float32)
-    y_exact = Sw.astype(np.float64)[None, :] * (
-        Sx.astype(np.float64)[:, None] * acc.astype(np.float64)
-        + X[:, cols].astype(np.float64) @ Wq[:, cols].astype(np.float64).T)
-    return {"colmax": colmax, "cols": cols.astype(np.int32), "Xq": Xq, "Sx": Sx, "acc": acc,
-            "o": o, "y16": fp16_rne(y), "y_exact": y_exact}
+    y_int8 = Sx.astype(np.float64)[:, None] * acc.astype(np.float64) * Sw.astype(np.float64)[None, :]
+    y_fp16 = X[:, cols].astype(np.float64) @ W[:, cols].astype(np.float64).T
+    return {"colmax": colmax, "cols": cols.astype(np.int32), "Xq": Xq, "Sx": Sx, "Wq": Wq,
+            "Sw": Sw, "acc": acc, "y_int8": y_int8, "y_fp16": y_fp16, "y_exact": y_int8 + y_fp16}

@@ -322,13 +322,14 @@ def gen_w8a8_smooth(M: int, K: int, N: int, seed: int, n_outlier: int = 8,
 
 def gen_int8_mixed(M: int, K: int, N: int, seed: int, n_outlier: int = 8,
                    outlier_scale: float = 20.0) -> dict:
-    """LLM.int8()-style inputs: fp16 activations with a few outlier channels.
+    """LLM.int8()-style inputs: fp16 activations with a few outlier channels, fp16 weight.
 
     Draw order: X ~ N(0,1) [M,K]; ``n_outlier`` distinct channels
     (``rng.choice``) multiplied by ``outlier_scale`` (most of their values
-    then exceed 6); X rounded to fp16.  W ~ N(0, 0.02) fp32 [K,N], quantised
-    offline per output channel: ``Sw = colabsmax/127``,
-    ``Wq = clip(rint(W/Sw), -127, 127)`` stored ``[N, K]``.
+    then exceed 6); X rounded to fp16.  W ~ N(0, 0.02) fp32 [K,N], rounded to
+    fp16 and stored ``[N, K]`` (K contiguous, one row per output channel).
+    The weight stays in fp16: the decomposition quantises its regular part
+    itself, after the split.
     """
     rng = np.random.default_rng(seed)
     X = rng.standard_normal((M, K)).astype(np.float32)
@@ -336,7 +337,5 @@ def gen_int8_mixed(M: int, K: int, N: int, seed: int, n_outlier: int = 8,
     X[:, cols] *= np.float32(outlier_scale)
     X = X.astype(np.float16)
     W = rng.normal(0.0, 0.02, size=(K, N)).astype(np.float32)
-    Sw = _absmax_scale(W, axis=0, qmax=127.0)
-    Wq = np.ascontiguousarray(_quantise(W, Sw[None, :], -127, 127).astype(np.int8).T)
-    return {"X": X, "W": W, "Wq": Wq, "Sw": Sw, "outlier_cols": cols.astype(np.int32),
-            "M": M, "K": K, "N": N}
+    W16 = np.ascontiguousarray(W.T.astype(np.float16))
+    return {"X": X, "W16": W16, "outlier_cols": cols.astype(np.int32), "M": M, "K": K, "N": N}

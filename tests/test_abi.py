@@ -124,11 +124,18 @@ def test_w8a8_validation(L):
     assert f(P, P, P, P, P, P, P_MIS, 256, 8192, 8192, None) == wq.WQ_ERR_ALIGN     # acc_out
     f3 = L.wq_gemm_int8_mixed
     c6 = ctypes.c_float(6.0)
-    assert f3(P, P, P, c6, P, P, P, P, P, None, None, 64, 1024, 64, None) == wq.WQ_ERR_NULL   # n_outlier
-    assert f3(P, P, P, c6, P, P, P, P, P, P, None, 64, 1000, 64, None) == wq.WQ_ERR_SHAPE
-    assert f3(P, P, P, ctypes.c_float(float("nan")), P, P, P, P, P, P, None, 64, 1024, 64,
+    #      X  W  thr Y  Xq Sx Wq Sw cm mk cols nout acc
+    assert f3(P, P, c6, P, P, P, P, P, P, P, P, None, None, 64, 1024, 64, None) == wq.WQ_ERR_NULL  # n_outlier
+    assert f3(P, None, c6, P, P, P, P, P, P, P, P, P, None, 64, 1024, 64, None) == wq.WQ_ERR_NULL  # W
+    assert f3(P, P, c6, P, P, P, None, P, P, P, P, P, None, 64, 1024, 64, None) == wq.WQ_ERR_NULL  # Wq
+    assert f3(P, P, c6, P, P, P, P, P, P, None, P, P, None, 64, 1024, 64, None) == wq.WQ_ERR_NULL  # mask
+    assert f3(P, P, c6, P, P, P, P, P, P, P, P, P, None, 64, 1000, 64, None) == wq.WQ_ERR_SHAPE
+    assert f3(P, P, c6, P, P, P, P, P, P, P, P, P, None, 64, 1024, 60, None) == wq.WQ_ERR_SHAPE
+    assert f3(P, P, ctypes.c_float(float("nan")), P, P, P, P, P, P, P, P, P, None, 64, 1024, 64,
               None) == wq.WQ_ERR_SHAPE
-    assert f3(P_MIS, P, P, c6, P, P, P, P, P, P, None, 64, 1024, 64, None) == wq.WQ_ERR_ALIGN
+    assert f3(P_MIS, P, c6, P, P, P, P, P, P, P, P, P, None, 64, 1024, 64, None) == wq.WQ_ERR_ALIGN
+    assert f3(P, P_MIS, c6, P, P, P, P, P, P, P, P, P, None, 64, 1024, 64, None) == wq.WQ_ERR_ALIGN
+    assert f3(P, P, c6, P, P, P, P, P, P, P_MIS, P, P, None, 64, 1024, 64, None) == wq.WQ_ERR_ALIGN
     f2 = L.wq_gemm_w8a8_smooth
     assert f2(P, None, P, P, P, P, P, None, 64, 1024, 64, None) == wq.WQ_ERR_NULL    # smooth
     assert f2(P, P_MIS, P, P, P, P, P, None, 64, 1024, 64, None) == wq.WQ_ERR_ALIGN

@@ -52,6 +52,32 @@ def assert_tol(y, y_exact, what=""):
     assert mx <= MAX_ABS_RMS, (what, mx)
 
 
+U32 = 2.0 ** -24
+
+
+def assert_fwd_bound(y, y_exact, abs_sum, n_terms, out="f16", what=""):
+    """Element-wise forward error bound of an fp32 evaluation, then the output rounding.
+
+    The kernels form every product exactly in fp32 and reach each output
+    through at most n_terms + 8 rounded fp32 operations (the additions of any
+    summation order, the scale and zero multiplies), so
+      |v - y_exact| <= gamma_{n+8} * abs_sum,  gamma_n = n u / (1 - n u),
+    abs_sum the sum of the magnitudes of the terms the kernel adds.  The
+    stored y = round(v) adds u_out (|y_exact| + that) plus half the smallest
+    subnormal of the output type.
+    """
+    y = np.asarray(y, np.float64)
+    e = np.asarray(y_exact, np.float64)
+    n = n_terms + 8
+    g = n * U32 / (1 - n * U32)
+    fwd = g * np.asarray(abs_sum, np.float64)
+    uo, tiny = (2.0 ** -11, 2.0 ** -25) if out == "f16" else (U32, 2.0 ** -150)
+    bound = fwd + uo * (np.abs(e) + fwd) + tiny
+    ratio = np.max(np.abs(y - e) / bound)
+    print(f"{what}: worst error / forward bound = {ratio:.3e}")
+    assert ratio <= 1.0, (what, ratio)
+
+
 # ================================================================== int8 ==
 
 @pytest.mark.parametrize("M,K,N,G", [
@@ -71,7 +97,10 @@ def assert_tol(y, y_exact, what=""):
 def test_q8_group_vs_oracle(wq, M, K, N, G):
     d = synth.gen_q8_group(M, K, N, G, seed=1100 if (M, K, N) == (1, 4096, 4096) else 7 + M + K + N)
     Y = wq.gemm_q8_group(cu(d["X"]), wq.prepack_q8(cu(d["q"])), cu(d["scales"]), G)
-    assert_tol(host(Y), oracle.gemm_q8_group(d["X"], d["q"], d["scales"], G), f"q8 {M}x{K}x{N} G{G}")
+    ref = oracle.gemm_q8_group(d["X"], d["q"], d["scales"], G)
+    assert_tol(host(Y), ref, f"q8 {M}x{K}x{N} G{G}")
+    A = np.abs(np.repeat(d["scales"].astype(np.float64), G, axis=0) * d["q"])
+    assert_fwd_bound(host(Y), ref, np.abs(d["X"].astype(np.float64)) @ A, K, "f16", f"q8 {M}x{K}x{N} G{G}")
 
 
 def test_q8_integer_exact(wq):
@@ -220,6 +249,11 @@ def test_q3_vs_oracle(wq, K, N, dt, seed):
     y = wq.matvec_q3(cu(d["x"]), wq.prepack_q3(cu(d["qweight"]), K), cu(d["scales"]), cu(d["zeros"]))
     ref = oracle.matvec_q3(d["x"], d["qweight"], d["scales"], d["zeros"])
     assert_tol(host(y), ref, f"q3 {dt} {K}x{N}")
+    # the kernel adds s * x * q and z * x terms (the zero is applied through sum x)
+    ax = np.abs(d["x"].astype(np.float64))
+    abs_sum = (ax @ d["codes"].astype(np.float64)) * np.abs(d["scales"].astype(np.float64)) \
+        + ax.sum() * np.abs(d["zeros"].astype(np.float64))
+    assert_fwd_bound(host(y), ref, abs_sum, K, dt, f"q3 {dt} {K}x{N}")
 
 
 @pytest.mark.parametrize("K,N,dt", [
@@ -267,6 +301,18 @@ def test_q3_one_hot_rows(wq):
 
 # ================================================================= 4-bit ==
 
+def _q4_abs_sum(X, qweight, scales, zeros, g_idx, G, unpack=None):
+    """sum_k |x| * s * (u + |zero|): the magnitudes of the terms the 4-bit and
+    2-bit kernels add (x * u * s, and the zero, 8 for symmetric codes, times
+    s * sum x)."""
+    u = (unpack or oracle.unpack_u4)(qweight).astype(np.float64)
+    K = u.shape[0]
+    g = np.asarray(g_idx) if g_idx is not None else np.arange(K) // G
+    s = np.abs(scales.astype(np.float64))[g]
+    z = np.full_like(s, 8.0) if zeros is None else np.abs(zeros.astype(np.float64))[g]
+    return np.abs(np.atleast_2d(X).astype(np.float64)) @ (s * (u + z))
+
+
 @pytest.mark.parametrize("act", [True, False])
 def test_unpack_q4_bit_exact(wq, act):
     K, N, G = 4096, 11008, 128
@@ -285,6 +331,8 @@ def test_q4_act_order_headline(wq, M):
     Y = wq.gemm_q4_group(cu(d["X"]), packed, cu(d["scales"]), G)
     ref = oracle.gemm_q4_group(d["X"], d["qweight"], d["scales"], d["g_idx"], G)
     assert_tol(host(Y), ref, f"q4 M{M}")
+    assert_fwd_bound(host(Y), ref, _q4_abs_sum(d["X"], d["qweight"], d["scales"], None, d["g_idx"], G),
+                     K, "f16", f"q4 M{M}")
 
 
 @pytest.mark.parametrize("M,K,N,G,act", [
@@ -344,6 +392,8 @@ def test_q4_zp_vs_oracle(wq, M, K, N, G, act):
     Y = wq.gemm_q4_group_zp(cu(d["X"]), packed, cu(d["scales"]), cu(d["zeros"]), G)
     ref = oracle.gemm_q4_zp(d["X"], d["qweight"], d["scales"], d["zeros"], d["g_idx"], G)
     assert_tol(host(Y), ref, f"q4 zp {M}x{K}x{N} G{G} act={act}")
+    assert_fwd_bound(host(Y), ref, _q4_abs_sum(d["X"], d["qweight"], d["scales"], d["zeros"], d["g_idx"], G),
+                     K, "f16", f"q4 zp {M}x{K}x{N}")
 
 
 def test_q4_zp_integer_exact_gpu(wq):
@@ -396,6 +446,8 @@ def test_q2_vs_oracle(wq, M, K, N, G, act):
     Y = wq.gemm_q2_group_zp(cu(d["X"]), packed, cu(d["scales"]), cu(d["zeros"]), G)
     ref = oracle.gemm_q2_zp(d["X"], d["qweight"], d["scales"], d["zeros"], d["g_idx"], G)
     assert_tol(host(Y), ref, f"q2 {M}x{K}x{N} G{G} act={act}")
+    assert_fwd_bound(host(Y), ref, _q4_abs_sum(d["X"], d["qweight"], d["scales"], d["zeros"], d["g_idx"], G,
+                                               unpack=oracle.unpack_u2), K, "f16", f"q2 {M}x{K}x{N}")
 
 
 def test_q2_integer_exact_and_one_hot(wq):
@@ -509,30 +561,70 @@ def test_w8a8_smooth_ones_equals_plain(wq):
 
 # ------------------------------------------------ LLM.int8() decomposition --
 
-def _mixed_check(wq, X16, Wq, Sw, threshold):
-    Y, Xq, Sx, colmax, cols, n_out, acc = wq.gemm_int8_mixed(cu(X16), cu(Wq), cu(Sw), threshold,
-                                                              want_acc=True)
+def _mixed_check(wq, X16, W16, threshold):
+    Y, Xq, Sx, Wq, Sw, colmax, mask, cols, n_out, acc = wq.gemm_int8_mixed(cu(X16), cu(W16), threshold,
+                                                                           want_acc=True)
     torch.cuda.synchronize()
-    r = oracle.int8_mixed_decompose(X16, Wq, Sw, threshold)
+    r = oracle.int8_mixed_decompose(X16, W16, threshold)
+    K = X16.shape[1]
     assert np.array_equal(colmax.cpu().numpy().view(np.uint32), r["colmax"].view(np.uint32))
+    bits = np.zeros(K, np.uint8)
+    bits[r["cols"]] = 1
+    assert np.array_equal(mask.cpu().numpy().view(np.uint32),
+                          np.packbits(bits, bitorder="little").view("<u4"))
     assert int(n_out.item()) == r["cols"].size
     assert np.array_equal(cols.cpu().numpy()[:r["cols"].size], r["cols"])
     assert np.array_equal(Xq.cpu().numpy(), r["Xq"])
     assert np.array_equal(Sx.cpu().numpy().view(np.uint32), r["Sx"].view(np.uint32))
+    assert np.array_equal(Wq.cpu().numpy(), r["Wq"])
+    assert np.array_equal(Sw.cpu().numpy().view(np.uint32), r["Sw"].view(np.uint32))
     assert np.array_equal(acc.cpu().numpy(), r["acc"])
-    assert np.array_equal(Y.view(torch.int16).cpu().numpy().view(np.uint16), r["y16"].view(np.uint16))
+    y = host(Y)
+    what = f"int8 mixed {X16.shape[0]}x{K}x{W16.shape[0]} thr {threshold}"
+    if np.any(r["y_exact"]):
+        assert_tol(y, r["y_exact"], what)
+    # the int8 part reaches fp32 through three roundings (float(acc), * Sx,
+    # * Sw); the fp16 part sums exact products of the outlier columns
+    c = r["cols"]
+    abs_sum = np.abs(r["y_int8"]) + np.abs(X16[:, c].astype(np.float64)) @ np.abs(W16[:, c].astype(np.float64)).T
+    assert_fwd_bound(y, r["y_exact"], abs_sum, c.size + 3, "f16", what)
     return r
 
 
 @pytest.mark.parametrize("M,K,N,nout", [(32, 1024, 64, 8), (130, 256, 528, 3), (7, 2048, 96, 0),
                                         (256, 8192, 8192, 8)])
-def test_int8_mixed_bit_exact(wq, M, K, N, nout):
-    # Outlier channels 20x (beyond 6.0); every output of the decomposition
-    # (column maxima, the outlier list, codes, scales, int32, fp16 bits)
-    # equals the oracle's.
+def test_int8_mixed_vs_oracle(wq, M, K, N, nout):
+    # Outlier channels 20x (beyond 6.0): the scan, the outlier list, the
+    # quantised regular part of X and W and the int32 accumulators equal the
+    # oracle's bit for bit; the fp16 output meets the tolerance and the
+    # forward error bound against the exact sum of the two parts.
     d = synth.gen_int8_mixed(M, K, N, seed=synth.SEEDS["int8_mixed"] + M + K + N, n_outlier=nout)
-    r = _mixed_check(wq, d["X"], d["Wq"], d["Sw"], 6.0)
+    r = _mixed_check(wq, d["X"], d["W16"], 6.0)
     assert np.array_equal(r["cols"], d["outlier_cols"])
+
+
+def test_int8_mixed_worked_example(wq):
+    # The hand-worked example of tests/golden/int8_mixed_worked.txt, padded
+    # with zero columns (K = 64) and zero output channels (N = 16); every
+    # step is exact in fp32, so Y is the fp16 rounding of the fixture's y.
+    from conftest import read_golden
+    rows = {k: v for k, v in read_golden("int8_mixed_worked.txt")}
+    f = lambda key: np.array([float(t) for t in rows[key].split()])
+    X = np.zeros((2, 64), np.float16)
+    W = np.zeros((16, 64), np.float16)
+    X[:, :4] = f("X").reshape(2, 4)
+    W[:2, :4] = f("W").reshape(2, 4)
+    Y, Xq, Sx, Wq, Sw, colmax, mask, cols, n_out, acc = wq.gemm_int8_mixed(cu(X), cu(W), 6.0, want_acc=True)
+    torch.cuda.synchronize()
+    assert int(n_out.item()) == 1 and int(cols[0].item()) == 2
+    assert Xq.cpu().numpy()[:, :4].ravel().tolist() == f("Xq").astype(int).tolist()
+    assert Wq.cpu().numpy()[:2, :4].ravel().tolist() == f("Wq").astype(int).tolist()
+    assert Sx.cpu().numpy().tolist() == f("Sx").tolist()
+    assert Sw.cpu().numpy()[:2].tolist() == f("Sw").tolist()
+    assert acc.cpu().numpy()[:, :2].ravel().tolist() == f("acc").astype(int).tolist()
+    y = host(Y)
+    assert y[:, :2].ravel().tolist() == f("y").astype(np.float16).astype(np.float64).tolist()
+    assert np.all(y[:, 2:] == 0)
 
 
 def test_int8_mixed_thresholds_and_zero_rows(wq):
@@ -542,12 +634,13 @@ def test_int8_mixed_thresholds_and_zero_rows(wq):
     X[:, 7] = 40.0                       # an outlier column
     X[3, :] = 0
     X[3, 7] = 9.0                        # row 3: only its outlier value is non-zero
-    Wq = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
-    Sw = rng.uniform(0.001, 0.01, size=N).astype(np.float32)
-    r = _mixed_check(wq, X, Wq, Sw, 6.0)
-    assert r["cols"].tolist() == [7] and r["Sx"][3] == 0
-    _mixed_check(wq, X, Wq, Sw, 1e30)    # nothing taken out
-    _mixed_check(wq, X, Wq, Sw, -1.0)    # every column taken out
+    W = rng.normal(0, 0.02, size=(N, K)).astype(np.float16)
+    W[4, :] = 0
+    W[4, 7] = 0.5                        # channel 4: only its outlier entry is non-zero
+    r = _mixed_check(wq, X, W, 6.0)
+    assert r["cols"].tolist() == [7] and r["Sx"][3] == 0 and r["Sw"][4] == 0
+    _mixed_check(wq, X, W, 1e30)    # nothing taken out
+    _mixed_check(wq, X, W, -1.0)    # every column taken out
 
 
 # ====================================================== large activations ==

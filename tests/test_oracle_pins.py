@@ -107,15 +107,44 @@ def test_q3_integer_case_brute_force():
         assert y[n] == acc
 
 
+def _gamma(n, u=Fraction(1, 2 ** 53)):
+    """Higham's gamma_n = n u / (1 - n u) (u the unit roundoff, fp64 by default)."""
+    return n * u / (1 - n * u)
+
+
 def test_q3_against_exact_rationals():
-    # 32x8 tile: fp64 oracle vs exact Fraction arithmetic on the stored fp32 values.
+    # 32x8 tile: fp64 oracle vs exact Fraction arithmetic on the stored fp32
+    # values, within the forward error bound of an fp64 dot product: each
+    # weight scale*q - zero is at most one rounding (scale*q is exact), each
+    # product one more, the sum of K terms K - 1 more, so
+    # |y - exact| <= gamma_{K+2} * sum_k |x_k| |w_k|.
     K, N = 32, 8
     x, qw, s, z, codes = _q3_inputs(K, N, 4)
     y = oracle.matvec_q3(x, qw, s, z)
     for n in range(N):
-        exact = sum(Fraction(float(x[k])) * (Fraction(float(s[n])) * int(codes[k, n])
-                                             - Fraction(float(z[n]))) for k in range(K))
-        assert abs(Fraction(float(y[n])) - exact) <= abs(exact) * Fraction(1, 10 ** 13) + Fraction(1, 10 ** 30)
+        terms = [Fraction(float(x[k])) * (Fraction(float(s[n])) * int(codes[k, n]) - Fraction(float(z[n])))
+                 for k in range(K)]
+        exact = sum(terms)
+        assert abs(Fraction(float(y[n])) - exact) <= _gamma(K + 2) * sum(abs(t) for t in terms)
+
+
+def test_q8_and_q4_forward_error_bound():
+    # Group-wise int8 and act-order 4-bit tiles against exact rationals, with
+    # the same rigorous fp64 dot-product bound (scale*q is exact in fp64, so
+    # only the products and the K - 1 additions round).
+    K, N, G = 256, 6, 64
+    d8 = synth.gen_q8_group(1, K, N, G, seed=31)
+    y8 = oracle.gemm_q8_group(d8["X"], d8["q"], d8["scales"], G)
+    d4 = synth.gen_q4_group(1, K, N, 32, seed=32)
+    y4 = oracle.gemm_q4_group(d4["X"], d4["qweight"], d4["scales"], d4["g_idx"], 32)
+    u4 = oracle.unpack_u4(d4["qweight"])
+    for n in range(N):
+        t8 = [Fraction(float(d8["X"][0, k])) * Fraction(float(d8["scales"][k // G, n])) * int(d8["q"][k, n])
+              for k in range(K)]
+        t4 = [Fraction(float(d4["X"][0, k])) * Fraction(float(d4["scales"][d4["g_idx"][k], n]))
+              * (int(u4[k, n]) - 8) for k in range(K)]
+        for y, t in ((y8, t8), (y4, t4)):
+            assert abs(Fraction(float(y[0, n])) - sum(t)) <= _gamma(K + 1) * sum(abs(v) for v in t)
 
 
 def test_q3_scaling_invariance():
@@ -297,6 +326,18 @@ def test_w8a8_epilogue_ties_through_path():
     assert y.tolist() == [[256.0, 260.0, 512.0, 520.0, -256.0]]
 
 
+def test_w8a8_epilogue_per_row_and_per_column_scales():
+    # tests/golden/w8a8_epilogue_worked.txt: distinct per-row Sx and
+    # per-column Sw, M != N and M == N, and two bf16 roundings, by hand.
+    for name, M, N, acc, sx, sw, y in read_golden("w8a8_epilogue_worked.txt"):
+        M, N = int(M), int(N)
+        acc = np.array([int(v) for v in acc.split()], np.int32).reshape(M, N)
+        sx = np.array([float(v) for v in sx.split()], np.float32)
+        sw = np.array([float(v) for v in sw.split()], np.float32)
+        got = oracle.bf16_bits_to_f32(oracle.w8a8_epilogue(acc, sx, sw))
+        assert got.ravel().tolist() == [float(v) for v in y.split()], name
+
+
 # ------------------------------------------------- asymmetric 4-bit (AWQ) --
 
 def test_q4_zp_worked_examples():
@@ -471,56 +512,92 @@ def test_smooth_reduces_error_with_outlier_channels():
 
 # -------------------------------------------------------------- LLM.int8() --
 
-def test_mixed_no_outliers_is_plain_w8a8():
-    # Above every value: no column is taken out, the int8 side is W8A8.
-    d = synth.gen_w8a8(6, 256, 32, seed=81)
-    X16 = d["X"].astype(np.float16)
-    r = oracle.int8_mixed_decompose(X16, d["Wq"], d["Sw"], threshold=1e30)
-    p = oracle.gemm_w8a8(X16.astype(np.float32), d["Wq"], d["Sw"])
-    assert r["cols"].size == 0
-    for key in ("Xq", "Sx", "acc"):
-        assert np.array_equal(r[key], p[key]), key
-    assert np.array_equal(r["y_exact"], p["y_exact"])
-
-
-def test_mixed_all_outliers_is_the_16bit_product():
-    # Below every magnitude: every column is 16-bit, the int8 side is empty
-    # and y is X . (Wq * Sw) exactly (integer-valued case, exact in fp32).
-    rng = np.random.default_rng(82)
-    M, K, N = 3, 64, 16
-    X = rng.integers(-4, 5, size=(M, K)).astype(np.float16)
-    X[:, 0] = 1                                       # no all-zero column
-    Wq = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
-    Sw = np.full(N, 0.5, np.float32)
-    r = oracle.int8_mixed_decompose(X, Wq, Sw, threshold=-1.0)
-    assert r["cols"].size == K and np.all(r["Xq"] == 0) and np.all(r["Sx"] == 0)
-    ref = X.astype(np.float64) @ (Wq.astype(np.float64) * 0.5).T
-    assert np.array_equal(r["y_exact"], ref)
-    assert np.array_equal(r["y16"].astype(np.float64), ref.astype(np.float16).astype(np.float64))
+def _mixed_fixture():
+    rows = {k: v for k, v in read_golden("int8_mixed_worked.txt")}
+    f = lambda key: np.array([float(t) for t in rows[key].split()])
+    return rows, f
 
 
 def test_mixed_worked_example():
-    # One row, K = 4, threshold 6: only column 2 (value 8) exceeds it.
-    #   regular part x = [127/32, 1/32, 0, 2/32]: absmax 127/32, so
-    #   Sx = 1/32 and Xq = [127, 1, 0, 2];
-    #   n = 0, w = [1, 2, 3, 4]: acc = 127 + 2 + 8 = 137, o = 8 * 3 = 24,
-    #          y = (137/32 + 24) * 0.25 = 28.28125 * 0.25 = 7.0703125;
-    #   n = 1, w = [0, 0, -1, 0]: acc = 0, o = -8, y = -8 * 2 = -16.
-    X = np.array([[127.0 / 32, 1.0 / 32, 8.0, 2.0 / 32]], np.float16)
-    Wq = np.array([[1, 2, 3, 4], [0, 0, -1, 0]], np.int8)
-    Sw = np.array([0.25, 2.0], np.float32)
-    r = oracle.int8_mixed_decompose(X, Wq, Sw, threshold=6.0)
-    assert r["cols"].tolist() == [2]
-    assert r["Xq"].tolist() == [[127, 1, 0, 2]] and r["Sx"].tolist() == [1.0 / 32]
-    assert r["acc"].tolist() == [[137, 0]] and r["o"].tolist() == [[24.0, -8.0]]
-    assert r["y16"].astype(np.float64).tolist() == [[7.0703125, -16.0]]
+    # tests/golden/int8_mixed_worked.txt: every intermediate of the page's
+    # steps, derived by hand; the outlier weight entries (5 and -1.5) enter
+    # in fp16, and the per-channel scales cover the regular columns only.
+    rows, f = _mixed_fixture()
+    X = f("X").reshape(2, 4).astype(np.float16)
+    W = f("W").reshape(2, 4).astype(np.float16)
+    r = oracle.int8_mixed_decompose(X, W, threshold=float(rows["thresh"]))
+    assert r["colmax"].tolist() == f("colmax").tolist()
+    assert r["cols"].tolist() == [int(v) for v in rows["cols"].split()]
+    assert r["Xq"].ravel().tolist() == f("Xq").astype(int).tolist()
+    assert r["Sx"].tolist() == f("Sx").tolist()
+    assert r["Wq"].ravel().tolist() == f("Wq").astype(int).tolist()
+    assert r["Sw"].tolist() == f("Sw").tolist()
+    assert r["acc"].ravel().tolist() == f("acc").astype(int).tolist()
+    assert r["y_exact"].ravel().tolist() == f("y").tolist()
+
+
+def test_mixed_outlier_rows_stay_fp16():
+    # Changing only the outlier weight entries changes y by exactly
+    # X[:, cols] . dW (the 16-bit side), and leaves the int8 side alone, even
+    # when the new entries are far off the regular part's int8 grid.
+    rows, f = _mixed_fixture()
+    X = f("X").reshape(2, 4).astype(np.float16)
+    W = f("W").reshape(2, 4).astype(np.float16)
+    W2 = W.copy()
+    W2[:, 2] = np.array([1000.0, -0.0009765625], np.float16)
+    a = oracle.int8_mixed_decompose(X, W, 6.0)
+    b = oracle.int8_mixed_decompose(X, W2, 6.0)
+    for key in ("Wq", "Sw", "Xq", "Sx", "acc"):
+        assert np.array_equal(a[key], b[key]), key
+    d = X[:, 2:3].astype(np.float64) @ (W2[:, 2:3].astype(np.float64) - W[:, 2:3].astype(np.float64)).T
+    assert np.array_equal(b["y_exact"] - a["y_exact"], d)
+
+
+def test_mixed_no_outliers_is_plain_w8a8():
+    # Above every value: no column is taken out; the int8 side is W8A8 with
+    # the weight quantised per output channel over all of K.
+    rng = np.random.default_rng(81)
+    X16 = rng.standard_normal((6, 256)).astype(np.float16)
+    W16 = rng.normal(0, 0.02, size=(32, 256)).astype(np.float16)
+    r = oracle.int8_mixed_decompose(X16, W16, threshold=1e30)
+    Wq, Sw = oracle.quantize_rows_int8(W16.astype(np.float32))
+    p = oracle.gemm_w8a8(X16.astype(np.float32), Wq, Sw)
+    assert r["cols"].size == 0 and np.all(r["y_fp16"] == 0)
+    for key in ("Xq", "Sx", "acc"):
+        assert np.array_equal(r[key], p[key]), key
+    assert np.array_equal(r["Wq"], Wq) and np.array_equal(r["Sw"], Sw)
+    assert np.array_equal(r["y_exact"], p["y_exact"])
+
+
+def test_mixed_all_outliers_is_the_fp16_product():
+    # Below every magnitude: every column is 16-bit, the int8 side is empty
+    # and y is X . W^T of the fp16 values, exactly.
+    rng = np.random.default_rng(82)
+    M, K, N = 3, 64, 16
+    X = rng.standard_normal((M, K)).astype(np.float16)
+    X[:, 0] = 1                                       # no all-zero column
+    W = rng.normal(0, 0.02, size=(N, K)).astype(np.float16)
+    r = oracle.int8_mixed_decompose(X, W, threshold=-1.0)
+    assert r["cols"].size == K
+    assert np.all(r["Xq"] == 0) and np.all(r["Sx"] == 0) and np.all(r["Wq"] == 0) and np.all(r["Sw"] == 0)
+    exact = [[sum(Fraction(float(X[m, k])) * Fraction(float(W[n, k])) for k in range(K))
+              for n in range(N)] for m in range(M)]
+    # every product of two fp16 values is exact in fp64; the sum of 64 such
+    # terms is within gamma_64 * sum |x w| of the exact rational
+    u = Fraction(1, 2 ** 53)
+    g = 64 * u / (1 - 64 * u)
+    for m in range(M):
+        for n in range(N):
+            bound = g * sum(abs(Fraction(float(X[m, k])) * Fraction(float(W[n, k]))) for k in range(K))
+            assert abs(Fraction(float(r["y_exact"][m, n])) - exact[m][n]) <= bound
 
 
 def test_mixed_reduces_error_with_outlier_channels():
     d = synth.gen_int8_mixed(32, 1024, 64, seed=synth.SEEDS["int8_mixed"])
-    ref = d["X"].astype(np.float64) @ d["W"].astype(np.float64)
-    plain = oracle.gemm_w8a8(d["X"].astype(np.float32), d["Wq"], d["Sw"])["y_exact"]
-    mixed = oracle.int8_mixed_decompose(d["X"], d["Wq"], d["Sw"], 6.0)
+    ref = d["X"].astype(np.float64) @ d["W16"].astype(np.float64).T
+    Wq, Sw = oracle.quantize_rows_int8(d["W16"].astype(np.float32))
+    plain = oracle.gemm_w8a8(d["X"].astype(np.float32), Wq, Sw)["y_exact"]
+    mixed = oracle.int8_mixed_decompose(d["X"], d["W16"], 6.0)
     assert np.array_equal(mixed["cols"], d["outlier_cols"])
     e_plain = np.linalg.norm(plain - ref) / np.linalg.norm(ref)
     e_mixed = np.linalg.norm(mixed["y_exact"] - ref) / np.linalg.norm(ref)

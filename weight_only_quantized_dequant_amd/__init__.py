@@ -48,8 +48,8 @@ _SIGNATURES = {
     "wq_gemm_q4_group_zp": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "wq_gemm_w8a8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
     "wq_gemm_w8a8_smooth": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
-    "wq_gemm_int8_mixed": (_i, [_vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                _i, _i, _i, _vp]),
+    "wq_gemm_int8_mixed": (_i, [_vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                _vp, _vp, _i, _i, _i, _vp]),
     "wq_prepack_q2": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
     "wq_gemm_q2_group_zp": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "wq_unpack_q2": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
@@ -415,33 +415,36 @@ def gemm_w8a8(X, Wq, Sw, want_acc=False, Y=None, Xq=None, Sx=None, acc=None, smo
     return Y, Xq, Sx, acc
 
 
-def gemm_int8_mixed(X, Wq, Sw, threshold=6.0, want_acc=False, Y=None):
-    """LLM.int8()-style product of fp16 X with a per-channel int8 weight.
+def gemm_int8_mixed(X, W16, threshold=6.0, want_acc=False, Y=None):
+    """LLM.int8() decomposition of fp16 X [M, K] times the fp16 weight W16 [N, K].
 
-    Returns ``(Y fp16 [M,N], Xq, Sx, colmax [K], outlier_cols [K], n_outlier [1],
-    acc | None)``, all on the device: the first ``n_outlier`` entries of
-    ``outlier_cols`` list the outlier columns.  Nothing is read back to the
-    host, so the call can be captured into a graph.
+    Returns ``(Y fp16 [M,N], Xq, Sx, Wq, Sw, colmax [K], outlier_mask [K/32],
+    outlier_cols [K], n_outlier [1], acc | None)``, all on the device: the
+    first ``n_outlier`` entries of ``outlier_cols`` list the outlier columns.
+    Nothing is read back to the host, so the call can be captured into a
+    graph.
     """
     M, K = X.shape
-    N = Wq.shape[0]
+    N = W16.shape[0]
     dev = X.device
     _need(X, "X", torch.float16, (M, K), dev)
-    _need(Wq, "Wq", torch.int8, (N, K), dev)
-    _need(Sw, "Sw", torch.float32, (N,), dev)
+    _need(W16, "W16", torch.float16, (N, K), dev)
     Y = torch.empty((M, N), dtype=torch.float16, device=dev) if Y is None else Y
     _need(Y, "Y", torch.float16, (M, N), dev)
     Xq = torch.empty((M, K), dtype=torch.int8, device=dev)
     Sx = torch.empty(M, dtype=torch.float32, device=dev)
+    Wq = torch.empty((N, K), dtype=torch.int8, device=dev)
+    Sw = torch.empty(N, dtype=torch.float32, device=dev)
     colmax = torch.empty(K, dtype=torch.float32, device=dev)
+    mask = torch.empty((K + 31) // 32, dtype=torch.int32, device=dev)
     cols = torch.empty(K, dtype=torch.int32, device=dev)
     n_out = torch.empty(1, dtype=torch.int32, device=dev)
     acc = torch.empty((M, N), dtype=torch.int32, device=dev) if want_acc else None
-    st = lib().wq_gemm_int8_mixed(_ptr(X), _ptr(Wq), _ptr(Sw), float(threshold), _ptr(Y), _ptr(Xq),
-                                  _ptr(Sx), _ptr(colmax), _ptr(cols), _ptr(n_out), _ptr(acc), M, K,
-                                  N, _stream(dev))
+    st = lib().wq_gemm_int8_mixed(_ptr(X), _ptr(W16), float(threshold), _ptr(Y), _ptr(Xq), _ptr(Sx),
+                                  _ptr(Wq), _ptr(Sw), _ptr(colmax), _ptr(mask), _ptr(cols),
+                                  _ptr(n_out), _ptr(acc), M, K, N, _stream(dev))
     _check("wq_gemm_int8_mixed", st)
-    return Y, Xq, Sx, colmax, cols, n_out, acc
+    return Y, Xq, Sx, Wq, Sw, colmax, mask, cols, n_out, acc
 
 
 # ---------------------------------------------------------- measurement --

@@ -263,20 +263,23 @@ int wq_gemm_w8a8_smooth(const float* X, const float* smooth, const int8_t* Wq, c
   return hip_status(wq::launch_w8a8(X, smooth, Wq, Sw, Y, Xq, Sx, acc_out, M, K, N, as_stream(stream)));
 }
 
-int wq_gemm_int8_mixed(const void* X, const int8_t* Wq, const float* Sw, float threshold, void* Y,
-                       int8_t* Xq, float* Sx, float* colmax, int32_t* outlier_cols,
-                       int32_t* n_outlier, int32_t* acc_out, int M, int K, int N, void* stream) {
-  if (!X || !Wq || !Sw || !Y || !Xq || !Sx || !colmax || !outlier_cols || !n_outlier)
+int wq_gemm_int8_mixed(const void* X, const void* W, float threshold, void* Y, int8_t* Xq,
+                       float* Sx, int8_t* Wq, float* Sw, float* colmax, uint32_t* outlier_mask,
+                       int32_t* outlier_cols, int32_t* n_outlier, int32_t* acc_out, int M, int K,
+                       int N, void* stream) {
+  if (!X || !W || !Y || !Xq || !Sx || !Wq || !Sw || !colmax || !outlier_mask || !outlier_cols ||
+      !n_outlier)
     return WQ_ERR_NULL;
   if (M < 1 || K < 64 || N < 16 || K % 64 || N % 16) return WQ_ERR_SHAPE;
   if ((long long)K * 127 * 127 >= (1LL << 31)) return WQ_ERR_SHAPE;
-  if ((long long)M * K * 2 > kMaxBytes || (long long)N * K > kMaxBytes) return WQ_ERR_SHAPE;
+  if ((long long)M * K * 2 > kMaxBytes || (long long)N * K * 2 > kMaxBytes) return WQ_ERR_SHAPE;
   if (threshold != threshold) return WQ_ERR_SHAPE;  // NaN
-  if (!aligned16(X) || !aligned16(Wq) || !aligned16(Xq) || !aligned16(Sw) || !aligned16(Y) ||
-      !aligned16(colmax) || !aligned16(acc_out))
+  if (!aligned16(X) || !aligned16(W) || !aligned16(Xq) || !aligned16(Wq) || !aligned16(Sw) ||
+      !aligned16(Y) || !aligned16(colmax) || !aligned16(outlier_mask) || !aligned16(acc_out))
     return WQ_ERR_ALIGN;
-  return hip_status(wq::launch_int8_mixed(X, Wq, Sw, threshold, Y, Xq, Sx, colmax, outlier_cols,
-                                          n_outlier, acc_out, M, K, N, as_stream(stream)));
+  return hip_status(wq::launch_int8_mixed(X, W, threshold, Y, Xq, Sx, Wq, Sw, colmax,
+                                          outlier_mask, outlier_cols, n_outlier, acc_out, M, K, N,
+                                          as_stream(stream)));
 }
 
 // ------------------------------------------------------ measurement only --

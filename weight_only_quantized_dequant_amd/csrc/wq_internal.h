@@ -70,11 +70,13 @@ hipError_t launch_q2_unpack(const void* packed, const int32_t* perm, int8_t* cod
 hipError_t launch_w8a8(const float* X, const float* smooth, const int8_t* Wq, const float* Sw,
                        void* Y, int8_t* Xq, float* Sx, int32_t* acc_out, int M, int K, int N,
                        hipStream_t s);
-// LLM.int8()-style decomposition: X16 [M, K] fp16; Y [M, N] fp16; colmax [K],
-// out_cols [K] and n_out [1] are written (column maxima, outlier list, count).
-hipError_t launch_int8_mixed(const void* X16, const int8_t* Wq, const float* Sw, float threshold,
-                             void* Y, int8_t* Xq, float* Sx, float* colmax, int32_t* out_cols,
-                             int32_t* n_out, int32_t* acc_out, int M, int K, int N, hipStream_t s);
+// LLM.int8() decomposition: X16 [M, K] and W16 [N, K] fp16; Y [M, N] fp16;
+// Xq, Sx, Wq, Sw (the quantised regular part), colmax [K], mask [K/32],
+// out_cols [K] and n_out [1] are written.
+hipError_t launch_int8_mixed(const void* X16, const void* W16, float threshold, void* Y,
+                             int8_t* Xq, float* Sx, int8_t* Wq, float* Sw, float* colmax,
+                             uint32_t* mask, int32_t* out_cols, int32_t* n_out, int32_t* acc_out,
+                             int M, int K, int N, hipStream_t s);
 
 // Measurement references (calib.hip): a launch that does nothing, and one that
 // only streams `bytes` of `buf` with the int8 GEMV's loads and grid shape.
