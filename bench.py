@@ -181,11 +181,12 @@ def wl_int8_mixed(wq, torch, dev):
 
     def make(R):
         base = [torch.from_numpy(a).to(dev) for a in (d["X"], d["W16"])]
-        return [[t.clone() for t in base] + [torch.empty((M, N), dtype=torch.float16, device=dev)]
+        ws = torch.empty(max(16, wq.workspace_bytes(wq.WQ_OP_W8A8, M, K, N)), dtype=torch.uint8, device=dev)
+        return [[t.clone() for t in base] + [torch.empty((M, N), dtype=torch.float16, device=dev), ws]
                 for _ in range(R)]
 
     def run(c):
-        wq.gemm_int8_mixed(c[0], c[1], 6.0, Y=c[2])
+        wq.gemm_int8_mixed(c[0], c[1], 6.0, Y=c[2], ws=c[3])
 
     w = Workload(f"int8_mixed_decomposition M={M} K={K} N={N} outlier_cols=8", nbytes, make, run,
                  flops=2 * M * K * N)
@@ -241,7 +242,9 @@ def wl_q2(wq, torch, dev, M, G=128):
 def wl_w8a8(wq, torch, dev, smooth=False):
     import synth
     M, K, N = 256, 8192, 8192
-    # quantiser: read X fp32 (and s), write Xq + Sx; GEMM: read Xq, Wq, Sx, Sw, write Y
+    # quantiser: read X fp32 (and s), write Xq + Sx; GEMM: read Xq, Wq, Sx, Sw, write Y.
+    # The split-K partials (S * M * N int32, written and read back once) are
+    # the kernel's own traffic, not the method's: they are not counted.
     nbytes = (M * K * 4 + M * K + M * 4) + (M * K + N * K + M * 4 + N * 4 + M * N * 2)
     if smooth:
         nbytes += K * 4
@@ -251,15 +254,17 @@ def wl_w8a8(wq, torch, dev, smooth=False):
 
     def make(R):
         base = [torch.from_numpy(a).to(dev) for a in (d["X"], d["Wq"], d["Sw"])]
-        extra = [torch.from_numpy(d["smooth"]).to(dev)] if smooth else []
+        extra = [torch.from_numpy(d["smooth"]).to(dev)] if smooth else [None]
+        # one workspace serves every copy: the calls run one after another
+        ws = torch.empty(max(16, wq.workspace_bytes(wq.WQ_OP_W8A8, M, K, N)), dtype=torch.uint8, device=dev)
         return [[t.clone() for t in base] + [torch.empty((M, N), dtype=torch.bfloat16, device=dev),
                                              torch.empty((M, K), dtype=torch.int8, device=dev),
                                              torch.empty(M, dtype=torch.float32, device=dev)]
-                + [t.clone() for t in extra]
+                + [t.clone() if t is not None else None for t in extra] + [ws]
                 for _ in range(R)]
 
     def run(c):
-        wq.gemm_w8a8(c[0], c[1], c[2], Y=c[3], Xq=c[4], Sx=c[5], smooth=c[6] if smooth else None)
+        wq.gemm_w8a8(c[0], c[1], c[2], Y=c[3], Xq=c[4], Sx=c[5], smooth=c[6], ws=c[7])
 
     kind = "w8a8_smoothquant" if smooth else "w8a8_dynamic"
     w = Workload(f"{kind} M={M} K={K} N={N}", nbytes, make, run, flops=2 * M * K * N)

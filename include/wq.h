@@ -42,8 +42,11 @@
  *   except where an argument is marked HOST.  The library never allocates or
  *   frees memory, never synchronises a stream, and never changes the current
  *   device; work runs on the device that owns the buffers, on `stream`
- *   (a hipStream_t; NULL means the default stream), asynchronously.  No
- *   workspace is needed: no partial result ever leaves a workgroup.
+ *   (a hipStream_t; NULL means the default stream), asynchronously.  The
+ *   weight-only products need no workspace (no partial result leaves a
+ *   workgroup); the W8A8 family takes one, sized by wq_workspace_bytes(), in
+ *   which it leaves nothing that a later call depends on (it needs no
+ *   clearing).  Calls that overlap in time need separate workspaces.
  * - Layout: row-major and contiguous.  Stored (unpacked) weights keep N (the
  *   output column) contiguous; codes are packed along K.
  * - Outputs are overwritten, never accumulated into.
@@ -73,6 +76,7 @@ typedef enum wq_status {
   WQ_ERR_SHAPE = 2,     /* a size or divisibility rule is violated            */
   WQ_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned                   */
   WQ_ERR_DTYPE = 4,     /* unknown dtype code                                 */
+  WQ_ERR_WORKSPACE = 5, /* workspace NULL or smaller than wq_workspace_bytes() */
   WQ_ERR_HIP = 6        /* a HIP runtime call failed; see wq_last_hip_error() */
 } wq_status_t;
 
@@ -85,12 +89,23 @@ typedef enum wq_op {
   WQ_OP_Q3 = 0,   /* 3-bit matvec              */
   WQ_OP_Q4G = 1,  /* 4-bit group-wise GEMM      */
   WQ_OP_Q8G = 2,  /* int8 group-wise GEMV/GEMM  */
-  WQ_OP_Q2G = 3   /* 2-bit group-wise GEMM      */
+  WQ_OP_Q2G = 3,  /* 2-bit group-wise GEMM      */
+  WQ_OP_W8A8 = 4  /* W8A8 GEMM (also SmoothQuant and LLM.int8()) */
 } wq_op_t;
 
 /* Bytes of the packed weight for `op` at this shape (G is used by
  * WQ_OP_Q4G and WQ_OP_Q2G only).  Returns 0 for an invalid op or shape.  Pure function. */
 size_t wq_packed_bytes(int op, int K, int N, int G);
+
+/* Bytes of device workspace a call of `op` needs at this shape; 0 when it
+ * needs none.  Only WQ_OP_W8A8 (wq_gemm_w8a8, wq_gemm_w8a8_smooth,
+ * wq_gemm_int8_mixed) ever needs one: when its GEMM splits K over
+ * workgroups it keeps S int32 partial tiles, S * M * N * 4 bytes (S = 2 at
+ * M = 256, K = N = 8192: 16 MiB; S = 1, no workspace, once the 128 x 128
+ * output tiles alone fill the GPU, e.g. for M > 256 at N = 8192).  The weight-only
+ * products never need one (no partial result leaves a workgroup), so every
+ * other op returns 0.  Returns 0 for an invalid shape.  Pure function. */
+size_t wq_workspace_bytes(int op, int M, int K, int N);
 
 /* ---------------------------------------------------------------- 3-bit -- */
 
@@ -206,7 +221,11 @@ int wq_gemm_q2_group_zp(const void* X, const void* packed, const void* scales, c
 
 /* ----------------------------------------------------------------- W8A8 -- */
 
-/* W8A8 dynamic-quantisation GEMM:
+/* W8A8 dynamic-quantisation GEMM ("Quantization CUDA", tom-jerr.github.io,
+ * section "Dynamic Quantization": Y = X.W = (Sx*Xint).(Wint*Sw) =
+ * Sx*(Xint.Wint)*Sw, activations quantised per token at run time, weights
+ * per output channel in preprocessing, int8 products accumulated in int32;
+ * section "优化": the rescale fused after the accumulation, bf16 result):
  *   a[m] = max_k |X[m, k]|;  Sx[m] = a[m] / 127 (fp32, round to nearest);
  *   Xq[m, k] = clamp(rint(X[m, k] / Sx[m]), -127, 127)  (0 when a[m] == 0);
  *   acc[m, n] = sum_k Xq[m, k] * Wq[n, k]   (exact int32);
@@ -215,12 +234,20 @@ int wq_gemm_q2_group_zp(const void* X, const void* packed, const void* scales, c
  * Sw [N] fp32 per-output-channel scale;  Y [M, N] bf16 (uint16 bits), written;
  * Xq [M, K] int8 and Sx [M] fp32: written (the run-time quantised X);
  * acc_out [M, N] int32: written when non-NULL (for checking), else the
- *   accumulator never leaves the chip.
- * Two launches on `stream` (quantiser, then GEMM).
- * Rules: M >= 1, K % 64 == 0, N % 16 == 0, and K * 127 * 127 < 2^31;
- * X, Wq, Sw, Y, Xq and acc_out (when given) 16-byte aligned. */
+ *   accumulator never reaches memory except as the split-K partials.
+ * workspace: device, workspace_bytes >= wq_workspace_bytes(WQ_OP_W8A8, M,
+ *   K, N) (may be NULL when that is 0), 16-byte aligned; scratch for the
+ *   int32 partial tiles of the K slices, summed in a fixed order, so the
+ *   result is bit-identical for any workspace.  WQ_ERR_WORKSPACE if missing
+ *   or too small.
+ * Two or three launches on `stream` (quantiser; GEMM; with a split K, the
+ * sum of the partials and the rescale).
+ * Rules: M >= 1, K % 64 == 0, N % 16 == 0, K * 127 * 127 < 2^31,
+ * M * K < 2^31, N * K < 2^31; X, Wq, Sw, Y, Xq and acc_out (when given)
+ * 16-byte aligned. */
 int wq_gemm_w8a8(const float* X, const int8_t* Wq, const float* Sw, void* Y, int8_t* Xq,
-                 float* Sx, int32_t* acc_out, int M, int K, int N, void* stream);
+                 float* Sx, int32_t* acc_out, void* workspace, size_t workspace_bytes, int M,
+                 int K, int N, void* stream);
 
 /* SmoothQuant around the same W8A8 step:  Y = (X diag(s)^-1) . (diag(s) W).
  * The activation side runs here: the row quantiser works on X[m, k] / s[k]
@@ -231,8 +258,8 @@ int wq_gemm_w8a8(const float* X, const int8_t* Wq, const float* Sw, void* Y, int
  * smooth [K] fp32, s[k] > 0, 16-byte aligned; other arguments and rules as
  * wq_gemm_w8a8. */
 int wq_gemm_w8a8_smooth(const float* X, const float* smooth, const int8_t* Wq, const float* Sw,
-                        void* Y, int8_t* Xq, float* Sx, int32_t* acc_out, int M, int K, int N,
-                        void* stream);
+                        void* Y, int8_t* Xq, float* Sx, int32_t* acc_out, void* workspace,
+                        size_t workspace_bytes, int M, int K, int N, void* stream);
 
 /* LLM.int8() mixed-precision decomposition of Y = X . W^T
  * ("Quantization CUDA", tom-jerr.github.io, section "LLM.int8()": the
@@ -255,17 +282,19 @@ int wq_gemm_w8a8_smooth(const float* X, const float* smooth, const int8_t* Wq, c
  * Wq [N, K] int8, Sw [N] fp32 (the quantised regular part), colmax [K] fp32,
  * outlier_mask [K / 32] uint32 (bit k % 32 of word k / 32 set for an outlier
  * column), outlier_cols [K] int32 (the first *n_outlier entries, ascending)
- * and n_outlier [1] int32; acc_out as wq_gemm_w8a8.  The weight is read in
- * fp16 and quantised on every call because its split depends on X.  Three
- * launches on `stream` (column scan; quantiser of the rows of X and W and
- * the outlier list; GEMM with the fp16 side in its epilogue).
+ * and n_outlier [1] int32; acc_out and workspace as wq_gemm_w8a8.  The
+ * weight is read in fp16 and quantised on every call because its split
+ * depends on X.  Three or four launches on `stream` (column scan; quantiser
+ * of the rows of X and W and the outlier list; GEMM; with a split K, the
+ * sum of the partials; the fp16 side joins the rescale).
  * Rules: M >= 1, K % 64 == 0, N % 16 == 0, K * 127 * 127 < 2^31, threshold
  * not NaN; X, W, Y, Xq, Wq, Sw, colmax, outlier_mask and acc_out (when
  * given) 16-byte aligned. */
 int wq_gemm_int8_mixed(const void* X, const void* W, float threshold, void* Y, int8_t* Xq,
                        float* Sx, int8_t* Wq, float* Sw, float* colmax, uint32_t* outlier_mask,
-                       int32_t* outlier_cols, int32_t* n_outlier, int32_t* acc_out, int M, int K,
-                       int N, void* stream);
+                       int32_t* outlier_cols, int32_t* n_outlier, int32_t* acc_out,
+                       void* workspace, size_t workspace_bytes, int M, int K, int N,
+                       void* stream);
 
 /* ------------------------------------------------------ bit-exact checks -- */
 

@@ -113,18 +113,38 @@ def test_q2_validation(L):
 
 def test_w8a8_validation(L):
     f = L.wq_gemm_w8a8
-    assert f(P, P, P, P, P, None, None, 256, 8192, 8192, None) == wq.WQ_ERR_NULL
-    assert f(P, P, P, P, P, P, None, 256, 8190, 8192, None) == wq.WQ_ERR_SHAPE
-    assert f(P, P, P, P, P, P, None, 256, 8192, 8200, None) == wq.WQ_ERR_SHAPE
-    assert f(P, P, P, P, P, P, None, 0, 8192, 8192, None) == wq.WQ_ERR_SHAPE
-    assert f(P, P, P, P, P, P, None, 1, 1 << 20, 64, None) == wq.WQ_ERR_SHAPE  # int32 range
-    assert f(P, P_MIS, P, P, P, P, None, 256, 8192, 8192, None) == wq.WQ_ERR_ALIGN
-    assert f(P, P, P, P_MIS, P, P, None, 256, 8192, 8192, None) == wq.WQ_ERR_ALIGN  # Y
-    assert f(P, P, P_MIS, P, P, P, None, 256, 8192, 8192, None) == wq.WQ_ERR_ALIGN  # Sw
-    assert f(P, P, P, P, P, P, P_MIS, 256, 8192, 8192, None) == wq.WQ_ERR_ALIGN     # acc_out
-    f3 = L.wq_gemm_int8_mixed
+    WS = 64 << 20
+    #        X  Wq Sw Y  Xq Sx acc  ws  bytes M    K     N
+    assert f(P, P, P, P, P, None, None, P, WS, 256, 8192, 8192, None) == wq.WQ_ERR_NULL
+    assert f(P, P, P, P, P, P, None, P, WS, 256, 8190, 8192, None) == wq.WQ_ERR_SHAPE
+    assert f(P, P, P, P, P, P, None, P, WS, 256, 8192, 8200, None) == wq.WQ_ERR_SHAPE
+    assert f(P, P, P, P, P, P, None, P, WS, 0, 8192, 8192, None) == wq.WQ_ERR_SHAPE
+    assert f(P, P, P, P, P, P, None, P, WS, 1, 1 << 20, 64, None) == wq.WQ_ERR_SHAPE  # int32 range
+    assert f(P, P_MIS, P, P, P, P, None, P, WS, 256, 8192, 8192, None) == wq.WQ_ERR_ALIGN
+    assert f(P, P, P, P_MIS, P, P, None, P, WS, 256, 8192, 8192, None) == wq.WQ_ERR_ALIGN  # Y
+    assert f(P, P, P_MIS, P, P, P, None, P, WS, 256, 8192, 8192, None) == wq.WQ_ERR_ALIGN  # Sw
+    assert f(P, P, P, P, P, P, P_MIS, P, WS, 256, 8192, 8192, None) == wq.WQ_ERR_ALIGN     # acc_out
+    # the workspace: missing, too small, misaligned
+    need = L.wq_workspace_bytes(wq.WQ_OP_W8A8, 256, 8192, 8192)
+    assert need == 2 * 256 * 8192 * 4                                   # two K slices
+    assert f(P, P, P, P, P, P, None, None, need, 256, 8192, 8192, None) == wq.WQ_ERR_WORKSPACE
+    assert f(P, P, P, P, P, P, None, P, need - 16, 256, 8192, 8192, None) == wq.WQ_ERR_WORKSPACE
+    assert f(P, P, P, P, P, P, None, P_MIS, need, 256, 8192, 8192, None) == wq.WQ_ERR_ALIGN
+    assert L.wq_status_str(wq.WQ_ERR_WORKSPACE).startswith(b"workspace")
+
+
+def test_workspace_bytes(L):
+    w = lambda M, K, N, op=wq.WQ_OP_W8A8: L.wq_workspace_bytes(op, M, K, N)
+    assert w(512, 8192, 8192) == 0                   # 4 x 64 output tiles fill the GPU: no split
+    assert w(256, 8192, 8192) == 2 * 256 * 8192 * 4  # 128 tiles: two K slices
+    assert w(64, 8192, 4096) == 8 * 64 * 4096 * 4    # 32 tiles: eight K slices
+    assert w(1, 64, 16) == 0                         # a single stage of K: nothing to split
+    assert w(256, 8190, 8192) == 0                   # invalid shape
+    for op in (wq.WQ_OP_Q3, wq.WQ_OP_Q4G, wq.WQ_OP_Q8G, wq.WQ_OP_Q2G):
+        assert w(256, 8192, 8192, op) == 0           # the weight-only products need none
+    f3 = lambda *a: L.wq_gemm_int8_mixed(*a[:13], P, 64 << 20, *a[13:])
     c6 = ctypes.c_float(6.0)
-    #      X  W  thr Y  Xq Sx Wq Sw cm mk cols nout acc
+    #      X  W  thr Y  Xq Sx Wq Sw cm mk cols nout acc (ws, bytes)
     assert f3(P, P, c6, P, P, P, P, P, P, P, P, None, None, 64, 1024, 64, None) == wq.WQ_ERR_NULL  # n_outlier
     assert f3(P, None, c6, P, P, P, P, P, P, P, P, P, None, 64, 1024, 64, None) == wq.WQ_ERR_NULL  # W
     assert f3(P, P, c6, P, P, P, None, P, P, P, P, P, None, 64, 1024, 64, None) == wq.WQ_ERR_NULL  # Wq
@@ -137,9 +157,9 @@ def test_w8a8_validation(L):
     assert f3(P, P_MIS, c6, P, P, P, P, P, P, P, P, P, None, 64, 1024, 64, None) == wq.WQ_ERR_ALIGN
     assert f3(P, P, c6, P, P, P, P, P, P, P_MIS, P, P, None, 64, 1024, 64, None) == wq.WQ_ERR_ALIGN
     f2 = L.wq_gemm_w8a8_smooth
-    assert f2(P, None, P, P, P, P, P, None, 64, 1024, 64, None) == wq.WQ_ERR_NULL    # smooth
-    assert f2(P, P_MIS, P, P, P, P, P, None, 64, 1024, 64, None) == wq.WQ_ERR_ALIGN
-    assert f2(P, P, P, P, P, P, P, None, 64, 1000, 64, None) == wq.WQ_ERR_SHAPE
+    assert f2(P, None, P, P, P, P, P, None, P, 1 << 20, 64, 1024, 64, None) == wq.WQ_ERR_NULL    # smooth
+    assert f2(P, P_MIS, P, P, P, P, P, None, P, 1 << 20, 64, 1024, 64, None) == wq.WQ_ERR_ALIGN
+    assert f2(P, P, P, P, P, P, P, None, P, 1 << 20, 64, 1000, 64, None) == wq.WQ_ERR_SHAPE
 
 
 def test_unpack_validation(L):

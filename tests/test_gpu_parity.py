@@ -498,9 +498,26 @@ def _w8a8_check(wq, d):
 
 @pytest.mark.parametrize("M,K,N", [(1, 64, 16), (17, 192, 80), (128, 512, 256), (130, 256, 528),
                                    (256, 1024, 1040), (64, 640, 64), (300, 4160, 208),
-                                   (3, 2048, 4096)])
+                                   (3, 2048, 4096), (600, 2048, 144), (1100, 512, 2048)])
 def test_w8a8_small_bit_exact(wq, M, K, N):
+    # K split into 1 to 8 slices (workspace partials summed by the second
+    # kernel, or the rescale in the GEMM itself), ragged M, N and K tiles.
     _w8a8_check(wq, synth.gen_w8a8(M, K, N, seed=70 + M + K + N))
+
+
+def test_w8a8_workspace_contents_do_not_matter(wq):
+    # The partial tiles overwrite the workspace: garbage in it, a larger one,
+    # or one reused by the previous call give the same bits.
+    d = synth.gen_w8a8(256, 4096, 1024, seed=77)
+    need = wq.workspace_bytes(wq.WQ_OP_W8A8, 256, 4096, 1024)
+    assert need > 0
+    ws = torch.randint(-128, 127, (need + 4096,), dtype=torch.int8, device=dev())
+    X, Wq, Sw = cu(d["X"]), cu(d["Wq"]), cu(d["Sw"])
+    ref = wq.gemm_w8a8(X, Wq, Sw, want_acc=True)
+    for _ in range(2):
+        got = wq.gemm_w8a8(X, Wq, Sw, want_acc=True, ws=ws)
+        for a, b in zip(ref, got):
+            assert torch.equal(a, b)
 
 
 def test_w8a8_headline_bit_exact(wq):

@@ -31,9 +31,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libwq.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "wq.h")
 
-WQ_OK, WQ_ERR_NULL, WQ_ERR_SHAPE, WQ_ERR_ALIGN, WQ_ERR_DTYPE, WQ_ERR_HIP = 0, 1, 2, 3, 4, 6
+WQ_OK, WQ_ERR_NULL, WQ_ERR_SHAPE, WQ_ERR_ALIGN, WQ_ERR_DTYPE, WQ_ERR_WORKSPACE, WQ_ERR_HIP = 0, 1, 2, 3, 4, 5, 6
 WQ_F32, WQ_F16 = 0, 1
-WQ_OP_Q3, WQ_OP_Q4G, WQ_OP_Q8G, WQ_OP_Q2G = 0, 1, 2, 3
+WQ_OP_Q3, WQ_OP_Q4G, WQ_OP_Q8G, WQ_OP_Q2G, WQ_OP_W8A8 = 0, 1, 2, 3, 4
 
 _vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 _SIGNATURES = {
@@ -46,10 +46,11 @@ _SIGNATURES = {
     "wq_prepack_q4": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
     "wq_gemm_q4_group": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "wq_gemm_q4_group_zp": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
-    "wq_gemm_w8a8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
-    "wq_gemm_w8a8_smooth": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
+    "wq_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "wq_gemm_w8a8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i, _i, _i, _vp]),
+    "wq_gemm_w8a8_smooth": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i, _i, _i, _vp]),
     "wq_gemm_int8_mixed": (_i, [_vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                _vp, _vp, _i, _i, _i, _vp]),
+                                _vp, _vp, _vp, _sz, _i, _i, _i, _vp]),
     "wq_prepack_q2": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
     "wq_gemm_q2_group_zp": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "wq_unpack_q2": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
@@ -380,12 +381,27 @@ def unpack_q2(packed, K: int, N: int, group_size: int = 128, perm=None):
 
 # ------------------------------------------------------------------ W8A8 --
 
-def gemm_w8a8(X, Wq, Sw, want_acc=False, Y=None, Xq=None, Sx=None, acc=None, smooth=None):
+def workspace_bytes(op: int, M: int, K: int, N: int) -> int:
+    """Device workspace bytes a call of ``op`` needs at this shape (0 if none)."""
+    return int(lib().wq_workspace_bytes(op, M, K, N))
+
+
+def _workspace(ws, M, K, N, dev):
+    need = workspace_bytes(WQ_OP_W8A8, M, K, N)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if not (ws.is_cuda and ws.is_contiguous() and ws.device == dev):
+        raise ValueError("ws must be a contiguous tensor on the device of X")
+    return ws, ws.numel() * ws.element_size()
+
+
+def gemm_w8a8(X, Wq, Sw, want_acc=False, Y=None, Xq=None, Sx=None, acc=None, smooth=None, ws=None):
     """Dynamic W8A8: returns ``(Y bf16 [M,N], Xq int8 [M,K], Sx fp32 [M], acc int32 | None)``.
 
     With ``smooth`` (fp32 [K]) the SmoothQuant entry point runs instead: X is
     divided by it per input channel before quantisation, and Wq, Sw must
-    quantise ``diag(smooth) . W``.
+    quantise ``diag(smooth) . W``.  ``ws``: a device workspace of at least
+    ``workspace_bytes(WQ_OP_W8A8, M, K, N)`` bytes, allocated here if None.
     """
     M, K = X.shape
     N = Wq.shape[0]
@@ -403,19 +419,20 @@ def gemm_w8a8(X, Wq, Sw, want_acc=False, Y=None, Xq=None, Sx=None, acc=None, smo
     _need(Sx, "Sx", torch.float32, (M,), dev)
     if acc is not None:
         _need(acc, "acc", torch.int32, (M, N), dev)
+    ws, ws_bytes = _workspace(ws, M, K, N, dev)
     if smooth is not None:
         _need(smooth, "smooth", torch.float32, (K,), dev)
         st = lib().wq_gemm_w8a8_smooth(_ptr(X), _ptr(smooth), _ptr(Wq), _ptr(Sw), _ptr(Y), _ptr(Xq),
-                                       _ptr(Sx), _ptr(acc), M, K, N, _stream(dev))
+                                       _ptr(Sx), _ptr(acc), _ptr(ws), ws_bytes, M, K, N, _stream(dev))
         _check("wq_gemm_w8a8_smooth", st)
         return Y, Xq, Sx, acc
     st = lib().wq_gemm_w8a8(_ptr(X), _ptr(Wq), _ptr(Sw), _ptr(Y), _ptr(Xq), _ptr(Sx), _ptr(acc),
-                            M, K, N, _stream(dev))
+                            _ptr(ws), ws_bytes, M, K, N, _stream(dev))
     _check("wq_gemm_w8a8", st)
     return Y, Xq, Sx, acc
 
 
-def gemm_int8_mixed(X, W16, threshold=6.0, want_acc=False, Y=None):
+def gemm_int8_mixed(X, W16, threshold=6.0, want_acc=False, Y=None, ws=None):
     """LLM.int8() decomposition of fp16 X [M, K] times the fp16 weight W16 [N, K].
 
     Returns ``(Y fp16 [M,N], Xq, Sx, Wq, Sw, colmax [K], outlier_mask [K/32],
@@ -440,9 +457,10 @@ def gemm_int8_mixed(X, W16, threshold=6.0, want_acc=False, Y=None):
     cols = torch.empty(K, dtype=torch.int32, device=dev)
     n_out = torch.empty(1, dtype=torch.int32, device=dev)
     acc = torch.empty((M, N), dtype=torch.int32, device=dev) if want_acc else None
+    ws, ws_bytes = _workspace(ws, M, K, N, dev)
     st = lib().wq_gemm_int8_mixed(_ptr(X), _ptr(W16), float(threshold), _ptr(Y), _ptr(Xq), _ptr(Sx),
                                   _ptr(Wq), _ptr(Sw), _ptr(colmax), _ptr(mask), _ptr(cols),
-                                  _ptr(n_out), _ptr(acc), M, K, N, _stream(dev))
+                                  _ptr(n_out), _ptr(acc), _ptr(ws), ws_bytes, M, K, N, _stream(dev))
     _check("wq_gemm_int8_mixed", st)
     return Y, Xq, Sx, Wq, Sw, colmax, mask, cols, n_out, acc
 

@@ -236,50 +236,77 @@ int wq_unpack_q2(const void* packed, const int32_t* perm, int8_t* codes, int K, 
 
 // ------------------------------------------------------------------- W8A8 --
 
-int wq_gemm_w8a8(const float* X, const int8_t* Wq, const float* Sw, void* Y, int8_t* Xq,
-                 float* Sx, int32_t* acc_out, int M, int K, int N, void* stream) {
-  if (!X || !Wq || !Sw || !Y || !Xq || !Sx) return WQ_ERR_NULL;
+namespace {
+
+// Xq [M, K] and Wq [N, K] are read through 32-bit buffer offsets.
+int check_w8a8(int M, int K, int N) {
   if (M < 1 || K < 64 || N < 16 || K % 64 || N % 16) return WQ_ERR_SHAPE;
   if ((long long)K * 127 * 127 >= (1LL << 31)) return WQ_ERR_SHAPE;
   if ((long long)M * K > kMaxBytes || (long long)N * K > kMaxBytes) return WQ_ERR_SHAPE;
+  return WQ_OK;
+}
+
+int check_ws(int M, int K, int N, const void* ws, size_t ws_bytes) {
+  const size_t need = wq::w8a8_workspace_bytes(M, K, N);
+  if (need == 0) return WQ_OK;
+  if (!ws || ws_bytes < need) return WQ_ERR_WORKSPACE;
+  if (!aligned16(ws)) return WQ_ERR_ALIGN;
+  return WQ_OK;
+}
+
+}  // namespace
+
+size_t wq_workspace_bytes(int op, int M, int K, int N) {
+  if (op != WQ_OP_W8A8) return 0;
+  if (check_w8a8(M, K, N)) return 0;
+  return wq::w8a8_workspace_bytes(M, K, N);
+}
+
+int wq_gemm_w8a8(const float* X, const int8_t* Wq, const float* Sw, void* Y, int8_t* Xq,
+                 float* Sx, int32_t* acc_out, void* workspace, size_t workspace_bytes, int M, int K,
+                 int N, void* stream) {
+  if (!X || !Wq || !Sw || !Y || !Xq || !Sx) return WQ_ERR_NULL;
+  if (int st = check_w8a8(M, K, N)) return st;
   if (!aligned16(X) || !aligned16(Wq) || !aligned16(Xq) || !aligned16(Sw) || !aligned16(Y) ||
       !aligned16(acc_out))
     return WQ_ERR_ALIGN;
-  return hip_status(wq::launch_w8a8(X, nullptr, Wq, Sw, Y, Xq, Sx, acc_out, M, K, N, as_stream(stream)));
+  if (int st = check_ws(M, K, N, workspace, workspace_bytes)) return st;
+  return hip_status(wq::launch_w8a8(X, nullptr, Wq, Sw, Y, Xq, Sx, acc_out, workspace, M, K, N,
+                                    as_stream(stream)));
 }
 
 int wq_gemm_w8a8_smooth(const float* X, const float* smooth, const int8_t* Wq, const float* Sw,
-                        void* Y, int8_t* Xq, float* Sx, int32_t* acc_out, int M, int K, int N,
-                        void* stream) {
+                        void* Y, int8_t* Xq, float* Sx, int32_t* acc_out, void* workspace,
+                        size_t workspace_bytes, int M, int K, int N, void* stream) {
   if (!smooth) return WQ_ERR_NULL;
   if (!aligned16(smooth)) return WQ_ERR_ALIGN;
   if (!X || !Wq || !Sw || !Y || !Xq || !Sx) return WQ_ERR_NULL;
-  if (M < 1 || K < 64 || N < 16 || K % 64 || N % 16) return WQ_ERR_SHAPE;
-  if ((long long)K * 127 * 127 >= (1LL << 31)) return WQ_ERR_SHAPE;
-  if ((long long)M * K > kMaxBytes || (long long)N * K > kMaxBytes) return WQ_ERR_SHAPE;
+  if (int st = check_w8a8(M, K, N)) return st;
   if (!aligned16(X) || !aligned16(Wq) || !aligned16(Xq) || !aligned16(Sw) || !aligned16(Y) ||
       !aligned16(acc_out))
     return WQ_ERR_ALIGN;
-  return hip_status(wq::launch_w8a8(X, smooth, Wq, Sw, Y, Xq, Sx, acc_out, M, K, N, as_stream(stream)));
+  if (int st = check_ws(M, K, N, workspace, workspace_bytes)) return st;
+  return hip_status(wq::launch_w8a8(X, smooth, Wq, Sw, Y, Xq, Sx, acc_out, workspace, M, K, N,
+                                    as_stream(stream)));
 }
 
 int wq_gemm_int8_mixed(const void* X, const void* W, float threshold, void* Y, int8_t* Xq,
                        float* Sx, int8_t* Wq, float* Sw, float* colmax, uint32_t* outlier_mask,
-                       int32_t* outlier_cols, int32_t* n_outlier, int32_t* acc_out, int M, int K,
-                       int N, void* stream) {
+                       int32_t* outlier_cols, int32_t* n_outlier, int32_t* acc_out,
+                       void* workspace, size_t workspace_bytes, int M, int K, int N,
+                       void* stream) {
   if (!X || !W || !Y || !Xq || !Sx || !Wq || !Sw || !colmax || !outlier_mask || !outlier_cols ||
       !n_outlier)
     return WQ_ERR_NULL;
-  if (M < 1 || K < 64 || N < 16 || K % 64 || N % 16) return WQ_ERR_SHAPE;
-  if ((long long)K * 127 * 127 >= (1LL << 31)) return WQ_ERR_SHAPE;
-  if ((long long)M * K * 2 > kMaxBytes || (long long)N * K * 2 > kMaxBytes) return WQ_ERR_SHAPE;
+  if (int st = check_w8a8(M, K, N)) return st;
   if (threshold != threshold) return WQ_ERR_SHAPE;  // NaN
   if (!aligned16(X) || !aligned16(W) || !aligned16(Xq) || !aligned16(Wq) || !aligned16(Sw) ||
       !aligned16(Y) || !aligned16(colmax) || !aligned16(outlier_mask) || !aligned16(acc_out))
     return WQ_ERR_ALIGN;
+  if (int st = check_ws(M, K, N, workspace, workspace_bytes)) return st;
   return hip_status(wq::launch_int8_mixed(X, W, threshold, Y, Xq, Sx, Wq, Sw, colmax,
-                                          outlier_mask, outlier_cols, n_outlier, acc_out, M, K, N,
-                                          as_stream(stream)));
+                                          outlier_mask, outlier_cols, n_outlier, acc_out,
+                                          workspace, M, K, N, as_stream(stream)));
 }
 
 // ------------------------------------------------------ measurement only --
@@ -306,6 +333,7 @@ const char* wq_status_str(int status) {
     case WQ_ERR_SHAPE: return "invalid shape (size or divisibility rule violated)";
     case WQ_ERR_ALIGN: return "pointer not 16-byte aligned";
     case WQ_ERR_DTYPE: return "unknown dtype";
+    case WQ_ERR_WORKSPACE: return "workspace missing or smaller than wq_workspace_bytes()";
     case WQ_ERR_HIP: return "HIP runtime error";
     default: return "unknown status";
   }

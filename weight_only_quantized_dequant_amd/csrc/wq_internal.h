@@ -66,17 +66,21 @@ hipError_t launch_q2_group(const void* X, const void* packed, const void* scales
 hipError_t launch_q2_unpack(const void* packed, const int32_t* perm, int8_t* codes, int K, int N,
                             int G, hipStream_t s);
 
+// Workspace of the W8A8 GEMM (and of the LLM.int8() decomposition) at this
+// shape: the int32 partial tiles of its K slices, 0 when K is not split.
+size_t w8a8_workspace_bytes(int M, int K, int N);
 // smooth: nullptr, or the SmoothQuant factor s [K] (X is divided by it).
+// ws: w8a8_workspace_bytes(M, K, N) bytes (unused when that is 0).
 hipError_t launch_w8a8(const float* X, const float* smooth, const int8_t* Wq, const float* Sw,
-                       void* Y, int8_t* Xq, float* Sx, int32_t* acc_out, int M, int K, int N,
-                       hipStream_t s);
+                       void* Y, int8_t* Xq, float* Sx, int32_t* acc_out, void* ws, int M, int K,
+                       int N, hipStream_t s);
 // LLM.int8() decomposition: X16 [M, K] and W16 [N, K] fp16; Y [M, N] fp16;
 // Xq, Sx, Wq, Sw (the quantised regular part), colmax [K], mask [K/32],
 // out_cols [K] and n_out [1] are written.
 hipError_t launch_int8_mixed(const void* X16, const void* W16, float threshold, void* Y,
                              int8_t* Xq, float* Sx, int8_t* Wq, float* Sw, float* colmax,
                              uint32_t* mask, int32_t* out_cols, int32_t* n_out, int32_t* acc_out,
-                             int M, int K, int N, hipStream_t s);
+                             void* ws, int M, int K, int N, hipStream_t s);
 
 // Measurement references (calib.hip): a launch that does nothing, and one that
 // only streams `bytes` of `buf` with the int8 GEMV's loads and grid shape.
