@@ -249,6 +249,22 @@ int wq_gemm_w8a8(const float* X, const int8_t* Wq, const float* Sw, void* Y, int
                  float* Sx, int32_t* acc_out, void* workspace, size_t workspace_bytes, int M,
                  int K, int N, void* stream);
 
+/* wq_gemm_w8a8 for callers that cannot allocate memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation and results, with the workspace taken from a device array the
+ * library holds on each GPU it runs on (16 MiB per GPU, kept until the
+ * process ends; its address is looked up once per device, with that device
+ * current).  Allocates and frees nothing.  Arguments and rules as
+ * wq_gemm_w8a8 without workspace; WQ_ERR_WORKSPACE when the shape needs
+ * more than 16 MiB (wq_workspace_bytes(WQ_OP_W8A8, M, K, N) > 16 MiB; e.g.
+ * M = 256, K = N = 8192 needs exactly 16 MiB).  Every call on one GPU shares
+ * that GPU's array: calls that overlap in time on one GPU (other streams,
+ * other threads) race and give undefined results; calls ordered on one
+ * stream are safe.  Nothing in the array needs clearing: each call writes
+ * every partial it reads. */
+int wq_gemm_w8a8_noalloc(const float* X, const int8_t* Wq, const float* Sw, void* Y, int8_t* Xq,
+                         float* Sx, int32_t* acc_out, int M, int K, int N, void* stream);
+
 /* SmoothQuant around the same W8A8 step:  Y = (X diag(s)^-1) . (diag(s) W).
  * The activation side runs here: the row quantiser works on X[m, k] / s[k]
  * (one IEEE fp32 division per element) and writes Xq and Sx of that matrix;

@@ -133,6 +133,15 @@ def test_w8a8_validation(L):
     assert L.wq_status_str(wq.WQ_ERR_WORKSPACE).startswith(b"workspace")
 
 
+def test_w8a8_noalloc_validation(L):
+    f = L.wq_gemm_w8a8_noalloc
+    assert f(P, P, P, P, P, None, None, 256, 8192, 8192, None) == wq.WQ_ERR_NULL
+    assert f(P, P, P, P, P, P, None, 256, 8190, 8192, None) == wq.WQ_ERR_SHAPE
+    assert f(P, P_MIS, P, P, P, P, None, 256, 8192, 8192, None) == wq.WQ_ERR_ALIGN
+    # 256 x 8704 with two K slices needs 17 MiB of partials: beyond the 16 MiB array
+    assert f(P, P, P, P, P, P, None, 256, 8192, 8704, None) == wq.WQ_ERR_WORKSPACE
+
+
 def test_workspace_bytes(L):
     w = lambda M, K, N, op=wq.WQ_OP_W8A8: L.wq_workspace_bytes(op, M, K, N)
     assert w(512, 8192, 8192) == 0                   # 4 x 64 output tiles fill the GPU: no split

@@ -48,6 +48,7 @@ _SIGNATURES = {
     "wq_gemm_q4_group_zp": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "wq_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "wq_gemm_w8a8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i, _i, _i, _vp]),
+    "wq_gemm_w8a8_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
     "wq_gemm_w8a8_smooth": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i, _i, _i, _vp]),
     "wq_gemm_int8_mixed": (_i, [_vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _vp, _vp, _sz, _i, _i, _i, _vp]),
@@ -430,6 +431,28 @@ def gemm_w8a8(X, Wq, Sw, want_acc=False, Y=None, Xq=None, Sx=None, acc=None, smo
                             _ptr(ws), ws_bytes, M, K, N, _stream(dev))
     _check("wq_gemm_w8a8", st)
     return Y, Xq, Sx, acc
+
+
+def gemm_w8a8_noalloc(X, Wq, Sw, Y, Xq, Sx, acc=None):
+    """wq_gemm_w8a8_noalloc: W8A8 into caller-given outputs, workspace held by the library.
+
+    Every output tensor is passed in (nothing is allocated here either):
+    Y bf16 [M,N], Xq int8 [M,K], Sx fp32 [M], acc int32 [M,N] or None.
+    """
+    M, K = X.shape
+    N = Wq.shape[0]
+    dev = X.device
+    _need(X, "X", torch.float32, (M, K), dev)
+    _need(Wq, "Wq", torch.int8, (N, K), dev)
+    _need(Sw, "Sw", torch.float32, (N,), dev)
+    _need(Y, "Y", torch.bfloat16, (M, N), dev)
+    _need(Xq, "Xq", torch.int8, (M, K), dev)
+    _need(Sx, "Sx", torch.float32, (M,), dev)
+    if acc is not None:
+        _need(acc, "acc", torch.int32, (M, N), dev)
+    st = lib().wq_gemm_w8a8_noalloc(_ptr(X), _ptr(Wq), _ptr(Sw), _ptr(Y), _ptr(Xq), _ptr(Sx),
+                                    _ptr(acc), M, K, N, _stream(dev))
+    _check("wq_gemm_w8a8_noalloc", st)
 
 
 def gemm_int8_mixed(X, W16, threshold=6.0, want_acc=False, Y=None, ws=None):

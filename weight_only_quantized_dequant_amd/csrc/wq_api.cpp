@@ -275,6 +275,21 @@ int wq_gemm_w8a8(const float* X, const int8_t* Wq, const float* Sw, void* Y, int
                                     as_stream(stream)));
 }
 
+int wq_gemm_w8a8_noalloc(const float* X, const int8_t* Wq, const float* Sw, void* Y, int8_t* Xq,
+                         float* Sx, int32_t* acc_out, int M, int K, int N, void* stream) {
+  if (!X || !Wq || !Sw || !Y || !Xq || !Sx) return WQ_ERR_NULL;
+  if (int st = check_w8a8(M, K, N)) return st;
+  if (!aligned16(X) || !aligned16(Wq) || !aligned16(Xq) || !aligned16(Sw) || !aligned16(Y) ||
+      !aligned16(acc_out))
+    return WQ_ERR_ALIGN;
+  const size_t need = wq::w8a8_workspace_bytes(M, K, N);
+  if (need > wq::w8a8_scratch_bytes()) return WQ_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (int st = hip_status(wq::w8a8_scratch_ptr(&ws))) return st;
+  return hip_status(wq::launch_w8a8(X, nullptr, Wq, Sw, Y, Xq, Sx, acc_out, ws, M, K, N,
+                                    as_stream(stream)));
+}
+
 int wq_gemm_w8a8_smooth(const float* X, const float* smooth, const int8_t* Wq, const float* Sw,
                         void* Y, int8_t* Xq, float* Sx, int32_t* acc_out, void* workspace,
                         size_t workspace_bytes, int M, int K, int N, void* stream) {

@@ -69,6 +69,10 @@ hipError_t launch_q2_unpack(const void* packed, const int32_t* perm, int8_t* cod
 // Workspace of the W8A8 GEMM (and of the LLM.int8() decomposition) at this
 // shape: the int32 partial tiles of its K slices, 0 when K is not split.
 size_t w8a8_workspace_bytes(int M, int K, int N);
+// The library's own W8A8 workspace (a device array of w8a8_scratch_bytes()
+// bytes per GPU): its device address on the current device.
+size_t w8a8_scratch_bytes();
+hipError_t w8a8_scratch_ptr(void** out);
 // smooth: nullptr, or the SmoothQuant factor s [K] (X is divided by it).
 // ws: w8a8_workspace_bytes(M, K, N) bytes (unused when that is 0).
 hipError_t launch_w8a8(const float* X, const float* smooth, const int8_t* Wq, const float* Sw,
