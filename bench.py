@@ -158,11 +158,14 @@ def wl_q4(wq, torch, dev, M):
         qw = torch.from_numpy(d["qweight"]).to(dev)
         packed, _ = wq.prepare_q4(qw, d["g_idx"], G)
         base = [torch.from_numpy(d["X"]).to(dev), packed, torch.from_numpy(d["scales"]).to(dev)]
-        return [[t.clone() for t in base] + [torch.empty((M, N), dtype=torch.float16, device=dev)]
+        # one workspace (X in the packed row order, above 8 rows) serves every copy
+        nws = wq.workspace_bytes(wq.WQ_OP_Q4G, M, K, N)
+        ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+        return [[t.clone() for t in base] + [torch.empty((M, N), dtype=torch.float16, device=dev), ws]
                 for _ in range(R)]
 
     def run(c):
-        wq.gemm_q4_group(c[0], c[1], c[2], G, Y=c[3])
+        wq.gemm_q4_group(c[0], c[1], c[2], G, Y=c[3], ws=c[4])
 
     w = Workload(f"q4_group_actorder M={M} K={K} N={N} G={G}", nbytes, make, run)
     w.oracle = lambda: __import__("oracle").gemm_q4_group(d["X"], d["qweight"], d["scales"], d["g_idx"], G)
@@ -195,25 +198,28 @@ def wl_int8_mixed(wq, torch, dev):
     return w
 
 
-def wl_q4zp(wq, torch, dev, M, G=128):
+def wl_q4zp(wq, torch, dev, M, G=128, act=False):
     import synth
     K, N = 4096, 11008
     # packed codes + scales + zeros + the uint16 row table + X + Y
     nbytes = (K // 8) * N * 4 + 2 * (K // G) * N * 2 + K * 2 + M * K * 2 + M * N * 2
-    d = synth.gen_q4_zp(M, K, N, G, seed=synth.SEEDS["q4_zp"])
+    d = synth.gen_q4_zp(M, K, N, G, seed=synth.SEEDS["q4_zp"], act_order=act)
 
     def make(R):
-        packed, _ = wq.prepare_q4(torch.from_numpy(d["qweight"]).to(dev), None, G)
+        packed, _ = wq.prepare_q4(torch.from_numpy(d["qweight"]).to(dev), d["g_idx"] if act else None, G)
         base = [torch.from_numpy(d["X"]).to(dev), packed, torch.from_numpy(d["scales"]).to(dev),
                 torch.from_numpy(d["zeros"]).to(dev)]
-        return [[t.clone() for t in base] + [torch.empty((M, N), dtype=torch.float16, device=dev)]
+        nws = wq.workspace_bytes(wq.WQ_OP_Q4G, M, K, N)
+        ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+        return [[t.clone() for t in base] + [torch.empty((M, N), dtype=torch.float16, device=dev), ws]
                 for _ in range(R)]
 
     def run(c):
-        wq.gemm_q4_group_zp(c[0], c[1], c[2], c[3], G, Y=c[4])
+        wq.gemm_q4_group_zp(c[0], c[1], c[2], c[3], G, Y=c[4], ws=c[5])
 
-    w = Workload(f"q4_zp_asymmetric M={M} K={K} N={N} G={G}", nbytes, make, run)
-    w.oracle = lambda: __import__("oracle").gemm_q4_zp(d["X"], d["qweight"], d["scales"], d["zeros"], None, G)
+    w = Workload(f"q4_zp_asymmetric{' act-order' if act else ''} M={M} K={K} N={N} G={G}", nbytes, make, run)
+    w.oracle = lambda: __import__("oracle").gemm_q4_zp(d["X"], d["qweight"], d["scales"], d["zeros"],
+                                                       d["g_idx"] if act else None, G)
     return w
 
 
@@ -477,6 +483,8 @@ def _make_workload(name, wq, torch, dev):
         return wl_q3(wq, torch, dev, K, N, "f16", seed)
     if name.startswith("q4_m"):
         return wl_q4(wq, torch, dev, int(name[4:]))
+    if name.startswith("q4zp_act_m"):
+        return wl_q4zp(wq, torch, dev, int(name[len("q4zp_act_m"):]), act=True)
     if name.startswith("q4zp_g64_m"):
         return wl_q4zp(wq, torch, dev, int(name[len("q4zp_g64_m"):]), 64)
     if name.startswith("q4zp_m"):
@@ -493,7 +501,8 @@ def _make_workload(name, wq, torch, dev):
 
 
 SECONDARY = ("q3_f32_1024", "q3_f16_4096x4096", "q3_f16_4096x11008", "q3_f16_11008x4096",
-             "q4_m1", "q4_m2", "q4_m4", "q4_m8", "q4zp_m1", "q4zp_g64_m1", "q2_m1", "q2_m8",
+             "q4_m1", "q4_m2", "q4_m4", "q4_m8", "q4_m16", "q4_m32", "q4_m64", "q4zp_m1",
+             "q4zp_act_m64", "q4zp_g64_m1", "q2_m1", "q2_m8",
              "q8_m2", "q8_m8", "q8_m512", "w8a8", "w8a8_smooth", "int8_mixed")
 
 

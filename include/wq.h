@@ -43,10 +43,11 @@
  *   frees memory, never synchronises a stream, and never changes the current
  *   device; work runs on the device that owns the buffers, on `stream`
  *   (a hipStream_t; NULL means the default stream), asynchronously.  The
- *   weight-only products need no workspace (no partial result leaves a
- *   workgroup); the W8A8 family takes one, sized by wq_workspace_bytes(), in
- *   which it leaves nothing that a later call depends on (it needs no
- *   clearing).  Calls that overlap in time need separate workspaces.
+ *   4-bit products above 8 rows of X and the W8A8 family take a workspace,
+ *   sized by wq_workspace_bytes(), in which a call leaves nothing that a
+ *   later call depends on (it needs no clearing); the other products need
+ *   none (no partial result leaves a workgroup).  Calls that overlap in time
+ *   need separate workspaces.
  * - Layout: row-major and contiguous.  Stored (unpacked) weights keep N (the
  *   output column) contiguous; codes are packed along K.
  * - Outputs are overwritten, never accumulated into.
@@ -98,13 +99,18 @@ typedef enum wq_op {
 size_t wq_packed_bytes(int op, int K, int N, int G);
 
 /* Bytes of device workspace a call of `op` needs at this shape; 0 when it
- * needs none.  Only WQ_OP_W8A8 (wq_gemm_w8a8, wq_gemm_w8a8_smooth,
- * wq_gemm_int8_mixed) ever needs one: when its GEMM splits K over
- * workgroups it keeps S int32 partial tiles, S * M * N * 4 bytes (S = 2 at
- * M = 256, K = N = 8192: 16 MiB; S = 1, no workspace, once the 128 x 128
- * output tiles alone fill the GPU, e.g. for M > 256 at N = 8192).  The weight-only
- * products never need one (no partial result leaves a workgroup), so every
- * other op returns 0.  Returns 0 for an invalid shape.  Pure function. */
+ * needs none.
+ * - WQ_OP_W8A8 (wq_gemm_w8a8, wq_gemm_w8a8_smooth, wq_gemm_int8_mixed): when
+ *   the GEMM splits K over workgroups it keeps S int32 partial tiles,
+ *   S * M * N * 4 bytes (S = 2 at M = 256, K = N = 8192: 16 MiB; S = 1, no
+ *   workspace, once the 128 x 128 output tiles alone fill the GPU, e.g. for
+ *   M > 256 at N = 8192).
+ * - WQ_OP_Q4G (wq_gemm_q4_group, wq_gemm_q4_group_zp): above 8 rows of X,
+ *   X in the packed weight's row order and its sums over runs of rows,
+ *   Mp * Kp * 2 + (Kp / 32) * Mp * 4 bytes (Mp = M rounded up to 16, Kp = K
+ *   rounded up to 128).
+ * - The other ops never need one (no partial result leaves a workgroup).
+ * Returns 0 for an invalid shape.  Pure function. */
 size_t wq_workspace_bytes(int op, int M, int K, int N);
 
 /* ---------------------------------------------------------------- 3-bit -- */
@@ -162,22 +168,41 @@ int wq_q4_act_order_perm(const int32_t* g_idx, int K, int G, int32_t* perm, int3
 /* Re-lay out a 4-bit weight qweight [K/8, N] int32 (row 8r + j in nibble j,
  * bits 4j..4j+3, of word r, stored as u = q + 8), its rows taken in the
  * order perm lists (device array [K], or NULL for the stored order).
+ * perm must be a permutation of 0..K-1 (wq_q4_act_order_perm builds one);
+ * the library does not copy it back to check: entries outside 0..K-1 are
+ * skipped, never used as addresses, and a perm that repeats rows leaves
+ * the packed weight undefined (but every access in bounds).
  * packed: wq_packed_bytes(WQ_OP_Q4G, K, N, G) bytes, written.
- * The packed weight also holds the inverse of perm as a table of K uint16.
+ * The packed weight also holds the inverse of perm as a table of K uint16,
+ * and perm itself as a table of K rounded up to 128 uint16 (0xFFFF past K).
  * Rules: K % G == 0, G a power of two >= 32, K <= 32768, N % 4 == 0. */
 int wq_prepack_q4(const int32_t* qweight, const int32_t* perm, void* packed, int K, int N, int G,
                   void* stream);
 
-/* Group-wise 4-bit GEMM (symmetric, optional act-order):
+/* Group-wise 4-bit GEMM (symmetric, optional act-order)
+ * ("Quantization CUDA", tom-jerr.github.io, sections "Int4 Weight Only
+ * Quantization" and "量化粒度": int4 codes packed along K, one scale per group
+ * of 128 rows; "GPTQ算法解析", intelliparadigm.com, section 4.1: act_order,
+ * a row -> group map g_idx that is not monotone in K):
  *   Y[m, n] = sum_k X[m, k] * scale[g_idx[k], n] * q[k, n]
  * computed from the packed weight (rows in perm order) as
  *   sum_i X[m, perm[i]] * scale[i / G, n] * q[perm[i], n].
  * X [M, K] fp16; packed: from wq_prepack_q4 (the row order perm travels
  * inside it); scales [K/G, N] fp16; Y [M, N] fp16, written (fp32
  * accumulation).
- * Rules: as wq_prepack_q4, M >= 1. */
+ * Up to 8 rows: one launch per 8 rows of X, X staged whole in LDS, no
+ * workspace.  More rows: X is first gathered into the packed weight's row
+ * order in the workspace (in matrix-core operand order, with its sums over
+ * runs of 64 or 32 rows), then one launch per 64 rows (48 for groups of 32)
+ * reads the packed weight once (16-row matrix-core tiles).
+ * workspace: device, workspace_bytes >= wq_workspace_bytes(WQ_OP_Q4G, M, K,
+ *   N) = Mp * Kp * 2 + (Kp / 32) * Mp * 4 bytes when M > 8 (Mp = M rounded
+ *   up to 16, Kp = K rounded up to 128), else 0 (NULL allowed); 16-byte
+ *   aligned; needs no clearing.  WQ_ERR_WORKSPACE if missing or too small.
+ *   Calls that overlap in time need separate workspaces.
+ * Rules: as wq_prepack_q4, M >= 1, M * K * 2 < 2^31. */
 int wq_gemm_q4_group(const void* X, const void* packed, const void* scales, void* Y, int M, int K,
-                     int N, int G, void* stream);
+                     int N, int G, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Asymmetric (AWQ-style) group-wise 4-bit GEMM:
  *   Y[m, n] = sum_k X[m, k] * (u[k, n] - zero[g, n]) * scale[g, n],
@@ -189,17 +214,19 @@ int wq_gemm_q4_group(const void* X, const void* packed, const void* scales, void
  * W_fp16 = (W_int4 - Zero) * Scale.)
  * X [M, K] fp16; scales and zeros [K/G, N] fp16 (zeros as values, e.g. the
  * integers 0..15); Y [M, N] fp16, written (fp32 accumulation; the zero is
- * applied once per group to the accumulated sums).
+ * applied once per group to the accumulated sums); workspace as
+ * wq_gemm_q4_group.
  * Rules: as wq_gemm_q4_group; zeros 16-byte aligned. */
 int wq_gemm_q4_group_zp(const void* X, const void* packed, const void* scales, const void* zeros,
-                        void* Y, int M, int K, int N, int G, void* stream);
+                        void* Y, int M, int K, int N, int G, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------- 2-bit -- */
 
 /* Re-lay out a 2-bit weight qweight [K/16, N] int32 (row 16r + j in bits
  * 2j, 2j+1 of word r, unsigned values 0..3), its rows taken in the order
  * perm lists (device array [K], from wq_q4_act_order_perm, or NULL for the
- * stored order).  packed: wq_packed_bytes(WQ_OP_Q2G, K, N, G) bytes, written;
+ * stored order; a permutation of 0..K-1, as for wq_prepack_q4).  packed: wq_packed_bytes(WQ_OP_Q2G, K, N, G) bytes, written;
  * it also holds the inverse of perm as a table of K uint16.
  * Rules: K % G == 0, G a power of two >= 32, K <= 32768, N % 4 == 0. */
 int wq_prepack_q2(const int32_t* qweight, const int32_t* perm, void* packed, int K, int N, int G,

@@ -43,7 +43,9 @@ def test_packed_bytes_pure_and_valid(L):
     assert L.wq_packed_bytes(wq.WQ_OP_Q3, 4096, 11008, 0) == 4096 // 32 * 3 * 11008 * 4
     assert L.wq_packed_bytes(wq.WQ_OP_Q3, 11008, 4096, 0) >= 11008 // 32 * 3 * 4096 * 4
     # 4-bit: the codes plus the uint16 row table
-    assert L.wq_packed_bytes(wq.WQ_OP_Q4G, 4096, 11008, 128) == 4096 // 8 * 11008 * 4 + 4096 * 2
+    # blocks, the inverse row table, the forward row table (K rounded up to 128)
+    assert L.wq_packed_bytes(wq.WQ_OP_Q4G, 4096, 11008, 128) == 4096 // 8 * 11008 * 4 + 4096 * 2 * 2
+    assert L.wq_packed_bytes(wq.WQ_OP_Q4G, 4160, 64, 32) == 33 * 4 * 1024 + 4160 * 2 + 4224 * 2
     # invalid shapes / ops -> 0
     assert L.wq_packed_bytes(wq.WQ_OP_Q8G, 4096, 4095, 128) == 0
     assert L.wq_packed_bytes(wq.WQ_OP_Q3, 100, 64, 0) == 0
@@ -78,7 +80,7 @@ def test_q8_validation(L):
 
 
 def test_q4_validation(L):
-    f = L.wq_gemm_q4_group
+    f = lambda *a: L.wq_gemm_q4_group(*a[:8], None, 0, a[8])        # no workspace
     assert f(P, P, None, P, 1, 4096, 11008, 128, None) == wq.WQ_ERR_NULL
     assert f(P, P, P, P, 1, 4096, 11006, 128, None) == wq.WQ_ERR_SHAPE
     assert f(P, P, P, P, 1, 4000, 11008, 128, None) == wq.WQ_ERR_SHAPE
@@ -86,10 +88,22 @@ def test_q4_validation(L):
     assert f(P, P, P, P, 0, 4096, 11008, 128, None) == wq.WQ_ERR_SHAPE
     assert f(P, P, P, P, 1, 32768 + 128, 64, 128, None) == wq.WQ_ERR_SHAPE   # K bound
     assert f(P, P_MIS, P, P, 1, 4096, 11008, 128, None) == wq.WQ_ERR_ALIGN
-    z = L.wq_gemm_q4_group_zp
+    # above 8 rows: X in the packed row order (rows rounded up to 16, K to
+    # 128, fp16) and its sums over 32-row runs (fp32)
+    q4ws = lambda Mp, Kp: Mp * Kp * 2 + (Kp // 32) * Mp * 4
+    need = L.wq_workspace_bytes(wq.WQ_OP_Q4G, 64, 4096, 11008)
+    assert need == q4ws(64, 4096)
+    assert L.wq_workspace_bytes(wq.WQ_OP_Q4G, 8, 4096, 11008) == 0
+    assert L.wq_workspace_bytes(wq.WQ_OP_Q4G, 9, 4160, 11008) == q4ws(16, 4224)
+    g4 = L.wq_gemm_q4_group
+    assert g4(P, P, P, P, 64, 4096, 11008, 128, None, need, None) == wq.WQ_ERR_WORKSPACE
+    assert g4(P, P, P, P, 64, 4096, 11008, 128, P, need - 2, None) == wq.WQ_ERR_WORKSPACE
+    assert g4(P, P, P, P, 64, 4096, 11008, 128, P_MIS, need, None) == wq.WQ_ERR_ALIGN
+    z = lambda *a: L.wq_gemm_q4_group_zp(*a[:9], None, 0, a[9])
     assert z(P, P, P, None, P, 1, 4096, 11008, 128, None) == wq.WQ_ERR_NULL      # zeros
     assert z(P, P, P, P, P, 1, 4096, 11006, 128, None) == wq.WQ_ERR_SHAPE
     assert z(P, P, P, P_MIS, P, 1, 4096, 11008, 128, None) == wq.WQ_ERR_ALIGN
+    assert z(P, P, P, P, P, 16, 4096, 11008, 128, None) == wq.WQ_ERR_WORKSPACE
     g = L.wq_prepack_q4
     assert g(P, None, P, 12, 16, 32, None) == wq.WQ_ERR_SHAPE
     assert g(P, None, None, 64, 16, 32, None) == wq.WQ_ERR_NULL
@@ -149,8 +163,9 @@ def test_workspace_bytes(L):
     assert w(64, 8192, 4096) == 8 * 64 * 4096 * 4    # 32 tiles: eight K slices
     assert w(1, 64, 16) == 0                         # a single stage of K: nothing to split
     assert w(256, 8190, 8192) == 0                   # invalid shape
-    for op in (wq.WQ_OP_Q3, wq.WQ_OP_Q4G, wq.WQ_OP_Q8G, wq.WQ_OP_Q2G):
-        assert w(256, 8192, 8192, op) == 0           # the weight-only products need none
+    for op in (wq.WQ_OP_Q3, wq.WQ_OP_Q8G, wq.WQ_OP_Q2G):
+        assert w(256, 8192, 8192, op) == 0           # these weight-only products need none
+    assert w(256, 8192, 8192, wq.WQ_OP_Q4G) == 256 * 8192 * 2 + 256 * 256 * 4   # 4-bit: X regathered
     f3 = lambda *a: L.wq_gemm_int8_mixed(*a[:13], P, 64 << 20, *a[13:])
     c6 = ctypes.c_float(6.0)
     #      X  W  thr Y  Xq Sx Wq Sw cm mk cols nout acc (ws, bytes)

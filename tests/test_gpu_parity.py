@@ -375,6 +375,102 @@ def test_q4_integer_exact(wq):
     assert np.array_equal(Y, ref)
 
 
+# ---------------------------- 4-bit above 8 rows: the packed weight read once
+
+@pytest.mark.parametrize("zp", [False, True])
+@pytest.mark.parametrize("M", [16, 32, 64])
+def test_q4_tiled_layer_shape(wq, M, zp):
+    # K = 4096, N = 11008, group 128, act-order, with and without zero points.
+    K, N, G = 4096, 11008, 128
+    if zp:
+        d = synth.gen_q4_zp(M, K, N, G, seed=synth.SEEDS["q4_zp"] + M, act_order=True)
+        packed, _ = wq.prepare_q4(cu(d["qweight"]), d["g_idx"], G)
+        Y = wq.gemm_q4_group_zp(cu(d["X"]), packed, cu(d["scales"]), cu(d["zeros"]), G)
+        ref = oracle.gemm_q4_zp(d["X"], d["qweight"], d["scales"], d["zeros"], d["g_idx"], G)
+    else:
+        d = synth.gen_q4_group(M, K, N, G, seed=1300, act_order=True)
+        packed, _ = wq.prepare_q4(cu(d["qweight"]), d["g_idx"], G)
+        Y = wq.gemm_q4_group(cu(d["X"]), packed, cu(d["scales"]), G)
+        ref = oracle.gemm_q4_group(d["X"], d["qweight"], d["scales"], d["g_idx"], G)
+    y = host(Y)
+    assert_tol(y, ref, f"q4 tiled M{M} zp={zp}")
+    assert_fwd_bound(y, ref, _q4_abs_sum(d["X"], d["qweight"], d["scales"], d.get("zeros") if zp else None,
+                                         d["g_idx"], G), K, "f16", f"q4 tiled M{M} zp={zp}")
+
+
+@pytest.mark.parametrize("M,K,N,G,act,zp", [
+    (9, 4096, 11008, 128, True, False),    # 9 rows in one 16-row tile
+    (17, 2048, 4100, 64, True, True),      # two tiles; ragged last panel
+    (33, 4160, 1040, 32, True, False),     # K = 32.5 blocks (padded to 4224), groups of 32
+    (40, 4160, 1040, 32, True, True),      # groups of 32 with zero points
+    (47, 1024, 256, 256, False, True),     # groups spanning two blocks
+    (63, 8192, 528, 512, True, False),     # groups spanning four blocks, long K
+    (65, 1024, 1024, 128, True, False),    # 64 + 1 rows: two launches over the weight
+    (130, 512, 64, 128, True, True),       # three launches, four panels
+    (12, 128, 4, 32, True, True),          # one block, one panel of four columns
+])
+def test_q4_tiled_ragged(wq, M, K, N, G, act, zp):
+    if zp:
+        d = synth.gen_q4_zp(M, K, N, G, seed=90 + M + K, act_order=act)
+    else:
+        d = synth.gen_q4_group(M, K, N, G, seed=90 + M + K, act_order=act)
+    packed, _ = wq.prepare_q4(cu(d["qweight"]), d["g_idx"] if act else None, G)
+    if zp:
+        Y = wq.gemm_q4_group_zp(cu(d["X"]), packed, cu(d["scales"]), cu(d["zeros"]), G)
+        ref = oracle.gemm_q4_zp(d["X"], d["qweight"], d["scales"], d["zeros"], d["g_idx"], G)
+    else:
+        Y = wq.gemm_q4_group(cu(d["X"]), packed, cu(d["scales"]), G)
+        ref = oracle.gemm_q4_group(d["X"], d["qweight"], d["scales"], d["g_idx"], G)
+    y = host(Y)
+    what = f"q4 tiled {M}x{K}x{N} G{G} act={act} zp={zp}"
+    assert_tol(y, ref, what)
+    assert_fwd_bound(y, ref, _q4_abs_sum(d["X"], d["qweight"], d["scales"], d["zeros"] if zp else None,
+                                         d["g_idx"], G), K, "f16", what)
+
+
+def test_q4_tiled_integer_exact_and_one_hot(wq):
+    # Scales 1 and small integer X: every fp32 partial sum is an exact
+    # integer, so Y is the oracle's value after one fp16 rounding.  Then one
+    # row of X per original row k (one-hot): row m of Y is scale[g_idx[k]] *
+    # q[k], which pins the row order through the act-order table.
+    M, K, N, G = 24, 1024, 64, 128
+    rng = np.random.default_rng(97)
+    d = synth.gen_q4_group(1, K, N, G, seed=98, act_order=True)
+    packed, _ = wq.prepare_q4(cu(d["qweight"]), d["g_idx"], G)
+    X = rng.integers(-2, 3, size=(M, K)).astype(np.float16)
+    ones = np.ones_like(d["scales"])
+    Y = host(wq.gemm_q4_group(cu(X), packed, cu(ones), G))
+    ref = oracle.gemm_q4_group(X, d["qweight"], ones, d["g_idx"], G).astype(np.float16).astype(np.float64)
+    assert np.array_equal(Y, ref)
+    rows = rng.choice(K, size=M, replace=False)
+    X1 = np.zeros((M, K), np.float16)
+    X1[np.arange(M), rows] = 1
+    Y1 = host(wq.gemm_q4_group(cu(X1), packed, cu(d["scales"]), G))
+    q = oracle.unpack_q4(d["qweight"])
+    expect = (d["scales"].astype(np.float64)[d["g_idx"][rows]] * q[rows]).astype(np.float16).astype(np.float64)
+    assert np.array_equal(Y1, expect)
+
+
+def test_q4_tiled_matches_row_by_row(wq):
+    # Rows of a 40-row call equal the same rows computed alone (the small-M
+    # kernel, one row per call) within the tolerance; and a call reusing a
+    # workspace with garbage in it gives the same bits as a fresh one.
+    M, K, N, G = 40, 2048, 1024, 128
+    d = synth.gen_q4_group(M, K, N, G, seed=99, act_order=True)
+    packed, _ = wq.prepare_q4(cu(d["qweight"]), d["g_idx"], G)
+    X, S = cu(d["X"]), cu(d["scales"])
+    Y = wq.gemm_q4_group(X, packed, S, G)
+    ws = torch.randint(-128, 127, (wq.workspace_bytes(wq.WQ_OP_Q4G, M, K, N) + 64,), dtype=torch.int8,
+                       device=dev())
+    assert torch.equal(wq.gemm_q4_group(X, packed, S, G, ws=ws), Y)
+    assert torch.equal(wq.gemm_q4_group(X, packed, S, G, ws=ws), Y)
+    ref = oracle.gemm_q4_group(d["X"], d["qweight"], d["scales"], d["g_idx"], G)
+    for m in (0, 17, 39):
+        ym = host(wq.gemm_q4_group(X[m:m + 1].contiguous(), packed, S, G))
+        assert_tol(ym, ref[m:m + 1], f"row {m} alone")
+    assert_tol(host(Y), ref, "40 rows")
+
+
 # ====================================================== asymmetric 4-bit ==
 
 @pytest.mark.parametrize("M,K,N,G,act", [

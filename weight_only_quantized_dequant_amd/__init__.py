@@ -44,8 +44,8 @@ _SIGNATURES = {
     "wq_gemm_q8_group": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "wq_q4_act_order_perm": (_i, [_vp, _i, _i, _vp, _vp]),
     "wq_prepack_q4": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
-    "wq_gemm_q4_group": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
-    "wq_gemm_q4_group_zp": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
+    "wq_gemm_q4_group": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "wq_gemm_q4_group_zp": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]),
     "wq_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "wq_gemm_w8a8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i, _i, _i, _vp]),
     "wq_gemm_w8a8_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
@@ -243,6 +243,13 @@ def q4_act_order_perm(g_idx, K: int, group_size: int = 128):
     return perm, inv
 
 
+def _check_perm(perm, K):
+    """``perm`` must list every row 0..K-1 exactly once (checked on the host)."""
+    p = perm.cpu().numpy()
+    if not np.array_equal(np.sort(p), np.arange(K, dtype=p.dtype)):
+        raise ValueError("perm must be a permutation of 0..K-1")
+
+
 def prepack_q4(qweight, perm=None, group_size=128):
     """Device: re-lay out a 4-bit weight [K/8, N], rows in ``perm`` order (or as stored)."""
     R, N = qweight.shape
@@ -251,6 +258,7 @@ def prepack_q4(qweight, perm=None, group_size=128):
     _need(qweight, "qweight", torch.int32, (R, N), dev)
     if perm is not None:
         _need(perm, "perm", torch.int32, (K,), dev)
+        _check_perm(perm, K)
     out = _packed(WQ_OP_Q4G, K, N, group_size, dev)
     st = lib().wq_prepack_q4(_ptr(qweight), _ptr(perm), _ptr(out), K, N, group_size, _stream(dev))
     _check("wq_prepack_q4", st)
@@ -272,8 +280,23 @@ def prepare_q4(qweight, g_idx, group_size=128):
     return prepack_q4(qweight, perm_d, group_size), perm_d
 
 
-def gemm_q4_group(X, packed, scales, group_size=128, Y=None):
-    """Y[m, n] = sum_k X[m, k] * scale[g_idx[k], n] * q[k, n] from a packed 4-bit weight."""
+def _workspace_q4(ws, M, K, N, dev):
+    need = workspace_bytes(WQ_OP_Q4G, M, K, N)
+    if ws is None:
+        if need == 0:
+            return None, 0
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    if not (ws.is_cuda and ws.is_contiguous() and ws.device == dev):
+        raise ValueError("ws must be a contiguous tensor on the device of X")
+    return ws, ws.numel() * ws.element_size()
+
+
+def gemm_q4_group(X, packed, scales, group_size=128, Y=None, ws=None):
+    """Y[m, n] = sum_k X[m, k] * scale[g_idx[k], n] * q[k, n] from a packed 4-bit weight.
+
+    ``ws``: device workspace of ``workspace_bytes(WQ_OP_Q4G, M, K, N)`` bytes
+    (needed above 8 rows of X; allocated here if None).
+    """
     squeeze = X.dim() == 1
     X2 = X.reshape(1, -1) if squeeze else X
     M, K = X2.shape
@@ -285,13 +308,14 @@ def gemm_q4_group(X, packed, scales, group_size=128, Y=None):
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float16, device=dev)
     _need(Y, "Y", torch.float16, (M, N), dev)
+    ws, ws_bytes = _workspace_q4(ws, M, K, N, dev)
     st = lib().wq_gemm_q4_group(_ptr(X2), _ptr(packed), _ptr(scales), _ptr(Y), M, K, N, group_size,
-                                _stream(dev))
+                                _ptr(ws), ws_bytes, _stream(dev))
     _check("wq_gemm_q4_group", st)
     return Y.reshape(N) if squeeze else Y
 
 
-def gemm_q4_group_zp(X, packed, scales, zeros, group_size=128, Y=None):
+def gemm_q4_group_zp(X, packed, scales, zeros, group_size=128, Y=None, ws=None):
     """Y[m, n] = sum_k X[m, k] * (u[k, n] - zero[g, n]) * scale[g, n] (asymmetric 4-bit)."""
     squeeze = X.dim() == 1
     X2 = X.reshape(1, -1) if squeeze else X
@@ -305,8 +329,9 @@ def gemm_q4_group_zp(X, packed, scales, zeros, group_size=128, Y=None):
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float16, device=dev)
     _need(Y, "Y", torch.float16, (M, N), dev)
+    ws, ws_bytes = _workspace_q4(ws, M, K, N, dev)
     st = lib().wq_gemm_q4_group_zp(_ptr(X2), _ptr(packed), _ptr(scales), _ptr(zeros), _ptr(Y), M, K,
-                                   N, group_size, _stream(dev))
+                                   N, group_size, _ptr(ws), ws_bytes, _stream(dev))
     _check("wq_gemm_q4_group_zp", st)
     return Y.reshape(N) if squeeze else Y
 
@@ -332,6 +357,7 @@ def prepack_q2(qweight, perm=None, group_size=128):
     _need(qweight, "qweight", torch.int32, (R, N), dev)
     if perm is not None:
         _need(perm, "perm", torch.int32, (K,), dev)
+        _check_perm(perm, K)
     out = _packed(WQ_OP_Q2G, K, N, group_size, dev)
     st = lib().wq_prepack_q2(_ptr(qweight), _ptr(perm), _ptr(out), K, N, group_size, _stream(dev))
     _check("wq_prepack_q2", st)

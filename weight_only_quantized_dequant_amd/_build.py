@@ -42,6 +42,7 @@ def sources() -> list[str]:
 # the register allocator shuttles them between AGPRs and VGPRs on every block.
 EXTRA = {
     "q4_group.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "q4_tiled.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "q8_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 

@@ -36,16 +36,11 @@
 // 2j and 2j + 1 (rows 256 b + 64 j + 8 (l / 16) + e and 32 rows further),
 // placed so that (w >> 2i) & 0x00030003 is the operand pair i: pairs 0..3
 // are step 2j's rows (e, e + 4), pairs 4..7 step 2j + 1's.
-#include "wq_device.hpp"
+#include "q4_layout.hpp"
 #include "wq_internal.h"
 
 namespace wq {
 
-constexpr int kQ4Panel = 16;   // columns per panel (one MFMA tile)
-constexpr int kQ4Block = 128;  // rows per 4-bit block (4 MFMA steps of 32)
-// Rows per 1 KB block: 128 four-bit or 256 two-bit codes per 16 columns.
-template <int BITS>
-constexpr int block_rows() { return BITS == 4 ? 128 : 256; }
 constexpr int kQ4Ring = 4;     // blocks in flight per wave
 constexpr int kQ4MaxRun = 8;   // panels a workgroup walks at most
 constexpr int kQ4Threads = 512;             // 8 waves: two per SIMD
@@ -58,8 +53,12 @@ constexpr int kQ4RowPad = 32;
 // u = blocks per panel = ceil(K / 128); cpp, nsa and bw are unused.  The
 // packed weight is the blocks, then the row table: K uint16, entry k = the
 // group-order row of original row k (the inverse of perm), padded to 16 B.
+// The 4-bit weight then holds the forward table too (q4_fwd_table_offset):
+// u * 128 uint16, entry i = the original row of group-order row i (perm[i]),
+// 0xFFFF for the padding rows K .. u * 128 - 1.
 static size_t q4_block_bytes(const PanelPlan& p) { return (size_t)p.npanels * p.u * 1024; }
-static PanelPlan plan_blocks(int K, int N, int rows) {
+static size_t q4_inv_table_bytes(int K) { return ((size_t)K * 2 + 15) / 16 * 16; }
+static PanelPlan plan_blocks(int K, int N, int rows, bool fwd) {
   PanelPlan p{};
   p.P = kQ4Panel;
   p.cpp = 0;
@@ -67,17 +66,20 @@ static PanelPlan plan_blocks(int K, int N, int rows) {
   p.u = (K + rows - 1) / rows;
   p.nsa = 0;
   p.bw = 0;
-  p.packed_bytes = q4_block_bytes(p) + ((size_t)K * 2 + 15) / 16 * 16;
+  p.packed_bytes = q4_block_bytes(p) + q4_inv_table_bytes(K) + (fwd ? (size_t)p.u * rows * 2 : 0);
   return p;
 }
 PanelPlan plan_q4(int K, int N, int G) {
   (void)G;
-  return plan_blocks(K, N, block_rows<4>());
+  return plan_blocks(K, N, block_rows<4>(), true);
 }
-// 2-bit: the same structure with 256-row blocks.
+size_t q4_fwd_table_offset(int K, int N) {
+  return q4_block_bytes(plan_blocks(K, N, block_rows<4>(), true)) + q4_inv_table_bytes(K);
+}
+// 2-bit: the same structure with 256-row blocks (no forward table).
 PanelPlan plan_q2(int K, int N, int G) {
   (void)G;
-  return plan_blocks(K, N, block_rows<2>());
+  return plan_blocks(K, N, block_rows<2>(), false);
 }
 
 // Rows of X staged per launch: the LDS copies of X (MT rows of the padded
@@ -97,11 +99,6 @@ __device__ __forceinline__ void q4_mfma_pairs(uint32_t w, h2 out[4]) {
   out[2] = as_h2((w >> 8) & 0x000F000Fu);
   out[3] = as_h2((w >> 12) & 0x000F000Fu);
 }
-// The same four pairs as one MFMA operand (built in place, no moves).
-__device__ __forceinline__ u32x4 q4_mfma_operand(uint32_t w) {
-  return u32x4{w & 0x000F000Fu, (w >> 4) & 0x000F000Fu, (w >> 8) & 0x000F000Fu,
-               (w >> 12) & 0x000F000Fu};
-}
 // 2-bit: the operand of step 2j + H of word j: pairs 4H .. 4H + 3, i.e.
 // (w >> 2i) & 0x00030003, each half an exact subnormal u * 2^-24.
 template <int H>
@@ -118,8 +115,6 @@ __device__ __forceinline__ u32x4 q2_mfma_operand(uint32_t w) {
 // Code position (0..15) of row e of step 2j + H inside word j.
 __host__ __device__ constexpr int q2_pos(int h, int e) { return e < 4 ? e + 4 * h : e + 4 + 4 * h; }
 
-// Position of row e (0..7) of an octet among the 8 halves of an operand.
-__device__ __forceinline__ int q4_pos(int e) { return 2 * (e & 3) + (e >> 2); }
 
 // ---------------------------------------------------------------------------
 // Offline re-layout: one thread per (panel, block, lane) 16-byte piece.
@@ -127,12 +122,20 @@ __device__ __forceinline__ int q4_pos(int e) { return 2 * (e & 3) + (e >> 2); }
 __global__ __launch_bounds__(kThreads) void q4_prepack_kernel(const uint32_t* __restrict__ qw,
                                                               const int* __restrict__ perm,
                                                               uint32_t* __restrict__ out,
-                                                              uint16_t* __restrict__ table, int K,
+                                                              uint16_t* __restrict__ table,
+                                                              uint16_t* __restrict__ fwd, int K,
                                                               int N, int nb, int npanels) {
   const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
-  // Row table: table[perm[i]] = i.
-  for (size_t i = idx; i < (size_t)K; i += (size_t)gridDim.x * kThreads)
-    table[perm ? perm[i] : (int)i] = (uint16_t)i;
+  // Row tables: table[perm[i]] = i and fwd[i] = perm[i].  Entries of perm
+  // outside 0..K-1 (perm not a permutation: a broken precondition) are
+  // skipped in table and stored as 0xFFFF (no row) in fwd, never used as an
+  // address.
+  for (size_t i = idx; i < (size_t)nb * kQ4Block; i += (size_t)gridDim.x * kThreads) {
+    const int k = i < (size_t)K ? (perm ? perm[i] : (int)i) : -1;
+    const bool ok = k >= 0 && k < K;
+    if (ok) table[k] = (uint16_t)i;
+    fwd[i] = ok ? (uint16_t)k : (uint16_t)0xFFFFu;
+  }
   if (idx >= (size_t)npanels * nb * 64) return;
   const int l = (int)(idx % 64);
   const size_t pb = idx / 64;
@@ -148,6 +151,7 @@ __global__ __launch_bounds__(kThreads) void q4_prepack_kernel(const uint32_t* __
         const int i = i0 + e;
         if (i >= K) break;
         const int src = perm ? perm[i] : i;
+        if (src < 0 || src >= K) continue;
         const uint32_t sw = qw[(size_t)(src >> 3) * N + n];
         word |= ((sw >> (4 * (src & 7))) & 15u) << (4 * e);
       }
@@ -166,8 +170,10 @@ __global__ __launch_bounds__(kThreads) void q2_prepack_kernel(const uint32_t* __
                                                               int N, int nb, int npanels) {
   constexpr int BR = block_rows<2>();
   const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
-  for (size_t i = idx; i < (size_t)K; i += (size_t)gridDim.x * kThreads)
-    table[perm ? perm[i] : (int)i] = (uint16_t)i;
+  for (size_t i = idx; i < (size_t)K; i += (size_t)gridDim.x * kThreads) {
+    const int k = perm ? perm[i] : (int)i;
+    if (k >= 0 && k < K) table[k] = (uint16_t)i;
+  }
   if (idx >= (size_t)npanels * nb * 64) return;
   const int l = (int)(idx % 64);
   const size_t pb = idx / 64;
@@ -184,6 +190,7 @@ __global__ __launch_bounds__(kThreads) void q2_prepack_kernel(const uint32_t* __
           const int i = BR * b + 64 * j + 32 * h + 8 * (l / 16) + e;
           if (i >= K) continue;
           const int src = perm ? perm[i] : i;
+          if (src < 0 || src >= K) continue;
           const uint32_t sw = qw[(size_t)(src >> 4) * N + n];
           word |= ((sw >> (2 * (src & 15))) & 3u) << (2 * q2_pos(h, e));
         }
@@ -511,8 +518,9 @@ __global__ __launch_bounds__(kThreads) void q4_unpack_kernel(const uint8_t* __re
     for (int e = 0; e < 4; ++e) {
       const uint32_t bits = as_u32(pr[e]);
       const int ia = i0 + e, ib = i0 + e + 4;
-      if (ia < K) codes[(size_t)(perm ? perm[ia] : ia) * N + n] = (int8_t)((int)(bits & 0xFFFFu) - 8);
-      if (ib < K) codes[(size_t)(perm ? perm[ib] : ib) * N + n] = (int8_t)((int)(bits >> 16) - 8);
+      const int ka = ia < K ? (perm ? perm[ia] : ia) : -1, kb = ib < K ? (perm ? perm[ib] : ib) : -1;
+      if (ka >= 0 && ka < K) codes[(size_t)ka * N + n] = (int8_t)((int)(bits & 0xFFFFu) - 8);
+      if (kb >= 0 && kb < K) codes[(size_t)kb * N + n] = (int8_t)((int)(bits >> 16) - 8);
     }
   }
 }
@@ -546,8 +554,9 @@ __global__ __launch_bounds__(kThreads) void q2_unpack_kernel(const uint8_t* __re
       for (int e = 0; e < 4; ++e) {
         const uint32_t bits = as_u32(pr[e]);
         const int ia = i0 + e, ib = i0 + e + 4;
-        if (ia < K) codes[(size_t)(perm ? perm[ia] : ia) * N + n] = (int8_t)(bits & 0xFFFFu);
-        if (ib < K) codes[(size_t)(perm ? perm[ib] : ib) * N + n] = (int8_t)(bits >> 16);
+        const int ka = ia < K ? (perm ? perm[ia] : ia) : -1, kb = ib < K ? (perm ? perm[ib] : ib) : -1;
+        if (ka >= 0 && ka < K) codes[(size_t)ka * N + n] = (int8_t)(bits & 0xFFFFu);
+        if (kb >= 0 && kb < K) codes[(size_t)kb * N + n] = (int8_t)(bits >> 16);
       }
     }
   }
@@ -560,8 +569,10 @@ hipError_t launch_q4_prepack(const int32_t* qw, const int32_t* perm, void* out, 
   hipLaunchKernelGGL(q4_prepack_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)),
                      dim3(kThreads), 0, s, reinterpret_cast<const uint32_t*>(qw), perm,
                      reinterpret_cast<uint32_t*>(out),
-                     reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(out) + q4_block_bytes(p)), K,
-                     N, p.u, p.npanels);
+                     reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(out) + q4_block_bytes(p)),
+                     reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(out) +
+                                                 q4_fwd_table_offset(K, N)),
+                     K, N, p.u, p.npanels);
   return hipGetLastError();
 }
 
@@ -657,7 +668,7 @@ static hipError_t launch_blocks(const void* X, const void* packed, const void* s
                                 const void* zeros, void* Y, int M, int K, int N, int G,
                                 hipStream_t s) {
   constexpr int BR = block_rows<BITS>();
-  const PanelPlan p = plan_blocks(K, N, BR);
+  const PanelPlan p = plan_blocks(K, N, BR, BITS == 4);
   const int mtmax = max_mt(K, BR);
   for (int m0 = 0; m0 < M; m0 += mtmax) {
     const int mc = (M - m0) < mtmax ? (M - m0) : mtmax;
@@ -677,7 +688,9 @@ static hipError_t launch_blocks(const void* X, const void* packed, const void* s
 }
 
 hipError_t launch_q4_group(const void* X, const void* packed, const void* scales,
-                           const void* zeros, void* Y, int M, int K, int N, int G, hipStream_t s) {
+                           const void* zeros, void* Y, void* ws, int M, int K, int N, int G,
+                           hipStream_t s) {
+  if (M > kQ4TiledMinRows) return launch_q4_tiled(X, packed, scales, zeros, Y, ws, M, K, N, G, s);
   return launch_blocks<4>(X, packed, scales, zeros, Y, M, K, N, G, s);
 }
 

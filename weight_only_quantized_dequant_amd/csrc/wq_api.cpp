@@ -176,25 +176,45 @@ int wq_prepack_q4(const int32_t* qweight, const int32_t* perm, void* packed, int
   return hip_status(wq::launch_q4_prepack(qweight, perm, packed, K, N, G, as_stream(stream)));
 }
 
+namespace {
+
+// The 4-bit products above kQ4TiledMinRows rows take a workspace for X in
+// the packed weight's row order (read through 32-bit buffer offsets).
+int check_q4_ws(int M, int K, const void* ws, size_t ws_bytes) {
+  const size_t need = wq::q4_tiled_workspace_bytes(M, K);
+  if (need == 0) return WQ_OK;
+  if (need > (size_t)kMaxBytes) return WQ_ERR_SHAPE;
+  if (!ws || ws_bytes < need) return WQ_ERR_WORKSPACE;
+  if (!aligned16(ws)) return WQ_ERR_ALIGN;
+  return WQ_OK;
+}
+
+}  // namespace
+
 int wq_gemm_q4_group(const void* X, const void* packed, const void* scales, void* Y, int M, int K,
-                     int N, int G, void* stream) {
+                     int N, int G, void* workspace, size_t workspace_bytes, void* stream) {
   if (!X || !packed || !scales || !Y) return WQ_ERR_NULL;
   if (int st = check_q4(K, N, G)) return st;
   if (M < 1) return WQ_ERR_SHAPE;
   if ((long long)M * K * 2 > kMaxBytes) return WQ_ERR_SHAPE;
   if (!aligned16(X) || !aligned16(packed) || !aligned16(scales)) return WQ_ERR_ALIGN;
-  return hip_status(wq::launch_q4_group(X, packed, scales, nullptr, Y, M, K, N, G, as_stream(stream)));
+  if (int st = check_q4_ws(M, K, workspace, workspace_bytes)) return st;
+  return hip_status(wq::launch_q4_group(X, packed, scales, nullptr, Y, workspace, M, K, N, G,
+                                        as_stream(stream)));
 }
 
 int wq_gemm_q4_group_zp(const void* X, const void* packed, const void* scales, const void* zeros,
-                        void* Y, int M, int K, int N, int G, void* stream) {
+                        void* Y, int M, int K, int N, int G, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   if (!X || !packed || !scales || !zeros || !Y) return WQ_ERR_NULL;
   if (int st = check_q4(K, N, G)) return st;
   if (M < 1) return WQ_ERR_SHAPE;
   if ((long long)M * K * 2 > kMaxBytes) return WQ_ERR_SHAPE;
   if (!aligned16(X) || !aligned16(packed) || !aligned16(scales) || !aligned16(zeros))
     return WQ_ERR_ALIGN;
-  return hip_status(wq::launch_q4_group(X, packed, scales, zeros, Y, M, K, N, G, as_stream(stream)));
+  if (int st = check_q4_ws(M, K, workspace, workspace_bytes)) return st;
+  return hip_status(wq::launch_q4_group(X, packed, scales, zeros, Y, workspace, M, K, N, G,
+                                        as_stream(stream)));
 }
 
 int wq_unpack_q4(const void* packed, const int32_t* perm, int8_t* codes, int K, int N, int G,
@@ -257,6 +277,10 @@ int check_ws(int M, int K, int N, const void* ws, size_t ws_bytes) {
 }  // namespace
 
 size_t wq_workspace_bytes(int op, int M, int K, int N) {
+  if (op == WQ_OP_Q4G) {
+    if (M < 1 || K < 32 || K % 32 || K > 32768 || N < 4 || N % 4) return 0;
+    return wq::q4_tiled_workspace_bytes(M, K);
+  }
   if (op != WQ_OP_W8A8) return 0;
   if (check_w8a8(M, K, N)) return 0;
   return wq::w8a8_workspace_bytes(M, K, N);

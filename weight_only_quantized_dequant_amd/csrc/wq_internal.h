@@ -54,8 +54,22 @@ hipError_t launch_q3_unpack(const void* packed, int8_t* codes, int K, int N, hip
 hipError_t launch_q4_prepack(const int32_t* qw, const int32_t* perm, void* packed, int K, int N,
                              int G, hipStream_t s);
 // zeros: nullptr for the symmetric codes (offset 8), else fp16 [K/G, N].
+// ws: q4_tiled_workspace_bytes(M, K) bytes (unused when that is 0).
 hipError_t launch_q4_group(const void* X, const void* packed, const void* scales,
-                           const void* zeros, void* Y, int M, int K, int N, int G, hipStream_t s);
+                           const void* zeros, void* Y, void* ws, int M, int K, int N, int G,
+                           hipStream_t s);
+// Byte offset, inside a 4-bit packed weight, of its forward row table
+// (group-order row -> original row, 0xFFFF for padding rows).
+size_t q4_fwd_table_offset(int K, int N);
+// More than kQ4TiledMinRows rows of X: X is gathered into the packed
+// weight's row order in the workspace (in matrix-core operand order, with
+// the sums of X over runs of rows), then the tiled kernel reads the packed
+// weight once per 64 rows (q4_tiled.hip).
+constexpr int kQ4TiledMinRows = 8;
+size_t q4_tiled_workspace_bytes(int M, int K);
+hipError_t launch_q4_tiled(const void* X, const void* packed, const void* scales,
+                           const void* zeros, void* Y, void* ws, int M, int K, int N, int G,
+                           hipStream_t s);
 hipError_t launch_q4_unpack(const void* packed, const int32_t* perm, int8_t* codes, int K, int N,
                             int G, hipStream_t s);
 // 2-bit, asymmetric only (zeros required): the 4-bit kernel with 256-row blocks.
