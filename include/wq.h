@@ -106,9 +106,8 @@ size_t wq_packed_bytes(int op, int K, int N, int G);
  *   workspace, once the 128 x 128 output tiles alone fill the GPU, e.g. for
  *   M > 256 at N = 8192).
  * - WQ_OP_Q4G (wq_gemm_q4_group, wq_gemm_q4_group_zp): above 8 rows of X,
- *   X in the packed weight's row order and its sums over runs of rows,
- *   Mp * Kp * 2 + (Kp / 32) * Mp * 4 bytes (Mp = M rounded up to 16, Kp = K
- *   rounded up to 128).
+ *   X in the packed weight's row order, Mp * Kp * 2 bytes (Mp = M rounded
+ *   up to 16, Kp = K rounded up to 128).
  * - The other ops never need one (no partial result leaves a workgroup).
  * Returns 0 for an invalid shape.  Pure function. */
 size_t wq_workspace_bytes(int op, int M, int K, int N);
@@ -192,14 +191,14 @@ int wq_prepack_q4(const int32_t* qweight, const int32_t* perm, void* packed, int
  * accumulation).
  * Up to 8 rows: one launch per 8 rows of X, X staged whole in LDS, no
  * workspace.  More rows: X is first gathered into the packed weight's row
- * order in the workspace (in matrix-core operand order, with its sums over
- * runs of 64 or 32 rows), then one launch per 64 rows (48 for groups of 32)
- * reads the packed weight once (16-row matrix-core tiles).
+ * order in the workspace (in matrix-core operand order), then one launch
+ * per 64 rows (48 for groups of 64, 32 for groups of 32) reads the packed
+ * weight once (16-row matrix-core tiles).
  * workspace: device, workspace_bytes >= wq_workspace_bytes(WQ_OP_Q4G, M, K,
- *   N) = Mp * Kp * 2 + (Kp / 32) * Mp * 4 bytes when M > 8 (Mp = M rounded
- *   up to 16, Kp = K rounded up to 128), else 0 (NULL allowed); 16-byte
- *   aligned; needs no clearing.  WQ_ERR_WORKSPACE if missing or too small.
- *   Calls that overlap in time need separate workspaces.
+ *   N) = Mp * Kp * 2 bytes when M > 8 (Mp = M rounded up to 16, Kp = K
+ *   rounded up to 128), else 0 (NULL allowed); 16-byte aligned; needs no
+ *   clearing.  WQ_ERR_WORKSPACE if missing or too small.  Calls that overlap
+ *   in time need separate workspaces.
  * Rules: as wq_prepack_q4, M >= 1, M * K * 2 < 2^31. */
 int wq_gemm_q4_group(const void* X, const void* packed, const void* scales, void* Y, int M, int K,
                      int N, int G, void* workspace, size_t workspace_bytes, void* stream);

@@ -88,9 +88,8 @@ def test_q4_validation(L):
     assert f(P, P, P, P, 0, 4096, 11008, 128, None) == wq.WQ_ERR_SHAPE
     assert f(P, P, P, P, 1, 32768 + 128, 64, 128, None) == wq.WQ_ERR_SHAPE   # K bound
     assert f(P, P_MIS, P, P, 1, 4096, 11008, 128, None) == wq.WQ_ERR_ALIGN
-    # above 8 rows: X in the packed row order (rows rounded up to 16, K to
-    # 128, fp16) and its sums over 32-row runs (fp32)
-    q4ws = lambda Mp, Kp: Mp * Kp * 2 + (Kp // 32) * Mp * 4
+    # above 8 rows: X in the packed row order (rows rounded up to 16, K to 128, fp16)
+    q4ws = lambda Mp, Kp: Mp * Kp * 2
     need = L.wq_workspace_bytes(wq.WQ_OP_Q4G, 64, 4096, 11008)
     assert need == q4ws(64, 4096)
     assert L.wq_workspace_bytes(wq.WQ_OP_Q4G, 8, 4096, 11008) == 0
@@ -165,7 +164,7 @@ def test_workspace_bytes(L):
     assert w(256, 8190, 8192) == 0                   # invalid shape
     for op in (wq.WQ_OP_Q3, wq.WQ_OP_Q8G, wq.WQ_OP_Q2G):
         assert w(256, 8192, 8192, op) == 0           # these weight-only products need none
-    assert w(256, 8192, 8192, wq.WQ_OP_Q4G) == 256 * 8192 * 2 + 256 * 256 * 4   # 4-bit: X regathered
+    assert w(256, 8192, 8192, wq.WQ_OP_Q4G) == 256 * 8192 * 2   # 4-bit: X in the packed row order
     f3 = lambda *a: L.wq_gemm_int8_mixed(*a[:13], P, 64 << 20, *a[13:])
     c6 = ctypes.c_float(6.0)
     #      X  W  thr Y  Xq Sx Wq Sw cm mk cols nout acc (ws, bytes)

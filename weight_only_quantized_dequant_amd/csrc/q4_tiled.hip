@@ -17,30 +17,27 @@
 //     step s (32 rows) and 16-row tile mb the 16 x 32 operand is 1 KB, lane
 //     l's 16 bytes holding row 16 mb + l % 16, group-order rows
 //     32 s + 8 (l / 16) .. +7 in the order 0 4 1 5 2 6 3 7 (the order of the
-//     codes in a packed word).  Each lane reads its 8 original row numbers
-//     from the forward row table and gathers the 8 values, so every operand
-//     block is written whole by one wave.  Rows of X past M and padding rows
-//     past K are zero.  The same launch writes the sums of X over runs of R
-//     group-order rows (R = 64, or 32 for groups of 32), times the offset's
-//     factor: S = -8 * 2^-24 * sum for the symmetric codes, 2^-24 * sum with
-//     zero points.
+//     codes in a packed word).  A wave stages one row of X in LDS with
+//     coalesced loads, reads 64 octets of original row numbers from the
+//     forward row table, and gathers from LDS.  Rows of X past M and padding
+//     rows past K are zero.
 // (2) The GEMM.  A workgroup takes a run of at most 3 panels and every row
-//     of the launch (one to four 16-row tiles).  K is cut into units of 64
-//     rows (two MFMA steps); each of the 8 waves walks a contiguous range of
-//     whole blocks on its own, with a ring of RD units in flight: per unit
-//     its X operands (1 KB per tile and step, contiguous), its weights
-//     (8 bytes per lane and panel), the row sums and the scales.  Every
-//     operand and table is read through a buffer range that ends where the
-//     wave's share ends, so the loads the ring issues past it return zeros
-//     and cost no memory traffic; no LDS and no barrier until the end.  A
-//     weight word, unpacked into an operand, feeds one MFMA per 16-row tile.
-//     The accumulation of each run starts from the offset term instead of
-//     zero:
-//       C = S' + 2^-24 * sum_i x_i u_i = 2^-24 * sum_i x_i (u_i - z),
-//     S' = S (symmetric) or -z * S (zero points), and closes with
-//       tot += scale * C.
-//     At the end the 8 waves' partial tiles are added in LDS in a fixed order
-//     and Y = 2^24 * tot.
+//     of the launch (one to four 16-row tiles); each of its 8 waves walks a
+//     contiguous share of the 128-row blocks with a ring of blocks in
+//     flight.  Per block a wave issues few, wide loads (the vector memory
+//     path's per-instruction cost bounds this kernel): its X operands (1 KB
+//     per tile and step), one 16-byte piece of every panel's block, and one
+//     8-byte piece of the block's scale (and zero) rows, whose values reach
+//     the lanes that need them through cross-lane permutes.  Every operand
+//     is read through a buffer range that ends where the wave's share ends.
+//     Per run of rows that shares a group (a block, or 64 / 32 rows):
+//       C1 = 2^-24 * c * sum_i x_i   (matrix cores, a constant operand c:
+//                                     -8 for the symmetric codes, 1 with zeros)
+//       C  = D + 2^-24 * sum_i x_i u_i,  D = C1, or -z * C1 with zeros
+//       tot += scale * C
+//     so C = 2^-24 * sum_i x_i (u_i - z), the codes entering as exact fp16
+//     subnormals.  At the end the 8 waves' tiles are added in LDS in a fixed
+//     order and Y = 2^24 * tot.
 #include "q4_layout.hpp"
 #include "wq_internal.h"
 
@@ -53,74 +50,76 @@ constexpr int kQTMaxRows = 64;  // rows of X per launch at most
 
 int q4_tiled_kp(int K) { return (K + kQ4Block - 1) / kQ4Block * kQ4Block; }
 
-// Workspace: the operand-order copy of X (mbt 16-row tiles of Kp halves
-// each), then the row sums S: [Kp / R][mbt * 16] fp32, sized for R = 32.
+// Workspace: the operand-order copy of X, mbt 16-row tiles of Kp halves.
 static size_t q4_xo_bytes(int mbt, int Kp) { return (size_t)mbt * 16 * Kp * 2; }
 size_t q4_tiled_workspace_bytes(int M, int K) {
   if (M <= kQ4TiledMinRows) return 0;
-  const int mbt = (M + 15) / 16, Kp = q4_tiled_kp(K);
-  return q4_xo_bytes(mbt, Kp) + (size_t)(Kp / 32) * mbt * 16 * 4;
+  return q4_xo_bytes((M + 15) / 16, q4_tiled_kp(K));
 }
 
-// (1) Workgroup (unit u of 64 group-order rows, tile mb); wave h builds the
-// operand block of step 2u + h.  R64: one sum per unit (both waves), else
-// one per step.  zs: the factor the sums are stored with.
-constexpr int kQXThreads = 128;
+// (1) One wave per (row m of the padded tiles, range r of 64 octets of
+// group-order rows).  The wave copies row m of X into LDS (coalesced), then
+// lane l takes octet o = 64 r + l (group-order rows 8 o .. 8 o + 7): their
+// original rows from the forward table (one 16-byte load, issued first),
+// the 8 values read from LDS, and one 16-byte store of the operand piece
+// (step o / 4, lane m % 16 + 16 (o % 4) of tile m / 16).  Rows m >= M and
+// padding rows give zeros.
+constexpr int kQXThreads = 64;
+constexpr int kQXBatch = 8 * 64 * 8;  // halves of X per batch: 8 pieces of 16 bytes per lane
 __global__ __launch_bounds__(kQXThreads) void q4_xgather_kernel(const _Float16* __restrict__ X,
                                                                 const uint16_t* __restrict__ fwd,
-                                                                _Float16* __restrict__ Xo,
-                                                                float* __restrict__ S, int M, int K,
-                                                                int mbt, int R64, float zs) {
-  __shared__ float part[16];
-  const int t = threadIdx.x, lane = t & 63, h = t >> 6;
-  const int u = blockIdx.x, mb = blockIdx.y;
-  const int step = 2 * u + h;
-  const int m = 16 * mb + (lane & 15);
-  // Original rows of group-order rows 32 step + 8 (lane / 16) + e, e = 0..7
-  // (0xFFFF: a padding row).
-  const u32x4 tv = *reinterpret_cast<const u32x4*>(fwd + 32 * step + 8 * (lane >> 4));
-  const uint16_t* xrow = reinterpret_cast<const uint16_t*>(X) + (size_t)m * K;
+                                                                _Float16* __restrict__ Xo, int M,
+                                                                int K, int Kp, int mbt) {
+  extern __shared__ uint16_t xrow[];  // K rounded up to kQXBatch halves
+  const int lane = threadIdx.x;
+  const int m = blockIdx.y;
+  const int o = blockIdx.x * 64 + lane;
+  // Loads past the ranges return zeros: the table past Kp rows, and the
+  // whole row when m >= M.
+  const __amdgpu_buffer_rsrc_t tr = make_rsrc(fwd, Kp * 2);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(X + (size_t)(m < M ? m : 0) * K, m < M ? K * 2 : 0);
+  const u32x4 tv = __builtin_amdgcn_raw_buffer_load_b128(tr, o * 16, 0, 0);
+  // Every load of a batch is issued before its LDS writes.
+  for (int i0 = 0; i0 < K; i0 += kQXBatch) {
+    u32x4 t[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b)
+      t[b] = __builtin_amdgcn_raw_buffer_load_b128(xr, (i0 + (b * 64 + lane) * 8) * 2, 0, 0);
+#pragma unroll
+    for (int b = 0; b < 8; ++b)
+      *reinterpret_cast<u32x4*>(xrow + i0 + (b * 64 + lane) * 8) = t[b];
+  }
+  __syncthreads();
   uint32_t v[8];
-  float sum = 0.0f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int k = (int)((tv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-    v[e] = (m < M && k < K) ? (uint32_t)xrow[k] : 0u;
+    const uint32_t x = xrow[k < K ? k : K - 1];
+    v[e] = k < K ? x : 0u;  // 0xFFFF: a padding row
   }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) sum += (float)__builtin_bit_cast(_Float16, (uint16_t)v[e]);
   // Operand order 0 4 1 5 2 6 3 7: half 2 j holds row j, half 2 j + 1 row j + 4.
-  const u32x4 o = {v[0] | (v[4] << 16), v[1] | (v[5] << 16), v[2] | (v[6] << 16),
-                   v[3] | (v[7] << 16)};
-  *reinterpret_cast<u32x4*>(Xo + (((size_t)step * mbt + mb) * 64 + lane) * 8) = o;
-  // Rows of the step: the 4 lanes of row m hold 8 each.
-  sum += __shfl_xor(sum, 16);
-  sum += __shfl_xor(sum, 32);
-  const size_t rows = (size_t)mbt * 16;
-  if (R64) {
-    if (h == 1 && lane < 16) part[lane] = sum;
-    __syncthreads();
-    if (h == 0 && lane < 16) S[(size_t)u * rows + m] = (sum + part[lane]) * zs;
-  } else if (lane < 16) {
-    S[(size_t)step * rows + m] = sum * zs;
+  const u32x4 op = {v[0] | (v[4] << 16), v[1] | (v[5] << 16), v[2] | (v[6] << 16),
+                    v[3] | (v[7] << 16)};
+  if (o < Kp / 8) {
+    const int step = o >> 2, mb = m >> 4;
+    *reinterpret_cast<u32x4*>(Xo + (((size_t)step * mbt + mb) * 64 + (m & 15) + 16 * (o & 3)) * 8) =
+        op;
   }
 }
 
-// (2) MB: 16-row tiles (M <= 16 MB); NCL: runs closed per unit (1 for groups
-// of 64 rows or more, 2 for groups of 32); RD: units in flight per wave
-// (even, so a unit's half of its weight block is known at compile time).
-// lgu: log2 of the units per group (NCL = 1).
-template <int MB, int NCL, bool ZP, int RD>
+// (2) MB: 16-row tiles (M <= 16 MB); CPB: groups per block (1 for groups of
+// 128 rows or more, else 128 / G); BD: blocks in flight per wave.
+template <int MB, int CPB, bool ZP, int BD>
 __global__ __launch_bounds__(kQTThreads) void q4_tiled_kernel(
-    const _Float16* __restrict__ Xo, const float* __restrict__ S, const uint8_t* __restrict__ Wp,
+    const _Float16* __restrict__ Xo, const uint8_t* __restrict__ Wp,
     const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
-    _Float16* __restrict__ Y, int M, int mb0, int mbt, int N, int ngroups, int lgu, int nb,
+    _Float16* __restrict__ Y, int M, int mb0, int mbt, int N, int ngroups, int G, int nb,
     int npanels) {
-  static_assert(RD % 2 == 0, "ring depth must be even");
   typedef _Float16 h8 __attribute__((ext_vector_type(8)));
   typedef float f4 __attribute__((ext_vector_type(4)));
   typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
   constexpr int MT = 16 * MB;
+  constexpr int SPC = 4 / CPB;  // MFMA steps per group run
   __shared__ float red[kQTMaxRun * kQTWaves * MT * 16];  // [run][wave][MT][16]
 
   const int t = threadIdx.x, lane = t & 63;
@@ -132,84 +131,80 @@ __global__ __launch_bounds__(kQTThreads) void q4_tiled_kernel(
   const int run = G8 ? (int)(blockIdx.x % 8) * G8 + (int)(blockIdx.x / 8) : (int)blockIdx.x;
   const int p_begin = (int)((long long)run * npanels / gridDim.x);
   const int npr = (int)((long long)(run + 1) * npanels / gridDim.x) - p_begin;
-  // This wave's blocks [bw0, bw1) of every panel: units [2 bw0, 2 bw1).
-  // The share a wave takes rotates with the workgroup, so the workgroups of
-  // an XCD do not all read the same rows of X at the same moment.
+  // This wave's blocks [bw0, bw0 + nbw).  The share a wave takes rotates
+  // with the workgroup, so the workgroups of an XCD do not all read the same
+  // rows of X at the same moment.
   const int share = (wave + run) % kQTWaves;
-  const int bw0 = share * nb / kQTWaves, bw1 = (share + 1) * nb / kQTWaves;
-  const int nu = 2 * (bw1 - bw0);
+  const int bw0 = share * nb / kQTWaves, nbw = (share + 1) * nb / kQTWaves - bw0;
   const int col = lane & 15;
 
   // Buffer ranges that end with this wave's share.
-  const int xunit = 2 * mbt * 1024;  // X operand bytes of one unit, all tiles
+  const int xblock = 4 * mbt * 1024;  // X operand bytes of one block, all tiles
   const __amdgpu_buffer_rsrc_t xr =
-      make_rsrc(reinterpret_cast<const char*>(Xo) + (size_t)2 * bw0 * xunit, nu * xunit);
-  constexpr int CPU = NCL;                   // sum chunks per unit
-  const int chunk = mbt * 16 * 4;            // bytes of one chunk of sums
-  const __amdgpu_buffer_rsrc_t sr =
-      make_rsrc(reinterpret_cast<const char*>(S) + (size_t)2 * bw0 * CPU * chunk, nu * CPU * chunk);
+      make_rsrc(reinterpret_cast<const char*>(Xo) + (size_t)bw0 * xblock, nbw * xblock);
   __amdgpu_buffer_rsrc_t wr[kQTMaxRun];
 #pragma unroll
   for (int p = 0; p < kQTMaxRun; ++p) {
     const int panel = p < npr ? p_begin + p : 0;
-    wr[p] = make_rsrc(Wp + ((size_t)panel * nb + bw0) * 1024, p < npr ? (bw1 - bw0) * 1024 : 0);
+    wr[p] = make_rsrc(Wp + ((size_t)panel * nb + bw0) * 1024, p < npr ? nbw * 1024 : 0);
   }
-  const __amdgpu_buffer_rsrc_t scr = make_rsrc(scales, ngroups * N * 2);
+  // Scale (and zero) rows of a block: CPB groups x 48 columns (the run's
+  // panels) as one table, lane l holding halves 4 l .. 4 l + 3: group
+  // l / 12, columns 4 (l % 12) .. +3 of the run.  Lanes past the table, and
+  // columns past N (N % 4 == 0: a piece never straddles it), read zeros.
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, ngroups * N * 2);
   const __amdgpu_buffer_rsrc_t zr = make_rsrc(ZP ? zeros : scales, ngroups * N * 2);
-  int slane[kQTMaxRun];  // this lane's column in a scale row, or out of range
-#pragma unroll
-  for (int p = 0; p < kQTMaxRun; ++p) {
-    const int n = (p_begin + p) * kQ4Panel + col;
-    slane[p] = (p < npr && n < N) ? n * 2 : kOutOfRange;
-  }
-  const int xlane = lane * 16, wlane = lane * 16, sl = (lane >> 4) * 16;
+  const int tcol = p_begin * kQ4Panel + 4 * (lane % 12);
+  const bool tlive = lane < 12 * CPB && tcol < N;
+  const int tlane = (lane / 12) * N * 2 + tcol * 2;
+  // Where this lane finds its column's value for panel p, group c of a
+  // block: lane (48 c + 16 p + col) / 4, dword (col / 2) % 2, half col % 2.
+  const int hshift = 16 * (col & 1);
+  const bool hi = (col & 2) != 0;
+  const int xlane = lane * 16, wlane = lane * 16;
 
-  struct Unit {
-    u32x4 a[2][MB];               // X operands: step s, tile mb
-    u32x2v w[kQTMaxRun];          // weight words of steps 2 (u & 1), +1
-    f4 s[NCL][MB];                // offset terms (row sums)
-    uint32_t sc[kQTMaxRun][NCL];  // scale bits of the runs' groups
-    uint32_t zq[kQTMaxRun][NCL];  // zero bits (ZP)
+  struct Block {
+    u32x4 a[4][MB];        // X operands: step, tile
+    u32x4 w[kQTMaxRun];    // weight words of the 4 steps, per panel
+    u32x2v sc;             // this lane's piece of the scale table
+    u32x2v zq;             // and of the zero table (ZP)
   };
-  // Loads of this wave's unit j (ring slot parity P = j & 1).  The ring asks
-  // for up to RD units past the wave's share; those loads take the share's
-  // last unit again (their values are never used), so every address stays
-  // inside the wave's ranges.  A wave with no share has empty ranges: its
-  // loads all return zeros.
-  auto load = [&](int jr, Unit& q, auto parity) {
-    constexpr int P = decltype(parity)::value;
-    const int j = jr < nu ? jr : (nu > 0 ? nu - 1 : 0);
-    const int xo = j * xunit + mb0 * 1024;
+  // Loads of this wave's block j.  The ring asks for blocks past the share;
+  // those loads take the share's last block again (their values are never
+  // used), so every address stays inside the wave's ranges.  A wave with no
+  // share has empty ranges: its loads all return zeros.
+  auto clampj = [&](int jr) { return jr < nbw ? jr : (nbw > 0 ? nbw - 1 : 0); };
+  auto load_x = [&](int jr, Block& q, int mb) {
+    const int j = clampj(jr);
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        q.a[st][mb] = __builtin_amdgcn_raw_buffer_load_b128(xr, xlane + mb * 1024,
-                                                            xo + st * mbt * 1024, 0);
-    const int wo = (j >> 1) * 1024;
+    for (int st = 0; st < 4; ++st)
+      q.a[st][mb] = __builtin_amdgcn_raw_buffer_load_b128(
+          xr, xlane + mb * 1024, (4 * j + st) * mbt * 1024 + mb0 * 1024, 0);
+  };
+  auto load_wt = [&](int jr, Block& q) {
+    const int j = clampj(jr);
 #pragma unroll
     for (int p = 0; p < kQTMaxRun; ++p)
-      q.w[p] = __builtin_bit_cast(
-          u32x2v, __builtin_amdgcn_raw_buffer_load_b64(wr[p], wlane + 8 * P, wo, 0));
+      q.w[p] = __builtin_amdgcn_raw_buffer_load_b128(wr[p], wlane, j * 1024, 2);
+    // First group of the block; the whole offset is in the lane's offset,
+    // so groups past the last one (padding rows) fall out of range.
+    const int g0 = ((bw0 + j) * kQ4Block) / G;
+    const int so = tlive ? tlane + g0 * N * 2 : kOutOfRange;
+    q.sc = __builtin_bit_cast(u32x2v, __builtin_amdgcn_raw_buffer_load_b64(sr, so, 0, 0));
+    if constexpr (ZP)
+      q.zq = __builtin_bit_cast(u32x2v, __builtin_amdgcn_raw_buffer_load_b64(zr, so, 0, 0));
+  };
+  auto load = [&](int jr, Block& q) {
 #pragma unroll
-    for (int k = 0; k < NCL; ++k)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        q.s[k][mb] = __builtin_bit_cast(
-            f4, __builtin_amdgcn_raw_buffer_load_b128(sr, sl + (mb0 + mb) * 64,
-                                                      (j * CPU + k) * chunk, 0));
-    const int u = 2 * bw0 + j;
-#pragma unroll
-    for (int k = 0; k < NCL; ++k) {
-      // Padding rows past K (zero in X) take the last group's scale.
-      const int g0 = NCL == 1 ? (u >> lgu) : 2 * u + k;
-      const int so = (g0 < ngroups ? g0 : ngroups - 1) * N * 2;
-#pragma unroll
-      for (int p = 0; p < kQTMaxRun; ++p) {
-        q.sc[p][k] = __builtin_amdgcn_raw_buffer_load_b16(scr, slane[p], so, 0);
-        if constexpr (ZP) q.zq[p][k] = __builtin_amdgcn_raw_buffer_load_b16(zr, slane[p], so, 0);
-      }
-    }
+    for (int mb = 0; mb < MB; ++mb) load_x(jr, q, mb);
+    load_wt(jr, q);
+  };
+  // This lane's column value of panel p, group c from a block's table.
+  auto table_value = [&](const u32x2v& tbl, int p, int c) {
+    const int src = ((48 * c + 16 * p + col) >> 2) * 4;
+    const uint32_t d0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)tbl[0]);
+    const uint32_t d1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)tbl[1]);
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)((hi ? d1 : d0) >> hshift));
   };
 
   f4 tot[kQTMaxRun][MB];
@@ -217,66 +212,132 @@ __global__ __launch_bounds__(kQTThreads) void q4_tiled_kernel(
   for (int p = 0; p < kQTMaxRun; ++p)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) tot[p][mb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+  // The constant operand of the row sums: -8 * 2^-24 (fp16 subnormal bits
+  // 0x8008) for the symmetric codes, 2^-24 (0x0001) with zeros.
+  const uint32_t cbits = ZP ? 0x00010001u : 0x80088008u;
+  const h8 cop = __builtin_bit_cast(h8, u32x4{cbits, cbits, cbits, cbits});
+  const f4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
-  // One unit.  Every panel slot runs, also past the run (its weights and
+  // One block.  Every panel slot runs, also past the run (its weights and
   // scales read as zero, its tile is never stored): no branch between an
   // MFMA and the first read of its result.
-  auto compute = [&](const Unit& q) {
-    h8 b[2][kQTMaxRun];
+  auto compute = [&](const Block& q) {
 #pragma unroll
-    for (int p = 0; p < kQTMaxRun; ++p) {
-      b[0][p] = __builtin_bit_cast(h8, q4_mfma_operand(q.w[p][0]));
-      b[1][p] = __builtin_bit_cast(h8, q4_mfma_operand(q.w[p][1]));
-    }
+    for (int c = 0; c < CPB; ++c) {
+      f4 c1[MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const h8 a[2] = {__builtin_bit_cast(h8, q.a[0][mb]), __builtin_bit_cast(h8, q.a[1][mb])};
+      for (int mb = 0; mb < MB; ++mb) {
+        f4 r = zero4;
+#pragma unroll
+        for (int st = c * SPC; st < (c + 1) * SPC; ++st)
+          r = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, q.a[st][mb]), cop, r,
+                                                     0, 0, 0);
+        c1[mb] = r;
+      }
 #pragma unroll
       for (int p = 0; p < kQTMaxRun; ++p) {
+        h8 b[SPC];
 #pragma unroll
-        for (int k = 0; k < NCL; ++k) {
-          f4 c = q.s[k][mb];
-          if constexpr (ZP) c *= -(float)__builtin_bit_cast(_Float16, (uint16_t)q.zq[p][k]);
-          if constexpr (NCL == 1) {
-            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], b[0][p], c, 0, 0, 0);
-            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[1], b[1][p], c, 0, 0, 0);
-          } else {
-            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[k], b[k][p], c, 0, 0, 0);
-          }
-          const float sv = (float)__builtin_bit_cast(_Float16, (uint16_t)q.sc[p][k]);
+        for (int i = 0; i < SPC; ++i)
+          b[i] = __builtin_bit_cast(h8, q4_mfma_operand(q.w[p][c * SPC + i]));
+        const float sv = table_value(q.sc, p, c);
+        float nz = 1.0f;
+        if constexpr (ZP) nz = -table_value(q.zq, p, c);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) tot[p][mb][r] = __builtin_fmaf(sv, c[r], tot[p][mb][r]);
+        for (int mb = 0; mb < MB; ++mb) {
+          f4 r = c1[mb];
+          if constexpr (ZP) r *= nz;
+#pragma unroll
+          for (int i = 0; i < SPC; ++i)
+            r = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, q.a[c * SPC + i][mb]),
+                                                       b[i], r, 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) tot[p][mb][e] = __builtin_fmaf(sv, r[e], tot[p][mb][e]);
         }
       }
     }
   };
 
-  // The ring: slot i holds unit j + i.  Loads are issued in unit order and
-  // scheduling barriers keep them so, so the oldest slot's loads are always
-  // the first outstanding ones and each wait before a compute covers only
-  // its own unit.
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
-  Unit q[RD];
+  if constexpr (BD > 0) {
+    // The ring: slot i holds block j + i.  Loads are issued in block order
+    // and scheduling barriers keep them so, so the oldest slot's loads are
+    // always the first outstanding ones and each wait before a compute
+    // covers only its own block.
+    Block q[BD];
 #pragma unroll
-  for (int i = 0; i < RD; ++i) {
-    if (i % 2 == 0) load(i, q[i], P0{});
-    else load(i, q[i], P1{});
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  int j = 0;
-  for (; j + RD < nu; j += RD) {
-#pragma unroll
-    for (int i = 0; i < RD; ++i) {
-      compute(q[i]);
-      if (i % 2 == 0) load(j + RD + i, q[i], P0{});
-      else load(j + RD + i, q[i], P1{});
+    for (int i = 0; i < BD; ++i) {
+      load(i, q[i]);
       __builtin_amdgcn_sched_barrier(0);
     }
-  }
+    int j = 0;
+    for (; j + BD < nbw; j += BD) {
 #pragma unroll
-  for (int i = 0; i < RD; ++i)
-    if (j + i < nu) compute(q[i]);
+      for (int i = 0; i < BD; ++i) {
+        compute(q[i]);
+        load(j + BD + i, q[i]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < BD; ++i)
+      if (j + i < nbw) compute(q[i]);
+  } else {
+    // Three or four tiles: one block's X fills the registers, so the next
+    // block streams in tile by tile.  The weights and tables of block j + 1
+    // are requested as soon as block j's are unpacked, and the X of tile mb
+    // of block j + 1 right after tile mb of block j is done.
+    // The prologue issues block 0 in the loop's order (weights and tables,
+    // then X tile by tile), so every wait in the loop counts the same loads.
+    Block q;
+    load_wt(0, q);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      load_x(0, q, mb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int j = 0; j < nbw; ++j) {
+      h8 b[kQTMaxRun][4];
+      float sv[kQTMaxRun][CPB], nz[kQTMaxRun][CPB];
+#pragma unroll
+      for (int p = 0; p < kQTMaxRun; ++p) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) b[p][st] = __builtin_bit_cast(h8, q4_mfma_operand(q.w[p][st]));
+#pragma unroll
+        for (int c = 0; c < CPB; ++c) {
+          sv[p][c] = table_value(q.sc, p, c);
+          nz[p][c] = ZP ? -table_value(q.zq, p, c) : 1.0f;
+        }
+      }
+      load_wt(j + 1, q);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int c = 0; c < CPB; ++c) {
+          f4 c1 = zero4;
+#pragma unroll
+          for (int st = c * SPC; st < (c + 1) * SPC; ++st)
+            c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, q.a[st][mb]), cop,
+                                                        c1, 0, 0, 0);
+#pragma unroll
+          for (int p = 0; p < kQTMaxRun; ++p) {
+            f4 r = c1;
+            if constexpr (ZP) r *= nz[p][c];
+#pragma unroll
+            for (int st = c * SPC; st < (c + 1) * SPC; ++st)
+              r = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, q.a[st][mb]),
+                                                         b[p][st], r, 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              tot[p][mb][e] = __builtin_fmaf(sv[p][c], r[e], tot[p][mb][e]);
+          }
+        }
+        load_x(j + 1, q, mb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
 
 #pragma unroll
   for (int p = 0; p < kQTMaxRun; ++p)
@@ -299,43 +360,52 @@ __global__ __launch_bounds__(kQTThreads) void q4_tiled_kernel(
   }
 }
 
-// Units in flight per wave: as many as fit the registers without spilling.
-constexpr int q4_tiled_depth(int MB, int NCL, bool ZP) {
-  return NCL == 1 ? (MB == 1 ? 6 : MB == 2 ? 4 : 2) : (MB == 1 ? 4 : 2);
+// Blocks in flight per wave: what fits the registers without spilling.
+// 0: the tile-by-tile stream of one block (three or four tiles).
+constexpr int q4_tiled_depth(int MB, int CPB, bool ZP) {
+  return (void)ZP, MB >= 3 ? 0 : (MB == 1 || CPB == 1) ? 2 : 1;
 }
+// Tiles per launch at most: groups of 64 and 32 close 2 and 4 times per
+// block, and their extra row sums and scale values no longer fit the
+// registers with four (three) tiles.
+constexpr int q4_tiled_max_tiles(int G) { return G == 32 ? 2 : G == 64 ? 3 : 4; }
 
-template <int MB, int NCL, bool ZP>
-static hipError_t launch_q4_tiled_t(const _Float16* Xo, const float* S, const uint8_t* Wp,
-                                    const _Float16* scales, const _Float16* zeros, _Float16* Y,
-                                    int M, int mb0, int mbt, int K, int N, int G, hipStream_t s) {
-  constexpr int RD = q4_tiled_depth(MB, NCL, ZP);
+template <int MB, int CPB, bool ZP>
+static hipError_t launch_q4_tiled_t(const _Float16* Xo, const uint8_t* Wp, const _Float16* scales,
+                                    const _Float16* zeros, _Float16* Y, int M, int mb0, int mbt,
+                                    int K, int N, int G, hipStream_t s) {
+  constexpr int BD = q4_tiled_depth(MB, CPB, ZP);
   const int nb = q4_tiled_kp(K) / kQ4Block, npanels = (N + kQ4Panel - 1) / kQ4Panel;
   const int cus = device_cus();
   int grid = npanels < cus ? npanels : cus;
   if ((npanels + grid - 1) / grid > kQTMaxRun) grid = (npanels + kQTMaxRun - 1) / kQTMaxRun;
-  int lgu = 0;
-  while ((64 << lgu) < G) ++lgu;
-  hipLaunchKernelGGL((q4_tiled_kernel<MB, NCL, ZP, RD>), dim3(grid), dim3(kQTThreads), 0, s, Xo, S,
-                     Wp, scales, zeros, Y, M, mb0, mbt, N, K / G, lgu, nb, npanels);
+  hipLaunchKernelGGL((q4_tiled_kernel<MB, CPB, ZP, BD>), dim3(grid), dim3(kQTThreads), 0, s, Xo,
+                     Wp, scales, zeros, Y, M, mb0, mbt, N, K / G, G, nb, npanels);
   return hipGetLastError();
 }
 
+template <int MB, int CPB>
+static hipError_t launch_q4_tiled_z(const _Float16* Xo, const uint8_t* Wp, const _Float16* scales,
+                                    const _Float16* zeros, _Float16* Y, int M, int mb0, int mbt,
+                                    int K, int N, int G, hipStream_t s) {
+  return zeros ? launch_q4_tiled_t<MB, CPB, true>(Xo, Wp, scales, zeros, Y, M, mb0, mbt, K, N, G, s)
+               : launch_q4_tiled_t<MB, CPB, false>(Xo, Wp, scales, zeros, Y, M, mb0, mbt, K, N, G,
+                                                   s);
+}
+
 template <int MB>
-static hipError_t launch_q4_tiled_mb(const _Float16* Xo, const float* S, const uint8_t* Wp,
-                                     const _Float16* scales, const _Float16* zeros, _Float16* Y,
-                                     int M, int mb0, int mbt, int K, int N, int G, hipStream_t s) {
+static hipError_t launch_q4_tiled_mb(const _Float16* Xo, const uint8_t* Wp, const _Float16* scales,
+                                     const _Float16* zeros, _Float16* Y, int M, int mb0, int mbt,
+                                     int K, int N, int G, hipStream_t s) {
   if (G == 32) {
-    // Launches for groups of 32 take at most three tiles (see below).
-    if constexpr (MB > 3) return hipErrorInvalidValue;
-    else
-      return zeros ? launch_q4_tiled_t<MB, 2, true>(Xo, S, Wp, scales, zeros, Y, M, mb0, mbt, K, N,
-                                                    G, s)
-                   : launch_q4_tiled_t<MB, 2, false>(Xo, S, Wp, scales, zeros, Y, M, mb0, mbt, K,
-                                                     N, G, s);
+    if constexpr (MB > q4_tiled_max_tiles(32)) return hipErrorInvalidValue;
+    else return launch_q4_tiled_z<MB, 4>(Xo, Wp, scales, zeros, Y, M, mb0, mbt, K, N, G, s);
   }
-  return zeros ? launch_q4_tiled_t<MB, 1, true>(Xo, S, Wp, scales, zeros, Y, M, mb0, mbt, K, N, G, s)
-               : launch_q4_tiled_t<MB, 1, false>(Xo, S, Wp, scales, zeros, Y, M, mb0, mbt, K, N, G,
-                                                 s);
+  if (G == 64) {
+    if constexpr (MB > q4_tiled_max_tiles(64)) return hipErrorInvalidValue;
+    else return launch_q4_tiled_z<MB, 2>(Xo, Wp, scales, zeros, Y, M, mb0, mbt, K, N, G, s);
+  }
+  return launch_q4_tiled_z<MB, 1>(Xo, Wp, scales, zeros, Y, M, mb0, mbt, K, N, G, s);
 }
 
 hipError_t launch_q4_tiled(const void* X, const void* packed, const void* scales,
@@ -346,27 +416,23 @@ hipError_t launch_q4_tiled(const void* X, const void* packed, const void* scales
   const uint8_t* Wp = reinterpret_cast<const uint8_t*>(packed);
   const uint16_t* fwd = reinterpret_cast<const uint16_t*>(Wp + q4_fwd_table_offset(K, N));
   _Float16* Xo = reinterpret_cast<_Float16*>(ws);
-  float* S = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + q4_xo_bytes(mbt, Kp));
-  const float zs = zeros ? 1.0f / kTwo24 : -8.0f / kTwo24;
-  hipLaunchKernelGGL(q4_xgather_kernel, dim3(Kp / 64, mbt), dim3(kQXThreads), 0, s,
-                     reinterpret_cast<const _Float16*>(X), fwd, Xo, S, M, K, mbt, G >= 64 ? 1 : 0,
-                     zs);
+  hipLaunchKernelGGL(q4_xgather_kernel, dim3((Kp / 8 + 63) / 64, mbt * 16), dim3(kQXThreads),
+                     (size_t)((K + kQXBatch - 1) / kQXBatch) * kQXBatch * 2, s,
+                     reinterpret_cast<const _Float16*>(X), fwd, Xo, M, K, Kp, mbt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const _Float16* sc = reinterpret_cast<const _Float16*>(scales);
   const _Float16* zp = reinterpret_cast<const _Float16*>(zeros);
-  // Groups of 32 close twice per unit; with four tiles that no longer fits
-  // the registers, so those launches take at most 48 rows.
-  const int rows = G == 32 ? 48 : kQTMaxRows;
+  const int rows = 16 * q4_tiled_max_tiles(G);
   for (int m0 = 0; m0 < M; m0 += rows) {
     const int mc = M - m0 < rows ? M - m0 : rows;
     _Float16* Yc = reinterpret_cast<_Float16*>(Y) + (size_t)m0 * N;
     const int mb0 = m0 / 16;
     switch ((mc + 15) / 16) {
-      case 1: e = launch_q4_tiled_mb<1>(Xo, S, Wp, sc, zp, Yc, mc, mb0, mbt, K, N, G, s); break;
-      case 2: e = launch_q4_tiled_mb<2>(Xo, S, Wp, sc, zp, Yc, mc, mb0, mbt, K, N, G, s); break;
-      case 3: e = launch_q4_tiled_mb<3>(Xo, S, Wp, sc, zp, Yc, mc, mb0, mbt, K, N, G, s); break;
-      default: e = launch_q4_tiled_mb<4>(Xo, S, Wp, sc, zp, Yc, mc, mb0, mbt, K, N, G, s); break;
+      case 1: e = launch_q4_tiled_mb<1>(Xo, Wp, sc, zp, Yc, mc, mb0, mbt, K, N, G, s); break;
+      case 2: e = launch_q4_tiled_mb<2>(Xo, Wp, sc, zp, Yc, mc, mb0, mbt, K, N, G, s); break;
+      case 3: e = launch_q4_tiled_mb<3>(Xo, Wp, sc, zp, Yc, mc, mb0, mbt, K, N, G, s); break;
+      default: e = launch_q4_tiled_mb<4>(Xo, Wp, sc, zp, Yc, mc, mb0, mbt, K, N, G, s); break;
     }
     if (e != hipSuccess) return e;
   }
