@@ -122,11 +122,18 @@ size_t wq_workspace_bytes(int op, int M, int K, int N);
  * Rules: K % 32 == 0, K >= 32, N % 4 == 0, N >= 4. */
 int wq_prepack_q3(const int32_t* qweight, void* packed, int K, int N, void* stream);
 
-/* 3-bit matvec:  y[n] = sum_k x[k] * (scale[n] * q[k, n] - zero[n]).
+/* 3-bit matvec ("GPTQ CUDA kernel walkthrough", yelogs.com, section
+ * "CUDA核函數設計與實現": 32 three-bit codes per 3 int32 words, each code
+ * shifted and masked out, dequantised as scale * q - zero with one scale and
+ * one zero per output column, and multiplied into the vector; the fp16 form
+ * is that page's half2 path):
+ *   y[n] = sum_k x[k] * (scale[n] * q[k, n] - zero[n]).
  * x [K], scales [N], zeros [N], y [N] (written) share `dtype` (WQ_F32 or
  * WQ_F16); zero is the stored per-column offset (w = scale*q - zero).
  * Accumulation is fp32 in both cases; the fp16 result is rounded once, to
- * nearest even.  packed: from wq_prepack_q3 at the same (K, N).
+ * nearest even.  Any finite x is taken as given (no step scales it up, so
+ * y is finite whenever the fp32 sums are).  packed: from wq_prepack_q3 at
+ * the same (K, N).
  * Rules: as wq_prepack_q3, and K <= 32768 (fp16) / 16384 (fp32). */
 int wq_matvec_q3(const void* x, const void* packed, const void* scales, const void* zeros,
                  void* y, int K, int N, int dtype, void* stream);
@@ -355,7 +362,10 @@ int wq_unpack_q2(const void* packed, const int32_t* perm, int8_t* codes, int K, 
 
 /* ---------------------------------------------------- measurement only -- */
 
-/* References for timing the streaming products; neither computes anything.
+/* References for timing the streaming products; neither computes anything
+ * and no product calls them.  They sit in the library so that the dispatch
+ * floor and the streaming ceiling are measured through the same build, launch
+ * path and loads as the products they are compared with.
  * wq_calib_empty: one launch of an empty kernel, grid x threads (1..1024),
  *   that touches no memory: the dispatch floor of a launch.
  * wq_calib_stream_read: one launch that reads bytes [0, bytes) of buf once

@@ -794,6 +794,20 @@ def test_large_fp16_activations_all_paths(wq):
                "q2 large x")
 
 
+def test_large_fp32_activations_q3(wq):
+    """fp32 3-bit matvec with |x| far beyond any fp16 range: a few rows at
+    +-2^110 over N(0,1), then every row scaled by 2^100.  The products stay
+    finite in fp32 (|y| ~ 2^110), so the kernel must too: no step may scale
+    x up on its way in."""
+    d = synth.gen_q3(1024, 256, seed=85, dtype="f32")
+    packed = wq.prepack_q3(cu(d["qweight"]), 1024)
+    for x in (_with_large_entries(d["x"], (3, 100, 517, 1000), value=2.0 ** 110).astype(np.float32),
+              (d["x"].astype(np.float64) * 2.0 ** 100).astype(np.float32)):
+        y = host(wq.matvec_q3(cu(x), packed, cu(d["scales"]), cu(d["zeros"])))
+        assert np.isfinite(y).all()
+        assert_tol(y, oracle.matvec_q3(x, d["qweight"], d["scales"], d["zeros"]), "q3 f32 large x")
+
+
 # ============================================================ measurement ==
 
 @pytest.mark.parametrize("nbytes,pos", [(1 << 24, 0), (1 << 24, (1 << 24) - 4), (65536 * 3 + 48, 65536 * 3 + 36),

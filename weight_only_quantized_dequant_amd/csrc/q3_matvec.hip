@@ -234,9 +234,11 @@ __global__ __launch_bounds__(THREADS) void q3_panel_kernel(
                        (_Float16)__builtin_ldexpf(xs[q.b], cls - q.pb - kQ3XShift)};
         xp[blk * 16 + P] = as_u32(hv);
       } else {
-        // fp32: undo the 2^(p - 24) of each subnormal code in the activation.
-        xp[(blk * 16 + P) * 2] = __builtin_bit_cast(uint32_t, __builtin_ldexpf(xs[q.a], 24 - q.pa));
-        xp[(blk * 16 + P) * 2 + 1] = __builtin_bit_cast(uint32_t, __builtin_ldexpf(xs[q.b], 24 - q.pb));
+        // fp32: x as given; the code's 2^(p - 24) is undone on the code
+        // itself (an exact power-of-two scale of a small integer), so no
+        // finite x can overflow.
+        xp[(blk * 16 + P) * 2] = __builtin_bit_cast(uint32_t, xs[q.a]);
+        xp[(blk * 16 + P) * 2 + 1] = __builtin_bit_cast(uint32_t, xs[q.b]);
       }
     }
   };
@@ -300,8 +302,10 @@ __global__ __launch_bounds__(THREADS) void q3_panel_kernel(
             const int slot = q3_class_slot(q3_class(P));
             acc[slot][col] = dot2(pr[P], as_h2(xr[P][0]), acc[slot][col]);
           } else {
-            acc[0][col] = __builtin_fmaf((float)pr[P].x, __builtin_bit_cast(float, xr[P][0]), acc[0][col]);
-            acc[0][col] = __builtin_fmaf((float)pr[P].y, __builtin_bit_cast(float, xr[P][1]), acc[0][col]);
+            const float ua = (float)(1 << (24 - q3_pair(P).pa));
+            const float ub = (float)(1 << (24 - q3_pair(P).pb));
+            acc[0][col] = __builtin_fmaf((float)pr[P].x * ua, __builtin_bit_cast(float, xr[P][0]), acc[0][col]);
+            acc[0][col] = __builtin_fmaf((float)pr[P].y * ub, __builtin_bit_cast(float, xr[P][1]), acc[0][col]);
           }
         }
       }
