@@ -110,14 +110,17 @@ def wl_q8(wq, torch, dev, M=1):
     def make(R):
         base = [torch.from_numpy(d["X"]).to(dev), wq.prepack_q8(torch.from_numpy(d["q"]).to(dev)),
                 torch.from_numpy(d["scales"]).to(dev)]
-        copies = [[t.clone() for t in base] + [torch.empty((M, N), dtype=torch.float16, device=dev)]
+        # one workspace (the K slices' partial tiles, above 8 rows) serves every copy
+        nws = wq.workspace_bytes(wq.WQ_OP_Q8G, M, K, N)
+        ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+        copies = [[t.clone() for t in base] + [torch.empty((M, N), dtype=torch.float16, device=dev), ws]
                   for _ in range(R)]
         return copies
 
     def run(c):
-        wq.gemm_q8_group(c[0], c[1], c[2], G, Y=c[3])
+        wq.gemm_q8_group(c[0], c[1], c[2], G, Y=c[3], ws=c[4])
 
-    kind = "gemv" if M == 1 else "streaming" if M < 32 else "gemm"
+    kind = "gemv" if M == 1 else "streaming" if M <= 8 else "gemm"
     w = Workload(f"q8_group_{kind} M={M} K={K} N={N} G={G}", nbytes, make, run,
                  flops=0 if M == 1 else 2 * M * K * N)
     w.peak_tops = FP16_PEAK_TFLOPS
@@ -503,7 +506,7 @@ def _make_workload(name, wq, torch, dev):
 SECONDARY = ("q3_f32_1024", "q3_f16_4096x4096", "q3_f16_4096x11008", "q3_f16_11008x4096",
              "q4_m1", "q4_m2", "q4_m4", "q4_m8", "q4_m16", "q4_m32", "q4_m64", "q4zp_m1",
              "q4zp_act_m64", "q4zp_g64_m1", "q2_m1", "q2_m8",
-             "q8_m2", "q8_m8", "q8_m512", "w8a8", "w8a8_smooth", "int8_mixed")
+             "q8_m2", "q8_m8", "q8_m16", "q8_m32", "q8_m512", "w8a8", "w8a8_smooth", "int8_mixed")
 
 
 def main():

@@ -105,6 +105,10 @@ size_t wq_packed_bytes(int op, int K, int N, int G);
  *   S * M * N * 4 bytes (S = 2 at M = 256, K = N = 8192: 16 MiB; S = 1, no
  *   workspace, once the 128 x 128 output tiles alone fill the GPU, e.g. for
  *   M > 256 at N = 8192).
+ * - WQ_OP_Q8G (wq_gemm_q8_group): above 8 rows of X, while the 32 x 128
+ *   output tiles alone do not fill the GPU, the fp32 partial tiles of S K
+ *   slices, S * M * N * 4 bytes (S = 8 for M <= 64 at K = N = 4096; the
+ *   size holds for every group size the tiled path takes).
  * - WQ_OP_Q4G (wq_gemm_q4_group, wq_gemm_q4_group_zp): above 8 rows of X,
  *   X in the packed weight's row order, Mp * Kp * 2 bytes (Mp = M rounded
  *   up to 16, Kp = K rounded up to 128).
@@ -151,15 +155,23 @@ int wq_prepack_q8(const int8_t* qweight, void* packed, int K, int N, void* strea
  * X [M, K] fp16; packed: from wq_prepack_q8; scales [K/G, N] fp32;
  * Y [M, N] fp16, written (fp32 accumulation, one round to nearest even).
  * Evaluated per group as scale * (sum of X * q), exact products, fp32 sums.
- * M < 32, or G not a multiple of 64: streaming passes over the packed weight
- * (one per 8 rows of X).  Otherwise one tiled matrix-core launch (32 x 128
- * output tiles) that reads the same packed weight.
+ * M <= 8, or G not a multiple of 64: streaming passes over the packed weight
+ * (one per 8 rows of X).  Otherwise a tiled matrix-core launch (32 x 128
+ * output tiles) reads the packed weight once; while those tiles alone do not
+ * fill the GPU (e.g. M <= 64 at N = 4096) K is split over 2..8 workgroups
+ * per tile, their fp32 partial tiles go to the workspace, and a second
+ * launch adds them in a fixed order and rounds once.
  * ("Quantization CUDA", tom-jerr.github.io, "Int8 Weight Only Quantization";
  * "融合反量化与GEMM：LLM推理的CUDA内核优化实践", zingnex.cn, "技术实现细节".)
+ * workspace: device, needed when G % 64 == 0 and wq_workspace_bytes(
+ *   WQ_OP_Q8G, M, K, N) > 0 (S * M * N * 4 bytes, S the number of K slices:
+ *   8 for 9 <= M <= 64 at K = N = 4096), else NULL allowed; 16-byte aligned;
+ *   needs no clearing.  WQ_ERR_WORKSPACE if missing or too small.  Calls
+ *   that overlap in time need separate workspaces.
  * Rules: M >= 1, K % 32 == 0, N % 16 == 0, G % 32 == 0, K % G == 0,
  * M * K * 2 < 2^31; Y 16-byte aligned as well. */
 int wq_gemm_q8_group(const void* X, const void* packed, const float* scales, void* Y, int M,
-                     int K, int N, int G, void* stream);
+                     int K, int N, int G, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------- 4-bit -- */
 

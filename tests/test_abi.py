@@ -67,14 +67,28 @@ def test_q3_validation(L):
 
 
 def test_q8_validation(L):
-    f = L.wq_gemm_q8_group
+    f = lambda *a: L.wq_gemm_q8_group(*a[:8], None, 0, a[8])        # no workspace
     assert f(P, None, P, P, 1, 4096, 4096, 128, None) == wq.WQ_ERR_NULL
     assert f(P, P, P, P, 0, 4096, 4096, 128, None) == wq.WQ_ERR_SHAPE    # M
     assert f(P, P, P, P, 1, 4096, 4104, 128, None) == wq.WQ_ERR_SHAPE    # N % 16
     assert f(P, P, P, P, 1, 4096, 4096, 96, None) == wq.WQ_ERR_SHAPE     # K % G
     assert f(P, P, P, P, 1, 4096, 4096, 48, None) == wq.WQ_ERR_SHAPE     # G % 32
     assert f(P, P_MIS, P, P, 1, 4096, 4096, 128, None) == wq.WQ_ERR_ALIGN
-    assert f(P, P, P, P_MIS, 64, 4096, 4096, 128, None) == wq.WQ_ERR_ALIGN    # Y: 8-byte stores
+    assert f(P, P, P, P_MIS, 8, 4096, 4096, 128, None) == wq.WQ_ERR_ALIGN    # Y: 8-byte stores
+    # above 8 rows the tiled path splits K: S slices of M x N fp32 partials
+    need = L.wq_workspace_bytes(wq.WQ_OP_Q8G, 16, 4096, 4096)
+    assert need == 8 * 16 * 4096 * 4
+    assert L.wq_workspace_bytes(wq.WQ_OP_Q8G, 8, 4096, 4096) == 0      # streaming passes
+    assert L.wq_workspace_bytes(wq.WQ_OP_Q8G, 64, 4096, 4096) == 8 * 64 * 4096 * 4
+    assert L.wq_workspace_bytes(wq.WQ_OP_Q8G, 256, 4096, 4096) == 2 * 256 * 4096 * 4
+    assert L.wq_workspace_bytes(wq.WQ_OP_Q8G, 512, 4096, 4096) == 0    # 512 tiles fill the GPU
+    assert L.wq_workspace_bytes(wq.WQ_OP_Q8G, 16, 4160, 4096) == 0     # K not whole slices
+    g8 = L.wq_gemm_q8_group
+    assert g8(P, P, P, P, 16, 4096, 4096, 128, None, need, None) == wq.WQ_ERR_WORKSPACE
+    assert g8(P, P, P, P, 16, 4096, 4096, 128, P, need - 16, None) == wq.WQ_ERR_WORKSPACE
+    assert g8(P, P, P, P, 16, 4096, 4096, 128, P_MIS, need, None) == wq.WQ_ERR_ALIGN
+    # groups of 32 run as streaming passes at any M: no workspace
+    assert f(P, P, P, P_MIS, 16, 4096, 4096, 32, None) == wq.WQ_ERR_ALIGN  # (reaches the Y check)
     assert L.wq_prepack_q8(P, P, 4096, 4100, None) == wq.WQ_ERR_SHAPE
     assert L.wq_prepack_q8(P_MIS, P, 4096, 4096, None) == wq.WQ_ERR_ALIGN
 

@@ -169,10 +169,18 @@ def test_q8_wide_panels_and_long_k(wq):
         assert_tol(host(Y), oracle.gemm_q8_group(d["X"], d["q"], d["scales"], 128), f"q8 {M}x{K}x{N}")
 
 
-# From 32 rows of X on (groups a multiple of 64 rows) the int8 product runs
-# on the matrix cores: 32 x 128 output tiles, K in stages of 128 rows.
+# From 9 rows of X on (groups a multiple of 64 rows) the int8 product runs
+# on the matrix cores: 32 x 128 output tiles, K in stages of 128 rows, and K
+# split over 2..8 workgroups while the tiles alone do not fill the GPU.
 @pytest.mark.parametrize("M,K,N,G", [
-    (32, 4096, 4096, 128),     # first row count on the tiled path
+    (9, 4096, 4096, 128),      # first row count on the tiled path: 8 K slices
+    (16, 4096, 11008, 128),    # 8 slices, wide N
+    (24, 4096, 4096, 64),      # groups of 64: two per stage
+    (31, 2048, 4096, 256),     # groups of two stages: slices of 256 rows
+    (32, 4096, 4096, 128),
+    (64, 4096, 4096, 128),     # two row tiles, 8 slices
+    (256, 4096, 4096, 128),    # 2 slices
+    (20, 4160, 4096, 64),      # K not whole slices: no split
     (100, 1088, 4112, 64),     # ragged row and column tiles, 17 stages
     (64, 64, 128, 64),         # a single stage
     (40, 11008, 4096, 128),    # a ragged last stage (K = 86 stages of 128)
@@ -186,10 +194,11 @@ def test_q8_gemm_tiles_vs_oracle(wq, M, K, N, G):
     assert_tol(host(Y), oracle.gemm_q8_group(d["X"], d["q"], d["scales"], G), f"q8 tiles {M}x{K}x{N} G{G}")
 
 
-def test_q8_gemm_integer_exact_and_deterministic(wq):
-    # Scales 1 and small integer X on the tiled path: every fp32 partial sum
-    # is an exact integer, so the result is bit-exact; repeated calls agree.
-    M, K, N, G = 80, 1024, 400, 128
+@pytest.mark.parametrize("M,K,N,G", [(80, 1024, 400, 128), (12, 2048, 1024, 128)])
+def test_q8_gemm_integer_exact_and_deterministic(wq, M, K, N, G):
+    # Scales 1 and small integer X on the tiled path (12 rows: K in 8
+    # slices): every fp32 partial sum is an exact integer, so the result is
+    # bit-exact; repeated calls agree.
     rng = np.random.default_rng(43)
     q = rng.integers(-127, 128, size=(K, N)).astype(np.int8)
     X = rng.integers(-2, 3, size=(M, K)).astype(np.float16)
@@ -200,6 +209,23 @@ def test_q8_gemm_integer_exact_and_deterministic(wq):
     assert np.array_equal(host(Y), ref)
     for _ in range(5):
         assert torch.equal(wq.gemm_q8_group(Xd, P, Sd, G), Y)
+
+
+def test_q8_split_k_workspace_contents_do_not_matter(wq):
+    # The K slices' partial tiles overwrite the workspace: garbage in it, or
+    # a larger one, changes nothing, and two calls in a row (the second
+    # smaller) agree with fresh ones.
+    d = synth.gen_q8_group(24, 4096, 4096, 128, seed=91)
+    X, P, Sd = cu(d["X"]), wq.prepack_q8(cu(d["q"])), cu(d["scales"])
+    need = wq.workspace_bytes(wq.WQ_OP_Q8G, 24, 4096, 4096)
+    assert need == 8 * 24 * 4096 * 4
+    ws = torch.full((need + 4096,), 0x7F, dtype=torch.uint8, device=dev())
+    Y0 = wq.gemm_q8_group(X, P, Sd, 128)
+    assert torch.equal(wq.gemm_q8_group(X, P, Sd, 128, ws=ws), Y0)
+    Y1 = wq.gemm_q8_group(X[:10], P, Sd, 128, ws=ws)
+    assert torch.equal(Y1, wq.gemm_q8_group(X[:10], P, Sd, 128))
+    assert_tol(host(Y0), oracle.gemm_q8_group(d["X"], d["q"], d["scales"], 128), "q8 split 24")
+    assert_tol(host(Y1), oracle.gemm_q8_group(d["X"][:10], d["q"], d["scales"], 128), "q8 split 10")
 
 
 def test_q8_gemm_rows_match_single_row_calls(wq):

@@ -41,7 +41,7 @@ _SIGNATURES = {
     "wq_prepack_q3": (_i, [_vp, _vp, _i, _i, _vp]),
     "wq_matvec_q3": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
     "wq_prepack_q8": (_i, [_vp, _vp, _i, _i, _vp]),
-    "wq_gemm_q8_group": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
+    "wq_gemm_q8_group": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]),
     "wq_q4_act_order_perm": (_i, [_vp, _i, _i, _vp, _vp]),
     "wq_prepack_q4": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
     "wq_gemm_q4_group": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]),
@@ -197,8 +197,12 @@ def prepack_q8(qweight):
     return out
 
 
-def gemm_q8_group(X, packed, scales, group_size=128, Y=None):
-    """Y = X . (scale[k // G] * q) from a packed int8 weight; X fp16 [M, K] or [K]."""
+def gemm_q8_group(X, packed, scales, group_size=128, Y=None, ws=None):
+    """Y = X . (scale[k // G] * q) from a packed int8 weight; X fp16 [M, K] or [K].
+
+    ``ws``: device workspace of ``workspace_bytes(WQ_OP_Q8G, M, K, N)`` bytes
+    (K split over workgroups above 8 rows), allocated here if None and needed.
+    """
     squeeze = X.dim() == 1
     X2 = X.reshape(1, -1) if squeeze else X
     M, K = X2.shape
@@ -210,8 +214,9 @@ def gemm_q8_group(X, packed, scales, group_size=128, Y=None):
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float16, device=dev)
     _need(Y, "Y", torch.float16, (M, N), dev)
+    ws, nws = _workspace_op(WQ_OP_Q8G, ws, M, K, N, dev)
     st = lib().wq_gemm_q8_group(_ptr(X2), _ptr(packed), _ptr(scales), _ptr(Y), M, K, N,
-                                group_size, _stream(dev))
+                                group_size, _ptr(ws) if ws is not None else None, nws, _stream(dev))
     _check("wq_gemm_q8_group", st)
     return Y.reshape(N) if squeeze else Y
 
@@ -281,7 +286,11 @@ def prepare_q4(qweight, g_idx, group_size=128):
 
 
 def _workspace_q4(ws, M, K, N, dev):
-    need = workspace_bytes(WQ_OP_Q4G, M, K, N)
+    return _workspace_op(WQ_OP_Q4G, ws, M, K, N, dev)
+
+
+def _workspace_op(op, ws, M, K, N, dev):
+    need = workspace_bytes(op, M, K, N)
     if ws is None:
         if need == 0:
             return None, 0

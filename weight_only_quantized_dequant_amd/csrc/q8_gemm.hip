@@ -70,22 +70,29 @@ __device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 15); }
 // 2 H + c, operand column t holds weight column w0 + 32 H + 2 t + c; the
 // transposed result then gives lane l, per half, the 8 consecutive columns
 // w0 + 32 H + 8 (l / 16) + 2 r + c (r = 0..3, c = 0, 1) of one row.
+// Split K (S > 1): workgroup b takes K slice b % S (S divides 8, so with
+// S = 8 every workgroup of an XCD reads the same slice of X) and writes its
+// fp32 partial tile, still in units of 2^-24, to ws [S][M][N]; a second
+// launch adds the slices in order and rounds once.  Slices are whole groups.
 __global__ __launch_bounds__(kThreadsG, 2) void q8_gemm_kernel(
     const _Float16* __restrict__ X, const uint8_t* __restrict__ Wp,
-    const float* __restrict__ scales, _Float16* __restrict__ Y, int M, int K, int N, int G, int KB,
-    int mtiles, int ntiles) {
+    const float* __restrict__ scales, _Float16* __restrict__ Y, float* __restrict__ ws, int M,
+    int K, int N, int G, int KB, int mtiles, int ntiles, int S) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStage];
 
   // Workgroups b and b + 8 run on the same XCD: the M tiles that share a
   // column tile of the weight are placed 8 apart.
-  const int bid = blockIdx.x;
+  const int slice = (int)blockIdx.x % S;
+  const int bid = (int)blockIdx.x / S;
   const int grp = bid / (8 * mtiles), rr = bid % (8 * mtiles);
   const int mt = rr / 8, nt = grp * 8 + (rr % 8);
   if (nt >= ntiles) return;
   const int m0 = mt * kBM, n0 = nt * kBN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nk = (K + kBK - 1) / kBK;
+  const int nkt = (K + kBK - 1) / kBK;   // stages of all of K
+  const int kt0 = slice * nkt / S;       // this slice's stages [kt0, kt0 + nk)
+  const int nk = (slice + 1) * nkt / S - kt0;
 
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, M * K * 2);
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wp, K * N);
@@ -116,7 +123,8 @@ __global__ __launch_bounds__(kThreadsG, 2) void q8_gemm_kernel(
   const int s_col = n0 + 4 * (lane & 31);
   const bool s_live = s_col < N;
 
-  auto issue = [&](int kt, int slot) {
+  auto issue = [&](int ktl, int slot) {
+    const int kt = kt0 + ktl;
     const int k0 = kt * kBK;
     lds_u8* base = (lds_u8*)smem + slot * kStage;
 #pragma unroll
@@ -257,7 +265,7 @@ __global__ __launch_bounds__(kThreadsG, 2) void q8_gemm_kernel(
 
   issue(0, 0);
   if (nk > 1) issue(1, 1);
-  int gpos = 0;
+  int gpos = (kt0 * kBK) % G;  // 0: slices are whole groups
   for (int kt = 0; kt < nk; ++kt) {
     // Stage kt has landed for this wave (stage kt + 1 may be in flight).
     if (kt + 1 < nk) {
@@ -286,6 +294,15 @@ __global__ __launch_bounds__(kThreadsG, 2) void q8_gemm_kernel(
     for (int H = 0; H < 2; ++H) {
       const int n = n0 + wn * 64 + 32 * H + 8 * fq;
       if (n >= N) continue;
+      if (S > 1) {
+        // Columns n + 2 r + c of tot[2 H + c][r]: 8 consecutive fp32.
+        float* o = ws + ((size_t)slice * M + m) * N + n;
+        const f32x4 lo = {tot[i][2 * H][0], tot[i][2 * H + 1][0], tot[i][2 * H][1], tot[i][2 * H + 1][1]};
+        const f32x4 hi = {tot[i][2 * H][2], tot[i][2 * H + 1][2], tot[i][2 * H][3], tot[i][2 * H + 1][3]};
+        *reinterpret_cast<f32x4*>(o) = lo;
+        *reinterpret_cast<f32x4*>(o + 4) = hi;
+        continue;
+      }
       uint32_t w[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -297,6 +314,20 @@ __global__ __launch_bounds__(kThreadsG, 2) void q8_gemm_kernel(
   }
 }
 
+// Y = fp16(2^24 * sum over the S slices, in slice order), 4 columns per thread.
+__global__ __launch_bounds__(256) void q8_splitk_reduce_kernel(const float* __restrict__ ws,
+                                                               _Float16* __restrict__ Y, int M,
+                                                               int N, int S) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  const size_t total = (size_t)M * N;
+  if (i >= total) return;
+  f32x4 a = *reinterpret_cast<const f32x4*>(ws + i);
+  for (int sl = 1; sl < S; ++sl) a += *reinterpret_cast<const f32x4*>(ws + (size_t)sl * total + i);
+  const h2 lo = {(_Float16)(a[0] * kTwo24), (_Float16)(a[1] * kTwo24)};
+  const h2 hi = {(_Float16)(a[2] * kTwo24), (_Float16)(a[3] * kTwo24)};
+  *reinterpret_cast<uint2*>(Y + i) = make_uint2(as_u32(lo), as_u32(hi));
+}
+
 bool q8_gemm_supported(int M, int K, int N, int G) {
   (void)M;
   (void)N;
@@ -304,13 +335,36 @@ bool q8_gemm_supported(int M, int K, int N, int G) {
   return G % 64 == 0;
 }
 
-hipError_t launch_q8_gemm(const void* X, const void* packed, const float* scales, void* Y, int M,
-                          int K, int N, int G, hipStream_t s) {
+// K slices: enough workgroups to fill the GPU twice over (two fit on a CU),
+// at most 8, each slice whole 128-row stages and whole groups.  The size of
+// the workspace takes the largest S any group size allows (G <= 128).
+static int q8_gemm_slices(int M, int K, int N, int G) {
   const int mtiles = (M + kBM - 1) / kBM, ntiles = (N + kBN - 1) / kBN;
-  const int grid = (ntiles + 7) / 8 * 8 * mtiles;
+  const int tiles = (ntiles + 7) / 8 * 8 * mtiles;
+  const int unit = G > kBK ? G : kBK;  // rows per slice: a multiple of this
+  int S = 1;
+  while (S < 8 && tiles * 2 * S <= 2 * kTargetCUs && K % (unit * 2 * S) == 0) S *= 2;
+  return S;
+}
+size_t q8_gemm_workspace_bytes(int M, int K, int N) {
+  const int S = q8_gemm_slices(M, K, N, 64);
+  return S > 1 ? (size_t)S * M * N * 4 : 0;
+}
+
+hipError_t launch_q8_gemm(const void* X, const void* packed, const float* scales, void* Y,
+                          void* ws, int M, int K, int N, int G, hipStream_t s) {
+  const int mtiles = (M + kBM - 1) / kBM, ntiles = (N + kBN - 1) / kBN;
+  const int S = ws ? q8_gemm_slices(M, K, N, G) : 1;
+  const int grid = (ntiles + 7) / 8 * 8 * mtiles * S;
   hipLaunchKernelGGL(q8_gemm_kernel, dim3(grid), dim3(kThreadsG), 0, s,
                      reinterpret_cast<const _Float16*>(X), reinterpret_cast<const uint8_t*>(packed),
-                     scales, reinterpret_cast<_Float16*>(Y), M, K, N, G, K / 8, mtiles, ntiles);
+                     scales, reinterpret_cast<_Float16*>(Y), reinterpret_cast<float*>(ws), M, K, N,
+                     G, K / 8, mtiles, ntiles, S);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  const size_t quads = ((size_t)M * N) / 4;
+  hipLaunchKernelGGL(q8_splitk_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<const float*>(ws), reinterpret_cast<_Float16*>(Y), M, N, S);
   return hipGetLastError();
 }
 

@@ -36,7 +36,7 @@ constexpr int kQ8Steps = 8;                    // pieces per lane per chunk
 constexpr int kQ8Chunk = 64 * kQ8Steps * 8;    // rows of K per chunk: 4096
 // From this many rows of X on, the product runs as a tiled matrix-core GEMM
 // (q8_gemm.hip) instead of one streaming pass over the weight per 8 rows.
-constexpr int kQ8GemmMinRows = 32;
+constexpr int kQ8GemmMinRows = 9;
 
 // Panel plan: 16-column panels (8 column pairs); u = pieces per pair.
 PanelPlan plan_q8(int K, int N) {
@@ -290,10 +290,14 @@ static hipError_t launch_q8_t(const void* X, const void* packed, const float* sc
   return hipGetLastError();
 }
 
-hipError_t launch_q8_group(const void* X, const void* packed, const float* scales, void* Y, int M,
-                           int K, int N, int G, hipStream_t s) {
+size_t q8_group_workspace_bytes(int M, int K, int N) {
+  return M >= kQ8GemmMinRows ? q8_gemm_workspace_bytes(M, K, N) : 0;
+}
+
+hipError_t launch_q8_group(const void* X, const void* packed, const float* scales, void* Y,
+                           void* ws, int M, int K, int N, int G, hipStream_t s) {
   if (M >= kQ8GemmMinRows && q8_gemm_supported(M, K, N, G))
-    return launch_q8_gemm(X, packed, scales, Y, M, K, N, G, s);
+    return launch_q8_gemm(X, packed, scales, Y, ws, M, K, N, G, s);
   // Rows of X beyond 8 run as further launches over the same weight.
   for (int m0 = 0; m0 < M; m0 += 8) {
     const int mc = (M - m0) < 8 ? (M - m0) : 8;

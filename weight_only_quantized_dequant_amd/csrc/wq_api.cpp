@@ -122,7 +122,7 @@ int wq_prepack_q8(const int8_t* qweight, void* packed, int K, int N, void* strea
 }
 
 int wq_gemm_q8_group(const void* X, const void* packed, const float* scales, void* Y, int M,
-                     int K, int N, int G, void* stream) {
+                     int K, int N, int G, void* workspace, size_t workspace_bytes, void* stream) {
   if (!X || !packed || !scales || !Y) return WQ_ERR_NULL;
   if (int st = check_q8(K, N)) return st;
   if (M < 1 || G < 32 || G % 32 || K % G) return WQ_ERR_SHAPE;
@@ -130,7 +130,14 @@ int wq_gemm_q8_group(const void* X, const void* packed, const float* scales, voi
     return WQ_ERR_SHAPE;
   if (!aligned16(X) || !aligned16(packed) || !aligned16(scales) || !aligned16(Y))
     return WQ_ERR_ALIGN;
-  return hip_status(wq::launch_q8_group(X, packed, scales, Y, M, K, N, G, as_stream(stream)));
+  // The tiled path (groups of 64 rows or more) splits K through the
+  // workspace when its tiles alone do not fill the GPU.
+  const size_t need = G % 64 == 0 ? wq::q8_group_workspace_bytes(M, K, N) : 0;
+  if (need > (size_t)kMaxBytes) return WQ_ERR_SHAPE;
+  if (need && (!workspace || workspace_bytes < need)) return WQ_ERR_WORKSPACE;
+  if (need && !aligned16(workspace)) return WQ_ERR_ALIGN;
+  return hip_status(wq::launch_q8_group(X, packed, scales, Y, need ? workspace : nullptr, M, K, N,
+                                        G, as_stream(stream)));
 }
 
 int wq_unpack_q8(const void* packed, int8_t* codes, int K, int N, void* stream) {
@@ -277,6 +284,10 @@ int check_ws(int M, int K, int N, const void* ws, size_t ws_bytes) {
 }  // namespace
 
 size_t wq_workspace_bytes(int op, int M, int K, int N) {
+  if (op == WQ_OP_Q8G) {
+    if (M < 1 || check_q8(K, N)) return 0;
+    return wq::q8_group_workspace_bytes(M, K, N);
+  }
   if (op == WQ_OP_Q4G) {
     if (M < 1 || K < 32 || K % 32 || K > 32768 || N < 4 || N % 4) return 0;
     return wq::q4_tiled_workspace_bytes(M, K);

@@ -38,13 +38,18 @@ PanelPlan plan_q2(int K, int N, int G);
 PanelPlan plan_q3(int K, int N);
 
 hipError_t launch_q8_prepack(const int8_t* W, void* packed, int K, int N, hipStream_t s);
-hipError_t launch_q8_group(const void* X, const void* packed, const float* scales, void* Y, int M,
-                           int K, int N, int G, hipStream_t s);
+// ws: q8_group_workspace_bytes(M, K, N) bytes (unused when that is 0).
+hipError_t launch_q8_group(const void* X, const void* packed, const float* scales, void* Y,
+                           void* ws, int M, int K, int N, int G, hipStream_t s);
+size_t q8_group_workspace_bytes(int M, int K, int N);
 hipError_t launch_q8_unpack(const void* packed, int8_t* codes, int K, int N, hipStream_t s);
-// Matrix-core path of the same product for many rows of X (q8_gemm.hip).
+// Matrix-core path of the same product for more rows of X (q8_gemm.hip);
+// with a workspace it splits K over workgroups (fp32 partial tiles in ws,
+// summed in a fixed order by a second launch).
 bool q8_gemm_supported(int M, int K, int N, int G);
-hipError_t launch_q8_gemm(const void* X, const void* packed, const float* scales, void* Y, int M,
-                          int K, int N, int G, hipStream_t s);
+size_t q8_gemm_workspace_bytes(int M, int K, int N);
+hipError_t launch_q8_gemm(const void* X, const void* packed, const float* scales, void* Y,
+                          void* ws, int M, int K, int N, int G, hipStream_t s);
 
 hipError_t launch_q3_prepack(const int32_t* qw, void* packed, int K, int N, hipStream_t s);
 hipError_t launch_q3(const void* x, const void* packed, const void* scales, const void* zeros,
