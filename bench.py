@@ -52,6 +52,7 @@ import numpy as np  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0     # dense int8 MFMA, POP/s x 1e-12
 FP16_PEAK_TFLOPS = 2500.0   # dense fp16 MFMA
+FP32_PEAK_TFLOPS = 157.3    # dense fp32 MFMA
 MALL_BYTES = 256 << 20
 
 
@@ -245,6 +246,39 @@ def wl_q2(wq, torch, dev, M, G=128):
 
     w = Workload(f"q2_zp_asymmetric M={M} K={K} N={N} G={G}", nbytes, make, run)
     w.oracle = lambda: __import__("oracle").gemm_q2_zp(d["X"], d["qweight"], d["scales"], d["zeros"], None, G)
+    return w
+
+
+def wl_q8_separated(wq, torch, dev, M=512, dt="f16"):
+    """The unfused comparator of the fused int8 product at the fused-kernel
+    page's workload: the dequantisation kernel writes the whole fp16 (or fp32)
+    weight, then a library GEMM (torch.matmul) reads it."""
+    import synth
+    K, N, G = 4096, 4096, 128
+    b = 2 if dt == "f16" else 4
+    # dequant: read codes + scales, write W; GEMM: read X and W, write Y
+    nbytes = (K * N + (K // G) * N * 4 + K * N * b) + (M * K * b + K * N * b + M * N * b)
+    d = synth.gen_q8_group(M, K, N, G, seed=synth.SEEDS["q8_group_m512"])
+    tdt = torch.float16 if dt == "f16" else torch.float32
+
+    def make(R):
+        X = torch.from_numpy(d["X"]).to(dev).to(tdt)
+        base = [X, torch.from_numpy(d["q"]).to(dev), torch.from_numpy(d["scales"]).to(dev)]
+        W = torch.empty((K, N), dtype=tdt, device=dev)   # the intermediate every call rewrites
+        return [[t.clone() for t in base] + [W, torch.empty((M, N), dtype=tdt, device=dev)]
+                for _ in range(R)]
+
+    def run(c):
+        wq.dequant_q8_group(c[1], c[2], G, tdt, W=c[3])
+        torch.matmul(c[0], c[3], out=c[4])
+
+    w = Workload(f"q8_group_separated_{dt} M={M} K={K} N={N} G={G}", nbytes, make, run,
+                 flops=2 * M * K * N)
+    w.peak_tops = FP16_PEAK_TFLOPS if dt == "f16" else FP32_PEAK_TFLOPS
+    w.config = {"workload": w.name, "M": M, "K": K, "N": N, "group": G,
+                "form": f"dequant kernel writes {dt} W, then torch.matmul"}
+    w.oracle = lambda: __import__("oracle").gemm_q8_group(d["X"], d["q"], d["scales"], G)
+    w.dtype = f"{dt} weight x {dt} act, library GEMM"
     return w
 
 
@@ -494,6 +528,9 @@ def _make_workload(name, wq, torch, dev):
         return wl_q4zp(wq, torch, dev, int(name[len("q4zp_m"):]))
     if name.startswith("q2_m"):
         return wl_q2(wq, torch, dev, int(name[len("q2_m"):]))
+    if name.startswith("q8_sep_"):        # q8_sep_f16_m512, q8_sep_f32_m512
+        dt, m = name[len("q8_sep_"):].split("_m")
+        return wl_q8_separated(wq, torch, dev, int(m), dt)
     if name == "w8a8":
         return wl_w8a8(wq, torch, dev)
     if name == "w8a8_smooth":
@@ -506,7 +543,8 @@ def _make_workload(name, wq, torch, dev):
 SECONDARY = ("q3_f32_1024", "q3_f16_4096x4096", "q3_f16_4096x11008", "q3_f16_11008x4096",
              "q4_m1", "q4_m2", "q4_m4", "q4_m8", "q4_m16", "q4_m32", "q4_m64", "q4zp_m1",
              "q4zp_act_m64", "q4zp_g64_m1", "q2_m1", "q2_m8",
-             "q8_m2", "q8_m8", "q8_m16", "q8_m32", "q8_m512", "w8a8", "w8a8_smooth", "int8_mixed")
+             "q8_m2", "q8_m8", "q8_m16", "q8_m32", "q8_m512", "q8_sep_f16_m512", "q8_sep_f32_m512",
+             "w8a8", "w8a8_smooth", "int8_mixed")
 
 
 def main():

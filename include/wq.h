@@ -173,6 +173,21 @@ int wq_prepack_q8(const int8_t* qweight, void* packed, int K, int N, void* strea
 int wq_gemm_q8_group(const void* X, const void* packed, const float* scales, void* Y, int M,
                      int K, int N, int G, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The separated (unfused) form's first step, for comparison with the fused
+ * product ("融合反量化与GEMM：LLM推理的CUDA内核优化实践", zingnex.cn, section
+ * "CUDA内核架构": a standalone INT8 -> FP32 dequantisation kernel that
+ * writes the whole weight, followed by a general GEMM; section "性能对比数据",
+ * the "CUDA分离" row): materialise
+ *   W[k, n] = scale[k / G, n] * q[k, n]
+ * as one fp32 multiply per weight; with dtype WQ_F16 that fp32 product is
+ * rounded once more, to nearest even.  qweight [K, N] int8 (the stored
+ * codes, not the packed copy), scales [K/G, N] fp32, W [K, N] fp32 or fp16,
+ * written.  A GEMM of the caller's choice then multiplies X by W.
+ * Rules: K % 32 == 0, N % 16 == 0, G % 32 == 0, K % G == 0,
+ * K * N * sizeof(W) < 2^31; all arrays 16-byte aligned. */
+int wq_dequant_q8_group(const int8_t* qweight, const float* scales, void* W, int K, int N, int G,
+                        int dtype, void* stream);
+
 /* ---------------------------------------------------------------- 4-bit -- */
 
 /* Act-order preparation (HOST arrays, runs on the CPU): from g_idx[K] (row k

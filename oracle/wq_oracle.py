@@ -86,6 +86,7 @@ import numpy as np
 
 __all__ = [
     "bits_le", "unpack_q3", "unpack_u4", "unpack_q4", "dequant_q3", "dequant_q8_group",
+    "materialize_q8_group",
     "dequant_q4_group", "dequant_q4_zp", "matvec_q3", "gemm_q8_group", "gemm_q4_group",
     "gemm_q4_zp", "unpack_u2", "gemm_q2_zp",
     "quantize_rows_int8", "w8a8_accumulate", "w8a8_epilogue",
@@ -171,6 +172,23 @@ def dequant_q8_group(q: np.ndarray, scales: np.ndarray, G: int) -> np.ndarray:
     K = q.shape[0]
     g = np.arange(K) // G
     return np.asarray(scales).astype(np.float64)[g, :] * q.astype(np.float64)
+
+
+def materialize_q8_group(q: np.ndarray, scales: np.ndarray, G: int, out: str = "f32") -> np.ndarray:
+    """The dense weight the separated (unfused) form writes before its GEMM.
+
+    "融合反量化与GEMM：LLM推理的CUDA内核优化实践" (zingnex.cn), "CUDA内核架构":
+    a standalone kernel dequantises the int8 weight to FP32 and writes all of
+    it.  Here: the exact product ``scale * q`` (fp64: 24 + 8 bits, exact),
+    rounded once to fp32; ``out="f16"`` rounds that fp32 weight once more to
+    fp16 (both to nearest even), the fp16 weight a half-precision GEMM reads.
+    """
+    W32 = dequant_q8_group(q, scales, G).astype(np.float32)
+    if out == "f32":
+        return W32
+    if out == "f16":
+        return W32.astype(np.float16)
+    raise ValueError(out)
 
 
 def dequant_q4_group(q: np.ndarray, scales: np.ndarray, g_idx: np.ndarray | None,

@@ -66,6 +66,16 @@ def test_q3_validation(L):
     assert L.wq_prepack_q3(P, P, 64, 66, None) == wq.WQ_ERR_SHAPE
 
 
+def test_dequant_q8_validation(L):
+    f = L.wq_dequant_q8_group
+    assert f(None, P, P, 4096, 4096, 128, wq.WQ_F32, None) == wq.WQ_ERR_NULL
+    assert f(P, P, P, 4096, 4104, 128, wq.WQ_F32, None) == wq.WQ_ERR_SHAPE    # N % 16
+    assert f(P, P, P, 4096, 4096, 96, wq.WQ_F16, None) == wq.WQ_ERR_SHAPE     # K % G
+    assert f(P, P, P, 4096, 4096, 128, 7, None) == wq.WQ_ERR_SHAPE            # dtype
+    assert f(P, P, P, 32768, 32768, 128, wq.WQ_F32, None) == wq.WQ_ERR_SHAPE  # W >= 2^31 bytes
+    assert f(P, P, P_MIS, 4096, 4096, 128, wq.WQ_F16, None) == wq.WQ_ERR_ALIGN
+
+
 def test_q8_validation(L):
     f = lambda *a: L.wq_gemm_q8_group(*a[:8], None, 0, a[8])        # no workspace
     assert f(P, None, P, P, 1, 4096, 4096, 128, None) == wq.WQ_ERR_NULL

@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 import synth
+from conftest import read_golden
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -253,6 +254,52 @@ def test_q8_gemm_full_size_sampled_rows(wq):
     ref = oracle.gemm_q8_group(d["X"][rows], d["q"], d["scales"], G)
     assert_tol(Y[rows], ref, "q8 512x4096x4096 sampled rows")
     assert np.all(np.isfinite(Y))
+
+
+# ============================================ separated form (comparator) ==
+
+@pytest.mark.parametrize("K,N,G", [(4096, 4096, 128), (1024, 4112, 64), (96, 48, 32), (11008, 4096, 128)])
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_dequant_q8_bit_exact(wq, K, N, G, dt):
+    # The materialised weight: one fp32 multiply per weight (then one fp16
+    # rounding): bit for bit the oracle's.
+    d = synth.gen_q8_group(1, K, N, G, seed=41 + K + N)
+    W = wq.dequant_q8_group(cu(d["q"]), cu(d["scales"]), G,
+                            torch.float32 if dt == "f32" else torch.float16)
+    ref = oracle.materialize_q8_group(d["q"], d["scales"], G, dt)
+    got = W.cpu().numpy()
+    bits = np.uint32 if dt == "f32" else np.uint16
+    assert np.array_equal(got.view(bits), ref.view(bits))
+
+
+def test_dequant_q8_worked_example(wq):
+    # tests/golden/q8_materialize_worked.txt on the GPU: fp32 product rounded
+    # down to an fp16 tie, then to even (16 columns: one row of the kernel).
+    for name, sc, q, b32, b16 in read_golden("q8_materialize_worked.txt"):
+        qq = np.full((32, 16), int(q), np.int8)
+        s = np.full((1, 16), np.float32(int(sc) * 2.0 ** -26), np.float32)
+        w32 = wq.dequant_q8_group(cu(qq), cu(s), 32, torch.float32).cpu().numpy()
+        w16 = wq.dequant_q8_group(cu(qq), cu(s), 32, torch.float16).cpu().numpy()
+        assert np.all(w32.view(np.uint32) == int(b32, 16)), name
+        assert np.all(w16.view(np.uint16) == int(b16, 16)), name
+
+
+def test_separated_form_vs_oracle(wq):
+    # The unfused comparator at the fused-kernel page's workload (M = 512,
+    # K = N = 4096, group 128): dequantise to fp16, then a library GEMM
+    # (fp32 accumulation); the oracle on a sample of rows.  The fp16 weight
+    # adds one rounding per weight (relative 2^-11), within the bar.
+    M, K, N, G = 512, 4096, 4096, 128
+    d = synth.gen_q8_group(M, K, N, G, seed=1500)
+    W16 = wq.dequant_q8_group(cu(d["q"]), cu(d["scales"]), G, torch.float16)
+    Y = torch.matmul(cu(d["X"]), W16)
+    rows = [0, 1, 255, 256, 511]
+    assert_tol(host(Y)[rows], oracle.gemm_q8_group(d["X"][rows], d["q"], d["scales"], G),
+               "separated fp16 512x4096x4096")
+    W32 = wq.dequant_q8_group(cu(d["q"]), cu(d["scales"]), G, torch.float32)
+    Y32 = torch.matmul(cu(d["X"]).float(), W32)
+    assert_tol(host(Y32)[rows], oracle.gemm_q8_group(d["X"][rows], d["q"], d["scales"], G),
+               "separated fp32 512x4096x4096")
 
 
 # ================================================================= 3-bit ==

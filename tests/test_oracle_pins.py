@@ -602,3 +602,54 @@ def test_mixed_reduces_error_with_outlier_channels():
     e_plain = np.linalg.norm(plain - ref) / np.linalg.norm(ref)
     e_mixed = np.linalg.norm(mixed["y_exact"] - ref) / np.linalg.norm(ref)
     assert e_mixed < 0.5 * e_plain, (e_plain, e_mixed)
+
+
+# ---------------------------------------------- separated form's weight --
+
+def test_materialize_q8_worked_example():
+    # tests/golden/q8_materialize_worked.txt: a product that rounds to an fp16
+    # tie only after the fp32 rounding (two-step rounding pinned by hand).
+    for name, sc, q, b32, b16 in read_golden("q8_materialize_worked.txt"):
+        scale = np.array([[np.float32(int(sc) * 2.0 ** -26)]], np.float32)
+        assert float(scale[0, 0]) == int(sc) * 2.0 ** -26   # the scale is an fp32 number
+        qq = np.array([[int(q)]], np.int8)
+        w32 = oracle.materialize_q8_group(qq, scale, 1, "f32")
+        w16 = oracle.materialize_q8_group(qq, scale, 1, "f16")
+        assert w32.dtype == np.float32 and w16.dtype == np.float16
+        assert int(w32.view(np.uint32)[0, 0]) == int(b32, 16), name
+        assert int(w16.view(np.uint16)[0, 0]) == int(b16, 16), name
+
+
+def test_materialize_q8_exact_with_power_of_two_scales_and_groups():
+    # Power-of-two scales: every product is exact in fp32 (and in fp16 for
+    # |q| <= 127 at these exponents), and row k takes the scale of group
+    # k // G: rows 0..31 of group 0 (scale 2^-7), rows 32..63 of group 1
+    # (scale 2^-3).
+    rng = np.random.default_rng(5)
+    K, N, G = 64, 16, 32
+    q = rng.integers(-127, 128, size=(K, N)).astype(np.int8)
+    s = np.empty((2, N), np.float32)
+    s[0], s[1] = 2.0 ** -7, 2.0 ** -3
+    w32 = oracle.materialize_q8_group(q, s, G, "f32").astype(np.float64)
+    w16 = oracle.materialize_q8_group(q, s, G, "f16").astype(np.float64)
+    exact = np.vstack([q[:32].astype(np.float64) / 128.0, q[32:].astype(np.float64) / 8.0])
+    assert np.array_equal(w32, exact)
+    assert np.array_equal(w16, exact)
+
+
+def test_materialize_q8_within_one_rounding_of_exact():
+    # Arbitrary fp32 scales: the fp32 weight is within half an fp32 ulp of
+    # the exact product, the fp16 weight within half an fp16 ulp plus half an
+    # fp32 ulp; a naive product with the fp32 weight stays within the
+    # weight's relative error of the exact GEMM.
+    d = synth.gen_q8_group(3, 256, 64, 128, seed=17)
+    q, s = d["q"], d["scales"]
+    ex = q.astype(np.float64) * np.repeat(s.astype(np.float64), 128, axis=0)
+    w32 = oracle.materialize_q8_group(q, s, 128, "f32").astype(np.float64)
+    w16 = oracle.materialize_q8_group(q, s, 128, "f16").astype(np.float64)
+    assert np.all(np.abs(w32 - ex) <= 2.0 ** -24 * np.abs(ex))
+    assert np.all(np.abs(w16 - ex) <= (2.0 ** -11 + 2.0 ** -24) * np.abs(ex) + 2.0 ** -25)
+    X = d["X"].astype(np.float64)
+    y = X @ w32
+    y_ex = oracle.gemm_q8_group(d["X"], q, s, 128)
+    assert np.all(np.abs(y - y_ex) <= 2.0 ** -24 * (np.abs(X) @ np.abs(ex)) * 1.0001)

@@ -42,6 +42,7 @@ _SIGNATURES = {
     "wq_matvec_q3": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
     "wq_prepack_q8": (_i, [_vp, _vp, _i, _i, _vp]),
     "wq_gemm_q8_group": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "wq_dequant_q8_group": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "wq_q4_act_order_perm": (_i, [_vp, _i, _i, _vp, _vp]),
     "wq_prepack_q4": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
     "wq_gemm_q4_group": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]),
@@ -219,6 +220,24 @@ def gemm_q8_group(X, packed, scales, group_size=128, Y=None, ws=None):
                                 group_size, _ptr(ws) if ws is not None else None, nws, _stream(dev))
     _check("wq_gemm_q8_group", st)
     return Y.reshape(N) if squeeze else Y
+
+
+def dequant_q8_group(qweight, scales, group_size=128, dtype=torch.float32, W=None):
+    """The separated form's dequantisation: ``W = scale[k // G] * q`` as a dense
+    fp32 (or fp16) [K, N] weight, from the stored int8 codes [K, N]."""
+    K, N = qweight.shape
+    dev = qweight.device
+    _need(qweight, "qweight", torch.int8, (K, N), dev)
+    _need(scales, "scales", torch.float32, (K // group_size, N), dev)
+    if dtype not in (torch.float32, torch.float16):
+        raise ValueError("dtype must be torch.float32 or torch.float16")
+    if W is None:
+        W = torch.empty((K, N), dtype=dtype, device=dev)
+    _need(W, "W", dtype, (K, N), dev)
+    st = lib().wq_dequant_q8_group(_ptr(qweight), _ptr(scales), _ptr(W), K, N, group_size,
+                                   WQ_F32 if dtype == torch.float32 else WQ_F16, _stream(dev))
+    _check("wq_dequant_q8_group", st)
+    return W
 
 
 def unpack_q8(packed, K: int, N: int):

@@ -140,6 +140,17 @@ int wq_gemm_q8_group(const void* X, const void* packed, const float* scales, voi
                                         G, as_stream(stream)));
 }
 
+int wq_dequant_q8_group(const int8_t* qweight, const float* scales, void* W, int K, int N, int G,
+                        int dtype, void* stream) {
+  if (!qweight || !scales || !W) return WQ_ERR_NULL;
+  if (int st = check_q8(K, N)) return st;
+  if (G < 32 || G % 32 || K % G || (dtype != WQ_F32 && dtype != WQ_F16)) return WQ_ERR_SHAPE;
+  if ((long long)K * N * (dtype == WQ_F32 ? 4 : 2) > kMaxBytes) return WQ_ERR_SHAPE;
+  if (!aligned16(qweight) || !aligned16(scales) || !aligned16(W)) return WQ_ERR_ALIGN;
+  return hip_status(wq::launch_q8_dequant(qweight, scales, W, K, N, G, dtype == WQ_F16,
+                                          as_stream(stream)));
+}
+
 int wq_unpack_q8(const void* packed, int8_t* codes, int K, int N, void* stream) {
   if (!packed || !codes) return WQ_ERR_NULL;
   if (int st = check_q8(K, N)) return st;

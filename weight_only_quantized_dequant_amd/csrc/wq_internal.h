@@ -51,6 +51,10 @@ size_t q8_gemm_workspace_bytes(int M, int K, int N);
 hipError_t launch_q8_gemm(const void* X, const void* packed, const float* scales, void* Y,
                           void* ws, int M, int K, int N, int G, hipStream_t s);
 
+// The separated form's dequantisation: W [K, N] = scale * q, fp32 or fp16.
+hipError_t launch_q8_dequant(const int8_t* q, const float* scales, void* W, int K, int N, int G,
+                             bool f16, hipStream_t s);
+
 hipError_t launch_q3_prepack(const int32_t* qw, void* packed, int K, int N, hipStream_t s);
 hipError_t launch_q3(const void* x, const void* packed, const void* scales, const void* zeros,
                      void* y, int K, int N, bool f16, hipStream_t s);
