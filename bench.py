@@ -433,6 +433,29 @@ def calibration(wq, torch, w, steps, warmup, gemv_ms):
             "share_of_stream_ceiling": round(s_ms / gemv_ms, 4), "rotation_copies": R}
 
 
+def stream_sweep(wq, torch, dev, steps, warmup):
+    """The per-launch streaming ceiling: a kernel that only reads `size` bytes
+    with the int8 GEMV's loads (wq_calib_stream_read), at 4..256 MiB, timed
+    like every workload (rotated copies, queued launches, median of trials);
+    and the empty kernel with the GEMV's grid (the dispatch floor)."""
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    ew = Workload("empty kernel", 0, lambda R: [[None]] * R, lambda c: wq.calib_empty(sink, 256, 512))
+    e_ms, _, _ = time_workload(torch, ew, steps, warmup, R=1)
+    print(json.dumps({"kernel": "calib_empty", "grid": 256, "threads": 512,
+                      "us": round(e_ms * 1e3, 3)}), flush=True)
+    for mib in (4, 8, 16, 32, 64, 128, 256):
+        nbytes = mib << 20
+        sw = Workload(f"stream {mib} MiB", nbytes,
+                      lambda R, n=nbytes: [[torch.empty(n // 4, dtype=torch.int32, device=dev).fill_(1)]
+                                           for _ in range(R)],
+                      lambda c: wq.calib_stream_read(c[0], sink))
+        ms, R, _ = time_workload(torch, sw, steps, warmup)
+        print(json.dumps({"kernel": "calib_stream_read", "MiB": mib, "bytes": nbytes, "rotation_copies": R,
+                          "us": round(ms * 1e3, 3), "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                          "pct_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}),
+              flush=True)
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -563,6 +586,9 @@ def main():
                     help="q8 (headline) | q8_m* | q3_* | q4_m* | q4zp_m* | q4zp_g64_m* | q2_m* | w8a8 | w8a8_smooth | int8_mixed (single line)")
     ap.add_argument("--graph", action="store_true",
                     help="replay a captured graph of the timed steps instead of issuing them one by one")
+    ap.add_argument("--stream-sweep", action="store_true",
+                    help="only time the bare weight stream (wq_calib_stream_read) at 4..256 MiB and "
+                         "the empty kernel, one JSON line each")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (counter calibration)")
     ap.add_argument("--cpu-leg", default=None, help=argparse.SUPPRESS)
@@ -577,7 +603,8 @@ def main():
 
     # The CPU oracle legs run first, in child processes, before this process
     # touches the GPU.
-    cpu = None if args.no_cpu_baseline or args.calibrate_copy else cpu_baseline(args.workload)
+    cpu = (None if args.no_cpu_baseline or args.calibrate_copy or args.stream_sweep
+           else cpu_baseline(args.workload))
 
     import torch
     dev = torch.device("cuda:0")
@@ -593,6 +620,9 @@ def main():
         return
     import weight_only_quantized_dequant_amd as wq
     wq.lib()
+    if args.stream_sweep:
+        stream_sweep(wq, torch, dev, args.steps, args.warmup)
+        return
 
     def make(name):
         return _make_workload(name, wq, torch, dev)
