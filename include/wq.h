@@ -43,7 +43,7 @@
  *   frees memory, never synchronises a stream, and never changes the current
  *   device; work runs on the device that owns the buffers, on `stream`
  *   (a hipStream_t; NULL means the default stream), asynchronously.  The
- *   4-bit products above 8 rows of X and the W8A8 family take a workspace,
+ *   int8 and 4-bit products above 8 and 4 rows of X and the W8A8 family take a workspace,
  *   sized by wq_workspace_bytes(), in which a call leaves nothing that a
  *   later call depends on (it needs no clearing); the other products need
  *   none (no partial result leaves a workgroup).  Calls that overlap in time
@@ -109,7 +109,7 @@ size_t wq_packed_bytes(int op, int K, int N, int G);
  *   output tiles alone do not fill the GPU, the fp32 partial tiles of S K
  *   slices, S * M * N * 4 bytes (S = 8 for M <= 64 at K = N = 4096; the
  *   size holds for every group size the tiled path takes).
- * - WQ_OP_Q4G (wq_gemm_q4_group, wq_gemm_q4_group_zp): above 8 rows of X,
+ * - WQ_OP_Q4G (wq_gemm_q4_group, wq_gemm_q4_group_zp): above 4 rows of X,
  *   X in the packed weight's row order, Mp * Kp * 2 bytes (Mp = M rounded
  *   up to 16, Kp = K rounded up to 128).
  * - The other ops never need one (no partial result leaves a workgroup).
@@ -223,13 +223,13 @@ int wq_prepack_q4(const int32_t* qweight, const int32_t* perm, void* packed, int
  * X [M, K] fp16; packed: from wq_prepack_q4 (the row order perm travels
  * inside it); scales [K/G, N] fp16; Y [M, N] fp16, written (fp32
  * accumulation).
- * Up to 8 rows: one launch per 8 rows of X, X staged whole in LDS, no
+ * Up to 4 rows: one launch, X staged whole in LDS, no
  * workspace.  More rows: X is first gathered into the packed weight's row
  * order in the workspace (in matrix-core operand order), then one launch
  * per 64 rows (48 for groups of 64, 32 for groups of 32) reads the packed
  * weight once (16-row matrix-core tiles).
  * workspace: device, workspace_bytes >= wq_workspace_bytes(WQ_OP_Q4G, M, K,
- *   N) = Mp * Kp * 2 bytes when M > 8 (Mp = M rounded up to 16, Kp = K
+ *   N) = Mp * Kp * 2 bytes when M > 4 (Mp = M rounded up to 16, Kp = K
  *   rounded up to 128), else 0 (NULL allowed); 16-byte aligned; needs no
  *   clearing.  WQ_ERR_WORKSPACE if missing or too small.  Calls that overlap
  *   in time need separate workspaces.

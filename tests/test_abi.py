@@ -112,11 +112,12 @@ def test_q4_validation(L):
     assert f(P, P, P, P, 0, 4096, 11008, 128, None) == wq.WQ_ERR_SHAPE
     assert f(P, P, P, P, 1, 32768 + 128, 64, 128, None) == wq.WQ_ERR_SHAPE   # K bound
     assert f(P, P_MIS, P, P, 1, 4096, 11008, 128, None) == wq.WQ_ERR_ALIGN
-    # above 8 rows: X in the packed row order (rows rounded up to 16, K to 128, fp16)
+    # above 4 rows: X in the packed row order (rows rounded up to 16, K to 128, fp16)
     q4ws = lambda Mp, Kp: Mp * Kp * 2
     need = L.wq_workspace_bytes(wq.WQ_OP_Q4G, 64, 4096, 11008)
     assert need == q4ws(64, 4096)
-    assert L.wq_workspace_bytes(wq.WQ_OP_Q4G, 8, 4096, 11008) == 0
+    assert L.wq_workspace_bytes(wq.WQ_OP_Q4G, 4, 4096, 11008) == 0
+    assert L.wq_workspace_bytes(wq.WQ_OP_Q4G, 5, 4096, 11008) == q4ws(16, 4096)
     assert L.wq_workspace_bytes(wq.WQ_OP_Q4G, 9, 4160, 11008) == q4ws(16, 4224)
     g4 = L.wq_gemm_q4_group
     assert g4(P, P, P, P, 64, 4096, 11008, 128, None, need, None) == wq.WQ_ERR_WORKSPACE

@@ -323,7 +323,7 @@ def gemm_q4_group(X, packed, scales, group_size=128, Y=None, ws=None):
     """Y[m, n] = sum_k X[m, k] * scale[g_idx[k], n] * q[k, n] from a packed 4-bit weight.
 
     ``ws``: device workspace of ``workspace_bytes(WQ_OP_Q4G, M, K, N)`` bytes
-    (needed above 8 rows of X; allocated here if None).
+    (needed above 4 rows of X; allocated here if None).
     """
     squeeze = X.dim() == 1
     X2 = X.reshape(1, -1) if squeeze else X

@@ -1,4 +1,4 @@
-// 4-bit group-wise GEMM for more rows of X (9 .. 64 per launch), reading the
+// 4-bit group-wise GEMM for more rows of X (5 .. 64 per launch), reading the
 // packed weight once per launch.
 //
 //   Y[m, n] = sum_g scale[g, n] * sum_{rows i of group g} X[m, perm[i]] * (u[i, n] - z[g, n])

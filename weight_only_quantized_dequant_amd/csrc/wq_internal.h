@@ -74,7 +74,7 @@ size_t q4_fwd_table_offset(int K, int N);
 // weight's row order in the workspace (in matrix-core operand order, with
 // the sums of X over runs of rows), then the tiled kernel reads the packed
 // weight once per 64 rows (q4_tiled.hip).
-constexpr int kQ4TiledMinRows = 8;
+constexpr int kQ4TiledMinRows = 4;
 size_t q4_tiled_workspace_bytes(int M, int K);
 hipError_t launch_q4_tiled(const void* X, const void* packed, const void* scales,
                            const void* zeros, void* Y, void* ws, int M, int K, int N, int G,
