@@ -91,6 +91,13 @@ __device__ __forceinline__ float q8_piece_bias(const u32x4 x) {
   return s * (-128.0f / kTwo24);
 }
 
+// x from lane (l + R) mod 16 of this lane's 16-lane row (DPP row_ror:R).
+template <int R>
+__device__ __forceinline__ float q8_row_rotate(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + R, 0xF, 0xF, false));
+}
+
 // Lane J of each 16-lane row, to every lane of the row (DPP row_newbcast).
 template <int J>
 __device__ __forceinline__ float q8_row_share(float x) {
@@ -112,11 +119,20 @@ __global__ __launch_bounds__(kQ8Threads) void q8_pair_kernel(
     const float* __restrict__ scales, _Float16* __restrict__ Y, int M, int K, int N, int G,
     int gsh) {
   __shared__ u32x4 xs[MT][kQ8Threads];  // rows r0 .. r0 + 4095 of the MT rows of X
-  // With several rows of X, each piece's sum of x is formed once, by the
-  // thread that stages it, for all eight waves (MT > 1 only: at one row the
-  // sums are cheaper inside each wave, off the path to the barrier).
-  constexpr bool XB = MT > 1;
+  // The sums of x that remove the code bias.  FOLD (all 16 pieces a quarter
+  // holds at a step share one group and so one scale): one sum per 128-row
+  // block, formed once per workgroup while x is staged (the 16 staging lanes
+  // of a block add their pieces' sums across the row) and read by every
+  // wave; each lane of the quarter adds a sixteenth of it, exactly, so the
+  // wave's reduction restores the whole.  Otherwise, with several rows of X,
+  // each piece's sum is formed once by the thread that stages it (at one row
+  // the per-piece sums are cheaper inside each wave).
+  constexpr bool GS = FOLD;
+  constexpr bool XB = MT > 1 && !FOLD;
   __shared__ float xb[XB ? MT : 1][kQ8Threads];  // -128 * 2^-24 * (sum of a piece's 8 x)
+  // -128 * 2^-24 / 16 * (sum of x over 128-row block 4 i + j of the chunk)
+  // at [m][j][i]: quarter j reads its 8 steps' values contiguously.
+  __shared__ float gs[GS ? MT : 1][4][kQ8Steps];
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -177,6 +193,15 @@ __global__ __launch_bounds__(kQ8Threads) void q8_pair_kernel(
     for (int m = 0; m < MT; ++m) {
       xs[m][t] = xg[m];
       if constexpr (XB) xb[m][t] = q8_piece_bias(xg[m]);
+      if constexpr (GS) {
+        // Piece t lies in block t / 16: the 16 lanes of a row (fixed order).
+        float ps = q8_piece_bias(xg[m]) * (1.0f / 16.0f);
+        ps += q8_row_rotate<8>(ps);
+        ps += q8_row_rotate<4>(ps);
+        ps += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, ps), 0x4E, 0xF, 0xF, false));
+        ps += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, ps), 0xB1, 0xF, 0xF, false));
+        if ((t & 15) == 0) gs[m][(t >> 4) & 3][t >> 6] = ps;
+      }
     }
     lds_barrier();
 
@@ -191,7 +216,12 @@ __global__ __launch_bounds__(kQ8Threads) void q8_pair_kernel(
         xv[i][m] = xs[m][64 * i + lane];
         if constexpr (XB) bias[i][m] = xb[m][64 * i + lane];
       }
-    if constexpr (!XB) {
+    if constexpr (GS) {
+#pragma unroll
+      for (int i = 0; i < kQ8Steps; ++i)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) bias[i][m] = gs[m][lane >> 4][i];
+    } else if constexpr (!XB) {
 #pragma unroll
       for (int i = 0; i < kQ8Steps; ++i)
 #pragma unroll
