@@ -95,14 +95,14 @@ __device__ __forceinline__ float q8_piece_bias(const u32x4 x) {
 template <int R>
 __device__ __forceinline__ float q8_row_rotate(float x) {
   return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + R, 0xF, 0xF, false));
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + R, 0xF, 0xF, true));
 }
 
 // Lane J of each 16-lane row, to every lane of the row (DPP row_newbcast).
 template <int J>
 __device__ __forceinline__ float q8_row_share(float x) {
   return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + J, 0xF, 0xF, false));
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + J, 0xF, 0xF, true));
 }
 // s[j] = lane j's value of this lane's 16-lane row, j = 0 .. 15.
 template <int J = 0>
@@ -198,8 +198,8 @@ __global__ __launch_bounds__(kQ8Threads) void q8_pair_kernel(
         float ps = q8_piece_bias(xg[m]) * (1.0f / 16.0f);
         ps += q8_row_rotate<8>(ps);
         ps += q8_row_rotate<4>(ps);
-        ps += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, ps), 0x4E, 0xF, 0xF, false));
-        ps += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, ps), 0xB1, 0xF, 0xF, false));
+        ps += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, ps), 0x4E, 0xF, 0xF, true));
+        ps += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, ps), 0xB1, 0xF, 0xF, true));
         if ((t & 15) == 0) gs[m][(t >> 4) & 3][t >> 6] = ps;
       }
     }

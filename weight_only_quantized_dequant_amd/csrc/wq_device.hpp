@@ -180,8 +180,10 @@ __device__ __forceinline__ float bfly_partner(float x) {
     r = __builtin_amdgcn_update_dpp(r, xi, 0x114, 0xF, 0xA, false);
     return __builtin_bit_cast(float, r);
   } else {
+    // Every lane is written and every source lane exists: bound_ctrl set, so
+    // the old value is not needed (no zero-initialising move).
     constexpr int ctrl = BIT == 3 ? 0x128 : BIT == 1 ? 0x4E : 0xB1;
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, xi, ctrl, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, xi, ctrl, 0xF, 0xF, true));
   }
 }
 
