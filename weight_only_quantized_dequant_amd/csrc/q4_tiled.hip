@@ -46,7 +46,6 @@ namespace wq {
 constexpr int kQTThreads = 512;
 constexpr int kQTWaves = kQTThreads / 64;
 constexpr int kQTMaxRun = 3;    // panels per workgroup at most
-constexpr int kQTMaxRows = 64;  // rows of X per launch at most
 
 int q4_tiled_kp(int K) { return (K + kQ4Block - 1) / kQ4Block * kQ4Block; }
 
