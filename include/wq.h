@@ -43,7 +43,7 @@
  *   frees memory, never synchronises a stream, and never changes the current
  *   device; work runs on the device that owns the buffers, on `stream`
  *   (a hipStream_t; NULL means the default stream), asynchronously.  The
- *   int8 and 4-bit products above 8 and 4 rows of X and the W8A8 family take a workspace,
+ *   int8 and 4-bit products above 16 and 4 rows of X and the W8A8 family take a workspace,
  *   sized by wq_workspace_bytes(), in which a call leaves nothing that a
  *   later call depends on (it needs no clearing); the other products need
  *   none (no partial result leaves a workgroup).  Calls that overlap in time
@@ -105,10 +105,10 @@ size_t wq_packed_bytes(int op, int K, int N, int G);
  *   S * M * N * 4 bytes (S = 2 at M = 256, K = N = 8192: 16 MiB; S = 1, no
  *   workspace, once the 128 x 128 output tiles alone fill the GPU, e.g. for
  *   M > 256 at N = 8192).
- * - WQ_OP_Q8G (wq_gemm_q8_group): above 8 rows of X, while the 32 x 128
+ * - WQ_OP_Q8G (wq_gemm_q8_group): above 16 rows of X, while the 32 x 128
  *   output tiles alone do not fill the GPU, the fp32 partial tiles of S K
- *   slices, S * M * N * 4 bytes (S = 8 for M <= 64 at K = N = 4096; the
- *   size holds for every group size the tiled path takes).
+ *   slices, S * M * N * 4 bytes (S = 8 for 17 <= M <= 64 at K = N = 4096;
+ *   the size holds for every group size the tiled path takes).
  * - WQ_OP_Q4G (wq_gemm_q4_group, wq_gemm_q4_group_zp): above 4 rows of X,
  *   X in the packed weight's row order, Mp * Kp * 2 bytes (Mp = M rounded
  *   up to 16, Kp = K rounded up to 128).
@@ -145,8 +145,12 @@ int wq_matvec_q3(const void* x, const void* packed, const void* scales, const vo
 /* ----------------------------------------------------------------- int8 -- */
 
 /* Re-lay out a group-wise int8 weight qweight [K, N] (codes -127..127) into
- * column pairs of 16-byte pieces (8 rows x 2 columns, K/8 pieces per pair).
- * packed: wq_packed_bytes(WQ_OP_Q8G, K, N, G) = K * N bytes, written.
+ * the matrix-core operand order: tiles of 16 columns x 64 rows (1 KB), the
+ * tiles of a 16-column panel contiguous; 16-byte slot l of a tile holds 8
+ * rows of column l % 16 for each of the tile's two 32-row halves.  K is
+ * rounded up to 64 (padding codes are 0).
+ * packed: wq_packed_bytes(WQ_OP_Q8G, K, N, G) = N * (K rounded up to 64)
+ *   bytes (K * N when K % 64 == 0), written.
  * Rules: K % 32 == 0, N % 16 == 0. */
 int wq_prepack_q8(const int8_t* qweight, void* packed, int K, int N, void* stream);
 
@@ -155,17 +159,17 @@ int wq_prepack_q8(const int8_t* qweight, void* packed, int K, int N, void* strea
  * X [M, K] fp16; packed: from wq_prepack_q8; scales [K/G, N] fp32;
  * Y [M, N] fp16, written (fp32 accumulation, one round to nearest even).
  * Evaluated per group as scale * (sum of X * q), exact products, fp32 sums.
- * M <= 8, or G not a multiple of 64: streaming passes over the packed weight
- * (one per 8 rows of X).  Otherwise a tiled matrix-core launch (32 x 128
- * output tiles) reads the packed weight once; while those tiles alone do not
- * fill the GPU (e.g. M <= 64 at N = 4096) K is split over 2..8 workgroups
- * per tile, their fp32 partial tiles go to the workspace, and a second
- * launch adds them in a fixed order and rounds once.
+ * M <= 16, or G not a multiple of 64: streaming matrix-core passes over the
+ * packed weight (one per 16 rows of X).  Otherwise a tiled matrix-core
+ * launch (32 x 128 output tiles) reads the packed weight once; while those
+ * tiles alone do not fill the GPU (e.g. M <= 64 at N = 4096) K is split over
+ * 2..8 workgroups per tile, their fp32 partial tiles go to the workspace, and
+ * a second launch adds them in a fixed order and rounds once.
  * ("Quantization CUDA", tom-jerr.github.io, "Int8 Weight Only Quantization";
  * "融合反量化与GEMM：LLM推理的CUDA内核优化实践", zingnex.cn, "技术实现细节".)
  * workspace: device, needed when G % 64 == 0 and wq_workspace_bytes(
  *   WQ_OP_Q8G, M, K, N) > 0 (S * M * N * 4 bytes, S the number of K slices:
- *   8 for 9 <= M <= 64 at K = N = 4096), else NULL allowed; 16-byte aligned;
+ *   8 for 17 <= M <= 64 at K = N = 4096), else NULL allowed; 16-byte aligned;
  *   needs no clearing.  WQ_ERR_WORKSPACE if missing or too small.  Calls
  *   that overlap in time need separate workspaces.
  * Rules: M >= 1, K % 32 == 0, N % 16 == 0, G % 32 == 0, K % G == 0,
