@@ -195,11 +195,36 @@ def test_q8_gemm_tiles_vs_oracle(wq, M, K, N, G):
     assert_tol(host(Y), oracle.gemm_q8_group(d["X"], d["q"], d["scales"], G), f"q8 tiles {M}x{K}x{N} G{G}")
 
 
-@pytest.mark.parametrize("M,K,N,G", [(80, 1024, 400, 128), (12, 2048, 1024, 128)])
+# Up to 16 rows of X the int8 product is one streaming matrix-core pass over
+# the packed tiles: chains of 32-row steps per scale (groups of 32 .. 512
+# rows a power of two, or one step per scale otherwise), X staged per 4096-row
+# chunk, the 8 waves of a panel summed in LDS.
+@pytest.mark.parametrize("M,K,N,G", [
+    (9, 4096, 4096, 128),      # first row count past the 8-row operand tile rows
+    (16, 4096, 11008, 128),    # the full 16-row pass, wide N
+    (12, 224, 48, 32),         # K % 64 == 32: the last packed tile half padding; 3 panels
+    (16, 1152, 272, 96),       # a scale per 32-row step (G not a power of two); 17 panels
+    (13, 8192, 512, 4096),     # one chain per wave and chunk (G > 512), two chunks
+    (11, 4608, 256, 512),      # a ragged second chunk (512 of 4096 rows)
+    (10, 4224, 4112, 64),      # chains of two steps, a ragged chunk, N not a multiple of 256
+    (15, 2048, 1024, 256),     # chains of eight steps
+])
+def test_q8_streaming_rows_vs_oracle(wq, M, K, N, G):
+    d = synth.gen_q8_group(M, K, N, G, seed=301 + M + K + N)
+    Y = wq.gemm_q8_group(cu(d["X"]), wq.prepack_q8(cu(d["q"])), cu(d["scales"]), G)
+    ref = oracle.gemm_q8_group(d["X"], d["q"], d["scales"], G)
+    assert_tol(host(Y), ref, f"q8 streaming {M}x{K}x{N} G{G}")
+    A = np.abs(np.repeat(d["scales"].astype(np.float64), G, axis=0) * d["q"])
+    assert_fwd_bound(host(Y), ref, np.abs(d["X"].astype(np.float64)) @ A, K, "f16",
+                     f"q8 streaming {M}x{K}x{N} G{G}")
+
+
+@pytest.mark.parametrize("M,K,N,G", [(80, 1024, 400, 128), (12, 2048, 1024, 128),
+                                     (16, 2048, 1024, 64), (3, 4160, 272, 32)])
 def test_q8_gemm_integer_exact_and_deterministic(wq, M, K, N, G):
-    # Scales 1 and small integer X on the tiled path (12 rows: K in 8
-    # slices): every fp32 partial sum is an exact integer, so the result is
-    # bit-exact; repeated calls agree.
+    # Scales 1 and small integer X on the tiled path (80 rows) and the
+    # streaming pass (3..16 rows): every fp32 partial sum is an exact
+    # integer, so the result is bit-exact; repeated calls agree.
     rng = np.random.default_rng(43)
     q = rng.integers(-127, 128, size=(K, N)).astype(np.int8)
     X = rng.integers(-2, 3, size=(M, K)).astype(np.float16)
