@@ -145,12 +145,8 @@ int wq_matvec_q3(const void* x, const void* packed, const void* scales, const vo
 /* ----------------------------------------------------------------- int8 -- */
 
 /* Re-lay out a group-wise int8 weight qweight [K, N] (codes -127..127) into
- * the matrix-core operand order: tiles of 16 columns x 64 rows (1 KB), the
- * tiles of a 16-column panel contiguous; 16-byte slot l of a tile holds 8
- * rows of column l % 16 for each of the tile's two 32-row halves.  K is
- * rounded up to 64 (padding codes are 0).
- * packed: wq_packed_bytes(WQ_OP_Q8G, K, N, G) = N * (K rounded up to 64)
- *   bytes (K * N when K % 64 == 0), written.
+ * column pairs of 16-byte pieces (8 rows x 2 columns, K/8 pieces per pair).
+ * packed: wq_packed_bytes(WQ_OP_Q8G, K, N, G) = K * N bytes, written.
  * Rules: K % 32 == 0, N % 16 == 0. */
 int wq_prepack_q8(const int8_t* qweight, void* packed, int K, int N, void* stream);
 
@@ -159,8 +155,9 @@ int wq_prepack_q8(const int8_t* qweight, void* packed, int K, int N, void* strea
  * X [M, K] fp16; packed: from wq_prepack_q8; scales [K/G, N] fp32;
  * Y [M, N] fp16, written (fp32 accumulation, one round to nearest even).
  * Evaluated per group as scale * (sum of X * q), exact products, fp32 sums.
- * M <= 16, or G not a multiple of 64: streaming matrix-core passes over the
- * packed weight (one per 16 rows of X).  Otherwise a tiled matrix-core
+ * M <= 16, or G not a multiple of 64: streaming passes over the packed
+ * weight, one per 16 rows of X (one or two rows on v_dot2, 3 to 16 on the
+ * matrix cores).  Otherwise a tiled matrix-core
  * launch (32 x 128 output tiles) reads the packed weight once; while those
  * tiles alone do not fill the GPU (e.g. M <= 64 at N = 4096) K is split over
  * 2..8 workgroups per tile, their fp32 partial tiles go to the workspace, and

@@ -36,9 +36,9 @@ def test_status_strings(L):
 def test_packed_bytes_pure_and_valid(L):
     a = L.wq_packed_bytes(wq.WQ_OP_Q8G, 4096, 4096, 128)
     assert a == 4096 * 4096 and a == L.wq_packed_bytes(wq.WQ_OP_Q8G, 4096, 4096, 0)
-    # int8 tiles of 64 rows: N * K rounded up to 64 (K * N when K % 64 == 0).
+    # int8 column pairs: exactly the stored weight's K * N bytes at any legal shape.
     for K, N in ((32, 16), (96, 48), (4224, 272), (11008, 4096), (8192, 11008)):
-        assert L.wq_packed_bytes(wq.WQ_OP_Q8G, K, N, 32) == N * ((K + 63) // 64 * 64)
+        assert L.wq_packed_bytes(wq.WQ_OP_Q8G, K, N, 32) == K * N
     # the configured shapes re-lay out without padding
     assert L.wq_packed_bytes(wq.WQ_OP_Q3, 4096, 11008, 0) == 4096 // 32 * 3 * 11008 * 4
     assert L.wq_packed_bytes(wq.WQ_OP_Q3, 11008, 4096, 0) >= 11008 // 32 * 3 * 4096 * 4

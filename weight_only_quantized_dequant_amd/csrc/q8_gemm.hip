@@ -12,14 +12,14 @@
 // Tiles.  A workgroup (4 waves) owns a 32 x 128 tile of Y and walks K in
 // stages of 128 rows.  Per stage, direct-to-LDS buffer loads bring the X tile
 // (fp16, 32 x 128), the int8 codes of the weight tile (128 rows x 128
-// columns: two 1 KB tiles of 64 rows of each of 8 panels of the packed
-// layout, copied as they are) and the scale rows of the stage's groups into
-// a ring of kStages slots (75 KB: two workgroups fit on a CU).  Each wave
-// builds its v_mfma_f32_16x16x32_f16 operands for a 16 x 64 sub-tile in
-// registers, straight from the int8 stage: slot l of a packed tile already
-// holds the 8 codes lane l takes for each of the tile's two k32 steps, and
-// one v_perm_b32 per two codes turns them into zero-exponent fp16s (the
-// exact subnormals u 2^-24, u = q + 128).  One more
+// columns: 16 pieces of each of 64 column pairs of the packed layout, 8 rows
+// x 2 columns per piece) and the scale rows of the stage's groups into a ring
+// of kStages slots (75 KB: two workgroups fit on a CU).  Each wave builds its
+// v_mfma_f32_16x16x32_f16 operands for a 16 x 64 sub-tile in registers,
+// straight from the int8 stage: a piece is the 8 rows of one k32 octet for
+// two columns, and one v_perm_b32 per word turns a column's two code bytes
+// into two zero-exponent fp16s (the exact subnormals u 2^-24, u = q + 128),
+// so one 16-byte LDS read gives the operands of two columns.  One more
 // matrix-core product per k32 step against a constant operand of 128 2^-24
 // gives the offset term.  Each wave keeps the current group's sums
 // and a running total; at the end of a group the total takes
@@ -44,7 +44,7 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 constexpr int kBM = 32, kBN = 128, kBK = 128, kStages = 3, kThreadsG = 256;
 constexpr int kRowA = kBK * 2;                   // 256 bytes: one fp16 row of X per stage
 constexpr int kStageA = kBM * kRowA;             // X tile, fp16 [m][k], 16 KB
-constexpr int kStageB = kBK * kBN;               // codes: 16 packed tiles of 1 KB
+constexpr int kStageB = kBK * kBN;               // codes: 128 rows x 8 chunks of 16 bytes
 constexpr int kStageS = 1024;                    // two scale rows of 128 columns
 constexpr int kStage = kStageA + kStageB + kStageS;
 constexpr int kLoads = 6;                        // direct-to-LDS loads per stage per wave
@@ -56,16 +56,20 @@ __device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 15); }
 
 }  // namespace
 
-// Codes of a stage in LDS: packed tile (panel n0 / 16 + q / 2, 64-row block
-// 2 kt + q % 2) at offset 1024 q, q = 0..15, each copied by one
-// direct-to-LDS load (lane l's 16 bytes land at 16 l, as in memory).
+// Codes of a stage in LDS: piece b (rows 8 b .. 8 b + 7 of the stage,
+// b = 0..15) of the tile's column pair p (0..63) sits at slot
+// 16 p + (b ^ (p % 16)).  A direct-to-LDS load writes 64 consecutive slots:
+// 4 pairs x 16 pieces, i.e. four 256-byte runs of the packed weight.  The
+// swizzle keeps the 16 lanes of one fragment read (16 pairs, one piece
+// each) on distinct banks.
 //
-// Fragments.  Lane l of a wave with columns w0 .. w0 + 63 (panels
-// w0 / 16 + jj, jj = 0..3) takes, for the k32 step h, bytes 8 (h % 2) .. + 7
-// of slot l of the panel's tile h / 2: the rows 32 h + 8 (l / 16) + e of
-// column w0 + 16 jj + l % 16, the operand of block jj.  With the codes as
-// the first operand the result is transposed: lane l holds the 4
-// consecutive columns w0 + 16 jj + 4 (l / 16) + r (r = 0..3) of one row.
+// Fragments.  Lane l of a wave with columns w0 .. w0 + 63 (pairs w0 / 2 ..)
+// takes, for the k32 step h and half H (0, 1), piece 4 h + l / 16 of pair
+// w0 / 2 + 16 H + l % 16: the 8 rows 32 h + 8 (l / 16) + e of two columns.
+// Column c of it goes to the matrix-core operand of block 2 H + c, so block
+// 2 H + c, operand column t holds weight column w0 + 32 H + 2 t + c; the
+// transposed result then gives lane l, per half, the 8 consecutive columns
+// w0 + 32 H + 8 (l / 16) + 2 r + c (r = 0..3, c = 0, 1) of one row.
 // Split K (S > 1): workgroup b takes K slice b % S (S divides 8, so with
 // S = 8 every workgroup of an XCD reads the same slice of X) and writes its
 // fp32 partial tile, still in units of 2^-24, to ws [S][M][N]; a second
@@ -73,7 +77,7 @@ __device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 15); }
 __global__ __launch_bounds__(kThreadsG, 2) void q8_gemm_kernel(
     const _Float16* __restrict__ X, const uint8_t* __restrict__ Wp,
     const float* __restrict__ scales, _Float16* __restrict__ Y, float* __restrict__ ws, int M,
-    int K, int N, int G, int KT, int mtiles, int ntiles, int S) {
+    int K, int N, int G, int KB, int mtiles, int ntiles, int S) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStage];
 
   // Workgroups b and b + 8 run on the same XCD: the M tiles that share a
@@ -91,7 +95,7 @@ __global__ __launch_bounds__(kThreadsG, 2) void q8_gemm_kernel(
   const int nk = (slice + 1) * nkt / S - kt0;
 
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, M * K * 2);
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wp, (N / 16) * KT * 1024);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wp, K * N);
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, (K / G) * N * 4);
 
   // X: load t of wave w fills stage rows 4 (4 w + t) .. + 3; lane l brings
@@ -102,15 +106,17 @@ __global__ __launch_bounds__(kThreadsG, 2) void q8_gemm_kernel(
     const int row = 4 * (2 * wave + t) + (lane >> 4);
     a_off[t] = m0 + row < M ? (m0 + row) * K * 2 + 16 * swz(row, lane & 15) : -1;
   }
-  // Codes: load t of wave w copies stage tile q = 4 w + t: panel
-  // n0 / 16 + q / 2, 64-row block 2 kt + q % 2.
-  int b_off[4];
+  // Codes: load t of wave w fills slots 64 (4 w + t) .. + 63, i.e. pair
+  // p = 4 (4 w + t) + l / 16 of the tile, the piece that slot 16 p + l % 16
+  // holds: b = (l % 16) ^ (p % 16), with p % 16 = 4 t + l / 16.
+  int b_off[4], b_sw[4];
   bool b_live[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int q = 4 * wave + t, pn = n0 / 16 + (q >> 1);
-    b_live[t] = pn < N / 16;
-    b_off[t] = b_live[t] ? (pn * KT + (q & 1)) * 1024 + 16 * lane : 0;
+    const int pg = n0 / 2 + 4 * (4 * wave + t) + (lane >> 4);
+    b_live[t] = pg < N / 2;
+    b_off[t] = b_live[t] ? pg * KB * 16 : 0;
+    b_sw[t] = (lane & 15) ^ (4 * t + (lane >> 4));
   }
   // Scales (wave 0): lanes 0..31 columns n0 + 4 l .. + 3 of the group of the
   // stage's first row, lanes 32..63 the same columns of the group of row 64.
@@ -130,10 +136,10 @@ __global__ __launch_bounds__(kThreadsG, 2) void q8_gemm_kernel(
           0, 0, 0);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int b = 2 * kt + (t & 1);  // t & 1 == q & 1
+      const int b = kt * 16 + b_sw[t];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           wr, (__attribute__((address_space(3))) void*)(base + kStageA + 1024 * (4 * wave + t)), 16,
-          (b_live[t] && b < KT) ? b_off[t] + 2048 * kt : kOutOfRange, 0, 0, 0);
+          (b_live[t] && b < KB) ? b_off[t] + 16 * b : kOutOfRange, 0, 0, 0);
     }
     if (wave == 0) {
       const int g = (k0 + (lane >= 32 ? 64 : 0)) / G;
@@ -146,9 +152,9 @@ __global__ __launch_bounds__(kThreadsG, 2) void q8_gemm_kernel(
   const int wm = wave >> 1, wn = wave & 1;  // 2 x 2 waves, each 16 rows x 64 columns
   const int fr = lane & 15, fq = lane >> 4;
   // LDS byte offsets (within a stage) of this lane's fragment reads, per k32
-  // step h: X row wm 16 + l % 16; bytes 8 (h % 2) .. of slot l of tile
-  // q = 2 (4 wn + jj) + h / 2.
-  int a_lds[4][1], b_lds[4][4];
+  // step h: X row wm 16 + l % 16; the piece 4 h + l / 16 of pair
+  // 32 wn + 16 H + l % 16 (whose p % 16 is l % 16).
+  int a_lds[4][1], b_lds[4][2];
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
 #pragma unroll
@@ -157,8 +163,8 @@ __global__ __launch_bounds__(kThreadsG, 2) void q8_gemm_kernel(
       a_lds[h][i] = row * kRowA + 16 * swz(row, 4 * h + fq);
     }
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-      b_lds[h][jj] = kStageA + 1024 * (2 * (4 * wn + jj) + (h >> 1)) + 16 * lane + 8 * (h & 1);
+    for (int H = 0; H < 2; ++H)
+      b_lds[h][H] = kStageA + (16 * (32 * wn + 16 * H + fr) + ((4 * h + fq) ^ fr)) * 16;
   }
 
   // acc: this group's sums of x * u (u = q + 128, as fp16 subnormals u 2^-24);
@@ -172,42 +178,48 @@ __global__ __launch_bounds__(kThreadsG, 2) void q8_gemm_kernel(
     for (int j = 0; j < 4; ++j) tot[i][j] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
   const h8 c128 = __builtin_bit_cast(h8, (u32x4){0x00800080u, 0x00800080u, 0x00800080u, 0x00800080u});
 
-  // One k32 step of the stage in slot S: LDS reads; then the code bytes into
-  // the low bytes of fp16s whose other bits are zero (the subnormals
-  // u 2^-24), one v_perm_b32 per two codes.
+  // One k32 step of the stage in slot S: LDS reads; then each column's two
+  // code bytes of a word into the low bytes of two fp16s whose other bits are
+  // zero (the subnormals u 2^-24), one v_perm_b32 per register.
   struct Step {
     h8 a[1];
-    u32x2 B[4];
+    u32x4 B[2];
   };
   auto read_step = [&](const unsigned char* S, int h, Step& st) {
 #pragma unroll
     for (int i = 0; i < 1; ++i) st.a[i] = *reinterpret_cast<const h8*>(S + a_lds[h][i]);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) st.B[jj] = *reinterpret_cast<const u32x2*>(S + b_lds[h][jj]);
+    for (int H = 0; H < 2; ++H) st.B[H] = *reinterpret_cast<const u32x4*>(S + b_lds[h][H]);
   };
   auto convert = [&](const Step& st, h8 b[4]) {
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const u32x2 w = st.B[jj];
-      const u32x4 c = {q8_byte_pair<0>(w[0]), q8_byte_pair<1>(w[0]), q8_byte_pair<0>(w[1]),
-                       q8_byte_pair<1>(w[1])};
-      b[jj] = __builtin_bit_cast(h8, c);
+    for (int H = 0; H < 2; ++H) {
+      const u32x4 w = st.B[H];
+      const u32x4 c0 = {q8_col_pair<0>(w[0]), q8_col_pair<0>(w[1]), q8_col_pair<0>(w[2]), q8_col_pair<0>(w[3])};
+      const u32x4 c1 = {q8_col_pair<1>(w[0]), q8_col_pair<1>(w[1]), q8_col_pair<1>(w[2]), q8_col_pair<1>(w[3])};
+      b[2 * H] = __builtin_bit_cast(h8, c0);
+      b[2 * H + 1] = __builtin_bit_cast(h8, c1);
     }
   };
   auto group_end = [&](const unsigned char* S, int h) {
-    // Scales of this lane's columns: v[jj] for columns
-    // 64 wn + 16 jj + 4 (l / 16) + 0 .. 3 of the tile.
-    const unsigned char* sc = S + kStageA + kStageB + 512 * (h >> 1) + 4 * (wn * 64 + 4 * fq);
-    f32x4 v[4];
+    // Scales of this lane's columns: v[H][0..1] for columns
+    // 64 wn + 32 H + 8 (l / 16) + 0 .. 7 of the tile.
+    const unsigned char* sc = S + kStageA + kStageB + 512 * (h >> 1) + 4 * (wn * 64 + 8 * fq);
+    f32x4 v[2][2];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) v[jj] = *reinterpret_cast<const f32x4*>(sc + 64 * jj);
+    for (int H = 0; H < 2; ++H)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) v[H][e] = *reinterpret_cast<const f32x4*>(sc + 128 * H + 16 * e);
 #pragma unroll
     for (int i = 0; i < 1; ++i) {
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
+      for (int j = 0; j < 4; ++j) {
+        const int H = j >> 1, c = j & 1;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          tot[i][jj][r] = __builtin_fmaf(acc[i][jj][r] - xacc[i][r], v[jj][r], tot[i][jj][r]);
+        for (int r = 0; r < 4; ++r) {
+          const int e = 2 * r + c;  // column 8 (l / 16) + e of half H
+          tot[i][j][r] = __builtin_fmaf(acc[i][j][r] - xacc[i][r], v[H][e >> 2][e & 3], tot[i][j][r]);
+        }
       }
     }
   };
@@ -279,17 +291,25 @@ __global__ __launch_bounds__(kThreadsG, 2) void q8_gemm_kernel(
     const int m = m0 + wm * 16 + 16 * i + fr;
     if (m >= M) continue;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      // Columns n .. n + 3 of tot[jj][0 .. 3] (N % 16 == 0 keeps them in range).
-      const int n = n0 + wn * 64 + 16 * jj + 4 * fq;
+    for (int H = 0; H < 2; ++H) {
+      const int n = n0 + wn * 64 + 32 * H + 8 * fq;
       if (n >= N) continue;
       if (S > 1) {
-        *reinterpret_cast<f32x4*>(ws + ((size_t)slice * M + m) * N + n) = tot[i][jj];
+        // Columns n + 2 r + c of tot[2 H + c][r]: 8 consecutive fp32.
+        float* o = ws + ((size_t)slice * M + m) * N + n;
+        const f32x4 lo = {tot[i][2 * H][0], tot[i][2 * H + 1][0], tot[i][2 * H][1], tot[i][2 * H + 1][1]};
+        const f32x4 hi = {tot[i][2 * H][2], tot[i][2 * H + 1][2], tot[i][2 * H][3], tot[i][2 * H + 1][3]};
+        *reinterpret_cast<f32x4*>(o) = lo;
+        *reinterpret_cast<f32x4*>(o + 4) = hi;
         continue;
       }
-      const h2 lo = {(_Float16)(tot[i][jj][0] * kTwo24), (_Float16)(tot[i][jj][1] * kTwo24)};
-      const h2 hi = {(_Float16)(tot[i][jj][2] * kTwo24), (_Float16)(tot[i][jj][3] * kTwo24)};
-      *reinterpret_cast<uint2*>(Y + (size_t)m * N + n) = make_uint2(as_u32(lo), as_u32(hi));
+      uint32_t w[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const h2 pr = {(_Float16)(tot[i][2 * H][r] * kTwo24), (_Float16)(tot[i][2 * H + 1][r] * kTwo24)};
+        w[r] = as_u32(pr);
+      }
+      *reinterpret_cast<uint4*>(Y + (size_t)m * N + n) = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
 }
@@ -339,7 +359,7 @@ hipError_t launch_q8_gemm(const void* X, const void* packed, const float* scales
   hipLaunchKernelGGL(q8_gemm_kernel, dim3(grid), dim3(kThreadsG), 0, s,
                      reinterpret_cast<const _Float16*>(X), reinterpret_cast<const uint8_t*>(packed),
                      scales, reinterpret_cast<_Float16*>(Y), reinterpret_cast<float*>(ws), M, K, N,
-                     G, (K + 63) / 64, mtiles, ntiles, S);
+                     G, K / 8, mtiles, ntiles, S);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   const size_t quads = ((size_t)M * N) / 4;

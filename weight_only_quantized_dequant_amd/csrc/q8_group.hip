@@ -10,123 +10,325 @@
 // rows of K per column).
 //
 // Layout.  The [K, N] weight is re-laid out once, offline (wq_prepack_q8),
-// into tiles of 16 columns x 64 rows, 1 KB each: tile (p, b) holds columns
-// 16p .. 16p + 15 and rows 64b .. 64b + 63 and sits at byte (p KT + b) 1024,
-// KT = ceil(K / 64), so the tiles of a 16-column panel are contiguous.  Slot
-// l of a tile (16 bytes at 16 l) holds column 16p + l % 16: bytes e = 0..7
-// rows 64b + 8 (l / 16) + e, bytes 8 + e rows 64b + 32 + 8 (l / 16) + e.
-// That is the matrix-core operand layout: a wave that reads a tile with one
-// 16-byte load per lane holds in lane l the codes v_mfma_f32_16x16x32_f16
-// takes for column l % 16 at k = 8 (l / 16) + e, for both 32-row steps of
-// the tile.  Codes are stored biased (u = q + 128) so that a byte goes
-// straight into an fp16 mantissa as the subnormal u 2^-24 (one v_perm_b32
-// per two codes) and every product x u 2^-24 is exact in fp32; rows past K
-// (K a multiple of 32 but not of 64) hold u = 128, i.e. q = 0.
+// into column pairs: pair q (columns 2q, 2q + 1) is K/8 contiguous 16-byte
+// pieces, piece b holding rows 8b .. 8b + 7.  Word d of a piece holds rows
+// 2d and 2d + 1 of column 2q in bytes 0 and 1, and the same rows of column
+// 2q + 1 in bytes 2 and 3, so one v_perm_b32 puts a column's two rows into
+// an fp16 pair (q8_col_pair).  Codes are stored biased (u = q + 128): the
+// bias is removed with one sum of x per piece, and the biased byte goes
+// straight into an fp16 mantissa as a subnormal, u * 2^-24, so every
+// product x * u * 2^-24 is exact in fp32.
 //
-// The product, up to 16 rows of X per launch.  A workgroup of 8 waves owns a
-// panel; K is taken in chunks of 4096 rows, of which wave w takes the 8
-// tiles 8w .. 8w + 7 (one 16-byte load each per lane, all issued at once).
-// X is staged per chunk in LDS; the A operand of a step is 8 halves of one
-// row of X (row l % 16 of the operand; at fewer rows, row 0 or zero rows).
-// The offset 128 comes out per chain of steps inside one group: the staging
-// threads form -128 2^-24 sum(x) over each chain's rows once per workgroup,
-// and a chain's sums of x u 2^-24 take it before its scale:
-// total += (chain sums - offset) * scale, in fp32, in units of 2^-24.  At the
-// end the 8 waves' totals are added in a fixed order and rounded once to fp16.
+// The product at one or two rows of X.  A wave owns one column pair over all
+// of K, so no partial sum ever leaves the wave: at step i lane l takes piece
+// 64 i + l of its pair (the wave reads 1 KB of contiguous memory per step),
+// and one cross-lane reduction at the end gives the two outputs.  Eight waves
+// (a 16-column panel) share the activations, staged once per 4096 rows in LDS.
+//
+// The product at 3 .. 16 rows (q8_mfma_kernel) runs on the matrix cores,
+// v_mfma_f32_16x16x32_f16, from the same packed weight: the 8 waves of a
+// panel split K, each load instruction of a wave brings 128 contiguous bytes
+// of each of the panel's 8 pairs, and a wave-private LDS copy turns them into
+// the operand order (16 columns x 32 rows per step).
 #include "wq_device.hpp"
 #include "wq_internal.h"
 
 namespace wq {
 
-namespace {
-
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-
-constexpr int kQ8Threads = 512;             // 8 wave64s, two per SIMD
-constexpr int kQ8Waves = kQ8Threads / 64;
-constexpr int kQ8Tiles = 8;                 // tiles per wave per chunk
-constexpr int kQ8Steps = 2 * kQ8Tiles;      // 32-row steps per wave per chunk
-constexpr int kQ8Chunk = kQ8Waves * kQ8Tiles * 64;  // rows of K per chunk: 4096
-// LDS row of X: a chunk of fp16 plus 16 bytes, so that the 16 rows an
-// operand read takes start on different banks.
-constexpr int kQ8RowBytes = 2 * kQ8Chunk + 16;
-// Rows of X per launch; from kQ8GemmMinRows rows on (groups a multiple of
-// 64 rows) the tiled matrix-core GEMM (q8_gemm.hip) takes over.
-constexpr int kQ8PassRows = 16;
+// 512 threads (8 wave64s, two per SIMD): while one wave of a SIMD converts
+// its codes the other's loads are still landing.
+constexpr int kQ8Threads = 512;
+constexpr int kQ8Steps = 8;                    // pieces per lane per chunk
+constexpr int kQ8Chunk = 64 * kQ8Steps * 8;    // rows of K per chunk: 4096
+// From this many rows of X on, the product runs as a tiled matrix-core GEMM
+// (q8_gemm.hip) instead of one streaming pass over the weight per 16 rows.
 constexpr int kQ8GemmMinRows = 17;
+constexpr int kQ8PassRows = 16;
 
-__host__ __device__ inline int q8_tiles_per_panel(int K) { return (K + 63) / 64; }
-
-}  // namespace
-
-// Panel plan: 16-column panels; u = tiles of 64 rows per panel.
+// Panel plan: 16-column panels (8 column pairs); u = pieces per pair.
 PanelPlan plan_q8(int K, int N) {
   PanelPlan p{};
   p.P = 16;
   p.cpp = 1;
   p.npanels = N / 16;
-  p.u = q8_tiles_per_panel(K);
+  p.u = K / 8;
   p.nsa = 0;
-  p.packed_bytes = (size_t)p.npanels * p.u * 1024;
+  p.packed_bytes = (size_t)K * N;
   return p;
 }
 
 // ---------------------------------------------------------------------------
-// Offline re-layout: one thread per 16-byte slot.
+// Offline re-layout: one thread per 16-byte piece (pair q, rows 8b .. 8b + 7).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void q8_prepack_kernel(const int8_t* __restrict__ W,
-                                                              uint8_t* __restrict__ out, int K,
+                                                              uint32_t* __restrict__ out, int K,
                                                               int N) {
-  const int KT = q8_tiles_per_panel(K);
+  const int KB = K / 8;
   const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= (size_t)(N / 16) * KT * 64) return;
-  const int l = (int)(idx % 64);
-  const size_t tile = idx / 64;
-  const int b = (int)(tile % KT), p = (int)(tile / KT);
-  const int col = 16 * p + (l & 15), h = l >> 4;
-  uint32_t w[4];
+  if (idx >= (size_t)(N / 2) * KB) return;
+  const int q = (int)(idx / KB), b = (int)(idx % KB);
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(W) + (size_t)8 * b * N + 2 * q;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    uint32_t v = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 64 * b + 32 * (d >> 1) + 8 * h + 4 * (d & 1) + e;
-      const uint32_t u = row < K ? ((uint32_t)(uint8_t)W[(size_t)row * N + col] ^ 0x80u) : 0x80u;
-      v |= u << (8 * e);
-    }
-    w[d] = v;
+    const uint32_t r0 = *reinterpret_cast<const uint16_t*>(src + (size_t)(2 * d) * N);
+    const uint32_t r1 = *reinterpret_cast<const uint16_t*>(src + (size_t)(2 * d + 1) * N);
+    // bytes: row 2d col 0, row 2d+1 col 0, row 2d col 1, row 2d+1 col 1
+    const uint32_t v = (r0 & 0xFFu) | ((r1 & 0xFFu) << 8) | ((r0 >> 8) << 16) | ((r1 >> 8) << 24);
+    out[idx * 4 + d] = v ^ 0x80808080u;
   }
-  *reinterpret_cast<u32x4*>(out + idx * 16) = (u32x4){w[0], w[1], w[2], w[3]};
 }
 
-// Bit-exact check of the packed layout: every slot through q8_byte_pair,
+// ---------------------------------------------------------------------------
+// The fused product, MT rows of X per pass.
+// ---------------------------------------------------------------------------
+// FOLD (one or two rows of X, G a power of two >= 128, log2 G = gsh): the
+// 16 lanes of a quarter-wave hold 128 consecutive rows at every step, i.e.
+// part of one group, so a quarter needs 16 scales per 4096 rows (8 steps x 2
+// columns).  Lane j of the quarter loads the one of step j / 2, column j % 2
+// (one 4-byte load per lane), and DPP row broadcasts hand all 16 to every
+// lane of the quarter as soon as it lands, before the weights.  Otherwise
+// each piece's two sums take their scales (one 8-byte load per piece).
+// u = q + 128: both columns of a piece start at -128 * sum(x) over the
+// piece's 8 activations, in 2^-24 units.
+__device__ __forceinline__ float q8_piece_bias(const u32x4 x) {
+  const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+  float s = 0.0f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) s = dot2(as_h2(x[d]), ones, s);
+  return s * (-128.0f / kTwo24);
+}
+
+// x from lane (l - R) mod 16 of this lane's 16-lane row (DPP row_ror:R).
+template <int R>
+__device__ __forceinline__ float q8_row_rotate(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + R, 0xF, 0xF, true));
+}
+
+// Lane J of each 16-lane row, to every lane of the row (DPP row_newbcast).
+template <int J>
+__device__ __forceinline__ float q8_row_share(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + J, 0xF, 0xF, true));
+}
+// s[j] = lane j's value of this lane's 16-lane row, j = 0 .. 15.
+template <int J = 0>
+__device__ __forceinline__ void q8_row_all(float x, float (&s)[2 * kQ8Steps]) {
+  if constexpr (J < 2 * kQ8Steps) {
+    s[J] = q8_row_share<J>(x);
+    q8_row_all<J + 1>(x, s);
+  }
+}
+
+template <int MT, bool FOLD>
+__global__ __launch_bounds__(kQ8Threads) void q8_pair_kernel(
+    const _Float16* __restrict__ X, const uint8_t* __restrict__ Wp,
+    const float* __restrict__ scales, _Float16* __restrict__ Y, int M, int K, int N, int G,
+    int gsh) {
+  __shared__ u32x4 xs[MT][kQ8Threads];  // rows r0 .. r0 + 4095 of the MT rows of X
+  // The sums of x that remove the code bias.  FOLD (all 16 pieces a quarter
+  // holds at a step share one group and so one scale): one sum per 128-row
+  // block, formed once per workgroup while x is staged (the 16 staging lanes
+  // of a block add their pieces' sums across the row) and read by every
+  // wave; each lane of the quarter adds a sixteenth of it, exactly, so the
+  // wave's reduction restores the whole.  Otherwise, with several rows of X,
+  // each piece's sum is formed once by the thread that stages it (at one row
+  // the per-piece sums are cheaper inside each wave).
+  constexpr bool GS = FOLD;
+  constexpr bool XB = MT > 1 && !FOLD;
+  __shared__ float xb[XB ? MT : 1][kQ8Threads];  // -128 * 2^-24 * (sum of a piece's 8 x)
+  // -128 * 2^-24 / 16 * (sum of x over 128-row block 4 i + j of the chunk)
+  // at [m][j][i]: quarter j reads its 8 steps' values contiguously.
+  __shared__ float gs[GS ? MT : 1][4][kQ8Steps];
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  // Workgroups b and b + 8 run on the same XCD (dispatch is round-robin over
+  // the 8 XCDs).  When the panel count allows, they take neighbouring panels,
+  // which share the 128-byte lines of the fp32 scale rows, so each line is
+  // fetched into one XCD's L2 only.
+  const int bid = blockIdx.x;
+  const int panel = (gridDim.x % 16 == 0) ? (bid & ~15) + 2 * (bid & 7) + ((bid >> 3) & 1) : bid;
+  const int q = panel * 8 + wave;  // this wave's column pair
+  const int KB = K / 8;            // pieces per pair
+
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wp, K * N);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, M * K * 2);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, (K / G) * N * 4);
+
+  float tot[MT][2];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) tot[m][0] = tot[m][1] = 0.0f;
+
+  for (int r0 = 0; r0 < K; r0 += kQ8Chunk) {
+    const int b0 = r0 / 8;
+    // Activations first (rows r0 + 8t .. + 7; zero past K and for m >= M),
+    // then the scales, then the weight stream, so waiting for the activations
+    // leaves the rest in flight.
+    u32x4 xg[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      xg[m] = __builtin_amdgcn_raw_buffer_load_b128(
+          xr, (m < M && r0 + 8 * t < K) ? (m * K + r0 + 8 * t) * 2 : kOutOfRange, 0, 0);
+    constexpr int NS = FOLD ? 1 : kQ8Steps;  // scale loads per lane per chunk
+    float fs = 0.0f;
+    u32x2 sc[NS];
+    if constexpr (FOLD) {
+      // Lane l's scale: step (l % 16) / 2, column l % 2, the group of rows
+      // r0 + 512 step + 128 (l / 16) .. + 127.
+      const int row = r0 + 512 * ((lane & 15) >> 1) + 128 * (lane >> 4);
+      fs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                         sr, row < K ? ((row >> gsh) * N + 2 * q + (lane & 1)) * 4 : kOutOfRange,
+                                         0, 0));
+    } else {
+#pragma unroll
+      for (int i = 0; i < kQ8Steps; ++i) {
+        const int b = b0 + 64 * i + lane;
+        sc[i] = __builtin_amdgcn_raw_buffer_load_b64(
+            sr, b < KB ? (((8 * b) / G) * N + 2 * q) * 4 : kOutOfRange, 0, 0);
+      }
+    }
+    u32x4 w[kQ8Steps];
+#pragma unroll
+    for (int i = 0; i < kQ8Steps; ++i) {
+      const int b = b0 + 64 * i + lane;
+      w[i] = buffer_stream(wr, b < KB ? (q * KB + b) * 16 : kOutOfRange);
+    }
+    wait_vmcnt<kQ8Steps + NS>();  // the activations have landed
+    if (r0 > 0) lds_barrier();     // every wave is done with the previous chunk
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      xs[m][t] = xg[m];
+      if constexpr (XB) xb[m][t] = q8_piece_bias(xg[m]);
+      if constexpr (GS) {
+        // Piece t lies in block t / 16: the 16 lanes of a row (fixed order).
+        float ps = q8_piece_bias(xg[m]) * (1.0f / 16.0f);
+        ps += q8_row_rotate<8>(ps);
+        ps += q8_row_rotate<4>(ps);
+        ps += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, ps), 0x4E, 0xF, 0xF, true));
+        ps += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, ps), 0xB1, 0xF, 0xF, true));
+        if ((t & 15) == 0) gs[m][(t >> 4) & 3][t >> 6] = ps;
+      }
+    }
+    lds_barrier();
+
+    // The activations of every step and their piece sums first: they do
+    // not wait for the weights.
+    u32x4 xv[kQ8Steps][MT];
+    float bias[kQ8Steps][MT];
+#pragma unroll
+    for (int i = 0; i < kQ8Steps; ++i)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        xv[i][m] = xs[m][64 * i + lane];
+        if constexpr (XB) bias[i][m] = xb[m][64 * i + lane];
+      }
+    if constexpr (GS) {
+#pragma unroll
+      for (int i = 0; i < kQ8Steps; ++i)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) bias[i][m] = gs[m][lane >> 4][i];
+    } else if constexpr (!XB) {
+#pragma unroll
+      for (int i = 0; i < kQ8Steps; ++i)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) bias[i][m] = q8_piece_bias(xv[i][m]);
+    }
+    // The quarter's 16 scales in every lane (FOLD): scale of step i,
+    // column c at fsq[2i + c].
+    float fsq[2 * kQ8Steps];
+    if constexpr (FOLD) q8_row_all(fs, fsq);
+#pragma unroll
+    for (int i = 0; i < kQ8Steps; ++i) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        float a0 = bias[i][m], a1 = bias[i][m];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          a0 = dot2(as_h2(q8_col_pair<0>(w[i][d])), as_h2(xv[i][m][d]), a0);
+          a1 = dot2(as_h2(q8_col_pair<1>(w[i][d])), as_h2(xv[i][m][d]), a1);
+        }
+        const float s0 = FOLD ? fsq[2 * i] : as_f32(sc[i][0]);
+        const float s1 = FOLD ? fsq[2 * i + 1] : as_f32(sc[i][1]);
+        tot[m][0] = __builtin_fmaf(a0, s0, tot[m][0]);
+        tot[m][1] = __builtin_fmaf(a1, s1, tot[m][1]);
+      }
+    }
+  }
+
+  {
+    // Value j = 2m + c per lane, reduced over the whole wave.
+    constexpr int V = 2 * MT;
+    float r[V];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      r[2 * m] = tot[m][0];
+      r[2 * m + 1] = tot[m][1];
+    }
+    bfly<V, 5, 0>(r, lane);
+    bool owner;
+    const int base = bfly_base<V, 0>(lane, owner);
+    constexpr int LEFT = bfly_left<V, 0>();
+    if (owner) {
+#pragma unroll
+      for (int j = 0; j < LEFT; ++j) {
+        const int m = (base + j) >> 1, c = (base + j) & 1;
+        if (m < M) Y[(size_t)m * N + 2 * q + c] = (_Float16)(r[j] * kTwo24);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Bit-exact check of the packed layout: every piece through q8_col_pair,
 // written back as signed codes in [K, N].
+// ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void q8_unpack_kernel(const uint8_t* __restrict__ Wp,
                                                              int8_t* __restrict__ codes, int K,
                                                              int N) {
-  const int KT = q8_tiles_per_panel(K);
+  const int KB = K / 8;
   const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= (size_t)(N / 16) * KT * 64) return;
-  const int l = (int)(idx % 64);
-  const size_t tile = idx / 64;
-  const int b = (int)(tile % KT), p = (int)(tile / KT);
-  const int col = 16 * p + (l & 15), h = l >> 4;
+  if (idx >= (size_t)(N / 2) * KB) return;
+  const int q = (int)(idx / KB), b = (int)(idx % KB);
   const u32x4 w = *reinterpret_cast<const u32x4*>(Wp + idx * 16);
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    const uint32_t pr[2] = {q8_byte_pair<0>(w[d]), q8_byte_pair<1>(w[d])};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 64 * b + 32 * (d >> 1) + 8 * h + 4 * (d & 1) + e;
-      if (row < K) codes[(size_t)row * N + col] = (int8_t)((int)((pr[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) - 128);
-    }
+    const uint32_t c0 = q8_col_pair<0>(w[d]), c1 = q8_col_pair<1>(w[d]);
+    const size_t row = (size_t)8 * b + 2 * d;
+    codes[row * N + 2 * q] = (int8_t)((int)(c0 & 0xFFFFu) - 128);
+    codes[(row + 1) * N + 2 * q] = (int8_t)((int)(c0 >> 16) - 128);
+    codes[row * N + 2 * q + 1] = (int8_t)((int)(c1 & 0xFFFFu) - 128);
+    codes[(row + 1) * N + 2 * q + 1] = (int8_t)((int)(c1 >> 16) - 128);
   }
 }
 
 // ---------------------------------------------------------------------------
-// The fused product.
+// The product at 3 .. 16 rows of X, on the matrix cores.
+//
+// A workgroup of 8 waves owns a panel (8 column pairs, 16 columns); of every
+// 4096-row chunk wave w takes rows 512 w .. 512 w + 511.  Its load i brings
+// rows 64 i .. 64 i + 63 of that range for all 8 pairs: lane l the piece
+// 8 i + l % 8 of pair l / 8, so each instruction reads 8 whole 128-byte
+// runs.  The wave writes the loaded KB into its own LDS slot and reads it
+// back in the operand order of v_mfma_f32_16x16x32_f16: for step 2 i + s,
+// lane l (column l % 16, rows 8 (l / 16) .. + 7 of the step) takes the piece
+// 4 s + l / 16 of pair (l % 16) / 2, and one v_perm_b32 per word keeps its
+// column's two code bytes as an fp16 pair (the subnormals u 2^-24).  X
+// (up to 16 rows) is the A operand, read from the LDS copy of the chunk (row
+// l % 16 of the operand; rows past M are zero).  The offset 128 comes out per
+// chain of steps inside one group: the staging threads form
+// -128 2^-24 sum(x) over each chain's rows once per workgroup, and a chain's
+// sums take it before the scale: total += (chain sums + offset) * scale, in
+// fp32, in units of 2^-24.  The 8 waves' totals are added in a fixed order.
 // ---------------------------------------------------------------------------
 namespace {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+
+// LDS row of X: a chunk of fp16 plus 16 bytes, so that the 16 rows an
+// operand read takes start on different banks.
+constexpr int kQ8RowBytes = 2 * kQ8Chunk + 16;
+constexpr int kQ8Waves = kQ8Threads / 64;
 
 // DPP move of a float across lanes (full masks: every lane is written).
 template <int CTRL>
@@ -146,25 +348,28 @@ template <int MT, int CL>
 __global__ __launch_bounds__(kQ8Threads) void q8_mfma_kernel(
     const _Float16* __restrict__ X, const uint8_t* __restrict__ Wp,
     const float* __restrict__ scales, _Float16* __restrict__ Y, int M, int K, int N, int G,
-    int KT) {
-  constexpr int NC = kQ8Steps / CL;            // chains per wave per chunk
+    int gsh) {
+  constexpr int NSTEP = 16;                    // 32-row steps per wave per chunk
+  constexpr int NC = NSTEP / CL;               // chains per wave per chunk
   constexpr int NG = kQ8Chunk / (32 * CL);     // chains per chunk
   constexpr int RR = MT < 4 ? MT : 4;          // accumulator rows that can hold rows of X
   static_assert(CL == 1 || CL == 2 || CL == 4 || CL == 8 || CL == 16, "chain length");
+  static_assert(kQ8Waves == 8 && kQ8Chunk == 512 * kQ8Waves, "a wave takes 512 rows of a chunk");
   __shared__ __attribute__((aligned(16))) unsigned char xs[MT * kQ8RowBytes];  // the chunk of X
   __shared__ float cs[NG][16];  // [chain][row of X]: -128 2^-24 sum of x over the chain's rows
-  __shared__ float red[kQ8Waves][MT][16];
+  // Per wave: two 1 KB slots for the operand reorder; its totals at the end.
+  __shared__ __attribute__((aligned(16))) unsigned char tr[kQ8Waves][2048];
 
   const int t = threadIdx.x, lane = t & 63, h = lane >> 4, j = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   // Workgroups b and b + 8 run on the same XCD (dispatch is round-robin over
   // the 8 XCDs).  When the panel count allows, they take neighbouring panels,
-  // which share the 128-byte lines of the fp32 scale rows, so each line is
-  // fetched into one XCD's L2 only.
+  // which share the 128-byte lines of the fp32 scale rows.
   const int bid = blockIdx.x;
   const int panel = (gridDim.x % 16 == 0) ? (bid & ~15) + 2 * (bid & 7) + ((bid >> 3) & 1) : bid;
+  const int KB = K / 8;  // pieces per pair
 
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wp, (N / 16) * KT * 1024);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wp, K * N);
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, M * K * 2);
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, (K / G) * N * 4);
 
@@ -172,11 +377,14 @@ __global__ __launch_bounds__(kQ8Threads) void q8_mfma_kernel(
   float tot[RR];
 #pragma unroll
   for (int r = 0; r < RR; ++r) tot[r] = 0.0f;
-  const int arow = (MT > 1 && j < MT) ? j : 0;  // row of X in this lane's A operand
+  const int arow = j < MT ? j : 0;                           // row of X in this lane's A operand
+  const int lpair = 8 * panel + (lane >> 3);                 // pair this lane loads
+  const uint32_t sel = (j & 1) ? 0x0c030c02u : 0x0c010c00u;  // its operand column in a piece
+  unsigned char* mytr = &tr[wave][0];
 
   for (int r0 = 0; r0 < K; r0 += kQ8Chunk) {
     // Activations first (rows r0 + 8t .. + 7; zero past K and for m >= M),
-    // then the scales, then the weight tiles, so waiting for the activations
+    // then the scales, then the weight, so waiting for the activations
     // leaves the rest in flight.
     u32x4 xg[MT];
 #pragma unroll
@@ -187,17 +395,19 @@ __global__ __launch_bounds__(kQ8Threads) void q8_mfma_kernel(
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int row = r0 + 512 * wave + 32 * CL * c;
+      const int g = gsh >= 0 ? row >> gsh : row / G;  // gsh = log2 G, or -1
       sc[c] = as_f32(__builtin_amdgcn_raw_buffer_load_b32(
-          sr, row < K ? ((row / G) * N + 16 * panel + j) * 4 : kOutOfRange, 0, 0));
+          sr, row < K ? (g * N + 16 * panel + j) * 4 : kOutOfRange, 0, 0));
     }
-    u32x4 wv[kQ8Tiles];
+    const int b0 = (r0 + 512 * wave) / 8;
+    u32x4 wv[8];
 #pragma unroll
-    for (int i = 0; i < kQ8Tiles; ++i) {
-      const int b = r0 / 64 + kQ8Tiles * wave + i;
-      wv[i] = buffer_stream(wr, b < KT ? (panel * KT + b) * 1024 + 16 * lane : kOutOfRange);
+    for (int i = 0; i < 8; ++i) {
+      const int b = b0 + 8 * i + (lane & 7);
+      wv[i] = buffer_stream(wr, b < KB ? (lpair * KB + b) * 16 : kOutOfRange);
     }
-    wait_vmcnt<NC + kQ8Tiles>();  // the activations have landed
-    if (r0 > 0) lds_barrier();     // every wave is done with the previous chunk
+    wait_vmcnt<NC + 8>();       // the activations have landed
+    if (r0 > 0) lds_barrier();  // every wave is done with the previous chunk
     // Stage X; the chain sums: thread t's 8 rows lie in chain t / (4 CL),
     // whose 4 CL threads are consecutive lanes (fixed-order DPP sums).
 #pragma unroll
@@ -208,8 +418,8 @@ __global__ __launch_bounds__(kQ8Threads) void q8_mfma_kernel(
 #pragma unroll
       for (int d = 0; d < 4; ++d) ps = dot2(as_h2(xg[m][d]), ones, ps);
       ps *= -128.0f / kTwo24;
-      ps += q8_dpp<0xB1>(ps);                        // quad_perm 1 0 3 2
-      ps += q8_dpp<0x4E>(ps);                        // quad_perm 2 3 0 1
+      ps += q8_dpp<0xB1>(ps);                          // quad_perm 1 0 3 2
+      ps += q8_dpp<0x4E>(ps);                          // quad_perm 2 3 0 1
       if constexpr (CL >= 2) ps += q8_dpp<0x12C>(ps);  // row_ror:12, lane l + 4
       if constexpr (CL >= 4) ps += q8_dpp<0x128>(ps);  // row_ror:8
       if constexpr (CL >= 8) ps += __shfl_xor(ps, 16);
@@ -220,9 +430,9 @@ __global__ __launch_bounds__(kQ8Threads) void q8_mfma_kernel(
 
     // Every step's A operand before any weight is waited for (the
     // scheduling barrier keeps the compiler from sinking the reads).
-    h8 av[kQ8Steps];
+    h8 av[NSTEP];
 #pragma unroll
-    for (int st = 0; st < kQ8Steps; ++st)
+    for (int st = 0; st < NSTEP; ++st)
       av[st] = *reinterpret_cast<const h8*>(xs + arow * kQ8RowBytes + 2 * (512 * wave + 32 * st + 8 * h));
     __builtin_amdgcn_sched_barrier(0);
 
@@ -232,13 +442,19 @@ __global__ __launch_bounds__(kQ8Threads) void q8_mfma_kernel(
     f32x4 c0 = {0.0f, 0.0f, 0.0f, 0.0f}, c1 = c0;
     const f32x4 zero4 = c0;
 #pragma unroll
-    for (int i = 0; i < kQ8Tiles; ++i) {
+    for (int i = 0; i < 8; ++i) {
+      // The loaded KB into this wave's slot (LDS accesses of one wave run in
+      // order; the wait makes every lane's write visible to the reads).
+      unsigned char* slot = mytr + 1024 * (i & 1);
+      *reinterpret_cast<u32x4*>(slot + 16 * lane) = wv[i];
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      asm volatile("" ::: "memory");
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int st = 2 * i + s;
-        const uint32_t d0 = wv[i][2 * s], d1 = wv[i][2 * s + 1];
-        const u32x4 bw = {q8_byte_pair<0>(d0), q8_byte_pair<1>(d0), q8_byte_pair<0>(d1),
-                          q8_byte_pair<1>(d1)};
+        const u32x4 pc = *reinterpret_cast<const u32x4*>(slot + 16 * (8 * (j >> 1) + 4 * s + h));
+        const u32x4 bw = {__builtin_amdgcn_perm(0u, pc[0], sel), __builtin_amdgcn_perm(0u, pc[1], sel),
+                          __builtin_amdgcn_perm(0u, pc[2], sel), __builtin_amdgcn_perm(0u, pc[3], sel)};
         const h8 b = __builtin_bit_cast(h8, bw);
         const int pos = st % CL;
         if (pos == 0)
@@ -259,55 +475,73 @@ __global__ __launch_bounds__(kQ8Threads) void q8_mfma_kernel(
           }
         }
       }
+      asm volatile("" ::: "memory");
     }
   }
 
-  // The 8 waves' totals, added in wave order.
+  // The 8 waves' totals (each in its own slot), added as a fixed-order
+  // pairwise tree ((w0 + w1) + (w2 + w3)) + ((w4 + w5) + (w6 + w7)).
+  float* red = reinterpret_cast<float*>(mytr);  // [MT][16]
 #pragma unroll
   for (int r = 0; r < RR; ++r) {
     const int row = 4 * h + r;
-    if (row < MT) red[wave][row][j] = tot[r];
+    if (row < MT) red[row * 16 + j] = tot[r];
   }
   __syncthreads();
   if (t < MT * 16) {
     const int row = t >> 4, col = t & 15;
-    float s = red[0][row][col];
+    float v[kQ8Waves];
 #pragma unroll
-    for (int w = 1; w < kQ8Waves; ++w) s += red[w][row][col];
+    for (int w = 0; w < kQ8Waves; ++w) v[w] = reinterpret_cast<const float*>(&tr[w][0])[row * 16 + col];
+    const float s = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
     if (row < M) Y[(size_t)row * N + 16 * panel + col] = (_Float16)(s * kTwo24);
   }
 }
 
 hipError_t launch_q8_prepack(const int8_t* W, void* packed, int K, int N, hipStream_t s) {
-  const size_t total = (size_t)(N / 16) * q8_tiles_per_panel(K) * 64;
+  const size_t total = (size_t)(N / 2) * (K / 8);
   hipLaunchKernelGGL(q8_prepack_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, s, W, reinterpret_cast<uint8_t*>(packed), K, N);
+                     dim3(kThreads), 0, s, W, reinterpret_cast<uint32_t*>(packed), K, N);
   return hipGetLastError();
 }
 
 hipError_t launch_q8_unpack(const void* packed, int8_t* codes, int K, int N, hipStream_t s) {
-  const size_t total = (size_t)(N / 16) * q8_tiles_per_panel(K) * 64;
+  const size_t total = (size_t)(N / 2) * (K / 8);
   hipLaunchKernelGGL(q8_unpack_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)),
                      dim3(kThreads), 0, s, reinterpret_cast<const uint8_t*>(packed), codes, K, N);
+  return hipGetLastError();
+}
+
+template <int MT, bool FOLD = false>
+static hipError_t launch_q8_t(const void* X, const void* packed, const float* scales, void* Y,
+                              int M, int K, int N, int G, hipStream_t s) {
+  int gsh = 0;
+  while ((1 << gsh) < G) ++gsh;
+  hipLaunchKernelGGL((q8_pair_kernel<MT, FOLD>), dim3(N / 16), dim3(kQ8Threads), 0, s,
+                     reinterpret_cast<const _Float16*>(X), reinterpret_cast<const uint8_t*>(packed),
+                     scales, reinterpret_cast<_Float16*>(Y), M, K, N, G, gsh);
   return hipGetLastError();
 }
 
 template <int MT>
 static hipError_t launch_q8_rows(const void* X, const void* packed, const float* scales, void* Y,
                                  int M, int K, int N, int G, hipStream_t s) {
-  const int KT = q8_tiles_per_panel(K);
   const bool pow2 = (G & (G - 1)) == 0;
   const int CL = !pow2 ? 1 : G >= 512 ? 16 : G / 32;
+  int gsh = -1;
+  if (pow2)
+    for (gsh = 0; (1 << gsh) < G; ++gsh) {
+    }
   const dim3 grid(N / 16), block(kQ8Threads);
   const _Float16* x = reinterpret_cast<const _Float16*>(X);
   const uint8_t* w = reinterpret_cast<const uint8_t*>(packed);
   _Float16* y = reinterpret_cast<_Float16*>(Y);
   switch (CL) {
-    case 16: hipLaunchKernelGGL((q8_mfma_kernel<MT, 16>), grid, block, 0, s, x, w, scales, y, M, K, N, G, KT); break;
-    case 8: hipLaunchKernelGGL((q8_mfma_kernel<MT, 8>), grid, block, 0, s, x, w, scales, y, M, K, N, G, KT); break;
-    case 4: hipLaunchKernelGGL((q8_mfma_kernel<MT, 4>), grid, block, 0, s, x, w, scales, y, M, K, N, G, KT); break;
-    case 2: hipLaunchKernelGGL((q8_mfma_kernel<MT, 2>), grid, block, 0, s, x, w, scales, y, M, K, N, G, KT); break;
-    default: hipLaunchKernelGGL((q8_mfma_kernel<MT, 1>), grid, block, 0, s, x, w, scales, y, M, K, N, G, KT); break;
+    case 16: hipLaunchKernelGGL((q8_mfma_kernel<MT, 16>), grid, block, 0, s, x, w, scales, y, M, K, N, G, gsh); break;
+    case 8: hipLaunchKernelGGL((q8_mfma_kernel<MT, 8>), grid, block, 0, s, x, w, scales, y, M, K, N, G, gsh); break;
+    case 4: hipLaunchKernelGGL((q8_mfma_kernel<MT, 4>), grid, block, 0, s, x, w, scales, y, M, K, N, G, gsh); break;
+    case 2: hipLaunchKernelGGL((q8_mfma_kernel<MT, 2>), grid, block, 0, s, x, w, scales, y, M, K, N, G, gsh); break;
+    default: hipLaunchKernelGGL((q8_mfma_kernel<MT, 1>), grid, block, 0, s, x, w, scales, y, M, K, N, G, gsh); break;
   }
   return hipGetLastError();
 }
@@ -320,16 +554,20 @@ hipError_t launch_q8_group(const void* X, const void* packed, const float* scale
                            void* ws, int M, int K, int N, int G, hipStream_t s) {
   if (M >= kQ8GemmMinRows && q8_gemm_supported(M, K, N, G))
     return launch_q8_gemm(X, packed, scales, Y, ws, M, K, N, G, s);
-  // Up to 16 rows of X per launch over the same weight.
+  // Up to 16 rows of X per launch over the same weight: one or two rows on
+  // the v_dot2 pair kernel, 3 .. 16 on the matrix cores.
   for (int m0 = 0; m0 < M; m0 += kQ8PassRows) {
     const int mc = (M - m0) < kQ8PassRows ? (M - m0) : kQ8PassRows;
     const void* Xc = reinterpret_cast<const char*>(X) + (size_t)m0 * K * 2;
     void* Yc = reinterpret_cast<char*>(Y) + (size_t)m0 * N * 2;
     hipError_t e;
+    const bool fold = G >= 128 && (G & (G - 1)) == 0;
     if (mc == 1)
-      e = launch_q8_rows<1>(Xc, packed, scales, Yc, mc, K, N, G, s);
+      e = fold ? launch_q8_t<1, true>(Xc, packed, scales, Yc, mc, K, N, G, s)
+               : launch_q8_t<1>(Xc, packed, scales, Yc, mc, K, N, G, s);
     else if (mc == 2)
-      e = launch_q8_rows<2>(Xc, packed, scales, Yc, mc, K, N, G, s);
+      e = fold ? launch_q8_t<2, true>(Xc, packed, scales, Yc, mc, K, N, G, s)
+               : launch_q8_t<2>(Xc, packed, scales, Yc, mc, K, N, G, s);
     else if (mc <= 4)
       e = launch_q8_rows<4>(Xc, packed, scales, Yc, mc, K, N, G, s);
     else if (mc <= 8)

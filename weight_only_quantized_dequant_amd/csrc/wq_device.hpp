@@ -99,12 +99,13 @@ __device__ __forceinline__ uint32_t q3_window(uint32_t w0, uint32_t w1, uint32_t
 // Subnormal-pair extractors (the fast path).  Values are in units of 2^-24.
 // ---------------------------------------------------------------------------
 
-// int8, stored biased as u = q + 128: a word holds four codes of one column
-// in consecutive bytes.  HI selects bytes 2 and 3 (else 0 and 1); the result
-// is the two codes as the fp16 pair (u_lo, u_hi) * 2^-24, one v_perm_b32.
-template <int HI>
-__device__ __forceinline__ uint32_t q8_byte_pair(uint32_t w) {
-  return __builtin_amdgcn_perm(0u, w, HI ? 0x0c030c02u : 0x0c010c00u);
+// int8, stored biased as u = q + 128, in the column-pair layout: byte 0 and
+// byte 1 of word w are two consecutive rows of one column, bytes 2 and 3 the
+// same rows of the next column.  C selects the column; the result is its two
+// rows as (u_lo, u_hi) * 2^-24, one v_perm_b32.
+template <int C>
+__device__ __forceinline__ uint32_t q8_col_pair(uint32_t w) {
+  return __builtin_amdgcn_perm(0u, w, C ? 0x0c030c02u : 0x0c010c00u);
 }
 
 // 3-bit: pair P of q3_pair(P) as (c_a * 2^pa, c_b * 2^pb) * 2^-24.
