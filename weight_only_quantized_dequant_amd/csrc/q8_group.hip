@@ -443,11 +443,11 @@ __global__ __launch_bounds__(kQ8Threads) void q8_mfma_kernel(
     const f32x4 zero4 = c0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      // The loaded KB into this wave's slot (LDS accesses of one wave run in
-      // order; the wait makes every lane's write visible to the reads).
+      // The loaded KB into this wave's slot.  The LDS executes one wave's
+      // accesses in issue order, so the reads below see every lane's write
+      // (and a slot is rewritten only after its reads) without a wait.
       unsigned char* slot = mytr + 1024 * (i & 1);
       *reinterpret_cast<u32x4*>(slot + 16 * lane) = wv[i];
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
