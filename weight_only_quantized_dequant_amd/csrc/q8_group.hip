@@ -330,6 +330,21 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 constexpr int kQ8RowBytes = 2 * kQ8Chunk + 16;
 constexpr int kQ8Waves = kQ8Threads / 64;
 
+// s_waitcnt vmcnt(left) for a count known once the loop around it is
+// unrolled.
+__device__ __forceinline__ void wait_vmcnt_dyn(int left) {
+  switch (left) {
+    case 7: wait_vmcnt<7>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    default: wait_vmcnt<0>(); break;
+  }
+}
+
 // DPP move of a float across lanes (full masks: every lane is written).
 template <int CTRL>
 __device__ __forceinline__ float q8_dpp(float x) {
@@ -357,8 +372,15 @@ __global__ __launch_bounds__(kQ8Threads) void q8_mfma_kernel(
   static_assert(kQ8Waves == 8 && kQ8Chunk == 512 * kQ8Waves, "a wave takes 512 rows of a chunk");
   __shared__ __attribute__((aligned(16))) unsigned char xs[MT * kQ8RowBytes];  // the chunk of X
   __shared__ float cs[NG][16];  // [chain][row of X]: -128 2^-24 sum of x over the chain's rows
-  // Per wave: two 1 KB slots for the operand reorder; its totals at the end.
-  __shared__ __attribute__((aligned(16))) unsigned char tr[kQ8Waves][2048];
+  // Per wave: the slots of the operand reorder (its totals at the end).  At
+  // 8 rows of X (DL) the loads go straight to LDS, one 1 KB slot each (the
+  // compiler then waits for all eight before the first read; measured
+  // 6.17 -> 5.98 us at M = 8, but 5.19 -> 5.36 at M = 4); otherwise they land
+  // in registers and pass through two slots (at 16 rows the LDS holds no
+  // eight).
+  constexpr bool DL = MT == 8;
+  constexpr int SLOTS = DL ? 8 : 2;
+  __shared__ __attribute__((aligned(1024))) unsigned char tr[kQ8Waves][SLOTS * 1024];
 
   const int t = threadIdx.x, lane = t & 63, h = lane >> 4, j = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -400,11 +422,16 @@ __global__ __launch_bounds__(kQ8Threads) void q8_mfma_kernel(
           sr, row < K ? (g * N + 16 * panel + j) * 4 : kOutOfRange, 0, 0));
     }
     const int b0 = (r0 + 512 * wave) / 8;
-    u32x4 wv[8];
+    u32x4 wv[DL ? 1 : 8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int b = b0 + 8 * i + (lane & 7);
-      wv[i] = buffer_stream(wr, b < KB ? (lpair * KB + b) * 16 : kOutOfRange);
+      const int off = b < KB ? (lpair * KB + b) * 16 : kOutOfRange;
+      if constexpr (DL)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            wr, (__attribute__((address_space(3))) void*)(mytr + 1024 * i), 16, off, 0, 0, 2);
+      else
+        wv[i] = buffer_stream(wr, off);
     }
     wait_vmcnt<NC + 8>();       // the activations have landed
     if (r0 > 0) lds_barrier();  // every wave is done with the previous chunk
@@ -446,8 +473,12 @@ __global__ __launch_bounds__(kQ8Threads) void q8_mfma_kernel(
       // The loaded KB into this wave's slot.  The LDS executes one wave's
       // accesses in issue order, so the reads below see every lane's write
       // (and a slot is rewritten only after its reads) without a wait.
-      unsigned char* slot = mytr + 1024 * (i & 1);
-      *reinterpret_cast<u32x4*>(slot + 16 * lane) = wv[i];
+      unsigned char* slot = mytr + 1024 * (DL ? i : (i & 1));
+      if constexpr (DL) {
+        wait_vmcnt_dyn(7 - i);  // load i has reached LDS (the later loads may not)
+      } else {
+        *reinterpret_cast<u32x4*>(slot + 16 * lane) = wv[i];
+      }
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
