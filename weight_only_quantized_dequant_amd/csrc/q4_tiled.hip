@@ -19,8 +19,9 @@
 //     32 s + 8 (l / 16) .. +7 in the order 0 4 1 5 2 6 3 7 (the order of the
 //     codes in a packed word).  A wave stages one row of X in LDS with
 //     coalesced loads, reads 64 octets of original row numbers from the
-//     forward row table, and gathers from LDS.  Rows of X past M and padding
-//     rows past K are zero.
+//     forward row table, and gathers from LDS.  Padding rows past K are
+//     zero; rows of the last tile past M are not written, and the GEMM's
+//     loads of them fall out of range.
 // (2) The GEMM.  A workgroup takes a run of at most 3 panels and every row
 //     of the launch (one to four 16-row tiles); each of its 8 waves walks a
 //     contiguous share of the 128-row blocks with a ring of blocks in
@@ -45,7 +46,8 @@ namespace wq {
 
 constexpr int kQTThreads = 512;
 constexpr int kQTWaves = kQTThreads / 64;
-constexpr int kQTMaxRun = 3;    // panels per workgroup at most
+constexpr int kQTMaxRun = 3;    // panels per workgroup at most, one row group
+constexpr int kQTWideRun = 6;   // the same with two row groups of two tiles
 
 int q4_tiled_kp(int K) { return (K + kQ4Block - 1) / kQ4Block * kQ4Block; }
 
@@ -56,13 +58,13 @@ size_t q4_tiled_workspace_bytes(int M, int K) {
   return q4_xo_bytes((M + 15) / 16, q4_tiled_kp(K));
 }
 
-// (1) One wave per (row m of the padded tiles, range r of 64 octets of
+// (1) One wave per (row m < M, range r of 64 octets of
 // group-order rows).  The wave copies row m of X into LDS (coalesced), then
 // lane l takes octet o = 64 r + l (group-order rows 8 o .. 8 o + 7): their
 // original rows from the forward table (one 16-byte load, issued first),
 // the 8 values read from LDS, and one 16-byte store of the operand piece
-// (step o / 4, lane m % 16 + 16 (o % 4) of tile m / 16).  Rows m >= M and
-// padding rows give zeros.
+// (step o / 4, lane m % 16 + 16 (o % 4) of tile m / 16).  Padding rows give
+// zeros.
 constexpr int kQXThreads = 64;
 constexpr int kQXBatch = 8 * 64 * 8;  // halves of X per batch: 8 pieces of 16 bytes per lane
 __global__ __launch_bounds__(kQXThreads) void q4_xgather_kernel(const _Float16* __restrict__ X,
@@ -106,9 +108,11 @@ __global__ __launch_bounds__(kQXThreads) void q4_xgather_kernel(const _Float16* 
   }
 }
 
-// (2) MB: 16-row tiles (M <= 16 MB); CPB: groups per block (1 for groups of
-// 128 rows or more, else 128 / G); BD: blocks in flight per wave.
-template <int MB, int CPB, bool ZP, int BD>
+// (2) MB: 16-row tiles per workgroup; CPB: groups per block (1 for groups of
+// 128 rows or more, else 128 / G); BD: blocks in flight per wave; RUN:
+// panels per workgroup at most.  blockIdx.y picks the row group: tiles
+// MB y .. MB y + MB - 1 of the launch's M rows.
+template <int MB, int CPB, bool ZP, int BD, int RUN>
 __global__ __launch_bounds__(kQTThreads) void q4_tiled_kernel(
     const _Float16* __restrict__ Xo, const uint8_t* __restrict__ Wp,
     const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
@@ -119,13 +123,19 @@ __global__ __launch_bounds__(kQTThreads) void q4_tiled_kernel(
   typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
   constexpr int MT = 16 * MB;
   constexpr int SPC = 4 / CPB;  // MFMA steps per group run
-  __shared__ float red[kQTMaxRun * kQTWaves * MT * 16];  // [run][wave][MT][16]
+  static_assert(4 * RUN * CPB <= 64, "a block's scale table is one 8-byte piece per lane");
+  __shared__ float red[RUN * kQTWaves * MT * 16];  // [run][wave][MT][16]
+  // This workgroup's row group.
+  M -= MT * (int)blockIdx.y;
+  mb0 += MB * (int)blockIdx.y;
+  Y += (size_t)MT * blockIdx.y * N;
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   // Each XCD (workgroups b = x mod 8) takes a contiguous range of panel runs,
   // so a 128-byte line of a scale or zero row (four panels) is fetched into
-  // one XCD's L2.
+  // one XCD's L2.  With gridDim.x a multiple of 8 the row groups of a run
+  // share the XCD too, and so the run's weight in that L2.
   const int G8 = gridDim.x % 8 == 0 ? gridDim.x / 8 : 0;
   const int run = G8 ? (int)(blockIdx.x % 8) * G8 + (int)(blockIdx.x / 8) : (int)blockIdx.x;
   const int p_begin = (int)((long long)run * npanels / gridDim.x);
@@ -141,30 +151,32 @@ __global__ __launch_bounds__(kQTThreads) void q4_tiled_kernel(
   const int xblock = 4 * mbt * 1024;  // X operand bytes of one block, all tiles
   const __amdgpu_buffer_rsrc_t xr =
       make_rsrc(reinterpret_cast<const char*>(Xo) + (size_t)bw0 * xblock, nbw * xblock);
-  __amdgpu_buffer_rsrc_t wr[kQTMaxRun];
+  __amdgpu_buffer_rsrc_t wr[RUN];
 #pragma unroll
-  for (int p = 0; p < kQTMaxRun; ++p) {
+  for (int p = 0; p < RUN; ++p) {
     const int panel = p < npr ? p_begin + p : 0;
     wr[p] = make_rsrc(Wp + ((size_t)panel * nb + bw0) * 1024, p < npr ? nbw * 1024 : 0);
   }
-  // Scale (and zero) rows of a block: CPB groups x 48 columns (the run's
+  // Scale (and zero) rows of a block: CPB groups x 16 RUN columns (the run's
   // panels) as one table, lane l holding halves 4 l .. 4 l + 3: group
-  // l / 12, columns 4 (l % 12) .. +3 of the run.  Lanes past the table, and
-  // columns past N (N % 4 == 0: a piece never straddles it), read zeros.
+  // l / (4 RUN), columns 4 (l % (4 RUN)) .. +3 of the run.  Lanes past the
+  // table, and columns past N (N % 4 == 0: a piece never straddles it), read
+  // zeros.
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, ngroups * N * 2);
   const __amdgpu_buffer_rsrc_t zr = make_rsrc(ZP ? zeros : scales, ngroups * N * 2);
-  const int tcol = p_begin * kQ4Panel + 4 * (lane % 12);
-  const bool tlive = lane < 12 * CPB && tcol < N;
-  const int tlane = (lane / 12) * N * 2 + tcol * 2;
+  const int tcol = p_begin * kQ4Panel + 4 * (lane % (4 * RUN));
+  const bool tlive = lane < 4 * RUN * CPB && tcol < N;
+  const int tlane = (lane / (4 * RUN)) * N * 2 + tcol * 2;
   // Where this lane finds its column's value for panel p, group c of a
-  // block: lane (48 c + 16 p + col) / 4, dword (col / 2) % 2, half col % 2.
+  // block: lane (16 RUN c + 16 p + col) / 4, dword (col / 2) % 2, half
+  // col % 2.
   const int hshift = 16 * (col & 1);
   const bool hi = (col & 2) != 0;
   const int xlane = lane * 16, wlane = lane * 16;
 
   struct Block {
     u32x4 a[4][MB];        // X operands: step, tile
-    u32x4 w[kQTMaxRun];    // weight words of the 4 steps, per panel
+    u32x4 w[RUN];          // weight words of the 4 steps, per panel
     u32x2v sc;             // this lane's piece of the scale table
     u32x2v zq;             // and of the zero table (ZP)
   };
@@ -173,17 +185,20 @@ __global__ __launch_bounds__(kQTThreads) void q4_tiled_kernel(
   // used), so every address stays inside the wave's ranges.  A wave with no
   // share has empty ranges: its loads all return zeros.
   auto clampj = [&](int jr) { return jr < nbw ? jr : (nbw > 0 ? nbw - 1 : 0); };
+  // Lanes whose row of the tile is past M read out of range (zeros, and no
+  // memory request): a partial tile moves only its live rows.
   auto load_x = [&](int jr, Block& q, int mb) {
     const int j = clampj(jr);
+    const int xo = 16 * mb + col < M ? xlane + mb * 1024 : kOutOfRange;
 #pragma unroll
     for (int st = 0; st < 4; ++st)
       q.a[st][mb] = __builtin_amdgcn_raw_buffer_load_b128(
-          xr, xlane + mb * 1024, (4 * j + st) * mbt * 1024 + mb0 * 1024, 0);
+          xr, xo, (4 * j + st) * mbt * 1024 + mb0 * 1024, 0);
   };
   auto load_wt = [&](int jr, Block& q) {
     const int j = clampj(jr);
 #pragma unroll
-    for (int p = 0; p < kQTMaxRun; ++p)
+    for (int p = 0; p < RUN; ++p)
       q.w[p] = __builtin_amdgcn_raw_buffer_load_b128(wr[p], wlane, j * 1024, 2);
     // First group of the block; the whole offset is in the lane's offset,
     // so groups past the last one (padding rows) fall out of range.
@@ -200,15 +215,15 @@ __global__ __launch_bounds__(kQTThreads) void q4_tiled_kernel(
   };
   // This lane's column value of panel p, group c from a block's table.
   auto table_value = [&](const u32x2v& tbl, int p, int c) {
-    const int src = ((48 * c + 16 * p + col) >> 2) * 4;
+    const int src = ((16 * RUN * c + 16 * p + col) >> 2) * 4;
     const uint32_t d0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)tbl[0]);
     const uint32_t d1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)tbl[1]);
     return (float)__builtin_bit_cast(_Float16, (uint16_t)((hi ? d1 : d0) >> hshift));
   };
 
-  f4 tot[kQTMaxRun][MB];
+  f4 tot[RUN][MB];
 #pragma unroll
-  for (int p = 0; p < kQTMaxRun; ++p)
+  for (int p = 0; p < RUN; ++p)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) tot[p][mb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
   // The constant operand of the row sums: -8 * 2^-24 (fp16 subnormal bits
@@ -234,7 +249,7 @@ __global__ __launch_bounds__(kQTThreads) void q4_tiled_kernel(
         c1[mb] = r;
       }
 #pragma unroll
-      for (int p = 0; p < kQTMaxRun; ++p) {
+      for (int p = 0; p < RUN; ++p) {
         h8 b[SPC];
 #pragma unroll
         for (int i = 0; i < SPC; ++i)
@@ -296,10 +311,10 @@ __global__ __launch_bounds__(kQTThreads) void q4_tiled_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
     for (int j = 0; j < nbw; ++j) {
-      h8 b[kQTMaxRun][4];
-      float sv[kQTMaxRun][CPB], nz[kQTMaxRun][CPB];
+      h8 b[RUN][4];
+      float sv[RUN][CPB], nz[RUN][CPB];
 #pragma unroll
-      for (int p = 0; p < kQTMaxRun; ++p) {
+      for (int p = 0; p < RUN; ++p) {
 #pragma unroll
         for (int st = 0; st < 4; ++st) b[p][st] = __builtin_bit_cast(h8, q4_mfma_operand(q.w[p][st]));
 #pragma unroll
@@ -320,7 +335,7 @@ __global__ __launch_bounds__(kQTThreads) void q4_tiled_kernel(
             c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, q.a[st][mb]), cop,
                                                         c1, 0, 0, 0);
 #pragma unroll
-          for (int p = 0; p < kQTMaxRun; ++p) {
+          for (int p = 0; p < RUN; ++p) {
             f4 r = c1;
             if constexpr (ZP) r *= nz[p][c];
 #pragma unroll
@@ -339,7 +354,7 @@ __global__ __launch_bounds__(kQTThreads) void q4_tiled_kernel(
   }
 
 #pragma unroll
-  for (int p = 0; p < kQTMaxRun; ++p)
+  for (int p = 0; p < RUN; ++p)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -360,51 +375,65 @@ __global__ __launch_bounds__(kQTThreads) void q4_tiled_kernel(
 }
 
 // Blocks in flight per wave: what fits the registers without spilling.
-// 0: the tile-by-tile stream of one block (three or four tiles).
-constexpr int q4_tiled_depth(int MB, int CPB, bool ZP) {
-  return (void)ZP, MB >= 3 ? 0 : (MB == 1 || CPB == 1) ? 2 : 1;
+// 0: the tile-by-tile stream of one block (three or four tiles).  One block
+// of a wide run is 14 KB per wave, so one in flight per wave already fills
+// the CU's request window.
+constexpr int q4_tiled_depth(int MB, int CPB, bool ZP, int RUN) {
+  return (void)ZP, MB >= 3 ? 0 : RUN > kQTMaxRun ? 1 : (MB == 1 || CPB == 1) ? 2 : 1;
 }
 // Tiles per launch at most: groups of 64 and 32 close 2 and 4 times per
 // block, and their extra row sums and scale values no longer fit the
 // registers with four (three) tiles.
 constexpr int q4_tiled_max_tiles(int G) { return G == 32 ? 2 : G == 64 ? 3 : 4; }
 
-template <int MB, int CPB, bool ZP>
+// RG row groups of MB tiles, runs of at most RUN panels: as many runs as
+// fill the CUs with RG workgroups each, fewer if a run would pass RUN.
+template <int MB, int CPB, bool ZP, int RUN, int RG>
 static hipError_t launch_q4_tiled_t(const _Float16* Xo, const uint8_t* Wp, const _Float16* scales,
                                     const _Float16* zeros, _Float16* Y, int M, int mb0, int mbt,
                                     int K, int N, int G, hipStream_t s) {
-  constexpr int BD = q4_tiled_depth(MB, CPB, ZP);
+  constexpr int BD = q4_tiled_depth(MB, CPB, ZP, RUN);
   const int nb = q4_tiled_kp(K) / kQ4Block, npanels = (N + kQ4Panel - 1) / kQ4Panel;
-  const int cus = device_cus();
+  const int cus = device_cus() / RG;
   int grid = npanels < cus ? npanels : cus;
-  if ((npanels + grid - 1) / grid > kQTMaxRun) grid = (npanels + kQTMaxRun - 1) / kQTMaxRun;
-  hipLaunchKernelGGL((q4_tiled_kernel<MB, CPB, ZP, BD>), dim3(grid), dim3(kQTThreads), 0, s, Xo,
-                     Wp, scales, zeros, Y, M, mb0, mbt, N, K / G, G, nb, npanels);
+  if ((npanels + grid - 1) / grid > RUN) grid = (npanels + RUN - 1) / RUN;
+  hipLaunchKernelGGL((q4_tiled_kernel<MB, CPB, ZP, BD, RUN>), dim3(grid, RG), dim3(kQTThreads), 0, s,
+                     Xo, Wp, scales, zeros, Y, M, mb0, mbt, N, K / G, G, nb, npanels);
   return hipGetLastError();
 }
 
-template <int MB, int CPB>
+template <int MB, int CPB, int RUN, int RG>
 static hipError_t launch_q4_tiled_z(const _Float16* Xo, const uint8_t* Wp, const _Float16* scales,
                                     const _Float16* zeros, _Float16* Y, int M, int mb0, int mbt,
                                     int K, int N, int G, hipStream_t s) {
-  return zeros ? launch_q4_tiled_t<MB, CPB, true>(Xo, Wp, scales, zeros, Y, M, mb0, mbt, K, N, G, s)
-               : launch_q4_tiled_t<MB, CPB, false>(Xo, Wp, scales, zeros, Y, M, mb0, mbt, K, N, G,
-                                                   s);
+  return zeros ? launch_q4_tiled_t<MB, CPB, true, RUN, RG>(Xo, Wp, scales, zeros, Y, M, mb0, mbt, K,
+                                                          N, G, s)
+               : launch_q4_tiled_t<MB, CPB, false, RUN, RG>(Xo, Wp, scales, zeros, Y, M, mb0, mbt, K,
+                                                           N, G, s);
 }
 
-template <int MB>
+// One to two tiles: one row group, runs of up to 3 panels.  Three or four
+// tiles with groups of 128 rows or more: two row groups of two tiles and
+// runs of up to 6 panels, so a workgroup reads half of X (X, read by every
+// workgroup, is most of what a workgroup loads at 64 rows); the two row
+// groups of a run take its weight from one L2.  (With groups of 64 the
+// second group per block does not fit the registers of a wide run.)
+template <int NT>
 static hipError_t launch_q4_tiled_mb(const _Float16* Xo, const uint8_t* Wp, const _Float16* scales,
                                      const _Float16* zeros, _Float16* Y, int M, int mb0, int mbt,
                                      int K, int N, int G, hipStream_t s) {
   if (G == 32) {
-    if constexpr (MB > q4_tiled_max_tiles(32)) return hipErrorInvalidValue;
-    else return launch_q4_tiled_z<MB, 4>(Xo, Wp, scales, zeros, Y, M, mb0, mbt, K, N, G, s);
+    if constexpr (NT > q4_tiled_max_tiles(32)) return hipErrorInvalidValue;
+    else return launch_q4_tiled_z<NT, 4, kQTMaxRun, 1>(Xo, Wp, scales, zeros, Y, M, mb0, mbt, K, N, G, s);
   }
   if (G == 64) {
-    if constexpr (MB > q4_tiled_max_tiles(64)) return hipErrorInvalidValue;
-    else return launch_q4_tiled_z<MB, 2>(Xo, Wp, scales, zeros, Y, M, mb0, mbt, K, N, G, s);
+    if constexpr (NT > q4_tiled_max_tiles(64)) return hipErrorInvalidValue;
+    else return launch_q4_tiled_z<NT, 2, kQTMaxRun, 1>(Xo, Wp, scales, zeros, Y, M, mb0, mbt, K, N, G, s);
   }
-  return launch_q4_tiled_z<MB, 1>(Xo, Wp, scales, zeros, Y, M, mb0, mbt, K, N, G, s);
+  if constexpr (NT <= 2)
+    return launch_q4_tiled_z<NT, 1, kQTMaxRun, 1>(Xo, Wp, scales, zeros, Y, M, mb0, mbt, K, N, G, s);
+  else
+    return launch_q4_tiled_z<2, 1, kQTWideRun, 2>(Xo, Wp, scales, zeros, Y, M, mb0, mbt, K, N, G, s);
 }
 
 hipError_t launch_q4_tiled(const void* X, const void* packed, const void* scales,
@@ -415,7 +444,9 @@ hipError_t launch_q4_tiled(const void* X, const void* packed, const void* scales
   const uint8_t* Wp = reinterpret_cast<const uint8_t*>(packed);
   const uint16_t* fwd = reinterpret_cast<const uint16_t*>(Wp + q4_fwd_table_offset(K, N));
   _Float16* Xo = reinterpret_cast<_Float16*>(ws);
-  hipLaunchKernelGGL(q4_xgather_kernel, dim3((Kp / 8 + 63) / 64, mbt * 16), dim3(kQXThreads),
+  // Rows past M are never read (the GEMM's loads of them fall out of range),
+  // so only the M live rows are gathered.
+  hipLaunchKernelGGL(q4_xgather_kernel, dim3((Kp / 8 + 63) / 64, M), dim3(kQXThreads),
                      (size_t)((K + kQXBatch - 1) / kQXBatch) * kQXBatch * 2, s,
                      reinterpret_cast<const _Float16*>(X), fwd, Xo, M, K, Kp, mbt);
   hipError_t e = hipGetLastError();
