@@ -714,6 +714,23 @@ def test_w8a8_workspace_contents_do_not_matter(wq):
             assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("M,K,N", [(256, 8192, 8192), (64, 8192, 4096)])
+def test_w8a8_alternating_inputs_share_a_workspace(wq, M, K, N):
+    # Two inputs in turn on one workspace, six calls each: the sum of the K
+    # slices must take this call's partials, never the previous call's (which
+    # hold the other input's values).
+    ds = [synth.gen_w8a8(M, K, N, seed=1410 + i) for i in range(2)]
+    args = [(cu(d["X"]), cu(d["Wq"]), cu(d["Sw"])) for d in ds]
+    refs = [wq.gemm_w8a8(*a, want_acc=True) for a in args]
+    ws = torch.zeros(wq.workspace_bytes(wq.WQ_OP_W8A8, M, K, N), dtype=torch.int8, device=dev())
+    for it in range(12):
+        got = wq.gemm_w8a8(*args[it % 2], want_acc=True, ws=ws)
+        for a, b in zip(refs[it % 2], got):
+            assert torch.equal(a, b), f"call {it}"
+    r = oracle.gemm_w8a8(ds[1]["X"], ds[1]["Wq"], ds[1]["Sw"])
+    assert np.array_equal(refs[1][3].cpu().numpy(), r["acc"])
+
+
 def test_w8a8_headline_bit_exact(wq):
     Y, r = _w8a8_check(wq, synth.gen_w8a8(256, 8192, 8192, seed=1400))
     # reported, not gated: distance of the bf16 result to the unrounded product
