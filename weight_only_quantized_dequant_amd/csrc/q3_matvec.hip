@@ -209,6 +209,38 @@ __global__ __launch_bounds__(THREADS) void q3_panel_kernel(
   // 3. Pairs into LDS in code-pair order (pre-scaled), and sum_k x[k].
   float my_sum = 0.0f;
   auto stage_block = [&](int blk, const u32x4* raw) {
+    if constexpr (F16) {
+      // The block's 32 halves sit in the 16 words raw[v][e] (word 4 v + e
+      // holds rows 2 (4 v + e) and 2 (4 v + e) + 1).  sum_k x[k]: v_dot2
+      // against ones.  Pair P: one v_perm_b32 takes row a's half into the
+      // low and row b's half into the high half, and one packed fp16
+      // multiply by the exact powers of two 2^(cls - pa - kQ3XShift),
+      // 2^(cls - pb - kQ3XShift) (one rounding, as the fp32 ldexp and the
+      // conversion to fp16 would give).
+      const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) my_sum = dot2(as_h2(raw[v][e]), ones, my_sum);
+      uint32_t pv[16];
+#pragma unroll
+      for (int P = 0; P < 16; ++P) {
+        const Q3Pair q = q3_pair(P);
+        const int cls = q3_class(P);
+        const uint32_t wa = raw[q.a / 8][(q.a / 2) % 4], wb = raw[q.b / 8][(q.b / 2) % 4];
+        // v_perm_b32(wb, wa, sel): selector bytes 0..3 pick wa's bytes,
+        // 4..7 wb's.
+        const uint32_t sel = (q.a & 1 ? 0x0302u : 0x0100u) | (q.b & 1 ? 0x07060000u : 0x05040000u);
+        const h2 m = {(_Float16)__builtin_ldexpf(1.0f, cls - q.pa - kQ3XShift),
+                      (_Float16)__builtin_ldexpf(1.0f, cls - q.pb - kQ3XShift)};
+        pv[P] = as_u32(as_h2(__builtin_amdgcn_perm(wb, wa, sel)) * m);
+      }
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4)
+        *reinterpret_cast<u32x4*>(xp + blk * 16 + 4 * v4) =
+            u32x4{pv[4 * v4], pv[4 * v4 + 1], pv[4 * v4 + 2], pv[4 * v4 + 3]};
+      return;
+    }
     float xs[32];
 #pragma unroll
     for (int v = 0; v < XV; ++v)
