@@ -758,6 +758,46 @@ def test_w8a8_ties_and_zero_row(wq):
     assert Sx.cpu().numpy()[2] == 0 and np.all(Xq.cpu().numpy()[2] == 0) and np.all(y[2] == 0)
 
 
+def test_w8a8_quantiser_division_at_ties_and_extreme_scales(wq):
+    # The quantiser divides by the row's Sx with one reciprocal per row and
+    # two fmas per element, which must give the IEEE quotient bit for bit.
+    # Rows with Sx from 2^-130 (subnormal) to 2^120 (below 2^-100 the plain
+    # division: near 2^-126 the remainder of the shortcut underflows), and
+    # entries whose quotients are exact halves and one ulp either side of
+    # them: rint then decides every code, so any quotient off by one ulp
+    # changes one.
+    rng = np.random.default_rng(1420)
+    K, N = 1024, 16
+    exps = [-130, -126, -125, -101, -100, -99, -20, -1, 0, 1, 20, 100, 120]
+    rows = []
+    for e in exps:
+        for _ in range(4):
+            a = np.float32(np.ldexp(rng.uniform(1.0, 2.0), e) * 127.0)
+            sx = np.float32(a / np.float32(127.0))
+            k = rng.integers(-127, 127, size=K).astype(np.float32)
+            x = (sx * (k + np.float32(0.5))).astype(np.float32)
+            sel = rng.integers(0, 3, size=K)
+            x = np.where(sel == 1, np.nextafter(x, np.float32(np.inf)), x)
+            x = np.where(sel == 2, np.nextafter(x, np.float32(-np.inf)), x)
+            x = np.clip(x, -a, a).astype(np.float32)
+            x[0] = a                                  # the row's maximum
+            rows.append(x)
+    X = np.stack(rows).astype(np.float32)
+    Wq = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    Sw = np.ones(N, np.float32)
+    _, Xq, Sx, _ = wq.gemm_w8a8(cu(X), cu(Wq), cu(Sw), want_acc=True)
+    torch.cuda.synchronize()
+    with np.errstate(over="ignore"):  # Y overflows at the largest scales; only Xq, Sx are checked
+        r = oracle.gemm_w8a8(X, Wq, Sw)
+    assert np.array_equal(Sx.cpu().numpy().view(np.uint32), r["Sx"].view(np.uint32))
+    got = Xq.cpu().numpy()
+    bad = np.nonzero((got != r["Xq"]).any(axis=1))[0]
+    assert bad.size == 0, (
+        f"rows {bad.tolist()} (scale exponents {[exps[i // 4] for i in bad]}): "
+        f"{int((got != r['Xq']).sum())} codes differ, max |diff| "
+        f"{int(np.abs(got.astype(np.int32) - r['Xq'].astype(np.int32)).max())}")
+
+
 # ----------------------------------------------------- SmoothQuant (W8A8) --
 
 @pytest.mark.parametrize("M,K,N", [(32, 1024, 64), (130, 256, 528), (7, 12288, 96),
