@@ -526,6 +526,22 @@ def test_q4_tiled_ragged(wq, M, K, N, G, act, zp):
                                          d["g_idx"], G), K, "f16", what)
 
 
+@pytest.mark.parametrize("M", [1, 9, 40])
+def test_q4_longest_k(wq, M):
+    # K = 32768, the longest K the packed row tables allow (uint16 rows):
+    # the small-M kernel at one row, the tiled kernel at 9 and 40 rows
+    # (one tile; three tiles in two row groups), act-order.
+    K, N, G = 32768, 64, 128
+    d = synth.gen_q4_group(M, K, N, G, seed=1330 + M, act_order=True)
+    packed, _ = wq.prepare_q4(cu(d["qweight"]), d["g_idx"], G)
+    y = host(wq.gemm_q4_group(cu(d["X"]), packed, cu(d["scales"]), G))
+    ref = oracle.gemm_q4_group(d["X"], d["qweight"], d["scales"], d["g_idx"], G)
+    what = f"q4 K=32768 M{M}"
+    assert_tol(y, ref, what)
+    assert_fwd_bound(y, ref, _q4_abs_sum(d["X"], d["qweight"], d["scales"], None, d["g_idx"], G), K,
+                     "f16", what)
+
+
 def test_q4_tiled_integer_exact_and_one_hot(wq):
     # Scales 1 and small integer X: every fp32 partial sum is an exact
     # integer, so Y is the oracle's value after one fp16 rounding.  Then one
@@ -756,6 +772,29 @@ def test_w8a8_ties_and_zero_row(wq):
     assert y[0, :4].tolist() == [256.0, 260.0, 512.0, 520.0]
     assert Xq.cpu().numpy()[1, :4].tolist() == [127, 2, -4, 0]
     assert Sx.cpu().numpy()[2] == 0 and np.all(Xq.cpu().numpy()[2] == 0) and np.all(y[2] == 0)
+
+
+def test_w8a8_longest_k_int32_range(wq):
+    # K = 133120, the largest multiple of 64 with K * 127 * 127 < 2^31.  Row
+    # 0 of X and every weight code sit at +127, so acc = K * 127^2 =
+    # 2,147,092,480: the int32 accumulators and the K-slice partials end
+    # within 0.02% of their range, and must still equal the oracle's exact
+    # sums; row 1 is random.
+    K, N = 133120, 32
+    assert K * 127 * 127 < 2**31 and (K + 64) * 127 * 127 >= 2**31
+    rng = np.random.default_rng(1430)
+    X = np.stack([np.ones(K, np.float32), rng.standard_normal(K).astype(np.float32)])
+    Wq = np.full((N, K), 127, np.int8)
+    Wq[N // 2:] = rng.integers(-127, 128, size=(N - N // 2, K)).astype(np.int8)
+    Sw = rng.uniform(0.5, 2.0, N).astype(np.float32)
+    Y, Xq, Sx, acc = wq.gemm_w8a8(cu(X), cu(Wq), cu(Sw), want_acc=True)
+    torch.cuda.synchronize()
+    r = oracle.gemm_w8a8(X, Wq, Sw)
+    a = acc.cpu().numpy()
+    assert int(a[0, 0]) == K * 127 * 127
+    assert np.array_equal(Xq.cpu().numpy(), r["Xq"])
+    assert np.array_equal(a, r["acc"])
+    assert np.array_equal(Y.view(torch.int16).cpu().numpy().view(np.uint16), r["y_bits"])
 
 
 def test_w8a8_quantiser_division_at_ties_and_extreme_scales(wq):
