@@ -111,7 +111,7 @@ def wl_q8(wq, torch, dev, M=1):
     def make(R):
         base = [torch.from_numpy(d["X"]).to(dev), wq.prepack_q8(torch.from_numpy(d["q"]).to(dev)),
                 torch.from_numpy(d["scales"]).to(dev)]
-        # one workspace (the K slices' partial tiles, above 16 rows) serves every copy
+        # one workspace (the K slices' partial tiles, above 32 rows) serves every copy
         nws = wq.workspace_bytes(wq.WQ_OP_Q8G, M, K, N)
         ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
         copies = [[t.clone() for t in base] + [torch.empty((M, N), dtype=torch.float16, device=dev), ws]
@@ -121,7 +121,7 @@ def wl_q8(wq, torch, dev, M=1):
     def run(c):
         wq.gemm_q8_group(c[0], c[1], c[2], G, Y=c[3], ws=c[4])
 
-    kind = "gemv" if M == 1 else "streaming" if M <= 16 else "gemm"
+    kind = "gemv" if M == 1 else "streaming" if M <= 32 else "gemm"
     w = Workload(f"q8_group_{kind} M={M} K={K} N={N} G={G}", nbytes, make, run,
                  flops=0 if M == 1 else 2 * M * K * N)
     w.peak_tops = FP16_PEAK_TFLOPS

@@ -43,7 +43,7 @@
  *   frees memory, never synchronises a stream, and never changes the current
  *   device; work runs on the device that owns the buffers, on `stream`
  *   (a hipStream_t; NULL means the default stream), asynchronously.  The
- *   int8 and 4-bit products above 16 and 4 rows of X and the W8A8 family take a workspace,
+ *   int8 and 4-bit products above 32 and 4 rows of X and the W8A8 family take a workspace,
  *   sized by wq_workspace_bytes(), in which a call leaves nothing that a
  *   later call depends on (it needs no clearing); the other products need
  *   none (no partial result leaves a workgroup).  Calls that overlap in time
@@ -105,9 +105,9 @@ size_t wq_packed_bytes(int op, int K, int N, int G);
  *   S * M * N * 4 bytes (S = 2 at M = 256, K = N = 8192: 16 MiB; S = 1, no
  *   workspace, once the 128 x 128 output tiles alone fill the GPU, e.g. for
  *   M > 256 at N = 8192).
- * - WQ_OP_Q8G (wq_gemm_q8_group): above 16 rows of X, while the 32 x 128
+ * - WQ_OP_Q8G (wq_gemm_q8_group): above 32 rows of X, while the 32 x 128
  *   output tiles alone do not fill the GPU, the fp32 partial tiles of S K
- *   slices, S * M * N * 4 bytes (S = 8 for 17 <= M <= 64 at K = N = 4096;
+ *   slices, S * M * N * 4 bytes (S = 8 for 33 <= M <= 64 at K = N = 4096;
  *   the size holds for every group size the tiled path takes).
  * - WQ_OP_Q4G (wq_gemm_q4_group, wq_gemm_q4_group_zp): above 4 rows of X,
  *   X in the packed weight's row order, Mp * Kp * 2 bytes (Mp = M rounded
@@ -155,8 +155,8 @@ int wq_prepack_q8(const int8_t* qweight, void* packed, int K, int N, void* strea
  * X [M, K] fp16; packed: from wq_prepack_q8; scales [K/G, N] fp32;
  * Y [M, N] fp16, written (fp32 accumulation, one round to nearest even).
  * Evaluated per group as scale * (sum of X * q), exact products, fp32 sums.
- * M <= 16, or G not a multiple of 64: streaming passes over the packed
- * weight, one per 16 rows of X (one or two rows on v_dot2, 3 to 16 on the
+ * M <= 32, or G not a multiple of 64: streaming passes over the packed
+ * weight, one per 32 rows of X (one or two rows on v_dot2, 3 to 32 on the
  * matrix cores).  Otherwise a tiled matrix-core
  * launch (32 x 128 output tiles) reads the packed weight once; while those
  * tiles alone do not fill the GPU (e.g. M <= 64 at N = 4096) K is split over
@@ -166,7 +166,7 @@ int wq_prepack_q8(const int8_t* qweight, void* packed, int K, int N, void* strea
  * "融合反量化与GEMM：LLM推理的CUDA内核优化实践", zingnex.cn, "技术实现细节".)
  * workspace: device, needed when G % 64 == 0 and wq_workspace_bytes(
  *   WQ_OP_Q8G, M, K, N) > 0 (S * M * N * 4 bytes, S the number of K slices:
- *   8 for 17 <= M <= 64 at K = N = 4096), else NULL allowed; 16-byte aligned;
+ *   8 for 33 <= M <= 64 at K = N = 4096), else NULL allowed; 16-byte aligned;
  *   needs no clearing.  WQ_ERR_WORKSPACE if missing or too small.  Calls
  *   that overlap in time need separate workspaces.
  * Rules: M >= 1, K % 32 == 0, N % 16 == 0, G % 32 == 0, K % G == 0,

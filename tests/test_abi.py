@@ -85,18 +85,19 @@ def test_q8_validation(L):
     assert f(P, P, P, P, 1, 4096, 4096, 48, None) == wq.WQ_ERR_SHAPE     # G % 32
     assert f(P, P_MIS, P, P, 1, 4096, 4096, 128, None) == wq.WQ_ERR_ALIGN
     assert f(P, P, P, P_MIS, 8, 4096, 4096, 128, None) == wq.WQ_ERR_ALIGN    # Y: 8-byte stores
-    # above 16 rows the tiled path splits K: S slices of M x N fp32 partials
-    need = L.wq_workspace_bytes(wq.WQ_OP_Q8G, 17, 4096, 4096)
-    assert need == 8 * 17 * 4096 * 4
-    assert L.wq_workspace_bytes(wq.WQ_OP_Q8G, 16, 4096, 4096) == 0     # streaming passes
+    # above 32 rows the tiled path splits K: S slices of M x N fp32 partials
+    need = L.wq_workspace_bytes(wq.WQ_OP_Q8G, 33, 4096, 4096)
+    assert need == 8 * 33 * 4096 * 4
+    assert L.wq_workspace_bytes(wq.WQ_OP_Q8G, 32, 4096, 4096) == 0     # one streaming pass
+    assert L.wq_workspace_bytes(wq.WQ_OP_Q8G, 17, 4096, 4096) == 0
     assert L.wq_workspace_bytes(wq.WQ_OP_Q8G, 64, 4096, 4096) == 8 * 64 * 4096 * 4
     assert L.wq_workspace_bytes(wq.WQ_OP_Q8G, 256, 4096, 4096) == 2 * 256 * 4096 * 4
     assert L.wq_workspace_bytes(wq.WQ_OP_Q8G, 512, 4096, 4096) == 0    # 512 tiles fill the GPU
-    assert L.wq_workspace_bytes(wq.WQ_OP_Q8G, 17, 4160, 4096) == 0     # K not whole slices
+    assert L.wq_workspace_bytes(wq.WQ_OP_Q8G, 33, 4160, 4096) == 0     # K not whole slices
     g8 = L.wq_gemm_q8_group
-    assert g8(P, P, P, P, 17, 4096, 4096, 128, None, need, None) == wq.WQ_ERR_WORKSPACE
-    assert g8(P, P, P, P, 17, 4096, 4096, 128, P, need - 16, None) == wq.WQ_ERR_WORKSPACE
-    assert g8(P, P, P, P, 17, 4096, 4096, 128, P_MIS, need, None) == wq.WQ_ERR_ALIGN
+    assert g8(P, P, P, P, 33, 4096, 4096, 128, None, need, None) == wq.WQ_ERR_WORKSPACE
+    assert g8(P, P, P, P, 33, 4096, 4096, 128, P, need - 16, None) == wq.WQ_ERR_WORKSPACE
+    assert g8(P, P, P, P, 33, 4096, 4096, 128, P_MIS, need, None) == wq.WQ_ERR_ALIGN
     # groups of 32 run as streaming passes at any M: no workspace
     assert f(P, P, P, P_MIS, 16, 4096, 4096, 32, None) == wq.WQ_ERR_ALIGN  # (reaches the Y check)
     assert L.wq_prepack_q8(P, P, 4096, 4100, None) == wq.WQ_ERR_SHAPE

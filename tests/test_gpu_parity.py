@@ -170,18 +170,19 @@ def test_q8_wide_panels_and_long_k(wq):
         assert_tol(host(Y), oracle.gemm_q8_group(d["X"], d["q"], d["scales"], 128), f"q8 {M}x{K}x{N}")
 
 
-# From 9 rows of X on (groups a multiple of 64 rows) the int8 product runs
-# on the matrix cores: 32 x 128 output tiles, K in stages of 128 rows, and K
-# split over 2..8 workgroups while the tiles alone do not fill the GPU.
+# From 33 rows of X on (groups a multiple of 64 rows) the int8 product runs
+# as the tiled matrix-core GEMM: 32 x 128 output tiles, K in stages of 128
+# rows, and K split over 2..8 workgroups while the tiles alone do not fill
+# the GPU.
 @pytest.mark.parametrize("M,K,N,G", [
-    (9, 4096, 4096, 128),      # first row count on the tiled path: 8 K slices
-    (16, 4096, 11008, 128),    # 8 slices, wide N
-    (24, 4096, 4096, 64),      # groups of 64: two per stage
-    (31, 2048, 4096, 256),     # groups of two stages: slices of 256 rows
-    (32, 4096, 4096, 128),
+    (33, 4096, 4096, 128),     # first row count on the tiled path: 8 K slices
+    (48, 4096, 11008, 128),    # 8 slices, wide N
+    (40, 4096, 4096, 64),      # groups of 64: two per stage
+    (47, 2048, 4096, 256),     # groups of two stages: slices of 256 rows
+    (56, 4096, 4096, 128),
     (64, 4096, 4096, 128),     # two row tiles, 8 slices
     (256, 4096, 4096, 128),    # 2 slices
-    (20, 4160, 4096, 64),      # K not whole slices: no split
+    (36, 4160, 4096, 64),      # K not whole slices: no split
     (100, 1088, 4112, 64),     # ragged row and column tiles, 17 stages
     (64, 64, 128, 64),         # a single stage
     (40, 11008, 4096, 128),    # a ragged last stage (K = 86 stages of 128)
@@ -195,10 +196,11 @@ def test_q8_gemm_tiles_vs_oracle(wq, M, K, N, G):
     assert_tol(host(Y), oracle.gemm_q8_group(d["X"], d["q"], d["scales"], G), f"q8 tiles {M}x{K}x{N} G{G}")
 
 
-# Up to 16 rows of X the int8 product is one streaming matrix-core pass over
+# Up to 32 rows of X the int8 product is one streaming matrix-core pass over
 # the packed tiles: chains of 32-row steps per scale (groups of 32 .. 512
 # rows a power of two, or one step per scale otherwise), X staged per 4096-row
-# chunk, the 8 waves of a panel summed in LDS.
+# chunk (per 2048-row chunk above 16 rows, two 16-row tiles per step), the 8
+# waves of a panel summed in LDS.
 @pytest.mark.parametrize("M,K,N,G", [
     (9, 4096, 4096, 128),      # first row count past the 8-row operand tile rows
     (16, 4096, 11008, 128),    # the full 16-row pass, wide N
@@ -208,6 +210,16 @@ def test_q8_gemm_tiles_vs_oracle(wq, M, K, N, G):
     (11, 4608, 256, 512),      # a ragged second chunk (512 of 4096 rows)
     (10, 4224, 4112, 64),      # chains of two steps, a ragged chunk, N not a multiple of 256
     (15, 2048, 1024, 256),     # chains of eight steps
+    # 17 .. 32 rows: two 16-row tiles per step, X staged per 2048-row chunk
+    (17, 4096, 4096, 128),     # first row count past one tile; two chunks
+    (32, 4096, 11008, 128),    # the full 32-row pass, wide N
+    (24, 224, 48, 32),         # K % 64 == 32, a scale per step; 3 panels
+    (32, 1152, 272, 96),       # G not a power of two; 17 panels
+    (29, 8192, 512, 4096),     # eight-step chains inside one large group, four chunks
+    (21, 4608, 256, 512),      # a ragged third chunk (512 of 2048 rows)
+    (18, 4224, 4112, 64),      # chains of two steps, a ragged chunk, N not a multiple of 256
+    (31, 2048, 1024, 256),     # eight-step chains of one group each
+    (40, 1152, 512, 96),       # 40 rows with G = 96 (no tiled path): passes of 32 and 8
 ])
 def test_q8_streaming_rows_vs_oracle(wq, M, K, N, G):
     d = synth.gen_q8_group(M, K, N, G, seed=301 + M + K + N)
@@ -220,10 +232,11 @@ def test_q8_streaming_rows_vs_oracle(wq, M, K, N, G):
 
 
 @pytest.mark.parametrize("M,K,N,G", [(80, 1024, 400, 128), (12, 2048, 1024, 128),
-                                     (16, 2048, 1024, 64), (3, 4160, 272, 32)])
+                                     (16, 2048, 1024, 64), (3, 4160, 272, 32),
+                                     (24, 2048, 1024, 64), (32, 4160, 272, 32)])
 def test_q8_gemm_integer_exact_and_deterministic(wq, M, K, N, G):
     # Scales 1 and small integer X on the tiled path (80 rows) and the
-    # streaming pass (3..16 rows): every fp32 partial sum is an exact
+    # streaming passes (3..32 rows): every fp32 partial sum is an exact
     # integer, so the result is bit-exact; repeated calls agree.
     rng = np.random.default_rng(43)
     q = rng.integers(-127, 128, size=(K, N)).astype(np.int8)
@@ -241,16 +254,16 @@ def test_q8_split_k_workspace_contents_do_not_matter(wq):
     # The K slices' partial tiles overwrite the workspace: garbage in it, or
     # a larger one, changes nothing, and two calls in a row (the second
     # smaller) agree with fresh ones.
-    d = synth.gen_q8_group(24, 4096, 4096, 128, seed=91)
+    d = synth.gen_q8_group(40, 4096, 4096, 128, seed=91)
     X, P, Sd = cu(d["X"]), wq.prepack_q8(cu(d["q"])), cu(d["scales"])
-    need = wq.workspace_bytes(wq.WQ_OP_Q8G, 24, 4096, 4096)
-    assert need == 8 * 24 * 4096 * 4
+    need = wq.workspace_bytes(wq.WQ_OP_Q8G, 40, 4096, 4096)
+    assert need == 8 * 40 * 4096 * 4
     ws = torch.full((need + 4096,), 0x7F, dtype=torch.uint8, device=dev())
     Y0 = wq.gemm_q8_group(X, P, Sd, 128)
     assert torch.equal(wq.gemm_q8_group(X, P, Sd, 128, ws=ws), Y0)
     Y1 = wq.gemm_q8_group(X[:10], P, Sd, 128, ws=ws)
     assert torch.equal(Y1, wq.gemm_q8_group(X[:10], P, Sd, 128))
-    assert_tol(host(Y0), oracle.gemm_q8_group(d["X"], d["q"], d["scales"], 128), "q8 split 24")
+    assert_tol(host(Y0), oracle.gemm_q8_group(d["X"], d["q"], d["scales"], 128), "q8 split 40")
     assert_tol(host(Y1), oracle.gemm_q8_group(d["X"][:10], d["q"], d["scales"], 128), "q8 split 10")
 
 

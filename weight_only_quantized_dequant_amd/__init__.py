@@ -202,7 +202,7 @@ def gemm_q8_group(X, packed, scales, group_size=128, Y=None, ws=None):
     """Y = X . (scale[k // G] * q) from a packed int8 weight; X fp16 [M, K] or [K].
 
     ``ws``: device workspace of ``workspace_bytes(WQ_OP_Q8G, M, K, N)`` bytes
-    (K split over workgroups above 16 rows), allocated here if None and needed.
+    (K split over workgroups above 32 rows), allocated here if None and needed.
     """
     squeeze = X.dim() == 1
     X2 = X.reshape(1, -1) if squeeze else X

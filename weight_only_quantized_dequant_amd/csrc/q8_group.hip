@@ -29,7 +29,9 @@
 // v_mfma_f32_16x16x32_f16, from the same packed weight: the 8 waves of a
 // panel split K, each load instruction of a wave brings 128 contiguous bytes
 // of each of the panel's 8 pairs, and a wave-private LDS copy turns them into
-// the operand order (16 columns x 32 rows per step).
+// the operand order (16 columns x 32 rows per step).  At 17 .. 32 rows
+// (q8_mfma32_kernel) each step takes two 16-row tiles of X, staged per
+// 2048-row chunk.
 #include "wq_device.hpp"
 #include "wq_internal.h"
 
@@ -41,9 +43,9 @@ constexpr int kQ8Threads = 512;
 constexpr int kQ8Steps = 8;                    // pieces per lane per chunk
 constexpr int kQ8Chunk = 64 * kQ8Steps * 8;    // rows of K per chunk: 4096
 // From this many rows of X on, the product runs as a tiled matrix-core GEMM
-// (q8_gemm.hip) instead of one streaming pass over the weight per 16 rows.
-constexpr int kQ8GemmMinRows = 17;
-constexpr int kQ8PassRows = 16;
+// (q8_gemm.hip) instead of one streaming pass over the weight per 32 rows.
+constexpr int kQ8GemmMinRows = 33;
+constexpr int kQ8PassRows = 32;
 
 // Panel plan: 16-column panels (8 column pairs); u = pieces per pair.
 PanelPlan plan_q8(int K, int N) {
@@ -529,6 +531,190 @@ __global__ __launch_bounds__(kQ8Threads) void q8_mfma_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// The product at 17 .. 32 rows of X: q8_mfma_kernel's scheme with two 16-row
+// tiles of X per step (two matrix-core products per weight operand) and X
+// staged per 2048-row chunk (32 rows of a 4096-row chunk do not fit the LDS):
+// of every chunk wave w takes rows 256 w .. 256 w + 255, four 1 KB loads.
+// Thread t stages piece t % 256 (8 rows of K) of the rows t / 256 + 2 i of X.
+// CL: 32-row steps per chain (one scale), at most the wave's 8 steps of a
+// chunk: G / 32 for groups of 32 .. 256 rows, 8 for larger powers of two, 1
+// for other group sizes.
+// ---------------------------------------------------------------------------
+template <int CL>
+__global__ __launch_bounds__(kQ8Threads) void q8_mfma32_kernel(
+    const _Float16* __restrict__ X, const uint8_t* __restrict__ Wp,
+    const float* __restrict__ scales, _Float16* __restrict__ Y, int M, int K, int N, int G,
+    int gsh) {
+  constexpr int MT = 32, CH = 2048;
+  constexpr int NL = CH / (64 * kQ8Waves);    // 1 KB loads per wave per chunk: 4
+  constexpr int NSTEP = 2 * NL;               // 32-row steps per wave per chunk: 8
+  constexpr int WR = CH / kQ8Waves;           // rows per wave per chunk: 256
+  constexpr int NC = NSTEP / CL;              // chains per wave per chunk
+  constexpr int NG = CH / (32 * CL);          // chains per chunk
+  constexpr int XRB = 2 * CH + 16;            // LDS bytes per row of X (bank spread)
+  constexpr int PPR = CH / 8;                 // 16-byte pieces per row of a chunk: 256
+  constexpr int XPT = MT * PPR / kQ8Threads;  // pieces of X per thread per chunk: 16
+  static_assert(CL == 1 || CL == 2 || CL == 4 || CL == 8, "chain length");
+  static_assert(kQ8Threads == 2 * PPR, "two row parities of 256 pieces");
+  __shared__ __attribute__((aligned(16))) unsigned char xs[MT * XRB];  // the chunk of X
+  __shared__ float cs[NG][MT];  // [chain][row of X]: -128 2^-24 sum of x over the chain's rows
+  __shared__ __attribute__((aligned(1024))) unsigned char tr[kQ8Waves][2 * 1024];
+
+  const int t = threadIdx.x, lane = t & 63, h = lane >> 4, j = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int bid = blockIdx.x;
+  const int panel = (gridDim.x % 16 == 0) ? (bid & ~15) + 2 * (bid & 7) + ((bid >> 3) & 1) : bid;
+  const int KB = K / 8;  // pieces per pair
+
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wp, K * N);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, M * K * 2);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, (K / G) * N * 4);
+
+  // tot[tt][r]: row 16 tt + 4 (l / 16) + r of X, column 16 panel + l % 16, units of 2^-24.
+  float tot[2][4];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) tot[tt][r] = 0.0f;
+  const int lpair = 8 * panel + (lane >> 3);                 // pair this lane loads
+  const uint32_t sel = (j & 1) ? 0x0c030c02u : 0x0c010c00u;  // its operand column in a piece
+  unsigned char* mytr = &tr[wave][0];
+  const int xp = t & (PPR - 1), xq = t / PPR;  // staged piece and row parity
+
+  // Chunk c + 1's activations, scales and weight are requested before chunk
+  // c's products (into registers), so only the first chunk waits for a full
+  // round trip; the next chunk's X is staged once every wave is done with
+  // the current one.
+  u32x4 xg[XPT];
+  float sc[NC], scn[NC];
+  u32x4 wv[NL], wn[NL];
+  auto issue = [&](int r0, u32x4 (&xgr)[XPT], float (&scr)[NC], u32x4 (&wvr)[NL]) {
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int m = xq + 2 * i;
+      xgr[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          xr, (r0 < K && m < M && r0 + 8 * xp < K) ? (m * K + r0 + 8 * xp) * 2 : kOutOfRange, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int row = r0 + WR * wave + 32 * CL * c;
+      const int g = gsh >= 0 ? row >> gsh : row / G;  // gsh = log2 G, or -1
+      scr[c] = as_f32(__builtin_amdgcn_raw_buffer_load_b32(
+          sr, row < K ? (g * N + 16 * panel + j) * 4 : kOutOfRange, 0, 0));
+    }
+    const int b0 = (r0 + WR * wave) / 8;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int b = b0 + 8 * i + (lane & 7);
+      wvr[i] = buffer_stream(wr, (r0 < K && b < KB) ? (lpair * KB + b) * 16 : kOutOfRange);
+    }
+  };
+  issue(0, xg, sc, wv);
+
+  for (int r0 = 0; r0 < K; r0 += CH) {
+    wait_vmcnt<NC + NL>();      // this chunk's activations have landed
+    if (r0 > 0) lds_barrier();  // every wave is done with the previous chunk
+    // Stage X; the chain sums: piece xp lies in chain xp / (4 CL), whose 4 CL
+    // threads are consecutive lanes (fixed-order DPP sums).
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int m = xq + 2 * i;
+      *reinterpret_cast<u32x4*>(xs + m * XRB + 16 * xp) = xg[i];
+      const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+      float ps = 0.0f;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) ps = dot2(as_h2(xg[i][d]), ones, ps);
+      ps *= -128.0f / kTwo24;
+      ps += q8_dpp<0xB1>(ps);                          // quad_perm 1 0 3 2
+      ps += q8_dpp<0x4E>(ps);                          // quad_perm 2 3 0 1
+      if constexpr (CL >= 2) ps += q8_dpp<0x12C>(ps);  // row_ror:12, lane l + 4
+      if constexpr (CL >= 4) ps += q8_dpp<0x128>(ps);  // row_ror:8
+      if constexpr (CL >= 8) ps += __shfl_xor(ps, 16);
+      if ((xp & (4 * CL - 1)) == 0) cs[xp / (4 * CL)][m] = ps;
+    }
+    lds_barrier();
+
+    // Every step's two A operands, then the next chunk's loads.
+    h8 av[NSTEP][2];
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int row = 16 * tt + j < M ? 16 * tt + j : 0;
+        av[st][tt] = *reinterpret_cast<const h8*>(xs + row * XRB + 2 * (WR * wave + 32 * st + 8 * h));
+      }
+    issue(r0 + CH, xg, scn, wn);  // past the last chunk: out of range, no request
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Two accumulators per tile alternate along a chain; a chain's first two
+    // steps start from the constant zero.
+    const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 c0[2] = {zero4, zero4}, c1[2] = {zero4, zero4};
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      // The loaded KB into this wave's slot (a wave's LDS accesses run in
+      // issue order: no wait between the write and the reads).
+      unsigned char* slot = mytr + 1024 * (i & 1);
+      *reinterpret_cast<u32x4*>(slot + 16 * lane) = wv[i];
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int st = 2 * i + s;
+        const u32x4 pc = *reinterpret_cast<const u32x4*>(slot + 16 * (8 * (j >> 1) + 4 * s + h));
+        const u32x4 bw = {__builtin_amdgcn_perm(0u, pc[0], sel), __builtin_amdgcn_perm(0u, pc[1], sel),
+                          __builtin_amdgcn_perm(0u, pc[2], sel), __builtin_amdgcn_perm(0u, pc[3], sel)};
+        const h8 b = __builtin_bit_cast(h8, bw);
+        const int pos = st % CL;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          if (pos == 0)
+            c0[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[st][tt], b, zero4, 0, 0, 0);
+          else if (pos == 1)
+            c1[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[st][tt], b, zero4, 0, 0, 0);
+          else if (pos % 2 == 0)
+            c0[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[st][tt], b, c0[tt], 0, 0, 0);
+          else
+            c1[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[st][tt], b, c1[tt], 0, 0, 0);
+        }
+        if (pos == CL - 1) {
+          const int c = st / CL;
+          const float* off = &cs[wave * NC + c][0];
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float v = CL == 1 ? c0[tt][r] : c0[tt][r] + c1[tt][r];
+              tot[tt][r] = __builtin_fmaf(v + off[16 * tt + 4 * h + r], sc[c], tot[tt][r]);
+            }
+        }
+      }
+      asm volatile("" ::: "memory");
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) sc[c] = scn[c];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) wv[i] = wn[i];
+  }
+
+  // The 8 waves' totals (each in its own 2 KB slot), added as a fixed-order
+  // pairwise tree ((w0 + w1) + (w2 + w3)) + ((w4 + w5) + (w6 + w7)).
+  float* red = reinterpret_cast<float*>(mytr);  // [32][16]
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[(16 * tt + 4 * h + r) * 16 + j] = tot[tt][r];
+  __syncthreads();
+  {
+    const int row = t >> 4, col = t & 15;  // 512 threads: the 32 x 16 outputs
+    float v[kQ8Waves];
+#pragma unroll
+    for (int w = 0; w < kQ8Waves; ++w) v[w] = reinterpret_cast<const float*>(&tr[w][0])[row * 16 + col];
+    const float s = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+    if (row < M) Y[(size_t)row * N + 16 * panel + col] = (_Float16)(s * kTwo24);
+  }
+}
+
 hipError_t launch_q8_prepack(const int8_t* W, void* packed, int K, int N, hipStream_t s) {
   const size_t total = (size_t)(N / 2) * (K / 8);
   hipLaunchKernelGGL(q8_prepack_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)),
@@ -577,6 +763,28 @@ static hipError_t launch_q8_rows(const void* X, const void* packed, const float*
   return hipGetLastError();
 }
 
+// 17 .. 32 rows: one pass of q8_mfma32_kernel.
+static hipError_t launch_q8_rows32(const void* X, const void* packed, const float* scales, void* Y,
+                                   int M, int K, int N, int G, hipStream_t s) {
+  const bool pow2 = (G & (G - 1)) == 0;
+  const int CL = !pow2 ? 1 : G >= 256 ? 8 : G / 32;
+  int gsh = -1;
+  if (pow2)
+    for (gsh = 0; (1 << gsh) < G; ++gsh) {
+    }
+  const dim3 grid(N / 16), block(kQ8Threads);
+  const _Float16* x = reinterpret_cast<const _Float16*>(X);
+  const uint8_t* w = reinterpret_cast<const uint8_t*>(packed);
+  _Float16* y = reinterpret_cast<_Float16*>(Y);
+  switch (CL) {
+    case 8: hipLaunchKernelGGL((q8_mfma32_kernel<8>), grid, block, 0, s, x, w, scales, y, M, K, N, G, gsh); break;
+    case 4: hipLaunchKernelGGL((q8_mfma32_kernel<4>), grid, block, 0, s, x, w, scales, y, M, K, N, G, gsh); break;
+    case 2: hipLaunchKernelGGL((q8_mfma32_kernel<2>), grid, block, 0, s, x, w, scales, y, M, K, N, G, gsh); break;
+    default: hipLaunchKernelGGL((q8_mfma32_kernel<1>), grid, block, 0, s, x, w, scales, y, M, K, N, G, gsh); break;
+  }
+  return hipGetLastError();
+}
+
 size_t q8_group_workspace_bytes(int M, int K, int N) {
   return M >= kQ8GemmMinRows ? q8_gemm_workspace_bytes(M, K, N) : 0;
 }
@@ -585,8 +793,8 @@ hipError_t launch_q8_group(const void* X, const void* packed, const float* scale
                            void* ws, int M, int K, int N, int G, hipStream_t s) {
   if (M >= kQ8GemmMinRows && q8_gemm_supported(M, K, N, G))
     return launch_q8_gemm(X, packed, scales, Y, ws, M, K, N, G, s);
-  // Up to 16 rows of X per launch over the same weight: one or two rows on
-  // the v_dot2 pair kernel, 3 .. 16 on the matrix cores.
+  // Up to 32 rows of X per launch over the same weight: one or two rows on
+  // the v_dot2 pair kernel, 3 .. 32 on the matrix cores.
   for (int m0 = 0; m0 < M; m0 += kQ8PassRows) {
     const int mc = (M - m0) < kQ8PassRows ? (M - m0) : kQ8PassRows;
     const void* Xc = reinterpret_cast<const char*>(X) + (size_t)m0 * K * 2;
@@ -603,8 +811,10 @@ hipError_t launch_q8_group(const void* X, const void* packed, const float* scale
       e = launch_q8_rows<4>(Xc, packed, scales, Yc, mc, K, N, G, s);
     else if (mc <= 8)
       e = launch_q8_rows<8>(Xc, packed, scales, Yc, mc, K, N, G, s);
-    else
+    else if (mc <= 16)
       e = launch_q8_rows<16>(Xc, packed, scales, Yc, mc, K, N, G, s);
+    else
+      e = launch_q8_rows32(Xc, packed, scales, Yc, mc, K, N, G, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
