@@ -122,11 +122,21 @@ __device__ __forceinline__ void q8_row_all(float x, float (&s)[2 * kQ8Steps]) {
   }
 }
 
-template <int MT, bool FOLD>
+// ONE (one row of X, FOLD, K exactly one 4096-row chunk): straight-line code
+// with no range selects, and the activation and scale requests pinned ahead
+// of the weight stream (the compiler otherwise hoists the sums of x above the
+// weight loads, and each wave then waits for its activations before it asks
+// for any weights).
+template <int MT, bool FOLD, bool ONE = false>
 __global__ __launch_bounds__(kQ8Threads) void q8_pair_kernel(
     const _Float16* __restrict__ X, const uint8_t* __restrict__ Wp,
     const float* __restrict__ scales, _Float16* __restrict__ Y, int M, int K, int N, int G,
     int gsh) {
+  static_assert(!ONE || (MT == 1 && FOLD), "the single-chunk form is for one row");
+  if constexpr (ONE) {
+    M = 1;
+    K = kQ8Chunk;
+  }
   __shared__ u32x4 xs[MT][kQ8Threads];  // rows r0 .. r0 + 4095 of the MT rows of X
   // The sums of x that remove the code bias.  FOLD (all 16 pieces a quarter
   // holds at a step share one group and so one scale): one sum per 128-row
@@ -190,6 +200,7 @@ __global__ __launch_bounds__(kQ8Threads) void q8_pair_kernel(
             sr, b < KB ? (((8 * b) / G) * N + 2 * q) * 4 : kOutOfRange, 0, 0);
       }
     }
+    if constexpr (ONE) __builtin_amdgcn_sched_barrier(0);
     u32x4 w[kQ8Steps];
 #pragma unroll
     for (int i = 0; i < kQ8Steps; ++i) {
@@ -197,6 +208,7 @@ __global__ __launch_bounds__(kQ8Threads) void q8_pair_kernel(
       w[i] = buffer_stream(wr, b < KB ? (q * KB + b) * 16 : kOutOfRange);
     }
     wait_vmcnt<kQ8Steps + NS>();  // the activations have landed
+    if constexpr (ONE) asm volatile("" : "+v"(xg[0])::"memory");
     if (r0 > 0) lds_barrier();     // every wave is done with the previous chunk
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
@@ -734,6 +746,14 @@ static hipError_t launch_q8_t(const void* X, const void* packed, const float* sc
                               int M, int K, int N, int G, hipStream_t s) {
   int gsh = 0;
   while ((1 << gsh) < G) ++gsh;
+  if constexpr (MT == 1 && FOLD) {
+    if (K == kQ8Chunk) {
+      hipLaunchKernelGGL((q8_pair_kernel<1, true, true>), dim3(N / 16), dim3(kQ8Threads), 0, s,
+                         reinterpret_cast<const _Float16*>(X), reinterpret_cast<const uint8_t*>(packed),
+                         scales, reinterpret_cast<_Float16*>(Y), M, K, N, G, gsh);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((q8_pair_kernel<MT, FOLD>), dim3(N / 16), dim3(kQ8Threads), 0, s,
                      reinterpret_cast<const _Float16*>(X), reinterpret_cast<const uint8_t*>(packed),
                      scales, reinterpret_cast<_Float16*>(Y), M, K, N, G, gsh);
