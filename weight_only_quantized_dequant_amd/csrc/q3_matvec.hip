@@ -114,8 +114,8 @@ __global__ __launch_bounds__(kThreads) void q3_prepack_kernel(const uint32_t* __
 template <bool F16, int CPP, int THREADS>
 __global__ __launch_bounds__(THREADS) void q3_panel_kernel(
     const void* __restrict__ xv, const uint8_t* __restrict__ Wp, const void* __restrict__ sv,
-    const void* __restrict__ zv, void* __restrict__ yv, int K, int N, int u, int nsa, int npanels,
-    int packed_bytes) {
+    const void* __restrict__ zv, void* __restrict__ yv, int K, int N, int u, int nsa, int pq,
+    int pe, int packed_bytes) {
   constexpr int P = 4 * CPP;
   constexpr int LOWBIT = CPP == 1 ? 0 : CPP == 2 ? 1 : CPP == 4 ? 2 : 3;
   constexpr int NACC = F16 ? kQ3Classes : 1;
@@ -129,8 +129,8 @@ __global__ __launch_bounds__(THREADS) void q3_panel_kernel(
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   // This workgroup's contiguous run of panels; a unit is UB blocks of a panel.
-  const int p_begin = (int)((long long)blockIdx.x * npanels / gridDim.x);
-  const int p_end = (int)((long long)(blockIdx.x + 1) * npanels / gridDim.x);
+  const SplitPart part = split_part((int)blockIdx.x, pq, pe);
+  const int p_begin = part.begin, p_end = part.begin + part.count;
   const int nr = (u + UB - 1) / UB;  // units per panel
   const int nunits = (p_end - p_begin) * nr;
   const int nta = nsa * CPP;
@@ -470,7 +470,7 @@ static hipError_t launch_q3_t(const void* x, const void* packed, const void* sca
   }
   hipLaunchKernelGGL((q3_panel_kernel<F16, CPP, THREADS>), dim3(grid), dim3(THREADS), lds, s, x,
                      reinterpret_cast<const uint8_t*>(packed), scales, zeros, y, K, N, p.u, p.nsa,
-                     p.npanels, (int)p.packed_bytes);
+                     p.npanels / grid, p.npanels % grid, (int)p.packed_bytes);
   return hipGetLastError();
 }
 

@@ -217,7 +217,8 @@ template <int MT, int NSC, bool ZP, int BITS>
 __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
     const _Float16* __restrict__ X, const uint8_t* __restrict__ Wp,
     const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
-    _Float16* __restrict__ Y, int M, int K, int N, int G, int nb, int npanels, int packed_bytes) {
+    _Float16* __restrict__ Y, int M, int K, int N, int G, int nb, int npanels, int pq, int pe,
+    int packed_bytes) {
   typedef _Float16 h8 __attribute__((ext_vector_type(8)));
   typedef float f4 __attribute__((ext_vector_type(4)));
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -240,9 +241,8 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
   // fetched into one XCD's L2, not into up to four.
   const int G8 = gridDim.x % 8 == 0 ? gridDim.x / 8 : 0;
   const int run = G8 ? (int)(blockIdx.x % 8) * G8 + (int)(blockIdx.x / 8) : (int)blockIdx.x;
-  const int p_begin = (int)((long long)run * npanels / gridDim.x);
-  const int p_end = (int)((long long)(run + 1) * npanels / gridDim.x);
-  const int npr = p_end - p_begin;
+  const SplitPart part = split_part(run, pq, pe);
+  const int p_begin = part.begin, npr = part.count;
 
   // Blocks of this wave: a group-aligned contiguous range.
   const int bpg = G >= BR ? G / BR : 1;
@@ -631,7 +631,8 @@ static hipError_t launch_q4_t(const void* X, const void* packed, const void* sca
                      reinterpret_cast<const _Float16*>(X), reinterpret_cast<const uint8_t*>(packed),
                      reinterpret_cast<const _Float16*>(scales),
                      reinterpret_cast<const _Float16*>(zeros), reinterpret_cast<_Float16*>(Y), M,
-                     K, N, G, p.u, p.npanels, (int)q4_block_bytes(p));
+                     K, N, G, p.u, p.npanels, p.npanels / grid, p.npanels % grid,
+                     (int)q4_block_bytes(p));
   return hipGetLastError();
 }
 

@@ -116,8 +116,8 @@ template <int MB, int CPB, bool ZP, int BD, int RUN>
 __global__ __launch_bounds__(kQTThreads) void q4_tiled_kernel(
     const _Float16* __restrict__ Xo, const uint8_t* __restrict__ Wp,
     const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
-    _Float16* __restrict__ Y, int M, int mb0, int mbt, int N, int ngroups, int G, int nb,
-    int npanels) {
+    _Float16* __restrict__ Y, int M, int mb0, int mbt, int N, int ngroups, int G, int nb, int pq,
+    int pe) {
   typedef _Float16 h8 __attribute__((ext_vector_type(8)));
   typedef float f4 __attribute__((ext_vector_type(4)));
   typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
@@ -138,8 +138,8 @@ __global__ __launch_bounds__(kQTThreads) void q4_tiled_kernel(
   // share the XCD too, and so the run's weight in that L2.
   const int G8 = gridDim.x % 8 == 0 ? gridDim.x / 8 : 0;
   const int run = G8 ? (int)(blockIdx.x % 8) * G8 + (int)(blockIdx.x / 8) : (int)blockIdx.x;
-  const int p_begin = (int)((long long)run * npanels / gridDim.x);
-  const int npr = (int)((long long)(run + 1) * npanels / gridDim.x) - p_begin;
+  const SplitPart part = split_part(run, pq, pe);
+  const int p_begin = part.begin, npr = part.count;
   // This wave's blocks [bw0, bw0 + nbw).  The share a wave takes rotates
   // with the workgroup, so the workgroups of an XCD do not all read the same
   // rows of X at the same moment.
@@ -398,7 +398,8 @@ static hipError_t launch_q4_tiled_t(const _Float16* Xo, const uint8_t* Wp, const
   int grid = npanels < cus ? npanels : cus;
   if ((npanels + grid - 1) / grid > RUN) grid = (npanels + RUN - 1) / RUN;
   hipLaunchKernelGGL((q4_tiled_kernel<MB, CPB, ZP, BD, RUN>), dim3(grid, RG), dim3(kQTThreads), 0, s,
-                     Xo, Wp, scales, zeros, Y, M, mb0, mbt, N, K / G, G, nb, npanels);
+                     Xo, Wp, scales, zeros, Y, M, mb0, mbt, N, K / G, G, nb, npanels / grid,
+                     npanels % grid);
   return hipGetLastError();
 }
 

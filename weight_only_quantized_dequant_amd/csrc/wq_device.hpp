@@ -43,6 +43,18 @@ __device__ __forceinline__ u32x4 buffer_stream(__amdgpu_buffer_rsrc_t r, int off
 // Offset that is always out of range: the load returns zeros.
 constexpr int kOutOfRange = 0x7FFFFFF0;
 
+// Part r of a contiguous split of n items into g parts, with q = n / g and
+// e = n % g worked out on the host: part r takes q + 1 items if r < e, else
+// q, and the parts follow each other in order.  (Two scalar multiplies; the
+// division n * r / g in the kernel costs a 64-bit software divide before the
+// first load can be addressed.)
+struct SplitPart {
+  int begin, count;
+};
+__device__ __forceinline__ SplitPart split_part(int r, int q, int e) {
+  return {r * q + (r < e ? r : e), q + (r < e ? 1 : 0)};
+}
+
 __device__ __forceinline__ float dot2(h2 a, h2 b, float c) {
   return __builtin_amdgcn_fdot2(a, b, c, false);
 }
