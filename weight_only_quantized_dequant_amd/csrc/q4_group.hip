@@ -217,8 +217,11 @@ template <int MT, int NSC, bool ZP, int BITS>
 __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
     const _Float16* __restrict__ X, const uint8_t* __restrict__ Wp,
     const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
-    _Float16* __restrict__ Y, int M, int K, int N, int G, int nb, int npanels, int pq, int pe,
+    _Float16* __restrict__ Y, int M, int K, int N, int lg, int nb, int npanels, int pq, int pe,
     int packed_bytes) {
+  // G = 2^lg (the entry points take powers of two only): group arithmetic by
+  // shifts, with no integer divide ahead of the first load.
+  const int G = 1 << lg;
   typedef _Float16 h8 __attribute__((ext_vector_type(8)));
   typedef float f4 __attribute__((ext_vector_type(4)));
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -245,19 +248,18 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
   const int p_begin = part.begin, npr = part.count;
 
   // Blocks of this wave: a group-aligned contiguous range.
-  const int bpg = G >= BR ? G / BR : 1;
-  const int nsplit = nb / bpg;
+  constexpr int lBR = __builtin_ctz(BR);
+  const int lbpg = lg > lBR ? lg - lBR : 0;  // log2(bpg)
+  const int bpg = 1 << lbpg;
+  const int nsplit = nb >> lbpg;
   const int blo = (wave * nsplit / kQ4Waves) * bpg, bhi = ((wave + 1) * nsplit / kQ4Waves) * bpg;
   const int nbw = bhi - blo;
   const int nitems = npr * nbw;
 
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wp, packed_bytes);
-  const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, (K / G) * N * 2);
-  const __amdgpu_buffer_rsrc_t zr = make_rsrc(ZP ? zeros : scales, (K / G) * N * 2);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, (K >> lg) * N * 2);
+  const __amdgpu_buffer_rsrc_t zr = make_rsrc(ZP ? zeros : scales, (K >> lg) * N * 2);
   const int col = lane & 15;
-
-  int lbpg = 0;  // log2(bpg): G is a power of two
-  while ((1 << lbpg) < bpg) ++lbpg;
 
   // Ring buffers: one 16-byte word quadruple, NL scale bits and (ZP) NL zero
   // bits per block.
@@ -360,8 +362,8 @@ __global__ __launch_bounds__(kQ4Threads) void q4_mfma_kernel(
   // never stored.
   {
     const h2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
-    const int octs = G / 8, part = lane & 7;
-    const int g0 = blo * BR / G, ng = nbw * BR / G;
+    const int octs = G >> 3, part = lane & 7;
+    const int g0 = (blo * BR) >> lg, ng = (nbw * BR) >> lg;
     for (int task = lane >> 3; task < ng * MT; task += 8) {
       const int g = g0 + task / MT, m = task % MT;
       const _Float16* row = xa + (size_t)m * rs + (size_t)g * G;
@@ -631,7 +633,7 @@ static hipError_t launch_q4_t(const void* X, const void* packed, const void* sca
                      reinterpret_cast<const _Float16*>(X), reinterpret_cast<const uint8_t*>(packed),
                      reinterpret_cast<const _Float16*>(scales),
                      reinterpret_cast<const _Float16*>(zeros), reinterpret_cast<_Float16*>(Y), M,
-                     K, N, G, p.u, p.npanels, p.npanels / grid, p.npanels % grid,
+                     K, N, __builtin_ctz((unsigned)G), p.u, p.npanels, p.npanels / grid, p.npanels % grid,
                      (int)q4_block_bytes(p));
   return hipGetLastError();
 }

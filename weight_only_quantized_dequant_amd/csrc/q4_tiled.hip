@@ -116,7 +116,7 @@ template <int MB, int CPB, bool ZP, int BD, int RUN>
 __global__ __launch_bounds__(kQTThreads) void q4_tiled_kernel(
     const _Float16* __restrict__ Xo, const uint8_t* __restrict__ Wp,
     const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
-    _Float16* __restrict__ Y, int M, int mb0, int mbt, int N, int ngroups, int G, int nb, int pq,
+    _Float16* __restrict__ Y, int M, int mb0, int mbt, int N, int ngroups, int lg, int nb, int pq,
     int pe) {
   typedef _Float16 h8 __attribute__((ext_vector_type(8)));
   typedef float f4 __attribute__((ext_vector_type(4)));
@@ -202,7 +202,7 @@ __global__ __launch_bounds__(kQTThreads) void q4_tiled_kernel(
       q.w[p] = __builtin_amdgcn_raw_buffer_load_b128(wr[p], wlane, j * 1024, 2);
     // First group of the block; the whole offset is in the lane's offset,
     // so groups past the last one (padding rows) fall out of range.
-    const int g0 = ((bw0 + j) * kQ4Block) / G;
+    const int g0 = ((bw0 + j) * kQ4Block) >> lg;  // G = 2^lg
     const int so = tlive ? tlane + g0 * N * 2 : kOutOfRange;
     q.sc = __builtin_bit_cast(u32x2v, __builtin_amdgcn_raw_buffer_load_b64(sr, so, 0, 0));
     if constexpr (ZP)
@@ -398,7 +398,7 @@ static hipError_t launch_q4_tiled_t(const _Float16* Xo, const uint8_t* Wp, const
   int grid = npanels < cus ? npanels : cus;
   if ((npanels + grid - 1) / grid > RUN) grid = (npanels + RUN - 1) / RUN;
   hipLaunchKernelGGL((q4_tiled_kernel<MB, CPB, ZP, BD, RUN>), dim3(grid, RG), dim3(kQTThreads), 0, s,
-                     Xo, Wp, scales, zeros, Y, M, mb0, mbt, N, K / G, G, nb, npanels / grid,
+                     Xo, Wp, scales, zeros, Y, M, mb0, mbt, N, K / G, __builtin_ctz((unsigned)G), nb, npanels / grid,
                      npanels % grid);
   return hipGetLastError();
 }
