@@ -131,7 +131,7 @@ template <int MT, bool FOLD, bool ONE = false>
 __global__ __launch_bounds__(kQ8Threads) void q8_pair_kernel(
     const _Float16* __restrict__ X, const uint8_t* __restrict__ Wp,
     const float* __restrict__ scales, _Float16* __restrict__ Y, int M, int K, int N, int G,
-    int gsh) {
+    int gsh, int ngroups) {
   static_assert(!ONE || (MT == 1 && FOLD), "the single-chunk form is for one row");
   if constexpr (ONE) {
     M = 1;
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kQ8Threads) void q8_pair_kernel(
 
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wp, K * N);
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, M * K * 2);
-  const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, (K / G) * N * 4);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, ngroups * N * 4);  // ngroups = K / G
 
   float tot[MT][2];
 #pragma unroll
@@ -377,7 +377,7 @@ template <int MT, int CL>
 __global__ __launch_bounds__(kQ8Threads) void q8_mfma_kernel(
     const _Float16* __restrict__ X, const uint8_t* __restrict__ Wp,
     const float* __restrict__ scales, _Float16* __restrict__ Y, int M, int K, int N, int G,
-    int gsh) {
+    int gsh, int ngroups) {
   constexpr int NSTEP = 16;                    // 32-row steps per wave per chunk
   constexpr int NC = NSTEP / CL;               // chains per wave per chunk
   constexpr int NG = kQ8Chunk / (32 * CL);     // chains per chunk
@@ -407,7 +407,7 @@ __global__ __launch_bounds__(kQ8Threads) void q8_mfma_kernel(
 
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wp, K * N);
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, M * K * 2);
-  const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, (K / G) * N * 4);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, ngroups * N * 4);  // ngroups = K / G
 
   // tot[r]: row 4 (l / 16) + r of X, column 16 panel + l % 16, units of 2^-24.
   float tot[RR];
@@ -557,7 +557,7 @@ template <int CL>
 __global__ __launch_bounds__(kQ8Threads) void q8_mfma32_kernel(
     const _Float16* __restrict__ X, const uint8_t* __restrict__ Wp,
     const float* __restrict__ scales, _Float16* __restrict__ Y, int M, int K, int N, int G,
-    int gsh) {
+    int gsh, int ngroups) {
   constexpr int MT = 32, CH = 2048;
   constexpr int NL = CH / (64 * kQ8Waves);    // 1 KB loads per wave per chunk: 4
   constexpr int NSTEP = 2 * NL;               // 32-row steps per wave per chunk: 8
@@ -581,7 +581,7 @@ __global__ __launch_bounds__(kQ8Threads) void q8_mfma32_kernel(
 
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wp, K * N);
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, M * K * 2);
-  const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, (K / G) * N * 4);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, ngroups * N * 4);  // ngroups = K / G
 
   // tot[tt][r]: row 16 tt + 4 (l / 16) + r of X, column 16 panel + l % 16, units of 2^-24.
   float tot[2][4];
@@ -750,13 +750,13 @@ static hipError_t launch_q8_t(const void* X, const void* packed, const float* sc
     if (K == kQ8Chunk) {
       hipLaunchKernelGGL((q8_pair_kernel<1, true, true>), dim3(N / 16), dim3(kQ8Threads), 0, s,
                          reinterpret_cast<const _Float16*>(X), reinterpret_cast<const uint8_t*>(packed),
-                         scales, reinterpret_cast<_Float16*>(Y), M, K, N, G, gsh);
+                         scales, reinterpret_cast<_Float16*>(Y), M, K, N, G, gsh, K / G);
       return hipGetLastError();
     }
   }
   hipLaunchKernelGGL((q8_pair_kernel<MT, FOLD>), dim3(N / 16), dim3(kQ8Threads), 0, s,
                      reinterpret_cast<const _Float16*>(X), reinterpret_cast<const uint8_t*>(packed),
-                     scales, reinterpret_cast<_Float16*>(Y), M, K, N, G, gsh);
+                     scales, reinterpret_cast<_Float16*>(Y), M, K, N, G, gsh, K / G);
   return hipGetLastError();
 }
 
@@ -774,11 +774,11 @@ static hipError_t launch_q8_rows(const void* X, const void* packed, const float*
   const uint8_t* w = reinterpret_cast<const uint8_t*>(packed);
   _Float16* y = reinterpret_cast<_Float16*>(Y);
   switch (CL) {
-    case 16: hipLaunchKernelGGL((q8_mfma_kernel<MT, 16>), grid, block, 0, s, x, w, scales, y, M, K, N, G, gsh); break;
-    case 8: hipLaunchKernelGGL((q8_mfma_kernel<MT, 8>), grid, block, 0, s, x, w, scales, y, M, K, N, G, gsh); break;
-    case 4: hipLaunchKernelGGL((q8_mfma_kernel<MT, 4>), grid, block, 0, s, x, w, scales, y, M, K, N, G, gsh); break;
-    case 2: hipLaunchKernelGGL((q8_mfma_kernel<MT, 2>), grid, block, 0, s, x, w, scales, y, M, K, N, G, gsh); break;
-    default: hipLaunchKernelGGL((q8_mfma_kernel<MT, 1>), grid, block, 0, s, x, w, scales, y, M, K, N, G, gsh); break;
+    case 16: hipLaunchKernelGGL((q8_mfma_kernel<MT, 16>), grid, block, 0, s, x, w, scales, y, M, K, N, G, gsh, K / G); break;
+    case 8: hipLaunchKernelGGL((q8_mfma_kernel<MT, 8>), grid, block, 0, s, x, w, scales, y, M, K, N, G, gsh, K / G); break;
+    case 4: hipLaunchKernelGGL((q8_mfma_kernel<MT, 4>), grid, block, 0, s, x, w, scales, y, M, K, N, G, gsh, K / G); break;
+    case 2: hipLaunchKernelGGL((q8_mfma_kernel<MT, 2>), grid, block, 0, s, x, w, scales, y, M, K, N, G, gsh, K / G); break;
+    default: hipLaunchKernelGGL((q8_mfma_kernel<MT, 1>), grid, block, 0, s, x, w, scales, y, M, K, N, G, gsh, K / G); break;
   }
   return hipGetLastError();
 }
@@ -797,10 +797,10 @@ static hipError_t launch_q8_rows32(const void* X, const void* packed, const floa
   const uint8_t* w = reinterpret_cast<const uint8_t*>(packed);
   _Float16* y = reinterpret_cast<_Float16*>(Y);
   switch (CL) {
-    case 8: hipLaunchKernelGGL((q8_mfma32_kernel<8>), grid, block, 0, s, x, w, scales, y, M, K, N, G, gsh); break;
-    case 4: hipLaunchKernelGGL((q8_mfma32_kernel<4>), grid, block, 0, s, x, w, scales, y, M, K, N, G, gsh); break;
-    case 2: hipLaunchKernelGGL((q8_mfma32_kernel<2>), grid, block, 0, s, x, w, scales, y, M, K, N, G, gsh); break;
-    default: hipLaunchKernelGGL((q8_mfma32_kernel<1>), grid, block, 0, s, x, w, scales, y, M, K, N, G, gsh); break;
+    case 8: hipLaunchKernelGGL((q8_mfma32_kernel<8>), grid, block, 0, s, x, w, scales, y, M, K, N, G, gsh, K / G); break;
+    case 4: hipLaunchKernelGGL((q8_mfma32_kernel<4>), grid, block, 0, s, x, w, scales, y, M, K, N, G, gsh, K / G); break;
+    case 2: hipLaunchKernelGGL((q8_mfma32_kernel<2>), grid, block, 0, s, x, w, scales, y, M, K, N, G, gsh, K / G); break;
+    default: hipLaunchKernelGGL((q8_mfma32_kernel<1>), grid, block, 0, s, x, w, scales, y, M, K, N, G, gsh, K / G); break;
   }
   return hipGetLastError();
 }
