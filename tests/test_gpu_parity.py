@@ -94,6 +94,10 @@ def assert_fwd_bound(y, y_exact, abs_sum, n_terms, out="f16", what=""):
     (1, 1536, 256, 384),         # group of 384 rows (not a power of two): a scale per piece
     (6, 8192, 512, 128),         # 8-row pass, activations restaged in LDS per chunk
     (7, 4224, 272, 64),          # 8-row pass, ragged chunk, scale per piece
+    # One row and K = 4096 run the single-chunk form: larger groups (the
+    # scale row of each 128-row block found by a shift), and panel counts
+    # that are not a multiple of 16 (the plain workgroup-to-panel order).
+    (1, 4096, 400, 256), (1, 4096, 1040, 1024), (1, 4096, 512, 4096), (1, 4096, 48, 2048),
 ])
 def test_q8_group_vs_oracle(wq, M, K, N, G):
     d = synth.gen_q8_group(M, K, N, G, seed=1100 if (M, K, N) == (1, 4096, 4096) else 7 + M + K + N)
