@@ -182,6 +182,10 @@ __global__ __launch_bounds__(kQ8Threads) void q8_pair_kernel(
     for (int m = 0; m < MT; ++m)
       xg[m] = __builtin_amdgcn_raw_buffer_load_b128(
           xr, (m < M && r0 + 8 * t < K) ? (m * K + r0 + 8 * t) * 2 : kOutOfRange, 0, 0);
+    if constexpr (ONE) {  // the activation load goes out first (IR and machine order)
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    }
     constexpr int NS = FOLD ? 1 : kQ8Steps;  // scale loads per lane per chunk
     float fs = 0.0f;
     u32x2 sc[NS];
