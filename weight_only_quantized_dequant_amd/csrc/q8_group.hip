@@ -179,9 +179,13 @@ __global__ __launch_bounds__(kQ8Threads) void q8_pair_kernel(
     // leaves the rest in flight.
     u32x4 xg[MT];
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
-      xg[m] = __builtin_amdgcn_raw_buffer_load_b128(
-          xr, (m < M && r0 + 8 * t < K) ? (m * K + r0 + 8 * t) * 2 : kOutOfRange, 0, 0);
+    for (int m = 0; m < MT; ++m) {
+      if constexpr (ONE)  // one row, one chunk, 8 t < 4096: always in range
+        xg[m] = __builtin_amdgcn_raw_buffer_load_b128(xr, 16 * t, 0, 0);
+      else
+        xg[m] = __builtin_amdgcn_raw_buffer_load_b128(
+            xr, (m < M && r0 + 8 * t < K) ? (m * K + r0 + 8 * t) * 2 : kOutOfRange, 0, 0);
+    }
     if constexpr (ONE) {  // the activation load goes out first (IR and machine order)
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
