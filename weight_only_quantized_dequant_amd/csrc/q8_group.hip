@@ -133,6 +133,10 @@ __global__ __launch_bounds__(kQ8Threads) void q8_pair_kernel(
     const float* __restrict__ scales, _Float16* __restrict__ Y, int M, int K, int N, int G,
     int gsh, int ngroups) {
   static_assert(!ONE || (MT == 1 && FOLD), "the single-chunk form is for one row");
+  // The host launches with K >= 32: the first chunk is unconditional, so
+  // the kernel arguments can be requested in one batch.
+  __builtin_assume(K > 0);
+  if constexpr (!ONE) asm volatile("" ::"s"(X), "s"(Wp), "s"(scales));
   if constexpr (ONE) {
     M = 1;
     K = kQ8Chunk;
@@ -386,6 +390,10 @@ __global__ __launch_bounds__(kQ8Threads) void q8_mfma_kernel(
     const _Float16* __restrict__ X, const uint8_t* __restrict__ Wp,
     const float* __restrict__ scales, _Float16* __restrict__ Y, int M, int K, int N, int G,
     int gsh, int ngroups) {
+  // The host launches with K >= 32: the first chunk is unconditional, so
+  // the kernel arguments can be requested in one batch.
+  __builtin_assume(K > 0);
+  asm volatile("" ::"s"(scales));
   constexpr int NSTEP = 16;                    // 32-row steps per wave per chunk
   constexpr int NC = NSTEP / CL;               // chains per wave per chunk
   constexpr int NG = kQ8Chunk / (32 * CL);     // chains per chunk
